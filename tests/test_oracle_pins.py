@@ -1,0 +1,456 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-types the oracle's formulas: they compare it with
+hand-derived values of the pages' examples (tests/golden), with torch.chunk
+(the library routine that implements the same ceil-chunk split), with
+brute-force forward maps on tiny inputs, with exact integer sums, with a
+float64 error bound, and with the group lists the pages print.  The
+planted-mistake tests at the end show that a plausible slip in the oracle
+fails at least one pin.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import fsdp_oracle as F
+from oracle import pointwise as PW
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------------------
+# pin helpers: each returns a list of failure strings (empty = pinned)
+# ---------------------------------------------------------------------------
+
+def pin_golden_dim0(golden):
+    bad = []
+    for c in golden["dim0"]:
+        lay = O.bucket_layout([tuple(c["shape"])], c["shard_size"])
+        got = (lay.chunk_rows[0], lay.row_off[0], lay.row_len[0], lay.padded[0])
+        want = (c["chunk_rows"], c["row_off"], c["row_len"], c["padded"])
+        if got != want:
+            bad.append(f"{c['shape']} S={c['shard_size']}: {got} != {want}")
+    for b in golden["buckets"]:
+        lay = O.bucket_layout([tuple(s) for s in b["shapes"]], b["shard_size"])
+        if (lay.in_off, lay.I) != (b["in_off"], b["I"]):
+            bad.append(f"bucket {b['shapes']}: {(lay.in_off, lay.I)}")
+    return bad
+
+
+def pin_torch_chunk(max_n0=40, max_s=9):
+    """Non-empty shards equal torch.chunk's pieces, in order; the rest are empty."""
+    bad = []
+    for n0 in range(0, max_n0 + 1):
+        x = torch.arange(n0 * 3).reshape(n0, 3)
+        for S in range(1, max_s + 1):
+            lay = O.bucket_layout([(n0, 3)], S)
+            shards = O.shard_params([x.numpy()], lay)
+            pieces = [p.numpy() for p in torch.chunk(x, S, dim=0)] if n0 > 0 else []
+            nonempty = [sh[0] for sh in shards if sh[0].shape[0] > 0]
+            if len(nonempty) != len(pieces) or any(
+                    not np.array_equal(a, b) for a, b in zip(nonempty, pieces)):
+                bad.append(f"n0={n0} S={S}")
+            # empty shards all come after the non-empty ones
+            lens = [sh[0].shape[0] for sh in shards]
+            if lens != sorted(lens, reverse=True):
+                bad.append(f"n0={n0} S={S}: lengths {lens} not non-increasing")
+            if lay.chunk_rows[0] != (pieces[0].shape[0] if pieces else 0):
+                bad.append(f"n0={n0} S={S}: chunk rows {lay.chunk_rows[0]}")
+    return bad
+
+
+def forward_map_ag(params, lay):
+    """Brute force: every element (r, c) of parameter i goes to the unique
+    rank whose rows contain r, at its row-within-shard; everything else 0."""
+    S, I = lay.S, lay.I
+    want = [None] * (S * I)
+    for i, x in enumerate(params):
+        x2 = x.reshape(x.shape[0], lay.inner[i])
+        for r in range(x2.shape[0]):
+            owners = [s for s in range(S) if lay.row_off[i][s] <= r < lay.row_off[i][s] + lay.row_len[i][s]]
+            assert len(owners) == 1
+            s = owners[0]
+            for c in range(x2.shape[1]):
+                pos = s * I + lay.in_off[i] + (r - lay.row_off[i][s]) * lay.inner[i] + c
+                assert want[pos] is None
+                want[pos] = x2[r, c]
+    return want
+
+
+def pin_ag_bruteforce(dtype=np.float32, max_s=9):
+    bad = []
+    for S in range(1, max_s + 1):
+        for inner in (1, 2, 3, 5, 8):
+            for n0 in range(0, 3 * S + 3):
+                shape = (n0,) if inner == 1 else (n0, inner)
+                x = (RNG.standard_normal(shape) * 100).astype(np.float32)
+                if dtype == np.uint16:
+                    x = x.view(np.uint32).astype(np.uint16)  # arbitrary bit patterns
+                lay = O.bucket_layout([shape], S)
+                ag = O.ag_copy_in(O.shard_params([x], lay), lay, x.dtype)
+                want = forward_map_ag([x], lay)
+                for p, w in enumerate(want):
+                    v = ag[p]
+                    if (w is None and v != 0) or (w is not None and v != w):
+                        bad.append(f"S={S} shape={shape} pos={p}")
+                        break
+                full = O.ag_copy_out(O.all_gather(ag), lay)[0]
+                if full.shape != x.shape or not np.array_equal(full.view(np.uint8), x.view(np.uint8)):
+                    bad.append(f"roundtrip S={S} shape={shape}")
+    return bad
+
+
+def pin_ag_multiparam():
+    """all_gather(shard(x)) == x for mixed buckets, and every padding element is 0."""
+    bad = []
+    shape_pool = [(7, 8), (5, 3), (16,), (3,), (1, 5), (0, 2), (9,), (2, 2, 3), (13, 1)]
+    for S in (1, 2, 3, 4, 5, 8):
+        for k in range(4):
+            idx = RNG.choice(len(shape_pool), size=4, replace=True)
+            shapes = [shape_pool[j] for j in idx]
+            xs = [(RNG.standard_normal(sh) + 3).astype(np.float32) for sh in shapes]  # nonzero
+            lay = O.bucket_layout(shapes, S)
+            ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np.float32)
+            outs = O.ag_copy_out(O.all_gather(ag), lay)
+            if any(not np.array_equal(a, b) for a, b in zip(outs, xs)):
+                bad.append(f"roundtrip {shapes} S={S}")
+            n_data = sum(x.size for x in xs)
+            if int(np.count_nonzero(ag)) != n_data or ag.size != S * sum(lay.padded):
+                bad.append(f"padding {shapes} S={S}")
+            want = forward_map_ag(xs, lay)
+            got_zero = [p for p, w in enumerate(want) if w is None]
+            if np.any(ag[got_zero] != 0):
+                bad.append(f"pad positions {shapes} S={S}")
+    return bad
+
+
+def textbook_rs(grads_int, shapes, members, s, S):
+    """Exact reduce-scatter: chunk s (torch.chunk) of the int64 sum over members."""
+    out = []
+    for i, sh in enumerate(shapes):
+        tot = sum(torch.as_tensor(grads_int[m][i]).to(torch.int64) for m in members)
+        pieces = torch.chunk(tot, S, dim=0) if sh[0] > 0 else []
+        out.append(pieces[s] if s < len(pieces) else torch.zeros((0,) + tuple(sh[1:]), dtype=torch.int64))
+    return out
+
+
+def pin_rs_exact(R, S, op, shapes):
+    bad = []
+    D = R // S
+    gi = [[RNG.integers(-8, 9, size=sh).astype(np.float32) for sh in shapes] for _ in range(R)]
+    lay = O.bucket_layout(shapes, S)
+    rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
+    outs = O.rs_reduce(rs_in, lay.I, R, S, op)
+    for g in range(R):
+        d, s = divmod(g, S)
+        members = list(range(d * S, d * S + S))
+        want = textbook_rs(gi, shapes, members, s, S)
+        for i in range(len(shapes)):
+            got = O.sharded_grad(outs[g], lay, i, s)
+            w = want[i].to(torch.float64).numpy() / (S if op == O.AVG else 1)
+            if got.shape != w.shape or not np.array_equal(got.astype(np.float64), w):
+                bad.append(f"RS R={R} S={S} {op} g={g} param={i}")
+        # padding of the RS output is zero (a zero-padded input reduces to zero)
+        mask = np.ones(lay.I, bool)
+        for i in range(len(shapes)):
+            a = lay.in_off[i]
+            mask[a:a + lay.row_len[i][s] * lay.inner[i]] = False
+        if np.any(outs[g][mask] != 0):
+            bad.append(f"RS padding g={g}")
+    return bad
+
+
+def pin_end_to_end_exact(R, S, op, shapes, buckets=None):
+    """After RS then AR, rank (d, s) holds chunk s of the sum over all R ranks
+    (SUM) or that sum over R (AVG; exact for power-of-two S and D)."""
+    bad = []
+    gi = [[RNG.integers(-8, 9, size=sh).astype(np.float32) for sh in shapes] for _ in range(R)]
+    buckets = buckets or [shapes]
+    res, fused, offs, lays = O.reduce_grads_fused(gi, buckets, R, S, op)
+    for g in range(R):
+        s = g % S
+        want = textbook_rs(gi, shapes, list(range(R)), s, S)
+        for i in range(len(shapes)):
+            w = want[i].to(torch.float64).numpy() / (R if op == O.AVG else 1)
+            got = res[g][i].astype(np.float64)
+            if got.shape != w.shape or not np.array_equal(got, w):
+                bad.append(f"e2e R={R} S={S} {op} g={g} param={i}")
+    return bad
+
+
+# ---------------------------------------------------------------------------
+# tests
+# ---------------------------------------------------------------------------
+
+def test_golden_dim0_and_bucket(golden):
+    assert pin_golden_dim0(golden) == []
+
+
+def test_chunk_matches_torch_chunk():
+    assert pin_torch_chunk() == []
+
+
+def test_chunk_differs_from_array_split():
+    # np.array_split balances the remainder over the first ranks (2,1,1,1);
+    # the pages' fixed-size chunking gives (2,2,1,0).
+    _, _, lens = O.dim0_chunk(5, 4)
+    assert lens == [2, 2, 1, 0]
+    assert [len(a) for a in np.array_split(np.arange(5), 4)] == [2, 1, 1, 1]
+
+
+def test_chunk_invariants():
+    for n0, S in itertools.product(range(0, 70), range(1, 17)):
+        chunk, offs, lens = O.dim0_chunk(n0, S)
+        assert sum(lens) == n0
+        assert all(0 <= n <= chunk for n in lens)
+        assert offs[0] == 0 and all(offs[s + 1] == offs[s] + lens[s] for s in range(S - 1))
+        partial = [n for n in lens if 0 < n < chunk]
+        assert len(partial) <= 1
+        assert chunk * S >= n0 and (chunk - 1) * S < n0 or n0 == 0
+        if n0 % S == 0:  # even parameter: no padding at all
+            assert chunk * S == n0 and all(n == chunk for n in lens)
+
+
+def test_ag_bruteforce_fp32():
+    assert pin_ag_bruteforce(np.float32, max_s=9) == []
+
+
+def test_ag_bruteforce_bf16_bits():
+    assert pin_ag_bruteforce(np.uint16, max_s=5) == []
+
+
+def test_ag_multiparam_roundtrip_and_padding():
+    assert pin_ag_multiparam() == []
+
+
+def test_pointwise_forms_match_full_forms():
+    shapes = [(7, 8), (5, 3), (16,), (0, 3), (3,)]
+    for S in (1, 3, 4, 8):
+        xs = [(RNG.standard_normal(sh) + 5).astype(np.float32) for sh in shapes]
+        lay = O.bucket_layout(shapes, S)
+        ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np.float32)
+        pos = np.arange(ag.size)
+        got = PW.packed_values(lay, pos, lambda i, f: xs[i].reshape(-1)[f], np.float32)
+        assert np.array_equal(got, ag)
+        outs = O.ag_copy_out(ag, lay)
+        for i, x in enumerate(xs):
+            src = PW.unpacked_sources(lay, i, np.arange(x.size))
+            assert np.array_equal(ag[src], outs[i].reshape(-1))
+        assert set(PW.boundary_positions(lay).tolist()) <= set(range(lay.I))
+
+
+@pytest.mark.parametrize("R,S", [(4, 4), (8, 4), (8, 8), (8, 2), (6, 3)])
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_rs_exact_integer_sums(R, S, op):
+    if op == O.AVG and S & (S - 1):
+        pytest.skip("division by a non-power-of-two is not exact")
+    assert pin_rs_exact(R, S, op, [(7, 8), (5, 3), (16,), (3,), (11, 2)]) == []
+
+
+@pytest.mark.parametrize("R,S", [(8, 4), (8, 1), (4, 4), (8, 2), (2, 1)])
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_end_to_end_exact_integer_sums(R, S, op):
+    shapes = [(7, 8), (5, 3), (16,), (3,), (9, 4)]
+    assert pin_end_to_end_exact(R, S, op, shapes) == []
+    # the same result with one bucket per parameter (several fused segments)
+    assert pin_end_to_end_exact(R, S, op, shapes, buckets=[[s] for s in shapes]) == []
+
+
+def test_float64_error_bound():
+    """Non-integer float32 sums: within the float32 rounding bound of the
+    exact (float64) result, whatever the summation order."""
+    shapes = [(33, 7), (10,), (5, 3)]
+    for R, S in ((8, 4), (8, 8), (16, 16)):
+        gi = [[RNG.standard_normal(sh).astype(np.float32) for sh in shapes] for _ in range(R)]
+        lay = O.bucket_layout(shapes, S)
+        rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
+        for op in (O.SUM, O.AVG):
+            outs = O.rs_reduce(rs_in, lay.I, R, S, op)
+            for g in range(R):
+                d, s = divmod(g, S)
+                xs = np.stack([rs_in[m][s * lay.I:(s + 1) * lay.I].astype(np.float64)
+                               for m in range(d * S, d * S + S)])
+                exact = xs.sum(0) / (S if op == O.AVG else 1)
+                bound = (S - 1) * 2.0 ** -24 * np.abs(xs).sum(0) / (S if op == O.AVG else 1) \
+                    + 2.0 ** -24 * np.abs(exact) + 1e-45
+                assert np.all(np.abs(outs[g].astype(np.float64) - exact) <= bound)
+
+
+def test_avg_is_sum_divided_by_replicate_size():
+    R, S = 8, 2
+    D = R // S
+    fused = [RNG.standard_normal(640).astype(np.float32) for _ in range(R)]
+    a = O.fused_ar(fused, R, S, O.AVG)
+    b = O.fused_ar(fused, R, S, O.SUM)
+    for g in range(R):
+        assert np.array_equal(a[g].view(np.uint32), (b[g] / np.float32(D)).view(np.uint32))
+        assert np.array_equal(a[g], a[g % S])  # every replica holds the result
+
+
+@pytest.mark.parametrize("R,S", [(8, 4), (8, 1), (4, 4), (8, 2), (6, 2)])
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_fused_equals_nonfused_bitwise(R, S, op):
+    shapes = [(7, 8), (5, 3), (16,), (3,), (130,), (9, 4)]
+    gi = [[RNG.standard_normal(sh).astype(np.float32) for sh in shapes] for _ in range(R)]
+    nf = O.reduce_grads_nonfused(gi, shapes, R, S, op)
+    for buckets in ([shapes], [shapes[:2], shapes[2:]], [[s] for s in shapes]):
+        fu, fused, offs, _ = O.reduce_grads_fused(gi, buckets, R, S, op)
+        for g in range(R):
+            for i in range(len(shapes)):
+                assert fu[g][i].shape == nf[g][i].shape
+                assert np.array_equal(fu[g][i].view(np.uint32), nf[g][i].view(np.uint32))
+        for o in offs:
+            assert (o * 4) % 512 == 0
+        assert (fused[0].size * 4) % 512 == 0
+
+
+def test_group_lists_and_decision_matrix(golden):
+    for c in golden["groups"]:
+        assert O.group_sizes(c["rank_size"], c["shard_size"]) == (c["shard_size"], c["dp_size"])
+        got = [[k, g] for k, g in O.grad_sync_plan(c["rank_size"], c["shard_size"])]
+        assert got == c["calls"], c["why"]
+    # every rank is in exactly one shard group and one replicate group, and
+    # a shard group and a replicate group meet in exactly one rank
+    for R, S in ((8, 4), (8, 2), (16, 4), (6, 3)):
+        sg, rg = O.shard_groups(R, S), O.replicate_groups(R, S)
+        assert sorted(sum(sg, [])) == list(range(R)) == sorted(sum(rg, []))
+        assert all(len(set(a) & set(b)) == 1 for a in sg for b in rg)
+
+
+def test_fused_layout_golden(golden):
+    for c in golden["fused"]:
+        offs, Fn = O.fused_layout(c["seg_numel"], c["elem_bytes"])
+        assert (offs, Fn) == (c["offsets"], c["F"]), c["why"]
+    sizes = [int(v) for v in RNG.integers(0, 3000, size=200)]
+    offs, Fn = O.fused_layout(sizes)
+    end = 0
+    for o, n in zip(offs, sizes):
+        assert o * 4 % 512 == 0 and o >= end and o * 4 - end * 4 < 512
+        end = o + n
+    assert Fn * 4 % 512 == 0 and Fn >= end and (Fn - end) * 4 < 512
+
+
+def test_oracle_rejects():
+    with pytest.raises(NotImplementedError):
+        O.bucket_layout([(4, 4)], 2, shard_dim=1)
+    with pytest.raises(ValueError):
+        O.bucket_layout([()], 2)
+    with pytest.raises(ValueError):
+        O.group_sizes(8, 3)
+    with pytest.raises(ValueError):
+        O.group_sizes(8, 0)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must break at least one pin
+# ---------------------------------------------------------------------------
+
+def _floor_chunk(n0, S):
+    chunk = max(n0 // S, 1) if n0 else 0
+    offs = [min(s * chunk, n0) for s in range(S)]
+    lens = [min(chunk, n0 - o) if s < S - 1 else n0 - o for s, o in enumerate(offs)]
+    return chunk, offs, lens
+
+
+def _array_split_chunk(n0, S):
+    lens = [len(a) for a in np.array_split(np.arange(n0), S)]
+    offs = list(np.cumsum([0] + lens[:-1]))
+    return max(lens), [int(o) for o in offs], lens
+
+
+def _head_padding_copy_in(shards, lay, dtype):
+    ag = np.zeros(lay.S * lay.I, dtype=dtype)
+    for s in range(lay.S):
+        for i in range(len(lay.shapes)):
+            flat = np.ascontiguousarray(shards[s][i]).reshape(-1)
+            end = s * lay.I + lay.in_off[i] + lay.padded[i]
+            ag[end - flat.size:end] = flat
+    return ag
+
+
+_ORIG_RS_REDUCE = F.rs_reduce
+_ORIG_BUCKET_LAYOUT = F.bucket_layout
+
+
+def _avg_over_rank_size(rs_in, I, R, S, op):
+    outs = _ORIG_RS_REDUCE(rs_in, I, R, S, F.SUM)
+    return [o / np.float32(R) for o in outs] if op == F.AVG else outs
+
+
+def _drop_last_operand(operands):
+    acc = np.array(operands[0], dtype=np.float32, copy=True)
+    for x in operands[1:-1]:
+        acc = acc + x
+    return acc
+
+
+def _transposed_replicate_groups(R, S):
+    _, D = F.group_sizes(R, S)
+    return [[s * D + d for d in range(D)] for s in range(S)]
+
+
+def _unpadded_bucket_layout(shapes, S, shard_dim=0):
+    lay = _ORIG_BUCKET_LAYOUT(shapes, S, shard_dim)
+    off = 0
+    for i, sh in enumerate(lay.shapes):
+        lay.in_off[i] = off
+        off += sh[0] * lay.inner[i] // S if sh[0] >= S else lay.padded[i]
+    return lay
+
+
+MUTANTS = {
+    "floor_chunk": ("dim0_chunk", _floor_chunk),
+    "array_split": ("dim0_chunk", _array_split_chunk),
+    "head_padding": ("ag_copy_in", _head_padding_copy_in),
+    "avg_over_R": ("rs_reduce", _avg_over_rank_size),
+    "dropped_term": ("_ordered_sum", _drop_last_operand),
+    "rank_mapping": ("replicate_groups", _transposed_replicate_groups),
+    "offset_by_actual": ("bucket_layout", _unpadded_bucket_layout),
+}
+
+
+def _groups_pin(golden):
+    return ["groups %s" % c["why"] for c in golden["groups"]
+            if [[k, g] for k, g in O.grad_sync_plan(c["rank_size"], c["shard_size"])] != c["calls"]]
+
+
+def _all_pins(golden):
+    """Run every pin; a pin that raises counts as failed (and is named)."""
+    pins = [
+        lambda: pin_golden_dim0(golden),
+        lambda: pin_torch_chunk(max_n0=12, max_s=5),
+        lambda: pin_ag_bruteforce(np.float32, max_s=4),
+        pin_ag_multiparam,
+        lambda: pin_rs_exact(8, 4, O.AVG, [(7, 8), (5, 3), (16,)]),
+        lambda: pin_rs_exact(8, 4, O.SUM, [(7, 8), (5, 3), (16,)]),
+        lambda: pin_end_to_end_exact(8, 4, O.SUM, [(7, 8), (5, 3), (16,)]),
+        lambda: pin_end_to_end_exact(8, 4, O.AVG, [(7, 8), (5, 3), (16,)]),
+        lambda: _groups_pin(golden),
+    ]
+    bad = []
+    for k, pin in enumerate(pins):
+        try:
+            bad += pin()
+        except Exception as e:
+            bad.append(f"pin {k} raised {e!r}")
+    return bad
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant, golden, monkeypatch):
+    name, fn = MUTANTS[mutant]
+    monkeypatch.setattr(F, name, fn)
+    if hasattr(O, name):  # the package re-exports most names
+        monkeypatch.setattr(O, name, fn)
+    bad = _all_pins(golden)
+    # caught by a value check, not only by something raising
+    assert [b for b in bad if " raised " not in b], \
+        f"planted mistake {mutant} ({name}) passed every value pin: {bad}"
+
+
+def test_unmutated_oracle_passes_all_pins(golden):
+    assert _all_pins(golden) == []
