@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the FSDP/HSDP flat-buffer hot path on one MI355X.
+
+One step is one pass of the whole hot path over one bucket, inputs already
+resident in HBM: AG copy-in (pack the shards of all S ranks into the padded
+AG buffer), AG copy-out (unpack into the full parameters), RS copy-in (chunk
+the R ranks' full gradients into their padded RS inputs), RS over every
+shard group into views of the 512-byte-aligned fused buffers, and the fused
+AR over every replicate group.  The default workload is the HSDP
+transformer block (hidden 1024; rank_size 8 = 2 replicas x 4 shards; bf16
+parameters, fp32 gradients, AVG).
+
+value = algorithmic bytes of one step x steps / time (GB/s, whole job).
+Algorithmic bytes count every required read and write once (padding is
+written, never read as a copy source):
+  AG copy-in   sum(N_i) e + S I e         AG copy-out  2 sum(N_i) e
+  RS copy-in   4 R (sum(N_i) + S I)       RS reduce    4 R S I + 4 R I
+  fused AR     8 R F
+Timing: W untimed steps, then K steps between synchronisations; HIP events
+on the launch stream around every step give each kernel's average time.
+The CPU oracle is timed on a bounded number of whole steps of the same
+workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s (and % of peak) for AG copy-in/out + RS/AR reduce per bucket"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kernel",
+                  "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
+                  "fused_ar": "reduce_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", "kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def step_bytes(w, lay, F: int):
+    import torch
+    e = 2 if w.param_dtype in (torch.bfloat16, torch.float16) else 4
+    R, S, I = w.rank_size, w.shard_size, lay.I
+    N = sum(_numel(s) for s in w.param_shapes)
+    return {
+        "ag_copy_in": N * e + S * I * e,
+        "ag_copy_out": 2 * N * e,
+        "rs_copy_in": 4 * R * (N + S * I),
+        "rs_reduce": 4 * R * S * I + 4 * R * I,
+        "fused_ar": 8 * R * F,
+    }
+
+
+def _numel(shape):
+    n = 1
+    for d in shape:
+        n *= d
+    return n
+
+
+def measured_traffic(step: str, launches_bytes: int):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 PMC summary, or None when absent or when the kernel source has
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    ent = t.get("steps", {}).get(step)
+    if not ent:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float, op: str):
+    """The oracle, as it stands, timed on whole steps of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    import workloads as W
+
+    R, S = w.rank_size, w.shard_size
+    lay = O.bucket_layout(w.param_shapes, S)
+    params = W.params(w, "cpu")
+    grads = W.grads(w, "cpu")
+    if w.param_dtype == torch.float32:
+        xs = [p.numpy() for p in params]
+        np_dt = np.float32
+    else:
+        xs = [p.view(torch.int16).numpy().view(np.uint16) for p in params]
+        np_dt = np.uint16
+    gnp = [[t.numpy() for t in grads[g]] for g in range(R)]
+    offs, F = O.fused_layout([lay.I])
+    do_ar = bool([c for c in O.grad_sync_plan(R, S) if c[0] == "AR"])
+
+    def one_step():
+        ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt)
+        O.ag_copy_out(O.all_gather(ag), lay)
+        rs_in = [O.rs_copy_in(gnp[g], lay) for g in range(R)]
+        out = O.rs_reduce(rs_in, lay.I, R, S, op)
+        fused = []
+        for g in range(R):
+            buf = np.zeros(F, np.float32)
+            buf[offs[0]:offs[0] + lay.I] = out[g]
+            fused.append(buf)
+        if do_ar:
+            O.fused_ar(fused, R, S, op)
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 200:
+            break
+    return n, el, F
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="hsdp_block_h1024_r8_s4_d2")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this build runs on one GPU only (the R ranks are "
+              "simulated as HBM-resident slices of one GPU); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = W.WORKLOADS[args.workload]
+    R, S, D = w.rank_size, w.shard_size, w.dp_size
+    op = w.reduce_ops[0]
+    P = len(w.param_shapes)
+    torch.cuda.set_device(0)
+    log(f"bench: workload {w.name} ({w.description}); R={R} S={S} D={D} op={op}")
+
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
+    params = W.params(w, "cuda")
+    grads = W.grads(w, "cuda")
+    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+    steps = fb.steps()
+    nbytes = step_bytes(w, fb.layout, fb.F)
+    bytes_per_step = sum(nbytes[s] for s in steps)
+
+    for _ in range(args.warmup):
+        fb.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(K):
+        for j, name in enumerate(steps):
+            ev[k][j][0].record()
+            fb.run(name)
+            ev[k][j][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    value = bytes_per_step * K / (total_ms * 1e-3) / 1e9
+
+    ops = {}
+    for j, name in enumerate(steps):
+        us = sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(K)) / K * 1e3
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        ops[name] = {"kernel": KERNEL_OF_STEP[name], "bytes": nbytes[name], "us": round(us, 2),
+                     "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  {name:12s} {nbytes[name] / 1e6:10.1f} MB  {us:9.1f} us  {gbs:8.1f} GB/s  "
+            f"{100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
+    dom = max(steps, key=lambda s: ops[s]["us"])
+    roof = {"bound": "hbm", "kernel": KERNEL_OF_STEP[dom], "step": dom,
+            "achieved": ops[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ops[dom]["GB/s"] / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom, nbytes[dom])}
+    log(f"  step: {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s; wall {wall:.3f} s for {K} steps")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n, el, F = cpu_baseline(w, args.cpu_seconds, op)
+        cpu = {"value": round(bytes_per_step * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} whole steps of {w.name} (all {len(steps)} steps, full size) in {el:.1f} s; "
+                         f"NumPy, single-threaded"}
+        log(f"  cpu oracle: {cpu['value']} GB/s over {n} steps ({el:.1f} s)")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "rank_size": R, "shard_size": S, "dp_size": D,
+                   "param_dtype": str(w.param_dtype).replace("torch.", ""), "grad_dtype": "float32",
+                   "reduce_op": op, "params": P, "elements": sum(_numel(s) for s in w.param_shapes),
+                   "slice_numel": fb.layout.I, "fused_numel": fb.F, "bytes_per_step": bytes_per_step,
+                   "steps_per_pass": steps},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "ops": ops,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

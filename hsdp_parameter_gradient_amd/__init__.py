@@ -1,0 +1,37 @@
+"""MI355X-native FSDP/HSDP flat-buffer hot path.
+
+A thin ctypes binding over libfsdpflat.so (the C ABI of include/fsdp_flat.h).
+The functions have the C entry points' names and only marshal arguments:
+every step of the path runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library has not been built, the first call raises.
+"""
+
+from ._binding import (  # noqa: F401
+    AVG,
+    SUM,
+    FSDPError,
+    Layout,
+    fsdp_ag_copy_in,
+    fsdp_ag_copy_out,
+    fsdp_bucket_layout,
+    fsdp_fused_ar,
+    fsdp_fused_layout,
+    fsdp_group_ranks,
+    fsdp_last_error,
+    fsdp_release_cache,
+    fsdp_rs_copy_in,
+    fsdp_rs_reduce,
+    lib,
+    lib_path,
+    prepare,
+)
+from .flat_bucket import FlatBucket  # noqa: F401
+
+__all__ = [
+    "FlatBucket",
+    "AVG", "SUM", "FSDPError", "Layout", "fsdp_ag_copy_in", "fsdp_ag_copy_out",
+    "fsdp_bucket_layout", "fsdp_fused_ar", "fsdp_fused_layout", "fsdp_group_ranks",
+    "fsdp_last_error", "fsdp_release_cache", "fsdp_rs_copy_in", "fsdp_rs_reduce",
+    "lib", "lib_path", "prepare",
+]

@@ -1,0 +1,318 @@
+"""ctypes binding of libfsdpflat.so: argument marshalling only.
+
+Each device function takes torch tensors for the buffers, checks that they
+are device tensors of the sizes the C entry point will read and write (the
+C ABI sees bare pointers and cannot check capacities), and calls the entry
+point of the same name on the current HIP stream (or the stream given).
+``prepare(fn, *args)`` does the checks and marshalling once and returns a
+callable that only issues the C call, for loops that repeat one call on the
+same buffers.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_int32, c_int64, c_void_p
+from typing import List, NamedTuple, Optional, Sequence, Tuple
+
+import torch
+
+SUM = "sum"
+AVG = "avg"
+_OPS = {SUM: 0, AVG: 1}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+_CODES = {1: "FSDP_EINVAL", 2: "FSDP_ENOTIMPL", 3: "FSDP_EALIGN", 4: "FSDP_EHIP", 5: "FSDP_EOVERLAP"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+class FSDPError(RuntimeError):
+    """A non-zero status from the library (code and message attached)."""
+
+    def __init__(self, fn: str, code: int, message: str):
+        super().__init__(f"{fn}: {_CODES.get(code, code)}: {message}")
+        self.fn = fn
+        self.code = code
+        self.message = message
+
+
+class _Bucket(ctypes.Structure):
+    _fields_ = [("n_params", c_int32), ("ndim", POINTER(c_int32)),
+                ("shape", POINTER(c_int64)), ("shard_dim", c_int32)]
+
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.environ.get("FSDP_FLAT_LIB", os.path.join(_PKG, "lib", "libfsdpflat.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise FSDPError("load", -1, f"{p} is not built; run `python -m hsdp_parameter_gradient_amd.build`")
+        L = ctypes.CDLL(p)
+        B = POINTER(_Bucket)
+        P64 = POINTER(c_int64)
+        P32 = POINTER(c_int32)
+        sig = {
+            "fsdp_bucket_layout": [B, c_int32, P64, P64, P64, P64, P64],
+            "fsdp_fused_layout": [c_int32, P64, c_int32, P64, P64],
+            "fsdp_group_ranks": [c_int32, c_int32, P32, P32, P32, P32],
+            "fsdp_ag_copy_in": [B, c_int32, c_int32, POINTER(c_void_p), c_void_p, c_void_p],
+            "fsdp_ag_copy_out": [B, c_int32, c_int32, c_void_p, POINTER(c_void_p), c_void_p],
+            "fsdp_rs_copy_in": [B, c_int32, c_int32, c_int32, POINTER(c_void_p), POINTER(c_void_p), c_void_p],
+            "fsdp_rs_reduce": [B, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p),
+                               POINTER(c_void_p), c_void_p],
+            "fsdp_fused_ar": [c_int32, P64, c_int32, c_int32, c_int32, c_int32, c_int32,
+                              POINTER(c_void_p), c_void_p],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = c_int32
+        L.fsdp_last_error.argtypes = []
+        L.fsdp_last_error.restype = c_char_p
+        L.fsdp_release_cache.argtypes = []
+        L.fsdp_release_cache.restype = None
+        _LIB = L
+    return _LIB
+
+
+def fsdp_last_error() -> str:
+    return lib().fsdp_last_error().decode()
+
+
+def fsdp_release_cache() -> None:
+    lib().fsdp_release_cache()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise FSDPError(fn, rc, fsdp_last_error())
+
+
+class _BucketArg:
+    """fsdp_bucket_t for a list of shapes (keeps its arrays alive)."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], shard_dim: int = 0):
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        P = len(self.shapes)
+        flat = [d for s in self.shapes for d in s]
+        self._ndim = (c_int32 * max(P, 1))(*[len(s) for s in self.shapes])
+        self._shape = (c_int64 * max(len(flat), 1))(*flat)
+        self.struct = _Bucket(P, self._ndim, self._shape, shard_dim)
+        self.ref = ctypes.byref(self.struct)
+
+
+class Layout(NamedTuple):
+    I: int                      # elements of one rank slice
+    padded: List[int]           # padded elements of each parameter
+    in_off: List[int]           # offset of each parameter in a slice
+    row_off: List[List[int]]    # [i][s] first row held by shard rank s
+    row_len: List[List[int]]    # [i][s] rows held by shard rank s
+
+
+def fsdp_bucket_layout(shapes: Sequence[Sequence[int]], shard_size: int, shard_dim: int = 0) -> Layout:
+    b = _BucketArg(shapes, shard_dim)
+    P, S = len(b.shapes), int(shard_size)
+    n = max(P, 1)
+    I = c_int64()
+    padded, in_off = (c_int64 * n)(), (c_int64 * n)()
+    ro, rl = (c_int64 * max(P * S, 1))(), (c_int64 * max(P * S, 1))()
+    _check("fsdp_bucket_layout", lib().fsdp_bucket_layout(b.ref, S, ctypes.byref(I), padded, in_off, ro, rl))
+    return Layout(I.value, list(padded[:P]), list(in_off[:P]),
+                  [list(ro[i * S:(i + 1) * S]) for i in range(P)],
+                  [list(rl[i * S:(i + 1) * S]) for i in range(P)])
+
+
+def fsdp_fused_layout(seg_numel: Sequence[int], elem_bytes: int = 4) -> Tuple[List[int], int]:
+    n = len(seg_numel)
+    sizes = (c_int64 * max(n, 1))(*[int(v) for v in seg_numel])
+    offs, F = (c_int64 * max(n, 1))(), c_int64()
+    _check("fsdp_fused_layout", lib().fsdp_fused_layout(n, sizes, int(elem_bytes), offs, ctypes.byref(F)))
+    return list(offs[:n]), F.value
+
+
+def fsdp_group_ranks(rank_size: int, shard_size: int) -> Tuple[List[List[int]], List[List[int]]]:
+    R, S = int(rank_size), int(shard_size)
+    nrs, nar = c_int32(), c_int32()
+    rs, ar = (c_int32 * max(R, 1))(), (c_int32 * max(R, 1))()
+    _check("fsdp_group_ranks", lib().fsdp_group_ranks(R, S, ctypes.byref(nrs), rs, ctypes.byref(nar), ar))
+    D = R // S
+    return ([list(rs[d * S:(d + 1) * S]) for d in range(nrs.value)],
+            [list(ar[s * D:(s + 1) * D]) for s in range(nar.value)])
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def _dev(t: torch.Tensor, what: str, numel: int, dtype: Optional[torch.dtype] = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{what}: {t.numel()} elements, expected {numel}")
+    return t.data_ptr() if numel else 0
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    return (c_void_p * max(len(ptrs), 1))(*[p or None for p in ptrs])
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return _DTYPES[dtype]
+
+
+def _stream(stream) -> c_void_p:
+    if stream is None:
+        return c_void_p(torch.cuda.current_stream().cuda_stream or None)
+    if isinstance(stream, torch.cuda.Stream):
+        return c_void_p(stream.cuda_stream or None)
+    return c_void_p(int(stream) or None)
+
+
+class _Call:
+    """A marshalled C call; calling it issues the call on a stream."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = args
+        self._keep = keep  # ctypes objects and tensors the pointers refer to
+
+    def __call__(self, stream=None) -> None:
+        _check(self.name, self.fn(*self.args, _stream(stream)))
+
+
+def _prep_ag_copy_in(shapes, shard_size, shards, ag):
+    b = _BucketArg(shapes)
+    lay = fsdp_bucket_layout(b.shapes, shard_size)
+    S, P = int(shard_size), len(b.shapes)
+    if len(shards) != S * P:
+        raise ValueError(f"shards: {len(shards)} tensors, expected S*P = {S * P} (rank-major)")
+    dt = ag.dtype
+    ptrs = [_dev(shards[s * P + i], f"shards[{s * P + i}]",
+                 lay.row_len[i][s] * _numel(b.shapes[i][1:]), dt)
+            for s in range(S) for i in range(P)]
+    arr = _ptr_array(ptrs)
+    agp = _dev(ag, "ag", S * lay.I)
+    return _Call("fsdp_ag_copy_in", (b.ref, S, _dtype_code(dt), arr, c_void_p(agp or None)),
+                 (b, arr, tuple(shards), ag))
+
+
+def _prep_ag_copy_out(shapes, shard_size, ag, full):
+    b = _BucketArg(shapes)
+    lay = fsdp_bucket_layout(b.shapes, shard_size)
+    S, P = int(shard_size), len(b.shapes)
+    if len(full) != P:
+        raise ValueError(f"full: {len(full)} tensors, expected {P}")
+    dt = ag.dtype
+    agp = _dev(ag, "ag", S * lay.I)
+    arr = _ptr_array([_dev(full[i], f"full[{i}]", _numel(b.shapes[i]), dt) for i in range(P)])
+    return _Call("fsdp_ag_copy_out", (b.ref, S, _dtype_code(dt), c_void_p(agp or None), arr),
+                 (b, arr, tuple(full), ag))
+
+
+def _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in):
+    b = _BucketArg(shapes)
+    lay = fsdp_bucket_layout(b.shapes, shard_size)
+    R, S, P = int(rank_size), int(shard_size), len(b.shapes)
+    if len(grads) != R * P or len(rs_in) != R:
+        raise ValueError(f"grads: {len(grads)} (expected R*P = {R * P}), rs_in: {len(rs_in)} (expected {R})")
+    dt = rs_in[0].dtype if R else torch.float32
+    garr = _ptr_array([_dev(grads[g * P + i], f"grads[{g * P + i}]", _numel(b.shapes[i]), dt)
+                       for g in range(R) for i in range(P)])
+    rarr = _ptr_array([_dev(rs_in[g], f"rs_in[{g}]", S * lay.I, dt) for g in range(R)])
+    return _Call("fsdp_rs_copy_in", (b.ref, R, S, _dtype_code(dt), garr, rarr),
+                 (b, garr, rarr, tuple(grads), tuple(rs_in)))
+
+
+def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out):
+    b = _BucketArg(shapes)
+    lay = fsdp_bucket_layout(b.shapes, shard_size)
+    R, S = int(rank_size), int(shard_size)
+    if len(rs_in) != R or len(rs_out) != R:
+        raise ValueError(f"rs_in / rs_out: {len(rs_in)} / {len(rs_out)} tensors, expected {R}")
+    iarr = _ptr_array([_dev(rs_in[g], f"rs_in[{g}]", S * lay.I, torch.float32) for g in range(R)])
+    oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, torch.float32) for g in range(R)])
+    return _Call("fsdp_rs_reduce", (b.ref, R, S, int(dp_size), _OPS[op], 0, iarr, oarr),
+                 (b, iarr, oarr, tuple(rs_in), tuple(rs_out)))
+
+
+def _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused):
+    n = len(seg_numel)
+    sizes = (c_int64 * max(n, 1))(*[int(v) for v in seg_numel])
+    _, F = fsdp_fused_layout(seg_numel, 4)
+    R = int(rank_size)
+    if len(fused) != R:
+        raise ValueError(f"fused: {len(fused)} tensors, expected {R}")
+    arr = _ptr_array([_dev(fused[g], f"fused[{g}]", F, torch.float32) for g in range(R)])
+    return _Call("fsdp_fused_ar", (n, sizes, R, int(shard_size), int(dp_size), _OPS[op], 0, arr),
+                 (sizes, arr, tuple(fused)))
+
+
+_PREP = {
+    "fsdp_ag_copy_in": _prep_ag_copy_in,
+    "fsdp_ag_copy_out": _prep_ag_copy_out,
+    "fsdp_rs_copy_in": _prep_rs_copy_in,
+    "fsdp_rs_reduce": _prep_rs_reduce,
+    "fsdp_fused_ar": _prep_fused_ar,
+}
+
+
+def prepare(fn, *args) -> _Call:
+    """Check and marshal the arguments of device entry point `fn` (a name
+    or one of this module's functions) once; the result issues the call."""
+    name = fn if isinstance(fn, str) else fn.__name__
+    return _PREP[name](*args)
+
+
+def fsdp_ag_copy_in(shapes, shard_size: int, shards: Sequence[torch.Tensor], ag: torch.Tensor,
+                    stream=None) -> None:
+    """Pack shards[s*P + i] into rank slice s of ag (S*I elements)."""
+    _prep_ag_copy_in(shapes, shard_size, shards, ag)(stream)
+
+
+def fsdp_ag_copy_out(shapes, shard_size: int, ag: torch.Tensor, full: Sequence[torch.Tensor],
+                     stream=None) -> None:
+    """Unpack the gathered ag into the full parameters full[i]."""
+    _prep_ag_copy_out(shapes, shard_size, ag, full)(stream)
+
+
+def fsdp_rs_copy_in(shapes, rank_size: int, shard_size: int, grads: Sequence[torch.Tensor],
+                    rs_in: Sequence[torch.Tensor], stream=None) -> None:
+    """Chunk grads[g*P + i] into the padded RS inputs rs_in[g] (S*I elements)."""
+    _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in)(stream)
+
+
+def fsdp_rs_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, op: str,
+                   rs_in: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None) -> None:
+    """Reduce-scatter within every shard group into rs_out[g] (I fp32 elements)."""
+    _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out)(stream)
+
+
+def fsdp_fused_ar(seg_numel, rank_size: int, shard_size: int, dp_size: int, op: str,
+                  fused: Sequence[torch.Tensor], stream=None) -> None:
+    """All-reduce the fused buffers fused[g] in place within every replicate group."""
+    _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused)(stream)

@@ -1,0 +1,585 @@
+// Host side of the FSDP/HSDP flat-buffer library: argument validation, the
+// dim-0 layout planner, descriptor-table construction and caching, and the
+// extern "C" entry points declared in include/fsdp_flat.h.
+//
+// Layout rules implemented here (cited by page title and section):
+//   FSDP dim-0 non-uniform sharding RFC (mindspore/hyper-parallel issue
+//   319) 6.4: chunk = ceil(N0 / S); rank s holds rows starting at
+//   min(s*chunk, N0), at most chunk of them, clamped to N0; the
+//   communication storage of every rank has chunk rows (zero padded at the
+//   tail); fused offsets advance by the padded element count.
+//   Hyper communication-overlap PR #758 write-up (mindspore/hyper-parallel
+//   issue 184) 2.1: the AG send buffer is this rank's slice of the AG
+//   output; RS outputs are written as views into a 512-byte-aligned fused
+//   buffer that one all-reduce covers.
+//   FullyShard multi-dimensional RFC (yide12/hyper-parallel issue 1) 2.2.2
+//   and 2.2.5: dp_size = rank_size / shard_size; RS when shard_size > 1,
+//   AR when dp_size > 1.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "fsdp_flat.h"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return FSDP_OK;
+}
+
+constexpr int64_t kMaxBytes = int64_t(1) << 60;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out) && *out <= kMaxBytes;
+}
+bool add_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_add_overflow(a, b, out) && *out <= kMaxBytes;
+}
+
+struct Layout {
+  int32_t P = 0;
+  int32_t S = 1;
+  int64_t I = 0;
+  std::vector<int64_t> chunk, inner, padded, in_off, numel;
+  std::vector<int64_t> row_off, row_len;  // [i*S + s]
+};
+
+int make_layout(const fsdp_bucket_t* b, int32_t S, Layout* L) {
+  if (!b) return fail(FSDP_EINVAL, "bucket is NULL");
+  if (b->shard_dim != 0)
+    return fail(FSDP_ENOTIMPL, "shard_dim %d: only dim-0 sharding is implemented", b->shard_dim);
+  if (S < 1) return fail(FSDP_EINVAL, "shard_size %d < 1", S);
+  if (b->n_params < 0) return fail(FSDP_EINVAL, "n_params %d < 0", b->n_params);
+  if (b->n_params > 0 && (!b->ndim || !b->shape))
+    return fail(FSDP_EINVAL, "ndim / shape arrays are NULL");
+  L->P = b->n_params;
+  L->S = S;
+  L->chunk.resize(L->P);
+  L->inner.resize(L->P);
+  L->padded.resize(L->P);
+  L->in_off.resize(L->P);
+  L->numel.resize(L->P);
+  L->row_off.resize((size_t)L->P * S);
+  L->row_len.resize((size_t)L->P * S);
+  int64_t off = 0;
+  size_t pos = 0;
+  for (int32_t i = 0; i < L->P; ++i) {
+    const int32_t nd = b->ndim[i];
+    if (nd < 1) return fail(FSDP_EINVAL, "param %d: ndim %d < 1 (a 0-d tensor has no dim 0)", i, nd);
+    const int64_t* sh = b->shape + pos;
+    pos += (size_t)nd;
+    int64_t inner = 1;
+    for (int32_t d = 0; d < nd; ++d) {
+      if (sh[d] < 0) return fail(FSDP_EINVAL, "param %d: negative dim %lld", i, (long long)sh[d]);
+      if (d > 0 && !mul_ok(inner, sh[d], &inner)) return fail(FSDP_EINVAL, "param %d: size overflow", i);
+    }
+    const int64_t n0 = sh[0];
+    const int64_t chunk = n0 / S + (n0 % S != 0);
+    int64_t padded, numel;
+    if (!mul_ok(chunk, inner, &padded) || !mul_ok(n0, inner, &numel))
+      return fail(FSDP_EINVAL, "param %d: size overflow", i);
+    L->chunk[i] = chunk;
+    L->inner[i] = inner;
+    L->padded[i] = padded;
+    L->numel[i] = numel;
+    L->in_off[i] = off;
+    for (int32_t s = 0; s < S; ++s) {
+      const int64_t start = std::min<int64_t>((int64_t)s * chunk, n0);
+      L->row_off[(size_t)i * S + s] = start;
+      L->row_len[(size_t)i * S + s] = std::min<int64_t>(chunk, n0 - start);
+    }
+    if (!add_ok(off, padded, &off)) return fail(FSDP_EINVAL, "bucket size overflow");
+  }
+  L->I = off;
+  int64_t tmp;
+  if (!mul_ok(L->I, S, &tmp) || !mul_ok(tmp, 4, &tmp)) return fail(FSDP_EINVAL, "bucket size overflow");
+  return FSDP_OK;
+}
+
+int elem_size(int32_t dtype) {
+  switch (dtype) {
+    case FSDP_F32: return 4;
+    case FSDP_BF16: return 2;
+    case FSDP_F16: return 2;
+    default: return 0;
+  }
+}
+
+int check_groups(int32_t R, int32_t S) {
+  if (R < 1 || S < 1) return fail(FSDP_EINVAL, "rank_size %d / shard_size %d must be >= 1", R, S);
+  if (R % S != 0) return fail(FSDP_EINVAL, "rank_size %d is not a multiple of shard_size %d", R, S);
+  return FSDP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// pointer checks
+// ---------------------------------------------------------------------------
+
+struct Span {
+  uint64_t a, b;  // [a, b)
+  int id;
+};
+
+int check_ptr(const void* p, int64_t nbytes, uint64_t align, const char* what, long idx) {
+  if (nbytes == 0) return FSDP_OK;
+  if (!p) return fail(FSDP_EINVAL, "%s[%ld] is NULL but holds %lld bytes", what, idx, (long long)nbytes);
+  if ((uint64_t)p % align)
+    return fail(FSDP_EALIGN, "%s[%ld] = %p is not %llu-byte aligned", what, idx, p, (unsigned long long)align);
+  return FSDP_OK;
+}
+
+// Outputs must be pairwise disjoint and disjoint from every input.
+int check_overlap(std::vector<Span> outs, const std::vector<Span>& ins) {
+  outs.erase(std::remove_if(outs.begin(), outs.end(), [](const Span& s) { return s.a == s.b; }), outs.end());
+  std::sort(outs.begin(), outs.end(), [](const Span& x, const Span& y) { return x.a < y.a; });
+  for (size_t k = 1; k < outs.size(); ++k)
+    if (outs[k].a < outs[k - 1].b)
+      return fail(FSDP_EOVERLAP, "output buffers %d and %d overlap", outs[k - 1].id, outs[k].id);
+  for (const Span& in : ins) {
+    if (in.a == in.b) continue;
+    // first output whose end is beyond in.a
+    auto it = std::upper_bound(outs.begin(), outs.end(), in.a,
+                               [](uint64_t v, const Span& s) { return v < s.b; });
+    if (it != outs.end() && it->a < in.b)
+      return fail(FSDP_EOVERLAP, "input buffer %d overlaps output buffer %d", in.id, it->id);
+  }
+  return FSDP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tuning (read once; the defaults are the measured best on MI355X)
+// ---------------------------------------------------------------------------
+
+struct Tuning {
+  uint32_t copy_shift = 15;    // 32 KiB of destination per chunk
+  uint32_t reduce_shift = 14;  // 16 KiB of destination per chunk
+  uint32_t max_grid = 1u << 20;
+};
+
+const Tuning& tuning() {
+  static Tuning t = [] {
+    Tuning x;
+    if (const char* e = getenv("FSDP_COPY_CHUNK_SHIFT")) x.copy_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
+    if (const char* e = getenv("FSDP_REDUCE_CHUNK_SHIFT")) x.reduce_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
+    if (const char* e = getenv("FSDP_MAX_GRID")) x.max_grid = (uint32_t)std::max(1, atoi(e));
+    return x;
+  }();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// descriptor-table cache (device memory, keyed by content and device)
+// ---------------------------------------------------------------------------
+
+struct Entry {
+  int device;
+  std::vector<uint8_t> host;  // the table; also the key
+  uint64_t hash;
+  void* dev = nullptr;
+  hipEvent_t ready = nullptr;  // recorded after the upload
+  hipStream_t upload_stream = nullptr;
+  bool ready_done = false;
+};
+
+constexpr size_t kMaxEntries = 128;
+
+std::mutex g_mu;
+std::list<Entry> g_lru;  // front = most recent
+std::unordered_map<uint64_t, std::vector<std::list<Entry>::iterator>> g_index;
+
+uint64_t fnv1a(const uint8_t* p, size_t n, uint64_t h) {
+  for (size_t k = 0; k < n; ++k) h = (h ^ p[k]) * 1099511628211ull;
+  return h;
+}
+
+uint64_t table_hash(const std::vector<uint8_t>& t, int device) {
+  // words at a time for speed; a full compare settles collisions
+  uint64_t h = 1469598103934665603ull ^ (uint64_t)device;
+  const size_t nw = t.size() / 8;
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(t.data());
+  for (size_t k = 0; k < nw; ++k) {
+    h ^= w[k];
+    h *= 0x9E3779B97F4A7C15ull;
+    h ^= h >> 29;
+  }
+  return fnv1a(t.data() + nw * 8, t.size() - nw * 8, h);
+}
+
+void drop_entry(std::list<Entry>::iterator it) {
+  auto& v = g_index[it->hash];
+  v.erase(std::remove(v.begin(), v.end(), it), v.end());
+  if (v.empty()) g_index.erase(it->hash);
+  if (it->ready) (void)hipEventDestroy(it->ready);
+  if (it->dev) (void)hipFree(it->dev);
+  g_lru.erase(it);
+}
+
+// Device copy of `table`, made visible to `stream` before anything it
+// enqueues next.  Returns FSDP_OK and sets *dev.
+int get_table(std::vector<uint8_t>&& table, hipStream_t stream, void** dev) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(FSDP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const uint64_t h = table_hash(table, device);
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto found = g_index.find(h);
+  if (found != g_index.end()) {
+    for (auto it : found->second) {
+      if (it->device == device && it->host == table) {
+        if (!it->ready_done && it->upload_stream != stream) {
+          if (hipEventQuery(it->ready) == hipSuccess) {
+            it->ready_done = true;
+          } else if ((e = hipStreamWaitEvent(stream, it->ready, 0)) != hipSuccess) {
+            return fail(FSDP_EHIP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+          }
+        }
+        g_lru.splice(g_lru.begin(), g_lru, it);
+        *dev = it->dev;
+        return FSDP_OK;
+      }
+    }
+  }
+  if (g_lru.size() >= kMaxEntries) {
+    // tables still in use by queued kernels must outlive them
+    (void)hipDeviceSynchronize();
+    while (g_lru.size() >= kMaxEntries / 2) drop_entry(std::prev(g_lru.end()));
+  }
+  Entry ent;
+  ent.device = device;
+  ent.hash = h;
+  ent.host = std::move(table);
+  if ((e = hipMalloc(&ent.dev, ent.host.size())) != hipSuccess)
+    return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", ent.host.size(), hipGetErrorString(e));
+  if ((e = hipMemcpyAsync(ent.dev, ent.host.data(), ent.host.size(), hipMemcpyHostToDevice, stream)) != hipSuccess) {
+    (void)hipFree(ent.dev);
+    return fail(FSDP_EHIP, "hipMemcpyAsync of a descriptor table: %s", hipGetErrorString(e));
+  }
+  if ((e = hipEventCreateWithFlags(&ent.ready, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventRecord(ent.ready, stream)) != hipSuccess) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(ent.dev);
+    return fail(FSDP_EHIP, "descriptor table event: %s", hipGetErrorString(e));
+  }
+  ent.upload_stream = stream;
+  g_lru.push_front(std::move(ent));
+  g_index[h].push_back(g_lru.begin());
+  *dev = g_lru.front().dev;
+  return FSDP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// table builders
+// ---------------------------------------------------------------------------
+
+template <typename T>
+void append(std::vector<uint8_t>& t, const T* p, size_t n) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
+  t.insert(t.end(), b, b + n * sizeof(T));
+}
+
+// Launch the segmented copy over `segs` (empty segments already dropped).
+int run_copy(std::vector<fsdp::CopySeg>& segs, int es, hipStream_t stream) {
+  if (segs.empty()) return ok();
+  const Tuning& tu = tuning();
+  std::vector<uint64_t> begin(segs.size());
+  uint64_t n = 0;
+  for (size_t k = 0; k < segs.size(); ++k) {
+    begin[k] = n;
+    n += fsdp::chunk_count(segs[k].dst, segs[k].total_bytes, tu.copy_shift);
+  }
+  if (segs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many segments");
+  std::vector<uint8_t> table;
+  table.reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
+  append(table, begin.data(), begin.size());
+  append(table, segs.data(), segs.size());
+  void* dev = nullptr;
+  int rc = get_table(std::move(table), stream, &dev);
+  if (rc) return rc;
+  int he = fsdp_launch_seg_copy(es, dev, (uint32_t)segs.size(), n, tu.copy_shift, tu.max_grid, stream);
+  if (he != hipSuccess) return fail(FSDP_EHIP, "seg_copy launch: %s", hipGetErrorString((hipError_t)he));
+  return ok();
+}
+
+int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int avg, hipStream_t stream) {
+  if (jobs.empty()) return ok();
+  const Tuning& tu = tuning();
+  std::vector<uint64_t> begin(jobs.size());
+  uint64_t n = 0;
+  for (size_t k = 0; k < jobs.size(); ++k) {
+    begin[k] = n;
+    n += fsdp::chunk_count(ptrs[jobs[k].dst0], jobs[k].nbytes, tu.reduce_shift);
+  }
+  std::vector<uint8_t> table;
+  append(table, begin.data(), begin.size());
+  append(table, jobs.data(), jobs.size());
+  append(table, ptrs.data(), ptrs.size());
+  void* dev = nullptr;
+  int rc = get_table(std::move(table), stream, &dev);
+  if (rc) return rc;
+  int he = fsdp_launch_reduce(dev, (uint32_t)jobs.size(), n, tu.reduce_shift, tu.max_grid, avg, stream);
+  if (he != hipSuccess) return fail(FSDP_EHIP, "reduce launch: %s", hipGetErrorString((hipError_t)he));
+  return ok();
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+const char* fsdp_last_error(void) { return g_err.c_str(); }
+
+void fsdp_release_cache(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_lru.empty()) (void)hipDeviceSynchronize();
+  while (!g_lru.empty()) drop_entry(g_lru.begin());
+}
+
+int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t* slice_numel,
+                       int64_t* padded, int64_t* in_off, int64_t* row_off, int64_t* row_len) {
+  Layout L;
+  int rc = make_layout(bucket, shard_size, &L);
+  if (rc) return rc;
+  if (slice_numel) *slice_numel = L.I;
+  if (padded) std::copy(L.padded.begin(), L.padded.end(), padded);
+  if (in_off) std::copy(L.in_off.begin(), L.in_off.end(), in_off);
+  if (row_off) std::copy(L.row_off.begin(), L.row_off.end(), row_off);
+  if (row_len) std::copy(L.row_len.begin(), L.row_len.end(), row_len);
+  return ok();
+}
+
+int fsdp_fused_layout(int32_t n_seg, const int64_t* seg_numel, int32_t elem_bytes, int64_t* seg_off,
+                      int64_t* fused_numel) {
+  if (n_seg < 0) return fail(FSDP_EINVAL, "n_seg %d < 0", n_seg);
+  if (n_seg > 0 && !seg_numel) return fail(FSDP_EINVAL, "seg_numel is NULL");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(FSDP_EINVAL, "elem_bytes %d not in {2, 4}", elem_bytes);
+  const int64_t A = FSDP_FUSED_ALIGN_BYTES;
+  int64_t end = 0;
+  for (int32_t j = 0; j < n_seg; ++j) {
+    if (seg_numel[j] < 0) return fail(FSDP_EINVAL, "segment %d: negative size", j);
+    const int64_t start = (end + A - 1) / A * A;
+    int64_t nb;
+    if (!mul_ok(seg_numel[j], elem_bytes, &nb) || !add_ok(start, nb, &end))
+      return fail(FSDP_EINVAL, "fused buffer size overflow");
+    if (seg_off) seg_off[j] = start / elem_bytes;
+  }
+  if (fused_numel) *fused_numel = (end + A - 1) / A * A / elem_bytes;
+  return ok();
+}
+
+int fsdp_group_ranks(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups, int32_t* rs_ranks,
+                     int32_t* n_ar_groups, int32_t* ar_ranks) {
+  int rc = check_groups(rank_size, shard_size);
+  if (rc) return rc;
+  const int32_t S = shard_size, D = rank_size / shard_size;
+  if (n_rs_groups) *n_rs_groups = S > 1 ? D : 0;
+  if (n_ar_groups) *n_ar_groups = D > 1 ? S : 0;
+  if (rs_ranks && S > 1)
+    for (int32_t d = 0; d < D; ++d)
+      for (int32_t s = 0; s < S; ++s) rs_ranks[d * S + s] = d * S + s;
+  if (ar_ranks && D > 1)
+    for (int32_t s = 0; s < S; ++s)
+      for (int32_t d = 0; d < D; ++d) ar_ranks[s * D + d] = d * S + s;
+  return ok();
+}
+
+int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype,
+                    const void* const* shards, void* ag, void* stream) {
+  Layout L;
+  int rc = make_layout(bucket, shard_size, &L);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "dtype %d is not supported", dtype);
+  const int32_t S = L.S, P = L.P;
+  const int64_t ag_bytes = (int64_t)S * L.I * es;
+  if ((rc = check_ptr(ag, ag_bytes, es, "ag", 0))) return rc;
+  if (S * (int64_t)P > 0 && !shards) return fail(FSDP_EINVAL, "shards array is NULL");
+  std::vector<Span> ins;
+  std::vector<fsdp::CopySeg> segs;
+  segs.reserve((size_t)S * P);
+  for (int32_t s = 0; s < S; ++s) {
+    for (int32_t i = 0; i < P; ++i) {
+      const int64_t nb = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
+      const void* p = shards[(size_t)s * P + i];
+      if ((rc = check_ptr(p, nb, es, "shards", (long)s * P + i))) return rc;
+      ins.push_back({(uint64_t)p, (uint64_t)p + (uint64_t)nb, s * P + i});
+      const int64_t total = L.padded[i] * es;
+      if (total == 0) continue;
+      segs.push_back({nb ? (uint64_t)p : 0, (uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es),
+                      (uint64_t)nb, (uint64_t)total});
+    }
+  }
+  if ((rc = check_overlap({{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}, ins))) return rc;
+  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+}
+
+int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
+                     void* const* full, void* stream) {
+  Layout L;
+  int rc = make_layout(bucket, shard_size, &L);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "dtype %d is not supported", dtype);
+  const int32_t S = L.S, P = L.P;
+  const int64_t ag_bytes = (int64_t)S * L.I * es;
+  if ((rc = check_ptr(ag, ag_bytes, es, "ag", 0))) return rc;
+  if (P > 0 && !full) return fail(FSDP_EINVAL, "full array is NULL");
+  std::vector<Span> outs;
+  std::vector<fsdp::CopySeg> segs;
+  for (int32_t i = 0; i < P; ++i) {
+    const int64_t nb = L.numel[i] * es;
+    if ((rc = check_ptr(full[i], nb, es, "full", i))) return rc;
+    outs.push_back({(uint64_t)full[i], (uint64_t)full[i] + (uint64_t)nb, i});
+    for (int32_t s = 0; s < S; ++s) {
+      const int64_t n = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
+      if (n == 0) continue;
+      segs.push_back({(uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es),
+                      (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es),
+                      (uint64_t)n, (uint64_t)n});
+    }
+  }
+  if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
+  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+}
+
+int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
+                    const void* const* grads, void* const* rs_in, void* stream) {
+  int rc = check_groups(rank_size, shard_size);
+  if (rc) return rc;
+  Layout L;
+  if ((rc = make_layout(bucket, shard_size, &L))) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "dtype %d is not supported", dtype);
+  const int32_t R = rank_size, S = L.S, P = L.P;
+  const int64_t buf_bytes = (int64_t)S * L.I * es;
+  if (!rs_in) return fail(FSDP_EINVAL, "rs_in array is NULL");
+  if ((int64_t)R * P > 0 && !grads) return fail(FSDP_EINVAL, "grads array is NULL");
+  std::vector<Span> outs, ins;
+  std::vector<fsdp::CopySeg> segs;
+  segs.reserve((size_t)R * S * P);
+  for (int32_t g = 0; g < R; ++g) {
+    if ((rc = check_ptr(rs_in[g], buf_bytes, es, "rs_in", g))) return rc;
+    outs.push_back({(uint64_t)rs_in[g], (uint64_t)rs_in[g] + (uint64_t)buf_bytes, g});
+    for (int32_t i = 0; i < P; ++i) {
+      const void* gp = grads[(size_t)g * P + i];
+      if ((rc = check_ptr(gp, L.numel[i] * es, es, "grads", (long)g * P + i))) return rc;
+      ins.push_back({(uint64_t)gp, (uint64_t)gp + (uint64_t)(L.numel[i] * es), g * P + i});
+    }
+  }
+  for (int32_t g = 0; g < R; ++g) {
+    for (int32_t s = 0; s < S; ++s) {
+      for (int32_t i = 0; i < P; ++i) {
+        const int64_t total = L.padded[i] * es;
+        if (total == 0) continue;
+        const int64_t nb = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
+        const uint64_t src = (uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
+        segs.push_back({nb ? src : 0, (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es),
+                        (uint64_t)nb, (uint64_t)total});
+      }
+    }
+  }
+  if ((rc = check_overlap(outs, ins))) return rc;
+  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+}
+
+int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+                   int32_t op, int32_t dtype, const void* const* rs_in, void* const* rs_out, void* stream) {
+  int rc = check_groups(rank_size, shard_size);
+  if (rc) return rc;
+  if (dp_size != rank_size / shard_size)
+    return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
+  if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
+  if (dtype != FSDP_F32) return fail(FSDP_ENOTIMPL, "rs_reduce takes fp32 only (dtype %d)", dtype);
+  Layout L;
+  if ((rc = make_layout(bucket, shard_size, &L))) return rc;
+  const int32_t R = rank_size, S = shard_size;
+  const int64_t in_bytes = (int64_t)S * L.I * 4, out_bytes = L.I * 4;
+  if (!rs_in || !rs_out) return fail(FSDP_EINVAL, "rs_in / rs_out array is NULL");
+  std::vector<Span> outs, ins;
+  for (int32_t g = 0; g < R; ++g) {
+    if ((rc = check_ptr(rs_in[g], in_bytes, 4, "rs_in", g))) return rc;
+    if ((rc = check_ptr(rs_out[g], out_bytes, 4, "rs_out", g))) return rc;
+    ins.push_back({(uint64_t)rs_in[g], (uint64_t)rs_in[g] + (uint64_t)in_bytes, g});
+    outs.push_back({(uint64_t)rs_out[g], (uint64_t)rs_out[g] + (uint64_t)out_bytes, g});
+  }
+  if ((rc = check_overlap(outs, ins))) return rc;
+  if (out_bytes == 0) return ok();
+  std::vector<fsdp::RedJob> jobs;
+  std::vector<uint64_t> ptrs;
+  for (int32_t g = 0; g < R; ++g) {
+    const int32_t d = g / S, s = g % S;
+    fsdp::RedJob jb;
+    jb.nbytes = (uint64_t)out_bytes;
+    jb.src0 = (uint32_t)ptrs.size();
+    jb.nsrc = (uint32_t)S;
+    for (int32_t t = 0; t < S; ++t) ptrs.push_back((uint64_t)rs_in[d * S + t] + (uint64_t)(s * out_bytes));
+    jb.dst0 = (uint32_t)ptrs.size();
+    jb.ndst = 1;
+    ptrs.push_back((uint64_t)rs_out[g]);
+    jobs.push_back(jb);
+  }
+  return run_reduce(jobs, ptrs, op == FSDP_AVG, static_cast<hipStream_t>(stream));
+}
+
+int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
+                  int32_t dp_size, int32_t op, int32_t dtype, void* const* fused, void* stream) {
+  int rc = check_groups(rank_size, shard_size);
+  if (rc) return rc;
+  if (dp_size != rank_size / shard_size)
+    return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
+  if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
+  if (dtype != FSDP_F32) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32 only (dtype %d)", dtype);
+  int64_t F = 0;
+  if ((rc = fsdp_fused_layout(n_seg, seg_numel, 4, nullptr, &F))) return rc;
+  const int32_t R = rank_size, S = shard_size, D = dp_size;
+  const int64_t nbytes = F * 4;
+  if (!fused) return fail(FSDP_EINVAL, "fused array is NULL");
+  std::vector<Span> outs;
+  for (int32_t g = 0; g < R; ++g) {
+    if ((rc = check_ptr(fused[g], nbytes, FSDP_FUSED_ALIGN_BYTES, "fused", g))) return rc;
+    outs.push_back({(uint64_t)fused[g], (uint64_t)fused[g] + (uint64_t)nbytes, g});
+  }
+  if ((rc = check_overlap(outs, {}))) return rc;
+  if (nbytes == 0 || D == 1) return ok();  // a group of one: the identity
+  std::vector<fsdp::RedJob> jobs;
+  std::vector<uint64_t> ptrs;
+  for (int32_t s = 0; s < S; ++s) {
+    fsdp::RedJob jb;
+    jb.nbytes = (uint64_t)nbytes;
+    jb.src0 = (uint32_t)ptrs.size();
+    jb.nsrc = (uint32_t)D;
+    for (int32_t d = 0; d < D; ++d) ptrs.push_back((uint64_t)fused[d * S + s]);
+    jb.dst0 = jb.src0;  // in place: every replica receives the result
+    jb.ndst = (uint32_t)D;
+    jobs.push_back(jb);
+  }
+  return run_reduce(jobs, ptrs, op == FSDP_AVG, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

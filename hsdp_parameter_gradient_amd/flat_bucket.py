@@ -1,0 +1,100 @@
+"""One FSDP/HSDP bucket on one GPU: its communication buffers and its steps.
+
+FlatBucket owns (through torch, which supplies device memory) the buffers
+of one bucket of parameters with all R simulated ranks resident in HBM:
+
+  ag        [S*I]   AG buffer; slice s is shard rank s's send buffer
+  full[i]           the full parameters written by AG copy-out
+  rs_in[g]  [S*I]   rank g's padded RS input (fp32)
+  fused[g]  [F]     rank g's 512-byte-aligned fused AR buffer; the RS output
+                    of rank g is the view fused[g][off : off + I]
+                    (zero-copy, PR #758 write-up of the Hyper
+                    communication-overlap scheme, section 2.1)
+
+and runs the hot path with one library call per step.  Which gradient
+collectives run follows the decision matrix of the FullyShard
+multi-dimensional RFC (sections 2.2.2 and 2.2.5): RS when shard_size > 1,
+AR when dp_size > 1.  The shard views (AG inputs) and the per-rank full
+gradients (RS copy-in inputs) belong to the caller.
+"""
+
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _binding as B
+
+
+class FlatBucket:
+    def __init__(self, shapes: Sequence[Sequence[int]], rank_size: int, shard_size: int,
+                 param_dtype: torch.dtype = torch.bfloat16, op: str = B.AVG,
+                 device: str = "cuda", fused_segments: Optional[Sequence[int]] = None,
+                 fused_index: int = 0):
+        """fused_segments: sizes of the segments of the fused buffer (default:
+        this bucket's RS output alone); fused_index: which one is this
+        bucket's."""
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.R, self.S = int(rank_size), int(shard_size)
+        rs, ar = B.fsdp_group_ranks(self.R, self.S)
+        if not rs:
+            raise ValueError("shard_size 1 has no AG / RS buffers (pure-TP compatible path): "
+                             "call fsdp_fused_ar on the gradients' fused buffers")
+        self.D = self.R // self.S
+        self.do_rs, self.do_ar = bool(rs), bool(ar)
+        self.op = op
+        self.param_dtype = param_dtype
+        self.layout = B.fsdp_bucket_layout(self.shapes, self.S)
+        I = self.layout.I
+        self.seg_numel = list(fused_segments) if fused_segments is not None else [I]
+        offs, self.F = B.fsdp_fused_layout(self.seg_numel, 4)
+        self.fused_off = offs[fused_index]
+        if self.seg_numel[fused_index] != I:
+            raise ValueError("the bucket's fused segment must hold I elements")
+        dev = torch.device(device)
+        self.ag = torch.empty(self.S * I, dtype=param_dtype, device=dev)
+        self.full = [torch.empty(s, dtype=param_dtype, device=dev) for s in self.shapes]
+        self.rs_in = [torch.empty(self.S * I, dtype=torch.float32, device=dev) for _ in range(self.R)]
+        # fused buffers are fully defined (gaps zero) before the first RS writes
+        # its views; torch's allocator returns 512-byte-aligned storage.
+        self.fused = [torch.zeros(self.F, dtype=torch.float32, device=dev) for _ in range(self.R)]
+        self.rs_out = [f[self.fused_off:self.fused_off + I] for f in self.fused]
+        self._calls = None
+
+    # -- the caller's inputs ------------------------------------------------
+    def shard_views(self, params: Sequence[torch.Tensor]) -> List[torch.Tensor]:
+        """Rank-major shard views [s*P + i] of full parameters (rows per the
+        dim-0 chunk rule)."""
+        out = []
+        for s in range(self.S):
+            for i, x in enumerate(params):
+                a, n = self.layout.row_off[i][s], self.layout.row_len[i][s]
+                out.append(x.reshape(self.shapes[i])[a:a + n].reshape(-1))
+        return out
+
+    def bind(self, shards: Sequence[torch.Tensor], grads: Sequence[torch.Tensor]) -> "FlatBucket":
+        """Marshal the five calls once: shards [S*P] rank-major, grads [R*P]."""
+        S, R = self.S, self.R
+        self._calls = {
+            "ag_copy_in": B.prepare("fsdp_ag_copy_in", self.shapes, S, list(shards), self.ag),
+            "ag_copy_out": B.prepare("fsdp_ag_copy_out", self.shapes, S, self.ag, self.full),
+            "rs_copy_in": B.prepare("fsdp_rs_copy_in", self.shapes, R, S, list(grads), self.rs_in),
+            "rs_reduce": B.prepare("fsdp_rs_reduce", self.shapes, R, S, self.D, self.op, self.rs_in, self.rs_out),
+            "fused_ar": B.prepare("fsdp_fused_ar", self.seg_numel, R, S, self.D, self.op, self.fused),
+        }
+        return self
+
+    def steps(self) -> List[str]:
+        """The steps one pass runs, in order (forward AG, then backward)."""
+        st = ["ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"]
+        if self.do_ar:
+            st.append("fused_ar")
+        return st
+
+    def run(self, step: str, stream=None) -> None:
+        self._calls[step](stream)
+
+    def step(self, stream=None) -> None:
+        for name in self.steps():
+            self._calls[name](stream)

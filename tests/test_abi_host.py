@@ -1,0 +1,188 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+The layout and group queries run on the host only, so they are compared
+with the oracle here.  Invalid arguments to the device entry points are
+rejected before any HIP call, so those error paths are exercised here too,
+with fake addresses that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsdp_flat.h")
+
+hp = pytest.importorskip("hsdp_parameter_gradient_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hp.lib_path()):
+        pytest.fail("libfsdpflat.so is not built (run __graft_entry__.build())")
+    return hp.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsdp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_ops_and_queries():
+    names = declared_functions()
+    for n in ("fsdp_ag_copy_in", "fsdp_ag_copy_out", "fsdp_rs_copy_in", "fsdp_rs_reduce",
+              "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
+              "fsdp_last_error", "fsdp_release_cache"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", hp.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(fsdp_\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(L, n)
+
+
+SHAPE_SETS = [
+    [(7, 8), (5, 3), (16,)],
+    [(3072, 1024), (1024, 1024), (4096, 1024), (1024, 4096), (1024,), (1024,)],
+    [(4097, 4096), (11009, 4096), (32001, 4096), (5, 64), (3,)],
+    [(0, 4), (1,), (2, 3, 4), (9,), (13, 1, 2)],
+    [],
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPE_SETS)
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 16])
+def test_bucket_layout_matches_oracle(L, shapes, S):
+    got = hp.fsdp_bucket_layout(shapes, S)
+    want = O.bucket_layout(shapes, S)
+    assert got.I == want.I
+    assert got.padded == want.padded
+    assert got.in_off == want.in_off
+    assert got.row_off == want.row_off
+    assert got.row_len == want.row_len
+
+
+def test_fused_layout_matches_oracle(L, golden):
+    for c in golden["fused"]:
+        assert hp.fsdp_fused_layout(c["seg_numel"], c["elem_bytes"]) == (c["offsets"], c["F"])
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        sizes = [int(v) for v in rng.integers(0, 5000, size=int(rng.integers(0, 300)))]
+        assert hp.fsdp_fused_layout(sizes, 4) == O.fused_layout(sizes, 4)
+        assert hp.fsdp_fused_layout(sizes, 2) == O.fused_layout(sizes, 2)
+
+
+def test_group_ranks_match_oracle(L, golden):
+    for R, S in [(8, 4), (8, 1), (8, 8), (1, 1), (16, 4), (6, 2), (12, 3)]:
+        rs, ar = hp.fsdp_group_ranks(R, S)
+        plan = dict((k, g) for k, g in O.grad_sync_plan(R, S))
+        assert rs == plan.get("RS", [])
+        assert ar == plan.get("AR", [])
+    for c in golden["groups"]:
+        rs, ar = hp.fsdp_group_ranks(c["rank_size"], c["shard_size"])
+        want = dict((k, g) for k, g in c["calls"])
+        assert rs == want.get("RS", []) and ar == want.get("AR", [])
+
+
+def test_query_errors(L):
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([(4, 4)], 2, shard_dim=1)
+    assert e.value.code == 2 and "dim-0" in e.value.message
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([()], 2)
+    assert e.value.code == 1
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([(4,)], 0)
+    assert e.value.code == 1
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([(-1, 2)], 2)
+    assert e.value.code == 1
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([(1 << 40, 1 << 30)], 2)
+    assert e.value.code == 1
+    with pytest.raises(hp.FSDPError):
+        hp.fsdp_group_ranks(8, 3)
+    with pytest.raises(hp.FSDPError):
+        hp.fsdp_fused_layout([4, -1])
+    with pytest.raises(hp.FSDPError):
+        hp.fsdp_fused_layout([4], 8)
+
+
+# --- device entry points: argument errors caught before any HIP call -------
+
+def _bucket(shapes, shard_dim=0):
+    from hsdp_parameter_gradient_amd._binding import _BucketArg
+    return _BucketArg(shapes, shard_dim)
+
+
+def _ptrs(vals):
+    return (ctypes.c_void_p * max(len(vals), 1))(*[v or None for v in vals])
+
+
+BASE = 1 << 40  # fake, never dereferenced
+
+
+def test_device_entry_points_reject_bad_arguments(L):
+    shapes = [(7, 8), (5, 3), (16,)]
+    S, P = 4, 3
+    lay = O.bucket_layout(shapes, S)
+    b = _bucket(shapes)
+    shards = _ptrs([BASE + 0x100000 * (k + 1) for k in range(S * P)])
+    ag = ctypes.c_void_p(BASE)
+    # shard_dim != 0
+    b1 = _bucket(shapes, shard_dim=1)
+    assert L.fsdp_ag_copy_in(b1.ref, S, 0, shards, ag, None) == 2
+    # unknown dtype
+    assert L.fsdp_ag_copy_in(b.ref, S, 7, shards, ag, None) == 2
+    # NULL output with bytes to write
+    assert L.fsdp_ag_copy_in(b.ref, S, 0, shards, None, None) == 1
+    # misaligned output
+    assert L.fsdp_ag_copy_in(b.ref, S, 0, shards, ctypes.c_void_p(BASE + 2), None) == 3
+    # a source inside the output buffer
+    bad = _ptrs([BASE + 64] + [BASE + 0x100000 * (k + 1) for k in range(1, S * P)])
+    assert L.fsdp_ag_copy_in(b.ref, S, 0, bad, ag, None) == 5
+    assert "overlap" in hp.fsdp_last_error()
+    # NULL shard pointer that should hold rows (rank 0 of param 0 holds 2 rows)
+    nul = _ptrs([0] + [BASE + 0x100000 * (k + 1) for k in range(1, S * P)])
+    assert L.fsdp_ag_copy_in(b.ref, S, 0, nul, ag, None) == 1
+    # copy-out: two full outputs overlap
+    full = _ptrs([BASE + 0x200000, BASE + 0x200000 + 8, BASE + 0x300000])
+    assert L.fsdp_ag_copy_out(b.ref, S, 0, ag, full, None) == 5
+    # rs_copy_in: rank_size not a multiple of shard_size
+    grads = _ptrs([BASE + 0x100000 * (k + 1) for k in range(6 * P)])
+    rs_in = _ptrs([BASE + 0x10000000 * (g + 1) for g in range(6)])
+    assert L.fsdp_rs_copy_in(b.ref, 6, S, 0, grads, rs_in, None) == 1
+    # rs_reduce: dp_size inconsistent, op unknown, dtype not fp32, output aliasing input
+    rs8 = _ptrs([BASE + 0x10000000 * (g + 1) for g in range(8)])
+    out8 = _ptrs([BASE + 0x1000000 * (g + 1) for g in range(8)])
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 3, 0, 0, rs8, out8, None) == 1
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 9, 0, rs8, out8, None) == 1
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 1, rs8, out8, None) == 2
+    alias = _ptrs([BASE + 0x10000000 * (g + 1) + 4 * lay.I for g in range(8)])
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 0, rs8, alias, None) == 5
+    # fused_ar: base not 512-byte aligned, dtype not fp32
+    segs = (ctypes.c_int64 * 2)(100, 3)
+    f8 = _ptrs([BASE + 0x100000 * g + 256 for g in range(8)])
+    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, f8, None) == 3
+    f8a = _ptrs([BASE + 0x100000 * g for g in range(8)])
+    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 1, f8a, None) == 2
+    ovl = _ptrs([BASE + 512 * g for g in range(8)])
+    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, ovl, None) == 5
+
+
+def test_binding_checks_buffer_sizes():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):  # host tensors are refused before any C call
+        hp.fsdp_ag_copy_in([(4,)], 1, [x], x)

@@ -1,0 +1,119 @@
+"""Full-size parity on the two big workloads, in the launch configuration the
+benchmark times (FlatBucket, inputs resident in HBM).
+
+The oracle cannot materialise these buffers quickly, so it is evaluated
+element by element (oracle/pointwise.py) at a few hundred thousand random
+positions plus every position next to a region, padding or slice edge, and
+compared bit for bit.  Properties that hold at any size are checked on the
+whole buffers: all_gather(shard(x)) == x and every padding element is 0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import bits, note, require_gpu
+from oracle import pointwise as PW
+
+hp = pytest.importorskip("hsdp_parameter_gradient_amd")
+
+pytestmark = pytest.mark.gpu
+
+N_RANDOM = 300_000
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    hp.lib()
+    yield
+    hp.fsdp_release_cache()
+    torch.cuda.empty_cache()
+
+
+def _np16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _fetcher(tensors):
+    """fetch(i, flat) -> host values (float32 or uint16 bits) of tensors[i]."""
+    def fetch(i, flat):
+        idx = torch.from_numpy(np.asarray(flat, dtype=np.int64)).cuda()
+        v = tensors[i].reshape(-1)[idx]
+        return v.cpu().numpy() if v.dtype == torch.float32 else _np16(v)
+    return fetch
+
+
+def _gpu_vals(t, pos):
+    idx = torch.from_numpy(np.asarray(pos, dtype=np.int64)).cuda()
+    return bits(t[idx])
+
+
+@pytest.mark.parametrize("wname", ["llama7b_4layer_r8_s8", "ragged_heavy_r8_s8"])
+def test_full_size_sampled(wname):
+    w = W.WORKLOADS[wname]
+    R, S, D = w.rank_size, w.shard_size, w.dp_size
+    P = len(w.param_shapes)
+    lay = O.bucket_layout(w.param_shapes, S)
+    I = lay.I
+    rng = np.random.default_rng(w.number)
+    note(f"[fullsize] {w.name}: P={P} I={I} R={R} S={S}")
+
+    params = W.params(w, device="cuda")
+    grads = W.grads(w, device="cuda")
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG)
+    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+    for step in ("ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"):
+        fb.run(step)
+    torch.cuda.synchronize()
+    np_dtype = np.float32 if w.param_dtype == torch.float32 else np.uint16
+    to_bits = (lambda a: a.view(np.int32)) if np_dtype == np.float32 else (lambda a: a.view(np.int16))
+
+    # --- AG copy-in: sampled values, and all padding is zero -------------
+    edges = PW.boundary_positions(lay)
+    pos = np.unique(np.concatenate([rng.integers(0, S * I, N_RANDOM),
+                                    (np.arange(S)[:, None] * I + edges[None, :]).reshape(-1)]))
+    want = PW.packed_values(lay, pos, _fetcher(params), np_dtype)
+    got = _gpu_vals(fb.ag, pos)
+    assert np.array_equal(got, to_bits(want)), "ag_copy_in sampled mismatch"
+    pad_nonzero = 0
+    for s in range(S):
+        for i in range(P):
+            a = s * I + lay.in_off[i] + lay.row_len[i][s] * lay.inner[i]
+            b = s * I + lay.in_off[i] + lay.padded[i]
+            if b > a:
+                pad_nonzero += int(torch.count_nonzero(fb.ag[a:b].view(torch.int16 if np_dtype == np.uint16 else torch.int32)))
+    assert pad_nonzero == 0
+
+    # --- AG copy-out: the round trip is exact on every element -----------
+    for i in range(P):
+        assert torch.equal(fb.full[i].view(torch.int16 if np_dtype == np.uint16 else torch.int32),
+                           params[i].reshape(-1).view(torch.int16 if np_dtype == np.uint16 else torch.int32)), \
+            f"ag_copy_out param {i} differs from the parameter"
+        n = fb.full[i].numel()
+        if n:
+            flat = np.unique(np.concatenate([rng.integers(0, n, 2000), [0, n - 1]]))
+            src = PW.unpacked_sources(lay, i, flat)
+            assert np.array_equal(_gpu_vals(fb.full[i], flat), _gpu_vals(fb.ag, src))
+
+    # --- RS copy-in: sampled per rank -------------------------------------
+    for g in range(R):
+        pos = np.unique(np.concatenate([rng.integers(0, S * I, N_RANDOM // R),
+                                        (np.arange(S)[:, None] * I + edges[None, :]).reshape(-1)]))
+        want = PW.packed_values(lay, pos, _fetcher(grads[g]), np.float32)
+        assert np.array_equal(_gpu_vals(fb.rs_in[g], pos), want.view(np.int32)), f"rs_copy_in rank {g}"
+
+    # --- RS reduce (AVG, then SUM): sampled, from the gradients directly ---
+    fetch_rs_in = lambda m, p: PW.packed_values(lay, p, _fetcher(grads[m]), np.float32)  # noqa: E731
+    for op in (O.AVG, O.SUM):
+        if op == O.SUM:
+            hp.fsdp_rs_reduce(w.param_shapes, R, S, D, op, fb.rs_in, fb.rs_out)
+            torch.cuda.synchronize()
+        for g in range(R):
+            k = np.unique(np.concatenate([rng.integers(0, I, N_RANDOM // R), edges]))
+            want = PW.rs_reduce_values(I, R, S, op, g, k, fetch_rs_in)
+            assert np.array_equal(_gpu_vals(fb.rs_out[g], k), want.view(np.int32)), f"rs_reduce {op} rank {g}"
+    del fb, params, grads
+    torch.cuda.empty_cache()

@@ -1,0 +1,328 @@
+"""GPU parity: every device entry point against the CPU oracle, bit for bit.
+
+Sizes here are ones the oracle finishes in seconds while still spanning
+many 16-32 KiB work chunks with ragged tails (and, for the HSDP block,
+the full benchmark size).  Outputs live inside guard-banded, NaN-filled
+buffers (tests/gpu_util.py), so writes outside a buffer and skipped
+elements are both caught.  Copies are compared as bit patterns; the fp32
+reductions too, because the kernels add in the same ascending rank order
+as the oracle (max relative error 0, inside the 1e-6 bound).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import Guarded, bits, first_mismatch, note, np_bits, require_gpu, to_oracle
+
+hp = pytest.importorskip("hsdp_parameter_gradient_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    hp.lib()  # raises if the library is not built
+    yield
+    hp.fsdp_release_cache()
+
+
+def _numel(shape):
+    n = 1
+    for d in shape:
+        n *= d
+    return n
+
+
+def make_shards(dparams, lay, dtype, offsets=None):
+    """Rank-major shards [s*P + i]: views of the full parameters, or (with
+    offsets) copies in their own guard-banded buffers at those element
+    offsets, to vary the source alignment."""
+    S, P = lay.S, len(lay.shapes)
+    out, keep = [], []
+    for s in range(S):
+        for i in range(P):
+            a, n = lay.row_off[i][s], lay.row_len[i][s]
+            v = dparams[i].reshape(lay.shapes[i])[a:a + n].reshape(-1)
+            if offsets is not None:
+                g = Guarded(v.numel(), dtype, offsets[(s * P + i) % len(offsets)])
+                g.t.copy_(v)
+                keep.append(g)
+                v = g.t
+            out.append(v)
+    return out, keep
+
+
+def run_copy_and_rs(name, shapes, R, S, params, grads, ops=(O.SUM, O.AVG),
+                    shard_offsets=None, out_offset=0):
+    note(f"[parity] {name}: R={R} S={S} P={len(shapes)} dtype={params[0].dtype if params else None} "
+         f"shard_offsets={shard_offsets} out_offset={out_offset}")
+    lay = O.bucket_layout(shapes, S)
+    P, I, D = len(shapes), lay.I, R // S
+    dtype = params[0].dtype if params else torch.float32
+    xs = [to_oracle(p) for p in params]
+    np_dtype = np.float32 if dtype == torch.float32 else np.uint16
+    ag_o = O.ag_copy_in(O.shard_params(xs, lay), lay, np_dtype)
+    full_o = O.ag_copy_out(O.all_gather(ag_o), lay)
+
+    dparams = [p.cuda() for p in params]
+    shards, _keep = make_shards(dparams, lay, dtype, shard_offsets)
+    ag = Guarded(S * I, dtype, out_offset)
+    hp.fsdp_ag_copy_in(shapes, S, shards, ag.t)
+    full = [Guarded(_numel(sh), dtype, out_offset) for sh in shapes]
+    hp.fsdp_ag_copy_out(shapes, S, ag.t, [f.t for f in full])
+    torch.cuda.synchronize()
+    assert ag.guards_intact(), "ag_copy_in wrote outside ag"
+    assert first_mismatch(bits(ag.t), np_bits(ag_o)) == "", "ag_copy_in: " + first_mismatch(bits(ag.t), np_bits(ag_o))
+    for i in range(P):
+        assert full[i].guards_intact(), f"ag_copy_out wrote outside full[{i}]"
+        m = first_mismatch(bits(full[i].t), np_bits(full_o[i].reshape(-1)))
+        assert m == "", f"ag_copy_out param {i}: {m}"
+        assert np.array_equal(bits(full[i].t), np_bits(xs[i].reshape(-1)))  # all_gather(shard(x)) == x
+
+    if grads is None:
+        return
+    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
+    rs_o = [O.rs_copy_in(gnp[g], lay, np.float32) for g in range(R)]
+    dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    rs_in = [Guarded(S * I, torch.float32, out_offset) for _ in range(R)]
+    hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in])
+    torch.cuda.synchronize()
+    for g in range(R):
+        assert rs_in[g].guards_intact(), f"rs_copy_in wrote outside rs_in[{g}]"
+        m = first_mismatch(bits(rs_in[g].t), np_bits(rs_o[g]))
+        assert m == "", f"rs_copy_in rank {g}: {m}"
+    for op in ops:
+        out_o = O.rs_reduce(rs_o, I, R, S, op)
+        out = [Guarded(I, torch.float32, out_offset + 1 + g % 3) for g in range(R)]
+        hp.fsdp_rs_reduce(shapes, R, S, D, op, [b.t for b in rs_in], [o.t for o in out])
+        torch.cuda.synchronize()
+        for g in range(R):
+            assert out[g].guards_intact(), f"rs_reduce wrote outside rs_out[{g}]"
+            m = first_mismatch(bits(out[g].t), np_bits(out_o[g]))
+            assert m == "", f"rs_reduce {op} rank {g}: {m}"
+
+
+def test_tiny_fsdp_workload():
+    w = W.TINY_FSDP
+    run_copy_and_rs(w.name, w.param_shapes, w.rank_size, w.shard_size, W.params(w), W.grads(w))
+
+
+@pytest.mark.parametrize("out_offset", [1, 2, 3])
+def test_tiny_fsdp_misaligned(out_offset):
+    w = W.TINY_FSDP
+    run_copy_and_rs(w.name + "_misaligned", w.param_shapes, w.rank_size, w.shard_size, W.params(w), W.grads(w),
+                    shard_offsets=[0, 1, 2, 3, 5, 7], out_offset=out_offset)
+
+
+def test_ragged_heavy_scaled():
+    """The ragged-heavy set with its second dim cut from 4096 to 8: same
+    dim-0 sizes, an odd slice size I, zero-length shards, many chunks."""
+    w = W.scaled(W.RAGGED_HEAVY, [(4097, 8), (11009, 8), (32001, 8), (5, 64), (3,)])
+    run_copy_and_rs(w.name, w.param_shapes, w.rank_size, w.shard_size, W.params(w), W.grads(w))
+
+
+def test_bf16_ragged_all_alignments():
+    """bf16 with 1-D parameters whose shards start at odd elements: every
+    2-byte source/destination misalignment, HSDP 16 = 2 x 8."""
+    shapes = [(100003,), (7, 3), (13,), (0, 5), (1,), (257, 33), (40001, 3)]
+    w = W.Workload("bf16_ragged", 11, 16, 8, tuple(shapes), torch.bfloat16, ("normal", 0.02),
+                   ("normal", 1e-3), ("sum", "avg"), W.ALL_STEPS)
+    run_copy_and_rs(w.name, shapes, 16, 8, W.params(w), W.grads(w),
+                    shard_offsets=[0, 1, 2, 3, 4, 5, 6, 7, 9, 13], out_offset=5)
+
+
+def test_fp16_copies_and_nonpow2_groups():
+    shapes = [(1001, 7), (17,), (3, 3, 3), (0,)]
+    w = W.Workload("fp16_r6_s3", 12, 6, 3, tuple(shapes), torch.float16, ("uniform", 1.0),
+                   ("uniform", 1.0), ("sum", "avg"), W.ALL_STEPS)
+    run_copy_and_rs(w.name, shapes, 6, 3, W.params(w), W.grads(w), shard_offsets=[0, 3, 1])
+
+
+def test_fp32_nonpow2_shard_group():
+    shapes = [(1001, 7), (17,), (3, 3, 3), (50000,)]
+    w = W.Workload("fp32_r6_s3", 13, 6, 3, tuple(shapes), torch.float32, ("uniform", 1.0),
+                   ("uniform", 1.0), ("sum", "avg"), W.ALL_STEPS)
+    run_copy_and_rs(w.name, shapes, 6, 3, W.params(w), W.grads(w))
+
+
+def test_random_buckets():
+    rng = np.random.default_rng(2024)
+    for case in range(16):
+        S = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        D = int(rng.choice([1, 2, 3]))
+        P = int(rng.integers(1, 6))
+        shapes = []
+        for _ in range(P):
+            n0 = int(rng.integers(0, 3 * S + 40))
+            rest = [int(rng.choice([1, 2, 3, 7, 64, 129]))] if rng.random() < 0.6 else []
+            shapes.append(tuple([n0] + rest))
+        dtype = [torch.float32, torch.bfloat16, torch.float16][case % 3]
+        w = W.Workload(f"random_{case}", 100 + case, S * D, S, tuple(shapes), dtype, ("uniform", 1.0),
+                       ("normal", 1.0), ("sum", "avg"), W.ALL_STEPS)
+        run_copy_and_rs(w.name, shapes, S * D, S, W.params(w), W.grads(w),
+                        shard_offsets=[int(v) for v in rng.integers(0, 8, size=5)],
+                        out_offset=int(rng.integers(0, 8)))
+
+
+def test_hsdp_block_full_size_copies_and_rs():
+    w = W.HSDP_BLOCK
+    run_copy_and_rs(w.name, w.param_shapes, w.rank_size, w.shard_size, W.params(w), W.grads(w),
+                    ops=(O.AVG, O.SUM))
+
+
+def test_padding_rewritten_on_reuse_and_side_stream():
+    """Padding is written as zero on every call (stale values in a reused
+    buffer are overwritten), also when the call runs on a side stream."""
+    shapes = [(7, 8), (5, 3), (16,), (3,)]
+    S = 4
+    lay = O.bucket_layout(shapes, S)
+    xs = [torch.randn(sh) for sh in shapes]
+    dparams = [x.cuda() for x in xs]
+    shards, _ = make_shards(dparams, lay, torch.float32)
+    ag = torch.full((S * lay.I,), float("nan"), device="cuda")
+    st = torch.cuda.Stream()
+    for rep in range(3):
+        ag.fill_(float(rep + 1))
+        with torch.cuda.stream(st):
+            hp.fsdp_ag_copy_in(shapes, S, shards, ag)
+        st.synchronize()
+        want = O.ag_copy_in(O.shard_params([x.numpy() for x in xs], lay), lay, np.float32)
+        assert np.array_equal(bits(ag), np_bits(want))
+
+
+def test_empty_buckets():
+    note("[parity] empty buckets")
+    S, R = 4, 8
+    for shapes in ([], [(0,), (0, 7)]):
+        lay = O.bucket_layout(shapes, S)
+        assert lay.I == 0
+        ag = torch.empty(0, device="cuda")
+        shards = [torch.empty(0, device="cuda") for _ in range(S * len(shapes))]
+        hp.fsdp_ag_copy_in(shapes, S, shards, ag)
+        hp.fsdp_ag_copy_out(shapes, S, ag, [torch.empty(sh, device="cuda").reshape(-1) for sh in shapes])
+        grads = [torch.empty(0, device="cuda") for _ in range(R * len(shapes))]
+        rs_in = [torch.empty(0, device="cuda") for _ in range(R)]
+        hp.fsdp_rs_copy_in(shapes, R, S, grads, rs_in)
+        hp.fsdp_rs_reduce(shapes, R, S, 2, O.AVG, rs_in, [torch.empty(0, device="cuda") for _ in range(R)])
+        hp.fsdp_fused_ar([], R, S, 2, O.AVG, [torch.empty(0, device="cuda") for _ in range(R)])
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# fused AR and the end-to-end gradient path
+# ---------------------------------------------------------------------------
+
+def fill_fused(seg_grads, offs, F):
+    """Fused buffers (gaps zero) holding rank g's segments at offs (on the GPU)."""
+    out = []
+    for segs in seg_grads:
+        buf = torch.zeros(F, dtype=torch.float32, device="cuda")
+        for o, t in zip(offs, segs):
+            buf[o:o + t.numel()] = t.reshape(-1)
+        out.append(buf)
+    return out
+
+
+@pytest.mark.parametrize("op", [O.AVG, O.SUM])
+def test_pure_tp_fused_ar_full_size(op):
+    """2000 gradients, log-uniform sizes, one 512-byte-aligned segment each,
+    AR over all 8 ranks (shard_size 1, dp_size 8)."""
+    w = W.PURE_TP
+    R, S = w.rank_size, w.shard_size
+    sizes = [s[0] for s in w.param_shapes]
+    note(f"[parity] {w.name} fused_ar {op}: {len(sizes)} segments")
+    g_cpu = W.grads(w)
+    offs_o, F_o = O.fused_layout(sizes)
+    fused_o = []
+    for g in range(R):
+        buf = np.zeros(F_o, np.float32)
+        for o, t in zip(offs_o, g_cpu[g]):
+            buf[o:o + t.numel()] = t.numpy()
+        fused_o.append(buf)
+    want = O.fused_ar(fused_o, R, S, op)
+    offs, F = hp.fsdp_fused_layout(sizes, 4)
+    assert (offs, F) == (offs_o, F_o)
+    fused = fill_fused([[t.cuda() for t in g_cpu[g]] for g in range(R)], offs, F)
+    hp.fsdp_fused_ar(sizes, R, S, R // S, op, fused)
+    torch.cuda.synchronize()
+    for g in range(R):
+        m = first_mismatch(bits(fused[g]), np_bits(want[g]))
+        assert m == "", f"fused_ar rank {g}: {m}"
+
+
+def run_hsdp_end_to_end(name, buckets, R, S, op, dtype=torch.float32, seed=7):
+    """Per bucket RS copy-in and RS into views of the fused buffers, then one
+    fused AR; compared with the oracle's fused path (final sharded grads
+    and the whole fused buffers, gaps included)."""
+    note(f"[parity] e2e {name}: R={R} S={S} op={op} buckets={len(buckets)}")
+    shapes = [sh for b in buckets for sh in b]
+    w = W.Workload(name, seed, R, S, tuple(shapes), dtype, ("normal", 1.0), ("normal", 1e-3),
+                   (op,), W.ALL_STEPS)
+    g_cpu = W.grads(w)
+    gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
+    res_o, fused_o, offs_o, lays = O.reduce_grads_fused(gnp, buckets, R, S, op)
+    D = R // S
+    lays_h = [hp.fsdp_bucket_layout(b, S) for b in buckets]
+    offs, F = hp.fsdp_fused_layout([l.I for l in lays_h], 4)
+    fused = [torch.zeros(F, dtype=torch.float32, device="cuda") for _ in range(R)]
+    j0 = 0
+    for b, lay, off in zip(buckets, lays_h, offs):
+        P = len(b)
+        grads = [g_cpu[g][j0 + i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+        rs_in = [torch.empty(S * lay.I, dtype=torch.float32, device="cuda") for _ in range(R)]
+        hp.fsdp_rs_copy_in(b, R, S, grads, rs_in)
+        hp.fsdp_rs_reduce(b, R, S, D, op, rs_in, [f[off:off + lay.I] for f in fused])
+        j0 += P
+    rs, ar = hp.fsdp_group_ranks(R, S)
+    if ar:
+        hp.fsdp_fused_ar([l.I for l in lays_h], R, S, D, op, fused)
+    torch.cuda.synchronize()
+    for g in range(R):
+        m = first_mismatch(bits(fused[g]), np_bits(fused_o[g]))
+        assert m == "", f"e2e fused buffer rank {g}: {m}"
+    # write-back by sharded_size: the optimizer's views match the oracle's
+    j0 = 0
+    for k, (b, lay) in enumerate(zip(buckets, lays_h)):
+        for g in range(R):
+            s = g % S
+            for i, sh in enumerate(b):
+                n = lay.row_len[i][s] * _numel(sh[1:])
+                v = fused[g][offs[k] + lay.in_off[i]: offs[k] + lay.in_off[i] + n]
+                assert np.array_equal(bits(v), np_bits(res_o[g][j0 + i].reshape(-1)))
+        j0 += len(b)
+
+
+@pytest.mark.parametrize("R,S", [(8, 4), (8, 2), (6, 2), (16, 8)])
+@pytest.mark.parametrize("op", [O.AVG, O.SUM])
+def test_hsdp_end_to_end_multi_bucket(R, S, op):
+    shapes = [(7, 8), (5, 3), (16,), (3,), (1000, 3), (129,), (4097, 2)]
+    run_hsdp_end_to_end(f"multi_bucket_{R}_{S}", [shapes[:3], shapes[3:5], shapes[5:]], R, S, op)
+    run_hsdp_end_to_end(f"per_param_{R}_{S}", [[s] for s in shapes], R, S, op)
+
+
+def test_hsdp_block_end_to_end_flat_bucket():
+    """The HSDP block through FlatBucket (the benchmark's object): all five
+    steps, RS outputs written as fused-buffer views, AR(2) with AVG."""
+    w = W.HSDP_BLOCK
+    R, S, D = w.rank_size, w.shard_size, w.dp_size
+    note(f"[parity] {w.name} FlatBucket step")
+    params = W.params(w)
+    g_cpu = W.grads(w)
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG)
+    dparams = [p.cuda() for p in params]
+    dgrads = [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(len(w.param_shapes))]
+    fb.bind(fb.shard_views(dparams), dgrads)
+    assert fb.steps() == list(W.ALL_STEPS)
+    fb.step()
+    torch.cuda.synchronize()
+    for i, p in enumerate(params):
+        assert np.array_equal(bits(fb.full[i]), bits(p.reshape(-1)))
+    gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
+    res_o, fused_o, _, _ = O.reduce_grads_fused(gnp, [list(w.param_shapes)], R, S, O.AVG)
+    for g in range(R):
+        m = first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g]))
+        assert m == "", f"fused rank {g}: {m}"

@@ -1,0 +1,331 @@
+"""CPU emulation of the kernels' work decomposition (no GPU).
+
+Mirrors, line for line in Python, the address arithmetic of seg_copy_kernel
+and reduce_kernel (hsdp_parameter_gradient_amd/csrc/kernels.hip): the
+64-ary chunk search, the chunk windows, the whole-vector ranges, the
+zero-fill range and the element-wise edge vectors.  For many segment
+tables it checks that
+
+  * every destination byte is written exactly once, with data from the
+    right source offset before the data/padding edge and zero after it;
+  * no byte outside the destination segments is written;
+  * every 16-byte source block read lies inside the aligned envelope of its
+    source range (so no read leaves the source's pages);
+  * the chunk search finds the right item for every chunk.
+
+This is the host-side bounds check of the kernels' indexing; it runs before
+any GPU does.
+"""
+
+import numpy as np
+import pytest
+
+CHUNK_SHIFTS = (9, 10, 15)
+
+
+def align_down16(a):
+    return a & ~15
+
+
+def align_up16(a):
+    return (a + 15) & ~15
+
+
+def chunk_count(dst, nbytes, shift):
+    return ((dst + nbytes - 1) >> shift) - (dst >> shift) + 1
+
+
+def find_item(begin, n, c):
+    """The kernel's 64-ary search (every lane probes one entry)."""
+    lo, cnt = 0, n
+    while cnt > 1:
+        step = (cnt + 63) >> 6
+        m = [off < cnt and begin[lo + off] <= c for off in (lane * step for lane in range(64))]
+        k = sum(m) - 1
+        assert m[:k + 1] == [True] * (k + 1) and not any(m[k + 1:])  # monotone ballot
+        lo += k * step
+        rest = cnt - k * step
+        cnt = rest if rest < step else step
+    return lo
+
+
+def emulate_copy(segs, es, shift):
+    """Writes as (dst_lo, dst_hi, kind, src_lo) and reads as aligned block
+    addresses, per segment, following seg_copy_kernel."""
+    CH = 1 << shift
+    begin, n = [], 0
+    for (src, dst, copy, total) in segs:
+        begin.append(n)
+        n += chunk_count(dst, total, shift)
+    writes, reads = [], []
+    for c in range(n):
+        j = find_item(begin, len(segs), c)
+        assert begin[j] <= c and (j + 1 == len(segs) or c < begin[j + 1])
+        src, dst, copy, total = segs[j]
+        k = c - begin[j]
+        base = (dst >> shift) << shift
+        seg_end, cend = dst + total, dst + copy
+        w0 = base + k * CH
+        lo = max(w0, dst)
+        hi = min(w0 + CH, seg_end)
+        assert lo < hi
+        ca, cb = align_up16(lo), align_down16(min(hi, cend))
+        if ca < cb:
+            s0 = src + (ca - dst)
+            r = s0 & 15
+            nv = (cb - ca) >> 4
+            writes.append((ca, cb, "data", s0, j))
+            first = s0 - r
+            last = first + 16 * (nv - 1) + (16 if r else 0)  # s[j] and, when shifted, s[j+1]
+            reads.append((first, last + 16, j))
+        za, zb = align_up16(max(lo, cend)), align_down16(hi)
+        if za < zb:
+            writes.append((za, zb, "zero", None, j))
+        a_lo, a_c, a_hi = align_down16(lo), align_down16(cend), align_down16(hi)
+        p_lo = (lo & 15) != 0
+        p_c = (cend & 15) != 0 and lo < cend < hi and not (p_lo and a_c == a_lo)
+        p_hi = (hi & 15) != 0 and not (p_lo and a_hi == a_lo) and not (p_c and a_hi == a_c)
+        for flag, a in ((p_lo, a_lo), (p_c, a_c), (p_hi, a_hi)):
+            if not flag:
+                continue
+            x0, x1 = max(a, lo), min(a + 16, hi)
+            for x in range(x0, x1, es):
+                if x < cend:
+                    writes.append((x, x + es, "data", src + (x - dst), j))
+                    reads.append((src + (x - dst), src + (x - dst) + es, j))
+                else:
+                    writes.append((x, x + es, "zero", None, j))
+    return writes, reads
+
+
+def check_copy(segs, es, shift):
+    writes, reads = emulate_copy(segs, es, shift)
+    # exact cover of every segment, no write outside
+    ws = sorted(writes)
+    spans = sorted((dst, dst + total) for (_, dst, _, total) in segs)
+    merged = []
+    for a, b in spans:
+        if merged and a < merged[-1][1]:
+            raise AssertionError("segments overlap")
+        merged.append((a, b))
+    cover = []
+    for (a, b, kind, s0, j) in ws:
+        if cover and a < cover[-1][1]:
+            raise AssertionError(f"byte {a:#x} written twice")
+        cover.append((a, b))
+        src, dst, copy, total = segs[j]
+        assert dst <= a and b <= dst + total, "write outside its segment"
+        if kind == "data":
+            assert b <= dst + copy and s0 == src + (a - dst), "data write with a wrong source"
+        else:
+            assert a >= dst + copy, "zero write over data"
+    # the union of writes equals the union of segments
+    def union(iv):
+        out = []
+        for a, b in sorted(iv):
+            if out and a == out[-1][1]:
+                out[-1] = (out[-1][0], b)
+            else:
+                out.append((a, b))
+        return out
+    assert union(cover) == union([s for s in merged if s[0] < s[1]])
+    for (a, b, j) in reads:
+        src, dst, copy, total = segs[j]
+        assert align_down16(src) <= a and b <= align_up16(src + copy), "read outside the source envelope"
+
+
+def emulate_reduce(jobs, ptr, shift):
+    """Writes per destination as (lo, hi) byte ranges and operand reads,
+    following reduce_kernel."""
+    CH = 1 << shift
+    begin, n = [], 0
+    for (nbytes, src0, nsrc, dst0, ndst) in jobs:
+        begin.append(n)
+        n += chunk_count(ptr[dst0], nbytes, shift)
+    writes, reads = [], []
+    for c in range(n):
+        j = find_item(begin, len(jobs), c)
+        nbytes, src0, nsrc, dst0, ndst = jobs[j]
+        k = c - begin[j]
+        d0 = ptr[dst0]
+        base = (d0 >> shift) << shift
+        w0 = base + k * CH
+        lo = max(w0, d0)
+        end = d0 + nbytes
+        hi = min(w0 + CH, end)
+        va, vb = align_up16(lo) - d0, align_down16(hi) - d0
+        if va < vb:
+            nv = (vb - va) >> 4
+            for t in range(nsrc):
+                sa = ptr[src0 + t] + va
+                r = sa & 15
+                reads.append((sa - r, sa - r + 16 * nv + (16 if r else 0), j, t))
+            for m in range(ndst):
+                writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + vb, j, m))
+        e0 = lo - d0
+        e_head = min(align_up16(lo), hi) - d0
+        e_tail = max(align_down16(hi), lo) - d0
+        e1 = hi - d0
+        n_head = (e_head - e0) >> 2
+        t0 = max(e_tail, e_head)
+        n_tail = (e1 - t0) >> 2
+        assert n_head + n_tail <= 256
+        for tid in range(n_head + n_tail):
+            x = e0 + 4 * tid if tid < n_head else t0 + 4 * (tid - n_head)
+            for t in range(nsrc):
+                reads.append((ptr[src0 + t] + x, ptr[src0 + t] + x + 4, j, t))
+            for m in range(ndst):
+                writes.append((ptr[dst0 + m] + x, ptr[dst0 + m] + x + 4, j, m))
+    return writes, reads
+
+
+def check_reduce(jobs, ptr, shift):
+    writes, reads = emulate_reduce(jobs, ptr, shift)
+    per = {}
+    for (a, b, j, m) in writes:
+        per.setdefault((j, m), []).append((a, b))
+    for j, (nbytes, src0, nsrc, dst0, ndst) in enumerate(jobs):
+        for m in range(ndst):
+            iv = sorted(per.get((j, m), []))
+            pos = ptr[dst0 + m]
+            for a, b in iv:
+                assert a == pos, f"job {j} dst {m}: gap or double write at {a:#x} (expected {pos:#x})"
+                pos = b
+            assert pos == ptr[dst0 + m] + nbytes
+    for (a, b, j, t) in reads:
+        nbytes, src0, nsrc, dst0, ndst = jobs[j]
+        s = ptr[src0 + t]
+        assert align_down16(s) <= a and b <= align_up16(s + nbytes), "operand read outside its envelope"
+
+
+# ---------------------------------------------------------------------------
+# tables like the planner's, on fake addresses
+# ---------------------------------------------------------------------------
+
+def layout(shapes, S):
+    chunk, inner, padded, in_off, ro, rl = [], [], [], [], [], []
+    off = 0
+    for sh in shapes:
+        n0 = sh[0]
+        inn = int(np.prod(sh[1:])) if len(sh) > 1 else 1
+        c = -(-n0 // S)
+        chunk.append(c)
+        inner.append(inn)
+        padded.append(c * inn)
+        in_off.append(off)
+        ro.append([min(s * c, n0) for s in range(S)])
+        rl.append([min(c, n0 - min(s * c, n0)) for s in range(S)])
+        off += c * inn
+    return dict(I=off, inner=inner, padded=padded, in_off=in_off, ro=ro, rl=rl)
+
+
+def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
+    L = layout(shapes, S)
+    segs = []
+    for s in range(S):
+        for i in range(len(shapes)):
+            nb = L["rl"][i][s] * L["inner"][i] * es
+            total = L["padded"][i] * es
+            if total:
+                segs.append((shard_addr(s, i) if nb else 0, ag + (s * L["I"] + L["in_off"][i]) * es, nb, total))
+    return segs
+
+
+def ag_copy_out_segs(shapes, S, es, ag, full_addr):
+    L = layout(shapes, S)
+    segs = []
+    for i in range(len(shapes)):
+        for s in range(S):
+            n = L["rl"][i][s] * L["inner"][i] * es
+            if n:
+                segs.append((ag + (s * L["I"] + L["in_off"][i]) * es,
+                             full_addr(i) + L["ro"][i][s] * L["inner"][i] * es, n, n))
+    return segs
+
+
+SHAPES = [
+    [(7, 8), (5, 3), (16,)],
+    [(4097, 8), (1009, 8), (5, 64), (3,)],
+    [(100003,), (7, 3), (13,), (0, 5), (1,), (257, 33)],
+    [(0,), (1,), (2,), (3,)],
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPES)
+@pytest.mark.parametrize("S", [1, 3, 4, 8])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", CHUNK_SHIFTS)
+def test_copy_ops_cover_exactly(shapes, S, es, shift):
+    base = 1 << 32
+    rng = np.random.default_rng(S * 100 + es)
+    ag = base + es * int(rng.integers(0, 9))
+    # shards at scattered element offsets (every relative alignment)
+    shard = {}
+    a = base + (1 << 28)
+    for s in range(S):
+        for i in range(len(shapes)):
+            shard[(s, i)] = a + es * int(rng.integers(0, 9))
+            a += 1 << 22
+    check_copy(ag_copy_in_segs(shapes, S, es, ag, lambda s, i: shard[(s, i)]), es, shift)
+    full = {i: base + (1 << 30) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    check_copy(ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i]), es, shift)
+
+
+def test_random_segments():
+    rng = np.random.default_rng(99)
+    for trial in range(300):
+        es = int(rng.choice([2, 4]))
+        shift = int(rng.choice(CHUNK_SHIFTS[:2]))
+        segs = []
+        dst = (1 << 33) + es * int(rng.integers(0, 64))
+        for _ in range(int(rng.integers(1, 12))):
+            total = es * int(rng.choice([0, 1, 2, 3, 7, 8, 9, 63, 64, 65, 300, 1000, 5000]))
+            copy = es * int(rng.integers(0, total // es + 1)) if total else 0
+            src = (1 << 40) + int(rng.integers(0, 1 << 20)) * es
+            if total:
+                segs.append((src if copy else 0, dst, copy, total))
+            dst += total + es * int(rng.choice([0, 0, 1, 5]))
+        if segs:
+            check_copy(segs, es, shift)
+
+
+@pytest.mark.parametrize("shift", CHUNK_SHIFTS)
+def test_reduce_jobs_cover_exactly(shift):
+    rng = np.random.default_rng(shift)
+    for trial in range(60):
+        R, S = [(8, 4), (8, 8), (6, 3), (8, 1), (2, 2)][trial % 5]
+        I = int(rng.choice([1, 2, 3, 5, 16, 17, 1000, 4097, 20000]))
+        rs_in = [(1 << 36) + g * (1 << 26) + 4 * int(rng.integers(0, 8)) for g in range(R)]
+        rs_out = [(1 << 38) + g * (1 << 26) + 4 * int(rng.integers(0, 8)) for g in range(R)]
+        # RS jobs, as fsdp_rs_reduce builds them
+        jobs, ptr = [], []
+        for g in range(R):
+            d, s = divmod(g, S)
+            src0 = len(ptr)
+            ptr += [rs_in[d * S + t] + s * I * 4 for t in range(S)]
+            dst0 = len(ptr)
+            ptr.append(rs_out[g])
+            jobs.append((I * 4, src0, S, dst0, 1))
+        check_reduce(jobs, ptr, shift)
+        # fused AR jobs (in place, 512-byte aligned bases, F a multiple of 128)
+        D = R // S
+        if D > 1:
+            F = 128 * int(rng.integers(1, 40))
+            fused = [(1 << 39) + g * (1 << 26) for g in range(R)]
+            jobs, ptr = [], []
+            for s in range(S):
+                src0 = len(ptr)
+                ptr += [fused[d * S + s] for d in range(D)]
+                jobs.append((F * 4, src0, D, src0, D))
+            check_reduce(jobs, ptr, shift)
+
+
+def test_find_item_all_chunks():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 63, 64, 65, 100, 4095, 4096, 4097, 9000):
+        sizes = rng.integers(1, 4, size=n)
+        begin = np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+        total = int(np.sum(sizes))
+        for c in list(range(0, min(total, 300))) + list(range(max(0, total - 300), total)):
+            j = find_item(begin, n, c)
+            assert begin[j] <= c and (j + 1 == n or c < begin[j + 1])
