@@ -93,6 +93,40 @@ def measured_traffic(step: str, launches_bytes: int):
     return ent.get("bytes_per_launch")
 
 
+class PureTPRunner:
+    """shard_size 1 (pure-TP compatible path): no AG and no RS; every
+    gradient is one 512-byte-aligned segment of its rank's fused buffer and
+    one fused AR over the replicate group (all R ranks) is the whole step."""
+
+    def __init__(self, w, op):
+        import torch
+
+        import hsdp_parameter_gradient_amd as hp
+        import workloads as W
+        R = w.rank_size
+        sizes = [_numel(s) for s in w.param_shapes]
+        self.layout = hp.fsdp_bucket_layout(w.param_shapes, 1)
+        offs, self.F = hp.fsdp_fused_layout(sizes, 4)
+        grads = W.grads(w, "cuda")
+        self.fused = []
+        for g in range(R):
+            buf = torch.zeros(self.F, dtype=torch.float32, device="cuda")
+            for o, t in zip(offs, grads[g]):
+                buf[o:o + t.numel()] = t.reshape(-1)
+            self.fused.append(buf)
+        del grads
+        self.call = hp.prepare("fsdp_fused_ar", sizes, R, 1, R, op, self.fused)
+
+    def steps(self):
+        return ["fused_ar"]
+
+    def run(self, name, stream=None):
+        self.call(stream)
+
+    def step(self, stream=None):
+        self.call(stream)
+
+
 def cpu_baseline(w, seconds: float, op: str):
     """The oracle, as it stands, timed on whole steps of the workload."""
     import numpy as np
@@ -115,7 +149,22 @@ def cpu_baseline(w, seconds: float, op: str):
     offs, F = O.fused_layout([lay.I])
     do_ar = bool([c for c in O.grad_sync_plan(R, S) if c[0] == "AR"])
 
-    def one_step():
+    if S == 1:  # pure-TP compatible path: the fused AR is the whole step
+        sizes = [_numel(s) for s in w.param_shapes]
+        offs, F = O.fused_layout(sizes)
+        fused0 = []
+        for g in range(R):
+            buf = np.zeros(F, np.float32)
+            for o, t in zip(offs, gnp[g]):
+                buf[o:o + t.size] = t.reshape(-1)
+            fused0.append(buf)
+
+        def one_step():
+            O.fused_ar(fused0, R, S, op)
+    else:
+        one_step = None
+
+    def hsdp_step():
         ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt)
         O.ag_copy_out(O.all_gather(ag), lay)
         rs_in = [O.rs_copy_in(gnp[g], lay) for g in range(R)]
@@ -128,6 +177,7 @@ def cpu_baseline(w, seconds: float, op: str):
         if do_ar:
             O.fused_ar(fused, R, S, op)
 
+    one_step = one_step or hsdp_step
     n, t0 = 0, time.perf_counter()
     while True:
         one_step()
@@ -168,16 +218,22 @@ def main():
     torch.cuda.set_device(0)
     log(f"bench: workload {w.name} ({w.description}); R={R} S={S} D={D} op={op}")
 
-    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
-    params = W.params(w, "cuda")
-    grads = W.grads(w, "cuda")
-    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
-    steps = fb.steps()
-    nbytes = step_bytes(w, fb.layout, fb.F)
+    if S > 1:
+        fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
+        params = W.params(w, "cuda")
+        grads = W.grads(w, "cuda")
+        fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+        runner = fb
+        lay, F = fb.layout, fb.F
+    else:
+        runner = PureTPRunner(w, op)
+        lay, F = runner.layout, runner.F
+    steps = runner.steps()
+    nbytes = step_bytes(w, lay, F)
     bytes_per_step = sum(nbytes[s] for s in steps)
 
     for _ in range(args.warmup):
-        fb.step()
+        runner.step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -190,7 +246,7 @@ def main():
     for k in range(K):
         for j, name in enumerate(steps):
             ev[k][j][0].record()
-            fb.run(name)
+            runner.run(name)
             ev[k][j][1].record()
     end.record()
     torch.cuda.synchronize()
@@ -230,7 +286,7 @@ def main():
         "config": {"workload": w.name, "rank_size": R, "shard_size": S, "dp_size": D,
                    "param_dtype": str(w.param_dtype).replace("torch.", ""), "grad_dtype": "float32",
                    "reduce_op": op, "params": P, "elements": sum(_numel(s) for s in w.param_shapes),
-                   "slice_numel": fb.layout.I, "fused_numel": fb.F, "bytes_per_step": bytes_per_step,
+                   "slice_numel": lay.I, "fused_numel": F, "bytes_per_step": bytes_per_step,
                    "steps_per_pass": steps},
         "roofline": roof,
         "cpu_baseline": cpu,

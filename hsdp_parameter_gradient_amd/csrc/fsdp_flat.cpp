@@ -175,8 +175,8 @@ int check_overlap(std::vector<Span> outs, const std::vector<Span>& ins) {
 // ---------------------------------------------------------------------------
 
 struct Tuning {
-  uint32_t copy_shift = 15;    // 32 KiB of destination per chunk
-  uint32_t reduce_shift = 14;  // 16 KiB of destination per chunk
+  uint32_t copy_shift = 14;    // 16 KiB of destination per chunk
+  uint32_t reduce_shift = 13;  // 8 KiB of destination per chunk
   uint32_t max_grid = 1u << 20;
 };
 
@@ -200,9 +200,6 @@ struct Entry {
   std::vector<uint8_t> host;  // the table; also the key
   uint64_t hash;
   void* dev = nullptr;
-  hipEvent_t ready = nullptr;  // recorded after the upload
-  hipStream_t upload_stream = nullptr;
-  bool ready_done = false;
 };
 
 constexpr size_t kMaxEntries = 128;
@@ -211,13 +208,8 @@ std::mutex g_mu;
 std::list<Entry> g_lru;  // front = most recent
 std::unordered_map<uint64_t, std::vector<std::list<Entry>::iterator>> g_index;
 
-uint64_t fnv1a(const uint8_t* p, size_t n, uint64_t h) {
-  for (size_t k = 0; k < n; ++k) h = (h ^ p[k]) * 1099511628211ull;
-  return h;
-}
-
 uint64_t table_hash(const std::vector<uint8_t>& t, int device) {
-  // words at a time for speed; a full compare settles collisions
+  // 8 bytes at a time; a full compare settles collisions
   uint64_t h = 1469598103934665603ull ^ (uint64_t)device;
   const size_t nw = t.size() / 8;
   const uint64_t* w = reinterpret_cast<const uint64_t*>(t.data());
@@ -226,21 +218,23 @@ uint64_t table_hash(const std::vector<uint8_t>& t, int device) {
     h *= 0x9E3779B97F4A7C15ull;
     h ^= h >> 29;
   }
-  return fnv1a(t.data() + nw * 8, t.size() - nw * 8, h);
+  for (size_t k = nw * 8; k < t.size(); ++k) h = (h ^ t[k]) * 1099511628211ull;
+  return h;
 }
 
 void drop_entry(std::list<Entry>::iterator it) {
   auto& v = g_index[it->hash];
   v.erase(std::remove(v.begin(), v.end(), it), v.end());
   if (v.empty()) g_index.erase(it->hash);
-  if (it->ready) (void)hipEventDestroy(it->ready);
   if (it->dev) (void)hipFree(it->dev);
   g_lru.erase(it);
 }
 
-// Device copy of `table`, made visible to `stream` before anything it
-// enqueues next.  Returns FSDP_OK and sets *dev.
-int get_table(std::vector<uint8_t>&& table, hipStream_t stream, void** dev) {
+// Device copy of `table` on the current device.  A table seen before is
+// reused; a new one is uploaded with a blocking copy, so it is complete
+// before anything is enqueued on any stream (no cross-stream ordering to
+// track, and steady-state calls make no HIP call besides the launch).
+int get_table(std::vector<uint8_t>&& table, void** dev) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail(FSDP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -250,13 +244,6 @@ int get_table(std::vector<uint8_t>&& table, hipStream_t stream, void** dev) {
   if (found != g_index.end()) {
     for (auto it : found->second) {
       if (it->device == device && it->host == table) {
-        if (!it->ready_done && it->upload_stream != stream) {
-          if (hipEventQuery(it->ready) == hipSuccess) {
-            it->ready_done = true;
-          } else if ((e = hipStreamWaitEvent(stream, it->ready, 0)) != hipSuccess) {
-            return fail(FSDP_EHIP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
-          }
-        }
         g_lru.splice(g_lru.begin(), g_lru, it);
         *dev = it->dev;
         return FSDP_OK;
@@ -265,7 +252,8 @@ int get_table(std::vector<uint8_t>&& table, hipStream_t stream, void** dev) {
   }
   if (g_lru.size() >= kMaxEntries) {
     // tables still in use by queued kernels must outlive them
-    (void)hipDeviceSynchronize();
+    if ((e = hipDeviceSynchronize()) != hipSuccess)
+      return fail(FSDP_EHIP, "hipDeviceSynchronize before evicting tables: %s", hipGetErrorString(e));
     while (g_lru.size() >= kMaxEntries / 2) drop_entry(std::prev(g_lru.end()));
   }
   Entry ent;
@@ -274,17 +262,10 @@ int get_table(std::vector<uint8_t>&& table, hipStream_t stream, void** dev) {
   ent.host = std::move(table);
   if ((e = hipMalloc(&ent.dev, ent.host.size())) != hipSuccess)
     return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", ent.host.size(), hipGetErrorString(e));
-  if ((e = hipMemcpyAsync(ent.dev, ent.host.data(), ent.host.size(), hipMemcpyHostToDevice, stream)) != hipSuccess) {
+  if ((e = hipMemcpy(ent.dev, ent.host.data(), ent.host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
     (void)hipFree(ent.dev);
-    return fail(FSDP_EHIP, "hipMemcpyAsync of a descriptor table: %s", hipGetErrorString(e));
+    return fail(FSDP_EHIP, "upload of a descriptor table: %s", hipGetErrorString(e));
   }
-  if ((e = hipEventCreateWithFlags(&ent.ready, hipEventDisableTiming)) != hipSuccess ||
-      (e = hipEventRecord(ent.ready, stream)) != hipSuccess) {
-    (void)hipStreamSynchronize(stream);
-    (void)hipFree(ent.dev);
-    return fail(FSDP_EHIP, "descriptor table event: %s", hipGetErrorString(e));
-  }
-  ent.upload_stream = stream;
   g_lru.push_front(std::move(ent));
   g_index[h].push_back(g_lru.begin());
   *dev = g_lru.front().dev;
@@ -317,7 +298,7 @@ int run_copy(std::vector<fsdp::CopySeg>& segs, int es, hipStream_t stream) {
   append(table, begin.data(), begin.size());
   append(table, segs.data(), segs.size());
   void* dev = nullptr;
-  int rc = get_table(std::move(table), stream, &dev);
+  int rc = get_table(std::move(table), &dev);
   if (rc) return rc;
   int he = fsdp_launch_seg_copy(es, dev, (uint32_t)segs.size(), n, tu.copy_shift, tu.max_grid, stream);
   if (he != hipSuccess) return fail(FSDP_EHIP, "seg_copy launch: %s", hipGetErrorString((hipError_t)he));
@@ -338,9 +319,10 @@ int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int
   append(table, jobs.data(), jobs.size());
   append(table, ptrs.data(), ptrs.size());
   void* dev = nullptr;
-  int rc = get_table(std::move(table), stream, &dev);
+  int rc = get_table(std::move(table), &dev);
   if (rc) return rc;
-  int he = fsdp_launch_reduce(dev, (uint32_t)jobs.size(), n, tu.reduce_shift, tu.max_grid, avg, stream);
+  int he = fsdp_launch_reduce(dev, (uint32_t)jobs.size(), jobs[0].nsrc, n, tu.reduce_shift, tu.max_grid,
+                              avg, stream);
   if (he != hipSuccess) return fail(FSDP_EHIP, "reduce launch: %s", hipGetErrorString((hipError_t)he));
   return ok();
 }

@@ -18,17 +18,33 @@
 // (each block read holds at least one byte the copy needs, so no read
 // leaves the source's own pages).  The few 16-byte vectors that straddle a
 // segment edge or the data/padding edge are written element by element, so
-// that no byte outside the segment is touched.
+// that no byte outside the segment is touched.  Every loop over a chunk's
+// vectors runs whole unguarded iterations (all loads of an iteration in
+// flight before the first use) and then a short guarded tail.
 //
 // Arithmetic: the reduce kernel adds operands one at a time in ascending
 // rank order, the accumulator starting from the first operand, in IEEE
-// fp32 with denormals preserved; AVG divides by the operand count (an
-// exact multiply for a power of two, a correctly rounded divide otherwise).
+// fp32 with denormals preserved; AVG divides the sum by the operand count
+// with a correctly rounded division (for a power of two that is the exact
+// multiply by its reciprocal).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "plan.hpp"
+
+// Sources are read exactly once: nontemporal loads keep them from
+// displacing the outputs in L2 and MALL (measured faster on MI355X for every
+// op; nontemporal stores measured slower and stay off).
+#ifndef FSDP_NT_LOADS
+#define FSDP_NT_LOADS 1
+#endif
+#ifndef FSDP_NT_STORES
+#define FSDP_NT_STORES 0
+#endif
+#ifndef FSDP_COPY_UNROLL
+#define FSDP_COPY_UNROLL 4
+#endif
 
 namespace {
 
@@ -46,10 +62,21 @@ __device__ __forceinline__ GMEM T* gptr(uint64_t a) {
 }
 
 constexpr int kBlock = 256;
-constexpr int kUnroll = 4;
+constexpr int kCopyUnroll = FSDP_COPY_UNROLL;
 
 __device__ __forceinline__ uint64_t align_down16(uint64_t a) { return a & ~uint64_t(15); }
 __device__ __forceinline__ uint64_t align_up16(uint64_t a) { return (a + 15) & ~uint64_t(15); }
+
+__device__ __forceinline__ u32x4 ldv(const gvec* p) {
+  if (FSDP_NT_LOADS) return __builtin_nontemporal_load(p);
+  return *p;
+}
+__device__ __forceinline__ void stv(gvec* p, u32x4 v) {
+  if (FSDP_NT_STORES)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
 
 // Largest j with begin[j] <= c, for begin[0] == 0 <= c and begin strictly
 // increasing.  64-ary search: every lane of the wave probes one entry, so a
@@ -83,12 +110,51 @@ __device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 c, uint32_t b) {
   return o;
 }
 
+// Lane l of a full wave receives v from lane l + 1 (lane 63 receives lane
+// 0's value, which the callers replace); ds_bpermute moves data through the
+// LDS crossbar without touching LDS memory.
+__device__ __forceinline__ u32x4 from_next_lane(u32x4 v, uint32_t lane) {
+  const int addr = (int)(((lane + 1u) & 63u) << 2);
+  u32x4 o;
+  o.x = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x);
+  o.y = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y);
+  o.z = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z);
+  o.w = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w);
+  return o;
+}
+
+// Lane 0's value of v, in every lane (the wave must be full).
+__device__ __forceinline__ u32x4 lane0(u32x4 v) {
+  u32x4 o;
+  o.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.x);
+  o.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.y);
+  o.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.z);
+  o.w = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.w);
+  return o;
+}
+
+// Shifted view of U consecutive 64-block groups held one block per lane:
+// a[u] is block wb + 64u + lane, tail is block wb + 64U (wave-uniform).
+// Returns, in a[u], the 16 bytes starting r = 4*Q + b bytes into a[u]; each
+// source block is loaded once.
+template <int Q, int U>
+__device__ __forceinline__ void realign_groups(u32x4 (&a)[U], u32x4 tail, uint32_t lane, uint32_t b) {
+  u32x4 nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const u32x4 first_of_next = (u + 1 < U) ? lane0(a[u + 1 < U ? u + 1 : u]) : tail;
+    const u32x4 up = from_next_lane(a[u], lane);
+    nxt[u] = lane == 63u ? first_of_next : up;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) a[u] = funnel<Q>(a[u], nxt[u], b);
+}
+
 // 16 source bytes starting r bytes into aligned block s[j] (0 <= r < 16).
-__device__ __forceinline__ u32x4 load_shifted(const gvec* __restrict__ s, uint64_t j,
-                                              uint32_t r) {
-  if (r == 0) return s[j];
-  const u32x4 a = s[j];
-  const u32x4 c = s[j + 1];
+__device__ __forceinline__ u32x4 load_shifted(const gvec* __restrict__ s, uint64_t j, uint32_t r) {
+  if (r == 0) return ldv(s + j);
+  const u32x4 a = ldv(s + j);
+  const u32x4 c = ldv(s + j + 1);
   const uint32_t b = r & 3u;
   switch (r >> 2) {
     case 0: return funnel<0>(a, c, b);
@@ -102,23 +168,42 @@ __device__ __forceinline__ u32x4 load_shifted(const gvec* __restrict__ s, uint64
 // seg_copy
 // ---------------------------------------------------------------------------
 
+// nv destination vectors d[0..nv) from source blocks s[0..nv] realigned by
+// r = 4*Q + b bytes (Q = -1: aligned, s[0..nv) read directly).
 template <int Q>
-__device__ __forceinline__ void copy_funnel(gvec* __restrict__ d, const gvec* __restrict__ s,
-                                            uint64_t nv, uint32_t b) {
-  for (uint64_t j0 = threadIdx.x; j0 < nv; j0 += (uint64_t)kBlock * kUnroll) {
-    u32x4 a[kUnroll], c[kUnroll];
+__device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __restrict__ s, uint64_t nv,
+                                         uint32_t b) {
+  constexpr int U = kCopyUnroll;
+  constexpr int QQ = Q >= 0 ? Q : 0;
+  const uint32_t lane = threadIdx.x & 63u;
+  uint64_t base = 0;
+  for (; base + (uint64_t)kBlock * U <= nv; base += (uint64_t)kBlock * U) {
+    u32x4 a[U];
+    if (Q < 0) {
+      const uint64_t j = base + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kBlock;
-      if (j < nv) {
-        a[u] = s[j];
-        c[u] = s[j + 1];
-      }
+      for (int u = 0; u < U; ++u) a[u] = ldv(s + j + u * kBlock);
+#pragma unroll
+      for (int u = 0; u < U; ++u) stv(d + j + u * kBlock, a[u]);
+    } else {
+      // each wave owns 64*U consecutive vectors; one extra uniform block
+      // (the first of the next wave's range, at most block nv) closes it
+      const uint64_t wb = base + (uint64_t)(threadIdx.x >> 6) * 64u * U;
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = ldv(s + wb + u * 64 + lane);
+      const u32x4 tail = s[wb + 64 * U];
+      realign_groups<QQ, U>(a, tail, lane, b);
+#pragma unroll
+      for (int u = 0; u < U; ++u) stv(d + wb + u * 64 + lane, a[u]);
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kBlock;
-      if (j < nv) d[j] = funnel<Q>(a[u], c[u], b);
+  }
+  for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
+    const u32x4 a = ldv(s + j);
+    if (Q >= 0) {
+      const u32x4 c = ldv(s + j + 1);
+      stv(d + j, funnel<QQ>(a, c, b));
+    } else {
+      stv(d + j, a);
     }
   }
 }
@@ -127,37 +212,24 @@ __device__ __forceinline__ void copy_funnel(gvec* __restrict__ d, const gvec* __
 __device__ __forceinline__ void copy_vectors(uint64_t dst, uint64_t src, uint64_t nv) {
   gvec* __restrict__ d = gptr<u32x4>(dst);
   const uint32_t r = (uint32_t)(src & 15u);
-  if (r == 0) {
-    const gvec* __restrict__ s = gptr<u32x4>(src);
-    for (uint64_t j0 = threadIdx.x; j0 < nv; j0 += (uint64_t)kBlock * kUnroll) {
-      u32x4 v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * kBlock;
-        if (j < nv) v[u] = s[j];
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * kBlock;
-        if (j < nv) d[j] = v[u];
-      }
-    }
-    return;
-  }
   const gvec* __restrict__ s = gptr<u32x4>(src - r);
   const uint32_t b = r & 3u;
+  if (r == 0) {
+    copy_run<-1>(d, s, nv, 0);
+    return;
+  }
   switch (r >> 2) {
-    case 0: copy_funnel<0>(d, s, nv, b); break;
-    case 1: copy_funnel<1>(d, s, nv, b); break;
-    case 2: copy_funnel<2>(d, s, nv, b); break;
-    default: copy_funnel<3>(d, s, nv, b); break;
+    case 0: copy_run<0>(d, s, nv, b); break;
+    case 1: copy_run<1>(d, s, nv, b); break;
+    case 2: copy_run<2>(d, s, nv, b); break;
+    default: copy_run<3>(d, s, nv, b); break;
   }
 }
 
 __device__ __forceinline__ void zero_vectors(uint64_t dst, uint64_t nv) {
   gvec* __restrict__ d = gptr<u32x4>(dst);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (uint64_t j = threadIdx.x; j < nv; j += kBlock) d[j] = z;
+  for (uint64_t j = threadIdx.x; j < nv; j += kBlock) stv(d + j, z);
 }
 
 template <typename T>
@@ -220,10 +292,133 @@ __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __rest
 __device__ __forceinline__ f32x4 as_f4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
 __device__ __forceinline__ u32x4 as_u4(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
 
-__device__ __forceinline__ float scale_avg(float acc, float n, float inv, bool pow2) {
-  return pow2 ? acc * inv : acc / n;
+// Operand vector q: MODE 0 aligned, MODE 1 shifted by r = 4*Q + b bytes
+// (compile-time dword shift), MODE 2 any shift r.
+template <int MODE, int Q>
+__device__ __forceinline__ u32x4 operand(const gvec* __restrict__ s, uint64_t q, uint32_t r, uint32_t b) {
+  if (MODE == 0) return ldv(s + q);
+  if (MODE == 1) return funnel<Q>(ldv(s + q), ldv(s + q + 1), b);
+  return load_shifted(s, q, r);
 }
 
+template <int U>
+__device__ __forceinline__ void store_result(f32x4 (&acc)[U], const fsdp::RedJob& jb,
+                                             const uint64_t* __restrict__ ptr, uint64_t va,
+                                             uint64_t j, uint64_t stride, int avg, float nf) {
+  if (avg) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = acc[u] / nf;
+  }
+  for (uint32_t m = 0; m < jb.ndst; ++m) {
+    gvec* __restrict__ d = gptr<u32x4>(ptr[jb.dst0 + m] + va);
+#pragma unroll
+    for (int u = 0; u < U; ++u) stv(d + j + u * stride, as_u4(acc[u]));
+  }
+}
+
+// All destination vectors [0, nv) of one job window for a compile-time
+// operand count K: whole iterations of U vectors per lane with the K*U
+// operand loads in flight together, then a tail of single vectors.
+template <int K, int U, int MODE, int Q>
+__device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
+                                           const uint64_t (&sb)[K], const uint32_t (&sr)[K], uint64_t va,
+                                           uint64_t nv, int avg, float nf) {
+  const uint32_t b = sr[0] & 3u;
+  const uint32_t lane = threadIdx.x & 63u;
+  uint64_t base = 0;
+  for (; base + (uint64_t)kBlock * U <= nv; base += (uint64_t)kBlock * U) {
+    u32x4 v[K][U];
+    uint64_t j;  // this lane's first vector; its U vectors are j + u * stride
+    uint64_t stride;
+    if (MODE == 1) {
+      // wave-contiguous groups, each source block loaded once (see copy_run)
+      const uint64_t wb = base + (uint64_t)(threadIdx.x >> 6) * 64u * U;
+      j = wb + lane;
+      stride = 64;
+      u32x4 tail[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) {
+        const gvec* __restrict__ s = gptr<u32x4>(sb[t]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[t][u] = ldv(s + j + u * 64);
+        tail[t] = s[wb + 64 * U];
+      }
+#pragma unroll
+      for (int t = 0; t < K; ++t) realign_groups<Q, U>(v[t], tail[t], lane, b);
+    } else {
+      j = base + threadIdx.x;
+      stride = kBlock;
+#pragma unroll
+      for (int t = 0; t < K; ++t)
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[t][u] = operand<MODE, Q>(gptr<u32x4>(sb[t]), j + u * kBlock, sr[t], b);
+    }
+    f32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = as_f4(v[0][u]);
+#pragma unroll
+      for (int t = 1; t < K; ++t) acc[u] = acc[u] + as_f4(v[t][u]);
+    }
+    store_result<U>(acc, jb, ptr, va, j, stride, avg, nf);
+  }
+  for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
+    u32x4 v[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) v[t] = operand<(MODE == 1 ? 2 : MODE), Q>(gptr<u32x4>(sb[t]), j, sr[t], b);
+    f32x4 acc[1] = {as_f4(v[0])};
+#pragma unroll
+    for (int t = 1; t < K; ++t) acc[0] = acc[0] + as_f4(v[t]);
+    store_result<1>(acc, jb, ptr, va, j, kBlock, avg, nf);
+  }
+}
+
+// Whole vectors of one job window: destination vector q at byte offset
+// va + 16 q of every destination, operand t read at the same offset of its
+// source.  K > 0: compile-time operand count; K == 0: any count, one
+// operand at a time.
+template <int K>
+__device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
+                                               uint64_t va, uint64_t nv, int avg, float nf) {
+  if constexpr (K > 0) {
+    constexpr int U = K >= 4 ? 2 : 4;
+    uint64_t sb[K];
+    uint32_t sr[K];
+    bool same = true;
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+      const uint64_t sa = ptr[jb.src0 + t] + va;
+      sr[t] = (uint32_t)(sa & 15u);
+      sb[t] = sa - sr[t];
+      same = same && sr[t] == sr[0];
+    }
+    if (same && sr[0] == 0) {
+      reduce_run<K, U, 0, 0>(jb, ptr, sb, sr, va, nv, avg, nf);
+    } else if (same) {
+      switch (sr[0] >> 2) {
+        case 0: reduce_run<K, U, 1, 0>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 1: reduce_run<K, U, 1, 1>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 2: reduce_run<K, U, 1, 2>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        default: reduce_run<K, U, 1, 3>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+      }
+    } else {
+      reduce_run<K, U, 2, 0>(jb, ptr, sb, sr, va, nv, avg, nf);
+    }
+  } else {
+    for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
+      f32x4 acc[1];
+      for (uint32_t t = 0; t < jb.nsrc; ++t) {
+        const uint64_t sa = ptr[jb.src0 + t] + va;
+        const uint32_t r = (uint32_t)(sa & 15u);
+        const f32x4 v = as_f4(load_shifted(gptr<u32x4>(sa - r), j, r));
+        acc[0] = (t == 0) ? v : acc[0] + v;
+      }
+      store_result<1>(acc, jb, ptr, va, j, kBlock, avg, nf);
+    }
+  }
+}
+
+template <int K>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restrict__ begin,
                                                         const fsdp::RedJob* __restrict__ jobs,
                                                         const uint64_t* __restrict__ ptr,
@@ -241,48 +436,12 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     const uint64_t end = d0 + jb.nbytes;
     const uint64_t hi = (w0 + CH) < end ? (w0 + CH) : end;
     const float nf = (float)jb.nsrc;
-    const float inv = 1.0f / nf;
-    const bool pow2 = (jb.nsrc & (jb.nsrc - 1u)) == 0u;
 
     // whole vectors: offsets [va, vb) relative to d0
     const uint64_t va = align_up16(lo) - d0;
     const uint64_t vb = align_down16(hi) - d0;
-    if (va < vb) {
-      const uint64_t nv = (vb - va) >> 4;
-      for (uint64_t j0 = threadIdx.x; j0 < nv; j0 += (uint64_t)kBlock * kUnroll) {
-        f32x4 acc[kUnroll];
-        for (uint32_t t = 0; t < jb.nsrc; ++t) {
-          const uint64_t sa = ptr[jb.src0 + t] + va;
-          const uint32_t r = (uint32_t)(sa & 15u);
-          const gvec* __restrict__ s = gptr<u32x4>(sa - r);
-          u32x4 v[kUnroll] = {};
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t q = j0 + (uint64_t)u * kBlock;
-            if (q < nv) v[u] = load_shifted(s, q, r);
-          }
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) acc[u] = (t == 0) ? as_f4(v[u]) : acc[u] + as_f4(v[u]);
-        }
-        if (avg) {
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            acc[u].x = scale_avg(acc[u].x, nf, inv, pow2);
-            acc[u].y = scale_avg(acc[u].y, nf, inv, pow2);
-            acc[u].z = scale_avg(acc[u].z, nf, inv, pow2);
-            acc[u].w = scale_avg(acc[u].w, nf, inv, pow2);
-          }
-        }
-        for (uint32_t m = 0; m < jb.ndst; ++m) {
-          gvec* __restrict__ d = gptr<u32x4>(ptr[jb.dst0 + m] + va);
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t q = j0 + (uint64_t)u * kBlock;
-            if (q < nv) d[q] = as_u4(acc[u]);
-          }
-        }
-      }
-    }
+    if (va < vb) reduce_vectors<K>(jb, ptr, va, (vb - va) >> 4, avg, nf);
+
     // elements of the vectors cut by the window start and the job end
     const uint64_t e0 = lo - d0;
     const uint64_t e_head = (align_up16(lo) < hi ? align_up16(lo) : hi) - d0;
@@ -299,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
         const float v = *gptr<float>(ptr[jb.src0 + t] + x);
         acc = (t == 0) ? v : acc + v;
       }
-      if (avg) acc = scale_avg(acc, nf, inv, pow2);
+      if (avg) acc = acc / nf;
       for (uint32_t m = 0; m < jb.ndst; ++m) *gptr<float>(ptr[jb.dst0 + m] + x) = acc;
     }
   }
@@ -326,14 +485,20 @@ int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, 
   return (int)hipGetLastError();
 }
 
-int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint64_t n_chunks,
+int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
   // the pointer array follows the jobs, 8-byte aligned (24 * n_job is a multiple of 8)
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
-  hipLaunchKernelGGL(reduce_kernel, grid, block, 0, static_cast<hipStream_t>(stream), begin, jobs,
-                     ptr, n_job, n_chunks, chunk_shift, avg);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (n_src) {
+    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: hipLaunchKernelGGL(reduce_kernel<0>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+  }
   return (int)hipGetLastError();
 }

@@ -54,6 +54,7 @@ extern "C++" {
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
                          uint64_t n_chunks, uint32_t chunk_shift, uint32_t max_grid,
                          void* stream);
-int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint64_t n_chunks,
+// Every job of one launch has the same operand count n_src.
+int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, void* stream);
 }

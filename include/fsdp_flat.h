@@ -4,7 +4,10 @@
  * One bucket of P parameters, sharded on dim 0 over a shard group of S ranks
  * and replicated over D = R / S replicate groups, R simulated ranks resident
  * in one GPU's HBM.  Every device entry point is one HIP kernel launch,
- * enqueued on the caller's stream; none of them synchronises the host.
+ * enqueued on the caller's stream.  A call whose descriptor table (a
+ * function of its shapes, sizes and pointers) is new uploads that table
+ * once with a blocking copy; a repeated call makes no HIP call besides the
+ * launch and does not synchronise the host.
  *
  * Sources (cited by page title and section):
  *   [FS-MD]  FullyShard multi-dimensional parallel adaptation RFC
@@ -44,7 +47,8 @@
  *   - Padding is written as zero on every call; no output needs to be
  *     cleared beforehand.
  *   - The library keeps a cache of device-resident descriptor tables keyed
- *     by the call's shapes and pointers; fsdp_release_cache() frees it.
+ *     by the call's shapes and pointers (at most 128; evicting waits for
+ *     the device); fsdp_release_cache() frees it.
  *   - Thread safe; calls that overlap in time on different streams must not
  *     share output buffers.
  */

@@ -52,12 +52,13 @@ class Guarded:
 def bits(t: torch.Tensor) -> np.ndarray:
     """Bit pattern of a tensor (device or host) as a numpy integer array."""
     it, nt, _ = _INT[t.dtype]
-    return t.detach().contiguous().view(it).cpu().numpy()
+    return t.detach().contiguous().view(it).cpu().numpy().reshape(-1)
 
 
 def np_bits(a: np.ndarray) -> np.ndarray:
     """Bit pattern of an oracle array (float32 or the uint16 bits of a
     16-bit type) as the same integer type bits() returns."""
+    a = np.ascontiguousarray(a).reshape(-1)
     if a.dtype == np.float32:
         return a.view(np.int32)
     if a.dtype == np.uint16:

@@ -48,7 +48,7 @@ def _fetcher(tensors):
 
 def _gpu_vals(t, pos):
     idx = torch.from_numpy(np.asarray(pos, dtype=np.int64)).cuda()
-    return bits(t[idx])
+    return bits(t.reshape(-1)[idx])
 
 
 @pytest.mark.parametrize("wname", ["llama7b_4layer_r8_s8", "ragged_heavy_r8_s8"])
@@ -89,8 +89,8 @@ def test_full_size_sampled(wname):
 
     # --- AG copy-out: the round trip is exact on every element -----------
     for i in range(P):
-        assert torch.equal(fb.full[i].view(torch.int16 if np_dtype == np.uint16 else torch.int32),
-                           params[i].reshape(-1).view(torch.int16 if np_dtype == np.uint16 else torch.int32)), \
+        it = torch.int16 if np_dtype == np.uint16 else torch.int32
+        assert torch.equal(fb.full[i].reshape(-1).view(it), params[i].reshape(-1).view(it)), \
             f"ag_copy_out param {i} differs from the parameter"
         n = fb.full[i].numel()
         if n:

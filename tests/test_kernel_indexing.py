@@ -329,3 +329,68 @@ def test_find_item_all_chunks():
         for c in list(range(0, min(total, 300))) + list(range(max(0, total - 300), total)):
             j = find_item(begin, n, c)
             assert begin[j] <= c and (j + 1 == n or c < begin[j + 1])
+
+
+# ---------------------------------------------------------------------------
+# per-lane loops inside one window (copy_run / reduce_run)
+# ---------------------------------------------------------------------------
+
+def lane_loop(nv, U, shifted, block=256):
+    """Vectors written and source blocks read by every lane, following the
+    kernels' loops: whole iterations of block*U vectors (wave-contiguous
+    groups of 64 when the source is shifted, block-strided otherwise), then
+    a block-strided tail.  Returns (writes, reads) as lists of
+    (thread, index)."""
+    writes, reads = [], []
+    base = 0
+    while base + block * U <= nv:
+        for tid in range(block):
+            lane, wave = tid & 63, tid >> 6
+            if shifted:
+                wb = base + wave * 64 * U
+                for u in range(U):
+                    writes.append((tid, wb + u * 64 + lane))
+                    reads.append((tid, wb + u * 64 + lane))
+                reads.append((tid, wb + 64 * U))  # the wave-uniform closing block
+            else:
+                for u in range(U):
+                    writes.append((tid, base + tid + u * block))
+                    reads.append((tid, base + tid + u * block))
+        base += block * U
+    for tid in range(block):
+        j = base + tid
+        while j < nv:
+            writes.append((tid, j))
+            reads.append((tid, j))
+            if shifted:
+                reads.append((tid, j + 1))
+            j += block
+    return writes, reads
+
+
+@pytest.mark.parametrize("U", [1, 2, 4, 8])
+@pytest.mark.parametrize("shifted", [False, True])
+def test_lane_loops_cover_each_vector_once(U, shifted):
+    for nv in (0, 1, 63, 64, 255, 256, 257, 511, 1024, 1025, 2048, 3000, 4096):
+        writes, reads = lane_loop(nv, U, shifted)
+        idx = sorted(v for _, v in writes)
+        assert idx == list(range(nv)), (nv, U, shifted)
+        top = nv if shifted else nv - 1  # a shifted source may read block nv
+        assert all(0 <= r <= top for _, r in reads), (nv, U, shifted)
+
+
+def test_realign_neighbour_is_next_block():
+    """Lane l of group u needs block wb + 64u + l + 1: lanes 0..62 take it
+    from lane l+1 of the same group, lane 63 from lane 0 of group u+1 or
+    from the closing block."""
+    for U in (1, 2, 4):
+        wb = 1000
+        blocks = {(u, l): wb + u * 64 + l for u in range(U) for l in range(64)}
+        tail = wb + 64 * U
+        for u in range(U):
+            for l in range(64):
+                if l < 63:
+                    got = blocks[(u, (l + 1) & 63)]
+                else:
+                    got = blocks[(u + 1, 0)] if u + 1 < U else tail
+                assert got == blocks[(u, l)] + 1
