@@ -16,8 +16,10 @@ written, never read as a copy source):
   AG copy-in   sum(N_i) e + S I e         AG copy-out  2 sum(N_i) e
   RS copy-in   4 R (sum(N_i) + S I)       RS reduce    4 R S I + 4 R I
   fused AR     8 R F
-Timing: W untimed steps, then K steps between synchronisations; HIP events
-on the launch stream around every step give each kernel's average time.
+Timing: W untimed steps, then K steps between synchronisations (the value);
+inside them HIP events on the launch stream around the dominant kernel (found
+on a few untimed steps) give its average launch time (the roofline); a
+separate pass afterwards gives every step's time (the "ops" breakdown).
 The CPU oracle is timed on a bounded number of whole steps of the same
 workload (cpu_baseline).
 
@@ -42,8 +44,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kernel",
                   "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
                   "fused_ar": "reduce_kernel"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
+# the kernels and the planner that sets their launch shapes (chunk sizes)
+KERNEL_SRC = [os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", f)
+              for f in ("kernels.hip", "fsdp_flat.cpp", "plan.hpp")]
 
 
 def log(msg: str) -> None:
@@ -51,8 +55,11 @@ def log(msg: str) -> None:
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRC:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def step_bytes(w, lay, F: int):
@@ -76,12 +83,12 @@ def _numel(shape):
     return n
 
 
-def measured_traffic(step: str, launches_bytes: int):
+def measured_traffic(workload: str, step: str):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 PMC summary, or None when absent or when the kernel source has
     changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -125,6 +132,42 @@ class PureTPRunner:
 
     def step(self, stream=None):
         self.call(stream)
+
+
+def per_step_us(runner, steps, n):
+    """Average duration (us) of every step over n passes, from HIP events
+    recorded on the launch stream around each launch."""
+    import torch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        for j, name in enumerate(steps):
+            ev[k][j][0].record()
+            runner.run(name)
+            ev[k][j][1].record()
+    torch.cuda.synchronize()
+    return {name: sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(n)) / n * 1e3
+            for j, name in enumerate(steps)}
+
+
+def calibration_copy(mib: int, reps: int) -> None:
+    """A plain copy of known size for calibrating the HBM byte counters: the
+    copy kernel on one aligned fp32 segment (AG copy-out with one shard), so
+    each launch reads and writes exactly mib MiB."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    n = mib * (1 << 20) // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    call = hp.prepare("fsdp_ag_copy_out", [(n,)], 1, a, [b])
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    print(json.dumps({"calibration_copy": {"bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                                           "launches": reps, "grid": -(-4 * n // (1 << 14))}}), flush=True)
 
 
 def cpu_baseline(w, seconds: float, op: str):
@@ -196,6 +239,8 @@ def main():
     ap.add_argument("--workload", default="hsdp_block_h1024_r8_s4_d2")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -211,6 +256,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibration_copy:
+        calibration_copy(args.calibration_copy, max(1, args.steps))
+        return
     w = W.WORKLOADS[args.workload]
     R, S, D = w.rank_size, w.shard_size, w.dp_size
     op = w.reduce_ops[0]
@@ -236,43 +284,55 @@ def main():
         runner.step()
     torch.cuda.synchronize()
 
+    # a few untimed steps with events around every step find the dominant
+    # kernel; the timed region then records events around that one only
+    probe = per_step_us(runner, steps, max(3, args.warmup))
+    dom = max(steps, key=probe.get)
+
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
-          for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(K):
-        for j, name in enumerate(steps):
-            ev[k][j][0].record()
-            runner.run(name)
-            ev[k][j][1].record()
+        for name in steps:
+            if name == dom:
+                ev[k][0].record()
+                runner.run(name)
+                ev[k][1].record()
+            else:
+                runner.run(name)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
     value = bytes_per_step * K / (total_ms * 1e-3) / 1e9
+    dom_us = sum(a.elapsed_time(b) for a, b in ev) / K * 1e3
 
+    # per-step breakdown, measured after the timed region (events around
+    # every step perturb the whole-step time, so they stay out of it)
+    after = per_step_us(runner, steps, K)
     ops = {}
-    for j, name in enumerate(steps):
-        us = sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(K)) / K * 1e3
+    for name in steps:
+        us = after[name]
         gbs = nbytes[name] / (us * 1e-6) / 1e9
         ops[name] = {"kernel": KERNEL_OF_STEP[name], "bytes": nbytes[name], "us": round(us, 2),
                      "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"  {name:12s} {nbytes[name] / 1e6:10.1f} MB  {us:9.1f} us  {gbs:8.1f} GB/s  "
             f"{100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
-    dom = max(steps, key=lambda s: ops[s]["us"])
+    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": KERNEL_OF_STEP[dom], "step": dom,
-            "achieved": ops[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ops[dom]["GB/s"] / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dom, nbytes[dom])}
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, dom),
+            "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": round(dom_us, 2)}
     log(f"  step: {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s; wall {wall:.3f} s for {K} steps")
 
     cpu = None
     if not args.no_cpu_baseline:
-        n, el, F = cpu_baseline(w, args.cpu_seconds, op)
+        n, el, _ = cpu_baseline(w, args.cpu_seconds, op)
         cpu = {"value": round(bytes_per_step * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{n} whole steps of {w.name} (all {len(steps)} steps, full size) in {el:.1f} s; "
