@@ -178,6 +178,14 @@ struct Tuning {
   uint32_t copy_shift = 14;    // 16 KiB of destination per chunk
   uint32_t reduce_shift = 13;  // 8 KiB of destination per chunk
   uint32_t max_grid = 1u << 20;
+  // Store policy.  An output that the next step of the path reads back (the
+  // AG buffer read by copy-out, the RS input read by the RS, the RS output
+  // read by the fused AR) keeps normal stores while it is at most this many
+  // bytes, so that part of it is still in the 256 MB MALL when it is read;
+  // larger outputs, and the path's final outputs (the full parameters, the
+  // AR result), use nontemporal stores.  Measured on MI355X: streaming stores
+  // are 3-5% faster on multi-GB buckets and 8% slower on a 0.4 GB one.
+  uint64_t cached_store_max = uint64_t(512) << 20;
 };
 
 const Tuning& tuning() {
@@ -186,6 +194,7 @@ const Tuning& tuning() {
     if (const char* e = getenv("FSDP_COPY_CHUNK_SHIFT")) x.copy_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
     if (const char* e = getenv("FSDP_REDUCE_CHUNK_SHIFT")) x.reduce_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
     if (const char* e = getenv("FSDP_MAX_GRID")) x.max_grid = (uint32_t)std::max(1, atoi(e));
+    if (const char* e = getenv("FSDP_CACHED_STORE_MAX_MIB")) x.cached_store_max = uint64_t(std::max(0, atoi(e))) << 20;
     return x;
   }();
   return t;
@@ -282,8 +291,15 @@ void append(std::vector<uint8_t>& t, const T* p, size_t n) {
   t.insert(t.end(), b, b + n * sizeof(T));
 }
 
+enum class Reuse { kReadNext, kFinal };
+
+// Nontemporal stores for this output?  (the policy of Tuning::cached_store_max)
+bool stream_stores(Reuse reuse, uint64_t out_bytes) {
+  return reuse == Reuse::kFinal || out_bytes > tuning().cached_store_max;
+}
+
 // Launch the segmented copy over `segs` (empty segments already dropped).
-int run_copy(std::vector<fsdp::CopySeg>& segs, int es, hipStream_t stream) {
+int run_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream) {
   if (segs.empty()) return ok();
   const Tuning& tu = tuning();
   std::vector<uint64_t> begin(segs.size());
@@ -300,12 +316,16 @@ int run_copy(std::vector<fsdp::CopySeg>& segs, int es, hipStream_t stream) {
   void* dev = nullptr;
   int rc = get_table(std::move(table), &dev);
   if (rc) return rc;
-  int he = fsdp_launch_seg_copy(es, dev, (uint32_t)segs.size(), n, tu.copy_shift, tu.max_grid, stream);
+  uint64_t out_bytes = 0;
+  for (const auto& sg : segs) out_bytes += sg.total_bytes;
+  int he = fsdp_launch_seg_copy(es, dev, (uint32_t)segs.size(), n, tu.copy_shift, tu.max_grid,
+                                stream_stores(reuse, out_bytes), stream);
   if (he != hipSuccess) return fail(FSDP_EHIP, "seg_copy launch: %s", hipGetErrorString((hipError_t)he));
   return ok();
 }
 
-int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int avg, hipStream_t stream) {
+int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int avg, Reuse reuse,
+               hipStream_t stream) {
   if (jobs.empty()) return ok();
   const Tuning& tu = tuning();
   std::vector<uint64_t> begin(jobs.size());
@@ -321,8 +341,10 @@ int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int
   void* dev = nullptr;
   int rc = get_table(std::move(table), &dev);
   if (rc) return rc;
+  uint64_t out_bytes = 0;
+  for (const auto& jb : jobs) out_bytes += jb.nbytes * jb.ndst;
   int he = fsdp_launch_reduce(dev, (uint32_t)jobs.size(), jobs[0].nsrc, n, tu.reduce_shift, tu.max_grid,
-                              avg, stream);
+                              avg, stream_stores(reuse, out_bytes), stream);
   if (he != hipSuccess) return fail(FSDP_EHIP, "reduce launch: %s", hipGetErrorString((hipError_t)he));
   return ok();
 }
@@ -418,7 +440,7 @@ int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dty
     }
   }
   if ((rc = check_overlap({{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}, ins))) return rc;
-  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+  return run_copy(segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
@@ -447,7 +469,7 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
-  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+  return run_copy(segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
@@ -487,7 +509,7 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
     }
   }
   if ((rc = check_overlap(outs, ins))) return rc;
-  return run_copy(segs, es, static_cast<hipStream_t>(stream));
+  return run_copy(segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
@@ -526,7 +548,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
     ptrs.push_back((uint64_t)rs_out[g]);
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, op == FSDP_AVG, static_cast<hipStream_t>(stream));
+  return run_reduce(jobs, ptrs, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
@@ -561,7 +583,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
     jb.ndst = (uint32_t)D;
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, op == FSDP_AVG, static_cast<hipStream_t>(stream));
+  return run_reduce(jobs, ptrs, op == FSDP_AVG, Reuse::kFinal, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

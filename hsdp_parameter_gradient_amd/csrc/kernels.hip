@@ -35,12 +35,11 @@
 
 // Sources are read exactly once: nontemporal loads keep them from
 // displacing the outputs in L2 and MALL (measured faster on MI355X for every
-// op; nontemporal stores measured slower and stay off).
+// op).  Stores are nontemporal only when the planner asks (NTS): for the
+// path's final outputs and for outputs too large to be re-read from the
+// MALL; an output the next step reads back stays cacheable.
 #ifndef FSDP_NT_LOADS
 #define FSDP_NT_LOADS 1
-#endif
-#ifndef FSDP_NT_STORES
-#define FSDP_NT_STORES 0
 #endif
 #ifndef FSDP_COPY_UNROLL
 #define FSDP_COPY_UNROLL 4
@@ -71,8 +70,9 @@ __device__ __forceinline__ u32x4 ldv(const gvec* p) {
   if (FSDP_NT_LOADS) return __builtin_nontemporal_load(p);
   return *p;
 }
+template <bool NTS>
 __device__ __forceinline__ void stv(gvec* p, u32x4 v) {
-  if (FSDP_NT_STORES)
+  if (NTS)
     __builtin_nontemporal_store(v, p);
   else
     *p = v;
@@ -170,7 +170,7 @@ __device__ __forceinline__ u32x4 load_shifted(const gvec* __restrict__ s, uint64
 
 // nv destination vectors d[0..nv) from source blocks s[0..nv] realigned by
 // r = 4*Q + b bytes (Q = -1: aligned, s[0..nv) read directly).
-template <int Q>
+template <int Q, bool NTS>
 __device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __restrict__ s, uint64_t nv,
                                          uint32_t b) {
   constexpr int U = kCopyUnroll;
@@ -184,7 +184,7 @@ __device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __res
 #pragma unroll
       for (int u = 0; u < U; ++u) a[u] = ldv(s + j + u * kBlock);
 #pragma unroll
-      for (int u = 0; u < U; ++u) stv(d + j + u * kBlock, a[u]);
+      for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * kBlock, a[u]);
     } else {
       // each wave owns 64*U consecutive vectors; one extra uniform block
       // (the first of the next wave's range, at most block nv) closes it
@@ -194,42 +194,44 @@ __device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __res
       const u32x4 tail = s[wb + 64 * U];
       realign_groups<QQ, U>(a, tail, lane, b);
 #pragma unroll
-      for (int u = 0; u < U; ++u) stv(d + wb + u * 64 + lane, a[u]);
+      for (int u = 0; u < U; ++u) stv<NTS>(d + wb + u * 64 + lane, a[u]);
     }
   }
   for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
     const u32x4 a = ldv(s + j);
     if (Q >= 0) {
       const u32x4 c = ldv(s + j + 1);
-      stv(d + j, funnel<QQ>(a, c, b));
+      stv<NTS>(d + j, funnel<QQ>(a, c, b));
     } else {
-      stv(d + j, a);
+      stv<NTS>(d + j, a);
     }
   }
 }
 
 // nv destination vectors from dst (16-aligned), source bytes from src.
+template <bool NTS>
 __device__ __forceinline__ void copy_vectors(uint64_t dst, uint64_t src, uint64_t nv) {
   gvec* __restrict__ d = gptr<u32x4>(dst);
   const uint32_t r = (uint32_t)(src & 15u);
   const gvec* __restrict__ s = gptr<u32x4>(src - r);
   const uint32_t b = r & 3u;
   if (r == 0) {
-    copy_run<-1>(d, s, nv, 0);
+    copy_run<-1, NTS>(d, s, nv, 0);
     return;
   }
   switch (r >> 2) {
-    case 0: copy_run<0>(d, s, nv, b); break;
-    case 1: copy_run<1>(d, s, nv, b); break;
-    case 2: copy_run<2>(d, s, nv, b); break;
-    default: copy_run<3>(d, s, nv, b); break;
+    case 0: copy_run<0, NTS>(d, s, nv, b); break;
+    case 1: copy_run<1, NTS>(d, s, nv, b); break;
+    case 2: copy_run<2, NTS>(d, s, nv, b); break;
+    default: copy_run<3, NTS>(d, s, nv, b); break;
   }
 }
 
+template <bool NTS>
 __device__ __forceinline__ void zero_vectors(uint64_t dst, uint64_t nv) {
   gvec* __restrict__ d = gptr<u32x4>(dst);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (uint64_t j = threadIdx.x; j < nv; j += kBlock) stv(d + j, z);
+  for (uint64_t j = threadIdx.x; j < nv; j += kBlock) stv<NTS>(d + j, z);
 }
 
 template <typename T>
@@ -245,7 +247,7 @@ __device__ __forceinline__ void copy_partial(uint64_t a, uint64_t lo, uint64_t h
   }
 }
 
-template <typename T>
+template <typename T, bool NTS>
 __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __restrict__ begin,
                                                           const fsdp::CopySeg* __restrict__ segs,
                                                           uint32_t n_seg, uint64_t n_chunks,
@@ -265,11 +267,11 @@ __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __rest
     // whole vectors of data
     const uint64_t ca = align_up16(lo);
     const uint64_t cb = align_down16(hi < cend ? hi : cend);
-    if (ca < cb) copy_vectors(ca, sg.src + (ca - sg.dst), (cb - ca) >> 4);
+    if (ca < cb) copy_vectors<NTS>(ca, sg.src + (ca - sg.dst), (cb - ca) >> 4);
     // whole vectors of padding
     const uint64_t za = align_up16(lo > cend ? lo : cend);
     const uint64_t zb = align_down16(hi);
-    if (za < zb) zero_vectors(za, (zb - za) >> 4);
+    if (za < zb) zero_vectors<NTS>(za, (zb - za) >> 4);
     // vectors cut by the window start, the data/padding edge, the segment end
     if (threadIdx.x < 3) {
       const uint64_t a_lo = align_down16(lo);
@@ -301,7 +303,7 @@ __device__ __forceinline__ u32x4 operand(const gvec* __restrict__ s, uint64_t q,
   return load_shifted(s, q, r);
 }
 
-template <int U>
+template <int U, bool NTS>
 __device__ __forceinline__ void store_result(f32x4 (&acc)[U], const fsdp::RedJob& jb,
                                              const uint64_t* __restrict__ ptr, uint64_t va,
                                              uint64_t j, uint64_t stride, int avg, float nf) {
@@ -312,14 +314,14 @@ __device__ __forceinline__ void store_result(f32x4 (&acc)[U], const fsdp::RedJob
   for (uint32_t m = 0; m < jb.ndst; ++m) {
     gvec* __restrict__ d = gptr<u32x4>(ptr[jb.dst0 + m] + va);
 #pragma unroll
-    for (int u = 0; u < U; ++u) stv(d + j + u * stride, as_u4(acc[u]));
+    for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * stride, as_u4(acc[u]));
   }
 }
 
 // All destination vectors [0, nv) of one job window for a compile-time
 // operand count K: whole iterations of U vectors per lane with the K*U
 // operand loads in flight together, then a tail of single vectors.
-template <int K, int U, int MODE, int Q>
+template <int K, int U, int MODE, int Q, bool NTS>
 __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                            const uint64_t (&sb)[K], const uint32_t (&sr)[K], uint64_t va,
                                            uint64_t nv, int avg, float nf) {
@@ -360,7 +362,7 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
 #pragma unroll
       for (int t = 1; t < K; ++t) acc[u] = acc[u] + as_f4(v[t][u]);
     }
-    store_result<U>(acc, jb, ptr, va, j, stride, avg, nf);
+    store_result<U, NTS>(acc, jb, ptr, va, j, stride, avg, nf);
   }
   for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
     u32x4 v[K];
@@ -369,7 +371,7 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
     f32x4 acc[1] = {as_f4(v[0])};
 #pragma unroll
     for (int t = 1; t < K; ++t) acc[0] = acc[0] + as_f4(v[t]);
-    store_result<1>(acc, jb, ptr, va, j, kBlock, avg, nf);
+    store_result<1, NTS>(acc, jb, ptr, va, j, kBlock, avg, nf);
   }
 }
 
@@ -377,7 +379,7 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
 // va + 16 q of every destination, operand t read at the same offset of its
 // source.  K > 0: compile-time operand count; K == 0: any count, one
 // operand at a time.
-template <int K>
+template <int K, bool NTS>
 __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                uint64_t va, uint64_t nv, int avg, float nf) {
   if constexpr (K > 0) {
@@ -393,16 +395,16 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
       same = same && sr[t] == sr[0];
     }
     if (same && sr[0] == 0) {
-      reduce_run<K, U, 0, 0>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     } else if (same) {
       switch (sr[0] >> 2) {
-        case 0: reduce_run<K, U, 1, 0>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 1: reduce_run<K, U, 1, 1>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 2: reduce_run<K, U, 1, 2>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        default: reduce_run<K, U, 1, 3>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 0: reduce_run<K, U, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 1: reduce_run<K, U, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 2: reduce_run<K, U, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        default: reduce_run<K, U, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
       }
     } else {
-      reduce_run<K, U, 2, 0>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<K, U, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     }
   } else {
     for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
@@ -413,12 +415,12 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
         const f32x4 v = as_f4(load_shifted(gptr<u32x4>(sa - r), j, r));
         acc[0] = (t == 0) ? v : acc[0] + v;
       }
-      store_result<1>(acc, jb, ptr, va, j, kBlock, avg, nf);
+      store_result<1, NTS>(acc, jb, ptr, va, j, kBlock, avg, nf);
     }
   }
 }
 
-template <int K>
+template <int K, bool NTS>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restrict__ begin,
                                                         const fsdp::RedJob* __restrict__ jobs,
                                                         const uint64_t* __restrict__ ptr,
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     // whole vectors: offsets [va, vb) relative to d0
     const uint64_t va = align_up16(lo) - d0;
     const uint64_t vb = align_down16(hi) - d0;
-    if (va < vb) reduce_vectors<K>(jb, ptr, va, (vb - va) >> 4, avg, nf);
+    if (va < vb) reduce_vectors<K, NTS>(jb, ptr, va, (vb - va) >> 4, avg, nf);
 
     // elements of the vectors cut by the window start and the job end
     const uint64_t e0 = lo - d0;
@@ -471,34 +473,51 @@ inline uint32_t grid_for(uint64_t n_chunks, uint32_t max_grid) {
 }  // namespace
 
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, uint64_t n_chunks,
-                         uint32_t chunk_shift, uint32_t max_grid, void* stream) {
+                         uint32_t chunk_shift, uint32_t max_grid, int stream_stores, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::CopySeg* segs = reinterpret_cast<const fsdp::CopySeg*>(begin + n_seg);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (elem_bytes == 4)
-    hipLaunchKernelGGL(seg_copy_kernel<uint32_t>, grid, block, 0, st, begin, segs, n_seg, n_chunks,
-                       chunk_shift);
-  else
-    hipLaunchKernelGGL(seg_copy_kernel<uint16_t>, grid, block, 0, st, begin, segs, n_seg, n_chunks,
-                       chunk_shift);
+  if (elem_bytes == 4) {
+    if (stream_stores)
+      hipLaunchKernelGGL((seg_copy_kernel<uint32_t, true>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+    else
+      hipLaunchKernelGGL((seg_copy_kernel<uint32_t, false>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+  } else {
+    if (stream_stores)
+      hipLaunchKernelGGL((seg_copy_kernel<uint16_t, true>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+    else
+      hipLaunchKernelGGL((seg_copy_kernel<uint16_t, false>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+  }
   return (int)hipGetLastError();
 }
 
+namespace {
+template <bool NTS>
+void launch_reduce_k(uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
+                     const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
+                     uint32_t chunk_shift, int avg) {
+  switch (n_src) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: hipLaunchKernelGGL((reduce_kernel<0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+  }
+}
+}  // namespace
+
 int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
-                       uint32_t chunk_shift, uint32_t max_grid, int avg, void* stream) {
+                       uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
   // the pointer array follows the jobs, 8-byte aligned (24 * n_job is a multiple of 8)
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (n_src) {
-    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    default: hipLaunchKernelGGL(reduce_kernel<0>, grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-  }
+  if (stream_stores)
+    launch_reduce_k<true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  else
+    launch_reduce_k<false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
   return (int)hipGetLastError();
 }

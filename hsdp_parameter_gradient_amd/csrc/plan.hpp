@@ -51,10 +51,13 @@ inline uint64_t chunk_count(uint64_t dst, uint64_t nbytes, uint32_t shift) {
 
 // Launchers (defined in kernels.hip).  Return hipSuccess or the launch error.
 extern "C++" {
+// stream_stores: nontemporal stores for the outputs (see the store policy in
+// fsdp_flat.cpp).
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
                          uint64_t n_chunks, uint32_t chunk_shift, uint32_t max_grid,
-                         void* stream);
+                         int stream_stores, void* stream);
 // Every job of one launch has the same operand count n_src.
 int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
-                       uint32_t chunk_shift, uint32_t max_grid, int avg, void* stream);
+                       uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores,
+                       void* stream);
 }
