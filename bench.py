@@ -43,7 +43,7 @@ METRIC = "effective HBM GB/s (and % of peak) for AG copy-in/out + RS/AR reduce p
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kernel",
                   "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
-                  "fused_ar": "reduce_kernel"}
+                  "rs_copy_reduce": "reduce_kernel", "fused_ar": "reduce_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
 # the kernels and the planner that sets their launch shapes (chunk sizes)
 KERNEL_SRC = [os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", f)
@@ -72,6 +72,7 @@ def step_bytes(w, lay, F: int):
         "ag_copy_out": 2 * N * e,
         "rs_copy_in": 4 * R * (N + S * I),
         "rs_reduce": 4 * R * S * I + 4 * R * I,
+        "rs_copy_reduce": 4 * R * N + 4 * R * I,
         "fused_ar": 8 * R * F,
     }
 
@@ -330,6 +331,30 @@ def main():
             "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": round(dom_us, 2)}
     log(f"  step: {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s; wall {wall:.3f} s for {K} steps")
 
+    # the same pass with RS copy-in fused into the RS (the RS input is never
+    # materialised): reported beside the contract's step, not instead of it
+    variants = {}
+    if isinstance(runner, hp.FlatBucket):
+        fsteps = runner.steps(fused_rs=True)
+        for _ in range(args.warmup):
+            runner.step(fused_rs=True)
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        fs.record()
+        for _ in range(K):
+            runner.step(fused_rs=True)
+        fe.record()
+        torch.cuda.synchronize()
+        f_ms = fs.elapsed_time(fe) / K
+        f_us = per_step_us(runner, ["rs_copy_reduce"], K)["rs_copy_reduce"]
+        b = nbytes["rs_copy_reduce"]
+        variants["fused_rs_copy_reduce"] = {
+            "steps_per_pass": fsteps, "ms_per_step": round(f_ms, 4),
+            "rs_copy_reduce": {"bytes": b, "us": round(f_us, 2), "GB/s": round(b / (f_us * 1e-6) / 1e9, 1)},
+            "note": "RS input never written; results identical to rs_copy_in + rs_reduce"}
+        log(f"  fused RS variant: step {f_ms * 1e3:.1f} us (vs {ms_per_step * 1e3:.1f}); rs_copy_reduce "
+            f"{f_us:.1f} us, {b / (f_us * 1e-6) / 1e9:.1f} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         n, el, _ = cpu_baseline(w, args.cpu_seconds, op)
@@ -351,6 +376,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "ops": ops,
+        "variants": variants,
     }
     print(json.dumps(out), flush=True)
 

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "fsdp_rs_copy_in": [B, c_int32, c_int32, c_int32, POINTER(c_void_p), POINTER(c_void_p), c_void_p],
             "fsdp_rs_reduce": [B, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p),
                                POINTER(c_void_p), c_void_p],
+            "fsdp_rs_copy_reduce": [B, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p),
+                                    POINTER(c_void_p), c_void_p],
             "fsdp_fused_ar": [c_int32, P64, c_int32, c_int32, c_int32, c_int32, c_int32,
                               POINTER(c_void_p), c_void_p],
         }
@@ -248,27 +250,53 @@ def _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in):
                  (b, garr, rarr, tuple(grads), tuple(rs_in)))
 
 
+_REDUCE_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _reduce_dtype(tensors, what) -> torch.dtype:
+    dt = tensors[0].dtype if len(tensors) else torch.float32
+    if dt not in _REDUCE_DTYPES:
+        raise ValueError(f"{what}: reductions take float32 or bfloat16, not {dt}")
+    return dt
+
+
 def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out):
     b = _BucketArg(shapes)
     lay = fsdp_bucket_layout(b.shapes, shard_size)
     R, S = int(rank_size), int(shard_size)
     if len(rs_in) != R or len(rs_out) != R:
         raise ValueError(f"rs_in / rs_out: {len(rs_in)} / {len(rs_out)} tensors, expected {R}")
-    iarr = _ptr_array([_dev(rs_in[g], f"rs_in[{g}]", S * lay.I, torch.float32) for g in range(R)])
-    oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, torch.float32) for g in range(R)])
-    return _Call("fsdp_rs_reduce", (b.ref, R, S, int(dp_size), _OPS[op], 0, iarr, oarr),
+    dt = _reduce_dtype(rs_in, "rs_in")
+    iarr = _ptr_array([_dev(rs_in[g], f"rs_in[{g}]", S * lay.I, dt) for g in range(R)])
+    oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, dt) for g in range(R)])
+    return _Call("fsdp_rs_reduce", (b.ref, R, S, int(dp_size), _OPS[op], _dtype_code(dt), iarr, oarr),
                  (b, iarr, oarr, tuple(rs_in), tuple(rs_out)))
+
+
+def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out):
+    b = _BucketArg(shapes)
+    lay = fsdp_bucket_layout(b.shapes, shard_size)
+    R, S, P = int(rank_size), int(shard_size), len(b.shapes)
+    if len(grads) != R * P or len(rs_out) != R:
+        raise ValueError(f"grads: {len(grads)} (expected R*P = {R * P}), rs_out: {len(rs_out)} (expected {R})")
+    dt = _reduce_dtype(rs_out, "rs_out")
+    garr = _ptr_array([_dev(grads[g * P + i], f"grads[{g * P + i}]", _numel(b.shapes[i]), dt)
+                       for g in range(R) for i in range(P)])
+    oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, dt) for g in range(R)])
+    return _Call("fsdp_rs_copy_reduce", (b.ref, R, S, int(dp_size), _OPS[op], _dtype_code(dt), garr, oarr),
+                 (b, garr, oarr, tuple(grads), tuple(rs_out)))
 
 
 def _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused):
     n = len(seg_numel)
     sizes = (c_int64 * max(n, 1))(*[int(v) for v in seg_numel])
-    _, F = fsdp_fused_layout(seg_numel, 4)
     R = int(rank_size)
     if len(fused) != R:
         raise ValueError(f"fused: {len(fused)} tensors, expected {R}")
-    arr = _ptr_array([_dev(fused[g], f"fused[{g}]", F, torch.float32) for g in range(R)])
-    return _Call("fsdp_fused_ar", (n, sizes, R, int(shard_size), int(dp_size), _OPS[op], 0, arr),
+    dt = _reduce_dtype(fused, "fused")
+    _, F = fsdp_fused_layout(seg_numel, dt.itemsize)
+    arr = _ptr_array([_dev(fused[g], f"fused[{g}]", F, dt) for g in range(R)])
+    return _Call("fsdp_fused_ar", (n, sizes, R, int(shard_size), int(dp_size), _OPS[op], _dtype_code(dt), arr),
                  (sizes, arr, tuple(fused)))
 
 
@@ -277,6 +305,7 @@ _PREP = {
     "fsdp_ag_copy_out": _prep_ag_copy_out,
     "fsdp_rs_copy_in": _prep_rs_copy_in,
     "fsdp_rs_reduce": _prep_rs_reduce,
+    "fsdp_rs_copy_reduce": _prep_rs_copy_reduce,
     "fsdp_fused_ar": _prep_fused_ar,
 }
 
@@ -310,6 +339,13 @@ def fsdp_rs_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, op: st
                    rs_in: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None) -> None:
     """Reduce-scatter within every shard group into rs_out[g] (I fp32 elements)."""
     _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out)(stream)
+
+
+def fsdp_rs_copy_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, op: str,
+                        grads: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None) -> None:
+    """RS copy-in and RS in one pass: reduce chunk s of every gradient over
+    each shard group straight into rs_out[g] (I elements, padding zero)."""
+    _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out)(stream)
 
 
 def fsdp_fused_ar(seg_numel, rank_size: int, shard_size: int, dp_size: int, op: str,

@@ -129,6 +129,11 @@ int elem_size(int32_t dtype) {
   }
 }
 
+// Element size of a reduction dtype: fp32, or bf16 summed in fp32.
+int reduce_elem_size(int32_t dtype) {
+  return dtype == FSDP_F32 ? 4 : dtype == FSDP_BF16 ? 2 : 0;
+}
+
 int check_groups(int32_t R, int32_t S) {
   if (R < 1 || S < 1) return fail(FSDP_EINVAL, "rank_size %d / shard_size %d must be >= 1", R, S);
   if (R % S != 0) return fail(FSDP_EINVAL, "rank_size %d is not a multiple of shard_size %d", R, S);
@@ -324,7 +329,7 @@ int run_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t 
   return ok();
 }
 
-int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int avg, Reuse reuse,
+int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg, Reuse reuse,
                hipStream_t stream) {
   if (jobs.empty()) return ok();
   const Tuning& tu = tuning();
@@ -343,7 +348,7 @@ int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int
   if (rc) return rc;
   uint64_t out_bytes = 0;
   for (const auto& jb : jobs) out_bytes += jb.nbytes * jb.ndst;
-  int he = fsdp_launch_reduce(dev, (uint32_t)jobs.size(), jobs[0].nsrc, n, tu.reduce_shift, tu.max_grid,
+  int he = fsdp_launch_reduce(es, dev, (uint32_t)jobs.size(), jobs[0].nsrc, n, tu.reduce_shift, tu.max_grid,
                               avg, stream_stores(reuse, out_bytes), stream);
   if (he != hipSuccess) return fail(FSDP_EHIP, "reduce launch: %s", hipGetErrorString((hipError_t)he));
   return ok();
@@ -519,16 +524,17 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
-  if (dtype != FSDP_F32) return fail(FSDP_ENOTIMPL, "rs_reduce takes fp32 only (dtype %d)", dtype);
+  const int es = reduce_elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "rs_reduce takes fp32 or bf16 (dtype %d)", dtype);
   Layout L;
   if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int32_t R = rank_size, S = shard_size;
-  const int64_t in_bytes = (int64_t)S * L.I * 4, out_bytes = L.I * 4;
+  const int64_t in_bytes = (int64_t)S * L.I * es, out_bytes = L.I * es;
   if (!rs_in || !rs_out) return fail(FSDP_EINVAL, "rs_in / rs_out array is NULL");
   std::vector<Span> outs, ins;
   for (int32_t g = 0; g < R; ++g) {
-    if ((rc = check_ptr(rs_in[g], in_bytes, 4, "rs_in", g))) return rc;
-    if ((rc = check_ptr(rs_out[g], out_bytes, 4, "rs_out", g))) return rc;
+    if ((rc = check_ptr(rs_in[g], in_bytes, es, "rs_in", g))) return rc;
+    if ((rc = check_ptr(rs_out[g], out_bytes, es, "rs_out", g))) return rc;
     ins.push_back({(uint64_t)rs_in[g], (uint64_t)rs_in[g] + (uint64_t)in_bytes, g});
     outs.push_back({(uint64_t)rs_out[g], (uint64_t)rs_out[g] + (uint64_t)out_bytes, g});
   }
@@ -539,7 +545,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
   for (int32_t g = 0; g < R; ++g) {
     const int32_t d = g / S, s = g % S;
     fsdp::RedJob jb;
-    jb.nbytes = (uint64_t)out_bytes;
+    jb.nbytes = jb.data_bytes = (uint64_t)out_bytes;
     jb.src0 = (uint32_t)ptrs.size();
     jb.nsrc = (uint32_t)S;
     for (int32_t t = 0; t < S; ++t) ptrs.push_back((uint64_t)rs_in[d * S + t] + (uint64_t)(s * out_bytes));
@@ -548,7 +554,60 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
     ptrs.push_back((uint64_t)rs_out[g]);
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+}
+
+int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+                        int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
+                        void* stream) {
+  int rc = check_groups(rank_size, shard_size);
+  if (rc) return rc;
+  if (dp_size != rank_size / shard_size)
+    return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
+  if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
+  const int es = reduce_elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "rs_copy_reduce takes fp32 or bf16 (dtype %d)", dtype);
+  Layout L;
+  if ((rc = make_layout(bucket, shard_size, &L))) return rc;
+  const int32_t R = rank_size, S = shard_size, P = L.P;
+  const int64_t out_bytes = L.I * es;
+  if (!rs_out) return fail(FSDP_EINVAL, "rs_out array is NULL");
+  if ((int64_t)R * P > 0 && !grads) return fail(FSDP_EINVAL, "grads array is NULL");
+  std::vector<Span> outs, ins;
+  for (int32_t g = 0; g < R; ++g) {
+    if ((rc = check_ptr(rs_out[g], out_bytes, es, "rs_out", g))) return rc;
+    outs.push_back({(uint64_t)rs_out[g], (uint64_t)rs_out[g] + (uint64_t)out_bytes, g});
+    for (int32_t i = 0; i < P; ++i) {
+      const void* gp = grads[(size_t)g * P + i];
+      if ((rc = check_ptr(gp, L.numel[i] * es, es, "grads", (long)g * P + i))) return rc;
+      ins.push_back({(uint64_t)gp, (uint64_t)gp + (uint64_t)(L.numel[i] * es), g * P + i});
+    }
+  }
+  if ((rc = check_overlap(outs, ins))) return rc;
+  // one job per (rank g, parameter i): rank g's region of parameter i is the
+  // sum over its shard group of chunk s of gradient i, then zeros
+  std::vector<fsdp::RedJob> jobs;
+  std::vector<uint64_t> ptrs;
+  for (int32_t g = 0; g < R; ++g) {
+    const int32_t d = g / S, s = g % S;
+    for (int32_t i = 0; i < P; ++i) {
+      if (L.padded[i] == 0) continue;
+      const int64_t row0 = L.row_off[(size_t)i * S + s] * L.inner[i] * es;
+      fsdp::RedJob jb;
+      jb.nbytes = (uint64_t)(L.padded[i] * es);
+      jb.data_bytes = (uint64_t)(L.row_len[(size_t)i * S + s] * L.inner[i] * es);
+      jb.src0 = (uint32_t)ptrs.size();
+      jb.nsrc = (uint32_t)S;
+      for (int32_t t = 0; t < S; ++t)
+        ptrs.push_back(jb.data_bytes ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + (uint64_t)row0 : 0);
+      jb.dst0 = (uint32_t)ptrs.size();
+      jb.ndst = 1;
+      ptrs.push_back((uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es));
+      jobs.push_back(jb);
+    }
+  }
+  if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
+  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
@@ -558,11 +617,12 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
-  if (dtype != FSDP_F32) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32 only (dtype %d)", dtype);
+  const int es = reduce_elem_size(dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32 or bf16 (dtype %d)", dtype);
   int64_t F = 0;
-  if ((rc = fsdp_fused_layout(n_seg, seg_numel, 4, nullptr, &F))) return rc;
+  if ((rc = fsdp_fused_layout(n_seg, seg_numel, es, nullptr, &F))) return rc;
   const int32_t R = rank_size, S = shard_size, D = dp_size;
-  const int64_t nbytes = F * 4;
+  const int64_t nbytes = F * es;
   if (!fused) return fail(FSDP_EINVAL, "fused array is NULL");
   std::vector<Span> outs;
   for (int32_t g = 0; g < R; ++g) {
@@ -575,7 +635,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
   std::vector<uint64_t> ptrs;
   for (int32_t s = 0; s < S; ++s) {
     fsdp::RedJob jb;
-    jb.nbytes = (uint64_t)nbytes;
+    jb.nbytes = jb.data_bytes = (uint64_t)nbytes;
     jb.src0 = (uint32_t)ptrs.size();
     jb.nsrc = (uint32_t)D;
     for (int32_t d = 0; d < D; ++d) ptrs.push_back((uint64_t)fused[d * S + s]);
@@ -583,7 +643,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
     jb.ndst = (uint32_t)D;
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, op == FSDP_AVG, Reuse::kFinal, static_cast<hipStream_t>(stream));
+  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kFinal, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

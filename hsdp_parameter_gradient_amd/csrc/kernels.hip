@@ -5,9 +5,13 @@
 //               padded rank slices), AG copy-out (unpack into the full
 //               parameters) and RS copy-in (chunk gradients into the padded
 //               rank-major RS input).  Bits are moved, never converted.
-//   reduce    — fixed-order fp32 reduction of K operands into M
-//               destinations: the RS of a shard group (K = S, M = 1) and the
-//               in-place fused AR of a replicate group (K = M = D).
+//   reduce    — fixed-order reduction, in fp32, of K operands into M
+//               destinations, with a zero-filled tail per job: the RS of a
+//               shard group (K = S, M = 1), the RS read straight from the
+//               full gradients (one job per parameter, its padding zero
+//               filled), and the in-place fused AR of a replicate group
+//               (K = M = D).  fp32 or bf16 elements (bf16 widened exactly,
+//               summed in fp32, rounded once to nearest even).
 //
 // Both are HBM-bound streaming kernels (no data reuse, no dense
 // contraction): one workgroup of 256 lanes handles one chunk of destination
@@ -26,10 +30,12 @@
 // rank order, the accumulator starting from the first operand, in IEEE
 // fp32 with denormals preserved; AVG divides the sum by the operand count
 // with a correctly rounded division (for a power of two that is the exact
-// multiply by its reciprocal).
+// multiply by its reciprocal); bf16 results are rounded once, at the store.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "plan.hpp"
 
@@ -294,6 +300,56 @@ __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __rest
 __device__ __forceinline__ f32x4 as_f4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
 __device__ __forceinline__ u32x4 as_u4(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
 
+// float32 -> bfloat16 bits, round to nearest, ties to even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
+}
+
+// The values of one 16-byte vector in float32: 4 fp32 (ES = 4) or 8 bf16
+// widened exactly (ES = 2).  bf16 element 2i is the low half of dword i.
+template <int ES>
+struct Acc {
+  static constexpr int N = ES == 4 ? 1 : 2;
+  f32x4 v[N];
+};
+
+template <int ES>
+__device__ __forceinline__ Acc<ES> widen(u32x4 w) {
+  Acc<ES> a;
+  if constexpr (ES == 4) {
+    a.v[0] = as_f4(w);
+  } else {
+    const uint32_t hi = 0xffff0000u;
+    a.v[0] = as_f4(u32x4{w.x << 16, w.x & hi, w.y << 16, w.y & hi});
+    a.v[1] = as_f4(u32x4{w.z << 16, w.z & hi, w.w << 16, w.w & hi});
+  }
+  return a;
+}
+
+template <int ES>
+__device__ __forceinline__ void accumulate(Acc<ES>& a, u32x4 w) {
+  const Acc<ES> b = widen<ES>(w);
+#pragma unroll
+  for (int i = 0; i < Acc<ES>::N; ++i) a.v[i] = a.v[i] + b.v[i];
+}
+
+template <int ES>
+__device__ __forceinline__ u32x4 narrow(Acc<ES>& a, int avg, float nf) {
+  if (avg) {
+#pragma unroll
+    for (int i = 0; i < Acc<ES>::N; ++i) a.v[i] = a.v[i] / nf;
+  }
+  if constexpr (ES == 4) {
+    return as_u4(a.v[0]);
+  } else {
+    const f32x4 l = a.v[0], h = a.v[1];
+    return u32x4{bf16_rne(l.x) | (bf16_rne(l.y) << 16), bf16_rne(l.z) | (bf16_rne(l.w) << 16),
+                 bf16_rne(h.x) | (bf16_rne(h.y) << 16), bf16_rne(h.z) | (bf16_rne(h.w) << 16)};
+  }
+}
+
 // Operand vector q: MODE 0 aligned, MODE 1 shifted by r = 4*Q + b bytes
 // (compile-time dword shift), MODE 2 any shift r.
 template <int MODE, int Q>
@@ -304,24 +360,20 @@ __device__ __forceinline__ u32x4 operand(const gvec* __restrict__ s, uint64_t q,
 }
 
 template <int U, bool NTS>
-__device__ __forceinline__ void store_result(f32x4 (&acc)[U], const fsdp::RedJob& jb,
-                                             const uint64_t* __restrict__ ptr, uint64_t va,
-                                             uint64_t j, uint64_t stride, int avg, float nf) {
-  if (avg) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = acc[u] / nf;
-  }
+__device__ __forceinline__ void store_vectors(const u32x4 (&o)[U], const fsdp::RedJob& jb,
+                                              const uint64_t* __restrict__ ptr, uint64_t va, uint64_t j,
+                                              uint64_t stride) {
   for (uint32_t m = 0; m < jb.ndst; ++m) {
     gvec* __restrict__ d = gptr<u32x4>(ptr[jb.dst0 + m] + va);
 #pragma unroll
-    for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * stride, as_u4(acc[u]));
+    for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * stride, o[u]);
   }
 }
 
-// All destination vectors [0, nv) of one job window for a compile-time
-// operand count K: whole iterations of U vectors per lane with the K*U
-// operand loads in flight together, then a tail of single vectors.
-template <int K, int U, int MODE, int Q, bool NTS>
+// All data vectors [0, nv) of one job window for a compile-time operand
+// count K: whole iterations of U vectors per lane with the K*U operand loads
+// in flight together, then a tail of single vectors.
+template <int ES, int K, int U, int MODE, int Q, bool NTS>
 __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                            const uint64_t (&sb)[K], const uint32_t (&sr)[K], uint64_t va,
                                            uint64_t nv, int avg, float nf) {
@@ -355,35 +407,37 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
 #pragma unroll
         for (int u = 0; u < U; ++u) v[t][u] = operand<MODE, Q>(gptr<u32x4>(sb[t]), j + u * kBlock, sr[t], b);
     }
-    f32x4 acc[U];
+    u32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      acc[u] = as_f4(v[0][u]);
+      Acc<ES> acc = widen<ES>(v[0][u]);
 #pragma unroll
-      for (int t = 1; t < K; ++t) acc[u] = acc[u] + as_f4(v[t][u]);
+      for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t][u]);
+      o[u] = narrow<ES>(acc, avg, nf);
     }
-    store_result<U, NTS>(acc, jb, ptr, va, j, stride, avg, nf);
+    store_vectors<U, NTS>(o, jb, ptr, va, j, stride);
   }
   for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
     u32x4 v[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) v[t] = operand<(MODE == 1 ? 2 : MODE), Q>(gptr<u32x4>(sb[t]), j, sr[t], b);
-    f32x4 acc[1] = {as_f4(v[0])};
+    Acc<ES> acc = widen<ES>(v[0]);
 #pragma unroll
-    for (int t = 1; t < K; ++t) acc[0] = acc[0] + as_f4(v[t]);
-    store_result<1, NTS>(acc, jb, ptr, va, j, kBlock, avg, nf);
+    for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t]);
+    const u32x4 o[1] = {narrow<ES>(acc, avg, nf)};
+    store_vectors<1, NTS>(o, jb, ptr, va, j, kBlock);
   }
 }
 
-// Whole vectors of one job window: destination vector q at byte offset
+// Data vectors of one job window: destination vector q at byte offset
 // va + 16 q of every destination, operand t read at the same offset of its
-// source.  K > 0: compile-time operand count; K == 0: any count, one
-// operand at a time.
-template <int K, bool NTS>
+// source.  K > 0: compile-time operand count; K == 0: any count, one operand
+// at a time.
+template <int ES, int K, bool NTS>
 __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                uint64_t va, uint64_t nv, int avg, float nf) {
   if constexpr (K > 0) {
-    constexpr int U = K >= 4 ? 2 : 4;
+    constexpr int U = (K >= 4 || ES == 2) ? 2 : 4;
     uint64_t sb[K];
     uint32_t sr[K];
     bool same = true;
@@ -395,32 +449,62 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
       same = same && sr[t] == sr[0];
     }
     if (same && sr[0] == 0) {
-      reduce_run<K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<ES, K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     } else if (same) {
       switch (sr[0] >> 2) {
-        case 0: reduce_run<K, U, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 1: reduce_run<K, U, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 2: reduce_run<K, U, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        default: reduce_run<K, U, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 0: reduce_run<ES, K, U, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 1: reduce_run<ES, K, U, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 2: reduce_run<ES, K, U, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        default: reduce_run<ES, K, U, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
       }
     } else {
-      reduce_run<K, U, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<ES, K, U, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     }
   } else {
     for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
-      f32x4 acc[1];
+      Acc<ES> acc;
       for (uint32_t t = 0; t < jb.nsrc; ++t) {
         const uint64_t sa = ptr[jb.src0 + t] + va;
         const uint32_t r = (uint32_t)(sa & 15u);
-        const f32x4 v = as_f4(load_shifted(gptr<u32x4>(sa - r), j, r));
-        acc[0] = (t == 0) ? v : acc[0] + v;
+        const u32x4 w = load_shifted(gptr<u32x4>(sa - r), j, r);
+        if (t == 0)
+          acc = widen<ES>(w);
+        else
+          accumulate<ES>(acc, w);
       }
-      store_result<1, NTS>(acc, jb, ptr, va, j, kBlock, avg, nf);
+      const u32x4 o[1] = {narrow<ES>(acc, avg, nf)};
+      store_vectors<1, NTS>(o, jb, ptr, va, j, kBlock);
     }
   }
 }
 
-template <int K, bool NTS>
+// Elements [max(a, lo), min(a + 16, hi)) of the 16-byte vector at d0-relative
+// address a: reduced below the data end, zero above it.
+template <int ES>
+__device__ __forceinline__ void reduce_partial(uint64_t a, uint64_t lo, uint64_t hi, uint64_t cend,
+                                               const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
+                                               uint64_t d0, int avg, float nf) {
+  typedef typename std::conditional<ES == 4, uint32_t, uint16_t>::type T;
+  const uint64_t x0 = a > lo ? a : lo;
+  const uint64_t x1 = (a + 16) < hi ? (a + 16) : hi;
+  for (uint64_t x = x0; x < x1; x += ES) {
+    const uint64_t off = x - d0;
+    T out = 0;
+    if (x < cend) {
+      float acc = 0.0f;
+      for (uint32_t t = 0; t < jb.nsrc; ++t) {
+        const T w = *gptr<T>(ptr[jb.src0 + t] + off);
+        const float v = ES == 4 ? __builtin_bit_cast(float, (uint32_t)w) : __builtin_bit_cast(float, (uint32_t)w << 16);
+        acc = (t == 0) ? v : acc + v;
+      }
+      if (avg) acc = acc / nf;
+      out = ES == 4 ? (T)__builtin_bit_cast(uint32_t, acc) : (T)bf16_rne(acc);
+    }
+    for (uint32_t m = 0; m < jb.ndst; ++m) *gptr<T>(ptr[jb.dst0 + m] + off) = out;
+  }
+}
+
+template <int ES, int K, bool NTS>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restrict__ begin,
                                                         const fsdp::RedJob* __restrict__ jobs,
                                                         const uint64_t* __restrict__ ptr,
@@ -437,31 +521,30 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     const uint64_t lo = w0 > d0 ? w0 : d0;
     const uint64_t end = d0 + jb.nbytes;
     const uint64_t hi = (w0 + CH) < end ? (w0 + CH) : end;
+    const uint64_t cend = d0 + jb.data_bytes;
     const float nf = (float)jb.nsrc;
 
-    // whole vectors: offsets [va, vb) relative to d0
-    const uint64_t va = align_up16(lo) - d0;
-    const uint64_t vb = align_down16(hi) - d0;
-    if (va < vb) reduce_vectors<K, NTS>(jb, ptr, va, (vb - va) >> 4, avg, nf);
-
-    // elements of the vectors cut by the window start and the job end
-    const uint64_t e0 = lo - d0;
-    const uint64_t e_head = (align_up16(lo) < hi ? align_up16(lo) : hi) - d0;
-    const uint64_t e_tail = (align_down16(hi) > lo ? align_down16(hi) : lo) - d0;
-    const uint64_t e1 = hi - d0;
-    // head elements [e0, e_head), tail elements [max(e_tail, e_head), e1)
-    const uint64_t n_head = (e_head - e0) >> 2;
-    const uint64_t t0 = e_tail > e_head ? e_tail : e_head;
-    const uint64_t n_tail = (e1 - t0) >> 2;
-    if (threadIdx.x < n_head + n_tail) {
-      const uint64_t x = threadIdx.x < n_head ? e0 + 4u * threadIdx.x : t0 + 4u * (threadIdx.x - n_head);
-      float acc = 0.0f;
-      for (uint32_t t = 0; t < jb.nsrc; ++t) {
-        const float v = *gptr<float>(ptr[jb.src0 + t] + x);
-        acc = (t == 0) ? v : acc + v;
-      }
-      if (avg) acc = acc / nf;
-      for (uint32_t m = 0; m < jb.ndst; ++m) *gptr<float>(ptr[jb.dst0 + m] + x) = acc;
+    // whole vectors of data: offsets [va, vb) relative to d0
+    const uint64_t ca = align_up16(lo);
+    const uint64_t cb = align_down16(hi < cend ? hi : cend);
+    if (ca < cb) reduce_vectors<ES, K, NTS>(jb, ptr, ca - d0, (cb - ca) >> 4, avg, nf);
+    // whole vectors of padding (zero) in every destination
+    const uint64_t za = align_up16(lo > cend ? lo : cend);
+    const uint64_t zb = align_down16(hi);
+    if (za < zb) {
+      for (uint32_t m = 0; m < jb.ndst; ++m) zero_vectors<NTS>(ptr[jb.dst0 + m] + (za - d0), (zb - za) >> 4);
+    }
+    // vectors cut by the window start, the data/padding edge, the job end
+    if (threadIdx.x < 3) {
+      const uint64_t a_lo = align_down16(lo);
+      const uint64_t a_c = align_down16(cend);
+      const uint64_t a_hi = align_down16(hi);
+      const bool p_lo = (lo & 15) != 0;
+      const bool p_c = (cend & 15) != 0 && lo < cend && cend < hi && !(p_lo && a_c == a_lo);
+      const bool p_hi = (hi & 15) != 0 && !(p_lo && a_hi == a_lo) && !(p_c && a_hi == a_c);
+      if (threadIdx.x == 0 && p_lo) reduce_partial<ES>(a_lo, lo, hi, cend, jb, ptr, d0, avg, nf);
+      if (threadIdx.x == 1 && p_c) reduce_partial<ES>(a_c, lo, hi, cend, jb, ptr, d0, avg, nf);
+      if (threadIdx.x == 2 && p_hi) reduce_partial<ES>(a_hi, lo, hi, cend, jb, ptr, d0, avg, nf);
     }
   }
 }
@@ -493,31 +576,38 @@ int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, 
 }
 
 namespace {
-template <bool NTS>
+template <int ES, bool NTS>
 void launch_reduce_k(uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
                      const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
                      uint32_t chunk_shift, int avg) {
   switch (n_src) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    default: hipLaunchKernelGGL((reduce_kernel<0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 1: hipLaunchKernelGGL((reduce_kernel<ES, 1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<ES, 2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<ES, 4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<ES, 8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: hipLaunchKernelGGL((reduce_kernel<ES, 0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
   }
 }
 }  // namespace
 
-int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
+int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
-  // the pointer array follows the jobs, 8-byte aligned (24 * n_job is a multiple of 8)
+  // the pointer array follows the jobs (32-byte records, so it is 8-byte aligned)
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (stream_stores)
-    launch_reduce_k<true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
-  else
-    launch_reduce_k<false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  if (elem_bytes == 4) {
+    if (stream_stores)
+      launch_reduce_k<4, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+    else
+      launch_reduce_k<4, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  } else {
+    if (stream_stores)
+      launch_reduce_k<2, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+    else
+      launch_reduce_k<2, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  }
   return (int)hipGetLastError();
 }

@@ -27,12 +27,14 @@ struct CopySeg {
   uint64_t total_bytes;
 };
 
-// One reduction job: nbytes of fp32 per operand; operands are
-// ptr[src0 .. src0+nsrc), destinations ptr[dst0 .. dst0+ndst).  All
-// destinations share their address modulo 16; every destination gets the
-// same result.  AVG divides by nsrc.
+// One reduction job over nbytes of destination: the first data_bytes are
+// the reduction of the operands ptr[src0 .. src0+nsrc) (read at the same
+// offsets), the rest is zero filled; every destination ptr[dst0 ..
+// dst0+ndst) gets the same result.  All destinations share their address
+// modulo 16.  AVG divides by nsrc.
 struct RedJob {
   uint64_t nbytes;
+  uint64_t data_bytes;
   uint32_t src0;
   uint32_t nsrc;
   uint32_t dst0;
@@ -40,7 +42,7 @@ struct RedJob {
 };
 
 static_assert(sizeof(CopySeg) == 32, "CopySeg layout");
-static_assert(sizeof(RedJob) == 24, "RedJob layout");
+static_assert(sizeof(RedJob) == 32, "RedJob layout");
 
 // Number of chunks of an item [dst, dst + nbytes), nbytes > 0.
 inline uint64_t chunk_count(uint64_t dst, uint64_t nbytes, uint32_t shift) {
@@ -56,8 +58,9 @@ extern "C++" {
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
                          uint64_t n_chunks, uint32_t chunk_shift, uint32_t max_grid,
                          int stream_stores, void* stream);
-// Every job of one launch has the same operand count n_src.
-int fsdp_launch_reduce(const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
+// Every job of one launch has the same operand count n_src; elem_bytes is 4
+// (fp32) or 2 (bf16).
+int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores,
                        void* stream);
 }

@@ -81,13 +81,18 @@ class FlatBucket:
             "ag_copy_out": B.prepare("fsdp_ag_copy_out", self.shapes, S, self.ag, self.full),
             "rs_copy_in": B.prepare("fsdp_rs_copy_in", self.shapes, R, S, list(grads), self.rs_in),
             "rs_reduce": B.prepare("fsdp_rs_reduce", self.shapes, R, S, self.D, self.op, self.rs_in, self.rs_out),
+            "rs_copy_reduce": B.prepare("fsdp_rs_copy_reduce", self.shapes, R, S, self.D, self.op, list(grads),
+                                        self.rs_out),
             "fused_ar": B.prepare("fsdp_fused_ar", self.seg_numel, R, S, self.D, self.op, self.fused),
         }
         return self
 
-    def steps(self) -> List[str]:
-        """The steps one pass runs, in order (forward AG, then backward)."""
-        st = ["ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"]
+    def steps(self, fused_rs: bool = False) -> List[str]:
+        """The steps one pass runs, in order (forward AG, then backward).
+        fused_rs: RS copy-in and RS as one pass (the RS input is never
+        materialised; same results)."""
+        st = ["ag_copy_in", "ag_copy_out"]
+        st += ["rs_copy_reduce"] if fused_rs else ["rs_copy_in", "rs_reduce"]
         if self.do_ar:
             st.append("fused_ar")
         return st
@@ -95,6 +100,6 @@ class FlatBucket:
     def run(self, step: str, stream=None) -> None:
         self._calls[step](stream)
 
-    def step(self, stream=None) -> None:
-        for name in self.steps():
+    def step(self, stream=None, fused_rs: bool = False) -> None:
+        for name in self.steps(fused_rs):
             self._calls[name](stream)

@@ -70,7 +70,8 @@ extern "C" {
 #define FSDP_EOVERLAP  5  /* an output overlaps an input or another output */
 
 /* element types: copies take any of them (bits are moved, not converted);
- * reductions take FSDP_F32 */
+ * reductions take FSDP_F32, or FSDP_BF16 (widened exactly, summed in fp32,
+ * rounded once to nearest even at the store; NaN stores as 0x7FC0) */
 #define FSDP_F32   0
 #define FSDP_BF16  1
 #define FSDP_F16   2
@@ -178,13 +179,29 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
  * summed in ascending t in fp32, the accumulator starting from t = 0; AVG
  * divides the sum by S.  rs_out[g] may be a view into rank g's fused AR
  * buffer (zero-copy, [HYPER] 2.1).
- *   rs_in   [R] device pointers, S*I fp32 each
- *   rs_out  [R] device pointers, I fp32 each
- *   dtype   FSDP_F32 only (else FSDP_ENOTIMPL)
+ *   rs_in   [R] device pointers, S*I elements each
+ *   rs_out  [R] device pointers, I elements each
+ *   dtype   FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
  */
 int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
                    int32_t dp_size, int32_t op, int32_t dtype,
                    const void* const* rs_in, void* const* rs_out, void* stream);
+
+/*
+ * RS copy-in and RS in one pass, without materialising the RS input:
+ *   rs_out[d*S+s][in_off_i + k] = op( sum_{t=0..S-1} grads[(d*S+t)*P + i][row_off(i,s)*inner_i + k] )
+ * for k < row_len(i,s)*inner_i, and 0 over the rest of parameter i's padded
+ * region.  Bit for bit the result of fsdp_rs_copy_in followed by
+ * fsdp_rs_reduce (same order, same rounding); each gradient element is read
+ * once and no S*I buffer is written ([RAGGED] 6.4 padded RS input;
+ * [FS-MD] 3.3 RS on the shard group).
+ *   grads   [R*P] device pointers, grads[g*P + i] holds N0_i * inner_i elements
+ *   rs_out  [R] device pointers, I elements each (may be fused-buffer views)
+ *   dtype   FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
+ */
+int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
+                        int32_t dp_size, int32_t op, int32_t dtype,
+                        const void* const* grads, void* const* rs_out, void* stream);
 
 /*
  * Fused AR over every replicate group, in place ([HYPER] 2.1, 2.3):
@@ -192,8 +209,9 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
  *   AVG: acc = acc / D;  fused[d*S+s][k] = acc for every d,
  * for every k of the whole fused buffer (segments and zero gaps).
  *   seg_numel  [n_seg] segment sizes; the buffer size is fsdp_fused_layout's
+ *              for the dtype's element size
  *   fused      [R] device pointers, each 512-byte aligned (FSDP_EALIGN)
- *   dtype      FSDP_F32 only (else FSDP_ENOTIMPL)
+ *   dtype      FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
  */
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size,
                   int32_t shard_size, int32_t dp_size, int32_t op, int32_t dtype,

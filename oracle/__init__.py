@@ -12,6 +12,8 @@ from .fsdp_oracle import (  # noqa: F401
     BucketLayout,
     ag_copy_in,
     ag_copy_out,
+    bf16_to_f32,
+    f32_to_bf16,
     all_gather,
     bucket_layout,
     dim0_chunk,
@@ -23,6 +25,7 @@ from .fsdp_oracle import (  # noqa: F401
     reduce_grads_nonfused,
     replicate_groups,
     rs_copy_in,
+    rs_copy_reduce,
     rs_reduce,
     shard_groups,
     shard_params,

@@ -39,7 +39,9 @@ Readings where the pages are silent (each one is listed in the design doc):
 Precision: copies move elements bit for bit (bfloat16 is carried as its
 uint16 bit pattern).  Reductions run in float32 because the pages reduce the
 float32 gradients in their own dtype; the test suite checks them against a
-float64 sum within the float32 rounding bound.
+float64 sum within the float32 rounding bound.  bfloat16 gradients (a
+bfloat16 reduce dtype) are widened exactly, summed in float32 in the same
+order, scaled, and rounded once to nearest even.
 
 Pins: every function here is pinned by tests that do not re-state its
 formula (worked examples, torch.chunk, brute-force inverse maps, exact
@@ -276,11 +278,38 @@ def rs_copy_in(grads: Sequence[np.ndarray], lay: BucketLayout, dtype=np.float32)
     return buf
 
 
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to float32: the bf16 bits are the top
+    half of the float32 bits, so the conversion is exact."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 to bfloat16 bits, round to nearest, ties to even; every NaN
+    becomes the quiet NaN 0x7FC0.  Written out on the bit pattern: keep the
+    top 16 bits, add one unit when the dropped 16 bits exceed half a unit, or
+    equal it and the kept part is odd (carries may round up to infinity)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    top = u >> 16
+    low = u & 0xFFFF
+    up = (low > 0x8000) | ((low == 0x8000) & ((top & 1) == 1))
+    out = (top + up).astype(np.uint16)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    out[nan] = 0x7FC0
+    return out
+
+
+def _as_f32(x: np.ndarray) -> np.ndarray:
+    """Gradient values in float32 (bfloat16 is carried as uint16 bits)."""
+    return bf16_to_f32(x) if x.dtype == np.uint16 else x.astype(np.float32, copy=False)
+
+
 def _ordered_sum(operands: Sequence[np.ndarray]) -> np.ndarray:
-    """Sum float32 operands one at a time in the given order (reading R2)."""
-    acc = np.array(operands[0], dtype=np.float32, copy=True)
+    """Sum operands one at a time in the given order (reading R2), in
+    float32 (bfloat16 operands are widened exactly first)."""
+    acc = np.array(_as_f32(operands[0]), dtype=np.float32, copy=True)
     for x in operands[1:]:
-        acc = acc + x.astype(np.float32, copy=False)
+        acc = acc + _as_f32(x)
     return acc
 
 
@@ -291,6 +320,12 @@ def _scale(acc: np.ndarray, op: str, n: int) -> np.ndarray:
     if op == AVG:
         return acc / np.float32(n)
     raise ValueError("unknown reduce op")
+
+
+def _store(acc: np.ndarray, like: np.ndarray) -> np.ndarray:
+    """The reduced value in the gradients' dtype: float32 as is, bfloat16
+    rounded once, to nearest even (the reduce dtype of [FS-MD] 5.2)."""
+    return f32_to_bf16(acc) if like.dtype == np.uint16 else acc
 
 
 def shard_groups(rank_size: int, shard_size: int) -> List[List[int]]:
@@ -318,7 +353,7 @@ def rs_reduce(rs_in: Sequence[np.ndarray], I: int, rank_size: int, shard_size: i
     for group in shard_groups(rank_size, shard_size):
         for s, g in enumerate(group):
             operands = [rs_in[m][s * I:(s + 1) * I] for m in group]
-            out[g] = _scale(_ordered_sum(operands), op, S)
+            out[g] = _store(_scale(_ordered_sum(operands), op, S), rs_in[group[0]])
     return out
 
 
@@ -333,10 +368,20 @@ def fused_ar(fused: Sequence[np.ndarray], rank_size: int, shard_size: int,
     S, D = group_sizes(rank_size, shard_size)
     out: List[np.ndarray] = [None] * rank_size  # type: ignore[list-item]
     for group in replicate_groups(rank_size, shard_size):
-        acc = _scale(_ordered_sum([fused[m] for m in group]), op, D)
+        acc = _store(_scale(_ordered_sum([fused[m] for m in group]), op, D), fused[group[0]])
         for m in group:
             out[m] = acc.copy()
     return out
+
+
+def rs_copy_reduce(grads: Sequence[Sequence[np.ndarray]], lay: BucketLayout, rank_size: int,
+                   op: str) -> List[np.ndarray]:
+    """RS copy-in and RS as one step: by definition the RS of the RS inputs
+    (the fused form only skips materialising them)."""
+    bf16 = rank_size > 0 and len(lay.shapes) > 0 and grads[0][0].dtype == np.uint16
+    dtype = np.uint16 if bf16 else np.float32
+    rs_in = [rs_copy_in(grads[g], lay, dtype) for g in range(rank_size)]
+    return rs_reduce(rs_in, lay.I, rank_size, lay.S, op)
 
 
 def grad_sync_plan(rank_size: int, shard_size: int) -> List[Tuple[str, List[List[int]]]]:

@@ -38,7 +38,7 @@ def declared_functions():
 def test_header_declares_the_five_ops_and_queries():
     names = declared_functions()
     for n in ("fsdp_ag_copy_in", "fsdp_ag_copy_out", "fsdp_rs_copy_in", "fsdp_rs_reduce",
-              "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
+              "fsdp_rs_copy_reduce", "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
               "fsdp_last_error", "fsdp_release_cache"):
         assert n in names
 
@@ -168,15 +168,21 @@ def test_device_entry_points_reject_bad_arguments(L):
     out8 = _ptrs([BASE + 0x1000000 * (g + 1) for g in range(8)])
     assert L.fsdp_rs_reduce(b.ref, 8, S, 3, 0, 0, rs8, out8, None) == 1
     assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 9, 0, rs8, out8, None) == 1
-    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 1, rs8, out8, None) == 2
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 2, rs8, out8, None) == 2
     alias = _ptrs([BASE + 0x10000000 * (g + 1) + 4 * lay.I for g in range(8)])
     assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 0, rs8, alias, None) == 5
+    # rs_copy_reduce: fp16 is not a reduction dtype; an output inside a gradient
+    g8 = _ptrs([BASE + 0x100000 * (k + 1) for k in range(8 * P)])
+    assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 2, g8, out8, None) == 2
+    inside = _ptrs([BASE + 0x100000 + 8] + [BASE + 0x10000000 * (g + 1) for g in range(1, 8)])
+    assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 0, g8, inside, None) == 5
+    assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 3, 0, 0, g8, out8, None) == 1
     # fused_ar: base not 512-byte aligned, dtype not fp32
     segs = (ctypes.c_int64 * 2)(100, 3)
     f8 = _ptrs([BASE + 0x100000 * g + 256 for g in range(8)])
     assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, f8, None) == 3
     f8a = _ptrs([BASE + 0x100000 * g for g in range(8)])
-    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 1, f8a, None) == 2
+    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 2, f8a, None) == 2
     ovl = _ptrs([BASE + 512 * g for g in range(8)])
     assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, ovl, None) == 5
 

@@ -115,5 +115,16 @@ def test_full_size_sampled(wname):
             k = np.unique(np.concatenate([rng.integers(0, I, N_RANDOM // R), edges]))
             want = PW.rs_reduce_values(I, R, S, op, g, k, fetch_rs_in)
             assert np.array_equal(_gpu_vals(fb.rs_out[g], k), want.view(np.int32)), f"rs_reduce {op} rank {g}"
-    del fb, params, grads
+    # --- RS copy-in fused into the RS: the whole result equals the two-step
+    # one (SUM, just computed) bit for bit, and samples match the oracle ---
+    fused_out = [torch.empty(I, dtype=torch.float32, device="cuda") for _ in range(R)]
+    hp.fsdp_rs_copy_reduce(w.param_shapes, R, S, D, O.SUM, [grads[g][i].reshape(-1) for g in range(R) for i in range(P)],
+                           fused_out)
+    torch.cuda.synchronize()
+    for g in range(R):
+        assert torch.equal(fused_out[g].view(torch.int32), fb.rs_out[g].view(torch.int32)), f"rs_copy_reduce rank {g}"
+        k = np.unique(np.concatenate([rng.integers(0, I, N_RANDOM // R), edges]))
+        want = PW.rs_reduce_values(I, R, S, O.SUM, g, k, fetch_rs_in)
+        assert np.array_equal(_gpu_vals(fused_out[g], k), want.view(np.int32)), f"rs_copy_reduce sampled rank {g}"
+    del fb, params, grads, fused_out
     torch.cuda.empty_cache()

@@ -326,3 +326,112 @@ def test_hsdp_block_end_to_end_flat_bucket():
     for g in range(R):
         m = first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g]))
         assert m == "", f"fused rank {g}: {m}"
+
+
+# ---------------------------------------------------------------------------
+# RS copy-in fused into the RS, and bfloat16 gradients
+# ---------------------------------------------------------------------------
+
+def run_rs_copy_reduce(name, shapes, R, S, grads, ops=(O.SUM, O.AVG), out_offset=0):
+    """fsdp_rs_copy_reduce against the oracle's RS of the RS inputs."""
+    dtype = grads[0][0].dtype if shapes else torch.float32
+    note(f"[parity] rs_copy_reduce {name}: R={R} S={S} P={len(shapes)} dtype={dtype} out_offset={out_offset}")
+    lay = O.bucket_layout(shapes, S)
+    P = len(shapes)
+    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
+    dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    for op in ops:
+        want = O.rs_copy_reduce(gnp, lay, R, op)
+        out = [Guarded(lay.I, dtype, out_offset + g % 3) for g in range(R)]
+        hp.fsdp_rs_copy_reduce(shapes, R, S, R // S, op, dgrads, [o.t for o in out])
+        torch.cuda.synchronize()
+        for g in range(R):
+            assert out[g].guards_intact(), f"rs_copy_reduce wrote outside rs_out[{g}]"
+            m = first_mismatch(bits(out[g].t), np_bits(want[g]))
+            assert m == "", f"rs_copy_reduce {op} rank {g}: {m}"
+
+
+def test_rs_copy_reduce_tiny_and_misaligned():
+    w = W.TINY_FSDP
+    for off in (0, 1, 3):
+        run_rs_copy_reduce(w.name, w.param_shapes, w.rank_size, w.shard_size, W.grads(w), out_offset=off)
+
+
+def test_rs_copy_reduce_ragged_heavy_scaled():
+    w = W.scaled(W.RAGGED_HEAVY, [(4097, 8), (11009, 8), (32001, 8), (5, 64), (3,)])
+    run_rs_copy_reduce(w.name, w.param_shapes, w.rank_size, w.shard_size, W.grads(w), out_offset=1)
+
+
+def test_rs_copy_reduce_hsdp_block_full_size():
+    w = W.HSDP_BLOCK
+    run_rs_copy_reduce(w.name, w.param_shapes, w.rank_size, w.shard_size, W.grads(w), ops=(O.AVG,))
+
+
+def test_rs_copy_reduce_random_buckets():
+    rng = np.random.default_rng(404)
+    for case in range(12):
+        S = int(rng.choice([1, 2, 3, 4, 8]))
+        D = int(rng.choice([1, 2, 3]))
+        shapes = []
+        for _ in range(int(rng.integers(1, 6))):
+            n0 = int(rng.integers(0, 3 * S + 40))
+            rest = [int(rng.choice([1, 2, 3, 7, 64, 129]))] if rng.random() < 0.6 else []
+            shapes.append(tuple([n0] + rest))
+        dtype = [torch.float32, torch.bfloat16][case % 2]
+        w = W.Workload(f"rcr_random_{case}", 300 + case, S * D, S, tuple(shapes), dtype, ("normal", 1.0),
+                       ("normal", 1.0), ("sum", "avg"), W.ALL_STEPS)
+        run_rs_copy_reduce(w.name, shapes, S * D, S, W.grads(w, dtype=dtype), out_offset=int(rng.integers(0, 5)))
+
+
+@pytest.mark.parametrize("R,S", [(8, 4), (16, 8), (6, 3), (4, 1)])
+def test_bf16_rs_copy_in_and_reduce(R, S):
+    """bf16 gradients: RS copy-in (a bit copy), RS (fp32 sum, one rounding)
+    and the fused form agree with the oracle bit for bit."""
+    shapes = [(1001, 7), (17,), (3, 3, 3), (0,), (40001,), (5, 64)]
+    w = W.Workload(f"bf16_rs_{R}_{S}", 21, R, S, tuple(shapes), torch.bfloat16, ("normal", 1.0),
+                   ("normal", 1e-3), ("sum", "avg"), W.ALL_STEPS)
+    grads = W.grads(w, dtype=torch.bfloat16)
+    note(f"[parity] bf16 RS R={R} S={S}")
+    lay = O.bucket_layout(shapes, S)
+    P = len(shapes)
+    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
+    rs_o = [O.rs_copy_in(gnp[g], lay, np.uint16) for g in range(R)]
+    dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    rs_in = [Guarded(S * lay.I, torch.bfloat16, 1) for _ in range(R)]
+    hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in])
+    for op in (O.SUM, O.AVG):
+        out = [Guarded(lay.I, torch.bfloat16, g % 4) for g in range(R)]
+        hp.fsdp_rs_reduce(shapes, R, S, R // S, op, [b.t for b in rs_in], [o.t for o in out])
+        torch.cuda.synchronize()
+        want = O.rs_reduce(rs_o, lay.I, R, S, op)
+        for g in range(R):
+            assert rs_in[g].guards_intact() and out[g].guards_intact()
+            assert first_mismatch(bits(rs_in[g].t), np_bits(rs_o[g])) == ""
+            m = first_mismatch(bits(out[g].t), np_bits(want[g]))
+            assert m == "", f"bf16 rs_reduce {op} rank {g}: {m}"
+    run_rs_copy_reduce(w.name, shapes, R, S, grads)
+
+
+@pytest.mark.parametrize("op", [O.AVG, O.SUM])
+def test_bf16_fused_ar_pure_tp(op):
+    """bf16 fused AR over 300 segments (512-byte alignment = 256 elements)."""
+    sizes = [s[0] for s in W.PURE_TP.param_shapes[:300]]
+    w = W.scaled(W.PURE_TP, [(n,) for n in sizes], name="pure_tp_bf16")
+    R, S = w.rank_size, w.shard_size
+    note(f"[parity] bf16 fused_ar {op}: {len(sizes)} segments")
+    g_cpu = W.grads(w, dtype=torch.bfloat16)
+    offs, F = O.fused_layout(sizes, elem_bytes=2)
+    fused_o = []
+    for g in range(R):
+        buf = np.zeros(F, np.uint16)
+        for o, t in zip(offs, g_cpu[g]):
+            buf[o:o + t.numel()] = to_oracle(t)
+        fused_o.append(buf)
+    want = O.fused_ar(fused_o, R, S, op)
+    assert hp.fsdp_fused_layout(sizes, 2) == (offs, F)
+    fused = [torch.from_numpy(f.view(np.int16).copy()).view(torch.bfloat16).cuda() for f in fused_o]
+    hp.fsdp_fused_ar(sizes, R, S, R // S, op, fused)
+    torch.cuda.synchronize()
+    for g in range(R):
+        m = first_mismatch(bits(fused[g]), np_bits(want[g]))
+        assert m == "", f"bf16 fused_ar rank {g}: {m}"

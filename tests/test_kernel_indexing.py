@@ -134,68 +134,76 @@ def check_copy(segs, es, shift):
         assert align_down16(src) <= a and b <= align_up16(src + copy), "read outside the source envelope"
 
 
-def emulate_reduce(jobs, ptr, shift):
-    """Writes per destination as (lo, hi) byte ranges and operand reads,
-    following reduce_kernel."""
+def emulate_reduce(jobs, ptr, shift, es=4):
+    """Writes per destination as (lo, hi, kind) byte ranges and operand reads,
+    following reduce_kernel.  A job is (nbytes, data_bytes, src0, nsrc, dst0,
+    ndst): the first data_bytes are reduced, the rest zero filled."""
     CH = 1 << shift
     begin, n = [], 0
-    for (nbytes, src0, nsrc, dst0, ndst) in jobs:
+    for (nbytes, data, src0, nsrc, dst0, ndst) in jobs:
         begin.append(n)
         n += chunk_count(ptr[dst0], nbytes, shift)
     writes, reads = [], []
     for c in range(n):
         j = find_item(begin, len(jobs), c)
-        nbytes, src0, nsrc, dst0, ndst = jobs[j]
+        nbytes, data, src0, nsrc, dst0, ndst = jobs[j]
         k = c - begin[j]
         d0 = ptr[dst0]
         base = (d0 >> shift) << shift
         w0 = base + k * CH
         lo = max(w0, d0)
-        end = d0 + nbytes
-        hi = min(w0 + CH, end)
-        va, vb = align_up16(lo) - d0, align_down16(hi) - d0
-        if va < vb:
-            nv = (vb - va) >> 4
+        hi = min(w0 + CH, d0 + nbytes)
+        cend = d0 + data
+        ca, cb = align_up16(lo), align_down16(min(hi, cend))
+        if ca < cb:
+            va, nv = ca - d0, (cb - ca) >> 4
             for t in range(nsrc):
                 sa = ptr[src0 + t] + va
                 r = sa & 15
                 reads.append((sa - r, sa - r + 16 * nv + (16 if r else 0), j, t))
             for m in range(ndst):
-                writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + vb, j, m))
-        e0 = lo - d0
-        e_head = min(align_up16(lo), hi) - d0
-        e_tail = max(align_down16(hi), lo) - d0
-        e1 = hi - d0
-        n_head = (e_head - e0) >> 2
-        t0 = max(e_tail, e_head)
-        n_tail = (e1 - t0) >> 2
-        assert n_head + n_tail <= 256
-        for tid in range(n_head + n_tail):
-            x = e0 + 4 * tid if tid < n_head else t0 + 4 * (tid - n_head)
-            for t in range(nsrc):
-                reads.append((ptr[src0 + t] + x, ptr[src0 + t] + x + 4, j, t))
+                writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + va + 16 * nv, "data", j, m))
+        za, zb = align_up16(max(lo, cend)), align_down16(hi)
+        if za < zb:
             for m in range(ndst):
-                writes.append((ptr[dst0 + m] + x, ptr[dst0 + m] + x + 4, j, m))
+                writes.append((ptr[dst0 + m] + za - d0, ptr[dst0 + m] + zb - d0, "zero", j, m))
+        a_lo, a_c, a_hi = align_down16(lo), align_down16(cend), align_down16(hi)
+        p_lo = (lo & 15) != 0
+        p_c = (cend & 15) != 0 and lo < cend < hi and not (p_lo and a_c == a_lo)
+        p_hi = (hi & 15) != 0 and not (p_lo and a_hi == a_lo) and not (p_c and a_hi == a_c)
+        for flag, a in ((p_lo, a_lo), (p_c, a_c), (p_hi, a_hi)):
+            if not flag:
+                continue
+            for x in range(max(a, lo), min(a + 16, hi), es):
+                off = x - d0
+                kind = "data" if x < cend else "zero"
+                if kind == "data":
+                    for t in range(nsrc):
+                        reads.append((ptr[src0 + t] + off, ptr[src0 + t] + off + es, j, t))
+                for m in range(ndst):
+                    writes.append((ptr[dst0 + m] + off, ptr[dst0 + m] + off + es, kind, j, m))
     return writes, reads
 
 
-def check_reduce(jobs, ptr, shift):
-    writes, reads = emulate_reduce(jobs, ptr, shift)
+def check_reduce(jobs, ptr, shift, es=4):
+    writes, reads = emulate_reduce(jobs, ptr, shift, es)
     per = {}
-    for (a, b, j, m) in writes:
-        per.setdefault((j, m), []).append((a, b))
-    for j, (nbytes, src0, nsrc, dst0, ndst) in enumerate(jobs):
+    for (a, b, kind, j, m) in writes:
+        per.setdefault((j, m), []).append((a, b, kind))
+    for j, (nbytes, data, src0, nsrc, dst0, ndst) in enumerate(jobs):
         for m in range(ndst):
             iv = sorted(per.get((j, m), []))
             pos = ptr[dst0 + m]
-            for a, b in iv:
+            for a, b, kind in iv:
                 assert a == pos, f"job {j} dst {m}: gap or double write at {a:#x} (expected {pos:#x})"
+                edge = ptr[dst0 + m] + data
+                assert (b <= edge) if kind == "data" else (a >= edge), f"job {j}: {kind} write across the data end"
                 pos = b
             assert pos == ptr[dst0 + m] + nbytes
     for (a, b, j, t) in reads:
-        nbytes, src0, nsrc, dst0, ndst = jobs[j]
+        nbytes, data, src0, nsrc, dst0, ndst = jobs[j]
         s = ptr[src0 + t]
-        assert align_down16(s) <= a and b <= align_up16(s + nbytes), "operand read outside its envelope"
+        assert align_down16(s) <= a and b <= align_up16(s + data), "operand read outside its envelope"
 
 
 # ---------------------------------------------------------------------------
@@ -290,34 +298,68 @@ def test_random_segments():
 
 
 @pytest.mark.parametrize("shift", CHUNK_SHIFTS)
-def test_reduce_jobs_cover_exactly(shift):
-    rng = np.random.default_rng(shift)
+@pytest.mark.parametrize("es", [4, 2])
+def test_reduce_jobs_cover_exactly(shift, es):
+    rng = np.random.default_rng(shift + es)
     for trial in range(60):
         R, S = [(8, 4), (8, 8), (6, 3), (8, 1), (2, 2)][trial % 5]
         I = int(rng.choice([1, 2, 3, 5, 16, 17, 1000, 4097, 20000]))
-        rs_in = [(1 << 36) + g * (1 << 26) + 4 * int(rng.integers(0, 8)) for g in range(R)]
-        rs_out = [(1 << 38) + g * (1 << 26) + 4 * int(rng.integers(0, 8)) for g in range(R)]
+        rs_in = [(1 << 36) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)]
+        rs_out = [(1 << 38) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)]
         # RS jobs, as fsdp_rs_reduce builds them
         jobs, ptr = [], []
         for g in range(R):
             d, s = divmod(g, S)
             src0 = len(ptr)
-            ptr += [rs_in[d * S + t] + s * I * 4 for t in range(S)]
+            ptr += [rs_in[d * S + t] + s * I * es for t in range(S)]
             dst0 = len(ptr)
             ptr.append(rs_out[g])
-            jobs.append((I * 4, src0, S, dst0, 1))
-        check_reduce(jobs, ptr, shift)
-        # fused AR jobs (in place, 512-byte aligned bases, F a multiple of 128)
+            jobs.append((I * es, I * es, src0, S, dst0, 1))
+        check_reduce(jobs, ptr, shift, es)
+        # fused AR jobs (in place, 512-byte aligned bases, F*es a multiple of 512)
         D = R // S
         if D > 1:
-            F = 128 * int(rng.integers(1, 40))
+            F = (512 // es) * int(rng.integers(1, 40))
             fused = [(1 << 39) + g * (1 << 26) for g in range(R)]
             jobs, ptr = [], []
             for s in range(S):
                 src0 = len(ptr)
                 ptr += [fused[d * S + s] for d in range(D)]
-                jobs.append((F * 4, src0, D, src0, D))
-            check_reduce(jobs, ptr, shift)
+                jobs.append((F * es, F * es, src0, D, src0, D))
+            check_reduce(jobs, ptr, shift, es)
+
+
+def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr):
+    """Jobs as fsdp_rs_copy_reduce builds them: one per (rank, parameter)."""
+    L = layout(shapes, S)
+    jobs, ptr = [], []
+    for g in range(R):
+        d, s = divmod(g, S)
+        for i, sh in enumerate(shapes):
+            if L["padded"][i] == 0:
+                continue
+            data = L["rl"][i][s] * L["inner"][i] * es
+            row0 = L["ro"][i][s] * L["inner"][i] * es
+            src0 = len(ptr)
+            ptr += [grad_addr(d * S + t, i) + row0 if data else 0 for t in range(S)]
+            dst0 = len(ptr)
+            ptr.append(out_addr(g) + L["in_off"][i] * es)
+            jobs.append((L["padded"][i] * es, data, src0, S, dst0, 1))
+    return jobs, ptr
+
+
+@pytest.mark.parametrize("shapes", SHAPES)
+@pytest.mark.parametrize("R,S", [(8, 4), (8, 8), (6, 3), (4, 1)])
+@pytest.mark.parametrize("es", [4, 2])
+@pytest.mark.parametrize("shift", (9, 13))
+def test_rs_copy_reduce_jobs_cover_exactly(shapes, R, S, es, shift):
+    rng = np.random.default_rng(R * 10 + S + es)
+    grads = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + es * int(rng.integers(0, 8))
+             for g in range(R) for i in range(len(shapes))}
+    outs = {g: (1 << 44) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)}
+    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: grads[(g, i)], lambda g: outs[g])
+    if jobs:
+        check_reduce(jobs, ptr, shift, es)
 
 
 def test_find_item_all_chunks():

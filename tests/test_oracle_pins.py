@@ -138,13 +138,21 @@ def textbook_rs(grads_int, shapes, members, s, S):
     return out
 
 
-def pin_rs_exact(R, S, op, shapes):
+def pin_rs_exact(R, S, op, shapes, bf16=False):
+    """Integer-valued gradients in [-8, 8]: every partial sum is exact in
+    float32 and in bfloat16 (|sum| <= 64 < 2**8), whatever the order."""
     bad = []
     D = R // S
     gi = [[RNG.integers(-8, 9, size=sh).astype(np.float32) for sh in shapes] for _ in range(R)]
     lay = O.bucket_layout(shapes, S)
-    rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
-    outs = O.rs_reduce(rs_in, lay.I, R, S, op)
+    if bf16:
+        gb = [[torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16) for x in row]
+              for row in gi]
+        rs_in = [O.rs_copy_in(gb[g], lay, np.uint16) for g in range(R)]
+        outs = [O.bf16_to_f32(o) for o in O.rs_reduce(rs_in, lay.I, R, S, op)]
+    else:
+        rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
+        outs = O.rs_reduce(rs_in, lay.I, R, S, op)
     for g in range(R):
         d, s = divmod(g, S)
         members = list(range(d * S, d * S + S))
@@ -249,6 +257,62 @@ def test_rs_exact_integer_sums(R, S, op):
     if op == O.AVG and S & (S - 1):
         pytest.skip("division by a non-power-of-two is not exact")
     assert pin_rs_exact(R, S, op, [(7, 8), (5, 3), (16,), (3,), (11, 2)]) == []
+
+
+@pytest.mark.parametrize("R,S", [(4, 4), (8, 4), (8, 8), (8, 2), (6, 3)])
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_rs_exact_integer_sums_bf16(R, S, op):
+    if op == O.AVG and S & (S - 1):
+        pytest.skip("division by a non-power-of-two is not exact")
+    assert pin_rs_exact(R, S, op, [(7, 8), (5, 3), (16,), (3,), (11, 2)], bf16=True) == []
+
+
+def _bf16_special_values():
+    rng = np.random.default_rng(77)
+    vals = [rng.standard_normal(20000).astype(np.float32),
+            (rng.standard_normal(2000) * 1e-40).astype(np.float32),          # denormals
+            np.array([0.0, -0.0, np.inf, -np.inf, np.nan, -np.nan, 3.3895314e38, -3.3895314e38,
+                      3.4028235e38, 1.0, -1.0, 1e-45, -1e-45], dtype=np.float32)]
+    # exact ties: a kept part with each parity and the dropped half exactly 0x8000
+    top = rng.integers(0, 0x7F7F, size=2000).astype(np.uint32)
+    vals.append(((top << 16) | 0x8000).view(np.float32))
+    vals.append(((top << 16) | 0x7FFF).view(np.float32))
+    vals.append(((top << 16) | 0x8001).view(np.float32))
+    return np.concatenate(vals)
+
+
+def test_bf16_conversions_match_torch():
+    x = _bf16_special_values()
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.f32_to_bf16(x)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.all(got[nan] == 0x7FC0)
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.bf16_to_f32(bits).view(np.uint32), back.view(np.uint32))
+
+
+def test_bf16_reductions_round_once():
+    """bf16 RS = round_to_bf16(float32 ordered sum of the widened operands),
+    checked against torch's float32 arithmetic and its bf16 rounding."""
+    R, S = 8, 4
+    shapes = [(33, 7), (10,)]
+    lay = O.bucket_layout(shapes, S)
+    gi = [[torch.randn(sh).to(torch.bfloat16) for sh in shapes] for _ in range(R)]
+    rs_in = [O.rs_copy_in([t.view(torch.int16).numpy().view(np.uint16) for t in gi[g]], lay, np.uint16)
+             for g in range(R)]
+    for op in (O.SUM, O.AVG):
+        outs = O.rs_reduce(rs_in, lay.I, R, S, op)
+        for g in range(R):
+            d, s = divmod(g, S)
+            acc = torch.from_numpy(rs_in[d * S][s * lay.I:(s + 1) * lay.I].view(np.int16)).view(torch.bfloat16).float()
+            for t in range(1, S):
+                acc = acc + torch.from_numpy(rs_in[d * S + t][s * lay.I:(s + 1) * lay.I].view(np.int16)).view(torch.bfloat16).float()
+            if op == O.AVG:
+                acc = acc / S
+            want = acc.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(outs[g], want)
 
 
 @pytest.mark.parametrize("R,S", [(8, 4), (8, 1), (4, 4), (8, 2), (2, 1)])
@@ -402,7 +466,12 @@ def _unpadded_bucket_layout(shapes, S, shard_dim=0):
     return lay
 
 
+def _truncating_bf16(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 MUTANTS = {
+    "bf16_truncation": ("f32_to_bf16", _truncating_bf16),
     "floor_chunk": ("dim0_chunk", _floor_chunk),
     "array_split": ("dim0_chunk", _array_split_chunk),
     "head_padding": ("ag_copy_in", _head_padding_copy_in),
@@ -411,6 +480,13 @@ MUTANTS = {
     "rank_mapping": ("replicate_groups", _transposed_replicate_groups),
     "offset_by_actual": ("bucket_layout", _unpadded_bucket_layout),
 }
+
+
+def _bf16_pin():
+    x = _bf16_special_values()
+    ok = ~np.isnan(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bool(np.array_equal(O.f32_to_bf16(x)[ok], want[ok]))
 
 
 def _groups_pin(golden):
@@ -430,6 +506,7 @@ def _all_pins(golden):
         lambda: pin_end_to_end_exact(8, 4, O.SUM, [(7, 8), (5, 3), (16,)]),
         lambda: pin_end_to_end_exact(8, 4, O.AVG, [(7, 8), (5, 3), (16,)]),
         lambda: _groups_pin(golden),
+        lambda: [] if _bf16_pin() else ["bf16 rounding"],
     ]
     bad = []
     for k, pin in enumerate(pins):
