@@ -152,6 +152,43 @@ def per_step_us(runner, steps, n):
             for j, name in enumerate(steps)}
 
 
+def pipeline_variant(w, op, layers: int, reps: int):
+    """The backward of `layers` buckets of this workload (RS copy-reduce of
+    each layer, fused AR of the previous layer): serial on one stream vs the
+    4-step overlap on two streams (BackwardPipeline)."""
+    import dataclasses
+
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+    R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+    buckets = []
+    for l in range(layers):
+        wl = dataclasses.replace(w, number=w.number * 1000 + l)
+        fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
+        params = [torch.zeros(sh, dtype=w.param_dtype, device="cuda") for sh in w.param_shapes]
+        grads = W.grads(wl, "cuda")
+        fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+        buckets.append(fb)
+    pipe = hp.BackwardPipeline(buckets, fused_rs=True)
+    out = {"layers": layers}
+    for name, fn in (("serial_ms", pipe.run_serial), ("pipelined_ms", pipe.run_pipelined)):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out[name] = round(s.elapsed_time(e) / reps, 4)
+    log(f"  backward pipeline, {layers} layers: serial {out['serial_ms']:.3f} ms, "
+        f"two streams {out['pipelined_ms']:.3f} ms")
+    return out
+
+
 def calibration_copy(mib: int, reps: int) -> None:
     """A plain copy of known size for calibrating the HBM byte counters: the
     copy kernel on one aligned fp32 segment (AG copy-out with one shard), so
@@ -240,6 +277,8 @@ def main():
     ap.add_argument("--workload", default="hsdp_block_h1024_r8_s4_d2")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline-layers", type=int, default=8,
+                    help="layers in the backward-overlap variant (0 = skip it)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -354,6 +393,8 @@ def main():
             "note": "RS input never written; results identical to rs_copy_in + rs_reduce"}
         log(f"  fused RS variant: step {f_ms * 1e3:.1f} us (vs {ms_per_step * 1e3:.1f}); rs_copy_reduce "
             f"{f_us:.1f} us, {b / (f_us * 1e-6) / 1e9:.1f} GB/s")
+        if args.pipeline_layers > 1 and runner.do_ar:
+            variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -73,6 +73,22 @@ class FlatBucket:
                 out.append(x.reshape(self.shapes[i])[a:a + n].reshape(-1))
         return out
 
+    def full_views(self) -> List[torch.Tensor]:
+        """Zero-copy AG for a one-parameter bucket: the parameter is the view
+        ag[:N] of the gathered buffer, so copy-out can be skipped.  With
+        fixed-size dim-0 chunks every padding element lies after the last
+        data row, so that prefix is exactly the full parameter (the
+        unsharded-parameter-as-view option of the Hyper PR #758 write-up,
+        section 4; it needs the AG buffer to stay alive while the view is
+        used)."""
+        if len(self.shapes) != 1:
+            raise ValueError("a view of the gathered buffer is the full parameter only for a "
+                             "one-parameter bucket; use the ag_copy_out step")
+        n = 1
+        for d in self.shapes[0]:
+            n *= d
+        return [self.ag[:n].view(self.shapes[0])]
+
     def bind(self, shards: Sequence[torch.Tensor], grads: Sequence[torch.Tensor]) -> "FlatBucket":
         """Marshal the five calls once: shards [S*P] rank-major, grads [R*P]."""
         S, R = self.S, self.R

@@ -235,6 +235,22 @@ def test_ag_multiparam_roundtrip_and_padding():
     assert pin_ag_multiparam() == []
 
 
+def test_single_parameter_gather_prefix_is_the_parameter():
+    """Zero-copy AG ('option 2' of the Hyper PR write-up): in a one-parameter
+    bucket the first N elements of the gathered buffer are the full
+    parameter, because fixed-size chunking leaves every padding element
+    after the last data row.  Brute force over shapes and shard counts."""
+    for S in range(1, 10):
+        for n0 in range(0, 3 * S + 4):
+            for inner in (1, 3):
+                shape = (n0, inner)
+                x = (RNG.standard_normal(shape) + 5).astype(np.float32)
+                lay = O.bucket_layout([shape], S)
+                ag = O.ag_copy_in(O.shard_params([x], lay), lay, np.float32)
+                assert np.array_equal(ag[:x.size], x.reshape(-1))
+                assert not np.any(ag[x.size:])  # the rest is padding
+
+
 def test_pointwise_forms_match_full_forms():
     shapes = [(7, 8), (5, 3), (16,), (0, 3), (3,)]
     for S in (1, 3, 4, 8):
