@@ -39,7 +39,8 @@ class FSDPError(RuntimeError):
 
 class _Bucket(ctypes.Structure):
     _fields_ = [("n_params", c_int32), ("ndim", POINTER(c_int32)),
-                ("shape", POINTER(c_int64)), ("shard_dim", c_int32)]
+                ("shape", POINTER(c_int64)), ("shard_dim", c_int32),
+                ("shard_dims", POINTER(c_int32))]
 
 
 _LIB = None
@@ -102,14 +103,22 @@ def _check(fn: str, rc: int) -> None:
 class _BucketArg:
     """fsdp_bucket_t for a list of shapes (keeps its arrays alive)."""
 
-    def __init__(self, shapes: Sequence[Sequence[int]], shard_dim: int = 0):
+    def __init__(self, shapes: Sequence[Sequence[int]], shard_dim: int = 0,
+                 shard_dims: Optional[Sequence[int]] = None):
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         P = len(self.shapes)
         flat = [d for s in self.shapes for d in s]
         self._ndim = (c_int32 * max(P, 1))(*[len(s) for s in self.shapes])
         self._shape = (c_int64 * max(len(flat), 1))(*flat)
-        self.struct = _Bucket(P, self._ndim, self._shape, shard_dim)
+        self.dims = [int(shard_dim)] * P if shard_dims is None else [int(k) for k in shard_dims]
+        self._dims = (c_int32 * max(P, 1))(*self.dims) if shard_dims is not None else None
+        self.struct = _Bucket(P, self._ndim, self._shape, int(shard_dim), self._dims)
         self.ref = ctypes.byref(self.struct)
+
+    def chunk_numel(self, lay: "Layout", i: int, s: int) -> int:
+        """Elements of rank s's chunk of parameter i (outer * rows * inner)."""
+        shape, k = self.shapes[i], self.dims[i]
+        return _numel(shape) // shape[k] * lay.row_len[i][s] if shape[k] else 0
 
 
 class Layout(NamedTuple):
@@ -120,8 +129,9 @@ class Layout(NamedTuple):
     row_len: List[List[int]]    # [i][s] rows held by shard rank s
 
 
-def fsdp_bucket_layout(shapes: Sequence[Sequence[int]], shard_size: int, shard_dim: int = 0) -> Layout:
-    b = _BucketArg(shapes, shard_dim)
+def fsdp_bucket_layout(shapes: Sequence[Sequence[int]], shard_size: int, shard_dim: int = 0,
+                       shard_dims: Optional[Sequence[int]] = None) -> Layout:
+    b = _BucketArg(shapes, shard_dim, shard_dims)
     P, S = len(b.shapes), int(shard_size)
     n = max(P, 1)
     I = c_int64()
@@ -207,15 +217,14 @@ class _Call:
         _check(self.name, self.fn(*self.args, _stream(stream)))
 
 
-def _prep_ag_copy_in(shapes, shard_size, shards, ag):
-    b = _BucketArg(shapes)
-    lay = fsdp_bucket_layout(b.shapes, shard_size)
+def _prep_ag_copy_in(shapes, shard_size, shards, ag, shard_dims=None):
+    b = _BucketArg(shapes, 0, shard_dims)
+    lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     S, P = int(shard_size), len(b.shapes)
     if len(shards) != S * P:
         raise ValueError(f"shards: {len(shards)} tensors, expected S*P = {S * P} (rank-major)")
     dt = ag.dtype
-    ptrs = [_dev(shards[s * P + i], f"shards[{s * P + i}]",
-                 lay.row_len[i][s] * _numel(b.shapes[i][1:]), dt)
+    ptrs = [_dev(shards[s * P + i], f"shards[{s * P + i}]", b.chunk_numel(lay, i, s), dt)
             for s in range(S) for i in range(P)]
     arr = _ptr_array(ptrs)
     agp = _dev(ag, "ag", S * lay.I)
@@ -223,9 +232,9 @@ def _prep_ag_copy_in(shapes, shard_size, shards, ag):
                  (b, arr, tuple(shards), ag))
 
 
-def _prep_ag_copy_out(shapes, shard_size, ag, full):
-    b = _BucketArg(shapes)
-    lay = fsdp_bucket_layout(b.shapes, shard_size)
+def _prep_ag_copy_out(shapes, shard_size, ag, full, shard_dims=None):
+    b = _BucketArg(shapes, 0, shard_dims)
+    lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     S, P = int(shard_size), len(b.shapes)
     if len(full) != P:
         raise ValueError(f"full: {len(full)} tensors, expected {P}")
@@ -236,9 +245,9 @@ def _prep_ag_copy_out(shapes, shard_size, ag, full):
                  (b, arr, tuple(full), ag))
 
 
-def _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in):
-    b = _BucketArg(shapes)
-    lay = fsdp_bucket_layout(b.shapes, shard_size)
+def _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in, shard_dims=None):
+    b = _BucketArg(shapes, 0, shard_dims)
+    lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     R, S, P = int(rank_size), int(shard_size), len(b.shapes)
     if len(grads) != R * P or len(rs_in) != R:
         raise ValueError(f"grads: {len(grads)} (expected R*P = {R * P}), rs_in: {len(rs_in)} (expected {R})")
@@ -260,9 +269,9 @@ def _reduce_dtype(tensors, what) -> torch.dtype:
     return dt
 
 
-def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out):
-    b = _BucketArg(shapes)
-    lay = fsdp_bucket_layout(b.shapes, shard_size)
+def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out, shard_dims=None):
+    b = _BucketArg(shapes, 0, shard_dims)
+    lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     R, S = int(rank_size), int(shard_size)
     if len(rs_in) != R or len(rs_out) != R:
         raise ValueError(f"rs_in / rs_out: {len(rs_in)} / {len(rs_out)} tensors, expected {R}")
@@ -273,9 +282,9 @@ def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out):
                  (b, iarr, oarr, tuple(rs_in), tuple(rs_out)))
 
 
-def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out):
-    b = _BucketArg(shapes)
-    lay = fsdp_bucket_layout(b.shapes, shard_size)
+def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims=None):
+    b = _BucketArg(shapes, 0, shard_dims)
+    lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     R, S, P = int(rank_size), int(shard_size), len(b.shapes)
     if len(grads) != R * P or len(rs_out) != R:
         raise ValueError(f"grads: {len(grads)} (expected R*P = {R * P}), rs_out: {len(rs_out)} (expected {R})")
@@ -318,34 +327,36 @@ def prepare(fn, *args) -> _Call:
 
 
 def fsdp_ag_copy_in(shapes, shard_size: int, shards: Sequence[torch.Tensor], ag: torch.Tensor,
-                    stream=None) -> None:
+                    stream=None, shard_dims=None) -> None:
     """Pack shards[s*P + i] into rank slice s of ag (S*I elements)."""
-    _prep_ag_copy_in(shapes, shard_size, shards, ag)(stream)
+    _prep_ag_copy_in(shapes, shard_size, shards, ag, shard_dims)(stream)
 
 
 def fsdp_ag_copy_out(shapes, shard_size: int, ag: torch.Tensor, full: Sequence[torch.Tensor],
-                     stream=None) -> None:
+                     stream=None, shard_dims=None) -> None:
     """Unpack the gathered ag into the full parameters full[i]."""
-    _prep_ag_copy_out(shapes, shard_size, ag, full)(stream)
+    _prep_ag_copy_out(shapes, shard_size, ag, full, shard_dims)(stream)
 
 
 def fsdp_rs_copy_in(shapes, rank_size: int, shard_size: int, grads: Sequence[torch.Tensor],
-                    rs_in: Sequence[torch.Tensor], stream=None) -> None:
+                    rs_in: Sequence[torch.Tensor], stream=None, shard_dims=None) -> None:
     """Chunk grads[g*P + i] into the padded RS inputs rs_in[g] (S*I elements)."""
-    _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in)(stream)
+    _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in, shard_dims)(stream)
 
 
 def fsdp_rs_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, op: str,
-                   rs_in: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None) -> None:
-    """Reduce-scatter within every shard group into rs_out[g] (I fp32 elements)."""
-    _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out)(stream)
+                   rs_in: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None,
+                   shard_dims=None) -> None:
+    """Reduce-scatter within every shard group into rs_out[g] (I elements)."""
+    _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out, shard_dims)(stream)
 
 
 def fsdp_rs_copy_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, op: str,
-                        grads: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None) -> None:
+                        grads: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None,
+                        shard_dims=None) -> None:
     """RS copy-in and RS in one pass: reduce chunk s of every gradient over
     each shard group straight into rs_out[g] (I elements, padding zero)."""
-    _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out)(stream)
+    _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims)(stream)
 
 
 def fsdp_fused_ar(seg_numel, rank_size: int, shard_size: int, dp_size: int, op: str,

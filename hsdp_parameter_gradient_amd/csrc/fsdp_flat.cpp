@@ -60,50 +60,63 @@ bool add_ok(int64_t a, int64_t b, int64_t* out) {
   return !__builtin_add_overflow(a, b, out) && *out <= kMaxBytes;
 }
 
+// Per parameter i sharded on dim k: outer = product of the dims before k,
+// dk = dim k, inner = product of the dims after k; rank s holds rows
+// [row_off, row_off + row_len) along k, i.e. outer runs of row_len*inner
+// elements; its region in a rank slice is padded = outer*chunk*inner.
 struct Layout {
   int32_t P = 0;
   int32_t S = 1;
   int64_t I = 0;
-  std::vector<int64_t> chunk, inner, padded, in_off, numel;
+  std::vector<int64_t> chunk, inner, outer, dk, padded, in_off, numel;
   std::vector<int64_t> row_off, row_len;  // [i*S + s]
 };
 
 int make_layout(const fsdp_bucket_t* b, int32_t S, Layout* L) {
   if (!b) return fail(FSDP_EINVAL, "bucket is NULL");
-  if (b->shard_dim != 0)
-    return fail(FSDP_ENOTIMPL, "shard_dim %d: only dim-0 sharding is implemented", b->shard_dim);
   if (S < 1) return fail(FSDP_EINVAL, "shard_size %d < 1", S);
   if (b->n_params < 0) return fail(FSDP_EINVAL, "n_params %d < 0", b->n_params);
   if (b->n_params > 0 && (!b->ndim || !b->shape))
     return fail(FSDP_EINVAL, "ndim / shape arrays are NULL");
   L->P = b->n_params;
   L->S = S;
-  L->chunk.resize(L->P);
-  L->inner.resize(L->P);
-  L->padded.resize(L->P);
-  L->in_off.resize(L->P);
-  L->numel.resize(L->P);
+  for (auto* v : {&L->chunk, &L->inner, &L->outer, &L->dk, &L->padded, &L->in_off, &L->numel})
+    v->resize(L->P);
   L->row_off.resize((size_t)L->P * S);
   L->row_len.resize((size_t)L->P * S);
   int64_t off = 0;
   size_t pos = 0;
   for (int32_t i = 0; i < L->P; ++i) {
     const int32_t nd = b->ndim[i];
-    if (nd < 1) return fail(FSDP_EINVAL, "param %d: ndim %d < 1 (a 0-d tensor has no dim 0)", i, nd);
+    if (nd < 1) return fail(FSDP_EINVAL, "param %d: ndim %d < 1 (a 0-d tensor has no dim to shard)", i, nd);
     const int64_t* sh = b->shape + pos;
     pos += (size_t)nd;
-    int64_t inner = 1;
+    const int32_t k = b->shard_dims ? b->shard_dims[i] : b->shard_dim;
+    if (k < 0 || k >= nd) return fail(FSDP_EINVAL, "param %d: shard dim %d outside [0, %d)", i, k, nd);
+    int64_t outer = 1, inner = 1;
     for (int32_t d = 0; d < nd; ++d) {
       if (sh[d] < 0) return fail(FSDP_EINVAL, "param %d: negative dim %lld", i, (long long)sh[d]);
-      if (d > 0 && !mul_ok(inner, sh[d], &inner)) return fail(FSDP_EINVAL, "param %d: size overflow", i);
+      if (d < k && !mul_ok(outer, sh[d], &outer)) return fail(FSDP_EINVAL, "param %d: size overflow", i);
+      if (d > k && !mul_ok(inner, sh[d], &inner)) return fail(FSDP_EINVAL, "param %d: size overflow", i);
     }
-    const int64_t n0 = sh[0];
-    const int64_t chunk = n0 / S + (n0 % S != 0);
-    int64_t padded, numel;
-    if (!mul_ok(chunk, inner, &padded) || !mul_ok(n0, inner, &numel))
+    const int64_t n0 = sh[k];
+    int64_t chunk;
+    if (k == 0) {
+      chunk = n0 / S + (n0 % S != 0);
+    } else {
+      if (n0 % S)
+        return fail(FSDP_ENOTIMPL, "param %d: dim %d of size %lld is not divisible by shard_size %d "
+                    "(only dim 0 may be uneven)", i, k, (long long)n0, S);
+      chunk = n0 / S;
+    }
+    int64_t padded, numel, t;
+    if (!mul_ok(outer, chunk, &t) || !mul_ok(t, inner, &padded) || !mul_ok(outer, n0, &t) ||
+        !mul_ok(t, inner, &numel))
       return fail(FSDP_EINVAL, "param %d: size overflow", i);
     L->chunk[i] = chunk;
     L->inner[i] = inner;
+    L->outer[i] = outer;
+    L->dk[i] = n0;
     L->padded[i] = padded;
     L->numel[i] = numel;
     L->in_off[i] = off;
@@ -305,6 +318,9 @@ bool stream_stores(Reuse reuse, uint64_t out_bytes) {
 
 // Launch the segmented copy over `segs` (empty segments already dropped).
 int run_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream) {
+  // the kernel's chunk search needs every item non-empty
+  segs.erase(std::remove_if(segs.begin(), segs.end(), [](const fsdp::CopySeg& sg) { return sg.total_bytes == 0; }),
+             segs.end());
   if (segs.empty()) return ok();
   const Tuning& tu = tuning();
   std::vector<uint64_t> begin(segs.size());
@@ -331,6 +347,8 @@ int run_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t 
 
 int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg, Reuse reuse,
                hipStream_t stream) {
+  jobs.erase(std::remove_if(jobs.begin(), jobs.end(), [](const fsdp::RedJob& jb) { return jb.nbytes == 0; }),
+             jobs.end());
   if (jobs.empty()) return ok();
   const Tuning& tu = tuning();
   std::vector<uint64_t> begin(jobs.size());
@@ -434,7 +452,7 @@ int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dty
   segs.reserve((size_t)S * P);
   for (int32_t s = 0; s < S; ++s) {
     for (int32_t i = 0; i < P; ++i) {
-      const int64_t nb = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
+      const int64_t nb = L.outer[i] * L.row_len[(size_t)i * S + s] * L.inner[i] * es;
       const void* p = shards[(size_t)s * P + i];
       if ((rc = check_ptr(p, nb, es, "shards", (long)s * P + i))) return rc;
       ins.push_back({(uint64_t)p, (uint64_t)p + (uint64_t)nb, s * P + i});
@@ -466,11 +484,14 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     if ((rc = check_ptr(full[i], nb, es, "full", i))) return rc;
     outs.push_back({(uint64_t)full[i], (uint64_t)full[i] + (uint64_t)nb, i});
     for (int32_t s = 0; s < S; ++s) {
-      const int64_t n = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
-      if (n == 0) continue;
-      segs.push_back({(uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es),
-                      (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es),
-                      (uint64_t)n, (uint64_t)n});
+      // rank s's chunk: outer runs of row_len*inner elements, dense in the
+      // slice, at stride dk*inner in the full parameter
+      const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+      if (run == 0) continue;
+      for (int64_t o = 0; o < L.outer[i]; ++o)
+        segs.push_back({(uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i] + o * run) * es),
+                        (uint64_t)full[i] + (uint64_t)((o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es),
+                        (uint64_t)(run * es), (uint64_t)(run * es)});
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
@@ -504,12 +525,18 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
   for (int32_t g = 0; g < R; ++g) {
     for (int32_t s = 0; s < S; ++s) {
       for (int32_t i = 0; i < P; ++i) {
-        const int64_t total = L.padded[i] * es;
-        if (total == 0) continue;
-        const int64_t nb = L.row_len[(size_t)i * S + s] * L.inner[i] * es;
-        const uint64_t src = (uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
-        segs.push_back({nb ? src : 0, (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es),
-                        (uint64_t)nb, (uint64_t)total});
+        if (L.padded[i] == 0) continue;
+        // outer runs of row_len*inner elements from the gradient (stride
+        // dk*inner), dense in the slice; the last run carries the zero tail
+        const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+        const uint64_t g0 = (uint64_t)grads[(size_t)g * P + i];
+        const uint64_t d0 = (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es);
+        for (int64_t o = 0; o < L.outer[i]; ++o) {
+          const bool last = o + 1 == L.outer[i];
+          const int64_t total = last ? (L.padded[i] - o * run) * es : run * es;
+          const uint64_t src = g0 + (uint64_t)((o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es);
+          segs.push_back({run ? src : 0, d0 + (uint64_t)(o * run * es), (uint64_t)(run * es), (uint64_t)total});
+        }
       }
     }
   }
@@ -592,18 +619,24 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     const int32_t d = g / S, s = g % S;
     for (int32_t i = 0; i < P; ++i) {
       if (L.padded[i] == 0) continue;
-      const int64_t row0 = L.row_off[(size_t)i * S + s] * L.inner[i] * es;
-      fsdp::RedJob jb;
-      jb.nbytes = (uint64_t)(L.padded[i] * es);
-      jb.data_bytes = (uint64_t)(L.row_len[(size_t)i * S + s] * L.inner[i] * es);
-      jb.src0 = (uint32_t)ptrs.size();
-      jb.nsrc = (uint32_t)S;
-      for (int32_t t = 0; t < S; ++t)
-        ptrs.push_back(jb.data_bytes ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + (uint64_t)row0 : 0);
-      jb.dst0 = (uint32_t)ptrs.size();
-      jb.ndst = 1;
-      ptrs.push_back((uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es));
-      jobs.push_back(jb);
+      // one job per run of rank s's chunk (outer runs, the last one with
+      // the zero tail)
+      const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+      for (int64_t o = 0; o < L.outer[i]; ++o) {
+        const bool last = o + 1 == L.outer[i];
+        const int64_t src_off = (o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es;
+        fsdp::RedJob jb;
+        jb.nbytes = (uint64_t)((last ? L.padded[i] - o * run : run) * es);
+        jb.data_bytes = (uint64_t)(run * es);
+        jb.src0 = (uint32_t)ptrs.size();
+        jb.nsrc = (uint32_t)S;
+        for (int32_t t = 0; t < S; ++t)
+          ptrs.push_back(run ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + (uint64_t)src_off : 0);
+        jb.dst0 = (uint32_t)ptrs.size();
+        jb.ndst = 1;
+        ptrs.push_back((uint64_t)rs_out[g] + (uint64_t)((L.in_off[i] + o * run) * es));
+        if (jb.nbytes) jobs.push_back(jb);
+      }
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");

@@ -21,12 +21,13 @@
  *            issue 319): 5.1 interface and errors, 6.4 chunk rule, padded
  *            communication storage, AG / RS padding rules.
  *
- * Notation (all counts in elements unless a name says bytes):
+ * Notation (all counts in elements unless a name says bytes), for a
+ * parameter sharded on dim 0 (see fsdp_bucket_t for other dims):
  *   param i: shape (N0_i, ...), inner_i = product of dims after dim 0
  *   chunk_i = ceil(N0_i / S); rank s holds rows
  *     [row_off(i,s), row_off(i,s) + row_len(i,s)) with
  *     row_off = min(s*chunk_i, N0_i), row_len = min(chunk_i, N0_i - row_off)
- *   padded_i = chunk_i * inner_i; in_off_i = sum_{j<i} padded_j;
+ *   padded_i = outer_i * chunk_i * inner_i; in_off_i = sum_{j<i} padded_j;
  *   I = sum_i padded_i (elements of one rank slice)
  *   rank g = d*S + s: shard group d = {d*S .. d*S+S-1},
  *   replicate group s = {s, S+s, .., (D-1)*S+s}
@@ -88,14 +89,24 @@ extern "C" {
  *   n_params   P >= 0
  *   ndim       [P] number of dims of each parameter, each >= 1
  *   shape      concatenation of all shapes (sum(ndim) entries, each >= 0)
- *   shard_dim  the sharded dim; only 0 is implemented ([RAGGED] 3.2 and the
- *              NotImplementedError of its 5.1 interface table)
+ *   shard_dim  the dim every parameter is sharded on
+ *   shard_dims [P] one shard dim per parameter, or NULL (= shard_dim for all)
+ * Dim 0 may be uneven (fixed-size chunks, zero padding at the tail,
+ * [RAGGED] 6.4).  Any other dim k must be divisible by shard_size: rank s
+ * holds the s-th of S equal chunks along k, stored contiguously, with no
+ * padding ([RAGGED] 3.2 keeps non-zero dims on the plain chunk/concatenate
+ * path; an uneven non-zero dim is FSDP_ENOTIMPL, as the NotImplementedError
+ * of its 5.1 interface table).  A dim outside [0, ndim) is FSDP_EINVAL.
+ * Below, for a parameter sharded on k: outer = product of the dims before
+ * k (1 for k = 0), inner = product of the dims after k, and "rows" are
+ * indices along k; rank s's chunk is outer runs of row_len * inner elements.
  */
 typedef struct fsdp_bucket {
   int32_t n_params;
   const int32_t* ndim;
   const int64_t* shape;
   int32_t shard_dim;
+  const int32_t* shard_dims;
 } fsdp_bucket_t;
 
 /* ------------------------------------------------------------------------
@@ -106,8 +117,8 @@ typedef struct fsdp_bucket {
  * Layout of a bucket sharded over shard_size ranks ([RAGGED] 6.4).
  * Outputs (any may be NULL): *slice_numel = I; padded[P], in_off[P];
  * row_off[P*S] and row_len[P*S], indexed [i*S + s].
- * Errors: FSDP_EINVAL (shard_size < 1, ndim < 1, negative dim, overflow),
- * FSDP_ENOTIMPL (shard_dim != 0).
+ * Errors: FSDP_EINVAL (shard_size < 1, ndim < 1, negative dim, shard dim
+ * out of range, overflow), FSDP_ENOTIMPL (uneven non-zero shard dim).
  */
 int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size,
                        int64_t* slice_numel, int64_t* padded, int64_t* in_off,
@@ -145,7 +156,8 @@ int fsdp_group_ranks(int32_t rank_size, int32_t shard_size,
  * zeros over the rest of its padded region.  All S slices are packed, so
  * the AllGather of one shard group is the identity on `ag`.
  *   shards  [S*P] device pointers, rank-major: shards[s*P + i] holds
- *           row_len(i,s) * inner_i contiguous elements (NULL allowed when 0)
+ *           outer_i * row_len(i,s) * inner_i contiguous elements (rank s's
+ *           chunk in its own dense layout; NULL allowed when 0)
  *   ag      device buffer of S*I elements (written entirely)
  *   dtype   FSDP_F32 / FSDP_BF16 / FSDP_F16 (element size only)
  */
@@ -154,8 +166,9 @@ int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dty
 
 /*
  * AG copy-out ([HYPER] 2.1 copy-out; [RAGGED] 6.4: only the logical shape
- * is exposed): full parameter i = concatenation over s of the row_len(i,s)
- * data rows of slice s's region of parameter i.  Padding is never read.
+ * is exposed): full parameter i = concatenation along its shard dim over s
+ * of rank s's chunk in slice s's region of parameter i.  Padding is never
+ * read.
  *   ag     device buffer of S*I elements
  *   full   [P] device pointers, full[i] holds N0_i * inner_i elements
  */
@@ -164,8 +177,8 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
 
 /*
  * RS copy-in ([RAGGED] 6.4 fused RS copy-in): for every rank g, chunk s of
- * every gradient i goes to rs_in[g][s*I + in_off_i ...], zero padded to
- * padded_i.
+ * every gradient i (along its shard dim, in dense layout) goes to
+ * rs_in[g][s*I + in_off_i ...], zero padded to padded_i.
  *   grads  [R*P] device pointers, grads[g*P + i] holds N0_i * inner_i elements
  *   rs_in  [R] device pointers, each S*I elements (written entirely)
  */
@@ -189,9 +202,9 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
 
 /*
  * RS copy-in and RS in one pass, without materialising the RS input:
- *   rs_out[d*S+s][in_off_i + k] = op( sum_{t=0..S-1} grads[(d*S+t)*P + i][row_off(i,s)*inner_i + k] )
- * for k < row_len(i,s)*inner_i, and 0 over the rest of parameter i's padded
- * region.  Bit for bit the result of fsdp_rs_copy_in followed by
+ *   rs_out[d*S+s][in_off_i + k] = op( sum_{t=0..S-1} chunk_s(grads[(d*S+t)*P + i])[k] )
+ * for k below the chunk's size, and 0 over the rest of parameter i's padded
+ * region (chunk_s = rank s's chunk along the shard dim, dense layout).  Bit for bit the result of fsdp_rs_copy_in followed by
  * fsdp_rs_reduce (same order, same rounding); each gradient element is read
  * once and no S*I buffer is written ([RAGGED] 6.4 padded RS input;
  * [FS-MD] 3.3 RS on the shard group).

@@ -109,9 +109,11 @@ class BucketLayout:
 
     shapes        logical parameter shapes, bucket order
     S             shard group size
-    chunk_rows[i] padded dim-0 of parameter i (the padded_sharded_param_size
-                  dim 0 of [RAGGED] 6.4)
-    inner[i]      product of the non-sharded dims (1 for a 1-D parameter)
+    shard_dims[i] the dim parameter i is sharded on
+    outer[i]      product of the dims before the shard dim (1 for dim 0)
+    chunk_rows[i] padded length of the shard dim per rank (for dim 0 the
+                  padded_sharded_param_size dim 0 of [RAGGED] 6.4)
+    inner[i]      product of the dims after the shard dim
     padded[i]     chunk_rows[i] * inner[i], elements per rank slice
     in_off[i]     offset of parameter i inside one rank slice; advances by
                   padded elements only ([RAGGED] 6.4, fused RS copy-in)
@@ -121,6 +123,8 @@ class BucketLayout:
 
     shapes: List[Tuple[int, ...]]
     S: int
+    shard_dims: List[int] = field(default_factory=list)
+    outer: List[int] = field(default_factory=list)
     chunk_rows: List[int] = field(default_factory=list)
     inner: List[int] = field(default_factory=list)
     padded: List[int] = field(default_factory=list)
@@ -131,37 +135,72 @@ class BucketLayout:
 
 
 def bucket_layout(shapes: Sequence[Sequence[int]], shard_size: int,
-                  shard_dim: int = 0) -> BucketLayout:
-    """Layout of a bucket of parameters sharded on dim 0.
+                  shard_dim: int = 0, shard_dims: Sequence[int] = None) -> BucketLayout:
+    """Layout of a bucket of parameters, each sharded on its shard dim.
 
-    Only dim 0 is supported for non-uniform sharding ([RAGGED] 3.2 and the
-    interface table of 5.1 raise NotImplementedError otherwise); a 0-d
-    parameter has no dim 0 and is rejected.
+    Dim 0 may be non-uniform ([RAGGED] 6.4, fixed-size chunks, zero padding
+    at the tail).  Any other dim must divide evenly ([RAGGED] 3.2 keeps it on
+    the plain chunk/concatenate path, and the interface table of 5.1 raises
+    NotImplementedError for an uneven non-zero dim): no padding, rank s holds
+    the s-th of S equal chunks along that dim.  shard_dims gives one dim per
+    parameter (default: shard_dim for all); a 0-d parameter has no dim to
+    shard and is rejected.
     """
-    if shard_dim != 0:
-        raise NotImplementedError("only shard_dim == 0 is supported")
     if shard_size < 1:
         raise ValueError("shard_size must be >= 1")
-    lay = BucketLayout(shapes=[tuple(int(d) for d in sh) for sh in shapes], S=shard_size)
+    S = shard_size
+    shapes = [tuple(int(d) for d in sh) for sh in shapes]
+    dims = [shard_dim] * len(shapes) if shard_dims is None else [int(k) for k in shard_dims]
+    if len(dims) != len(shapes):
+        raise ValueError("one shard dim per parameter")
+    lay = BucketLayout(shapes=shapes, S=S)
     offset = 0
-    for shape in lay.shapes:
+    for shape, k in zip(lay.shapes, dims):
         if len(shape) < 1:
             raise ValueError("a parameter needs at least one dimension")
         if any(d < 0 for d in shape):
             raise ValueError("negative dimension")
+        if not 0 <= k < len(shape):
+            raise ValueError("shard dim out of range")
+        outer = 1
+        for d in shape[:k]:
+            outer *= d
         inner = 1
-        for d in shape[1:]:
+        for d in shape[k + 1:]:
             inner *= d
-        chunk, offs, lens = dim0_chunk(shape[0], shard_size)
+        if k == 0:
+            chunk, offs, lens = dim0_chunk(shape[0], S)
+        else:
+            if shape[k] % S:
+                raise NotImplementedError("a non-zero shard dim must divide evenly by the shard size")
+            chunk = shape[k] // S
+            offs, lens = [s * chunk for s in range(S)], [chunk] * S
+        lay.shard_dims.append(k)
+        lay.outer.append(outer)
         lay.chunk_rows.append(chunk)
         lay.inner.append(inner)
-        lay.padded.append(chunk * inner)
+        lay.padded.append(outer * chunk * inner)
         lay.in_off.append(offset)
         lay.row_off.append(offs)
         lay.row_len.append(lens)
-        offset += chunk * inner
+        offset += outer * chunk * inner
     lay.I = offset
     return lay
+
+
+def _shard_shape(lay: BucketLayout, i: int, s: int) -> Tuple[int, ...]:
+    shape = list(lay.shapes[i])
+    shape[lay.shard_dims[i]] = lay.row_len[i][s]
+    return tuple(shape)
+
+
+def _chunk(x: np.ndarray, lay: BucketLayout, i: int, s: int) -> np.ndarray:
+    """Rank s's chunk of a full parameter or gradient of parameter i."""
+    k = lay.shard_dims[i]
+    a, n = lay.row_off[i][s], lay.row_len[i][s]
+    idx = [slice(None)] * x.ndim
+    idx[k] = slice(a, a + n)
+    return x[tuple(idx)]
 
 
 def fused_layout(seg_numel: Sequence[int], elem_bytes: int = 4,
@@ -191,18 +230,15 @@ def fused_layout(seg_numel: Sequence[int], elem_bytes: int = 4,
 # ---------------------------------------------------------------------------
 
 def shard_params(params: Sequence[np.ndarray], lay: BucketLayout) -> List[List[np.ndarray]]:
-    """shards[s][i]: rows [row_off, row_off + row_len) of parameter i.
+    """shards[s][i]: rank s's chunk of parameter i along its shard dim
+    (rows [row_off, row_off + row_len) for dim 0), stored contiguously.
 
     [RAGGED] 6.4: the sharded parameter is the actual local rows, possibly
     zero rows; padding is not part of it.
     """
     out = []
     for s in range(lay.S):
-        row = []
-        for i, x in enumerate(params):
-            a = lay.row_off[i][s]
-            row.append(x[a:a + lay.row_len[i][s]])
-        out.append(row)
+        out.append([np.ascontiguousarray(_chunk(x, lay, i, s)) for i, x in enumerate(params)])
     return out
 
 
@@ -248,9 +284,9 @@ def ag_copy_out(ag: np.ndarray, lay: BucketLayout) -> List[np.ndarray]:
         pieces = []
         for s in range(lay.S):
             base = s * lay.I + lay.in_off[i]
-            pieces.append(ag[base:base + lay.row_len[i][s] * lay.inner[i]])
-        full = np.concatenate(pieces) if pieces else np.zeros(0, ag.dtype)
-        out.append(full.reshape(shape))
+            n = lay.outer[i] * lay.row_len[i][s] * lay.inner[i]
+            pieces.append(ag[base:base + n].reshape(_shard_shape(lay, i, s)))
+        out.append(np.concatenate(pieces, axis=lay.shard_dims[i]).reshape(shape))
     return out
 
 
@@ -269,10 +305,9 @@ def rs_copy_in(grads: Sequence[np.ndarray], lay: BucketLayout, dtype=np.float32)
     """
     buf = np.zeros(lay.S * lay.I, dtype=dtype)
     for i in range(len(lay.shapes)):
-        g = np.ascontiguousarray(grads[i])
+        g = np.ascontiguousarray(grads[i]).reshape(lay.shapes[i])
         for s in range(lay.S):
-            a, n = lay.row_off[i][s], lay.row_len[i][s]
-            flat = g[a:a + n].reshape(-1)
+            flat = np.ascontiguousarray(_chunk(g, lay, i, s)).reshape(-1)
             base = s * lay.I + lay.in_off[i]
             buf[base:base + flat.size] = flat
     return buf
@@ -406,10 +441,9 @@ def sharded_grad(rs_out_g: np.ndarray, lay: BucketLayout, i: int, s: int) -> np.
     [RAGGED] 6.4: only the sharded_size rows are written back; the padded
     tail of the RS output region is dropped.
     """
-    rest = lay.shapes[i][1:]
-    n = lay.row_len[i][s]
+    n = lay.outer[i] * lay.row_len[i][s] * lay.inner[i]
     a = lay.in_off[i]
-    return rs_out_g[a:a + n * lay.inner[i]].reshape((n,) + tuple(rest))
+    return rs_out_g[a:a + n].reshape(_shard_shape(lay, i, s))
 
 
 # ---------------------------------------------------------------------------

@@ -73,6 +73,16 @@ def test_bucket_layout_matches_oracle(L, shapes, S):
     assert got.row_len == want.row_len
 
 
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_bucket_layout_nonzero_shard_dims_match_oracle(L, S):
+    shapes = [(6, 8), (4, 12, 3), (5, 3, 8), (7, 3), (16,), (2, 0, 4), (3, 4, 4)]
+    dims = [1, 1, 2, 0, 0, 2, 2]
+    got = hp.fsdp_bucket_layout(shapes, S, shard_dims=dims)
+    want = O.bucket_layout(shapes, S, shard_dims=dims)
+    assert (got.I, got.padded, got.in_off, got.row_off, got.row_len) == \
+        (want.I, want.padded, want.in_off, want.row_off, want.row_len)
+
+
 def test_fused_layout_matches_oracle(L, golden):
     for c in golden["fused"]:
         assert hp.fsdp_fused_layout(c["seg_numel"], c["elem_bytes"]) == (c["offsets"], c["F"])
@@ -97,8 +107,11 @@ def test_group_ranks_match_oracle(L, golden):
 
 def test_query_errors(L):
     with pytest.raises(hp.FSDPError) as e:
-        hp.fsdp_bucket_layout([(4, 4)], 2, shard_dim=1)
-    assert e.value.code == 2 and "dim-0" in e.value.message
+        hp.fsdp_bucket_layout([(4, 3)], 2, shard_dim=1)
+    assert e.value.code == 2 and "divisible" in e.value.message
+    with pytest.raises(hp.FSDPError) as e:
+        hp.fsdp_bucket_layout([(4,)], 2, shard_dim=1)
+    assert e.value.code == 1
     with pytest.raises(hp.FSDPError) as e:
         hp.fsdp_bucket_layout([()], 2)
     assert e.value.code == 1

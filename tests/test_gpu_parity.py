@@ -490,3 +490,54 @@ def test_backward_pipeline_two_streams_matches_serial_and_oracle(fused_rs):
             for g in range(R):
                 m = first_mismatch(bits(fb.fused[g]), np_bits(want[l][g]))
                 assert m == "", f"rep {rep} layer {l} rank {g}: {m}"
+
+
+@pytest.mark.parametrize("S,R,dtype", [(4, 8, torch.float32), (2, 4, torch.bfloat16), (1, 2, torch.float32),
+                                       (8, 8, torch.float32)])
+def test_nonzero_shard_dims_all_steps(S, R, dtype):
+    """A bucket mixing dim-0 (ragged) parameters with parameters sharded on
+    dims 1 and 2 (divisible): every step against the oracle."""
+    shapes = [(6, 8), (4, 16, 3), (5, 3, 8), (7, 3), (16,), (64, 1024), (3, 4, 8)]
+    dims = [1, 1, 2, 0, 0, 1, 2]
+    note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype}")
+    w = W.Workload(f"dims_{S}", 600 + S, R, S, tuple(shapes), dtype, ("normal", 1.0), ("normal", 1.0),
+                   ("sum", "avg"), W.ALL_STEPS)
+    params, grads = W.params(w), W.grads(w, dtype=dtype)
+    lay = O.bucket_layout(shapes, S, shard_dims=dims)
+    P, I = len(shapes), lay.I
+    xs = [to_oracle(p) for p in params]
+    np_dt = np.float32 if dtype == torch.float32 else np.uint16
+    ag_o = O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt)
+    dparams = [p.cuda() for p in params]
+    keep, shards = [], []
+    for s in range(S):
+        for i in range(P):
+            v = dparams[i].narrow(dims[i], lay.row_off[i][s], lay.row_len[i][s]).contiguous().reshape(-1)
+            g = Guarded(v.numel(), dtype, (s + i) % 5)
+            g.t.copy_(v)
+            keep.append(g)
+            shards.append(g.t)
+    ag = Guarded(S * I, dtype, 3)
+    hp.fsdp_ag_copy_in(shapes, S, shards, ag.t, shard_dims=dims)
+    full = [Guarded(p.numel(), dtype, 1) for p in params]
+    hp.fsdp_ag_copy_out(shapes, S, ag.t, [f.t for f in full], shard_dims=dims)
+    torch.cuda.synchronize()
+    assert ag.guards_intact() and first_mismatch(bits(ag.t), np_bits(ag_o)) == ""
+    for i in range(P):
+        assert full[i].guards_intact() and np.array_equal(bits(full[i].t), np_bits(xs[i]))
+    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
+    rs_o = [O.rs_copy_in(gnp[g], lay, np_dt) for g in range(R)]
+    dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    rs_in = [Guarded(S * I, dtype, g % 3) for g in range(R)]
+    hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in], shard_dims=dims)
+    for op in (O.SUM, O.AVG):
+        want = O.rs_reduce(rs_o, I, R, S, op)
+        out = [Guarded(I, dtype, 1 + g % 2) for g in range(R)]
+        hp.fsdp_rs_reduce(shapes, R, S, R // S, op, [b.t for b in rs_in], [o.t for o in out], shard_dims=dims)
+        out2 = [Guarded(I, dtype, g % 4) for g in range(R)]
+        hp.fsdp_rs_copy_reduce(shapes, R, S, R // S, op, dgrads, [o.t for o in out2], shard_dims=dims)
+        torch.cuda.synchronize()
+        for g in range(R):
+            assert rs_in[g].guards_intact() and first_mismatch(bits(rs_in[g].t), np_bits(rs_o[g])) == ""
+            assert out[g].guards_intact() and first_mismatch(bits(out[g].t), np_bits(want[g])) == ""
+            assert out2[g].guards_intact() and first_mismatch(bits(out2[g].t), np_bits(want[g])) == ""

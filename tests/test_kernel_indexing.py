@@ -210,21 +210,25 @@ def check_reduce(jobs, ptr, shift, es=4):
 # tables like the planner's, on fake addresses
 # ---------------------------------------------------------------------------
 
-def layout(shapes, S):
-    chunk, inner, padded, in_off, ro, rl = [], [], [], [], [], []
+def layout(shapes, S, dims=None):
+    dims = dims or [0] * len(shapes)
+    chunk, inner, outer, dk, padded, in_off, ro, rl = [], [], [], [], [], [], [], []
     off = 0
-    for sh in shapes:
-        n0 = sh[0]
-        inn = int(np.prod(sh[1:])) if len(sh) > 1 else 1
-        c = -(-n0 // S)
+    for sh, k in zip(shapes, dims):
+        n0 = sh[k]
+        inn = int(np.prod(sh[k + 1:])) if len(sh) > k + 1 else 1
+        out = int(np.prod(sh[:k])) if k else 1
+        c = -(-n0 // S) if k == 0 else n0 // S
         chunk.append(c)
         inner.append(inn)
-        padded.append(c * inn)
+        outer.append(out)
+        dk.append(n0)
+        padded.append(out * c * inn)
         in_off.append(off)
         ro.append([min(s * c, n0) for s in range(S)])
         rl.append([min(c, n0 - min(s * c, n0)) for s in range(S)])
-        off += c * inn
-    return dict(I=off, inner=inner, padded=padded, in_off=in_off, ro=ro, rl=rl)
+        off += out * c * inn
+    return dict(I=off, inner=inner, outer=outer, dk=dk, padded=padded, in_off=in_off, ro=ro, rl=rl)
 
 
 def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
@@ -239,15 +243,37 @@ def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
     return segs
 
 
-def ag_copy_out_segs(shapes, S, es, ag, full_addr):
-    L = layout(shapes, S)
+def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None):
+    L = layout(shapes, S, dims)
     segs = []
     for i in range(len(shapes)):
         for s in range(S):
-            n = L["rl"][i][s] * L["inner"][i] * es
-            if n:
-                segs.append((ag + (s * L["I"] + L["in_off"][i]) * es,
-                             full_addr(i) + L["ro"][i][s] * L["inner"][i] * es, n, n))
+            run = L["rl"][i][s] * L["inner"][i]
+            if run == 0:
+                continue
+            for o in range(L["outer"][i]):
+                segs.append((ag + (s * L["I"] + L["in_off"][i] + o * run) * es,
+                             full_addr(i) + (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es,
+                             run * es, run * es))
+    return segs
+
+
+def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None):
+    """One rank's RS copy-in segments, as fsdp_rs_copy_in builds them."""
+    L = layout(shapes, S, dims)
+    segs = []
+    for s in range(S):
+        for i in range(len(shapes)):
+            if L["padded"][i] == 0:
+                continue
+            run = L["rl"][i][s] * L["inner"][i]
+            d0 = rs_in_addr + (s * L["I"] + L["in_off"][i]) * es
+            for o in range(L["outer"][i]):
+                last = o + 1 == L["outer"][i]
+                total = (L["padded"][i] - o * run) * es if last else run * es
+                src = grad_addr(i) + (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es
+                if total:
+                    segs.append((src if run else 0, d0 + o * run * es, run * es, total))
     return segs
 
 
@@ -329,22 +355,27 @@ def test_reduce_jobs_cover_exactly(shift, es):
             check_reduce(jobs, ptr, shift, es)
 
 
-def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr):
-    """Jobs as fsdp_rs_copy_reduce builds them: one per (rank, parameter)."""
-    L = layout(shapes, S)
+def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None):
+    """Jobs as fsdp_rs_copy_reduce builds them: one per (rank, parameter,
+    run of the chunk)."""
+    L = layout(shapes, S, dims)
     jobs, ptr = [], []
     for g in range(R):
         d, s = divmod(g, S)
         for i, sh in enumerate(shapes):
             if L["padded"][i] == 0:
                 continue
-            data = L["rl"][i][s] * L["inner"][i] * es
-            row0 = L["ro"][i][s] * L["inner"][i] * es
-            src0 = len(ptr)
-            ptr += [grad_addr(d * S + t, i) + row0 if data else 0 for t in range(S)]
-            dst0 = len(ptr)
-            ptr.append(out_addr(g) + L["in_off"][i] * es)
-            jobs.append((L["padded"][i] * es, data, src0, S, dst0, 1))
+            run = L["rl"][i][s] * L["inner"][i]
+            for o in range(L["outer"][i]):
+                last = o + 1 == L["outer"][i]
+                src_off = (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es
+                src0 = len(ptr)
+                ptr += [grad_addr(d * S + t, i) + src_off if run else 0 for t in range(S)]
+                dst0 = len(ptr)
+                ptr.append(out_addr(g) + (L["in_off"][i] + o * run) * es)
+                nbytes = ((L["padded"][i] - o * run) if last else run) * es
+                if nbytes:
+                    jobs.append((nbytes, run * es, src0, S, dst0, 1))
     return jobs, ptr
 
 
@@ -436,3 +467,26 @@ def test_realign_neighbour_is_next_block():
                 else:
                     got = blocks[(u + 1, 0)] if u + 1 < U else tail
                 assert got == blocks[(u, l)] + 1
+
+
+MIXED_DIMS = [([(6, 8), (4, 12, 3), (5, 3, 8), (7, 3), (16,), (3, 4, 4)], [1, 1, 2, 0, 0, 2])]
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", (9, 14))
+def test_nonzero_shard_dim_tables_cover_exactly(S, es, shift):
+    shapes, dims = MIXED_DIMS[0]
+    rng = np.random.default_rng(S + es)
+    base = 1 << 32
+    ag = base + es * int(rng.integers(0, 9))
+    full = {i: base + (1 << 30) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    check_copy(ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims), es, shift)
+    grads = {i: (1 << 40) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    check_copy(rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + es * 3, dims), es, shift)
+    R = 2 * S
+    gr = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + es * int(rng.integers(0, 8))
+          for g in range(R) for i in range(len(shapes))}
+    outs = {g: (1 << 46) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)}
+    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims)
+    check_reduce(jobs, ptr, shift, es)

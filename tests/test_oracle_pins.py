@@ -415,8 +415,10 @@ def test_fused_layout_golden(golden):
 
 
 def test_oracle_rejects():
-    with pytest.raises(NotImplementedError):
-        O.bucket_layout([(4, 4)], 2, shard_dim=1)
+    with pytest.raises(NotImplementedError):  # uneven on a non-zero dim
+        O.bucket_layout([(4, 3)], 2, shard_dim=1)
+    with pytest.raises(ValueError):  # no such dim
+        O.bucket_layout([(4,)], 2, shard_dim=1)
     with pytest.raises(ValueError):
         O.bucket_layout([()], 2)
     with pytest.raises(ValueError):
@@ -547,3 +549,60 @@ def test_planted_mistake_is_caught(mutant, golden, monkeypatch):
 
 def test_unmutated_oracle_passes_all_pins(golden):
     assert _all_pins(golden) == []
+
+
+# ---------------------------------------------------------------------------
+# non-zero shard dims (divisible only)
+# ---------------------------------------------------------------------------
+
+MIXED = [((6, 8), 1), ((4, 12, 3), 1), ((5, 3, 8), 2), ((7, 3), 0), ((16,), 0), ((2, 0, 4), 2)]
+
+
+def test_nonzero_shard_dim_matches_torch_chunk_and_roundtrips():
+    for S in (1, 2, 4):
+        shapes = [sh for sh, k in MIXED]
+        dims = [k for sh, k in MIXED]
+        lay = O.bucket_layout(shapes, S, shard_dims=dims)
+        xs = [(RNG.standard_normal(sh) + 3).astype(np.float32) for sh in shapes]
+        shards = O.shard_params(xs, lay)
+        for i, (x, k) in enumerate(zip(xs, dims)):
+            if k == 0:
+                continue
+            pieces = torch.chunk(torch.from_numpy(x), S, dim=k)
+            for s in range(S):
+                assert np.array_equal(shards[s][i], pieces[s].numpy())
+            assert lay.padded[i] * S == x.size  # even: no padding
+        ag = O.ag_copy_in(shards, lay, np.float32)
+        outs = O.ag_copy_out(O.all_gather(ag), lay)
+        assert all(np.array_equal(a, b) for a, b in zip(outs, xs))
+        # slice s, region i = rank s's chunk, contiguous
+        for s in range(S):
+            for i in range(len(shapes)):
+                region = ag[s * lay.I + lay.in_off[i]: s * lay.I + lay.in_off[i] + shards[s][i].size]
+                assert np.array_equal(region, shards[s][i].reshape(-1))
+
+
+def test_nonzero_shard_dim_rejects_uneven():
+    with pytest.raises(NotImplementedError):
+        O.bucket_layout([(6, 7)], 2, shard_dims=[1])
+    with pytest.raises(ValueError):
+        O.bucket_layout([(6,)], 2, shard_dims=[1])
+
+
+@pytest.mark.parametrize("R,S", [(8, 4), (4, 2), (8, 8)])
+def test_nonzero_shard_dim_exact_reduce_scatter(R, S):
+    shapes = [((6, 8), 1), ((4, 8, 3), 1), ((5, 3, 8), 2), ((7, 3), 0)]
+    lay = O.bucket_layout([sh for sh, _ in shapes], S, shard_dims=[k for _, k in shapes])
+    gi = [[RNG.integers(-8, 9, size=sh).astype(np.float32) for sh, _ in shapes] for _ in range(R)]
+    rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
+    outs = O.rs_reduce(rs_in, lay.I, R, S, O.SUM)
+    for g in range(R):
+        d, s = divmod(g, S)
+        for i, (sh, k) in enumerate(shapes):
+            tot = sum(torch.from_numpy(gi[m][i]).to(torch.int64) for m in range(d * S, d * S + S))
+            pieces = torch.chunk(tot, S, dim=k) if sh[k] else ()
+            empty = list(sh)
+            empty[k] = 0
+            want = pieces[s] if s < len(pieces) else torch.zeros(empty, dtype=torch.int64)
+            got = O.sharded_grad(outs[g], lay, i, s)
+            assert got.shape == tuple(want.shape) and np.array_equal(got.astype(np.int64), want.numpy())
