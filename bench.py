@@ -45,9 +45,10 @@ KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kern
                   "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
                   "rs_copy_reduce": "reduce_kernel", "fused_ar": "reduce_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
-# the kernels and the planner that sets their launch shapes (chunk sizes)
+# what fixes the kernels' memory traffic: their code, the descriptor formats
+# and the launch tuning (chunk sizes, store policy)
 KERNEL_SRC = [os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", f)
-              for f in ("kernels.hip", "fsdp_flat.cpp", "plan.hpp")]
+              for f in ("kernels.hip", "plan.hpp", "tuning.hpp")]
 
 
 def log(msg: str) -> None:

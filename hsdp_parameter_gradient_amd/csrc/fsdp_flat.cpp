@@ -31,6 +31,7 @@
 
 #include "fsdp_flat.h"
 #include "plan.hpp"
+#include "tuning.hpp"
 
 namespace {
 
@@ -189,118 +190,151 @@ int check_overlap(std::vector<Span> outs, const std::vector<Span>& ins) {
 }
 
 // ---------------------------------------------------------------------------
-// tuning (read once; the defaults are the measured best on MI355X)
+// plan cache: per call signature, the call's descriptor table in device
+// memory and its launch parameters.  A repeated call (same entry point,
+// arguments, shapes and pointers, same device) skips validation, planning
+// and the upload: its result depends on nothing else.
 // ---------------------------------------------------------------------------
 
-struct Tuning {
-  uint32_t copy_shift = 14;    // 16 KiB of destination per chunk
-  uint32_t reduce_shift = 13;  // 8 KiB of destination per chunk
-  uint32_t max_grid = 1u << 20;
-  // Store policy.  An output that the next step of the path reads back (the
-  // AG buffer read by copy-out, the RS input read by the RS, the RS output
-  // read by the fused AR) keeps normal stores while it is at most this many
-  // bytes, so that part of it is still in the 256 MB MALL when it is read;
-  // larger outputs, and the path's final outputs (the full parameters, the
-  // AR result), use nontemporal stores.  Measured on MI355X: streaming stores
-  // are 3-5% faster on multi-GB buckets and 8% slower on a 0.4 GB one.
-  uint64_t cached_store_max = uint64_t(512) << 20;
+// Everything a call's result depends on, as 64-bit words.
+class Key {
+ public:
+  explicit Key(uint64_t entry) {
+    int device = 0;
+    ok_ = hipGetDevice(&device) == hipSuccess;
+    w_.push_back(entry);
+    w_.push_back((uint64_t)device);
+  }
+  void add(int64_t v) { w_.push_back((uint64_t)v); }
+  // false if the bucket's arrays cannot be read (validation then reports it)
+  bool bucket(const fsdp_bucket_t* b) {
+    if (!b || b->n_params < 0 || (b->n_params > 0 && (!b->ndim || !b->shape))) return ok_ = false;
+    add(b->n_params);
+    add(b->shard_dim);
+    add(b->shard_dims ? 1 : 0);
+    size_t nshape = 0;
+    for (int32_t i = 0; i < b->n_params; ++i) {
+      if (b->ndim[i] < 0) return ok_ = false;
+      add(b->ndim[i]);
+      nshape += (size_t)b->ndim[i];
+    }
+    for (size_t k = 0; k < nshape; ++k) add(b->shape[k]);
+    if (b->shard_dims)
+      for (int32_t i = 0; i < b->n_params; ++i) add(b->shard_dims[i]);
+    return ok_;
+  }
+  bool ptrs(const void* const* p, int64_t n) {
+    if (n < 0 || (n > 0 && !p)) return ok_ = false;
+    for (int64_t k = 0; k < n; ++k) w_.push_back((uint64_t)p[k]);
+    return ok_;
+  }
+  bool valid() const { return ok_; }
+  uint64_t hash() const {
+    uint64_t h = 1469598103934665603ull;
+    for (uint64_t x : w_) {
+      h ^= x;
+      h *= 0x9E3779B97F4A7C15ull;
+      h ^= h >> 29;
+    }
+    return h;
+  }
+  bool operator==(const Key& o) const { return w_ == o.w_; }
+
+ private:
+  std::vector<uint64_t> w_;
+  bool ok_ = true;
 };
 
-const Tuning& tuning() {
-  static Tuning t = [] {
-    Tuning x;
-    if (const char* e = getenv("FSDP_COPY_CHUNK_SHIFT")) x.copy_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
-    if (const char* e = getenv("FSDP_REDUCE_CHUNK_SHIFT")) x.reduce_shift = (uint32_t)std::max(9, std::min(24, atoi(e)));
-    if (const char* e = getenv("FSDP_MAX_GRID")) x.max_grid = (uint32_t)std::max(1, atoi(e));
-    if (const char* e = getenv("FSDP_CACHED_STORE_MAX_MIB")) x.cached_store_max = uint64_t(std::max(0, atoi(e))) << 20;
-    return x;
-  }();
-  return t;
-}
+enum : uint64_t { kAgCopyIn = 1, kAgCopyOut, kRsCopyIn, kRsReduce, kRsCopyReduce, kFusedAr };
 
-// ---------------------------------------------------------------------------
-// descriptor-table cache (device memory, keyed by content and device)
-// ---------------------------------------------------------------------------
+// A prepared launch.
+struct Plan {
+  bool launch = false;  // false: nothing to enqueue
+  bool reduce = false;  // seg_copy_kernel or reduce_kernel
+  void* dev = nullptr;  // the descriptor table (owned by the cache entry)
+  size_t bytes = 0;
+  uint32_t n_items = 0;
+  uint64_t n_chunks = 0;
+  uint32_t shift = 0;
+  int es = 0;
+  uint32_t nsrc = 0;
+  int avg = 0;
+  int nts = 0;
+};
 
 struct Entry {
-  int device;
-  std::vector<uint8_t> host;  // the table; also the key
+  Key key;
   uint64_t hash;
-  void* dev = nullptr;
+  Plan plan;
 };
 
-constexpr size_t kMaxEntries = 128;
+constexpr size_t kMaxEntries = 256;
+constexpr size_t kMaxTableBytes = size_t(256) << 20;
 
 std::mutex g_mu;
 std::list<Entry> g_lru;  // front = most recent
 std::unordered_map<uint64_t, std::vector<std::list<Entry>::iterator>> g_index;
-
-uint64_t table_hash(const std::vector<uint8_t>& t, int device) {
-  // 8 bytes at a time; a full compare settles collisions
-  uint64_t h = 1469598103934665603ull ^ (uint64_t)device;
-  const size_t nw = t.size() / 8;
-  const uint64_t* w = reinterpret_cast<const uint64_t*>(t.data());
-  for (size_t k = 0; k < nw; ++k) {
-    h ^= w[k];
-    h *= 0x9E3779B97F4A7C15ull;
-    h ^= h >> 29;
-  }
-  for (size_t k = nw * 8; k < t.size(); ++k) h = (h ^ t[k]) * 1099511628211ull;
-  return h;
-}
+size_t g_table_bytes = 0;
 
 void drop_entry(std::list<Entry>::iterator it) {
   auto& v = g_index[it->hash];
   v.erase(std::remove(v.begin(), v.end(), it), v.end());
   if (v.empty()) g_index.erase(it->hash);
-  if (it->dev) (void)hipFree(it->dev);
+  if (it->plan.dev) (void)hipFree(it->plan.dev);
+  g_table_bytes -= it->plan.bytes;
   g_lru.erase(it);
 }
 
-// Device copy of `table` on the current device.  A table seen before is
-// reused; a new one is uploaded with a blocking copy, so it is complete
-// before anything is enqueued on any stream (no cross-stream ordering to
-// track, and steady-state calls make no HIP call besides the launch).
-int get_table(std::vector<uint8_t>&& table, void** dev) {
-  int device = 0;
-  hipError_t e = hipGetDevice(&device);
-  if (e != hipSuccess) return fail(FSDP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-  const uint64_t h = table_hash(table, device);
+int enqueue(const Plan& p, hipStream_t stream) {
+  if (!p.launch) return ok();
+  const uint32_t max_grid = fsdp::tuning().max_grid;
+  int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
+                                         p.nts, stream)
+                    : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream);
+  if (he != hipSuccess)
+    return fail(FSDP_EHIP, "%s launch: %s", p.reduce ? "reduce" : "seg_copy", hipGetErrorString((hipError_t)he));
+  return ok();
+}
+
+// Launch the cached plan of `key`, if there is one.
+bool launch_cached(const Key& key, hipStream_t stream, int* rc) {
+  if (!key.valid()) return false;
+  const uint64_t h = key.hash();
   std::lock_guard<std::mutex> lock(g_mu);
   auto found = g_index.find(h);
-  if (found != g_index.end()) {
-    for (auto it : found->second) {
-      if (it->device == device && it->host == table) {
-        g_lru.splice(g_lru.begin(), g_lru, it);
-        *dev = it->dev;
-        return FSDP_OK;
-      }
+  if (found == g_index.end()) return false;
+  for (auto it : found->second) {
+    if (it->key == key) {
+      g_lru.splice(g_lru.begin(), g_lru, it);
+      *rc = enqueue(it->plan, stream);
+      return true;
     }
   }
-  if (g_lru.size() >= kMaxEntries) {
+  return false;
+}
+
+// Keep `plan` under `key` (evicting old plans first if needed) and launch it.
+int store_and_launch(Key&& key, Plan&& plan, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_lru.size() >= kMaxEntries || g_table_bytes + plan.bytes > kMaxTableBytes) {
     // tables still in use by queued kernels must outlive them
-    if ((e = hipDeviceSynchronize()) != hipSuccess)
-      return fail(FSDP_EHIP, "hipDeviceSynchronize before evicting tables: %s", hipGetErrorString(e));
-    while (g_lru.size() >= kMaxEntries / 2) drop_entry(std::prev(g_lru.end()));
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      if (plan.dev) (void)hipFree(plan.dev);
+      return fail(FSDP_EHIP, "hipDeviceSynchronize before evicting plans: %s", hipGetErrorString(e));
+    }
+    while (!g_lru.empty() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + plan.bytes > kMaxTableBytes / 2))
+      drop_entry(std::prev(g_lru.end()));
   }
-  Entry ent;
-  ent.device = device;
-  ent.hash = h;
-  ent.host = std::move(table);
-  if ((e = hipMalloc(&ent.dev, ent.host.size())) != hipSuccess)
-    return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", ent.host.size(), hipGetErrorString(e));
-  if ((e = hipMemcpy(ent.dev, ent.host.data(), ent.host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
-    (void)hipFree(ent.dev);
-    return fail(FSDP_EHIP, "upload of a descriptor table: %s", hipGetErrorString(e));
-  }
-  g_lru.push_front(std::move(ent));
+  const uint64_t h = key.hash();
+  g_lru.push_front(Entry{std::move(key), h, plan});
   g_index[h].push_back(g_lru.begin());
-  *dev = g_lru.front().dev;
-  return FSDP_OK;
+  g_table_bytes += plan.bytes;
+  return enqueue(g_lru.front().plan, stream);
 }
 
 // ---------------------------------------------------------------------------
-// table builders
+// planning
 // ---------------------------------------------------------------------------
 
 template <typename T>
@@ -311,65 +345,103 @@ void append(std::vector<uint8_t>& t, const T* p, size_t n) {
 
 enum class Reuse { kReadNext, kFinal };
 
-// Nontemporal stores for this output?  (the policy of Tuning::cached_store_max)
+// Nontemporal stores for this output?  (the policy of fsdp::Tuning::cached_store_max)
 bool stream_stores(Reuse reuse, uint64_t out_bytes) {
-  return reuse == Reuse::kFinal || out_bytes > tuning().cached_store_max;
+  return reuse == Reuse::kFinal || out_bytes > fsdp::tuning().cached_store_max;
 }
 
-// Launch the segmented copy over `segs` (empty segments already dropped).
-int run_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream) {
+// Upload a table (blocking copy into fresh device memory, so it is complete
+// before anything is enqueued on any stream).
+int upload(const std::vector<uint8_t>& table, Plan* p) {
+  hipError_t e = hipMalloc(&p->dev, table.size());
+  if (e != hipSuccess) return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", table.size(), hipGetErrorString(e));
+  if ((e = hipMemcpy(p->dev, table.data(), table.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(p->dev);
+    p->dev = nullptr;
+    return fail(FSDP_EHIP, "upload of a descriptor table: %s", hipGetErrorString(e));
+  }
+  p->bytes = table.size();
+  return FSDP_OK;
+}
+
+// Plan the segmented copy over `segs`.
+int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
   // the kernel's chunk search needs every item non-empty
   segs.erase(std::remove_if(segs.begin(), segs.end(), [](const fsdp::CopySeg& sg) { return sg.total_bytes == 0; }),
              segs.end());
-  if (segs.empty()) return ok();
-  const Tuning& tu = tuning();
+  if (segs.empty()) return FSDP_OK;
+  if (segs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many segments");
+  const fsdp::Tuning& tu = fsdp::tuning();
   std::vector<uint64_t> begin(segs.size());
-  uint64_t n = 0;
+  uint64_t n = 0, out_bytes = 0;
   for (size_t k = 0; k < segs.size(); ++k) {
     begin[k] = n;
     n += fsdp::chunk_count(segs[k].dst, segs[k].total_bytes, tu.copy_shift);
+    out_bytes += segs[k].total_bytes;
   }
-  if (segs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many segments");
   std::vector<uint8_t> table;
   table.reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
   append(table, begin.data(), begin.size());
   append(table, segs.data(), segs.size());
-  void* dev = nullptr;
-  int rc = get_table(std::move(table), &dev);
+  int rc = upload(table, p);
   if (rc) return rc;
-  uint64_t out_bytes = 0;
-  for (const auto& sg : segs) out_bytes += sg.total_bytes;
-  int he = fsdp_launch_seg_copy(es, dev, (uint32_t)segs.size(), n, tu.copy_shift, tu.max_grid,
-                                stream_stores(reuse, out_bytes), stream);
-  if (he != hipSuccess) return fail(FSDP_EHIP, "seg_copy launch: %s", hipGetErrorString((hipError_t)he));
-  return ok();
+  p->launch = true;
+  p->reduce = false;
+  p->n_items = (uint32_t)segs.size();
+  p->n_chunks = n;
+  p->shift = tu.copy_shift;
+  p->es = es;
+  p->nts = stream_stores(reuse, out_bytes);
+  return FSDP_OK;
 }
 
-int run_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg, Reuse reuse,
-               hipStream_t stream) {
+// Plan the reduction over `jobs` (every job with the same operand count).
+int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg, Reuse reuse,
+                Plan* p) {
   jobs.erase(std::remove_if(jobs.begin(), jobs.end(), [](const fsdp::RedJob& jb) { return jb.nbytes == 0; }),
              jobs.end());
-  if (jobs.empty()) return ok();
-  const Tuning& tu = tuning();
+  if (jobs.empty()) return FSDP_OK;
+  if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
+  const fsdp::Tuning& tu = fsdp::tuning();
   std::vector<uint64_t> begin(jobs.size());
-  uint64_t n = 0;
+  uint64_t n = 0, out_bytes = 0;
   for (size_t k = 0; k < jobs.size(); ++k) {
     begin[k] = n;
     n += fsdp::chunk_count(ptrs[jobs[k].dst0], jobs[k].nbytes, tu.reduce_shift);
+    out_bytes += jobs[k].nbytes * jobs[k].ndst;
   }
   std::vector<uint8_t> table;
   append(table, begin.data(), begin.size());
   append(table, jobs.data(), jobs.size());
   append(table, ptrs.data(), ptrs.size());
-  void* dev = nullptr;
-  int rc = get_table(std::move(table), &dev);
+  int rc = upload(table, p);
   if (rc) return rc;
-  uint64_t out_bytes = 0;
-  for (const auto& jb : jobs) out_bytes += jb.nbytes * jb.ndst;
-  int he = fsdp_launch_reduce(es, dev, (uint32_t)jobs.size(), jobs[0].nsrc, n, tu.reduce_shift, tu.max_grid,
-                              avg, stream_stores(reuse, out_bytes), stream);
-  if (he != hipSuccess) return fail(FSDP_EHIP, "reduce launch: %s", hipGetErrorString((hipError_t)he));
-  return ok();
+  p->launch = true;
+  p->reduce = true;
+  p->n_items = (uint32_t)jobs.size();
+  p->n_chunks = n;
+  p->shift = tu.reduce_shift;
+  p->es = es;
+  p->nsrc = jobs[0].nsrc;
+  p->avg = avg;
+  p->nts = stream_stores(reuse, out_bytes);
+  return FSDP_OK;
+}
+
+// Finish a validated call: plan it, cache the plan and launch it.
+int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream) {
+  Plan p;
+  int rc = plan_copy(segs, es, reuse, &p);
+  if (rc) return rc;
+  return store_and_launch(std::move(key), std::move(p), stream);
+}
+
+int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg,
+               Reuse reuse, hipStream_t stream) {
+  Plan p;
+  int rc = plan_reduce(jobs, ptrs, es, avg, reuse, &p);
+  if (rc) return rc;
+  return store_and_launch(std::move(key), std::move(p), stream);
 }
 
 }  // namespace
@@ -438,9 +510,17 @@ int fsdp_group_ranks(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups
 
 int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype,
                     const void* const* shards, void* ag, void* stream) {
+  Key key(kAgCopyIn);
+  if (key.bucket(bucket)) {
+    key.add(shard_size);
+    key.add(dtype);
+    key.add((int64_t)ag);
+    key.ptrs(shards, (int64_t)shard_size * bucket->n_params);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
   Layout L;
-  int rc = make_layout(bucket, shard_size, &L);
-  if (rc) return rc;
+  if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int es = elem_size(dtype);
   if (!es) return fail(FSDP_ENOTIMPL, "dtype %d is not supported", dtype);
   const int32_t S = L.S, P = L.P;
@@ -463,14 +543,22 @@ int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dty
     }
   }
   if ((rc = check_overlap({{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}, ins))) return rc;
-  return run_copy(segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
                      void* const* full, void* stream) {
+  Key key(kAgCopyOut);
+  if (key.bucket(bucket)) {
+    key.add(shard_size);
+    key.add(dtype);
+    key.add((int64_t)ag);
+    key.ptrs(full, bucket->n_params);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
   Layout L;
-  int rc = make_layout(bucket, shard_size, &L);
-  if (rc) return rc;
+  if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int es = elem_size(dtype);
   if (!es) return fail(FSDP_ENOTIMPL, "dtype %d is not supported", dtype);
   const int32_t S = L.S, P = L.P;
@@ -495,13 +583,22 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
-  return run_copy(segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream));
+  return run_copy(std::move(key), segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
                     const void* const* grads, void* const* rs_in, void* stream) {
-  int rc = check_groups(rank_size, shard_size);
-  if (rc) return rc;
+  Key key(kRsCopyIn);
+  if (key.bucket(bucket)) {
+    key.add(rank_size);
+    key.add(shard_size);
+    key.add(dtype);
+    key.ptrs(grads, (int64_t)rank_size * bucket->n_params);
+    key.ptrs(rs_in, rank_size);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
+  if ((rc = check_groups(rank_size, shard_size))) return rc;
   Layout L;
   if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int es = elem_size(dtype);
@@ -541,13 +638,21 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
     }
   }
   if ((rc = check_overlap(outs, ins))) return rc;
-  return run_copy(segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
 int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
                    int32_t op, int32_t dtype, const void* const* rs_in, void* const* rs_out, void* stream) {
-  int rc = check_groups(rank_size, shard_size);
-  if (rc) return rc;
+  Key key(kRsReduce);
+  if (key.bucket(bucket)) {
+    for (int64_t v : {(int64_t)rank_size, (int64_t)shard_size, (int64_t)dp_size, (int64_t)op, (int64_t)dtype})
+      key.add(v);
+    key.ptrs(rs_in, rank_size);
+    key.ptrs(rs_out, rank_size);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
+  if ((rc = check_groups(rank_size, shard_size))) return rc;
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
@@ -581,14 +686,23 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
     ptrs.push_back((uint64_t)rs_out[g]);
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext,
+                    static_cast<hipStream_t>(stream));
 }
 
 int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
                         int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
                         void* stream) {
-  int rc = check_groups(rank_size, shard_size);
-  if (rc) return rc;
+  Key key(kRsCopyReduce);
+  if (key.bucket(bucket)) {
+    for (int64_t v : {(int64_t)rank_size, (int64_t)shard_size, (int64_t)dp_size, (int64_t)op, (int64_t)dtype})
+      key.add(v);
+    key.ptrs(grads, (int64_t)rank_size * bucket->n_params);
+    key.ptrs(rs_out, rank_size);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
+  if ((rc = check_groups(rank_size, shard_size))) return rc;
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
@@ -640,13 +754,25 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
-  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext,
+                    static_cast<hipStream_t>(stream));
 }
 
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
                   int32_t dp_size, int32_t op, int32_t dtype, void* const* fused, void* stream) {
-  int rc = check_groups(rank_size, shard_size);
-  if (rc) return rc;
+  Key key(kFusedAr);
+  if (n_seg >= 0 && (n_seg == 0 || seg_numel)) {
+    for (int64_t v : {(int64_t)n_seg, (int64_t)rank_size, (int64_t)shard_size, (int64_t)dp_size, (int64_t)op,
+                      (int64_t)dtype})
+      key.add(v);
+    for (int32_t j = 0; j < n_seg; ++j) key.add(seg_numel[j]);
+    key.ptrs(fused, rank_size);
+  } else {
+    key.ptrs(nullptr, 1);  // unreadable: validation reports it
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
+  if ((rc = check_groups(rank_size, shard_size))) return rc;
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
@@ -676,7 +802,8 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
     jb.ndst = (uint32_t)D;
     jobs.push_back(jb);
   }
-  return run_reduce(jobs, ptrs, es, op == FSDP_AVG, Reuse::kFinal, static_cast<hipStream_t>(stream));
+  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kFinal,
+                    static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -47,9 +47,12 @@
  *     fsdp_fused_ar, which works in place by definition.
  *   - Padding is written as zero on every call; no output needs to be
  *     cleared beforehand.
- *   - The library keeps a cache of device-resident descriptor tables keyed
- *     by the call's shapes and pointers (at most 128; evicting waits for
- *     the device); fsdp_release_cache() frees it.
+ *   - The library caches a plan per call signature (entry point, sizes,
+ *     shapes, shard dims, pointers, device): the call's descriptor table in
+ *     device memory and its launch parameters.  A repeated call launches its
+ *     plan without validating or planning again (its result cannot differ).
+ *     At most 256 plans and 256 MiB of tables; evicting waits for the
+ *     device.  fsdp_release_cache() frees them all.
  *   - Thread safe; calls that overlap in time on different streams must not
  *     share output buffers.
  */

@@ -541,3 +541,28 @@ def test_nonzero_shard_dims_all_steps(S, R, dtype):
             assert rs_in[g].guards_intact() and first_mismatch(bits(rs_in[g].t), np_bits(rs_o[g])) == ""
             assert out[g].guards_intact() and first_mismatch(bits(out[g].t), np_bits(want[g])) == ""
             assert out2[g].guards_intact() and first_mismatch(bits(out2[g].t), np_bits(want[g])) == ""
+
+
+def test_plan_cache_reuse_and_eviction():
+    """Distinct calls get their own plans; more distinct calls than the
+    cache holds evict old plans (after the device drains) without changing
+    any result; repeated calls reuse plans."""
+    note("[parity] plan cache eviction")
+    shapes = [(7, 8), (5, 3), (16,)]
+    S = 4
+    lay = O.bucket_layout(shapes, S)
+    xs = [torch.randn(sh) for sh in shapes]
+    want = O.ag_copy_in(O.shard_params([x.numpy() for x in xs], lay), lay, np.float32)
+    dparams = [x.cuda() for x in xs]
+    shards, _ = make_shards(dparams, lay, torch.float32)
+    outs = [torch.full((S * lay.I,), float("nan"), device="cuda") for _ in range(300)]
+    for rnd in range(2):
+        for o in outs:
+            o.fill_(float("nan"))
+        for o in outs:  # 300 distinct signatures (the output pointer differs)
+            hp.fsdp_ag_copy_in(shapes, S, shards, o)
+        for o in outs[:20]:  # repeats: cached or re-planned, same result
+            hp.fsdp_ag_copy_in(shapes, S, shards, o)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert np.array_equal(bits(o), np_bits(want))
