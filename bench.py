@@ -63,18 +63,21 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def step_bytes(w, lay, F: int):
+def step_bytes(w, lay, F: int, grad_bytes: int = 4):
+    """Algorithmic bytes of every step (e = parameter element size, g =
+    gradient element size)."""
     import torch
     e = 2 if w.param_dtype in (torch.bfloat16, torch.float16) else 4
+    g = grad_bytes
     R, S, I = w.rank_size, w.shard_size, lay.I
     N = sum(_numel(s) for s in w.param_shapes)
     return {
         "ag_copy_in": N * e + S * I * e,
         "ag_copy_out": 2 * N * e,
-        "rs_copy_in": 4 * R * (N + S * I),
-        "rs_reduce": 4 * R * S * I + 4 * R * I,
-        "rs_copy_reduce": 4 * R * N + 4 * R * I,
-        "fused_ar": 8 * R * F,
+        "rs_copy_in": g * R * (N + S * I),
+        "rs_reduce": g * R * S * I + g * R * I,
+        "rs_copy_reduce": g * R * N + g * R * I,
+        "fused_ar": 2 * g * R * F,
     }
 
 
@@ -151,6 +154,42 @@ def per_step_us(runner, steps, n):
     torch.cuda.synchronize()
     return {name: sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(n)) / n * 1e3
             for j, name in enumerate(steps)}
+
+
+def bucket_variant(w, op, K: int, warmup: int, grad_dtype=None, shard_dims=None):
+    """The whole pass of the workload with bf16 gradients (reduce dtype
+    bf16), or with the 2-D parameters sharded on dim 1: time per pass, GB/s
+    of its algorithmic bytes, and each step's time."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+    R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+    gdt = grad_dtype or torch.float32
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op, grad_dtype=gdt, shard_dims=shard_dims)
+    params = W.params(w, "cuda")
+    grads = W.grads(w, "cuda", dtype=gdt)
+    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+    steps = fb.steps()
+    nbytes = step_bytes(w, fb.layout, fb.F, gdt.itemsize)
+    total = sum(nbytes[s] for s in steps)
+    for _ in range(warmup):
+        fb.step()
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record()
+    for _ in range(K):
+        fb.step()
+    e0.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(e0) / K
+    per = per_step_us(fb, steps, K)
+    out = {"grad_dtype": str(gdt).replace("torch.", ""), "shard_dims": shard_dims, "ms_per_step": round(ms, 4),
+           "bytes_per_step": total, "GB/s": round(total / (ms * 1e-3) / 1e9, 1),
+           "ops": {n: {"us": round(per[n], 2), "GB/s": round(nbytes[n] / (per[n] * 1e-6) / 1e9, 1)} for n in steps}}
+    log(f"  variant grad_dtype={out['grad_dtype']} shard_dims={shard_dims}: step {ms * 1e3:.1f} us, "
+        f"{out['GB/s']:.1f} GB/s")
+    return out
 
 
 def pipeline_variant(w, op, layers: int, reps: int):
@@ -278,6 +317,8 @@ def main():
     ap.add_argument("--workload", default="hsdp_block_h1024_r8_s4_d2")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the bf16-gradient and shard-dim-1 variants")
     ap.add_argument("--pipeline-layers", type=int, default=8,
                     help="layers in the backward-overlap variant (0 = skip it)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -396,6 +437,11 @@ def main():
             f"{f_us:.1f} us, {b / (f_us * 1e-6) / 1e9:.1f} GB/s")
         if args.pipeline_layers > 1 and runner.do_ar:
             variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
+        if not args.no_variants:
+            variants["bf16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.bfloat16)
+            dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
+            if any(dims):
+                variants["shard_dim_1"] = bucket_variant(w, op, K, args.warmup, shard_dims=dims)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -23,6 +23,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <list>
 #include <mutex>
 #include <string>
@@ -364,6 +365,34 @@ int upload(const std::vector<uint8_t>& table, Plan* p) {
   return FSDP_OK;
 }
 
+// Strided blocks: `rows` runs of row_bytes, row r from src + r*src_pitch to
+// dst + r*dst_pitch.  One block item when every row is whole aligned
+// vectors and fits a chunk (the kernels then move whole rows per chunk);
+// otherwise one item per row.
+bool block_ok(std::initializer_list<uint64_t> addrs, uint64_t row_bytes, uint64_t rows, uint32_t shift) {
+  if (rows < 2 || row_bytes == 0 || row_bytes % 16 || row_bytes > (uint64_t(1) << shift)) return false;
+  for (uint64_t a : addrs)
+    if (a % 16) return false;
+  return true;
+}
+
+void push_rows(std::vector<fsdp::CopySeg>& segs, uint64_t src, uint64_t dst, uint64_t row_bytes, uint64_t rows,
+               uint64_t src_pitch, uint64_t dst_pitch) {
+  if (row_bytes == 0 || rows == 0) return;
+  const uint32_t shift = fsdp::tuning().copy_shift;
+  if (block_ok({src, dst, src_pitch, dst_pitch}, row_bytes, rows, shift)) {
+    fsdp::CopySeg sg{src, dst, row_bytes, row_bytes};
+    sg.rows = rows;
+    sg.src_pitch = src_pitch;
+    sg.dst_pitch = dst_pitch;
+    sg.rows_per_chunk = (uint64_t(1) << shift) / row_bytes;
+    segs.push_back(sg);
+    return;
+  }
+  for (uint64_t r = 0; r < rows; ++r)
+    segs.push_back({src + r * src_pitch, dst + r * dst_pitch, row_bytes, row_bytes});
+}
+
 // Plan the segmented copy over `segs`.
 int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
   // the kernel's chunk search needs every item non-empty
@@ -376,8 +405,8 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
   uint64_t n = 0, out_bytes = 0;
   for (size_t k = 0; k < segs.size(); ++k) {
     begin[k] = n;
-    n += fsdp::chunk_count(segs[k].dst, segs[k].total_bytes, tu.copy_shift);
-    out_bytes += segs[k].total_bytes;
+    n += fsdp::item_chunks(segs[k].dst, segs[k].total_bytes, segs[k].rows, segs[k].rows_per_chunk, tu.copy_shift);
+    out_bytes += segs[k].total_bytes * segs[k].rows;
   }
   std::vector<uint8_t> table;
   table.reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
@@ -407,8 +436,9 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
   uint64_t n = 0, out_bytes = 0;
   for (size_t k = 0; k < jobs.size(); ++k) {
     begin[k] = n;
-    n += fsdp::chunk_count(ptrs[jobs[k].dst0], jobs[k].nbytes, tu.reduce_shift);
-    out_bytes += jobs[k].nbytes * jobs[k].ndst;
+    n += fsdp::item_chunks(ptrs[jobs[k].dst0], jobs[k].nbytes, jobs[k].rows, jobs[k].rows_per_chunk,
+                           tu.reduce_shift);
+    out_bytes += jobs[k].nbytes * jobs[k].ndst * jobs[k].rows;
   }
   std::vector<uint8_t> table;
   append(table, begin.data(), begin.size());
@@ -575,11 +605,9 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
       // rank s's chunk: outer runs of row_len*inner elements, dense in the
       // slice, at stride dk*inner in the full parameter
       const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
-      if (run == 0) continue;
-      for (int64_t o = 0; o < L.outer[i]; ++o)
-        segs.push_back({(uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i] + o * run) * es),
-                        (uint64_t)full[i] + (uint64_t)((o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es),
-                        (uint64_t)(run * es), (uint64_t)(run * es)});
+      push_rows(segs, (uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es),
+                (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es), (uint64_t)(run * es),
+                (uint64_t)L.outer[i], (uint64_t)(run * es), (uint64_t)(L.dk[i] * L.inner[i] * es));
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
@@ -624,16 +652,21 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
       for (int32_t i = 0; i < P; ++i) {
         if (L.padded[i] == 0) continue;
         // outer runs of row_len*inner elements from the gradient (stride
-        // dk*inner), dense in the slice; the last run carries the zero tail
+        // dk*inner), dense in the slice, then the zero tail (a dim-0 chunk's
+        // padding rows; outer is 1 there)
         const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
-        const uint64_t g0 = (uint64_t)grads[(size_t)g * P + i];
+        const uint64_t src = (uint64_t)grads[(size_t)g * P + i] +
+                             (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
         const uint64_t d0 = (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es);
-        for (int64_t o = 0; o < L.outer[i]; ++o) {
-          const bool last = o + 1 == L.outer[i];
-          const int64_t total = last ? (L.padded[i] - o * run) * es : run * es;
-          const uint64_t src = g0 + (uint64_t)((o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es);
-          segs.push_back({run ? src : 0, d0 + (uint64_t)(o * run * es), (uint64_t)(run * es), (uint64_t)total});
+        const int64_t data = L.outer[i] * run;  // elements; the tail is padded - data
+        if (L.outer[i] == 1) {
+          segs.push_back({run ? src : 0, d0, (uint64_t)(run * es), (uint64_t)(L.padded[i] * es)});
+          continue;
         }
+        push_rows(segs, src, d0, (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es),
+                  (uint64_t)(run * es));
+        if (L.padded[i] > data)
+          segs.push_back({0, d0 + (uint64_t)(data * es), 0, (uint64_t)((L.padded[i] - data) * es)});
       }
     }
   }
@@ -733,9 +766,33 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     const int32_t d = g / S, s = g % S;
     for (int32_t i = 0; i < P; ++i) {
       if (L.padded[i] == 0) continue;
-      // one job per run of rank s's chunk (outer runs, the last one with
-      // the zero tail)
+      // rank s's chunk: outer runs of row_len*inner elements (stride
+      // dk*inner in the gradients, dense in the output), then the zero
+      // tail; one strided job when the runs are whole aligned vectors,
+      // else one job per run, the last one with the tail
       const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+      const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
+      const uint64_t out0 = (uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es);
+      const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
+      bool block = L.padded[i] == L.outer[i] * run &&
+                   block_ok({out0, src_off, pitch}, (uint64_t)(run * es), (uint64_t)L.outer[i], fsdp::tuning().reduce_shift);
+      for (int32_t t = 0; block && t < S; ++t) block = (uint64_t)grads[(size_t)(d * S + t) * P + i] % 16 == 0;
+      if (block) {
+        fsdp::RedJob jb;
+        jb.nbytes = jb.data_bytes = (uint64_t)(run * es);
+        jb.src0 = (uint32_t)ptrs.size();
+        jb.nsrc = (uint32_t)S;
+        for (int32_t t = 0; t < S; ++t) ptrs.push_back((uint64_t)grads[(size_t)(d * S + t) * P + i] + src_off);
+        jb.dst0 = (uint32_t)ptrs.size();
+        jb.ndst = 1;
+        ptrs.push_back(out0);
+        jb.rows = (uint64_t)L.outer[i];
+        jb.src_pitch = pitch;
+        jb.dst_pitch = (uint64_t)(run * es);
+        jb.rows_per_chunk = (uint64_t(1) << fsdp::tuning().reduce_shift) / jb.nbytes;
+        jobs.push_back(jb);
+        continue;
+      }
       for (int64_t o = 0; o < L.outer[i]; ++o) {
         const bool last = o + 1 == L.outer[i];
         const int64_t src_off = (o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es;

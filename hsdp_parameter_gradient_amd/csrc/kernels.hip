@@ -26,6 +26,12 @@
 // vectors runs whole unguarded iterations (all loads of an iteration in
 // flight before the first use) and then a short guarded tail.
 //
+// The chunk of a parameter sharded on a non-zero dim is a strided block
+// (`outer` rows, one per index of the dims before the shard dim).  When its
+// rows are whole aligned vectors the planner hands it over as one item;
+// each chunk of it is a group of whole rows, copied or reduced as one flat
+// range of vectors (row and column from one integer division).
+//
 // Arithmetic: the reduce kernel adds operands one at a time in ascending
 // rank order, the accumulator starting from the first operand, in IEEE
 // fp32 with denormals preserved; AVG divides the sum by the operand count
@@ -253,6 +259,49 @@ __device__ __forceinline__ void copy_partial(uint64_t a, uint64_t lo, uint64_t h
   }
 }
 
+// Vector q of a strided block of whole-vector rows, vpr vectors per row:
+// its byte offsets from the block's first source and destination rows.
+struct RowVec {
+  uint64_t src, dst;
+};
+__device__ __forceinline__ RowVec row_vec(uint32_t q, uint32_t vpr, uint64_t src_pitch, uint64_t dst_pitch) {
+  const uint32_t row = q / vpr;
+  const uint64_t col = (uint64_t)(q - row * vpr) << 4;
+  return {row * src_pitch + col, row * dst_pitch + col};
+}
+
+// Chunk k of a strided block (CopySeg with rows > 1): rows
+// [k*rows_per_chunk, ...) as one flat range of vectors, U per lane per
+// iteration with all loads issued before the first store.
+template <bool NTS>
+__device__ __forceinline__ void copy_rows(const fsdp::CopySeg& sg, uint64_t k) {
+  constexpr int U = kCopyUnroll;
+  const uint64_t r0 = k * sg.rows_per_chunk;
+  const uint64_t left = sg.rows - r0;
+  const uint32_t nr = (uint32_t)(left < sg.rows_per_chunk ? left : sg.rows_per_chunk);
+  const uint32_t vpr = (uint32_t)(sg.copy_bytes >> 4);
+  const uint32_t nv = nr * vpr;
+  const uint64_t s0 = sg.src + r0 * sg.src_pitch;
+  const uint64_t d0 = sg.dst + r0 * sg.dst_pitch;
+  uint32_t base = 0;
+  for (; base + (uint32_t)kBlock * U <= nv; base += (uint32_t)kBlock * U) {
+    u32x4 a[U];
+    uint64_t dof[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const RowVec x = row_vec(base + threadIdx.x + u * kBlock, vpr, sg.src_pitch, sg.dst_pitch);
+      a[u] = ldv(gptr<u32x4>(s0 + x.src));
+      dof[u] = x.dst;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) stv<NTS>(gptr<u32x4>(d0 + dof[u]), a[u]);
+  }
+  for (uint32_t q = base + threadIdx.x; q < nv; q += kBlock) {
+    const RowVec x = row_vec(q, vpr, sg.src_pitch, sg.dst_pitch);
+    stv<NTS>(gptr<u32x4>(d0 + x.dst), ldv(gptr<u32x4>(s0 + x.src)));
+  }
+}
+
 template <typename T, bool NTS>
 __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __restrict__ begin,
                                                           const fsdp::CopySeg* __restrict__ segs,
@@ -263,6 +312,10 @@ __global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __rest
     const uint32_t j = find_item(begin, n_seg, c);
     const fsdp::CopySeg sg = segs[j];
     const uint64_t k = c - begin[j];
+    if (sg.rows > 1) {
+      copy_rows<NTS>(sg, k);
+      continue;
+    }
     const uint64_t base = (sg.dst >> shift) << shift;
     const uint64_t seg_end = sg.dst + sg.total_bytes;
     const uint64_t cend = sg.dst + sg.copy_bytes;
@@ -478,6 +531,65 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
   }
 }
 
+// Chunk k of a strided reduction block (RedJob with rows > 1): rows
+// [k*rows_per_chunk, ...) as one flat range of vectors; operand t's vector
+// read at the same row and column of its block.  Compile-time K: U vectors
+// per lane per iteration with the K*U loads in flight together.
+template <int ES, int K, bool NTS>
+__device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr, uint64_t k,
+                                            int avg, float nf) {
+  const uint64_t r0 = k * jb.rows_per_chunk;
+  const uint64_t left = jb.rows - r0;
+  const uint32_t nr = (uint32_t)(left < jb.rows_per_chunk ? left : jb.rows_per_chunk);
+  const uint32_t vpr = (uint32_t)(jb.nbytes >> 4);
+  const uint32_t nv = nr * vpr;
+  const uint64_t soff = r0 * jb.src_pitch, doff = r0 * jb.dst_pitch;
+  auto store = [&](uint64_t dof, u32x4 o) {
+    for (uint32_t m = 0; m < jb.ndst; ++m) stv<NTS>(gptr<u32x4>(ptr[jb.dst0 + m] + doff + dof), o);
+  };
+  if constexpr (K > 0) {
+    constexpr int U = (K >= 4 || ES == 2) ? 2 : 4;
+    uint64_t sb[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) sb[t] = ptr[jb.src0 + t] + soff;
+    uint32_t base = 0;
+    for (; base + (uint32_t)kBlock * U <= nv; base += (uint32_t)kBlock * U) {
+      u32x4 v[K][U];
+      RowVec x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = row_vec(base + threadIdx.x + u * kBlock, vpr, jb.src_pitch, jb.dst_pitch);
+#pragma unroll
+      for (int t = 0; t < K; ++t)
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[t][u] = ldv(gptr<u32x4>(sb[t] + x[u].src));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Acc<ES> acc = widen<ES>(v[0][u]);
+#pragma unroll
+        for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t][u]);
+        store(x[u].dst, narrow<ES>(acc, avg, nf));
+      }
+    }
+    for (uint32_t q = base + threadIdx.x; q < nv; q += kBlock) {
+      const RowVec x = row_vec(q, vpr, jb.src_pitch, jb.dst_pitch);
+      u32x4 v[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t] + x.src));
+      Acc<ES> acc = widen<ES>(v[0]);
+#pragma unroll
+      for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t]);
+      store(x.dst, narrow<ES>(acc, avg, nf));
+    }
+  } else {
+    for (uint32_t q = threadIdx.x; q < nv; q += kBlock) {
+      const RowVec x = row_vec(q, vpr, jb.src_pitch, jb.dst_pitch);
+      Acc<ES> acc = widen<ES>(ldv(gptr<u32x4>(ptr[jb.src0] + soff + x.src)));
+      for (uint32_t t = 1; t < jb.nsrc; ++t) accumulate<ES>(acc, ldv(gptr<u32x4>(ptr[jb.src0 + t] + soff + x.src)));
+      store(x.dst, narrow<ES>(acc, avg, nf));
+    }
+  }
+}
+
 // Elements [max(a, lo), min(a + 16, hi)) of the 16-byte vector at d0-relative
 // address a: reduced below the data end, zero above it.
 template <int ES>
@@ -515,6 +627,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     const uint32_t j = find_item(begin, n_job, c);
     const fsdp::RedJob jb = jobs[j];
     const uint64_t k = c - begin[j];
+    if (jb.rows > 1) {
+      reduce_rows<ES, K, NTS>(jb, ptr, k, avg, (float)jb.nsrc);
+      continue;
+    }
     const uint64_t d0 = ptr[jb.dst0];
     const uint64_t base = (d0 >> shift) << shift;
     const uint64_t w0 = base + k * CH;
@@ -594,7 +710,7 @@ int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, ui
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
-  // the pointer array follows the jobs (32-byte records, so it is 8-byte aligned)
+  // the pointer array follows the jobs (64-byte records, so it is 8-byte aligned)
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
   hipStream_t st = static_cast<hipStream_t>(stream);

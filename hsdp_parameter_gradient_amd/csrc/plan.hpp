@@ -7,11 +7,14 @@
 //   reduce table  uint64 chunk_begin[n]  |  RedJob job[n]  |  uint64 ptr[m]
 //
 // Work is cut into chunks of (1 << chunk_shift) destination bytes.  Chunk k
-// of an item covers the window [base + k*CH, base + (k+1)*CH) clipped to
-// the item, where base is the item's first destination byte rounded down
-// to a multiple of CH, so that chunk edges inside an item are CH-aligned
-// (whole cache lines, never shared between workgroups).  chunk_begin[j] is
-// the global index of item j's first chunk; items are never empty.
+// of a one-row item covers the window [base + k*CH, base + (k+1)*CH)
+// clipped to the item, where base is the item's first destination byte
+// rounded down to a multiple of CH, so that chunk edges inside an item are
+// CH-aligned (whole cache lines, never shared between workgroups).  An item
+// of several rows (a strided block: the chunk of a parameter sharded on a
+// non-zero dim) is cut into whole rows instead, rows_per_chunk rows (at most
+// CH bytes) per chunk.  chunk_begin[j] is the global index of item j's first
+// chunk; items are never empty.
 #pragma once
 
 #include <stdint.h>
@@ -20,11 +23,21 @@ namespace fsdp {
 
 // One destination segment of a copy: copy_bytes from src, then
 // (total_bytes - copy_bytes) zero bytes.  copy_bytes may be 0.
+//
+// rows > 1 makes it a strided block of `rows` such rows, row r copied from
+// src + r*src_pitch to dst + r*dst_pitch.  Such a block has no zero fill
+// (copy_bytes == total_bytes), and src, dst, both pitches and copy_bytes are
+// multiples of 16 (whole aligned vectors); rows_per_chunk * copy_bytes is at
+// most the chunk size.
 struct CopySeg {
   uint64_t src;
   uint64_t dst;
   uint64_t copy_bytes;
   uint64_t total_bytes;
+  uint64_t rows = 1;
+  uint64_t src_pitch = 0;
+  uint64_t dst_pitch = 0;
+  uint64_t rows_per_chunk = 1;
 };
 
 // One reduction job over nbytes of destination: the first data_bytes are
@@ -32,6 +45,12 @@ struct CopySeg {
 // offsets), the rest is zero filled; every destination ptr[dst0 ..
 // dst0+ndst) gets the same result.  All destinations share their address
 // modulo 16.  AVG divides by nsrc.
+//
+// rows > 1 makes it a strided block of `rows` rows of nbytes: row r of
+// operand t at ptr[src0 + t] + r*src_pitch, of destination m at
+// ptr[dst0 + m] + r*dst_pitch.  Such a job has no zero fill (data_bytes ==
+// nbytes), and every base address, both pitches and nbytes are multiples of
+// 16; rows_per_chunk * nbytes is at most the chunk size.
 struct RedJob {
   uint64_t nbytes;
   uint64_t data_bytes;
@@ -39,14 +58,25 @@ struct RedJob {
   uint32_t nsrc;
   uint32_t dst0;
   uint32_t ndst;
+  uint64_t rows = 1;
+  uint64_t src_pitch = 0;
+  uint64_t dst_pitch = 0;
+  uint64_t rows_per_chunk = 1;
 };
 
-static_assert(sizeof(CopySeg) == 32, "CopySeg layout");
-static_assert(sizeof(RedJob) == 32, "RedJob layout");
+static_assert(sizeof(CopySeg) == 64, "CopySeg layout");
+static_assert(sizeof(RedJob) == 64, "RedJob layout");
 
-// Number of chunks of an item [dst, dst + nbytes), nbytes > 0.
+// Number of chunks of a one-row item [dst, dst + nbytes), nbytes > 0.
 inline uint64_t chunk_count(uint64_t dst, uint64_t nbytes, uint32_t shift) {
   return ((dst + nbytes - 1) >> shift) - (dst >> shift) + 1;
+}
+
+// Number of chunks of any item whose first destination row starts at dst.
+inline uint64_t item_chunks(uint64_t dst, uint64_t row_bytes, uint64_t rows, uint64_t rows_per_chunk,
+                            uint32_t shift) {
+  if (rows > 1) return (rows + rows_per_chunk - 1) / rows_per_chunk;
+  return chunk_count(dst, row_bytes, shift);
 }
 
 }  // namespace fsdp

@@ -31,10 +31,12 @@ class FlatBucket:
     def __init__(self, shapes: Sequence[Sequence[int]], rank_size: int, shard_size: int,
                  param_dtype: torch.dtype = torch.bfloat16, op: str = B.AVG,
                  device: str = "cuda", fused_segments: Optional[Sequence[int]] = None,
-                 fused_index: int = 0):
+                 fused_index: int = 0, grad_dtype: torch.dtype = torch.float32,
+                 shard_dims: Optional[Sequence[int]] = None):
         """fused_segments: sizes of the segments of the fused buffer (default:
         this bucket's RS output alone); fused_index: which one is this
-        bucket's."""
+        bucket's; grad_dtype: float32 or bfloat16 (the reduce dtype);
+        shard_dims: one shard dim per parameter (default 0)."""
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.R, self.S = int(rank_size), int(shard_size)
         rs, ar = B.fsdp_group_ranks(self.R, self.S)
@@ -45,32 +47,37 @@ class FlatBucket:
         self.do_rs, self.do_ar = bool(rs), bool(ar)
         self.op = op
         self.param_dtype = param_dtype
-        self.layout = B.fsdp_bucket_layout(self.shapes, self.S)
+        self.grad_dtype = grad_dtype
+        self.shard_dims = list(shard_dims) if shard_dims is not None else None
+        self.layout = B.fsdp_bucket_layout(self.shapes, self.S, shard_dims=self.shard_dims)
         I = self.layout.I
         self.seg_numel = list(fused_segments) if fused_segments is not None else [I]
-        offs, self.F = B.fsdp_fused_layout(self.seg_numel, 4)
+        offs, self.F = B.fsdp_fused_layout(self.seg_numel, grad_dtype.itemsize)
         self.fused_off = offs[fused_index]
         if self.seg_numel[fused_index] != I:
             raise ValueError("the bucket's fused segment must hold I elements")
         dev = torch.device(device)
         self.ag = torch.empty(self.S * I, dtype=param_dtype, device=dev)
         self.full = [torch.empty(s, dtype=param_dtype, device=dev) for s in self.shapes]
-        self.rs_in = [torch.empty(self.S * I, dtype=torch.float32, device=dev) for _ in range(self.R)]
+        self.rs_in = [torch.empty(self.S * I, dtype=grad_dtype, device=dev) for _ in range(self.R)]
         # fused buffers are fully defined (gaps zero) before the first RS writes
         # its views; torch's allocator returns 512-byte-aligned storage.
-        self.fused = [torch.zeros(self.F, dtype=torch.float32, device=dev) for _ in range(self.R)]
+        self.fused = [torch.zeros(self.F, dtype=grad_dtype, device=dev) for _ in range(self.R)]
         self.rs_out = [f[self.fused_off:self.fused_off + I] for f in self.fused]
         self._calls = None
 
     # -- the caller's inputs ------------------------------------------------
     def shard_views(self, params: Sequence[torch.Tensor]) -> List[torch.Tensor]:
-        """Rank-major shard views [s*P + i] of full parameters (rows per the
-        dim-0 chunk rule)."""
+        """Rank-major shards [s*P + i] of full parameters: views of the rows
+        (dim-0 chunk rule) for dim 0, dense copies of the chunks for a
+        non-zero shard dim (a rank stores its chunk densely)."""
         out = []
+        dims = self.shard_dims or [0] * len(self.shapes)
         for s in range(self.S):
             for i, x in enumerate(params):
                 a, n = self.layout.row_off[i][s], self.layout.row_len[i][s]
-                out.append(x.reshape(self.shapes[i])[a:a + n].reshape(-1))
+                c = x.reshape(self.shapes[i]).narrow(dims[i], a, n)
+                out.append(c.reshape(-1) if dims[i] == 0 else c.contiguous().reshape(-1))
         return out
 
     def full_views(self) -> List[torch.Tensor]:
@@ -81,9 +88,9 @@ class FlatBucket:
         unsharded-parameter-as-view option of the Hyper PR #758 write-up,
         section 4; it needs the AG buffer to stay alive while the view is
         used)."""
-        if len(self.shapes) != 1:
+        if len(self.shapes) != 1 or (self.shard_dims and self.shard_dims[0] != 0):
             raise ValueError("a view of the gathered buffer is the full parameter only for a "
-                             "one-parameter bucket; use the ag_copy_out step")
+                             "one-parameter bucket sharded on dim 0; use the ag_copy_out step")
         n = 1
         for d in self.shapes[0]:
             n *= d
@@ -91,14 +98,15 @@ class FlatBucket:
 
     def bind(self, shards: Sequence[torch.Tensor], grads: Sequence[torch.Tensor]) -> "FlatBucket":
         """Marshal the five calls once: shards [S*P] rank-major, grads [R*P]."""
-        S, R = self.S, self.R
+        S, R, dims = self.S, self.R, self.shard_dims
         self._calls = {
-            "ag_copy_in": B.prepare("fsdp_ag_copy_in", self.shapes, S, list(shards), self.ag),
-            "ag_copy_out": B.prepare("fsdp_ag_copy_out", self.shapes, S, self.ag, self.full),
-            "rs_copy_in": B.prepare("fsdp_rs_copy_in", self.shapes, R, S, list(grads), self.rs_in),
-            "rs_reduce": B.prepare("fsdp_rs_reduce", self.shapes, R, S, self.D, self.op, self.rs_in, self.rs_out),
+            "ag_copy_in": B.prepare("fsdp_ag_copy_in", self.shapes, S, list(shards), self.ag, dims),
+            "ag_copy_out": B.prepare("fsdp_ag_copy_out", self.shapes, S, self.ag, self.full, dims),
+            "rs_copy_in": B.prepare("fsdp_rs_copy_in", self.shapes, R, S, list(grads), self.rs_in, dims),
+            "rs_reduce": B.prepare("fsdp_rs_reduce", self.shapes, R, S, self.D, self.op, self.rs_in, self.rs_out,
+                                   dims),
             "rs_copy_reduce": B.prepare("fsdp_rs_copy_reduce", self.shapes, R, S, self.D, self.op, list(grads),
-                                        self.rs_out),
+                                        self.rs_out, dims),
             "fused_ar": B.prepare("fsdp_fused_ar", self.seg_numel, R, S, self.D, self.op, self.fused),
         }
         return self

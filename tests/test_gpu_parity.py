@@ -328,6 +328,40 @@ def test_hsdp_block_end_to_end_flat_bucket():
         assert m == "", f"fused rank {g}: {m}"
 
 
+@pytest.mark.parametrize("grad_dtype,on_dim_1", [(torch.bfloat16, False), (torch.float32, True),
+                                                (torch.bfloat16, True)])
+def test_flat_bucket_bf16_grads_and_shard_dim_1(grad_dtype, on_dim_1):
+    """FlatBucket with bfloat16 gradients and/or its 2-D parameters sharded
+    on dim 1 (the benchmark's variants), on a scaled-down HSDP block: the
+    gathered parameters and the fused buffers (unfused and fused RS) against
+    the oracle."""
+    w = W.scaled(W.HSDP_BLOCK, [(97, 64), (32, 64), (130, 32), (33, 128), (64,), (3,)])
+    R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+    dims = [1 if on_dim_1 and len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
+    note(f"[parity] FlatBucket grad_dtype={grad_dtype} shard_dims={dims} shapes={w.param_shapes}")
+    params, g_cpu = W.params(w), W.grads(w, dtype=grad_dtype)
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG, grad_dtype=grad_dtype,
+                       shard_dims=dims if on_dim_1 else None)
+    fb.bind(fb.shard_views([p.cuda() for p in params]),
+            [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)])
+    lay = O.bucket_layout(w.param_shapes, S, shard_dims=dims)
+    gnp = [[to_oracle(t) for t in g_cpu[g]] for g in range(R)]
+    rs_o = O.rs_copy_reduce(gnp, lay, R, O.AVG)
+    _, F = O.fused_layout([lay.I], grad_dtype.itemsize)
+    fused_o = O.fused_ar([np.concatenate([rs_o[g], np.zeros(F - lay.I, rs_o[g].dtype)]) for g in range(R)],
+                         R, S, O.AVG)
+    for fused_rs in (False, True):
+        for v in fb.rs_out:
+            v.fill_(float("nan"))
+        fb.step(fused_rs=fused_rs)
+        torch.cuda.synchronize()
+        for i, p in enumerate(params):
+            assert np.array_equal(bits(fb.full[i]), bits(p.reshape(-1))), f"full param {i}"
+        for g in range(R):
+            m = first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g]))
+            assert m == "", f"fused_rs={fused_rs} rank {g}: {m}"
+
+
 # ---------------------------------------------------------------------------
 # RS copy-in fused into the RS, and bfloat16 gradients
 # ---------------------------------------------------------------------------
@@ -496,10 +530,29 @@ def test_backward_pipeline_two_streams_matches_serial_and_oracle(fused_rs):
                                        (8, 8, torch.float32)])
 def test_nonzero_shard_dims_all_steps(S, R, dtype):
     """A bucket mixing dim-0 (ragged) parameters with parameters sharded on
-    dims 1 and 2 (divisible): every step against the oracle."""
+    dims 1 and 2 (divisible): every step against the oracle, buffers at
+    every element offset (chunks moved one row at a time)."""
     shapes = [(6, 8), (4, 16, 3), (5, 3, 8), (7, 3), (16,), (64, 1024), (3, 4, 8)]
     dims = [1, 1, 2, 0, 0, 1, 2]
-    note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype}")
+    run_nonzero_dims(shapes, dims, S, R, dtype, aligned=False)
+
+
+@pytest.mark.parametrize("S,R,dtype", [(4, 8, torch.float32), (4, 8, torch.bfloat16), (2, 4, torch.float32),
+                                       (8, 8, torch.bfloat16)])
+def test_strided_blocks_all_steps(S, R, dtype):
+    """Chunks of dim-1 parameters as strided blocks (16-byte-aligned buffers,
+    rows of whole vectors): several rows per chunk, a short last chunk, a
+    row as large as a chunk, and rows that are not whole vectors beside
+    them; every step against the oracle."""
+    shapes = [(64, 1024), (300, 256), (2, 8192), (3, 24, 2), (7, 3), (16,), (5, 32, 8)]
+    dims = [1, 1, 1, 1, 0, 0, 1]
+    run_nonzero_dims(shapes, dims, S, R, dtype, aligned=True)
+
+
+def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):
+    note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype} aligned={aligned}")
+    # element offsets of the buffers: any, or multiples of 16 bytes
+    v = (16 // (4 if dtype == torch.float32 else 2)) if aligned else 1
     w = W.Workload(f"dims_{S}", 600 + S, R, S, tuple(shapes), dtype, ("normal", 1.0), ("normal", 1.0),
                    ("sum", "avg"), W.ALL_STEPS)
     params, grads = W.params(w), W.grads(w, dtype=dtype)
@@ -512,14 +565,14 @@ def test_nonzero_shard_dims_all_steps(S, R, dtype):
     keep, shards = [], []
     for s in range(S):
         for i in range(P):
-            v = dparams[i].narrow(dims[i], lay.row_off[i][s], lay.row_len[i][s]).contiguous().reshape(-1)
-            g = Guarded(v.numel(), dtype, (s + i) % 5)
-            g.t.copy_(v)
+            x = dparams[i].narrow(dims[i], lay.row_off[i][s], lay.row_len[i][s]).contiguous().reshape(-1)
+            g = Guarded(x.numel(), dtype, v * ((s + i) % 5))
+            g.t.copy_(x)
             keep.append(g)
             shards.append(g.t)
-    ag = Guarded(S * I, dtype, 3)
+    ag = Guarded(S * I, dtype, 3 * v)
     hp.fsdp_ag_copy_in(shapes, S, shards, ag.t, shard_dims=dims)
-    full = [Guarded(p.numel(), dtype, 1) for p in params]
+    full = [Guarded(p.numel(), dtype, v) for p in params]
     hp.fsdp_ag_copy_out(shapes, S, ag.t, [f.t for f in full], shard_dims=dims)
     torch.cuda.synchronize()
     assert ag.guards_intact() and first_mismatch(bits(ag.t), np_bits(ag_o)) == ""
@@ -528,13 +581,13 @@ def test_nonzero_shard_dims_all_steps(S, R, dtype):
     gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
     rs_o = [O.rs_copy_in(gnp[g], lay, np_dt) for g in range(R)]
     dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
-    rs_in = [Guarded(S * I, dtype, g % 3) for g in range(R)]
+    rs_in = [Guarded(S * I, dtype, v * (g % 3)) for g in range(R)]
     hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in], shard_dims=dims)
     for op in (O.SUM, O.AVG):
         want = O.rs_reduce(rs_o, I, R, S, op)
-        out = [Guarded(I, dtype, 1 + g % 2) for g in range(R)]
+        out = [Guarded(I, dtype, v * (1 + g % 2)) for g in range(R)]
         hp.fsdp_rs_reduce(shapes, R, S, R // S, op, [b.t for b in rs_in], [o.t for o in out], shard_dims=dims)
-        out2 = [Guarded(I, dtype, g % 4) for g in range(R)]
+        out2 = [Guarded(I, dtype, v * (g % 4)) for g in range(R)]
         hp.fsdp_rs_copy_reduce(shapes, R, S, R // S, op, dgrads, [o.t for o in out2], shard_dims=dims)
         torch.cuda.synchronize()
         for g in range(R):

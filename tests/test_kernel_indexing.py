@@ -49,20 +49,49 @@ def find_item(begin, n, c):
     return lo
 
 
+def seg8(sg):
+    """A copy segment with the strided-block fields (rows, src_pitch,
+    dst_pitch, rows_per_chunk) filled in; a 4-tuple is one row."""
+    return tuple(sg) if len(sg) == 8 else tuple(sg) + (1, 0, 0, 1)
+
+
+def item_chunks(dst, row_bytes, rows, per, shift):
+    return -(-rows // per) if rows > 1 else chunk_count(dst, row_bytes, shift)
+
+
+def row_vectors(k, rows, per, row_bytes, CH):
+    """Chunk k of a strided block: (row, byte column) of every vector, in
+    the kernel's flat order (row = q // vpr)."""
+    r0 = k * per
+    nr = min(per, rows - r0)
+    assert nr >= 1 and nr * row_bytes <= CH
+    vpr = row_bytes >> 4
+    return [(r0 + q // vpr, (q % vpr) * 16) for q in range(nr * vpr)]
+
+
 def emulate_copy(segs, es, shift):
-    """Writes as (dst_lo, dst_hi, kind, src_lo) and reads as aligned block
-    addresses, per segment, following seg_copy_kernel."""
+    """Writes as (dst_lo, dst_hi, kind, src_lo, item, row) and reads as
+    aligned source ranges, per segment, following seg_copy_kernel."""
     CH = 1 << shift
+    segs = [seg8(sg) for sg in segs]
     begin, n = [], 0
-    for (src, dst, copy, total) in segs:
+    for (src, dst, copy, total, rows, sp, dp, per) in segs:
         begin.append(n)
-        n += chunk_count(dst, total, shift)
+        n += item_chunks(dst, total, rows, per, shift)
     writes, reads = [], []
     for c in range(n):
         j = find_item(begin, len(segs), c)
         assert begin[j] <= c and (j + 1 == len(segs) or c < begin[j + 1])
-        src, dst, copy, total = segs[j]
+        src, dst, copy, total, rows, sp, dp, per = segs[j]
         k = c - begin[j]
+        if rows > 1:
+            # the block contract the planner guarantees
+            assert copy == total and all(v % 16 == 0 for v in (src, dst, sp, dp, copy))
+            for row, col in row_vectors(k, rows, per, copy, CH):
+                a, sa = dst + row * dp + col, src + row * sp + col
+                writes.append((a, a + 16, "data", sa, j, row))
+                reads.append((sa, sa + 16, j, row))
+            continue
         base = (dst >> shift) << shift
         seg_end, cend = dst + total, dst + copy
         w0 = base + k * CH
@@ -74,13 +103,13 @@ def emulate_copy(segs, es, shift):
             s0 = src + (ca - dst)
             r = s0 & 15
             nv = (cb - ca) >> 4
-            writes.append((ca, cb, "data", s0, j))
+            writes.append((ca, cb, "data", s0, j, 0))
             first = s0 - r
             last = first + 16 * (nv - 1) + (16 if r else 0)  # s[j] and, when shifted, s[j+1]
-            reads.append((first, last + 16, j))
+            reads.append((first, last + 16, j, 0))
         za, zb = align_up16(max(lo, cend)), align_down16(hi)
         if za < zb:
-            writes.append((za, zb, "zero", None, j))
+            writes.append((za, zb, "zero", None, j, 0))
         a_lo, a_c, a_hi = align_down16(lo), align_down16(cend), align_down16(hi)
         p_lo = (lo & 15) != 0
         p_c = (cend & 15) != 0 and lo < cend < hi and not (p_lo and a_c == a_lo)
@@ -91,29 +120,37 @@ def emulate_copy(segs, es, shift):
             x0, x1 = max(a, lo), min(a + 16, hi)
             for x in range(x0, x1, es):
                 if x < cend:
-                    writes.append((x, x + es, "data", src + (x - dst), j))
-                    reads.append((src + (x - dst), src + (x - dst) + es, j))
+                    writes.append((x, x + es, "data", src + (x - dst), j, 0))
+                    reads.append((src + (x - dst), src + (x - dst) + es, j, 0))
                 else:
-                    writes.append((x, x + es, "zero", None, j))
+                    writes.append((x, x + es, "zero", None, j, 0))
     return writes, reads
+
+
+def seg_row(sg, row):
+    """(src, dst, copy_bytes, total_bytes) of one row of a segment."""
+    src, dst, copy, total, rows, sp, dp, per = seg8(sg)
+    assert 0 <= row < rows
+    return src + row * sp, dst + row * dp, copy, total
 
 
 def check_copy(segs, es, shift):
     writes, reads = emulate_copy(segs, es, shift)
-    # exact cover of every segment, no write outside
+    # exact cover of every row of every segment, no write outside
     ws = sorted(writes)
-    spans = sorted((dst, dst + total) for (_, dst, _, total) in segs)
+    spans = sorted((seg_row(sg, r)[1], seg_row(sg, r)[1] + seg_row(sg, r)[3])
+                   for sg in segs for r in range(seg8(sg)[4]))
     merged = []
     for a, b in spans:
         if merged and a < merged[-1][1]:
             raise AssertionError("segments overlap")
         merged.append((a, b))
     cover = []
-    for (a, b, kind, s0, j) in ws:
+    for (a, b, kind, s0, j, row) in ws:
         if cover and a < cover[-1][1]:
             raise AssertionError(f"byte {a:#x} written twice")
         cover.append((a, b))
-        src, dst, copy, total = segs[j]
+        src, dst, copy, total = seg_row(segs[j], row)
         assert dst <= a and b <= dst + total, "write outside its segment"
         if kind == "data":
             assert b <= dst + copy and s0 == src + (a - dst), "data write with a wrong source"
@@ -129,25 +166,45 @@ def check_copy(segs, es, shift):
                 out.append((a, b))
         return out
     assert union(cover) == union([s for s in merged if s[0] < s[1]])
-    for (a, b, j) in reads:
-        src, dst, copy, total = segs[j]
+    for (a, b, j, row) in reads:
+        src, dst, copy, total = seg_row(segs[j], row)
         assert align_down16(src) <= a and b <= align_up16(src + copy), "read outside the source envelope"
 
 
+def job10(jb):
+    """A reduce job with the strided-block fields (rows, src_pitch,
+    dst_pitch, rows_per_chunk) filled in; a 6-tuple is one row."""
+    return tuple(jb) if len(jb) == 10 else tuple(jb) + (1, 0, 0, 1)
+
+
 def emulate_reduce(jobs, ptr, shift, es=4):
-    """Writes per destination as (lo, hi, kind) byte ranges and operand reads,
-    following reduce_kernel.  A job is (nbytes, data_bytes, src0, nsrc, dst0,
-    ndst): the first data_bytes are reduced, the rest zero filled."""
+    """Writes per destination as (lo, hi, kind, job, dst, row) byte ranges
+    and operand reads, following reduce_kernel.  A job is (nbytes,
+    data_bytes, src0, nsrc, dst0, ndst[, rows, src_pitch, dst_pitch,
+    rows_per_chunk]): the first data_bytes of each row are reduced, the rest
+    zero filled."""
     CH = 1 << shift
+    jobs = [job10(jb) for jb in jobs]
     begin, n = [], 0
-    for (nbytes, data, src0, nsrc, dst0, ndst) in jobs:
+    for (nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, per) in jobs:
         begin.append(n)
-        n += chunk_count(ptr[dst0], nbytes, shift)
+        n += item_chunks(ptr[dst0], nbytes, rows, per, shift)
     writes, reads = [], []
     for c in range(n):
         j = find_item(begin, len(jobs), c)
-        nbytes, data, src0, nsrc, dst0, ndst = jobs[j]
+        nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, per = jobs[j]
         k = c - begin[j]
+        if rows > 1:
+            bases = [ptr[src0 + t] for t in range(nsrc)] + [ptr[dst0 + m] for m in range(ndst)]
+            assert data == nbytes and all(v % 16 == 0 for v in bases + [sp, dp, nbytes])
+            for row, col in row_vectors(k, rows, per, nbytes, CH):
+                for t in range(nsrc):
+                    sa = ptr[src0 + t] + row * sp + col
+                    reads.append((sa, sa + 16, j, t, row))
+                for m in range(ndst):
+                    a = ptr[dst0 + m] + row * dp + col
+                    writes.append((a, a + 16, "data", j, m, row))
+            continue
         d0 = ptr[dst0]
         base = (d0 >> shift) << shift
         w0 = base + k * CH
@@ -160,13 +217,13 @@ def emulate_reduce(jobs, ptr, shift, es=4):
             for t in range(nsrc):
                 sa = ptr[src0 + t] + va
                 r = sa & 15
-                reads.append((sa - r, sa - r + 16 * nv + (16 if r else 0), j, t))
+                reads.append((sa - r, sa - r + 16 * nv + (16 if r else 0), j, t, 0))
             for m in range(ndst):
-                writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + va + 16 * nv, "data", j, m))
+                writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + va + 16 * nv, "data", j, m, 0))
         za, zb = align_up16(max(lo, cend)), align_down16(hi)
         if za < zb:
             for m in range(ndst):
-                writes.append((ptr[dst0 + m] + za - d0, ptr[dst0 + m] + zb - d0, "zero", j, m))
+                writes.append((ptr[dst0 + m] + za - d0, ptr[dst0 + m] + zb - d0, "zero", j, m, 0))
         a_lo, a_c, a_hi = align_down16(lo), align_down16(cend), align_down16(hi)
         p_lo = (lo & 15) != 0
         p_c = (cend & 15) != 0 and lo < cend < hi and not (p_lo and a_c == a_lo)
@@ -179,30 +236,34 @@ def emulate_reduce(jobs, ptr, shift, es=4):
                 kind = "data" if x < cend else "zero"
                 if kind == "data":
                     for t in range(nsrc):
-                        reads.append((ptr[src0 + t] + off, ptr[src0 + t] + off + es, j, t))
+                        reads.append((ptr[src0 + t] + off, ptr[src0 + t] + off + es, j, t, 0))
                 for m in range(ndst):
-                    writes.append((ptr[dst0 + m] + off, ptr[dst0 + m] + off + es, kind, j, m))
+                    writes.append((ptr[dst0 + m] + off, ptr[dst0 + m] + off + es, kind, j, m, 0))
     return writes, reads
 
 
 def check_reduce(jobs, ptr, shift, es=4):
     writes, reads = emulate_reduce(jobs, ptr, shift, es)
     per = {}
-    for (a, b, kind, j, m) in writes:
-        per.setdefault((j, m), []).append((a, b, kind))
-    for j, (nbytes, data, src0, nsrc, dst0, ndst) in enumerate(jobs):
+    for (a, b, kind, j, m, row) in writes:
+        per.setdefault((j, m, row), []).append((a, b, kind))
+    for j, jb in enumerate(jobs):
+        nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, _ = job10(jb)
         for m in range(ndst):
-            iv = sorted(per.get((j, m), []))
-            pos = ptr[dst0 + m]
-            for a, b, kind in iv:
-                assert a == pos, f"job {j} dst {m}: gap or double write at {a:#x} (expected {pos:#x})"
-                edge = ptr[dst0 + m] + data
-                assert (b <= edge) if kind == "data" else (a >= edge), f"job {j}: {kind} write across the data end"
-                pos = b
-            assert pos == ptr[dst0 + m] + nbytes
-    for (a, b, j, t) in reads:
-        nbytes, data, src0, nsrc, dst0, ndst = jobs[j]
-        s = ptr[src0 + t]
+            for row in range(rows):
+                iv = sorted(per.pop((j, m, row), []))
+                start = ptr[dst0 + m] + row * dp
+                pos = start
+                for a, b, kind in iv:
+                    assert a == pos, f"job {j} dst {m} row {row}: gap or double write at {a:#x} (expected {pos:#x})"
+                    edge = start + data
+                    assert (b <= edge) if kind == "data" else (a >= edge), f"job {j}: {kind} write across the data end"
+                    pos = b
+                assert pos == start + nbytes
+    assert not per, "writes attributed to no row"
+    for (a, b, j, t, row) in reads:
+        nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, _ = job10(jobs[j])
+        s = ptr[src0 + t] + row * sp
         assert align_down16(s) <= a and b <= align_up16(s + data), "operand read outside its envelope"
 
 
@@ -243,22 +304,33 @@ def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
     return segs
 
 
-def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None):
+def block_ok(addrs, row_bytes, rows, shift):
+    """When the planner emits one strided block instead of one item per row."""
+    return (rows >= 2 and row_bytes > 0 and row_bytes % 16 == 0 and row_bytes <= (1 << shift)
+            and all(a % 16 == 0 for a in addrs))
+
+
+def push_rows(segs, src, dst, row_bytes, rows, sp, dp, shift):
+    if row_bytes == 0 or rows == 0:
+        return
+    if block_ok((src, dst, sp, dp), row_bytes, rows, shift):
+        segs.append((src, dst, row_bytes, row_bytes, rows, sp, dp, (1 << shift) // row_bytes))
+    else:
+        segs.extend((src + r * sp, dst + r * dp, row_bytes, row_bytes) for r in range(rows))
+
+
+def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None, shift=14):
     L = layout(shapes, S, dims)
     segs = []
     for i in range(len(shapes)):
         for s in range(S):
             run = L["rl"][i][s] * L["inner"][i]
-            if run == 0:
-                continue
-            for o in range(L["outer"][i]):
-                segs.append((ag + (s * L["I"] + L["in_off"][i] + o * run) * es,
-                             full_addr(i) + (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es,
-                             run * es, run * es))
+            push_rows(segs, ag + (s * L["I"] + L["in_off"][i]) * es, full_addr(i) + L["ro"][i][s] * L["inner"][i] * es,
+                      run * es, L["outer"][i], run * es, L["dk"][i] * L["inner"][i] * es, shift)
     return segs
 
 
-def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None):
+def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None, shift=14):
     """One rank's RS copy-in segments, as fsdp_rs_copy_in builds them."""
     L = layout(shapes, S, dims)
     segs = []
@@ -267,13 +339,15 @@ def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None):
             if L["padded"][i] == 0:
                 continue
             run = L["rl"][i][s] * L["inner"][i]
+            src = grad_addr(i) + L["ro"][i][s] * L["inner"][i] * es
             d0 = rs_in_addr + (s * L["I"] + L["in_off"][i]) * es
-            for o in range(L["outer"][i]):
-                last = o + 1 == L["outer"][i]
-                total = (L["padded"][i] - o * run) * es if last else run * es
-                src = grad_addr(i) + (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es
-                if total:
-                    segs.append((src if run else 0, d0 + o * run * es, run * es, total))
+            if L["outer"][i] == 1:
+                segs.append((src if run else 0, d0, run * es, L["padded"][i] * es))
+                continue
+            push_rows(segs, src, d0, run * es, L["outer"][i], L["dk"][i] * L["inner"][i] * es, run * es, shift)
+            data = L["outer"][i] * run
+            if L["padded"][i] > data:
+                segs.append((0, d0 + data * es, 0, (L["padded"][i] - data) * es))
     return segs
 
 
@@ -355,9 +429,10 @@ def test_reduce_jobs_cover_exactly(shift, es):
             check_reduce(jobs, ptr, shift, es)
 
 
-def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None):
-    """Jobs as fsdp_rs_copy_reduce builds them: one per (rank, parameter,
-    run of the chunk)."""
+def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None, shift=13):
+    """Jobs as fsdp_rs_copy_reduce builds them: one strided job per (rank,
+    parameter) when the chunk's runs are whole aligned vectors, else one job
+    per (rank, parameter, run of the chunk)."""
     L = layout(shapes, S, dims)
     jobs, ptr = [], []
     for g in range(R):
@@ -366,6 +441,19 @@ def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None):
             if L["padded"][i] == 0:
                 continue
             run = L["rl"][i][s] * L["inner"][i]
+            src_off = L["ro"][i][s] * L["inner"][i] * es
+            out0 = out_addr(g) + L["in_off"][i] * es
+            pitch = L["dk"][i] * L["inner"][i] * es
+            srcs = [grad_addr(d * S + t, i) for t in range(S)]
+            if (L["padded"][i] == L["outer"][i] * run and block_ok((out0, src_off, pitch), run * es, L["outer"][i], shift)
+                    and all(a % 16 == 0 for a in srcs)):
+                src0 = len(ptr)
+                ptr += [a + src_off for a in srcs]
+                dst0 = len(ptr)
+                ptr.append(out0)
+                jobs.append((run * es, run * es, src0, S, dst0, 1, L["outer"][i], pitch, run * es,
+                             (1 << shift) // (run * es)))
+                continue
             for o in range(L["outer"][i]):
                 last = o + 1 == L["outer"][i]
                 src_off = (o * L["dk"][i] + L["ro"][i][s]) * L["inner"][i] * es
@@ -481,12 +569,47 @@ def test_nonzero_shard_dim_tables_cover_exactly(S, es, shift):
     base = 1 << 32
     ag = base + es * int(rng.integers(0, 9))
     full = {i: base + (1 << 30) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
-    check_copy(ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims), es, shift)
+    check_copy(ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims, shift), es, shift)
     grads = {i: (1 << 40) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
-    check_copy(rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + es * 3, dims), es, shift)
+    check_copy(rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + es * 3, dims, shift), es, shift)
     R = 2 * S
     gr = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + es * int(rng.integers(0, 8))
           for g in range(R) for i in range(len(shapes))}
     outs = {g: (1 << 46) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)}
-    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims)
+    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims,
+                                    shift)
+    check_reduce(jobs, ptr, shift, es)
+
+
+# Strided blocks: rows of whole aligned vectors (bf16 and fp32), several
+# rows per chunk, a last chunk of fewer rows, rows as large as a chunk, and
+# parameters whose rows are not whole vectors (one item per row) beside them.
+BLOCK_SHAPES = ([(96, 64), (32, 64), (130, 32), (33, 128), (64,), (3,), (5, 24, 2), (7, 40), (3, 2048)],
+                [1, 1, 1, 1, 0, 0, 1, 1, 1])
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", (9, 10, 14))
+def test_strided_block_tables_cover_exactly(S, es, shift):
+    shapes, dims = BLOCK_SHAPES
+    dims = [k if k == 0 or shapes[i][k] % S == 0 else 0 for i, k in enumerate(dims)]
+    rng = np.random.default_rng(S * 7 + es + shift)
+    base = 1 << 32
+    L = layout(shapes, S, dims)
+    ag = base + 512 * int(rng.integers(0, 9))
+    full = {i: base + (1 << 30) + i * (1 << 24) + 16 * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims, shift)
+    assert any(len(sg) == 8 for sg in segs), "no strided block planned"
+    check_copy(segs, es, shift)
+    grads = {i: (1 << 40) + i * (1 << 24) + 16 * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + 512, dims, shift)
+    assert any(len(sg) == 8 for sg in segs)
+    check_copy(segs, es, shift)
+    R = 2 * S
+    gr = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + 16 * int(rng.integers(0, 8))
+          for g in range(R) for i in range(len(shapes))}
+    outs = {g: (1 << 46) + g * (1 << 26) + 512 * int(rng.integers(0, 8)) for g in range(R)}
+    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims, shift)
+    assert any(len(jb) == 10 for jb in jobs) or L["I"] * es < 16
     check_reduce(jobs, ptr, shift, es)
