@@ -19,7 +19,10 @@ written, never read as a copy source):
 Timing: W untimed steps, then K steps between synchronisations (the value);
 inside them HIP events on the launch stream around the dominant kernel (found
 on a few untimed steps) give its average launch time (the roofline); a
-separate pass afterwards gives every step's time (the "ops" breakdown).
+separate pass afterwards gives every step's time (the "ops" breakdown), and
+medians of single launches with the Infinity Cache flushed first (cold) or
+not (warm).  A 4 GiB device-to-device copy (hipMemcpyAsync, and the
+library's copy kernel) gives the plain-copy ceiling.
 The CPU oracle is timed on a bounded number of whole steps of the same
 workload (cpu_baseline).
 
@@ -154,6 +157,77 @@ def per_step_us(runner, steps, n):
     torch.cuda.synchronize()
     return {name: sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(n)) / n * 1e3
             for j, name in enumerate(steps)}
+
+
+def op_medians(runner, steps, reps: int, flush):
+    """Median single-launch duration (us) of every step, cold and warm: a
+    cold launch follows a read of a scratch buffer four times the 256 MB
+    Infinity Cache (so the caches hold clean, unrelated lines: neither the
+    step's inputs nor its outputs), a warm one follows a launch of the same
+    step."""
+    import statistics
+
+    import torch
+    out = {}
+    for name in steps:
+        res = {}
+        for mode in ("cold", "warm"):
+            t = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.sum()
+                else:
+                    runner.run(name)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                runner.run(name)
+                b.record()
+                b.synchronize()
+                t.append(a.elapsed_time(b) * 1e3)
+            res[mode] = statistics.median(t)
+        out[name] = res
+    return out
+
+
+def copy_ceiling(mib: int, reps: int):
+    """Device-to-device copy of mib MiB with hipMemcpyAsync (torch's copy_
+    of a contiguous tensor) and with the library's copy kernel (one aligned
+    segment): read + write GB/s, the achievable ceiling of a plain copy."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    call = hp.prepare("fsdp_ag_copy_out", [(n,)], 1, a, [b])
+    out = {"bytes_each_way": 4 * n}
+    for name, fn in (("hipMemcpyAsync_DtoD", lambda: b.copy_(a)), ("seg_copy_kernel", lambda: call())):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) / reps * 1e3
+        out[name] = {"us": round(us, 1), "GB/s": round(2 * 4 * n / (us * 1e-6) / 1e9, 1)}
+    del a, b
+    torch.cuda.empty_cache()
+    log(f"  copy ceiling ({mib} MiB): hipMemcpyAsync {out['hipMemcpyAsync_DtoD']['GB/s']} GB/s, "
+        f"seg_copy_kernel {out['seg_copy_kernel']['GB/s']} GB/s")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bucket_variant(w, op, K: int, warmup: int, grad_dtype=None, shard_dims=None):
@@ -321,6 +395,10 @@ def main():
                     help="skip the bf16-gradient and shard-dim-1 variants")
     ap.add_argument("--pipeline-layers", type=int, default=8,
                     help="layers in the backward-overlap variant (0 = skip it)")
+    ap.add_argument("--cold-warm-reps", type=int, default=20,
+                    help="single launches per step for the cold/warm medians (0 = skip)")
+    ap.add_argument("--ceiling-mib", type=int, default=4096,
+                    help="size of the plain device-to-device copy ceiling (0 = skip)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -404,6 +482,19 @@ def main():
                      "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"  {name:12s} {nbytes[name] / 1e6:10.1f} MB  {us:9.1f} us  {gbs:8.1f} GB/s  "
             f"{100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
+    # cold / warm medians of single launches, and the plain-copy ceiling
+    cw = {}
+    if args.cold_warm_reps > 0:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        med = op_medians(runner, steps, args.cold_warm_reps, flush)
+        del flush
+        for name in steps:
+            cw[name] = {m: {"us": round(med[name][m], 2),
+                            "GB/s": round(nbytes[name] / (med[name][m] * 1e-6) / 1e9, 1)} for m in ("cold", "warm")}
+            log(f"  {name:12s} median of {args.cold_warm_reps}: cold {med[name]['cold']:8.1f} us "
+                f"({cw[name]['cold']['GB/s']:7.1f} GB/s), warm {med[name]['warm']:8.1f} us "
+                f"({cw[name]['warm']['GB/s']:7.1f} GB/s)")
+    ceiling = copy_ceiling(args.ceiling_mib, 10) if args.ceiling_mib > 0 else None
     achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": KERNEL_OF_STEP[dom], "step": dom,
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -449,7 +540,7 @@ def main():
         cpu = {"value": round(bytes_per_step * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{n} whole steps of {w.name} (all {len(steps)} steps, full size) in {el:.1f} s; "
-                         f"NumPy, single-threaded"}
+                         f"NumPy, single-threaded: 1 core of {os.cpu_count()} ({cpu_model()})"}
         log(f"  cpu oracle: {cpu['value']} GB/s over {n} steps ({el:.1f} s)")
 
     out = {
@@ -464,6 +555,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "ops": ops,
+        "ops_cold_warm": cw or None,
+        "copy_ceiling": ceiling,
         "variants": variants,
     }
     print(json.dumps(out), flush=True)
