@@ -128,3 +128,70 @@ def test_full_size_sampled(wname):
         assert np.array_equal(_gpu_vals(fused_out[g], k), want.view(np.int32)), f"rs_copy_reduce sampled rank {g}"
     del fb, params, grads, fused_out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wname", ["hsdp_block_h1024_r8_s4_d2", "llama7b_4layer_r8_s8"])
+def test_full_size_shard_dim_1(wname):
+    """The 2-D weights sharded on dim 1 (strided blocks), at full size, in
+    the benchmark's configuration, checked on every element by properties
+    that hold at any size: each AG slice region is the dense dim-1 chunk of
+    its parameter, copy-out restores the parameters bit for bit, each RS
+    input region is the dense chunk of the gradient, and with integer-valued
+    gradients (every sum exact in any order) the RS output is the chunk of
+    the group's sum divided by S, and the fused AR output that divided by D."""
+    w = W.WORKLOADS[wname]
+    R, S, D = w.rank_size, w.shard_size, w.dp_size
+    P = len(w.param_shapes)
+    dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
+    lay = O.bucket_layout(w.param_shapes, S, shard_dims=dims)
+    I = lay.I
+    note(f"[fullsize] {w.name} shard dims {sorted(set(dims))}: P={P} I={I} R={R} S={S}")
+    params = W.params(w, device="cuda")
+    grads = W.integer_grads(w, device="cuda")
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG, shard_dims=dims)
+    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+    fb.step()
+    torch.cuda.synchronize()
+    it = torch.int16 if w.param_dtype != torch.float32 else torch.int32
+
+    def chunk(x, i, s):
+        c = x.narrow(dims[i], lay.row_off[i][s], lay.row_len[i][s]).contiguous().reshape(-1)
+        return c
+
+    def region(buf, s, i, n):
+        a = s * I + lay.in_off[i]
+        return buf[a:a + n]
+
+    for i in range(P):
+        assert torch.equal(fb.full[i].reshape(-1).view(it), params[i].reshape(-1).view(it)), f"ag_copy_out {i}"
+        for s in range(S):
+            c = chunk(params[i], i, s)
+            r = region(fb.ag, s, i, lay.padded[i])
+            assert torch.equal(r[:c.numel()].view(it), c.view(it)), f"ag_copy_in slice {s} param {i}"
+            assert int(torch.count_nonzero(r[c.numel():].view(it))) == 0, f"ag padding {s} {i}"
+    for g in range(R):
+        for i in range(P):
+            for s in range(S):
+                c = chunk(grads[g][i], i, s)
+                r = region(fb.rs_in[g], s, i, lay.padded[i])
+                assert torch.equal(r[:c.numel()], c) and int(torch.count_nonzero(r[c.numel():])) == 0, \
+                    f"rs_copy_in rank {g} slice {s} param {i}"
+    for d in range(D):
+        for s in range(S):
+            g = d * S + s
+            for i in range(P):
+                want = sum(chunk(grads[d * S + t][i], i, s) for t in range(S)) / S
+                if D > 1:  # the fused AR over the replicate group of g
+                    want = sum(sum(chunk(grads[e * S + t][i], i, s) for t in range(S)) / S for e in range(D)) / D
+                got = fb.rs_out[g][lay.in_off[i]:lay.in_off[i] + want.numel()]
+                assert torch.equal(got, want), f"reduced rank {g} param {i}"
+    # the fused RS pass gives the same fused buffers bit for bit
+    before = [f.clone() for f in fb.fused]
+    for v in fb.rs_out:
+        v.fill_(float("nan"))
+    fb.step(fused_rs=True)
+    torch.cuda.synchronize()
+    for g in range(R):
+        assert torch.equal(fb.fused[g].view(torch.int32), before[g].view(torch.int32)), f"fused RS rank {g}"
+    del fb, params, grads, before
+    torch.cuda.empty_cache()
