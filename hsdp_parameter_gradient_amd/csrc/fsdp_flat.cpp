@@ -23,7 +23,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <initializer_list>
 #include <list>
 #include <mutex>
 #include <string>
@@ -366,21 +365,19 @@ int upload(const std::vector<uint8_t>& table, Plan* p) {
 }
 
 // Strided blocks: `rows` runs of row_bytes, row r from src + r*src_pitch to
-// dst + r*dst_pitch.  One block item when every row is whole aligned
-// vectors and fits a chunk (the kernels then move whole rows per chunk);
-// otherwise one item per row.
-bool block_ok(std::initializer_list<uint64_t> addrs, uint64_t row_bytes, uint64_t rows, uint32_t shift) {
-  if (rows < 2 || row_bytes == 0 || row_bytes % 16 || row_bytes > (uint64_t(1) << shift)) return false;
-  for (uint64_t a : addrs)
-    if (a % 16) return false;
-  return true;
+// dst + r*dst_pitch.  The kernels move whole rows per chunk; pitches that
+// are multiples of 16 keep every row at the alignment of the first.  Rows
+// longer than a chunk, or other pitches, go one item per row.
+bool block_ok(uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes, uint64_t rows, uint32_t shift) {
+  return rows >= 2 && row_bytes > 0 && row_bytes <= (uint64_t(1) << shift) && src_pitch % 16 == 0 &&
+         dst_pitch % 16 == 0;
 }
 
 void push_rows(std::vector<fsdp::CopySeg>& segs, uint64_t src, uint64_t dst, uint64_t row_bytes, uint64_t rows,
                uint64_t src_pitch, uint64_t dst_pitch) {
   if (row_bytes == 0 || rows == 0) return;
   const uint32_t shift = fsdp::tuning().copy_shift;
-  if (block_ok({src, dst, src_pitch, dst_pitch}, row_bytes, rows, shift)) {
+  if (block_ok(src_pitch, dst_pitch, row_bytes, rows, shift)) {
     fsdp::CopySeg sg{src, dst, row_bytes, row_bytes};
     sg.rows = rows;
     sg.src_pitch = src_pitch;
@@ -768,15 +765,16 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
       if (L.padded[i] == 0) continue;
       // rank s's chunk: outer runs of row_len*inner elements (stride
       // dk*inner in the gradients, dense in the output), then the zero
-      // tail; one strided job when the runs are whole aligned vectors,
-      // else one job per run, the last one with the tail
+      // tail; one strided job when both pitches keep the rows' alignment
+      // (and there is no tail), else one job per run, the last one with
+      // the tail
       const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
       const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
       const uint64_t out0 = (uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es);
       const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
-      bool block = L.padded[i] == L.outer[i] * run &&
-                   block_ok({out0, src_off, pitch}, (uint64_t)(run * es), (uint64_t)L.outer[i], fsdp::tuning().reduce_shift);
-      for (int32_t t = 0; block && t < S; ++t) block = (uint64_t)grads[(size_t)(d * S + t) * P + i] % 16 == 0;
+      const bool block = L.padded[i] == L.outer[i] * run &&
+                         block_ok(pitch, (uint64_t)(run * es), (uint64_t)(run * es), (uint64_t)L.outer[i],
+                                  fsdp::tuning().reduce_shift);
       if (block) {
         fsdp::RedJob jb;
         jb.nbytes = jb.data_bytes = (uint64_t)(run * es);

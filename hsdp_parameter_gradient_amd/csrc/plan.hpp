@@ -26,8 +26,8 @@ namespace fsdp {
 //
 // rows > 1 makes it a strided block of `rows` such rows, row r copied from
 // src + r*src_pitch to dst + r*dst_pitch.  Such a block has no zero fill
-// (copy_bytes == total_bytes), and src, dst, both pitches and copy_bytes are
-// multiples of 16 (whole aligned vectors); rows_per_chunk * copy_bytes is at
+// (copy_bytes == total_bytes), both pitches are multiples of 16 (every row
+// has the alignment of the first), and rows_per_chunk * copy_bytes is at
 // most the chunk size.
 struct CopySeg {
   uint64_t src;
@@ -49,8 +49,8 @@ struct CopySeg {
 // rows > 1 makes it a strided block of `rows` rows of nbytes: row r of
 // operand t at ptr[src0 + t] + r*src_pitch, of destination m at
 // ptr[dst0 + m] + r*dst_pitch.  Such a job has no zero fill (data_bytes ==
-// nbytes), and every base address, both pitches and nbytes are multiples of
-// 16; rows_per_chunk * nbytes is at most the chunk size.
+// nbytes), both pitches are multiples of 16 (every row has the alignment of
+// the first), and rows_per_chunk * nbytes is at most the chunk size.
 struct RedJob {
   uint64_t nbytes;
   uint64_t data_bytes;

@@ -86,11 +86,28 @@ def emulate_copy(segs, es, shift):
         k = c - begin[j]
         if rows > 1:
             # the block contract the planner guarantees
-            assert copy == total and all(v % 16 == 0 for v in (src, dst, sp, dp, copy))
-            for row, col in row_vectors(k, rows, per, copy, CH):
+            assert copy == total and sp % 16 == 0 and dp % 16 == 0
+            r0 = k * per
+            nr = min(per, rows - r0)
+            assert nr >= 1 and nr * copy <= CH
+            d0, s0 = dst + r0 * dp, src + r0 * sp
+            head = min((16 - (d0 & 15)) & 15, copy)
+            vpr = (copy - head) >> 4
+            tail = head + 16 * vpr
+            for q in range(nr * vpr):  # rows_run's flat range
+                row, col = r0 + q // vpr, head + (q % vpr) * 16
                 a, sa = dst + row * dp + col, src + row * sp + col
+                assert a % 16 == 0
                 writes.append((a, a + 16, "data", sa, j, row))
-                reads.append((sa, sa + 16, j, row))
+                r = sa & 15
+                reads.append((sa - r, sa - r + (32 if r else 16), j, row))
+            for t in range(2 * nr):  # heads and tails, one row end per lane
+                row = r0 + (t >> 1)
+                lo, hi = (tail, copy) if t & 1 else (0, head)
+                for x in range(lo, hi, es):
+                    a, sa = dst + row * dp + x, src + row * sp + x
+                    writes.append((a, a + es, "data", sa, j, row))
+                    reads.append((sa, sa + es, j, row))
             continue
         base = (dst >> shift) << shift
         seg_end, cend = dst + total, dst + copy
@@ -195,15 +212,35 @@ def emulate_reduce(jobs, ptr, shift, es=4):
         nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, per = jobs[j]
         k = c - begin[j]
         if rows > 1:
-            bases = [ptr[src0 + t] for t in range(nsrc)] + [ptr[dst0 + m] for m in range(ndst)]
-            assert data == nbytes and all(v % 16 == 0 for v in bases + [sp, dp, nbytes])
-            for row, col in row_vectors(k, rows, per, nbytes, CH):
+            assert data == nbytes and sp % 16 == 0 and dp % 16 == 0
+            assert len({ptr[dst0 + m] & 15 for m in range(ndst)}) == 1
+            r0 = k * per
+            nr = min(per, rows - r0)
+            assert nr >= 1 and nr * nbytes <= CH
+            soff, doff = r0 * sp, r0 * dp
+            head = min((16 - ((ptr[dst0] + doff) & 15)) & 15, nbytes)
+            vpr = (nbytes - head) >> 4
+            tail = head + 16 * vpr
+            for q in range(nr * vpr):
+                row, col = r0 + q // vpr, head + (q % vpr) * 16
                 for t in range(nsrc):
                     sa = ptr[src0 + t] + row * sp + col
-                    reads.append((sa, sa + 16, j, t, row))
+                    r = sa & 15
+                    reads.append((sa - r, sa - r + (32 if r else 16), j, t, row))
                 for m in range(ndst):
                     a = ptr[dst0 + m] + row * dp + col
+                    assert a % 16 == 0
                     writes.append((a, a + 16, "data", j, m, row))
+            for t in range(2 * nr):
+                row = r0 + (t >> 1)
+                lo, hi = (tail, nbytes) if t & 1 else (0, head)
+                for x in range(lo, hi, es):
+                    for i in range(nsrc):
+                        sa = ptr[src0 + i] + row * sp + x
+                        reads.append((sa, sa + es, j, i, row))
+                    for m in range(ndst):
+                        a = ptr[dst0 + m] + row * dp + x
+                        writes.append((a, a + es, "data", j, m, row))
             continue
         d0 = ptr[dst0]
         base = (d0 >> shift) << shift
@@ -304,16 +341,15 @@ def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
     return segs
 
 
-def block_ok(addrs, row_bytes, rows, shift):
+def block_ok(sp, dp, row_bytes, rows, shift):
     """When the planner emits one strided block instead of one item per row."""
-    return (rows >= 2 and row_bytes > 0 and row_bytes % 16 == 0 and row_bytes <= (1 << shift)
-            and all(a % 16 == 0 for a in addrs))
+    return rows >= 2 and 0 < row_bytes <= (1 << shift) and sp % 16 == 0 and dp % 16 == 0
 
 
 def push_rows(segs, src, dst, row_bytes, rows, sp, dp, shift):
     if row_bytes == 0 or rows == 0:
         return
-    if block_ok((src, dst, sp, dp), row_bytes, rows, shift):
+    if block_ok(sp, dp, row_bytes, rows, shift):
         segs.append((src, dst, row_bytes, row_bytes, rows, sp, dp, (1 << shift) // row_bytes))
     else:
         segs.extend((src + r * sp, dst + r * dp, row_bytes, row_bytes) for r in range(rows))
@@ -445,8 +481,7 @@ def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None, shift=
             out0 = out_addr(g) + L["in_off"][i] * es
             pitch = L["dk"][i] * L["inner"][i] * es
             srcs = [grad_addr(d * S + t, i) for t in range(S)]
-            if (L["padded"][i] == L["outer"][i] * run and block_ok((out0, src_off, pitch), run * es, L["outer"][i], shift)
-                    and all(a % 16 == 0 for a in srcs)):
+            if L["padded"][i] == L["outer"][i] * run and block_ok(pitch, run * es, run * es, L["outer"][i], shift):
                 src0 = len(ptr)
                 ptr += [a + src_off for a in srcs]
                 dst0 = len(ptr)
@@ -613,3 +648,98 @@ def test_strided_block_tables_cover_exactly(S, es, shift):
     jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims, shift)
     assert any(len(jb) == 10 for jb in jobs) or L["I"] * es < 16
     check_reduce(jobs, ptr, shift, es)
+
+
+# ---------------------------------------------------------------------------
+# XCD-aware chunk order (xcd_chunk in kernels.hip)
+# ---------------------------------------------------------------------------
+
+XCD_RUN = 64
+
+
+def xcd_chunk(c, n, run=XCD_RUN):
+    G = 8 * run
+    if c >= n // G * G:
+        return c
+    rem = c % G
+    return c - rem + (rem & 7) * run + (rem >> 3)
+
+
+def grid_for(n_chunks, max_grid):
+    if n_chunks < max_grid:
+        return n_chunks
+    return max_grid & ~7 if max_grid >= 8 else max_grid
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 511, 512, 513, 1023, 1024, 1556, 6148, 12296, 24736, 100003])
+def test_xcd_chunk_order_is_a_bijection(n):
+    assert sorted(xcd_chunk(c, n) for c in range(n)) == list(range(n))
+
+
+@pytest.mark.parametrize("n,max_grid", [(24736, 1 << 20), (5000, 1000), (5000, 1003), (100003, 4096), (9, 5)])
+def test_xcd_runs_are_contiguous_per_xcd(n, max_grid):
+    """Every chunk is processed exactly once over the grid-stride loop, and
+    in every full group the chunks of one XCD (slot % 8 under round-robin
+    dispatch) are kXcdRun consecutive chunks."""
+    G = grid_for(n, max_grid)
+    seen = []
+    xcd_of = {}
+    for b in range(G):
+        slot = b
+        while slot < n:
+            c = xcd_chunk(slot, n)
+            seen.append(c)
+            xcd_of[c] = b % 8
+            slot += G
+    assert sorted(seen) == list(range(n))
+    if G % 8 == 0 or G == n:
+        full = n // (8 * XCD_RUN) * 8 * XCD_RUN
+        for g0 in range(0, full, 8 * XCD_RUN):
+            for x in range(8):
+                run = range(g0 + x * XCD_RUN, g0 + (x + 1) * XCD_RUN)
+                assert {xcd_of[c] for c in run} == {x}
+
+
+@pytest.mark.parametrize("S", [2, 4, 8])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", (9, 14))
+def test_misaligned_strided_blocks_cover_exactly(S, es, shift):
+    """Copy blocks whose rows are not whole aligned vectors (odd slice
+    sizes put every rank slice at another offset mod 16; rows of a few
+    bytes; buffers at element offsets): heads, tails and realigned whole
+    vectors cover every row exactly, reads stay in each row's envelope."""
+    shapes = [(96, 64), (7, 40), (3,), (33, 128), (5, 24, 2), (2, 2048), (9, 8)]
+    dims = [1, 1, 0, 1, 1, 1, 1]
+    dims = [k if k == 0 or shapes[i][k] % S == 0 else 0 for i, k in enumerate(dims)]
+    rng = np.random.default_rng(S * 11 + es + shift)
+    base = 1 << 32
+    ag = base + es * int(rng.integers(1, 9))
+    full = {i: base + (1 << 30) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims, shift)
+    blocks = [sg for sg in segs if len(sg) == 8]
+    assert any((sg[0] | sg[1]) & 15 for sg in blocks), "no misaligned block planned"
+    check_copy(segs, es, shift)
+    grads = {i: (1 << 40) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + es * 5, dims, shift)
+    assert any(len(sg) == 8 for sg in segs)
+    check_copy(segs, es, shift)
+
+
+@pytest.mark.parametrize("S", [2, 4, 8])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", (9, 13))
+def test_misaligned_strided_reduce_jobs_cover_exactly(S, es, shift):
+    """RS copy-reduce blocks with gradients and outputs at element offsets
+    (operands shifted alike or differently, heads and tails per row)."""
+    shapes = [(96, 64), (7, 40), (3,), (33, 128), (5, 24, 2), (2, 2048), (9, 8)]
+    dims = [1, 1, 0, 1, 1, 1, 1]
+    dims = [k if k == 0 or shapes[i][k] % S == 0 else 0 for i, k in enumerate(dims)]
+    R = 2 * S
+    rng = np.random.default_rng(S * 13 + es + shift)
+    for same_shift in (True, False):
+        off = {(g, i): es * (3 if same_shift else int(rng.integers(0, 8))) for g in range(R) for i in range(len(shapes))}
+        gr = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + off[(g, i)] for g in range(R) for i in range(len(shapes))}
+        outs = {g: (1 << 46) + g * (1 << 26) + es * int(rng.integers(1, 8)) for g in range(R)}
+        jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims, shift)
+        assert any(len(jb) == 10 for jb in jobs)
+        check_reduce(jobs, ptr, shift, es)
