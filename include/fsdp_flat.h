@@ -1,9 +1,9 @@
 /*
  * fsdp_flat.h — C ABI of the MI355X (gfx950) FSDP/HSDP flat-buffer hot path.
  *
- * One bucket of P parameters, sharded on dim 0 over a shard group of S ranks
- * and replicated over D = R / S replicate groups, R simulated ranks resident
- * in one GPU's HBM.  Every device entry point is one HIP kernel launch,
+ * One bucket of P parameters, sharded (on dim 0 unless a parameter states
+ * another dim) over a shard group of S ranks and replicated over D = R / S
+ * replicate groups, R simulated ranks resident in one GPU's HBM.  Every device entry point is one HIP kernel launch,
  * enqueued on the caller's stream.  A call whose descriptor table (a
  * function of its shapes, sizes and pointers) is new uploads that table
  * once with a blocking copy; a repeated call makes no HIP call besides the
@@ -68,7 +68,7 @@ extern "C" {
 /* status codes */
 #define FSDP_OK        0
 #define FSDP_EINVAL    1  /* bad size, count, pointer or group arithmetic */
-#define FSDP_ENOTIMPL  2  /* shard_dim != 0, or a dtype the op does not take */
+#define FSDP_ENOTIMPL  2  /* an uneven non-zero shard dim, or a dtype the op does not take */
 #define FSDP_EALIGN    3  /* pointer not aligned as required */
 #define FSDP_EHIP      4  /* a HIP runtime call failed */
 #define FSDP_EOVERLAP  5  /* an output overlaps an input or another output */

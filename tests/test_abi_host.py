@@ -205,3 +205,24 @@ def test_binding_checks_buffer_sizes():
     x = torch.zeros(4)
     with pytest.raises(ValueError):  # host tensors are refused before any C call
         hp.fsdp_ag_copy_in([(4,)], 1, [x], x)
+
+
+def test_plain_c_consumer_of_the_header(tmp_path):
+    """A C program that includes only include/fsdp_flat.h, links the library
+    and calls the host-only entry points (and two argument errors) gets the
+    hand-derived values."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        pytest.skip("no C compiler")
+    lib = hp.lib_path()
+    if not os.path.exists(lib):
+        pytest.fail("libfsdpflat.so is not built (run __graft_entry__.build())")
+    exe = str(tmp_path / "c_abi_host")
+    src = os.path.join(ROOT, "tests", "c_abi_host.c")
+    libdir = os.path.dirname(lib)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src, "-o", exe,
+                        "-L", libdir, "-lfsdpflat", "-Wl,-rpath," + libdir], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
