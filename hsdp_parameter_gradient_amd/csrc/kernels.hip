@@ -299,7 +299,8 @@ __device__ __forceinline__ RowVec row_vec(uint32_t q, uint32_t vpr, uint64_t src
 template <int Q, bool NTS>
 __device__ __forceinline__ void rows_run(uint64_t s0, uint64_t d0, uint32_t nr, uint32_t vpr, uint64_t src_pitch,
                                          uint64_t dst_pitch, uint32_t b) {
-  constexpr int U = kCopyUnroll;
+  // a shifted vector takes two loads: half as many per lane
+  constexpr int U = Q < 0 ? kCopyUnroll : (kCopyUnroll > 1 ? kCopyUnroll / 2 : 1);
   constexpr int QQ = Q >= 0 ? Q : 0;
   const uint32_t nv = nr * vpr;
   uint32_t base = 0;
@@ -557,6 +558,10 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
                                                uint64_t va, uint64_t nv, int avg, float nf) {
   if constexpr (K > 0) {
     constexpr int U = (K >= 4 || ES == 2) ? 2 : 4;
+    // Shifted operands also hold a closing block each; with 8 of them one
+    // vector per lane keeps the kernel at 4 waves per SIMD (measured on
+    // MI355X: the RS of 8 misaligned slices 1320 -> 1206 us).
+    constexpr int US = K >= 8 ? 1 : U;
     uint64_t sb[K];
     uint32_t sr[K];
     bool same = true;
@@ -571,13 +576,13 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
       reduce_run<ES, K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     } else if (same) {
       switch (sr[0] >> 2) {
-        case 0: reduce_run<ES, K, U, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 1: reduce_run<ES, K, U, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 2: reduce_run<ES, K, U, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        default: reduce_run<ES, K, U, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 0: reduce_run<ES, K, US, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 1: reduce_run<ES, K, US, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 2: reduce_run<ES, K, US, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        default: reduce_run<ES, K, US, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
       }
     } else {
-      reduce_run<ES, K, U, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<ES, K, US, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     }
   } else {
     for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
@@ -627,7 +632,9 @@ template <int ES, int K, int MODE, int Q, bool NTS>
 __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                 const uint64_t (&sb)[K], uint64_t doff, uint32_t nr, uint32_t vpr,
                                                 uint32_t b, int avg, float nf) {
-  constexpr int U = (K >= 4 || ES == 2) ? 2 : 4;
+  // a shifted operand vector takes two loads: half as many per lane
+  constexpr int U0 = (K >= 4 || ES == 2) ? 2 : 4;
+  constexpr int U = MODE == 0 ? U0 : (U0 > 1 ? U0 / 2 : 1);
   const uint32_t nv = nr * vpr;
   auto store = [&](uint64_t dof, u32x4 o) {
     for (uint32_t m = 0; m < jb.ndst; ++m) stv<NTS>(gptr<u32x4>(ptr[jb.dst0 + m] + doff + dof), o);
