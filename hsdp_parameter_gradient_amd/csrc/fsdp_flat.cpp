@@ -16,7 +16,7 @@
 //   and 2.2.5: dp_size = rank_size / shard_size; RS when shard_size > 1,
 //   AR when dp_size > 1.
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdarg>

@@ -1,0 +1,177 @@
+// Host-side driver for a sanitizer build of the planner (fsdp_flat.cpp built
+// with g++ -fsanitize=address,undefined, without the device kernels).
+//
+// With no GPU visible, every call runs its validation and builds its
+// descriptor table; the upload then fails (no device) and the call returns
+// FSDP_EHIP, so the planner's table construction runs in full under the
+// sanitizers.  Calls that are rejected earlier must return the documented
+// error code.  The device kernels are replaced by launchers that must never
+// be reached.  Buffers are fake addresses that are never dereferenced.
+//
+// Prints "ok" (exit 0), "skip" (exit 0) when a GPU is visible, or the
+// failed checks (exit 1).
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "fsdp_flat.h"
+
+int fsdp_launch_seg_copy(int, const void*, uint32_t, uint64_t, uint32_t, uint32_t, int, void*) {
+  std::fprintf(stderr, "seg_copy launcher reached without a device\n");
+  std::abort();
+}
+int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, uint32_t, int, int, void*) {
+  std::fprintf(stderr, "reduce launcher reached without a device\n");
+  std::abort();
+}
+
+namespace {
+
+int failures = 0;
+
+void expect(int got, int want, const char* what, int line) {
+  if (got != want) {
+    std::fprintf(stderr, "line %d: %s returned %d, expected %d (%s)\n", line, what, got, want, fsdp_last_error());
+    ++failures;
+  }
+}
+#define EXPECT(call, want) expect((call), (want), #call, __LINE__)
+
+// Fake, disjoint, 512-byte-aligned buffers (plus an element offset).
+struct Fake {
+  uint64_t next = uint64_t(1) << 40;
+  void* get(uint64_t bytes, uint64_t offset = 0) {
+    void* p = reinterpret_cast<void*>(next + offset);
+    next += (bytes + offset + 4096 + 511) / 512 * 512;
+    return p;
+  }
+};
+
+struct Case {
+  std::vector<std::vector<int64_t>> shapes;
+  std::vector<int32_t> dims;  // empty: all 0
+};
+
+int64_t numel(const std::vector<int64_t>& s) {
+  int64_t n = 1;
+  for (int64_t d : s) n *= d;
+  return n;
+}
+
+void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
+  const int32_t P = (int32_t)c.shapes.size();
+  std::vector<int32_t> ndim;
+  std::vector<int64_t> shape;
+  for (const auto& s : c.shapes) {
+    ndim.push_back((int32_t)s.size());
+    shape.insert(shape.end(), s.begin(), s.end());
+  }
+  fsdp_bucket_t b = {P, ndim.data(), shape.data(), 0, c.dims.empty() ? nullptr : c.dims.data()};
+  int64_t I = 0;
+  if (fsdp_bucket_layout(&b, S, &I, nullptr, nullptr, nullptr, nullptr) != FSDP_OK) {
+    std::fprintf(stderr, "layout failed: %s\n", fsdp_last_error());
+    ++failures;
+    return;
+  }
+  std::vector<int64_t> row_len((size_t)P * S);
+  fsdp_bucket_layout(&b, S, nullptr, nullptr, nullptr, nullptr, row_len.data());
+  const int32_t dtype = es == 4 ? FSDP_F32 : FSDP_BF16;
+  const int32_t D = R / S;
+  Fake f;
+  const uint64_t off = misalign ? (uint64_t)es : 0;
+  // the layout's total bytes of chunk s of parameter i
+  auto chunk_bytes = [&](int32_t i, int32_t s) {
+    const auto& sh = c.shapes[(size_t)i];
+    const int32_t k = c.dims.empty() ? 0 : c.dims[(size_t)i];
+    return numel(sh) / (sh[(size_t)k] ? sh[(size_t)k] : 1) * row_len[(size_t)i * S + s] * es;
+  };
+  const bool work = I > 0;
+  const int want = work ? FSDP_EHIP : FSDP_OK;
+
+  std::vector<const void*> shards;
+  for (int32_t s = 0; s < S; ++s)
+    for (int32_t i = 0; i < P; ++i) shards.push_back(f.get((uint64_t)chunk_bytes(i, s), off));
+  void* ag = f.get((uint64_t)(S * I * es), off);
+  EXPECT(fsdp_ag_copy_in(&b, S, dtype, shards.data(), ag, nullptr), want);
+  std::vector<void*> full;
+  bool any_full = false;
+  for (int32_t i = 0; i < P; ++i) {
+    full.push_back(f.get((uint64_t)(numel(c.shapes[(size_t)i]) * es), off));
+    any_full = any_full || numel(c.shapes[(size_t)i]) > 0;
+  }
+  EXPECT(fsdp_ag_copy_out(&b, S, dtype, ag, full.data(), nullptr), any_full ? FSDP_EHIP : FSDP_OK);
+
+  std::vector<const void*> grads;
+  for (int32_t g = 0; g < R; ++g)
+    for (int32_t i = 0; i < P; ++i) grads.push_back(f.get((uint64_t)(numel(c.shapes[(size_t)i]) * es), off));
+  std::vector<void*> rs_in, rs_out;
+  for (int32_t g = 0; g < R; ++g) {
+    rs_in.push_back(f.get((uint64_t)(S * I * es), off));
+    rs_out.push_back(f.get((uint64_t)(I * es), off));
+  }
+  EXPECT(fsdp_rs_copy_in(&b, R, S, dtype, grads.data(), rs_in.data(), nullptr), want);
+  const void* const* rs_in_c = rs_in.data();
+  EXPECT(fsdp_rs_reduce(&b, R, S, D, FSDP_AVG, dtype, rs_in_c, rs_out.data(), nullptr), want);
+  EXPECT(fsdp_rs_copy_reduce(&b, R, S, D, FSDP_SUM, dtype, grads.data(), rs_out.data(), nullptr), want);
+
+  // fused buffers: this bucket's RS output plus two more segments
+  const int64_t segs[3] = {I, 3, 1000};
+  int64_t F = 0;
+  fsdp_fused_layout(3, segs, es, nullptr, &F);
+  std::vector<void*> fused;
+  for (int32_t g = 0; g < R; ++g) fused.push_back(f.get((uint64_t)(F * es)));
+  EXPECT(fsdp_fused_ar(3, segs, R, S, D, FSDP_AVG, dtype, fused.data(), nullptr), D > 1 ? FSDP_EHIP : FSDP_OK);
+
+  // argument errors, caught before planning
+  EXPECT(fsdp_rs_reduce(&b, R, S, D + 1, FSDP_AVG, dtype, rs_in_c, rs_out.data(), nullptr), FSDP_EINVAL);
+  EXPECT(fsdp_rs_copy_reduce(&b, R, S, D, 7, dtype, grads.data(), rs_out.data(), nullptr), FSDP_EINVAL);
+  EXPECT(fsdp_ag_copy_in(&b, S, 9, shards.data(), ag, nullptr), FSDP_ENOTIMPL);
+  if (work) {
+    // an output inside an input
+    std::vector<void*> bad(rs_out);
+    bad[0] = const_cast<void*>(rs_in_c[0]);
+    EXPECT(fsdp_rs_reduce(&b, R, S, D, FSDP_SUM, dtype, rs_in_c, bad.data(), nullptr), FSDP_EOVERLAP);
+  }
+}
+
+}  // namespace
+
+int main() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) == hipSuccess && n > 0) {
+    std::printf("skip\n");
+    return 0;
+  }
+  const std::vector<Case> cases = {
+      {{{7, 8}, {5, 3}, {16}}, {}},
+      {{{0, 4}, {1}, {2, 3, 4}, {9}, {13, 1, 2}}, {}},
+      {{{4097, 8}, {1009, 8}, {5, 64}, {3}}, {}},
+      {{{6, 8}, {4, 16, 3}, {5, 3, 8}, {7, 3}, {16}, {64, 1024}, {3, 4, 8}}, {1, 1, 2, 0, 0, 1, 2}},
+      {{{96, 64}, {7, 40}, {3}, {33, 128}, {5, 24, 2}, {2, 2048}, {9, 8}}, {1, 1, 0, 1, 1, 1, 1}},
+      {{}, {}},
+  };
+  for (size_t ci = 0; ci < cases.size(); ++ci) {
+    for (int32_t S : {1, 2, 4, 8}) {
+      const Case& c = cases[ci];
+      bool divisible = true;
+      for (size_t i = 0; i < c.dims.size(); ++i)
+        if (c.dims[i] != 0 && c.shapes[i][(size_t)c.dims[i]] % S) divisible = false;
+      if (!divisible) continue;
+      for (int32_t es : {2, 4})
+        for (bool mis : {false, true}) {
+          run_case(c, S, S, es, mis);
+          run_case(c, S, 2 * S, es, mis);
+        }
+    }
+  }
+  fsdp_release_cache();
+  if (failures) {
+    std::fprintf(stderr, "%d checks failed\n", failures);
+    return 1;
+  }
+  std::printf("ok\n");
+  return 0;
+}
