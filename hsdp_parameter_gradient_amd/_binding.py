@@ -196,25 +196,63 @@ def _dtype_code(dtype: torch.dtype) -> int:
     return _DTYPES[dtype]
 
 
-def _stream(stream) -> c_void_p:
+# torch's raw current-stream query costs ~0.1 us; torch.cuda.current_stream()
+# builds a Stream object (~3 us per call), which dominated small launches.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _stream(stream, device: int) -> c_void_p:
     if stream is None:
-        return c_void_p(torch.cuda.current_stream().cuda_stream or None)
+        if _raw_stream is not None:
+            return c_void_p(_raw_stream(device) or None)
+        return c_void_p(torch.cuda.current_stream(device).cuda_stream or None)
     if isinstance(stream, torch.cuda.Stream):
+        if stream.device_index != device:
+            raise ValueError(f"stream is on device {stream.device_index}, the buffers on device {device}")
         return c_void_p(stream.cuda_stream or None)
     return c_void_p(int(stream) or None)
 
 
+def _tensors(x):
+    if isinstance(x, torch.Tensor):
+        yield x
+    elif isinstance(x, (list, tuple)):
+        for y in x:
+            yield from _tensors(y)
+
+
+def _device_of(keep) -> int:
+    """The one device all tensors of a call live on."""
+    devs = {t.device.index for t in _tensors(keep)}
+    if len(devs) > 1:
+        raise ValueError(f"the buffers of one call are on several devices: {sorted(devs)}")
+    if not devs:
+        return torch.cuda.current_device()
+    (d,) = devs
+    return torch.cuda.current_device() if d is None else d
+
+
 class _Call:
-    """A marshalled C call; calling it issues the call on a stream."""
+    """A marshalled C call; calling it issues the call on a stream (default:
+    the current stream of the buffers' device), with that device current."""
 
     def __init__(self, name: str, args: tuple, keep: tuple):
         self.name = name
         self.fn = getattr(lib(), name)
         self.args = args
         self._keep = keep  # ctypes objects and tensors the pointers refer to
+        self.device = _device_of(keep)
 
     def __call__(self, stream=None) -> None:
-        _check(self.name, self.fn(*self.args, _stream(stream)))
+        st = _stream(stream, self.device)
+        cur = _get_device() if _get_device is not None else torch.cuda.current_device()
+        if cur == self.device:
+            rc = self.fn(*self.args, st)
+        else:
+            with torch.cuda.device(self.device):
+                rc = self.fn(*self.args, st)
+        _check(self.name, rc)
 
 
 def _prep_ag_copy_in(shapes, shard_size, shards, ag, shard_dims=None):
