@@ -195,3 +195,33 @@ def test_full_size_shard_dim_1(wname):
         assert torch.equal(fb.fused[g].view(torch.int32), before[g].view(torch.int32)), f"fused RS rank {g}"
     del fb, params, grads, before
     torch.cuda.empty_cache()
+
+
+def test_items_beyond_4gib():
+    """A copy segment and a reduction job each larger than 4 GiB (64-bit
+    offsets everywhere): AG copy-in of one bf16 parameter of 2^31 + 1001
+    elements with shard_size 1 (one 4 GiB + 2 KiB segment), and the fused
+    AR of two replicas of 2^30 + 1000 fp32 elements (integer-valued, so the
+    sum is exact)."""
+    note("[fullsize] items beyond 4 GiB")
+    n = (1 << 31) + 1001
+    x = torch.empty(n, dtype=torch.int16, device="cuda").random_().view(torch.bfloat16)
+    ag = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    hp.fsdp_ag_copy_in([(n,)], 1, [x], ag)
+    torch.cuda.synchronize()
+    assert torch.equal(ag.view(torch.int16), x.view(torch.int16))
+    del x, ag
+    torch.cuda.empty_cache()
+
+    m = (1 << 30) + 1000
+    _, F = hp.fsdp_fused_layout([m], 4)
+    fused = [torch.zeros(F, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for k, f in enumerate(fused):
+        f[:m] = torch.randint(-8, 9, (m,), device="cuda", generator=torch.Generator("cuda").manual_seed(k)).float()
+    want = fused[0] + fused[1]
+    hp.fsdp_fused_ar([m], 2, 1, 2, O.SUM, fused)
+    torch.cuda.synchronize()
+    for f in fused:
+        assert torch.equal(f, want)
+    del fused, want
+    torch.cuda.empty_cache()

@@ -149,6 +149,17 @@ def test_fp32_nonpow2_shard_group():
     run_copy_and_rs(w.name, shapes, 6, 3, W.params(w), W.grads(w))
 
 
+def test_many_parameters_deep_chunk_search():
+    """700 small ragged parameters over 8 ranks: 5600 AG segments and 44800
+    RS copy-in segments, so the 64-ary chunk search takes three levels."""
+    rng = np.random.default_rng(77)
+    shapes = [tuple([int(rng.integers(0, 40))] + ([int(rng.choice([1, 3, 8]))] if rng.random() < 0.5 else []))
+              for _ in range(700)]
+    w = W.Workload("many_params", 21, 8, 8, tuple(shapes), torch.float32, ("uniform", 1.0), ("normal", 1.0),
+                   ("sum", "avg"), W.ALL_STEPS)
+    run_copy_and_rs(w.name, shapes, 8, 8, W.params(w), W.grads(w), shard_offsets=[0, 1, 2, 3], out_offset=1)
+
+
 def test_random_buckets():
     rng = np.random.default_rng(2024)
     for case in range(16):
