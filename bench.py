@@ -59,10 +59,17 @@ def log(msg: str) -> None:
 
 
 def kernel_source_sha() -> str:
+    """Hash of the code (comments and whitespace removed) of the sources that
+    fix the kernels' traffic, so that editing a comment keeps the measured
+    traffic valid."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SRC:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

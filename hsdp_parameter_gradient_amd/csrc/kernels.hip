@@ -1,6 +1,6 @@
 // gfx950 kernels of the FSDP/HSDP flat-buffer hot path.
 //
-// Two kernels serve the five entry points:
+// Two kernels serve the six device entry points:
 //   seg_copy  — segmented copy with zero fill: AG copy-in (pack shards into
 //               padded rank slices), AG copy-out (unpack into the full
 //               parameters) and RS copy-in (chunk gradients into the padded
@@ -8,9 +8,9 @@
 //   reduce    — fixed-order reduction, in fp32, of K operands into M
 //               destinations, with a zero-filled tail per job: the RS of a
 //               shard group (K = S, M = 1), the RS read straight from the
-//               full gradients (one job per parameter, its padding zero
-//               filled), and the in-place fused AR of a replicate group
-//               (K = M = D).  fp32 or bf16 elements (bf16 widened exactly,
+//               full gradients (one job per rank and parameter, its
+//               padding zero filled), and the in-place fused AR of a
+//               replicate group (K = M = D).  fp32 or bf16 elements (bf16 widened exactly,
 //               summed in fp32, rounded once to nearest even).
 //
 // Both are HBM-bound streaming kernels (no data reuse, no dense
@@ -27,10 +27,12 @@
 // flight before the first use) and then a short guarded tail.
 //
 // The chunk of a parameter sharded on a non-zero dim is a strided block
-// (`outer` rows, one per index of the dims before the shard dim).  When its
-// rows are whole aligned vectors the planner hands it over as one item;
-// each chunk of it is a group of whole rows, copied or reduced as one flat
-// range of vectors (row and column from one integer division).
+// (`outer` rows, one per index of the dims before the shard dim).  When both
+// pitches are multiples of 16 bytes (every row then has the alignment of the
+// first) the planner hands it over as one item; each chunk of it is a group
+// of whole rows: their whole aligned destination vectors form one flat range
+// (row and column from one integer division), and each row's head and tail
+// bytes are moved element by element.
 //
 // Arithmetic: the reduce kernel adds operands one at a time in ascending
 // rank order, the accumulator starting from the first operand, in IEEE
@@ -81,11 +83,12 @@ constexpr int kCopyUnroll = FSDP_COPY_UNROLL;
 // group of 8*kXcdRun consecutive chunks, XCD x takes the kXcdRun
 // consecutive chunks [x*kXcdRun, (x+1)*kXcdRun): each XCD streams runs of
 // contiguous memory (1 MiB for the copy, 512 KiB for the reduce, at the
-// default chunk sizes) while all XCDs stay near the same front.  A bijection on [0, n): the last partial group keeps
-// the plain order.  Measured on MI355X against the plain order: the HSDP
-// block step -1.8 %, a 4-layer Llama-7B bucket -3.2 %, the ragged fp32 set
-// -3.6 % (runs of 16 to 128 chunks are all better than the plain order;
-// 256 and one contiguous eighth per XCD are worse on the small bucket).
+// default chunk sizes) while all XCDs stay near the same front.  A
+// bijection on [0, n): the last partial group keeps the plain order.
+// Measured on MI355X against the plain order: the HSDP block step -1.8 %,
+// a 4-layer Llama-7B bucket -3.6 %, the ragged fp32 set -3.9 % (runs of 16
+// to 128 chunks are all better than the plain order; runs of 256 and one
+// contiguous eighth per XCD are worse on the small bucket).
 constexpr uint64_t kXcdRun = 64;
 
 __device__ __forceinline__ uint64_t xcd_chunk(uint64_t c, uint64_t n) {
