@@ -630,3 +630,82 @@ def test_plan_cache_reuse_and_eviction():
         torch.cuda.synchronize()
         for o in outs:
             assert np.array_equal(bits(o), np_bits(want))
+
+
+# ---------------------------------------------------------------------------
+# IEEE special values through the reductions
+# ---------------------------------------------------------------------------
+
+SPECIAL_F32 = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 3.0, np.inf, -np.inf, np.nan, 1e-40, -1e-41, 1.4e-45,
+                        3.4028235e38, -3.4028235e38, 1e38, 2.0 ** -126, 7.0, -2.5], dtype=np.float32)
+
+
+def _special(n, rng, dtype):
+    v = SPECIAL_F32[rng.integers(0, len(SPECIAL_F32), n)]
+    t = torch.from_numpy(v)
+    return t if dtype == torch.float32 else t.to(torch.bfloat16)
+
+
+def _same_up_to_nan_payload(got_t, want_np):
+    """Bit-equal everywhere the oracle is not NaN; NaN where it is (fp32 NaN
+    payloads are not part of the result; bf16 NaN is one pattern, 0x7FC0,
+    on both sides and compared bit for bit)."""
+    got = bits(got_t)
+    want = np_bits(want_np)
+    if want_np.dtype == np.float32:
+        nan = np.isnan(want_np.reshape(-1))
+        g = got_t.detach().cpu().numpy().reshape(-1)
+        if not np.array_equal(np.isnan(g), nan):
+            return "NaN positions differ"
+        got, want = got[~nan], want[~nan]
+    return first_mismatch(got, want)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("R,S", [(8, 4), (6, 3), (8, 8), (6, 2)])
+def test_special_values_rs_and_fused_ar(dtype, R, S):
+    """Signed zeros, infinities, NaN, denormals and values that overflow when
+    added, through the RS (from the RS input and straight from the
+    gradients) and the fused AR, SUM and AVG (AVG by 3 included): the fixed
+    ascending order, IEEE fp32 with denormals kept, and one rounding to
+    bf16."""
+    note(f"[parity] special values dtype={dtype} R={R} S={S}")
+    rng = np.random.default_rng(R * 10 + S + (dtype == torch.bfloat16))
+    shapes = [(1027, 3), (5,), (2049,)]
+    lay = O.bucket_layout(shapes, S)
+    I, P, D = lay.I, len(shapes), R // S
+    grads = [[_special(int(np.prod(sh)), rng, dtype).reshape(sh) for sh in shapes] for _ in range(R)]
+    gnp = [[to_oracle(t) for t in grads[g]] for g in range(R)]
+    np_dt = np.float32 if dtype == torch.float32 else np.uint16
+    dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    rs_in = [torch.empty(S * I, dtype=dtype, device="cuda") for _ in range(R)]
+    hp.fsdp_rs_copy_in(shapes, R, S, dgrads, rs_in)
+    rs_o = [O.rs_copy_in(gnp[g], lay, np_dt) for g in range(R)]
+    with np.errstate(all="ignore"):
+        for op in (O.SUM, O.AVG):
+            want = O.rs_reduce(rs_o, I, R, S, op)
+            out = [torch.empty(I, dtype=dtype, device="cuda") for _ in range(R)]
+            out2 = [torch.empty(I, dtype=dtype, device="cuda") for _ in range(R)]
+            hp.fsdp_rs_reduce(shapes, R, S, D, op, rs_in, out)
+            hp.fsdp_rs_copy_reduce(shapes, R, S, D, op, dgrads, out2)
+            torch.cuda.synchronize()
+            for g in range(R):
+                assert _same_up_to_nan_payload(out[g], want[g]) == "", f"rs_reduce {op} rank {g}"
+                assert _same_up_to_nan_payload(out2[g], want[g]) == "", f"rs_copy_reduce {op} rank {g}"
+            if D > 1:
+                segs = [I, 300]
+                offs, F = O.fused_layout(segs, 4 if dtype == torch.float32 else 2)
+                fused_np = []
+                for g in range(R):
+                    f = np.zeros(F, np_dt)
+                    f[offs[0]:offs[0] + I] = want[g]
+                    f[offs[1]:offs[1] + 300] = to_oracle(_special(300, rng, dtype))
+                    fused_np.append(f)
+                fused = [torch.from_numpy(f.view(np.int16) if np_dt == np.uint16 else f).cuda() for f in fused_np]
+                if dtype == torch.bfloat16:
+                    fused = [f.view(torch.bfloat16) for f in fused]
+                want_ar = O.fused_ar(fused_np, R, S, op)
+                hp.fsdp_fused_ar(segs, R, S, D, op, fused)
+                torch.cuda.synchronize()
+                for g in range(R):
+                    assert _same_up_to_nan_payload(fused[g], want_ar[g]) == "", f"fused_ar {op} rank {g}"
