@@ -296,7 +296,8 @@ def ag_copy_out(ag: np.ndarray, lay: BucketLayout) -> List[np.ndarray]:
 # ---------------------------------------------------------------------------
 
 def rs_copy_in(grads: Sequence[np.ndarray], lay: BucketLayout, dtype=np.float32) -> np.ndarray:
-    """One rank's RS input: every gradient chunked on dim 0 and zero padded.
+    """One rank's RS input: every gradient chunked along its shard dim and
+    zero padded.
 
     [RAGGED] 6.4: the RS input of a non-uniform gradient is padded at the
     tail with zeros; with fused communication each gradient goes straight

@@ -309,13 +309,15 @@ def test_bf16_conversions_match_torch():
     assert np.array_equal(O.bf16_to_f32(bits).view(np.uint32), back.view(np.uint32))
 
 
-def test_bf16_reductions_round_once():
+def pin_bf16_round_once():
     """bf16 RS = round_to_bf16(float32 ordered sum of the widened operands),
     checked against torch's float32 arithmetic and its bf16 rounding."""
+    bad = []
     R, S = 8, 4
     shapes = [(33, 7), (10,)]
     lay = O.bucket_layout(shapes, S)
-    gi = [[torch.randn(sh).to(torch.bfloat16) for sh in shapes] for _ in range(R)]
+    gen = torch.Generator().manual_seed(5)
+    gi = [[torch.randn(sh, generator=gen).to(torch.bfloat16) for sh in shapes] for _ in range(R)]
     rs_in = [O.rs_copy_in([t.view(torch.int16).numpy().view(np.uint16) for t in gi[g]], lay, np.uint16)
              for g in range(R)]
     for op in (O.SUM, O.AVG):
@@ -328,7 +330,40 @@ def test_bf16_reductions_round_once():
             if op == O.AVG:
                 acc = acc / S
             want = acc.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-            assert np.array_equal(outs[g], want)
+            if not np.array_equal(outs[g], want):
+                bad.append(f"bf16 RS {op} rank {g}")
+    return bad
+
+
+def test_bf16_reductions_round_once():
+    assert pin_bf16_round_once() == []
+
+
+def pin_avg_correctly_rounded():
+    """AVG over a group of 3 or 6 (not a power of two) on integer-valued
+    gradients: the sum is exact, so the result must be the exact quotient
+    rounded once to float32 (the quotient of an integer by 3 is never a
+    float32 tie, so rounding the float64 quotient is rounding the exact
+    one)."""
+    from fractions import Fraction
+    bad = []
+    for R, S in ((6, 3), (6, 6), (12, 3)):
+        shapes = [(7, 8), (5, 3), (40,)]
+        lay = O.bucket_layout(shapes, S)
+        gi = [[RNG.integers(-9, 10, size=sh).astype(np.float32) for sh in shapes] for _ in range(R)]
+        rs_in = [O.rs_copy_in(gi[g], lay) for g in range(R)]
+        outs = O.rs_reduce(rs_in, lay.I, R, S, O.AVG)
+        for g in range(R):
+            d, s = divmod(g, S)
+            tot = sum(rs_in[m][s * lay.I:(s + 1) * lay.I].astype(np.int64) for m in range(d * S, d * S + S))
+            want = np.array([float(Fraction(int(v), S)) for v in tot], dtype=np.float64).astype(np.float32)
+            if not np.array_equal(outs[g].view(np.uint32), want.view(np.uint32)):
+                bad.append(f"AVG/{S} rank {g}")
+    return bad
+
+
+def test_avg_over_non_power_of_two_is_correctly_rounded():
+    assert pin_avg_correctly_rounded() == []
 
 
 @pytest.mark.parametrize("R,S", [(8, 4), (8, 1), (4, 4), (8, 2), (2, 1)])
@@ -401,10 +436,13 @@ def test_group_lists_and_decision_matrix(golden):
         assert all(len(set(a) & set(b)) == 1 for a in sg for b in rg)
 
 
+def pin_fused_layout(golden):
+    return ["fused " + c["why"] for c in golden["fused"]
+            if list(O.fused_layout(c["seg_numel"], c["elem_bytes"])) != [c["offsets"], c["F"]]]
+
+
 def test_fused_layout_golden(golden):
-    for c in golden["fused"]:
-        offs, Fn = O.fused_layout(c["seg_numel"], c["elem_bytes"])
-        assert (offs, Fn) == (c["offsets"], c["F"]), c["why"]
+    assert pin_fused_layout(golden) == []
     sizes = [int(v) for v in RNG.integers(0, 3000, size=200)]
     offs, Fn = O.fused_layout(sizes)
     end = 0
@@ -488,6 +526,44 @@ def _truncating_bf16(x):
     return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _avg_by_reciprocal(acc, op, n):
+    return acc * np.float32(1.0 / n) if op == F.AVG else acc
+
+
+def _round_each_add(operands):
+    bf = operands[0].dtype == np.uint16
+    acc = np.array(F._as_f32(operands[0]), dtype=np.float32, copy=True)
+    for x in operands[1:]:
+        acc = acc + F._as_f32(x)
+        if bf:
+            acc = F.bf16_to_f32(F.f32_to_bf16(acc))
+    return acc
+
+
+def _chunk_on_dim0(x, lay, i, s):
+    a, n = lay.row_off[i][s], lay.row_len[i][s]
+    return x[a:a + n]
+
+
+def _fused_align_256(seg_numel, elem_bytes=4, align_bytes=512):
+    return _ORIG_FUSED_LAYOUT(seg_numel, elem_bytes, 256)
+
+
+_ORIG_FUSED_LAYOUT = F.fused_layout
+_ORIG_RS_COPY_IN = F.rs_copy_in
+
+
+def _rs_copy_in_pad_one(grads, lay, dtype=np.float32):
+    buf = _ORIG_RS_COPY_IN(grads, lay, dtype)
+    data = np.zeros(buf.size, bool)
+    for i in range(len(lay.shapes)):
+        for s in range(lay.S):
+            a = s * lay.I + lay.in_off[i]
+            data[a:a + lay.row_len[i][s] * lay.inner[i] * lay.outer[i]] = True
+    buf[~data] = 1
+    return buf
+
+
 MUTANTS = {
     "bf16_truncation": ("f32_to_bf16", _truncating_bf16),
     "floor_chunk": ("dim0_chunk", _floor_chunk),
@@ -497,6 +573,11 @@ MUTANTS = {
     "dropped_term": ("_ordered_sum", _drop_last_operand),
     "rank_mapping": ("replicate_groups", _transposed_replicate_groups),
     "offset_by_actual": ("bucket_layout", _unpadded_bucket_layout),
+    "avg_by_reciprocal": ("_scale", _avg_by_reciprocal),
+    "bf16_round_each_add": ("_ordered_sum", _round_each_add),
+    "chunk_on_dim0": ("_chunk", _chunk_on_dim0),
+    "fused_align_256": ("fused_layout", _fused_align_256),
+    "rs_padding_not_zero": ("rs_copy_in", _rs_copy_in_pad_one),
 }
 
 
@@ -525,6 +606,10 @@ def _all_pins(golden):
         lambda: pin_end_to_end_exact(8, 4, O.AVG, [(7, 8), (5, 3), (16,)]),
         lambda: _groups_pin(golden),
         lambda: [] if _bf16_pin() else ["bf16 rounding"],
+        pin_bf16_round_once,
+        pin_avg_correctly_rounded,
+        pin_nonzero_dims,
+        lambda: pin_fused_layout(golden),
     ]
     bad = []
     for k, pin in enumerate(pins):
@@ -558,7 +643,10 @@ def test_unmutated_oracle_passes_all_pins(golden):
 MIXED = [((6, 8), 1), ((4, 12, 3), 1), ((5, 3, 8), 2), ((7, 3), 0), ((16,), 0), ((2, 0, 4), 2)]
 
 
-def test_nonzero_shard_dim_matches_torch_chunk_and_roundtrips():
+def pin_nonzero_dims():
+    """Chunks along a non-zero dim equal torch.chunk along that dim, sit
+    contiguously in their slice region, and gather back to the parameter."""
+    bad = []
     for S in (1, 2, 4):
         shapes = [sh for sh, k in MIXED]
         dims = [k for sh, k in MIXED]
@@ -570,16 +658,25 @@ def test_nonzero_shard_dim_matches_torch_chunk_and_roundtrips():
                 continue
             pieces = torch.chunk(torch.from_numpy(x), S, dim=k)
             for s in range(S):
-                assert np.array_equal(shards[s][i], pieces[s].numpy())
-            assert lay.padded[i] * S == x.size  # even: no padding
+                if not np.array_equal(shards[s][i], pieces[s].numpy()):
+                    bad.append(f"dim-{k} chunk S={S} param {i} rank {s}")
+            if lay.padded[i] * S != x.size:  # even: no padding
+                bad.append(f"dim-{k} padding S={S} param {i}")
         ag = O.ag_copy_in(shards, lay, np.float32)
         outs = O.ag_copy_out(O.all_gather(ag), lay)
-        assert all(np.array_equal(a, b) for a, b in zip(outs, xs))
+        if not all(np.array_equal(a, b) for a, b in zip(outs, xs)):
+            bad.append(f"dim-k round trip S={S}")
         # slice s, region i = rank s's chunk, contiguous
         for s in range(S):
             for i in range(len(shapes)):
                 region = ag[s * lay.I + lay.in_off[i]: s * lay.I + lay.in_off[i] + shards[s][i].size]
-                assert np.array_equal(region, shards[s][i].reshape(-1))
+                if not np.array_equal(region, shards[s][i].reshape(-1)):
+                    bad.append(f"dim-k region S={S} param {i} rank {s}")
+    return bad
+
+
+def test_nonzero_shard_dim_matches_torch_chunk_and_roundtrips():
+    assert pin_nonzero_dims() == []
 
 
 def test_nonzero_shard_dim_rejects_uneven():
