@@ -25,7 +25,7 @@ Sources (the pages, cited by title and section):
            padded_sharded_param_size, padded communication storage, AG / RS
            padding rules), 9.1 unit-test boundary list.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * rank g = d * S + s (mesh order (replicate, shard));
   * reductions add the group's operands one at a time in ascending rank
     order, the accumulator starting from the first operand;
