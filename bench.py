@@ -411,7 +411,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus}: this build runs on one GPU only (the R ranks are "
+        print(f"bench.py: --gpus {args.gpus}: the benchmark runs on one GPU only (the R ranks are "
               "simulated as HBM-resident slices of one GPU); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
