@@ -709,3 +709,48 @@ def test_special_values_rs_and_fused_ar(dtype, R, S):
                 torch.cuda.synchronize()
                 for g in range(R):
                     assert _same_up_to_nan_payload(fused[g], want_ar[g]) == "", f"fused_ar {op} rank {g}"
+
+
+def test_concurrent_calls_from_threads_on_their_own_streams():
+    """Four host threads, each with its own bucket and stream, issue passes
+    concurrently (ctypes releases the GIL, so the library's plan cache is
+    shared by truly concurrent callers); every thread's results match the
+    oracle."""
+    import threading
+    R, S = 8, 4
+    shape_sets = [[(7, 8), (5, 3), (16,)], [(1000, 3), (129,)], [(4097, 2), (3,)], [(33, 7), (2048, 64)]]
+    note("[parity] concurrent threads")
+    work = []
+    for t, shapes in enumerate(shape_sets):
+        w = W.Workload(f"thread_{t}", 700 + t, R, S, tuple(shapes), torch.float32, ("normal", 1.0), ("normal", 1.0),
+                       ("avg",), W.ALL_STEPS)
+        g_cpu = W.grads(w)
+        params = W.params(w)
+        fb = hp.FlatBucket(shapes, R, S, torch.float32, op=O.AVG)
+        fb.bind(fb.shard_views([p.cuda() for p in params]),
+                [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(len(shapes))])
+        _, fused_o, _, _ = O.reduce_grads_fused([[x.numpy() for x in g_cpu[g]] for g in range(R)], [shapes], R, S,
+                                                O.AVG)
+        work.append((fb, params, fused_o, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(fb, stream):
+        try:
+            for k in range(20):
+                fb.step(stream, fused_rs=bool(k % 2))
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(fb, st)) for fb, _, _, st in work]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for fb, params, fused_o, _ in work:
+        for i, p in enumerate(params):
+            assert np.array_equal(bits(fb.full[i]), bits(p.reshape(-1)))
+        for g in range(R):
+            assert first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g])) == "", f"rank {g}"
