@@ -555,8 +555,8 @@ def test_strided_blocks_all_steps(S, R, dtype):
     rows of whole vectors): several rows per chunk, a short last chunk, a
     row as large as a chunk, and rows that are not whole vectors beside
     them; every step against the oracle."""
-    shapes = [(64, 1024), (300, 256), (2, 8192), (3, 24, 2), (7, 3), (16,), (5, 32, 8)]
-    dims = [1, 1, 1, 1, 0, 0, 1]
+    shapes = [(64, 1024), (300, 256), (2, 8192), (3, 24, 2), (7, 3), (16,), (5, 32, 8), (0, 8), (2, 0, 8)]
+    dims = [1, 1, 1, 1, 0, 0, 1, 1, 2]
     run_nonzero_dims(shapes, dims, S, R, dtype, aligned=True)
 
 
