@@ -3,9 +3,10 @@
 FlatBucket owns (through torch, which supplies device memory) the buffers
 of one bucket of parameters with all R simulated ranks resident in HBM:
 
-  ag        [S*I]   AG buffer; slice s is shard rank s's send buffer
+  ag        [S*I]   AG buffer (parameter dtype); slice s is shard rank s's
+                    send buffer
   full[i]           the full parameters written by AG copy-out
-  rs_in[g]  [S*I]   rank g's padded RS input (fp32)
+  rs_in[g]  [S*I]   rank g's padded RS input (gradient dtype: fp32 or bf16)
   fused[g]  [F]     rank g's 512-byte-aligned fused AR buffer; the RS output
                     of rank g is the view fused[g][off : off + I]
                     (zero-copy, PR #758 write-up of the Hyper
