@@ -238,9 +238,9 @@ def cpu_model() -> str:
 
 
 def bucket_variant(w, op, K: int, warmup: int, grad_dtype=None, shard_dims=None):
-    """The whole pass of the workload with bf16 gradients (reduce dtype
-    bf16), or with the 2-D parameters sharded on dim 1: time per pass, GB/s
-    of its algorithmic bytes, and each step's time."""
+    """The whole pass of the workload with 16-bit gradients (reduce dtype
+    bf16 or fp16), or with the 2-D parameters sharded on dim 1: time per
+    pass, GB/s of its algorithmic bytes, and each step's time."""
     import torch
 
     import hsdp_parameter_gradient_amd as hp
@@ -399,7 +399,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the bf16-gradient and shard-dim-1 variants")
+                    help="skip the 16-bit-gradient and shard-dim-1 variants")
     ap.add_argument("--pipeline-layers", type=int, default=8,
                     help="layers in the backward-overlap variant (0 = skip it)")
     ap.add_argument("--cold-warm-reps", type=int, default=20,
@@ -537,6 +537,7 @@ def main():
             variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
         if not args.no_variants:
             variants["bf16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.bfloat16)
+            variants["fp16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.float16)
             dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
             if any(dims):
                 variants["shard_dim_1"] = bucket_variant(w, op, K, args.warmup, shard_dims=dims)

@@ -297,13 +297,13 @@ def _prep_rs_copy_in(shapes, rank_size, shard_size, grads, rs_in, shard_dims=Non
                  (b, garr, rarr, tuple(grads), tuple(rs_in)))
 
 
-_REDUCE_DTYPES = (torch.float32, torch.bfloat16)
+_REDUCE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 
 
 def _reduce_dtype(tensors, what) -> torch.dtype:
     dt = tensors[0].dtype if len(tensors) else torch.float32
     if dt not in _REDUCE_DTYPES:
-        raise ValueError(f"{what}: reductions take float32 or bfloat16, not {dt}")
+        raise ValueError(f"{what}: reductions take float32, bfloat16 or float16, not {dt}")
     return dt
 
 

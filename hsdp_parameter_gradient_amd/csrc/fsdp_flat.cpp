@@ -143,9 +143,9 @@ int elem_size(int32_t dtype) {
   }
 }
 
-// Element size of a reduction dtype: fp32, or bf16 summed in fp32.
+// Element size of a reduction dtype: fp32, or bf16 / fp16 (summed in fp32).
 int reduce_elem_size(int32_t dtype) {
-  return dtype == FSDP_F32 ? 4 : dtype == FSDP_BF16 ? 2 : 0;
+  return dtype == FSDP_F32 ? 4 : (dtype == FSDP_BF16 || dtype == FSDP_F16) ? 2 : 0;
 }
 
 int check_groups(int32_t R, int32_t S) {
@@ -256,7 +256,7 @@ struct Plan {
   uint32_t n_items = 0;
   uint64_t n_chunks = 0;
   uint32_t shift = 0;
-  int es = 0;
+  int es = 0;  // copies: element bytes; reductions: the dtype code
   uint32_t nsrc = 0;
   int avg = 0;
   int nts = 0;
@@ -422,7 +422,7 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
 }
 
 // Plan the reduction over `jobs` (every job with the same operand count).
-int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg, Reuse reuse,
+int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int dtype, int avg, Reuse reuse,
                 Plan* p) {
   jobs.erase(std::remove_if(jobs.begin(), jobs.end(), [](const fsdp::RedJob& jb) { return jb.nbytes == 0; }),
              jobs.end());
@@ -448,7 +448,7 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
   p->n_items = (uint32_t)jobs.size();
   p->n_chunks = n;
   p->shift = tu.reduce_shift;
-  p->es = es;
+  p->es = dtype;
   p->nsrc = jobs[0].nsrc;
   p->avg = avg;
   p->nts = stream_stores(reuse, out_bytes);
@@ -463,10 +463,10 @@ int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, h
   return store_and_launch(std::move(key), std::move(p), stream);
 }
 
-int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int es, int avg,
+int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int dtype, int avg,
                Reuse reuse, hipStream_t stream) {
   Plan p;
-  int rc = plan_reduce(jobs, ptrs, es, avg, reuse, &p);
+  int rc = plan_reduce(jobs, ptrs, dtype, avg, reuse, &p);
   if (rc) return rc;
   return store_and_launch(std::move(key), std::move(p), stream);
 }
@@ -687,7 +687,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
   const int es = reduce_elem_size(dtype);
-  if (!es) return fail(FSDP_ENOTIMPL, "rs_reduce takes fp32 or bf16 (dtype %d)", dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "rs_reduce takes fp32, bf16 or fp16 (dtype %d)", dtype);
   Layout L;
   if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int32_t R = rank_size, S = shard_size;
@@ -716,7 +716,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
     ptrs.push_back((uint64_t)rs_out[g]);
     jobs.push_back(jb);
   }
-  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext,
+  return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -737,7 +737,7 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
   const int es = reduce_elem_size(dtype);
-  if (!es) return fail(FSDP_ENOTIMPL, "rs_copy_reduce takes fp32 or bf16 (dtype %d)", dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "rs_copy_reduce takes fp32, bf16 or fp16 (dtype %d)", dtype);
   Layout L;
   if ((rc = make_layout(bucket, shard_size, &L))) return rc;
   const int32_t R = rank_size, S = shard_size, P = L.P;
@@ -809,7 +809,7 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
-  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kReadNext,
+  return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -832,7 +832,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
   if (op != FSDP_SUM && op != FSDP_AVG) return fail(FSDP_EINVAL, "reduce op %d", op);
   const int es = reduce_elem_size(dtype);
-  if (!es) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32 or bf16 (dtype %d)", dtype);
+  if (!es) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32, bf16 or fp16 (dtype %d)", dtype);
   int64_t F = 0;
   if ((rc = fsdp_fused_layout(n_seg, seg_numel, es, nullptr, &F))) return rc;
   const int32_t R = rank_size, S = shard_size, D = dp_size;
@@ -857,7 +857,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
     jb.ndst = (uint32_t)D;
     jobs.push_back(jb);
   }
-  return run_reduce(std::move(key), jobs, ptrs, es, op == FSDP_AVG, Reuse::kFinal,
+  return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kFinal,
                     static_cast<hipStream_t>(stream));
 }
 

@@ -10,8 +10,9 @@
 //               shard group (K = S, M = 1), the RS read straight from the
 //               full gradients (one job per rank and parameter, its
 //               padding zero filled), and the in-place fused AR of a
-//               replicate group (K = M = D).  fp32 or bf16 elements (bf16 widened exactly,
-//               summed in fp32, rounded once to nearest even).
+//               replicate group (K = M = D).  fp32, bf16 or fp16 elements
+//               (16-bit elements widened exactly, summed in fp32, rounded
+//               once to nearest even).
 //
 // Both are HBM-bound streaming kernels (no data reuse, no dense
 // contraction): one workgroup of 256 lanes handles one chunk of destination
@@ -38,7 +39,8 @@
 // rank order, the accumulator starting from the first operand, in IEEE
 // fp32 with denormals preserved; AVG divides the sum by the operand count
 // with a correctly rounded division (for a power of two that is the exact
-// multiply by its reciprocal); bf16 results are rounded once, at the store.
+// multiply by its reciprocal); bf16 and fp16 results are rounded once, at
+// the store.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -430,46 +432,78 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
 }
 
-// The values of one 16-byte vector in float32: 4 fp32 (ES = 4) or 8 bf16
-// widened exactly (ES = 2).  bf16 element 2i is the low half of dword i.
-template <int ES>
+// Element kinds of the reductions (the values of the FSDP dtype codes).
+enum : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// float32 -> float16 bits, round to nearest, ties to even (the hardware
+// conversion; overflow to infinity, float16 denormals kept).
+__device__ __forceinline__ uint32_t f16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// One element of kind E (its bits in the low bits of w) in float32, exactly.
+template <int E>
+__device__ __forceinline__ float elt_to_f32(uint32_t w) {
+  if constexpr (E == kF32) return __builtin_bit_cast(float, w);
+  else if constexpr (E == kBF16) return __builtin_bit_cast(float, w << 16);
+  else return f16_to_f32(w & 0xffffu);
+}
+// float32 rounded once to kind E, as bits.
+template <int E>
+__device__ __forceinline__ uint32_t f32_to_elt(float f) {
+  if constexpr (E == kF32) return __builtin_bit_cast(uint32_t, f);
+  else if constexpr (E == kBF16) return bf16_rne(f);
+  else return f16_rne(f);
+}
+
+// The values of one 16-byte vector in float32: 4 fp32, or 8 bf16 / fp16
+// widened exactly.  16-bit element 2i is the low half of dword i.
+template <int E>
 struct Acc {
-  static constexpr int N = ES == 4 ? 1 : 2;
+  static constexpr int N = E == kF32 ? 1 : 2;
   f32x4 v[N];
 };
 
-template <int ES>
-__device__ __forceinline__ Acc<ES> widen(u32x4 w) {
-  Acc<ES> a;
-  if constexpr (ES == 4) {
+template <int E>
+__device__ __forceinline__ Acc<E> widen(u32x4 w) {
+  Acc<E> a;
+  if constexpr (E == kF32) {
     a.v[0] = as_f4(w);
-  } else {
+  } else if constexpr (E == kBF16) {
     const uint32_t hi = 0xffff0000u;
     a.v[0] = as_f4(u32x4{w.x << 16, w.x & hi, w.y << 16, w.y & hi});
     a.v[1] = as_f4(u32x4{w.z << 16, w.z & hi, w.w << 16, w.w & hi});
+  } else {
+    a.v[0] = f32x4{f16_to_f32(w.x & 0xffffu), f16_to_f32(w.x >> 16), f16_to_f32(w.y & 0xffffu),
+                   f16_to_f32(w.y >> 16)};
+    a.v[1] = f32x4{f16_to_f32(w.z & 0xffffu), f16_to_f32(w.z >> 16), f16_to_f32(w.w & 0xffffu),
+                   f16_to_f32(w.w >> 16)};
   }
   return a;
 }
 
-template <int ES>
-__device__ __forceinline__ void accumulate(Acc<ES>& a, u32x4 w) {
-  const Acc<ES> b = widen<ES>(w);
+template <int E>
+__device__ __forceinline__ void accumulate(Acc<E>& a, u32x4 w) {
+  const Acc<E> b = widen<E>(w);
 #pragma unroll
-  for (int i = 0; i < Acc<ES>::N; ++i) a.v[i] = a.v[i] + b.v[i];
+  for (int i = 0; i < Acc<E>::N; ++i) a.v[i] = a.v[i] + b.v[i];
 }
 
-template <int ES>
-__device__ __forceinline__ u32x4 narrow(Acc<ES>& a, int avg, float nf) {
+template <int E>
+__device__ __forceinline__ u32x4 narrow(Acc<E>& a, int avg, float nf) {
   if (avg) {
 #pragma unroll
-    for (int i = 0; i < Acc<ES>::N; ++i) a.v[i] = a.v[i] / nf;
+    for (int i = 0; i < Acc<E>::N; ++i) a.v[i] = a.v[i] / nf;
   }
-  if constexpr (ES == 4) {
+  if constexpr (E == kF32) {
     return as_u4(a.v[0]);
   } else {
     const f32x4 l = a.v[0], h = a.v[1];
-    return u32x4{bf16_rne(l.x) | (bf16_rne(l.y) << 16), bf16_rne(l.z) | (bf16_rne(l.w) << 16),
-                 bf16_rne(h.x) | (bf16_rne(h.y) << 16), bf16_rne(h.z) | (bf16_rne(h.w) << 16)};
+    return u32x4{f32_to_elt<E>(l.x) | (f32_to_elt<E>(l.y) << 16), f32_to_elt<E>(l.z) | (f32_to_elt<E>(l.w) << 16),
+                 f32_to_elt<E>(h.x) | (f32_to_elt<E>(h.y) << 16), f32_to_elt<E>(h.z) | (f32_to_elt<E>(h.w) << 16)};
   }
 }
 
@@ -496,7 +530,7 @@ __device__ __forceinline__ void store_vectors(const u32x4 (&o)[U], const fsdp::R
 // All data vectors [0, nv) of one job window for a compile-time operand
 // count K: whole iterations of U vectors per lane with the K*U operand loads
 // in flight together, then a tail of single vectors.
-template <int ES, int K, int U, int MODE, int Q, bool NTS>
+template <int E, int K, int U, int MODE, int Q, bool NTS>
 __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                            const uint64_t (&sb)[K], const uint32_t (&sr)[K], uint64_t va,
                                            uint64_t nv, int avg, float nf) {
@@ -533,10 +567,10 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
     u32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      Acc<ES> acc = widen<ES>(v[0][u]);
+      Acc<E> acc = widen<E>(v[0][u]);
 #pragma unroll
-      for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t][u]);
-      o[u] = narrow<ES>(acc, avg, nf);
+      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t][u]);
+      o[u] = narrow<E>(acc, avg, nf);
     }
     store_vectors<U, NTS>(o, jb, ptr, va, j, stride);
   }
@@ -544,10 +578,10 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
     u32x4 v[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) v[t] = operand<(MODE == 1 ? 2 : MODE), Q>(gptr<u32x4>(sb[t]), j, sr[t], b);
-    Acc<ES> acc = widen<ES>(v[0]);
+    Acc<E> acc = widen<E>(v[0]);
 #pragma unroll
-    for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t]);
-    const u32x4 o[1] = {narrow<ES>(acc, avg, nf)};
+    for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
+    const u32x4 o[1] = {narrow<E>(acc, avg, nf)};
     store_vectors<1, NTS>(o, jb, ptr, va, j, kBlock);
   }
 }
@@ -556,11 +590,11 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
 // va + 16 q of every destination, operand t read at the same offset of its
 // source.  K > 0: compile-time operand count; K == 0: any count, one operand
 // at a time.
-template <int ES, int K, bool NTS>
+template <int E, int K, bool NTS>
 __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                uint64_t va, uint64_t nv, int avg, float nf) {
   if constexpr (K > 0) {
-    constexpr int U = (K >= 4 || ES == 2) ? 2 : 4;
+    constexpr int U = (K >= 4 || E != kF32) ? 2 : 4;
     // Shifted operands also hold a closing block each; with 8 of them one
     // vector per lane keeps the kernel at 4 waves per SIMD (measured on
     // MI355X: the RS of 8 misaligned slices 1320 -> 1206 us).
@@ -576,30 +610,30 @@ __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uin
       same = same && sr[t] == sr[0];
     }
     if (same && sr[0] == 0) {
-      reduce_run<ES, K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<E, K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     } else if (same) {
       switch (sr[0] >> 2) {
-        case 0: reduce_run<ES, K, US, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 1: reduce_run<ES, K, US, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 2: reduce_run<ES, K, US, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        default: reduce_run<ES, K, US, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 0: reduce_run<E, K, US, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 1: reduce_run<E, K, US, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 2: reduce_run<E, K, US, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        default: reduce_run<E, K, US, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
       }
     } else {
-      reduce_run<ES, K, US, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<E, K, US, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
     }
   } else {
     for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
-      Acc<ES> acc;
+      Acc<E> acc;
       for (uint32_t t = 0; t < jb.nsrc; ++t) {
         const uint64_t sa = ptr[jb.src0 + t] + va;
         const uint32_t r = (uint32_t)(sa & 15u);
         const u32x4 w = load_shifted(gptr<u32x4>(sa - r), j, r);
         if (t == 0)
-          acc = widen<ES>(w);
+          acc = widen<E>(w);
         else
-          accumulate<ES>(acc, w);
+          accumulate<E>(acc, w);
       }
-      const u32x4 o[1] = {narrow<ES>(acc, avg, nf)};
+      const u32x4 o[1] = {narrow<E>(acc, avg, nf)};
       store_vectors<1, NTS>(o, jb, ptr, va, j, kBlock);
     }
   }
@@ -631,12 +665,12 @@ __device__ __forceinline__ u32x4 row_operand(uint64_t a, uint32_t b) {
 // column q % vpr; operand t's bytes at sb[t] + the row's source offset, the
 // result at every destination + the row's destination offset.  U vectors
 // per lane per iteration with the K*U loads in flight together.
-template <int ES, int K, int MODE, int Q, bool NTS>
+template <int E, int K, int MODE, int Q, bool NTS>
 __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                 const uint64_t (&sb)[K], uint64_t doff, uint32_t nr, uint32_t vpr,
                                                 uint32_t b, int avg, float nf) {
   // a shifted operand vector takes two loads: half as many per lane
-  constexpr int U0 = (K >= 4 || ES == 2) ? 2 : 4;
+  constexpr int U0 = (K >= 4 || E != kF32) ? 2 : 4;
   constexpr int U = MODE == 0 ? U0 : (U0 > 1 ? U0 / 2 : 1);
   const uint32_t nv = nr * vpr;
   auto store = [&](uint64_t dof, u32x4 o) {
@@ -654,10 +688,10 @@ __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const ui
       for (int u = 0; u < U; ++u) v[t][u] = row_operand<MODE, Q>(sb[t] + x[u].src, b);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      Acc<ES> acc = widen<ES>(v[0][u]);
+      Acc<E> acc = widen<E>(v[0][u]);
 #pragma unroll
-      for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t][u]);
-      store(x[u].dst, narrow<ES>(acc, avg, nf));
+      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t][u]);
+      store(x[u].dst, narrow<E>(acc, avg, nf));
     }
   }
   for (uint32_t q = base + threadIdx.x; q < nv; q += kBlock) {
@@ -665,10 +699,10 @@ __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const ui
     u32x4 v[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) v[t] = row_operand<MODE, Q>(sb[t] + x.src, b);
-    Acc<ES> acc = widen<ES>(v[0]);
+    Acc<E> acc = widen<E>(v[0]);
 #pragma unroll
-    for (int t = 1; t < K; ++t) accumulate<ES>(acc, v[t]);
-    store(x.dst, narrow<ES>(acc, avg, nf));
+    for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
+    store(x.dst, narrow<E>(acc, avg, nf));
   }
 }
 
@@ -678,10 +712,11 @@ __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const ui
 // before its first aligned vector, whole vectors, a tail.  The whole
 // vectors of all rows are one flat range; heads and tails are reduced
 // element by element, one row end per lane, in the same operand order.
-template <int ES, int K, bool NTS>
+template <int E, int K, bool NTS>
 __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr, uint64_t k,
                                             int avg, float nf) {
-  typedef typename std::conditional<ES == 4, uint32_t, uint16_t>::type T;
+  typedef typename std::conditional<E == kF32, uint32_t, uint16_t>::type T;
+  constexpr int ES = sizeof(T);
   const uint64_t r0 = k * jb.rows_per_chunk;
   const uint64_t left = jb.rows - r0;
   const uint32_t nr = (uint32_t)(left < jb.rows_per_chunk ? left : jb.rows_per_chunk);
@@ -703,25 +738,25 @@ __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64
       const uint32_t r = (uint32_t)(sb[0] & 15u), b = r & 3u;
       const uint64_t dh = doff + head;
       if (same && r == 0) {
-        reduce_rows_run<ES, K, 0, 0, NTS>(jb, ptr, sb, dh, nr, vpr, 0, avg, nf);
+        reduce_rows_run<E, K, 0, 0, NTS>(jb, ptr, sb, dh, nr, vpr, 0, avg, nf);
       } else if (same) {
         switch (r >> 2) {
-          case 0: reduce_rows_run<ES, K, 1, 0, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
-          case 1: reduce_rows_run<ES, K, 1, 1, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
-          case 2: reduce_rows_run<ES, K, 1, 2, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
-          default: reduce_rows_run<ES, K, 1, 3, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
+          case 0: reduce_rows_run<E, K, 1, 0, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
+          case 1: reduce_rows_run<E, K, 1, 1, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
+          case 2: reduce_rows_run<E, K, 1, 2, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
+          default: reduce_rows_run<E, K, 1, 3, NTS>(jb, ptr, sb, dh, nr, vpr, b, avg, nf); break;
         }
       } else {
-        reduce_rows_run<ES, K, 2, 0, NTS>(jb, ptr, sb, dh, nr, vpr, 0, avg, nf);
+        reduce_rows_run<E, K, 2, 0, NTS>(jb, ptr, sb, dh, nr, vpr, 0, avg, nf);
       }
     } else {
       const uint32_t nv = nr * vpr;
       for (uint32_t q = threadIdx.x; q < nv; q += kBlock) {
         const RowVec x = row_vec(q, vpr, jb.src_pitch, jb.dst_pitch);
-        Acc<ES> acc = widen<ES>(row_operand<2, 0>(ptr[jb.src0] + soff + head + x.src, 0));
+        Acc<E> acc = widen<E>(row_operand<2, 0>(ptr[jb.src0] + soff + head + x.src, 0));
         for (uint32_t t = 1; t < jb.nsrc; ++t)
-          accumulate<ES>(acc, row_operand<2, 0>(ptr[jb.src0 + t] + soff + head + x.src, 0));
-        const u32x4 o = narrow<ES>(acc, avg, nf);
+          accumulate<E>(acc, row_operand<2, 0>(ptr[jb.src0 + t] + soff + head + x.src, 0));
+        const u32x4 o = narrow<E>(acc, avg, nf);
         for (uint32_t m = 0; m < jb.ndst; ++m) stv<NTS>(gptr<u32x4>(ptr[jb.dst0 + m] + doff + head + x.dst), o);
       }
     }
@@ -735,11 +770,11 @@ __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64
         float acc = 0.0f;
         for (uint32_t i = 0; i < jb.nsrc; ++i) {
           const T w = *gptr<T>(ptr[jb.src0 + i] + so);
-          const float v = ES == 4 ? __builtin_bit_cast(float, (uint32_t)w) : __builtin_bit_cast(float, (uint32_t)w << 16);
+          const float v = elt_to_f32<E>((uint32_t)w);
           acc = (i == 0) ? v : acc + v;
         }
         if (avg) acc = acc / nf;
-        const T out = ES == 4 ? (T)__builtin_bit_cast(uint32_t, acc) : (T)bf16_rne(acc);
+        const T out = (T)f32_to_elt<E>(acc);
         const uint64_t dof = doff + row * jb.dst_pitch + x;
         for (uint32_t m = 0; m < jb.ndst; ++m) *gptr<T>(ptr[jb.dst0 + m] + dof) = out;
       }
@@ -749,11 +784,12 @@ __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64
 
 // Elements [max(a, lo), min(a + 16, hi)) of the 16-byte vector at d0-relative
 // address a: reduced below the data end, zero above it.
-template <int ES>
+template <int E>
 __device__ __forceinline__ void reduce_partial(uint64_t a, uint64_t lo, uint64_t hi, uint64_t cend,
                                                const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                uint64_t d0, int avg, float nf) {
-  typedef typename std::conditional<ES == 4, uint32_t, uint16_t>::type T;
+  typedef typename std::conditional<E == kF32, uint32_t, uint16_t>::type T;
+  constexpr int ES = sizeof(T);
   const uint64_t x0 = a > lo ? a : lo;
   const uint64_t x1 = (a + 16) < hi ? (a + 16) : hi;
   for (uint64_t x = x0; x < x1; x += ES) {
@@ -763,17 +799,17 @@ __device__ __forceinline__ void reduce_partial(uint64_t a, uint64_t lo, uint64_t
       float acc = 0.0f;
       for (uint32_t t = 0; t < jb.nsrc; ++t) {
         const T w = *gptr<T>(ptr[jb.src0 + t] + off);
-        const float v = ES == 4 ? __builtin_bit_cast(float, (uint32_t)w) : __builtin_bit_cast(float, (uint32_t)w << 16);
+        const float v = elt_to_f32<E>((uint32_t)w);
         acc = (t == 0) ? v : acc + v;
       }
       if (avg) acc = acc / nf;
-      out = ES == 4 ? (T)__builtin_bit_cast(uint32_t, acc) : (T)bf16_rne(acc);
+      out = (T)f32_to_elt<E>(acc);
     }
     for (uint32_t m = 0; m < jb.ndst; ++m) *gptr<T>(ptr[jb.dst0 + m] + off) = out;
   }
 }
 
-template <int ES, int K, bool NTS>
+template <int E, int K, bool NTS>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restrict__ begin,
                                                         const fsdp::RedJob* __restrict__ jobs,
                                                         const uint64_t* __restrict__ ptr,
@@ -786,7 +822,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     const fsdp::RedJob jb = jobs[j];
     const uint64_t k = c - begin[j];
     if (jb.rows > 1) {
-      reduce_rows<ES, K, NTS>(jb, ptr, k, avg, (float)jb.nsrc);
+      reduce_rows<E, K, NTS>(jb, ptr, k, avg, (float)jb.nsrc);
       continue;
     }
     const uint64_t d0 = ptr[jb.dst0];
@@ -801,7 +837,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     // whole vectors of data: offsets [va, vb) relative to d0
     const uint64_t ca = align_up16(lo);
     const uint64_t cb = align_down16(hi < cend ? hi : cend);
-    if (ca < cb) reduce_vectors<ES, K, NTS>(jb, ptr, ca - d0, (cb - ca) >> 4, avg, nf);
+    if (ca < cb) reduce_vectors<E, K, NTS>(jb, ptr, ca - d0, (cb - ca) >> 4, avg, nf);
     // whole vectors of padding (zero) in every destination
     const uint64_t za = align_up16(lo > cend ? lo : cend);
     const uint64_t zb = align_down16(hi);
@@ -816,9 +852,9 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
       const bool p_lo = (lo & 15) != 0;
       const bool p_c = (cend & 15) != 0 && lo < cend && cend < hi && !(p_lo && a_c == a_lo);
       const bool p_hi = (hi & 15) != 0 && !(p_lo && a_hi == a_lo) && !(p_c && a_hi == a_c);
-      if (threadIdx.x == 0 && p_lo) reduce_partial<ES>(a_lo, lo, hi, cend, jb, ptr, d0, avg, nf);
-      if (threadIdx.x == 1 && p_c) reduce_partial<ES>(a_c, lo, hi, cend, jb, ptr, d0, avg, nf);
-      if (threadIdx.x == 2 && p_hi) reduce_partial<ES>(a_hi, lo, hi, cend, jb, ptr, d0, avg, nf);
+      if (threadIdx.x == 0 && p_lo) reduce_partial<E>(a_lo, lo, hi, cend, jb, ptr, d0, avg, nf);
+      if (threadIdx.x == 1 && p_c) reduce_partial<E>(a_c, lo, hi, cend, jb, ptr, d0, avg, nf);
+      if (threadIdx.x == 2 && p_hi) reduce_partial<E>(a_hi, lo, hi, cend, jb, ptr, d0, avg, nf);
     }
   }
 }
@@ -853,21 +889,31 @@ int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, 
 }
 
 namespace {
-template <int ES, bool NTS>
+template <int E, bool NTS>
 void launch_reduce_k(uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
                      const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
                      uint32_t chunk_shift, int avg) {
   switch (n_src) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<ES, 1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<ES, 2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<ES, 4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<ES, 8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    default: hipLaunchKernelGGL((reduce_kernel<ES, 0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 1: hipLaunchKernelGGL((reduce_kernel<E, 1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<E, 2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<E, 4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<E, 8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: hipLaunchKernelGGL((reduce_kernel<E, 0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
   }
+}
+
+template <int E>
+void launch_reduce_e(int stream_stores, uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
+                     const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
+                     uint32_t chunk_shift, int avg) {
+  if (stream_stores)
+    launch_reduce_k<E, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  else
+    launch_reduce_k<E, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
 }
 }  // namespace
 
-int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
+int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
@@ -875,16 +921,11 @@ int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, ui
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
   const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (elem_bytes == 4) {
-    if (stream_stores)
-      launch_reduce_k<4, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
-    else
-      launch_reduce_k<4, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
-  } else {
-    if (stream_stores)
-      launch_reduce_k<2, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
-    else
-      launch_reduce_k<2, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+  switch (elt) {
+    case kF32: launch_reduce_e<kF32>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case kBF16: launch_reduce_e<kBF16>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case kF16: launch_reduce_e<kF16>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
 }

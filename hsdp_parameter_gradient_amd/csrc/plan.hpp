@@ -88,9 +88,9 @@ extern "C++" {
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
                          uint64_t n_chunks, uint32_t chunk_shift, uint32_t max_grid,
                          int stream_stores, void* stream);
-// Every job of one launch has the same operand count n_src; elem_bytes is 4
-// (fp32) or 2 (bf16).
-int fsdp_launch_reduce(int elem_bytes, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
+// Every job of one launch has the same operand count n_src; elt is the
+// element kind, an FSDP dtype code: FSDP_F32, FSDP_BF16 or FSDP_F16.
+int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores,
                        void* stream);
 }

@@ -6,7 +6,7 @@ of one bucket of parameters with all R simulated ranks resident in HBM:
   ag        [S*I]   AG buffer (parameter dtype); slice s is shard rank s's
                     send buffer
   full[i]           the full parameters written by AG copy-out
-  rs_in[g]  [S*I]   rank g's padded RS input (gradient dtype: fp32 or bf16)
+  rs_in[g]  [S*I]   rank g's padded RS input (gradient dtype: fp32, bf16 or fp16)
   fused[g]  [F]     rank g's 512-byte-aligned fused AR buffer; the RS output
                     of rank g is the view fused[g][off : off + I]
                     (zero-copy, PR #758 write-up of the Hyper
@@ -36,7 +36,7 @@ class FlatBucket:
                  shard_dims: Optional[Sequence[int]] = None):
         """fused_segments: sizes of the segments of the fused buffer (default:
         this bucket's RS output alone); fused_index: which one is this
-        bucket's; grad_dtype: float32 or bfloat16 (the reduce dtype);
+        bucket's; grad_dtype: float32, bfloat16 or float16 (the reduce dtype);
         shard_dims: one shard dim per parameter (default 0)."""
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.R, self.S = int(rank_size), int(shard_size)

@@ -74,8 +74,10 @@ extern "C" {
 #define FSDP_EOVERLAP  5  /* an output overlaps an input or another output */
 
 /* element types: copies take any of them (bits are moved, not converted);
- * reductions take FSDP_F32, or FSDP_BF16 (widened exactly, summed in fp32,
- * rounded once to nearest even at the store; NaN stores as 0x7FC0) */
+ * reductions take FSDP_F32, FSDP_BF16 or FSDP_F16 (16-bit elements are
+ * widened exactly, summed in fp32 and rounded once to nearest even at the
+ * store; a bf16 NaN stores as 0x7FC0, an fp16 NaN as a quiet NaN; fp16
+ * overflows to infinity and keeps its denormals) */
 #define FSDP_F32   0
 #define FSDP_BF16  1
 #define FSDP_F16   2
@@ -197,7 +199,7 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
  * buffer (zero-copy, [HYPER] 2.1).
  *   rs_in   [R] device pointers, S*I elements each
  *   rs_out  [R] device pointers, I elements each
- *   dtype   FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
+ *   dtype   FSDP_F32, FSDP_BF16 or FSDP_F16 (else FSDP_ENOTIMPL)
  */
 int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
                    int32_t dp_size, int32_t op, int32_t dtype,
@@ -213,7 +215,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
  * [FS-MD] 3.3 RS on the shard group).
  *   grads   [R*P] device pointers, grads[g*P + i] holds N0_i * inner_i elements
  *   rs_out  [R] device pointers, I elements each (may be fused-buffer views)
- *   dtype   FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
+ *   dtype   FSDP_F32, FSDP_BF16 or FSDP_F16 (else FSDP_ENOTIMPL)
  */
 int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
                         int32_t dp_size, int32_t op, int32_t dtype,
@@ -227,7 +229,7 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
  *   seg_numel  [n_seg] segment sizes; the buffer size is fsdp_fused_layout's
  *              for the dtype's element size
  *   fused      [R] device pointers, each 512-byte aligned (FSDP_EALIGN)
- *   dtype      FSDP_F32 or FSDP_BF16 (else FSDP_ENOTIMPL)
+ *   dtype      FSDP_F32, FSDP_BF16 or FSDP_F16 (else FSDP_ENOTIMPL)
  */
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size,
                   int32_t shard_size, int32_t dp_size, int32_t op, int32_t dtype,

@@ -39,9 +39,9 @@ Readings where the pages are silent:
 Precision: copies move elements bit for bit (bfloat16 is carried as its
 uint16 bit pattern).  Reductions run in float32 because the pages reduce the
 float32 gradients in their own dtype; the test suite checks them against a
-float64 sum within the float32 rounding bound.  bfloat16 gradients (a
-bfloat16 reduce dtype) are widened exactly, summed in float32 in the same
-order, scaled, and rounded once to nearest even.
+float64 sum within the float32 rounding bound.  bfloat16 or float16
+gradients (a 16-bit reduce dtype) are widened exactly, summed in float32 in
+the same order, scaled, and rounded once to nearest even.
 
 Pins: every function here is pinned by tests that do not re-state its
 formula (worked examples, torch.chunk, brute-force inverse maps, exact
@@ -336,7 +336,8 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def _as_f32(x: np.ndarray) -> np.ndarray:
-    """Gradient values in float32 (bfloat16 is carried as uint16 bits)."""
+    """Gradient values in float32, exactly (bfloat16 is carried as uint16
+    bits; float16 widens exactly)."""
     return bf16_to_f32(x) if x.dtype == np.uint16 else x.astype(np.float32, copy=False)
 
 
@@ -359,9 +360,15 @@ def _scale(acc: np.ndarray, op: str, n: int) -> np.ndarray:
 
 
 def _store(acc: np.ndarray, like: np.ndarray) -> np.ndarray:
-    """The reduced value in the gradients' dtype: float32 as is, bfloat16
-    rounded once, to nearest even (the reduce dtype of [FS-MD] 5.2)."""
-    return f32_to_bf16(acc) if like.dtype == np.uint16 else acc
+    """The reduced value in the gradients' dtype: float32 as is, bfloat16 or
+    float16 rounded once, to nearest even (the reduce dtype of [FS-MD] 5.2;
+    float16 by NumPy's IEEE conversion: ties to even, overflow to infinity,
+    denormals kept)."""
+    if like.dtype == np.uint16:
+        return f32_to_bf16(acc)
+    if like.dtype == np.float16:
+        return acc.astype(np.float16)
+    return acc
 
 
 def shard_groups(rank_size: int, shard_size: int) -> List[List[int]]:
@@ -414,8 +421,8 @@ def rs_copy_reduce(grads: Sequence[Sequence[np.ndarray]], lay: BucketLayout, ran
                    op: str) -> List[np.ndarray]:
     """RS copy-in and RS as one step: by definition the RS of the RS inputs
     (the fused form only skips materialising them)."""
-    bf16 = rank_size > 0 and len(lay.shapes) > 0 and grads[0][0].dtype == np.uint16
-    dtype = np.uint16 if bf16 else np.float32
+    first = grads[0][0].dtype if rank_size > 0 and len(lay.shapes) > 0 else np.dtype(np.float32)
+    dtype = first if first in (np.uint16, np.float16) else np.float32
     rs_in = [rs_copy_in(grads[g], lay, dtype) for g in range(rank_size)]
     return rs_reduce(rs_in, lay.I, rank_size, lay.S, op)
 

@@ -61,9 +61,18 @@ def np_bits(a: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(a).reshape(-1)
     if a.dtype == np.float32:
         return a.view(np.int32)
-    if a.dtype == np.uint16:
+    if a.dtype in (np.uint16, np.float16):
         return a.view(np.int16)
     raise TypeError(a.dtype)
+
+
+def to_oracle_values(t: torch.Tensor) -> np.ndarray:
+    """Host numpy form of reduction operands: float32, bfloat16 as uint16
+    bits (the oracle's bf16 form), float16 as numpy float16."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float16:
+        return t.numpy()
+    return to_oracle(t)
 
 
 def to_oracle(t: torch.Tensor) -> np.ndarray:

@@ -176,26 +176,26 @@ def test_device_entry_points_reject_bad_arguments(L):
     grads = _ptrs([BASE + 0x100000 * (k + 1) for k in range(6 * P)])
     rs_in = _ptrs([BASE + 0x10000000 * (g + 1) for g in range(6)])
     assert L.fsdp_rs_copy_in(b.ref, 6, S, 0, grads, rs_in, None) == 1
-    # rs_reduce: dp_size inconsistent, op unknown, dtype not fp32, output aliasing input
+    # rs_reduce: dp_size inconsistent, op unknown, dtype not a reduction dtype, output aliasing input
     rs8 = _ptrs([BASE + 0x10000000 * (g + 1) for g in range(8)])
     out8 = _ptrs([BASE + 0x1000000 * (g + 1) for g in range(8)])
     assert L.fsdp_rs_reduce(b.ref, 8, S, 3, 0, 0, rs8, out8, None) == 1
     assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 9, 0, rs8, out8, None) == 1
-    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 2, rs8, out8, None) == 2
+    assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 5, rs8, out8, None) == 2
     alias = _ptrs([BASE + 0x10000000 * (g + 1) + 4 * lay.I for g in range(8)])
     assert L.fsdp_rs_reduce(b.ref, 8, S, 2, 0, 0, rs8, alias, None) == 5
-    # rs_copy_reduce: fp16 is not a reduction dtype; an output inside a gradient
+    # rs_copy_reduce: an unknown dtype; an output inside a gradient
     g8 = _ptrs([BASE + 0x100000 * (k + 1) for k in range(8 * P)])
-    assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 2, g8, out8, None) == 2
+    assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 5, g8, out8, None) == 2
     inside = _ptrs([BASE + 0x100000 + 8] + [BASE + 0x10000000 * (g + 1) for g in range(1, 8)])
     assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 0, g8, inside, None) == 5
     assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 3, 0, 0, g8, out8, None) == 1
-    # fused_ar: base not 512-byte aligned, dtype not fp32
+    # fused_ar: base not 512-byte aligned, an unknown dtype
     segs = (ctypes.c_int64 * 2)(100, 3)
     f8 = _ptrs([BASE + 0x100000 * g + 256 for g in range(8)])
     assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, f8, None) == 3
     f8a = _ptrs([BASE + 0x100000 * g for g in range(8)])
-    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 2, f8a, None) == 2
+    assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 5, f8a, None) == 2
     ovl = _ptrs([BASE + 512 * g for g in range(8)])
     assert L.fsdp_fused_ar(2, segs, 8, 4, 2, 1, 0, ovl, None) == 5
 

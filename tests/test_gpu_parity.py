@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import Guarded, bits, first_mismatch, note, np_bits, require_gpu, to_oracle
+from gpu_util import Guarded, bits, first_mismatch, note, np_bits, require_gpu, to_oracle, to_oracle_values
 
 hp = pytest.importorskip("hsdp_parameter_gradient_amd")
 
@@ -340,7 +340,8 @@ def test_hsdp_block_end_to_end_flat_bucket():
 
 
 @pytest.mark.parametrize("grad_dtype,on_dim_1", [(torch.bfloat16, False), (torch.float32, True),
-                                                (torch.bfloat16, True)])
+                                                (torch.bfloat16, True), (torch.float16, False),
+                                                (torch.float16, True)])
 def test_flat_bucket_bf16_grads_and_shard_dim_1(grad_dtype, on_dim_1):
     """FlatBucket with bfloat16 gradients and/or its 2-D parameters sharded
     on dim 1 (the benchmark's variants), on a scaled-down HSDP block: the
@@ -356,7 +357,7 @@ def test_flat_bucket_bf16_grads_and_shard_dim_1(grad_dtype, on_dim_1):
     fb.bind(fb.shard_views([p.cuda() for p in params]),
             [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)])
     lay = O.bucket_layout(w.param_shapes, S, shard_dims=dims)
-    gnp = [[to_oracle(t) for t in g_cpu[g]] for g in range(R)]
+    gnp = [[to_oracle_values(t) for t in g_cpu[g]] for g in range(R)]
     rs_o = O.rs_copy_reduce(gnp, lay, R, O.AVG)
     _, F = O.fused_layout([lay.I], grad_dtype.itemsize)
     fused_o = O.fused_ar([np.concatenate([rs_o[g], np.zeros(F - lay.I, rs_o[g].dtype)]) for g in range(R)],
@@ -383,7 +384,7 @@ def run_rs_copy_reduce(name, shapes, R, S, grads, ops=(O.SUM, O.AVG), out_offset
     note(f"[parity] rs_copy_reduce {name}: R={R} S={S} P={len(shapes)} dtype={dtype} out_offset={out_offset}")
     lay = O.bucket_layout(shapes, S)
     P = len(shapes)
-    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
+    gnp = [[to_oracle_values(g) for g in grads[r]] for r in range(R)]
     dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
     for op in ops:
         want = O.rs_copy_reduce(gnp, lay, R, op)
@@ -428,24 +429,28 @@ def test_rs_copy_reduce_random_buckets():
         run_rs_copy_reduce(w.name, shapes, S * D, S, W.grads(w, dtype=dtype), out_offset=int(rng.integers(0, 5)))
 
 
+NP16 = {torch.bfloat16: np.uint16, torch.float16: np.float16}
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("R,S", [(8, 4), (16, 8), (6, 3), (4, 1)])
-def test_bf16_rs_copy_in_and_reduce(R, S):
-    """bf16 gradients: RS copy-in (a bit copy), RS (fp32 sum, one rounding)
-    and the fused form agree with the oracle bit for bit."""
+def test_16bit_rs_copy_in_and_reduce(R, S, dtype):
+    """bf16 / fp16 gradients: RS copy-in (a bit copy), RS (fp32 sum, one
+    rounding) and the fused form agree with the oracle bit for bit."""
     shapes = [(1001, 7), (17,), (3, 3, 3), (0,), (40001,), (5, 64)]
-    w = W.Workload(f"bf16_rs_{R}_{S}", 21, R, S, tuple(shapes), torch.bfloat16, ("normal", 1.0),
+    w = W.Workload(f"{str(dtype)[6:]}_rs_{R}_{S}", 21, R, S, tuple(shapes), dtype, ("normal", 1.0),
                    ("normal", 1e-3), ("sum", "avg"), W.ALL_STEPS)
-    grads = W.grads(w, dtype=torch.bfloat16)
-    note(f"[parity] bf16 RS R={R} S={S}")
+    grads = W.grads(w, dtype=dtype)
+    note(f"[parity] {dtype} RS R={R} S={S}")
     lay = O.bucket_layout(shapes, S)
     P = len(shapes)
-    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
-    rs_o = [O.rs_copy_in(gnp[g], lay, np.uint16) for g in range(R)]
+    gnp = [[to_oracle_values(g) for g in grads[r]] for r in range(R)]
+    rs_o = [O.rs_copy_in(gnp[g], lay, NP16[dtype]) for g in range(R)]
     dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
-    rs_in = [Guarded(S * lay.I, torch.bfloat16, 1) for _ in range(R)]
+    rs_in = [Guarded(S * lay.I, dtype, 1) for _ in range(R)]
     hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in])
     for op in (O.SUM, O.AVG):
-        out = [Guarded(lay.I, torch.bfloat16, g % 4) for g in range(R)]
+        out = [Guarded(lay.I, dtype, g % 4) for g in range(R)]
         hp.fsdp_rs_reduce(shapes, R, S, R // S, op, [b.t for b in rs_in], [o.t for o in out])
         torch.cuda.synchronize()
         want = O.rs_reduce(rs_o, lay.I, R, S, op)
@@ -453,33 +458,35 @@ def test_bf16_rs_copy_in_and_reduce(R, S):
             assert rs_in[g].guards_intact() and out[g].guards_intact()
             assert first_mismatch(bits(rs_in[g].t), np_bits(rs_o[g])) == ""
             m = first_mismatch(bits(out[g].t), np_bits(want[g]))
-            assert m == "", f"bf16 rs_reduce {op} rank {g}: {m}"
+            assert m == "", f"{dtype} rs_reduce {op} rank {g}: {m}"
     run_rs_copy_reduce(w.name, shapes, R, S, grads)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("op", [O.AVG, O.SUM])
-def test_bf16_fused_ar_pure_tp(op):
-    """bf16 fused AR over 300 segments (512-byte alignment = 256 elements)."""
+def test_16bit_fused_ar_pure_tp(op, dtype):
+    """bf16 / fp16 fused AR over 300 segments (512-byte alignment = 256
+    elements)."""
     sizes = [s[0] for s in W.PURE_TP.param_shapes[:300]]
-    w = W.scaled(W.PURE_TP, [(n,) for n in sizes], name="pure_tp_bf16")
+    w = W.scaled(W.PURE_TP, [(n,) for n in sizes], name=f"pure_tp_{str(dtype)[6:]}")
     R, S = w.rank_size, w.shard_size
-    note(f"[parity] bf16 fused_ar {op}: {len(sizes)} segments")
-    g_cpu = W.grads(w, dtype=torch.bfloat16)
+    note(f"[parity] {dtype} fused_ar {op}: {len(sizes)} segments")
+    g_cpu = W.grads(w, dtype=dtype)
     offs, F = O.fused_layout(sizes, elem_bytes=2)
     fused_o = []
     for g in range(R):
-        buf = np.zeros(F, np.uint16)
+        buf = np.zeros(F, NP16[dtype])
         for o, t in zip(offs, g_cpu[g]):
-            buf[o:o + t.numel()] = to_oracle(t)
+            buf[o:o + t.numel()] = to_oracle_values(t)
         fused_o.append(buf)
     want = O.fused_ar(fused_o, R, S, op)
     assert hp.fsdp_fused_layout(sizes, 2) == (offs, F)
-    fused = [torch.from_numpy(f.view(np.int16).copy()).view(torch.bfloat16).cuda() for f in fused_o]
+    fused = [torch.from_numpy(f.view(np.int16).copy()).view(dtype).cuda() for f in fused_o]
     hp.fsdp_fused_ar(sizes, R, S, R // S, op, fused)
     torch.cuda.synchronize()
     for g in range(R):
         m = first_mismatch(bits(fused[g]), np_bits(want[g]))
-        assert m == "", f"bf16 fused_ar rank {g}: {m}"
+        assert m == "", f"{dtype} fused_ar rank {g}: {m}"
 
 
 def test_zero_copy_ag_views_one_parameter_buckets():
@@ -640,28 +647,34 @@ SPECIAL_F32 = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 3.0, np.inf, -np.inf, np.nan,
                         3.4028235e38, -3.4028235e38, 1e38, 2.0 ** -126, 7.0, -2.5], dtype=np.float32)
 
 
+# fp16's own edges: its largest finite value, denormals, the smallest
+# normal, values whose sums overflow
+SPECIAL_F16 = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 3.0, np.inf, -np.inf, np.nan, 65504.0, -65504.0, 6e-8, -3e-8,
+                        6.1035156e-05, 3e4, 7.0, -2.5, 1e-3], dtype=np.float32)
+
+
 def _special(n, rng, dtype):
-    v = SPECIAL_F32[rng.integers(0, len(SPECIAL_F32), n)]
-    t = torch.from_numpy(v)
-    return t if dtype == torch.float32 else t.to(torch.bfloat16)
+    pool = SPECIAL_F16 if dtype == torch.float16 else SPECIAL_F32
+    t = torch.from_numpy(pool[rng.integers(0, len(pool), n)])
+    return t if dtype == torch.float32 else t.to(dtype)
 
 
 def _same_up_to_nan_payload(got_t, want_np):
-    """Bit-equal everywhere the oracle is not NaN; NaN where it is (fp32 NaN
-    payloads are not part of the result; bf16 NaN is one pattern, 0x7FC0,
-    on both sides and compared bit for bit)."""
+    """Bit-equal everywhere the oracle is not NaN; NaN where it is (fp32 and
+    fp16 NaN payloads are not part of the result; bf16 NaN is one pattern,
+    0x7FC0, on both sides and compared bit for bit)."""
     got = bits(got_t)
     want = np_bits(want_np)
-    if want_np.dtype == np.float32:
+    if want_np.dtype in (np.float32, np.float16):
         nan = np.isnan(want_np.reshape(-1))
-        g = got_t.detach().cpu().numpy().reshape(-1)
+        g = got_t.detach().cpu().float().numpy().reshape(-1)
         if not np.array_equal(np.isnan(g), nan):
             return "NaN positions differ"
         got, want = got[~nan], want[~nan]
     return first_mismatch(got, want)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("R,S", [(8, 4), (6, 3), (8, 8), (6, 2)])
 def test_special_values_rs_and_fused_ar(dtype, R, S):
     """Signed zeros, infinities, NaN, denormals and values that overflow when
@@ -670,13 +683,13 @@ def test_special_values_rs_and_fused_ar(dtype, R, S):
     ascending order, IEEE fp32 with denormals kept, and one rounding to
     bf16."""
     note(f"[parity] special values dtype={dtype} R={R} S={S}")
-    rng = np.random.default_rng(R * 10 + S + (dtype == torch.bfloat16))
+    rng = np.random.default_rng(R * 10 + S + (dtype == torch.bfloat16) + 2 * (dtype == torch.float16))
     shapes = [(1027, 3), (5,), (2049,)]
     lay = O.bucket_layout(shapes, S)
     I, P, D = lay.I, len(shapes), R // S
     grads = [[_special(int(np.prod(sh)), rng, dtype).reshape(sh) for sh in shapes] for _ in range(R)]
-    gnp = [[to_oracle(t) for t in grads[g]] for g in range(R)]
-    np_dt = np.float32 if dtype == torch.float32 else np.uint16
+    gnp = [[to_oracle_values(t) for t in grads[g]] for g in range(R)]
+    np_dt = np.float32 if dtype == torch.float32 else NP16[dtype]
     dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
     rs_in = [torch.empty(S * I, dtype=dtype, device="cuda") for _ in range(R)]
     hp.fsdp_rs_copy_in(shapes, R, S, dgrads, rs_in)
@@ -699,7 +712,7 @@ def test_special_values_rs_and_fused_ar(dtype, R, S):
                 for g in range(R):
                     f = np.zeros(F, np_dt)
                     f[offs[0]:offs[0] + I] = want[g]
-                    f[offs[1]:offs[1] + 300] = to_oracle(_special(300, rng, dtype))
+                    f[offs[1]:offs[1] + 300] = to_oracle_values(_special(300, rng, dtype))
                     fused_np.append(f)
                 fused = [torch.from_numpy(f.view(np.int16) if np_dt == np.uint16 else f).cuda() for f in fused_np]
                 if dtype == torch.bfloat16:

@@ -339,6 +339,53 @@ def test_bf16_reductions_round_once():
     assert pin_bf16_round_once() == []
 
 
+def pin_f16_round_once():
+    """fp16 RS = round_to_fp16(float32 ordered sum of the widened operands),
+    checked against torch's float32 arithmetic and its fp16 rounding, with
+    sums that overflow fp16 and results in its denormal range."""
+    bad = []
+    R, S = 8, 4
+    shapes = [(33, 7), (10,)]
+    lay = O.bucket_layout(shapes, S)
+    gen = torch.Generator().manual_seed(6)
+    scale = [1.0, 3e4, 1e-5]  # ordinary, overflowing, denormal results
+    gi = [[(torch.randn(sh, generator=gen) * scale[(g + i) % 3]).half() for i, sh in enumerate(shapes)]
+          for g in range(R)]
+    rs_in = [O.rs_copy_in([t.numpy() for t in gi[g]], lay, np.float16) for g in range(R)]
+    with np.errstate(all="ignore"):
+        for op in (O.SUM, O.AVG):
+            outs = O.rs_reduce(rs_in, lay.I, R, S, op)
+            for g in range(R):
+                d, s = divmod(g, S)
+                acc = torch.from_numpy(rs_in[d * S][s * lay.I:(s + 1) * lay.I]).float()
+                for t in range(1, S):
+                    acc = acc + torch.from_numpy(rs_in[d * S + t][s * lay.I:(s + 1) * lay.I]).float()
+                if op == O.AVG:
+                    acc = acc / S
+                want = acc.half().numpy()
+                if outs[g].dtype != np.float16 or not np.array_equal(outs[g].view(np.uint16), want.view(np.uint16)):
+                    bad.append(f"fp16 RS {op} rank {g}")
+    return bad
+
+
+def test_f16_reductions_round_once():
+    assert pin_f16_round_once() == []
+
+
+def test_f16_conversion_matches_torch():
+    x = _bf16_special_values()
+    x = np.concatenate([x, np.array([65504.0, 65519.99, 65520.0, 7e4, -7e4, 6e-8, 3e-8, 2.98e-8], np.float32)])
+    # exact fp16 ties in the normal range: 13 dropped bits equal to 0x1000
+    top = np.random.default_rng(3).integers(0, 0x0F00, size=4000).astype(np.uint32)
+    x = np.concatenate([x, (((top << 13) | 0x1000) + 0x38000000).astype(np.uint32).view(np.float32)])
+    with np.errstate(all="ignore"):
+        got = O.fsdp_oracle._store(x, np.zeros(1, np.float16))
+    want = torch.from_numpy(x.copy()).half().numpy()
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan].view(np.uint16), want[~nan].view(np.uint16))
+    assert np.all(np.isnan(got[nan]))
+
+
 def pin_avg_correctly_rounded():
     """AVG over a group of 3 or 6 (not a power of two) on integer-valued
     gradients: the sum is exact, so the result must be the exact quotient
@@ -540,6 +587,27 @@ def _round_each_add(operands):
     return acc
 
 
+def _f16_round_each_add(operands):
+    f16 = operands[0].dtype == np.float16
+    acc = np.array(F._as_f32(operands[0]), dtype=np.float32, copy=True)
+    for x in operands[1:]:
+        acc = acc + F._as_f32(x)
+        if f16:
+            acc = acc.astype(np.float16).astype(np.float32)
+    return acc
+
+
+_ORIG_STORE = F._store
+
+
+def _f16_truncating_store(acc, like):
+    if like.dtype == np.float16:
+        # drop the 13 low mantissa bits (round toward zero in magnitude)
+        b = np.asarray(acc, np.float32).view(np.uint32) & np.uint32(0xFFFFE000)
+        return b.view(np.float32).astype(np.float16)
+    return _ORIG_STORE(acc, like)
+
+
 def _chunk_on_dim0(x, lay, i, s):
     a, n = lay.row_off[i][s], lay.row_len[i][s]
     return x[a:a + n]
@@ -578,6 +646,8 @@ MUTANTS = {
     "chunk_on_dim0": ("_chunk", _chunk_on_dim0),
     "fused_align_256": ("fused_layout", _fused_align_256),
     "rs_padding_not_zero": ("rs_copy_in", _rs_copy_in_pad_one),
+    "f16_round_each_add": ("_ordered_sum", _f16_round_each_add),
+    "f16_truncating_store": ("_store", _f16_truncating_store),
 }
 
 
@@ -607,6 +677,7 @@ def _all_pins(golden):
         lambda: _groups_pin(golden),
         lambda: [] if _bf16_pin() else ["bf16 rounding"],
         pin_bf16_round_once,
+        pin_f16_round_once,
         pin_avg_correctly_rounded,
         pin_nonzero_dims,
         lambda: pin_fused_layout(golden),
