@@ -130,25 +130,30 @@ def test_full_size_sampled(wname):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wname", ["hsdp_block_h1024_r8_s4_d2", "llama7b_4layer_r8_s8"])
-def test_full_size_shard_dim_1(wname):
-    """The 2-D weights sharded on dim 1 (strided blocks), at full size, in
-    the benchmark's configuration, checked on every element by properties
-    that hold at any size: each AG slice region is the dense dim-1 chunk of
-    its parameter, copy-out restores the parameters bit for bit, each RS
-    input region is the dense chunk of the gradient, and with integer-valued
-    gradients (every sum exact in any order) the RS output is the chunk of
-    the group's sum divided by S, and the fused AR output that divided by D."""
+@pytest.mark.parametrize("wname,grad_dtype,on_dim_1", [
+    ("hsdp_block_h1024_r8_s4_d2", torch.float32, True), ("llama7b_4layer_r8_s8", torch.float32, True),
+    ("hsdp_block_h1024_r8_s4_d2", torch.bfloat16, False), ("hsdp_block_h1024_r8_s4_d2", torch.float16, False),
+    ("hsdp_block_h1024_r8_s4_d2", torch.bfloat16, True)])
+def test_full_size_properties(wname, grad_dtype, on_dim_1):
+    """The benchmark's variants at full size (the 2-D weights sharded on dim
+    1 as strided blocks; bf16 and fp16 gradients), in the benchmark's
+    configuration, checked on every element by properties that hold at any
+    size: each AG slice region is the dense chunk of its parameter, copy-out
+    restores the parameters bit for bit, each RS input region is the dense
+    chunk of the gradient, and with integer-valued gradients (every sum and
+    quotient exact in the gradient dtype, whatever the order) the RS output
+    is the chunk of the group's sum divided by S, and the fused AR output
+    that divided by D."""
     w = W.WORKLOADS[wname]
     R, S, D = w.rank_size, w.shard_size, w.dp_size
     P = len(w.param_shapes)
-    dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
+    dims = [1 if on_dim_1 and len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
     lay = O.bucket_layout(w.param_shapes, S, shard_dims=dims)
     I = lay.I
-    note(f"[fullsize] {w.name} shard dims {sorted(set(dims))}: P={P} I={I} R={R} S={S}")
+    note(f"[fullsize] {w.name} {grad_dtype} shard dims {sorted(set(dims))}: P={P} I={I} R={R} S={S}")
     params = W.params(w, device="cuda")
-    grads = W.integer_grads(w, device="cuda")
-    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG, shard_dims=dims)
+    grads = [[t.to(grad_dtype) for t in row] for row in W.integer_grads(w, device="cuda")]
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG, shard_dims=dims, grad_dtype=grad_dtype)
     fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
     fb.step()
     torch.cuda.synchronize()
@@ -191,8 +196,9 @@ def test_full_size_shard_dim_1(wname):
         v.fill_(float("nan"))
     fb.step(fused_rs=True)
     torch.cuda.synchronize()
+    gi = torch.int32 if grad_dtype == torch.float32 else torch.int16
     for g in range(R):
-        assert torch.equal(fb.fused[g].view(torch.int32), before[g].view(torch.int32)), f"fused RS rank {g}"
+        assert torch.equal(fb.fused[g].view(gi), before[g].view(gi)), f"fused RS rank {g}"
     del fb, params, grads, before
     torch.cuda.empty_cache()
 
