@@ -767,3 +767,38 @@ def test_concurrent_calls_from_threads_on_their_own_streams():
             assert np.array_equal(bits(fb.full[i]), bits(p.reshape(-1)))
         for g in range(R):
             assert first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g])) == "", f"rank {g}"
+
+
+def test_many_passes_stay_bit_identical():
+    """600 passes of the HSDP block (unfused and fused RS alternating in
+    runs of 100, on the current stream and a side stream) leave every
+    output bit-identical to the first pass's, which matches the oracle."""
+    w = W.HSDP_BLOCK
+    R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+    note(f"[parity] {w.name}: 600 passes")
+    params, g_cpu = W.params(w), W.grads(w)
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG)
+    fb.bind(fb.shard_views([p.cuda() for p in params]),
+            [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)])
+    fb.step()
+    torch.cuda.synchronize()
+    gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
+    _, fused_o, _, _ = O.reduce_grads_fused(gnp, [list(w.param_shapes)], R, S, O.AVG)
+    for g in range(R):
+        assert first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g])) == "", f"first pass rank {g}"
+    first_full = [f.clone() for f in fb.full]
+    first_fused = [f.clone() for f in fb.fused]
+    side = torch.cuda.Stream()
+    for run in range(6):
+        stream = side if run % 2 else None
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+        for _ in range(100):
+            fb.step(stream, fused_rs=bool(run % 3 == 1))
+        if stream is not None:
+            torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        for a, b in zip(fb.full, first_full):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"full params after run {run}"
+        for g, (a, b) in enumerate(zip(fb.fused, first_fused)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"fused rank {g} after run {run}"
