@@ -33,6 +33,16 @@
 #include "plan.hpp"
 #include "tuning.hpp"
 
+#ifdef FSDP_TABLE_HOOK
+// Test builds only (the host sanitizer driver): every planned table is
+// handed to this function before its upload (reduce: 0 copy / 1 reduce;
+// elt: element bytes of a copy, dtype code of a reduction), so the tables
+// the planner really builds can be checked against an emulation of the
+// kernels.
+void fsdp_table_hook(int reduce, int elt, uint32_t n_items, uint64_t n_chunks, uint32_t shift,
+                     const std::vector<uint8_t>& table);
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -409,6 +419,9 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
   table.reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
   append(table, begin.data(), begin.size());
   append(table, segs.data(), segs.size());
+#ifdef FSDP_TABLE_HOOK
+  fsdp_table_hook(0, es, (uint32_t)segs.size(), n, tu.copy_shift, table);
+#endif
   int rc = upload(table, p);
   if (rc) return rc;
   p->launch = true;
@@ -441,6 +454,9 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
   append(table, begin.data(), begin.size());
   append(table, jobs.data(), jobs.size());
   append(table, ptrs.data(), ptrs.size());
+#ifdef FSDP_TABLE_HOOK
+  fsdp_table_hook(1, dtype, (uint32_t)jobs.size(), n, tu.reduce_shift, table);
+#endif
   int rc = upload(table, p);
   if (rc) return rc;
   p->launch = true;

@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <utility>
 #include <vector>
 
 #include "fsdp_flat.h"
@@ -28,9 +29,49 @@ int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t,
   std::abort();
 }
 
+// With FSDP_TABLE_HOOK, every planned table is appended to the file named
+// by FSDP_DUMP_TABLES (if set): a 32-byte header (reduce, elt, n_items,
+// shift, n_chunks, table bytes) and the table itself.
+void fsdp_table_hook(int reduce, int elt, uint32_t n_items, uint64_t n_chunks, uint32_t shift,
+                     const std::vector<uint8_t>& table) {
+  const char* path = std::getenv("FSDP_DUMP_TABLES");
+  if (!path) return;
+  FILE* f = std::fopen(path, "ab");
+  if (!f) return;
+  const uint32_t h32[4] = {(uint32_t)reduce, (uint32_t)elt, n_items, shift};
+  const uint64_t h64[2] = {n_chunks, (uint64_t)table.size()};
+  std::fwrite(h32, sizeof h32, 1, f);
+  std::fwrite(h64, sizeof h64, 1, f);
+  std::fwrite(table.data(), 1, table.size(), f);
+  std::fclose(f);
+}
+
+// Before each device call the driver appends the call's output and input
+// byte spans (a record with reduce = 2), so each dumped table can be
+// checked against what its call must write and may read.
+void dump_io(const std::vector<std::pair<uint64_t, uint64_t>>& outs,
+             const std::vector<std::pair<uint64_t, uint64_t>>& ins) {
+  const char* path = std::getenv("FSDP_DUMP_TABLES");
+  if (!path) return;
+  FILE* f = std::fopen(path, "ab");
+  if (!f) return;
+  std::vector<uint64_t> body;
+  for (auto& o : outs) body.insert(body.end(), {o.first, o.second});
+  for (auto& i : ins) body.insert(body.end(), {i.first, i.second});
+  const uint32_t h32[4] = {2u, 0u, (uint32_t)outs.size(), (uint32_t)ins.size()};
+  const uint64_t h64[2] = {0, (uint64_t)(body.size() * 8)};
+  std::fwrite(h32, sizeof h32, 1, f);
+  std::fwrite(h64, sizeof h64, 1, f);
+  std::fwrite(body.data(), 8, body.size(), f);
+  std::fclose(f);
+}
+
 namespace {
 
 int failures = 0;
+
+using Spans = std::vector<std::pair<uint64_t, uint64_t>>;
+uint64_t A(const void* p) { return reinterpret_cast<uint64_t>(p); }
 
 void expect(int got, int want, const char* what, int line) {
   if (got != want) {
@@ -78,7 +119,7 @@ void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
   }
   std::vector<int64_t> row_len((size_t)P * S);
   fsdp_bucket_layout(&b, S, nullptr, nullptr, nullptr, nullptr, row_len.data());
-  const int32_t dtype = es == 4 ? FSDP_F32 : FSDP_BF16;
+  const int32_t dtype = es == 4 ? FSDP_F32 : misalign ? FSDP_F16 : FSDP_BF16;
   const int32_t D = R / S;
   Fake f;
   const uint64_t off = misalign ? (uint64_t)es : 0;
@@ -92,29 +133,51 @@ void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
   const int want = work ? FSDP_EHIP : FSDP_OK;
 
   std::vector<const void*> shards;
+  Spans shard_sp;
   for (int32_t s = 0; s < S; ++s)
-    for (int32_t i = 0; i < P; ++i) shards.push_back(f.get((uint64_t)chunk_bytes(i, s), off));
+    for (int32_t i = 0; i < P; ++i) {
+      const uint64_t nb = (uint64_t)chunk_bytes(i, s);
+      shards.push_back(f.get(nb, off));
+      shard_sp.push_back({A(shards.back()), nb});
+    }
   void* ag = f.get((uint64_t)(S * I * es), off);
+  const Spans ag_sp = {{A(ag), (uint64_t)(S * I * es)}};
+  dump_io(ag_sp, shard_sp);
   EXPECT(fsdp_ag_copy_in(&b, S, dtype, shards.data(), ag, nullptr), want);
   std::vector<void*> full;
+  Spans full_sp;
   bool any_full = false;
   for (int32_t i = 0; i < P; ++i) {
-    full.push_back(f.get((uint64_t)(numel(c.shapes[(size_t)i]) * es), off));
-    any_full = any_full || numel(c.shapes[(size_t)i]) > 0;
+    const uint64_t nb = (uint64_t)(numel(c.shapes[(size_t)i]) * es);
+    full.push_back(f.get(nb, off));
+    full_sp.push_back({A(full.back()), nb});
+    any_full = any_full || nb > 0;
   }
+  dump_io(full_sp, ag_sp);
   EXPECT(fsdp_ag_copy_out(&b, S, dtype, ag, full.data(), nullptr), any_full ? FSDP_EHIP : FSDP_OK);
 
   std::vector<const void*> grads;
+  Spans grad_sp;
   for (int32_t g = 0; g < R; ++g)
-    for (int32_t i = 0; i < P; ++i) grads.push_back(f.get((uint64_t)(numel(c.shapes[(size_t)i]) * es), off));
+    for (int32_t i = 0; i < P; ++i) {
+      const uint64_t nb = (uint64_t)(numel(c.shapes[(size_t)i]) * es);
+      grads.push_back(f.get(nb, off));
+      grad_sp.push_back({A(grads.back()), nb});
+    }
   std::vector<void*> rs_in, rs_out;
+  Spans in_sp, out_sp;
   for (int32_t g = 0; g < R; ++g) {
     rs_in.push_back(f.get((uint64_t)(S * I * es), off));
     rs_out.push_back(f.get((uint64_t)(I * es), off));
+    in_sp.push_back({A(rs_in.back()), (uint64_t)(S * I * es)});
+    out_sp.push_back({A(rs_out.back()), (uint64_t)(I * es)});
   }
+  dump_io(in_sp, grad_sp);
   EXPECT(fsdp_rs_copy_in(&b, R, S, dtype, grads.data(), rs_in.data(), nullptr), want);
   const void* const* rs_in_c = rs_in.data();
+  dump_io(out_sp, in_sp);
   EXPECT(fsdp_rs_reduce(&b, R, S, D, FSDP_AVG, dtype, rs_in_c, rs_out.data(), nullptr), want);
+  dump_io(out_sp, grad_sp);
   EXPECT(fsdp_rs_copy_reduce(&b, R, S, D, FSDP_SUM, dtype, grads.data(), rs_out.data(), nullptr), want);
 
   // fused buffers: this bucket's RS output plus two more segments
@@ -122,7 +185,12 @@ void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
   int64_t F = 0;
   fsdp_fused_layout(3, segs, es, nullptr, &F);
   std::vector<void*> fused;
-  for (int32_t g = 0; g < R; ++g) fused.push_back(f.get((uint64_t)(F * es)));
+  Spans fused_sp;
+  for (int32_t g = 0; g < R; ++g) {
+    fused.push_back(f.get((uint64_t)(F * es)));
+    fused_sp.push_back({A(fused.back()), (uint64_t)(F * es)});
+  }
+  dump_io(fused_sp, fused_sp);
   EXPECT(fsdp_fused_ar(3, segs, R, S, D, FSDP_AVG, dtype, fused.data(), nullptr), D > 1 ? FSDP_EHIP : FSDP_OK);
 
   // argument errors, caught before planning

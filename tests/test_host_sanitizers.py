@@ -1,37 +1,141 @@
-"""The host planner under AddressSanitizer and UndefinedBehaviorSanitizer.
+"""The host planner under AddressSanitizer and UndefinedBehaviorSanitizer,
+and the tables it really builds against the CPU emulation of the kernels.
 
 fsdp_flat.cpp (validation, layout, descriptor-table construction, plan
-cache) is built with g++ -fsanitize=address,undefined, without the device
-kernels, and driven by tests/host_sanitizer_driver.cpp over ragged, empty,
-non-zero-dim and misaligned buckets.  With no GPU visible every call plans
-in full and then fails its upload (FSDP_EHIP), so any out-of-bounds access,
-overflow or leak in the planner is reported.  CPU only.
+cache) is built with g++ -fsanitize=address,undefined and the table hook,
+without the device kernels, and driven by tests/host_sanitizer_driver.cpp
+over ragged, empty, non-zero-dim and misaligned buckets.  With no GPU
+visible every call plans in full and then fails its upload (FSDP_EHIP), so
+any out-of-bounds access, overflow or leak in the planner is reported; the
+hook dumps every planned table, and the kernels' indexing (emulated in
+tests/test_kernel_indexing.py) is run over each one: every destination byte
+written exactly once with the right source, nothing outside, every read
+inside its source envelope.  CPU only.
 """
 
 import os
 import shutil
+import struct
 import subprocess
 
+import numpy as np
 import pytest
+
+import test_kernel_indexing as KI
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc")
 
 
-def test_planner_under_asan_and_ubsan(tmp_path):
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
     gxx = shutil.which("g++")
     if not gxx or not os.path.exists("/opt/rocm/lib/libamdhip64.so"):
         pytest.skip("needs g++ and the ROCm runtime library")
-    exe = str(tmp_path / "host_sanitizer_driver")
+    exe = str(tmp_path_factory.mktemp("drv") / "host_sanitizer_driver")
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
-           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-DFSDP_TABLE_HOOK", "-I/opt/rocm/include",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "fsdp_flat.cpp"), os.path.join(ROOT, "tests", "host_sanitizer_driver.cpp"),
            "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
+    return exe
+
+
+def _run(exe, extra_env=None):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", HIP_VISIBLE_DEVICES="")
+    env.update(extra_env or {})
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
     if r.stdout.strip() == "skip":
         pytest.skip("a GPU is visible: the driver needs the uploads to fail")
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout + r.stderr)[-4000:]
+
+
+def test_planner_under_asan_and_ubsan(driver):
+    _run(driver)
+
+
+def _records(path):
+    data = open(path, "rb").read()
+    pos = 0
+    while pos < len(data):
+        kind, elt, a, b = struct.unpack_from("<4I", data, pos)
+        n_chunks, nbytes = struct.unpack_from("<2Q", data, pos + 16)
+        pos += 32
+        yield kind, elt, a, b, n_chunks, data[pos:pos + nbytes]
+        pos += nbytes
+
+
+def _merge(iv):
+    out = []
+    for a, b in sorted(x for x in iv if x[0] < x[1]):
+        if out and a <= out[-1][1]:
+            out[-1] = (out[-1][0], max(out[-1][1], b))
+        else:
+            out.append((a, b))
+    return out
+
+
+def _inside(iv, allowed):
+    """Every interval of iv lies inside one interval of allowed (merged)."""
+    import bisect
+    starts = [a for a, _ in allowed]
+    for a, b in iv:
+        k = bisect.bisect_right(starts, a) - 1
+        if k < 0 or b > allowed[k][1]:
+            return (a, b)
+    return None
+
+
+def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path):
+    """Every table the planner builds, run through the emulated kernels,
+    writes exactly its call's output buffers (every byte once) and reads
+    only inside the aligned envelopes of its call's inputs."""
+    dump = str(tmp_path / "tables.bin")
+    _run(driver, {"FSDP_DUMP_TABLES": dump})
+    counts = {0: 0, 1: 0, "blocks": 0}
+    outs = ins = None
+    for kind, elt, a, b, n_chunks, blob in _records(dump):
+        words = np.frombuffer(blob, dtype=np.uint64)
+        if kind == 2:  # the next call's output and input spans
+            sp = [(int(words[2 * k]), int(words[2 * k]) + int(words[2 * k + 1])) for k in range(a + b)]
+            outs, ins = _merge(sp[:a]), _merge(sp[a:])
+            continue
+        n, shift = a, b
+        begin = [int(v) for v in words[:n]]
+        if kind == 0:
+            recs = words[n:n + 8 * n].reshape(n, 8)
+            segs = [tuple(int(v) for v in r) for r in recs]
+            # the planner's chunk prefix is the one the kernel searches
+            want, c = [], 0
+            for sg in segs:
+                want.append(c)
+                c += KI.item_chunks(sg[1], sg[3], sg[4], sg[7], shift)
+            assert begin == want and c == n_chunks
+            writes, reads = KI.check_copy(segs, elt, shift)
+            w_iv = [(w[0], w[1]) for w in writes]
+            r_iv = [(r[0], r[1]) for r in reads]
+            counts["blocks"] += sum(sg[4] > 1 for sg in segs)
+        else:
+            raw = blob[8 * n:8 * n + 64 * n]
+            jobs = [struct.unpack_from("<2Q4I4Q", raw, 64 * k) for k in range(n)]
+            ptr = [int(v) for v in np.frombuffer(blob[8 * n + 64 * n:], dtype=np.uint64)]
+            want, c = [], 0
+            for jb in jobs:
+                want.append(c)
+                c += KI.item_chunks(ptr[jb[4]], jb[0], jb[6], jb[9], shift)
+            assert begin == want and c == n_chunks
+            es = 4 if elt == 0 else 2
+            writes, reads = KI.check_reduce(jobs, ptr, shift, es)
+            w_iv = [(w[0], w[1]) for w in writes]
+            r_iv = [(r[0], r[1]) for r in reads]
+            counts["blocks"] += sum(jb[6] > 1 for jb in jobs)
+        # exactly the call's outputs are written (each byte once: checked above)
+        assert _merge(w_iv) == outs, f"table {counts[0] + counts[1]}: writes do not cover exactly the outputs"
+        env = _merge([(x & ~15, (y + 15) & ~15) for x, y in ins])
+        bad = _inside(r_iv, env)
+        assert bad is None, f"read {bad} outside the inputs' aligned envelopes"
+        counts[kind] += 1
+    # the driver's buckets produce copy and reduce tables, strided blocks included
+    assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > 50, counts

@@ -186,6 +186,7 @@ def check_copy(segs, es, shift):
     for (a, b, j, row) in reads:
         src, dst, copy, total = seg_row(segs[j], row)
         assert align_down16(src) <= a and b <= align_up16(src + copy), "read outside the source envelope"
+    return writes, reads
 
 
 def job10(jb):
@@ -302,6 +303,7 @@ def check_reduce(jobs, ptr, shift, es=4):
         nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, _ = job10(jobs[j])
         s = ptr[src0 + t] + row * sp
         assert align_down16(s) <= a and b <= align_up16(s + data), "operand read outside its envelope"
+    return writes, reads
 
 
 # ---------------------------------------------------------------------------
