@@ -809,17 +809,17 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
       }
       for (int64_t o = 0; o < L.outer[i]; ++o) {
         const bool last = o + 1 == L.outer[i];
-        const int64_t src_off = (o * L.dk[i] + L.row_off[(size_t)i * S + s]) * L.inner[i] * es;
+        const uint64_t row_src = src_off + (uint64_t)o * pitch;
         fsdp::RedJob jb;
         jb.nbytes = (uint64_t)((last ? L.padded[i] - o * run : run) * es);
         jb.data_bytes = (uint64_t)(run * es);
         jb.src0 = (uint32_t)ptrs.size();
         jb.nsrc = (uint32_t)S;
         for (int32_t t = 0; t < S; ++t)
-          ptrs.push_back(run ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + (uint64_t)src_off : 0);
+          ptrs.push_back(run ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + row_src : 0);
         jb.dst0 = (uint32_t)ptrs.size();
         jb.ndst = 1;
-        ptrs.push_back((uint64_t)rs_out[g] + (uint64_t)((L.in_off[i] + o * run) * es));
+        ptrs.push_back(out0 + (uint64_t)(o * run * es));
         if (jb.nbytes) jobs.push_back(jb);
       }
     }
