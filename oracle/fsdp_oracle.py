@@ -114,7 +114,7 @@ class BucketLayout:
     chunk_rows[i] padded length of the shard dim per rank (for dim 0 the
                   padded_sharded_param_size dim 0 of [RAGGED] 6.4)
     inner[i]      product of the dims after the shard dim
-    padded[i]     chunk_rows[i] * inner[i], elements per rank slice
+    padded[i]     outer[i] * chunk_rows[i] * inner[i], elements per rank slice
     in_off[i]     offset of parameter i inside one rank slice; advances by
                   padded elements only ([RAGGED] 6.4, fused RS copy-in)
     I             elements per rank slice (sum of padded)
