@@ -273,6 +273,45 @@ def bucket_variant(w, op, K: int, warmup: int, grad_dtype=None, shard_dims=None)
     return out
 
 
+def zero_copy_ag_variant(w, op, reps: int):
+    """The forward AG of the workload with one bucket per parameter: AG
+    copy-in + copy-out per bucket, against AG copy-in alone with each
+    parameter used as the zero-copy prefix view of its gathered buffer."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+    R, S = w.rank_size, w.shard_size
+    params = W.params(w, "cuda")
+    buckets = []
+    for sh, p in zip(w.param_shapes, params):
+        fb = hp.FlatBucket([sh], R, S, w.param_dtype, op=op)
+        g0 = torch.zeros(p.numel(), device="cuda")  # the AG steps read no gradient
+        fb.bind(fb.shard_views([p]), [g0] * R)
+        fb.full_views()  # a one-parameter bucket: the view is valid
+        buckets.append(fb)
+    out = {"buckets": len(buckets)}
+    passes = {"copy_in_and_out": ("ag_copy_in", "ag_copy_out"), "zero_copy_views": ("ag_copy_in",)}
+    for name, steps in passes.items():
+        def run():
+            for fb in buckets:
+                for st in steps:
+                    fb.run(st)
+        for _ in range(3):
+            run()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            run()
+        e0.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(s0.elapsed_time(e0) / reps * 1e3, 1)
+    log(f"  zero-copy AG, one bucket per parameter: copy-in + copy-out {out['copy_in_and_out_us']:.1f} us, "
+        f"copy-in with views {out['zero_copy_views_us']:.1f} us")
+    return out
+
+
 def pipeline_variant(w, op, layers: int, reps: int):
     """The backward of `layers` buckets of this workload (RS copy-reduce of
     each layer, fused AR of the previous layer): serial on one stream vs the
@@ -536,6 +575,7 @@ def main():
         if args.pipeline_layers > 1 and runner.do_ar:
             variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
         if not args.no_variants:
+            variants["zero_copy_ag"] = zero_copy_ag_variant(w, op, K)
             variants["bf16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.bfloat16)
             variants["fp16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.float16)
             dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
