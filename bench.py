@@ -312,6 +312,49 @@ def zero_copy_ag_variant(w, op, reps: int):
     return out
 
 
+def fused_group_variant(w, op, reps: int, warmup: int):
+    """The pass with one bucket per parameter whose RS outputs share one
+    512-byte-aligned fused buffer and one fused AR (FusedGroup): time per
+    pass and GB/s of its algorithmic bytes."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+    R, S = w.rank_size, w.shard_size
+    buckets = [[sh] for sh in w.param_shapes]
+    grp = hp.FusedGroup(buckets, R, S, w.param_dtype, op=op)
+    params = W.params(w, "cuda")
+    grads = W.grads(w, "cuda")
+    grp.bind([fb.shard_views([params[k]]) for k, fb in enumerate(grp.buckets)],
+             [[grads[g][k].reshape(-1) for g in range(R)] for k in range(len(buckets))])
+    total = 0
+    for k, fb in enumerate(grp.buckets):
+        wk = dataclasses_replace(w, param_shapes=(w.param_shapes[k],))
+        nb = step_bytes(wk, fb.layout, 0)
+        total += sum(nb[s] for s in ("ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"))
+    if grp.do_ar:
+        total += 8 * R * grp.fused[0].numel()
+    for _ in range(warmup):
+        grp.step()
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record()
+    for _ in range(reps):
+        grp.step()
+    e0.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(e0) / reps
+    out = {"buckets": len(buckets), "fused_numel": grp.fused[0].numel(), "ms_per_step": round(ms, 4),
+           "bytes_per_step": total, "GB/s": round(total / (ms * 1e-3) / 1e9, 1)}
+    log(f"  one bucket per parameter, one fused AR: step {ms * 1e3:.1f} us, {out['GB/s']:.1f} GB/s")
+    return out
+
+
+def dataclasses_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)
+
+
 def pipeline_variant(w, op, layers: int, reps: int):
     """The backward of `layers` buckets of this workload (RS copy-reduce of
     each layer, fused AR of the previous layer): serial on one stream vs the
@@ -576,6 +619,7 @@ def main():
             variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
         if not args.no_variants:
             variants["zero_copy_ag"] = zero_copy_ag_variant(w, op, K)
+            variants["per_parameter_buckets_one_ar"] = fused_group_variant(w, op, K, args.warmup)
             variants["bf16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.bfloat16)
             variants["fp16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.float16)
             dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]

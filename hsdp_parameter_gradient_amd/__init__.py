@@ -27,11 +27,11 @@ from ._binding import (  # noqa: F401
     lib_path,
     prepare,
 )
-from .flat_bucket import FlatBucket  # noqa: F401
+from .flat_bucket import FlatBucket, FusedGroup  # noqa: F401
 from .pipeline import BackwardPipeline  # noqa: F401
 
 __all__ = [
-    "FlatBucket", "BackwardPipeline",
+    "FlatBucket", "FusedGroup", "BackwardPipeline",
     "AVG", "SUM", "FSDPError", "Layout", "fsdp_ag_copy_in", "fsdp_ag_copy_out",
     "fsdp_bucket_layout", "fsdp_fused_ar", "fsdp_fused_layout", "fsdp_group_ranks",
     "fsdp_last_error", "fsdp_release_cache", "fsdp_rs_copy_in", "fsdp_rs_copy_reduce", "fsdp_rs_reduce",

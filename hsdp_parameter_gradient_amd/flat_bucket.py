@@ -33,11 +33,14 @@ class FlatBucket:
                  param_dtype: torch.dtype = torch.bfloat16, op: str = B.AVG,
                  device: str = "cuda", fused_segments: Optional[Sequence[int]] = None,
                  fused_index: int = 0, grad_dtype: torch.dtype = torch.float32,
-                 shard_dims: Optional[Sequence[int]] = None):
+                 shard_dims: Optional[Sequence[int]] = None,
+                 fused: Optional[Sequence[torch.Tensor]] = None):
         """fused_segments: sizes of the segments of the fused buffer (default:
         this bucket's RS output alone); fused_index: which one is this
         bucket's; grad_dtype: float32, bfloat16 or float16 (the reduce dtype);
-        shard_dims: one shard dim per parameter (default 0)."""
+        shard_dims: one shard dim per parameter (default 0); fused: the R
+        fused buffers to write the RS output into, shared with other buckets
+        (default: this bucket's own, zero-initialised)."""
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.R, self.S = int(rank_size), int(shard_size)
         rs, ar = B.fsdp_group_ranks(self.R, self.S)
@@ -63,7 +66,12 @@ class FlatBucket:
         self.rs_in = [torch.empty(self.S * I, dtype=grad_dtype, device=dev) for _ in range(self.R)]
         # fused buffers are fully defined (gaps zero) before the first RS writes
         # its views; torch's allocator returns 512-byte-aligned storage.
-        self.fused = [torch.zeros(self.F, dtype=grad_dtype, device=dev) for _ in range(self.R)]
+        if fused is None:
+            self.fused = [torch.zeros(self.F, dtype=grad_dtype, device=dev) for _ in range(self.R)]
+        else:
+            self.fused = list(fused)
+            if len(self.fused) != self.R or any(f.numel() != self.F or f.dtype != grad_dtype for f in self.fused):
+                raise ValueError(f"fused: expected {self.R} buffers of {self.F} {grad_dtype} elements")
         self.rs_out = [f[self.fused_off:self.fused_off + I] for f in self.fused]
         self._calls = None
 
@@ -128,3 +136,42 @@ class FlatBucket:
     def step(self, stream=None, fused_rs: bool = False) -> None:
         for name in self.steps(fused_rs):
             self._calls[name](stream)
+
+
+class FusedGroup:
+    """Several buckets whose RS outputs share one fused buffer per rank and
+    one fused AR (the AllReduceParamGroup of the PR #758 write-up of the
+    Hyper communication-overlap scheme, section 2.1): bucket k's RS output
+    is segment k, on a 512-byte boundary; the AR runs once over the whole
+    buffer, gaps included.  Each bucket keeps its own AG and RS buffers."""
+
+    def __init__(self, buckets: Sequence[Sequence[Sequence[int]]], rank_size: int, shard_size: int,
+                 param_dtype: torch.dtype = torch.bfloat16, op: str = B.AVG, device: str = "cuda",
+                 grad_dtype: torch.dtype = torch.float32):
+        self.R, self.S = int(rank_size), int(shard_size)
+        seg = [B.fsdp_bucket_layout(b, self.S).I for b in buckets]
+        _, F = B.fsdp_fused_layout(seg, grad_dtype.itemsize)
+        self.seg_numel = seg
+        self.fused = [torch.zeros(F, dtype=grad_dtype, device=torch.device(device)) for _ in range(self.R)]
+        self.buckets = [FlatBucket(b, rank_size, shard_size, param_dtype, op, device, seg, k, grad_dtype,
+                                   fused=self.fused) for k, b in enumerate(buckets)]
+        self.op = op
+        self.D = self.R // self.S
+        self.do_ar = self.buckets[0].do_ar if self.buckets else False
+        self._ar = None
+
+    def bind(self, shards: Sequence[Sequence[torch.Tensor]], grads: Sequence[Sequence[torch.Tensor]]) -> "FusedGroup":
+        """shards[k] and grads[k]: bucket k's inputs, as FlatBucket.bind."""
+        for fb, sh, gr in zip(self.buckets, shards, grads):
+            fb.bind(sh, gr)
+        self._ar = B.prepare("fsdp_fused_ar", self.seg_numel, self.R, self.S, self.D, self.op, self.fused)
+        return self
+
+    def step(self, stream=None, fused_rs: bool = False) -> None:
+        """Every bucket's AG and RS, then the one fused AR."""
+        for fb in self.buckets:
+            for name in fb.steps(fused_rs):
+                if name != "fused_ar":
+                    fb.run(name, stream)
+        if self.do_ar:
+            self._ar(stream)

@@ -802,3 +802,35 @@ def test_many_passes_stay_bit_identical():
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"full params after run {run}"
         for g, (a, b) in enumerate(zip(fb.fused, first_fused)):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"fused rank {g} after run {run}"
+
+
+@pytest.mark.parametrize("fused_rs", [False, True])
+def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
+    """The HSDP block with one bucket per parameter: six RS outputs as
+    512-byte-aligned segments of one fused buffer per rank, one fused AR;
+    the fused buffers (gaps included) and the gathered parameters against
+    the oracle's fused path."""
+    w = W.scaled(W.HSDP_BLOCK, [(97, 64), (32, 64), (130, 32), (33, 128), (64,), (3,)])
+    R, S = w.rank_size, w.shard_size
+    buckets = [[sh] for sh in w.param_shapes]
+    note(f"[parity] FusedGroup of {len(buckets)} buckets fused_rs={fused_rs}")
+    params, g_cpu = W.params(w), W.grads(w)
+    grp = hp.FusedGroup(buckets, R, S, w.param_dtype, op=O.AVG)
+    dparams = [p.cuda() for p in params]
+    shards = [fb.shard_views([dparams[k]]) for k, fb in enumerate(grp.buckets)]
+    grads = [[g_cpu[g][k].cuda().reshape(-1) for g in range(R)] for k in range(len(buckets))]
+    grp.bind(shards, grads)
+    for rep in range(2):
+        for fb in grp.buckets:
+            for v in fb.rs_out:
+                v.fill_(float("nan"))
+        grp.step(fused_rs=fused_rs)
+        torch.cuda.synchronize()
+        gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
+        _, fused_o, offs_o, _ = O.reduce_grads_fused(gnp, buckets, R, S, O.AVG)
+        assert [fb.fused_off for fb in grp.buckets] == offs_o
+        for g in range(R):
+            m = first_mismatch(bits(grp.fused[g]), np_bits(fused_o[g]))
+            assert m == "", f"rep {rep} fused rank {g}: {m}"
+        for k, fb in enumerate(grp.buckets):
+            assert np.array_equal(bits(fb.full[0]), bits(params[k].reshape(-1)))
