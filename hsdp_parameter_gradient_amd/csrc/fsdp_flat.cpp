@@ -270,6 +270,7 @@ struct Plan {
   uint32_t nsrc = 0;
   int avg = 0;
   int nts = 0;
+  int device = 0;  // the device whose memory holds `dev`
 };
 
 struct Entry {
@@ -323,15 +324,35 @@ bool launch_cached(const Key& key, hipStream_t stream, int* rc) {
   return false;
 }
 
+// Synchronize every device that holds a cached table (the key's second
+// word is the device), then make the caller's device current again.
+hipError_t sync_cached_devices() {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  std::vector<int> devs;
+  for (const Entry& en : g_lru)
+    if (en.plan.dev && std::find(devs.begin(), devs.end(), en.plan.device) == devs.end())
+      devs.push_back(en.plan.device);
+  if (std::find(devs.begin(), devs.end(), cur) == devs.end()) devs.push_back(cur);
+  for (int d : devs) {
+    if ((e = hipSetDevice(d)) != hipSuccess) break;
+    if ((e = hipDeviceSynchronize()) != hipSuccess) break;
+  }
+  const hipError_t r = hipSetDevice(cur);
+  return e != hipSuccess ? e : r;
+}
+
 // Keep `plan` under `key` (evicting old plans first if needed) and launch it.
 int store_and_launch(Key&& key, Plan&& plan, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_mu);
   if (g_lru.size() >= kMaxEntries || g_table_bytes + plan.bytes > kMaxTableBytes) {
-    // tables still in use by queued kernels must outlive them
-    hipError_t e = hipDeviceSynchronize();
+    // tables still in use by queued kernels must outlive them: wait for
+    // every device that owns a cached table, not only the current one
+    hipError_t e = sync_cached_devices();
     if (e != hipSuccess) {
       if (plan.dev) (void)hipFree(plan.dev);
-      return fail(FSDP_EHIP, "hipDeviceSynchronize before evicting plans: %s", hipGetErrorString(e));
+      return fail(FSDP_EHIP, "device synchronize before evicting plans: %s", hipGetErrorString(e));
     }
     while (!g_lru.empty() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + plan.bytes > kMaxTableBytes / 2))
       drop_entry(std::prev(g_lru.end()));
@@ -363,7 +384,9 @@ bool stream_stores(Reuse reuse, uint64_t out_bytes) {
 // Upload a table (blocking copy into fresh device memory, so it is complete
 // before anything is enqueued on any stream).
 int upload(const std::vector<uint8_t>& table, Plan* p) {
-  hipError_t e = hipMalloc(&p->dev, table.size());
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) return fail(FSDP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  e = hipMalloc(&p->dev, table.size());
   if (e != hipSuccess) return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", table.size(), hipGetErrorString(e));
   if ((e = hipMemcpy(p->dev, table.data(), table.size(), hipMemcpyHostToDevice)) != hipSuccess) {
     (void)hipFree(p->dev);
@@ -499,7 +522,7 @@ const char* fsdp_last_error(void) { return g_err.c_str(); }
 
 void fsdp_release_cache(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_lru.empty()) (void)hipDeviceSynchronize();
+  if (!g_lru.empty()) (void)sync_cached_devices();
   while (!g_lru.empty()) drop_entry(g_lru.begin());
 }
 

@@ -51,8 +51,8 @@
  *     shapes, shard dims, pointers, device): the call's descriptor table in
  *     device memory and its launch parameters.  A repeated call launches its
  *     plan without validating or planning again (its result cannot differ).
- *     At most 256 plans and 256 MiB of tables; evicting waits for the
- *     device.  fsdp_release_cache() frees them all.
+ *     At most 256 plans and 256 MiB of tables; evicting waits for every
+ *     device that holds a cached table.  fsdp_release_cache() frees them all.
  *   - Thread safe; calls that overlap in time on different streams must not
  *     share output buffers.
  */
@@ -238,7 +238,8 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size,
 /* Message for the calling thread's last error ("" after success). */
 const char* fsdp_last_error(void);
 
-/* Free the cached descriptor tables (waits for the device first). */
+/* Free the cached descriptor tables (waits first for every device that
+ * holds one). */
 void fsdp_release_cache(void);
 
 #ifdef __cplusplus
