@@ -22,7 +22,8 @@ SUM = "sum"
 AVG = "avg"
 _OPS = {SUM: 0, AVG: 1}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
-_CODES = {1: "FSDP_EINVAL", 2: "FSDP_ENOTIMPL", 3: "FSDP_EALIGN", 4: "FSDP_EHIP", 5: "FSDP_EOVERLAP"}
+_CODES = {1: "FSDP_EINVAL", 2: "FSDP_ENOTIMPL", 3: "FSDP_EALIGN", 4: "FSDP_EHIP", 5: "FSDP_EOVERLAP",
+          6: "FSDP_ENOMEM"}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 

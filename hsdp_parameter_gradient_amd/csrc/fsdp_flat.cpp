@@ -23,8 +23,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <exception>
 #include <list>
 #include <mutex>
+#include <new>
+#include <stdexcept>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -53,7 +56,11 @@ int fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_err = buf;
+  try {
+    g_err = buf;
+  } catch (...) {  // no memory for the message: the code still stands
+    g_err.clear();
+  }
   return code;
 }
 
@@ -358,8 +365,20 @@ int store_and_launch(Key&& key, Plan&& plan, hipStream_t stream) {
       drop_entry(std::prev(g_lru.end()));
   }
   const uint64_t h = key.hash();
-  g_lru.push_front(Entry{std::move(key), h, plan});
-  g_index[h].push_back(g_lru.begin());
+  // the table must not leak if the host bookkeeping cannot grow
+  try {
+    g_lru.push_front(Entry{std::move(key), h, plan});
+  } catch (...) {
+    if (plan.dev) (void)hipFree(plan.dev);
+    throw;
+  }
+  try {
+    g_index[h].push_back(g_lru.begin());
+  } catch (...) {
+    g_lru.pop_front();
+    if (plan.dev) (void)hipFree(plan.dev);
+    throw;
+  }
   g_table_bytes += plan.bytes;
   return enqueue(g_lru.front().plan, stream);
 }
@@ -513,20 +532,12 @@ int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>
 }  // namespace
 
 // ===========================================================================
-// C ABI
+// entry points (wrapped below for the C ABI)
 // ===========================================================================
 
-extern "C" {
+namespace {
 
-const char* fsdp_last_error(void) { return g_err.c_str(); }
-
-void fsdp_release_cache(void) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_lru.empty()) (void)sync_cached_devices();
-  while (!g_lru.empty()) drop_entry(g_lru.begin());
-}
-
-int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t* slice_numel,
+int bucket_layout_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t* slice_numel,
                        int64_t* padded, int64_t* in_off, int64_t* row_off, int64_t* row_len) {
   Layout L;
   int rc = make_layout(bucket, shard_size, &L);
@@ -539,7 +550,7 @@ int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t*
   return ok();
 }
 
-int fsdp_fused_layout(int32_t n_seg, const int64_t* seg_numel, int32_t elem_bytes, int64_t* seg_off,
+int fused_layout_impl(int32_t n_seg, const int64_t* seg_numel, int32_t elem_bytes, int64_t* seg_off,
                       int64_t* fused_numel) {
   if (n_seg < 0) return fail(FSDP_EINVAL, "n_seg %d < 0", n_seg);
   if (n_seg > 0 && !seg_numel) return fail(FSDP_EINVAL, "seg_numel is NULL");
@@ -558,7 +569,7 @@ int fsdp_fused_layout(int32_t n_seg, const int64_t* seg_numel, int32_t elem_byte
   return ok();
 }
 
-int fsdp_group_ranks(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups, int32_t* rs_ranks,
+int group_ranks_impl(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups, int32_t* rs_ranks,
                      int32_t* n_ar_groups, int32_t* ar_ranks) {
   int rc = check_groups(rank_size, shard_size);
   if (rc) return rc;
@@ -574,7 +585,7 @@ int fsdp_group_ranks(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups
   return ok();
 }
 
-int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype,
+int ag_copy_in_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype,
                     const void* const* shards, void* ag, void* stream) {
   Key key(kAgCopyIn);
   if (key.bucket(bucket)) {
@@ -612,7 +623,7 @@ int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dty
   return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
-int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
+int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
                      void* const* full, void* stream) {
   Key key(kAgCopyOut);
   if (key.bucket(bucket)) {
@@ -650,7 +661,7 @@ int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
   return run_copy(std::move(key), segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream));
 }
 
-int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
+int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
                     const void* const* grads, void* const* rs_in, void* stream) {
   Key key(kRsCopyIn);
   if (key.bucket(bucket)) {
@@ -710,7 +721,7 @@ int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
   return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
 }
 
-int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+int rs_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
                    int32_t op, int32_t dtype, const void* const* rs_in, void* const* rs_out, void* stream) {
   Key key(kRsReduce);
   if (key.bucket(bucket)) {
@@ -759,7 +770,7 @@ int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
                     static_cast<hipStream_t>(stream));
 }
 
-int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
                         int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
                         void* stream) {
   Key key(kRsCopyReduce);
@@ -852,7 +863,7 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
                     static_cast<hipStream_t>(stream));
 }
 
-int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
+int fused_ar_impl(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
                   int32_t dp_size, int32_t op, int32_t dtype, void* const* fused, void* stream) {
   Key key(kFusedAr);
   if (n_seg >= 0 && (n_seg == 0 || seg_numel)) {
@@ -873,7 +884,7 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
   const int es = reduce_elem_size(dtype);
   if (!es) return fail(FSDP_ENOTIMPL, "fused_ar takes fp32, bf16 or fp16 (dtype %d)", dtype);
   int64_t F = 0;
-  if ((rc = fsdp_fused_layout(n_seg, seg_numel, es, nullptr, &F))) return rc;
+  if ((rc = fused_layout_impl(n_seg, seg_numel, es, nullptr, &F))) return rc;
   const int32_t R = rank_size, S = shard_size, D = dp_size;
   const int64_t nbytes = F * es;
   if (!fused) return fail(FSDP_EINVAL, "fused array is NULL");
@@ -898,6 +909,95 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, in
   }
   return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kFinal,
                     static_cast<hipStream_t>(stream));
+}
+
+// No C++ exception may cross the C ABI: host allocation failures while
+// planning become FSDP_ENOMEM, anything else FSDP_EINVAL.  Nothing has been
+// enqueued when an exception is thrown (launches come last).
+template <class F>
+int guarded(F&& f) noexcept {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(FSDP_ENOMEM, "out of host memory while planning the call");
+  } catch (const std::length_error&) {
+    return fail(FSDP_ENOMEM, "the call's host tables would exceed the largest allocation");
+  } catch (const std::exception& e) {
+    return fail(FSDP_EINVAL, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(FSDP_EINVAL, "internal error");
+  }
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+const char* fsdp_last_error(void) { return g_err.c_str(); }
+
+void fsdp_release_cache(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  try {
+    if (!g_lru.empty()) (void)sync_cached_devices();
+  } catch (...) {  // no memory to list the devices: wait for every one
+    int n = 0, cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && hipGetDeviceCount(&n) == hipSuccess) {
+      for (int d = 0; d < n; ++d)
+        if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
+      (void)hipSetDevice(cur);
+    }
+  }
+  while (!g_lru.empty()) drop_entry(g_lru.begin());
+}
+
+int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t* slice_numel,
+                       int64_t* padded, int64_t* in_off, int64_t* row_off, int64_t* row_len) {
+  return guarded([&] { return bucket_layout_impl(bucket, shard_size, slice_numel, padded, in_off, row_off, row_len); });
+}
+
+int fsdp_fused_layout(int32_t n_seg, const int64_t* seg_numel, int32_t elem_bytes, int64_t* seg_off,
+                      int64_t* fused_numel) {
+  return guarded([&] { return fused_layout_impl(n_seg, seg_numel, elem_bytes, seg_off, fused_numel); });
+}
+
+int fsdp_group_ranks(int32_t rank_size, int32_t shard_size, int32_t* n_rs_groups, int32_t* rs_ranks,
+                     int32_t* n_ar_groups, int32_t* ar_ranks) {
+  return guarded([&] { return group_ranks_impl(rank_size, shard_size, n_rs_groups, rs_ranks, n_ar_groups, ar_ranks); });
+}
+
+int fsdp_ag_copy_in(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype,
+                    const void* const* shards, void* ag, void* stream) {
+  return guarded([&] { return ag_copy_in_impl(bucket, shard_size, dtype, shards, ag, stream); });
+}
+
+int fsdp_ag_copy_out(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dtype, const void* ag,
+                     void* const* full, void* stream) {
+  return guarded([&] { return ag_copy_out_impl(bucket, shard_size, dtype, ag, full, stream); });
+}
+
+int fsdp_rs_copy_in(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
+                    const void* const* grads, void* const* rs_in, void* stream) {
+  return guarded([&] { return rs_copy_in_impl(bucket, rank_size, shard_size, dtype, grads, rs_in, stream); });
+}
+
+int fsdp_rs_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+                   int32_t op, int32_t dtype, const void* const* rs_in, void* const* rs_out, void* stream) {
+  return guarded([&] { return rs_reduce_impl(bucket, rank_size, shard_size, dp_size, op, dtype, rs_in, rs_out, stream); });
+}
+
+int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+                        int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
+                        void* stream) {
+  return guarded([&] { return rs_copy_reduce_impl(bucket, rank_size, shard_size, dp_size, op, dtype, grads, rs_out, stream); });
+}
+
+int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
+                  int32_t dp_size, int32_t op, int32_t dtype, void* const* fused, void* stream) {
+  return guarded([&] { return fused_ar_impl(n_seg, seg_numel, rank_size, shard_size, dp_size, op, dtype, fused, stream); });
 }
 
 }  // extern "C"

@@ -35,7 +35,9 @@
  * Conventions shared by every entry point:
  *   - Status: FSDP_OK (0) or a positive error code; fsdp_last_error() gives
  *     a message for the calling thread.  Arguments are validated completely
- *     before anything is enqueued: on error nothing is launched.
+ *     before anything is enqueued: on error nothing is launched.  No C++
+ *     exception leaves the library: a host allocation that fails while a
+ *     call is planned returns FSDP_ENOMEM.
  *   - Device pointers are plain addresses of device memory owned by the
  *     caller.  The caller keeps every buffer alive and unchanged (inputs) or
  *     untouched (outputs) until the stream has passed the call.  Buffer
@@ -72,6 +74,7 @@ extern "C" {
 #define FSDP_EALIGN    3  /* pointer not aligned as required */
 #define FSDP_EHIP      4  /* a HIP runtime call failed */
 #define FSDP_EOVERLAP  5  /* an output overlaps an input or another output */
+#define FSDP_ENOMEM    6  /* host memory for the call's plan could not be allocated */
 
 /* element types: copies take any of them (bits are moved, not converted);
  * reductions take FSDP_F32, FSDP_BF16 or FSDP_F16 (16-bit elements are

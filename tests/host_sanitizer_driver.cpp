@@ -15,6 +15,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <new>
+#include <stdexcept>
 #include <utility>
 #include <vector>
 
@@ -29,11 +32,19 @@ int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t,
   std::abort();
 }
 
+// Set by the "throw" mode: the hook then throws the given exception kind
+// (1 bad_alloc, 2 length_error, 3 runtime_error), as an allocation inside
+// the planner would.
+int g_hook_throw = 0;
+
 // With FSDP_TABLE_HOOK, every planned table is appended to the file named
 // by FSDP_DUMP_TABLES (if set): a 32-byte header (reduce, elt, n_items,
 // shift, n_chunks, table bytes) and the table itself.
 void fsdp_table_hook(int reduce, int elt, uint32_t n_items, uint64_t n_chunks, uint32_t shift,
                      const std::vector<uint8_t>& table) {
+  if (g_hook_throw == 1) throw std::bad_alloc();
+  if (g_hook_throw == 2) throw std::length_error("table");
+  if (g_hook_throw == 3) throw std::runtime_error("planted");
   const char* path = std::getenv("FSDP_DUMP_TABLES");
   if (!path) return;
   FILE* f = std::fopen(path, "ab");
@@ -207,10 +218,57 @@ void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
 
 }  // namespace
 
-int main() {
+// An exception thrown while a call is planned must come back as a status
+// code (FSDP_ENOMEM for allocation failures, FSDP_EINVAL otherwise), for
+// copies and reductions alike, and the next call must work normally.
+void run_throw_mode() {
+  const std::vector<int64_t> shape = {7, 8, 5, 3, 16};
+  const int32_t ndim[3] = {2, 2, 1};
+  fsdp_bucket_t b = {3, ndim, shape.data(), 0, nullptr};
+  const int32_t S = 4;
+  int64_t I = 0;
+  fsdp_bucket_layout(&b, S, &I, nullptr, nullptr, nullptr, nullptr);
+  std::vector<int64_t> row_len(3 * S);
+  fsdp_bucket_layout(&b, S, nullptr, nullptr, nullptr, nullptr, row_len.data());
+  Fake f;
+  std::vector<const void*> shards;
+  const int64_t inner[3] = {8, 3, 1};
+  for (int32_t s = 0; s < S; ++s)
+    for (int32_t i = 0; i < 3; ++i) shards.push_back(f.get((uint64_t)(row_len[(size_t)i * S + s] * inner[i] * 4)));
+  void* ag = f.get((uint64_t)(S * I * 4));
+  std::vector<void*> fused;
+  const int64_t seg[1] = {I};
+  int64_t F = 0;
+  fsdp_fused_layout(1, seg, 4, nullptr, &F);
+  for (int g = 0; g < 2; ++g) fused.push_back(f.get((uint64_t)(F * 4)));
+  const int want[4] = {FSDP_EHIP, FSDP_ENOMEM, FSDP_ENOMEM, FSDP_EINVAL};
+  for (int kind = 1; kind <= 3; ++kind) {
+    g_hook_throw = kind;
+    EXPECT(fsdp_ag_copy_in(&b, S, FSDP_F32, shards.data(), ag, nullptr), want[kind]);
+    if (kind == 3 && !std::strstr(fsdp_last_error(), "planted")) {
+      std::fprintf(stderr, "message does not carry the exception's text: %s\n", fsdp_last_error());
+      ++failures;
+    }
+    EXPECT(fsdp_fused_ar(1, seg, 2, 1, 2, FSDP_AVG, FSDP_F32, fused.data(), nullptr), want[kind]);
+  }
+  g_hook_throw = 0;  // and the library works on
+  EXPECT(fsdp_ag_copy_in(&b, S, FSDP_F32, shards.data(), ag, nullptr), want[0]);
+  EXPECT(fsdp_fused_ar(1, seg, 2, 1, 2, FSDP_AVG, FSDP_F32, fused.data(), nullptr), want[0]);
+}
+
+int main(int argc, char** argv) {
   int n = 0;
   if (hipGetDeviceCount(&n) == hipSuccess && n > 0) {
     std::printf("skip\n");
+    return 0;
+  }
+  if (argc > 1 && std::strcmp(argv[1], "throw") == 0) {
+    run_throw_mode();
+    if (failures) {
+      std::fprintf(stderr, "%d checks failed\n", failures);
+      return 1;
+    }
+    std::printf("ok\n");
     return 0;
   }
   const std::vector<Case> cases = {

@@ -43,10 +43,10 @@ def driver(tmp_path_factory):
     return exe
 
 
-def _run(exe, extra_env=None):
+def _run(exe, extra_env=None, args=()):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", HIP_VISIBLE_DEVICES="")
     env.update(extra_env or {})
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=300, env=env)
     if r.stdout.strip() == "skip":
         pytest.skip("a GPU is visible: the driver needs the uploads to fail")
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout + r.stderr)[-4000:]
@@ -54,6 +54,14 @@ def _run(exe, extra_env=None):
 
 def test_planner_under_asan_and_ubsan(driver):
     _run(driver)
+
+
+def test_exceptions_do_not_cross_the_c_abi(driver):
+    """An exception thrown while a call is planned (planted in the table
+    hook: bad_alloc, length_error, another std::exception) comes back as
+    FSDP_ENOMEM / FSDP_ENOMEM / FSDP_EINVAL from copies and reductions, and
+    the following calls plan normally (no leak under LeakSanitizer)."""
+    _run(driver, args=("throw",))
 
 
 def _records(path):
