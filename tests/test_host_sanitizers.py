@@ -96,12 +96,22 @@ def _inside(iv, allowed):
     return None
 
 
-def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path):
+TUNINGS = {
+    "default": {},
+    # the smallest and a large chunk size the tuning accepts (for both kernels)
+    "chunks_512B": {"FSDP_COPY_CHUNK_SHIFT": "9", "FSDP_REDUCE_CHUNK_SHIFT": "9"},
+    "chunks_1MiB": {"FSDP_COPY_CHUNK_SHIFT": "20", "FSDP_REDUCE_CHUNK_SHIFT": "20"},
+}
+
+
+@pytest.mark.parametrize("tuning", list(TUNINGS))
+def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
     """Every table the planner builds, run through the emulated kernels,
     writes exactly its call's output buffers (every byte once) and reads
-    only inside the aligned envelopes of its call's inputs."""
+    only inside the aligned envelopes of its call's inputs; at the default
+    chunk sizes and at the extremes the tuning overrides allow."""
     dump = str(tmp_path / "tables.bin")
-    _run(driver, {"FSDP_DUMP_TABLES": dump})
+    _run(driver, {"FSDP_DUMP_TABLES": dump, **TUNINGS[tuning]})
     counts = {0: 0, 1: 0, "blocks": 0}
     outs = ins = None
     for kind, elt, a, b, n_chunks, blob in _records(dump):
@@ -146,4 +156,4 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path):
         assert bad is None, f"read {bad} outside the inputs' aligned envelopes"
         counts[kind] += 1
     # the driver's buckets produce copy and reduce tables, strided blocks included
-    assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > 50, counts
+    assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
