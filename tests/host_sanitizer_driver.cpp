@@ -92,10 +92,16 @@ void expect(int got, int want, const char* what, int line) {
 }
 #define EXPECT(call, want) expect((call), (want), #call, __LINE__)
 
-// Fake, disjoint, 512-byte-aligned buffers (plus an element offset).
+// Fake, disjoint, 512-byte-aligned buffers (plus an element offset).  With
+// vary set, a non-zero offset (one element) becomes 1..7 elements, changing
+// from buffer to buffer.
+bool g_vary_offsets = false;
+
 struct Fake {
   uint64_t next = uint64_t(1) << 40;
+  uint64_t count = 0;
   void* get(uint64_t bytes, uint64_t offset = 0) {
+    if (g_vary_offsets && offset) offset *= 1 + (count++ % 7);
     void* p = reinterpret_cast<void*>(next + offset);
     next += (bytes + offset + 4096 + 511) / 512 * 512;
     return p;
@@ -260,6 +266,43 @@ int main(int argc, char** argv) {
   int n = 0;
   if (hipGetDeviceCount(&n) == hipSuccess && n > 0) {
     std::printf("skip\n");
+    return 0;
+  }
+  if (argc > 2 && std::strcmp(argv[1], "cases") == 0) {
+    // one case per line: S R es misaligned P, then per parameter ndim, its
+    // dims and its shard dim
+    FILE* f = std::fopen(argv[2], "r");
+    if (!f) {
+      std::fprintf(stderr, "cannot open %s\n", argv[2]);
+      return 1;
+    }
+    g_vary_offsets = true;
+    int S, R, es, mis, P, n_cases = 0;
+    while (std::fscanf(f, "%d %d %d %d %d", &S, &R, &es, &mis, &P) == 5) {
+      Case c;
+      for (int i = 0; i < P; ++i) {
+        int nd = 0, k = 0;
+        if (std::fscanf(f, "%d", &nd) != 1) return 1;
+        std::vector<int64_t> sh((size_t)nd);
+        for (int d = 0; d < nd; ++d) {
+          long long v = 0;
+          if (std::fscanf(f, "%lld", &v) != 1) return 1;
+          sh[(size_t)d] = v;
+        }
+        if (std::fscanf(f, "%d", &k) != 1) return 1;
+        c.shapes.push_back(sh);
+        c.dims.push_back(k);
+      }
+      run_case(c, S, R, es, mis != 0);
+      ++n_cases;
+    }
+    std::fclose(f);
+    fsdp_release_cache();
+    if (failures || n_cases == 0) {
+      std::fprintf(stderr, "%d checks failed over %d cases\n", failures, n_cases);
+      return 1;
+    }
+    std::printf("ok\n");
     return 0;
   }
   if (argc > 1 && std::strcmp(argv[1], "throw") == 0) {

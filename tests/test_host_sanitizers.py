@@ -112,6 +112,29 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
     chunk sizes and at the extremes the tuning overrides allow."""
     dump = str(tmp_path / "tables.bin")
     _run(driver, {"FSDP_DUMP_TABLES": dump, **TUNINGS[tuning]})
+    counts = _check_tables(dump)
+    # the driver's buckets produce copy and reduce tables, strided blocks included
+    assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
+
+
+def test_random_bucket_tables_pass_the_kernel_emulation(driver, tmp_path):
+    """The seeded random buckets that test_gpu_random.py runs on the GPU
+    (ragged and zero dims, shard dims 1 and 2, group sizes up to 32, every
+    buffer at its own element offset), planned by the real planner and run
+    through the emulated kernels: exact writes, reads inside the inputs."""
+    import bucket_cases as BC
+    cases = tmp_path / "cases.txt"
+    cases.write_text("\n".join(BC.case_line(c) for c in BC.random_cases(BC_SEED, BC_COUNT)) + "\n")
+    dump = str(tmp_path / "tables.bin")
+    _run(driver, {"FSDP_DUMP_TABLES": dump}, args=("cases", str(cases)))
+    counts = _check_tables(dump)
+    assert counts[0] > 2 * BC_COUNT and counts[1] > 2 * BC_COUNT, counts
+
+
+BC_SEED, BC_COUNT = 20261202, 40  # the cases of test_gpu_random.py (its SEED, COUNT)
+
+
+def _check_tables(dump):
     counts = {0: 0, 1: 0, "blocks": 0}
     outs = ins = None
     for kind, elt, a, b, n_chunks, blob in _records(dump):
@@ -155,5 +178,4 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
         bad = _inside(r_iv, env)
         assert bad is None, f"read {bad} outside the inputs' aligned envelopes"
         counts[kind] += 1
-    # the driver's buckets produce copy and reduce tables, strided blocks included
-    assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
+    return counts
