@@ -417,19 +417,41 @@ int upload(const std::vector<uint8_t>& table, Plan* p) {
 }
 
 // Strided blocks: `rows` runs of row_bytes, row r from src + r*src_pitch to
-// dst + r*dst_pitch.  The kernels move whole rows per chunk; pitches that
-// are multiples of 16 keep every row at the alignment of the first.  Rows
-// longer than a chunk, or other pitches, go one item per row.
-bool block_ok(uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes, uint64_t rows, uint32_t shift) {
-  return rows >= 2 && row_bytes > 0 && row_bytes <= (uint64_t(1) << shift) && src_pitch % 16 == 0 &&
-         dst_pitch % 16 == 0;
+// dst + r*dst_pitch.  The kernels move whole rows per chunk.  Pitches that
+// are multiples of 16 keep every row at the alignment of the first (16-byte
+// vectors); other pitches are moved in 8-, 4- or element-sized units, which
+// beats one item (one workgroup) per row for short rows and for 8-byte
+// units.  Rows longer than a chunk, and long rows of narrow units, go one
+// item per row.
+constexpr uint64_t kShortRow = 1024;
+
+bool vector_rows(uint64_t src_pitch, uint64_t dst_pitch) { return src_pitch % 16 == 0 && dst_pitch % 16 == 0; }
+
+bool rows_fit(uint64_t row_bytes, uint64_t rows, uint32_t shift) {
+  return rows >= 2 && row_bytes > 0 && row_bytes <= (uint64_t(1) << shift);
+}
+
+bool copy_block_ok(uint64_t src, uint64_t dst, uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes,
+                   uint64_t rows, uint32_t shift) {
+  if (!rows_fit(row_bytes, rows, shift)) return false;
+  if (vector_rows(src_pitch, dst_pitch)) return true;
+  // unit-wise rows: a chunk's rows lie within 4 GiB of its first row (the
+  // kernel's offsets are 32-bit)
+  const uint64_t per = (uint64_t(1) << shift) / row_bytes;
+  if (per * std::max(src_pitch, dst_pitch) >= (uint64_t(1) << 32)) return false;
+  return row_bytes <= kShortRow || ((src | dst | src_pitch | dst_pitch | row_bytes) & 7u) == 0;
+}
+
+// The reduction kernel moves rows of other pitches element by element.
+bool reduce_block_ok(uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes, uint64_t rows, uint32_t shift) {
+  return rows_fit(row_bytes, rows, shift) && (vector_rows(src_pitch, dst_pitch) || row_bytes <= kShortRow);
 }
 
 void push_rows(std::vector<fsdp::CopySeg>& segs, uint64_t src, uint64_t dst, uint64_t row_bytes, uint64_t rows,
                uint64_t src_pitch, uint64_t dst_pitch) {
   if (row_bytes == 0 || rows == 0) return;
   const uint32_t shift = fsdp::tuning().copy_shift;
-  if (block_ok(src_pitch, dst_pitch, row_bytes, rows, shift)) {
+  if (copy_block_ok(src, dst, src_pitch, dst_pitch, row_bytes, rows, shift)) {
     fsdp::CopySeg sg{src, dst, row_bytes, row_bytes};
     sg.rows = rows;
     sg.src_pitch = src_pitch;
@@ -815,16 +837,16 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
       if (L.padded[i] == 0) continue;
       // rank s's chunk: outer runs of row_len*inner elements (stride
       // dk*inner in the gradients, dense in the output), then the zero
-      // tail; one strided job when both pitches keep the rows' alignment
-      // (and there is no tail), else one job per run, the last one with
-      // the tail
+      // tail; one strided job when the rows fit a chunk and either both
+      // pitches keep the rows' alignment or the rows are short (and there
+      // is no tail), else one job per run, the last one with the tail
       const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
       const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
       const uint64_t out0 = (uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es);
       const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
       const bool block = L.padded[i] == L.outer[i] * run &&
-                         block_ok(pitch, (uint64_t)(run * es), (uint64_t)(run * es), (uint64_t)L.outer[i],
-                                  fsdp::tuning().reduce_shift);
+                         reduce_block_ok(pitch, (uint64_t)(run * es), (uint64_t)(run * es), (uint64_t)L.outer[i],
+                                         fsdp::tuning().reduce_shift);
       if (block) {
         fsdp::RedJob jb;
         jb.nbytes = jb.data_bytes = (uint64_t)(run * es);

@@ -329,12 +329,59 @@ __device__ __forceinline__ void rows_run(uint64_t s0, uint64_t d0, uint32_t nr, 
   }
 }
 
+// Width in bytes of the units a block of rows can move whole: 8 or 4 when
+// both first-row addresses, both pitches and the row length are multiples of
+// it (then every unit of every row is aligned), else the element size.
+template <typename T>
+__device__ __forceinline__ uint32_t unit_bytes(uint64_t s0, uint64_t d0, uint64_t sp, uint64_t dp, uint64_t row) {
+  const uint64_t m = s0 | d0 | sp | dp | row;
+  return (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : (uint32_t)sizeof(T);
+}
+
+// The nr rows of a strided block as one flat range of W-typed units, upr
+// per row: unit q is row q / upr, column q % upr.  For pitches that are not
+// multiples of 16 (each row starts at another offset mod 16).  The planner
+// keeps a chunk's rows within 4 GiB of its first row on both sides, so
+// offsets are 32-bit (the workgroup-uniform base plus a 32-bit offset per
+// lane keeps the register count of the whole kernel down).  U units per
+// lane per iteration, all loads before the first store.
+template <typename W, bool NTS>
+__device__ __forceinline__ void rows_units(uint64_t s0, uint64_t d0, uint32_t nr, uint32_t upr, uint32_t sp,
+                                           uint32_t dp) {
+  constexpr int U = sizeof(W) >= 8 ? 4 : 6;
+  const uint32_t n = nr * upr;
+  const GMEM uint8_t* __restrict__ sb = gptr<uint8_t>(s0);
+  GMEM uint8_t* __restrict__ db = gptr<uint8_t>(d0);
+  auto off = [&](uint32_t q, uint32_t pitch) -> uint32_t {
+    const uint32_t row = q / upr;
+    return row * pitch + (q - row * upr) * (uint32_t)sizeof(W);
+  };
+  auto ld = [&](uint32_t o) { return __builtin_nontemporal_load(reinterpret_cast<const GMEM W*>(sb + o)); };
+  auto st = [&](uint32_t o, W v) {
+    GMEM W* a = reinterpret_cast<GMEM W*>(db + o);
+    if (NTS)
+      __builtin_nontemporal_store(v, a);
+    else
+      *a = v;
+  };
+  uint32_t base = 0;
+  for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
+    W v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld(off(base + threadIdx.x + u * kBlock, sp));
+#pragma unroll
+    for (int u = 0; u < U; ++u) st(off(base + threadIdx.x + u * kBlock, dp), v[u]);
+  }
+  for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) st(off(q, dp), ld(off(q, sp)));
+}
+
 // Chunk k of a strided block (CopySeg with rows > 1): rows
-// [k*rows_per_chunk, ...).  Both pitches are multiples of 16, so every row
+// [k*rows_per_chunk, ...).  When both pitches are multiples of 16, every row
 // has the same alignment: a head of up to 15 bytes before the row's first
 // aligned destination vector, whole vectors, and a tail after the last one.
 // The whole vectors of all rows are one flat range (rows_run); heads and
-// tails are copied element by element, one row end per lane.
+// tails are copied element by element, one row end per lane.  Other pitches
+// move the rows in 8-, 4- or element-sized units (rows_units).
 template <typename T, bool NTS>
 __device__ __forceinline__ void copy_rows(const fsdp::CopySeg& sg, uint64_t k) {
   const uint64_t r0 = k * sg.rows_per_chunk;
@@ -343,6 +390,17 @@ __device__ __forceinline__ void copy_rows(const fsdp::CopySeg& sg, uint64_t k) {
   const uint64_t B = sg.copy_bytes;
   const uint64_t s0 = sg.src + r0 * sg.src_pitch;
   const uint64_t d0 = sg.dst + r0 * sg.dst_pitch;
+  if ((sg.src_pitch | sg.dst_pitch) & 15u) {
+    const uint32_t w = unit_bytes<T>(s0, d0, sg.src_pitch, sg.dst_pitch, B);
+    const uint32_t sp = (uint32_t)sg.src_pitch, dp = (uint32_t)sg.dst_pitch;
+    if (w == 8)
+      rows_units<uint64_t, NTS>(s0, d0, nr, (uint32_t)(B >> 3), sp, dp);
+    else if (w == 4)
+      rows_units<uint32_t, NTS>(s0, d0, nr, (uint32_t)(B >> 2), sp, dp);
+    else
+      rows_units<T, NTS>(s0, d0, nr, (uint32_t)(B / sizeof(T)), sp, dp);
+    return;
+  }
   uint64_t head = (16u - (uint32_t)(d0 & 15u)) & 15u;
   if (head > B) head = B;
   const uint32_t vpr = (uint32_t)((B - head) >> 4);
@@ -706,12 +764,77 @@ __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const ui
   }
 }
 
+// The nr rows of a strided reduction block, element by element, as one
+// flat range (element q is row q / epr, column q % epr), for pitches that
+// are not multiples of 16.  Same arithmetic and operand order as the vector
+// paths; a compile-time operand count keeps all K loads in flight.
+template <int E, int K, bool NTS>
+__device__ __forceinline__ void reduce_rows_elems(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
+                                                  uint64_t soff, uint64_t doff, uint32_t nr, int avg, float nf) {
+  typedef typename std::conditional<E == kF32, uint32_t, uint16_t>::type T;
+  constexpr int ES = sizeof(T);
+  const uint32_t epr = (uint32_t)(jb.nbytes / ES);
+  const uint32_t n = nr * epr;
+  auto offs = [&](uint32_t q, uint64_t* so, uint64_t* dof) {
+    const uint32_t row = q / epr;
+    const uint64_t col = (uint64_t)(q - row * epr) * ES;
+    *so = row * jb.src_pitch + col;
+    *dof = doff + row * jb.dst_pitch + col;
+  };
+  auto put = [&](uint64_t dof, float acc) {
+    if (avg) acc = acc / nf;
+    const T out = (T)f32_to_elt<E>(acc);
+    for (uint32_t m = 0; m < jb.ndst; ++m) {
+      if (NTS)
+        __builtin_nontemporal_store(out, gptr<T>(ptr[jb.dst0 + m] + dof));
+      else
+        *gptr<T>(ptr[jb.dst0 + m] + dof) = out;
+    }
+  };
+  uint32_t base = 0;
+  if constexpr (K > 0) {
+    // U elements per lane per iteration, all K*U loads in flight together
+    constexpr int U = K >= 4 ? 2 : 4;
+    uint64_t sb[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) sb[t] = ptr[jb.src0 + t] + soff;
+    for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
+      uint64_t so[U], dof[U];
+      T w[K][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) offs(base + threadIdx.x + u * kBlock, &so[u], &dof[u]);
+#pragma unroll
+      for (int t = 0; t < K; ++t)
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[t][u] = __builtin_nontemporal_load(gptr<T>(sb[t] + so[u]));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float acc = elt_to_f32<E>((uint32_t)w[0][u]);
+#pragma unroll
+        for (int t = 1; t < K; ++t) acc = acc + elt_to_f32<E>((uint32_t)w[t][u]);
+        put(dof[u], acc);
+      }
+    }
+  }
+  for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
+    uint64_t so, dof;
+    offs(q, &so, &dof);
+    float acc = 0.0f;
+    for (uint32_t i = 0; i < jb.nsrc; ++i) {
+      const float v = elt_to_f32<E>((uint32_t)*gptr<T>(ptr[jb.src0 + i] + soff + so));
+      acc = (i == 0) ? v : acc + v;
+    }
+    put(dof, acc);
+  }
+}
+
 // Chunk k of a strided reduction block (RedJob with rows > 1): rows
-// [k*rows_per_chunk, ...).  Both pitches are multiples of 16, so every row
+// [k*rows_per_chunk, ...).  When both pitches are multiples of 16, every row
 // has the alignment of the first: a head of up to 15 destination bytes
 // before its first aligned vector, whole vectors, a tail.  The whole
 // vectors of all rows are one flat range; heads and tails are reduced
 // element by element, one row end per lane, in the same operand order.
+// Other pitches go element by element (reduce_rows_elems).
 template <int E, int K, bool NTS>
 __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr, uint64_t k,
                                             int avg, float nf) {
@@ -722,6 +845,10 @@ __device__ __forceinline__ void reduce_rows(const fsdp::RedJob& jb, const uint64
   const uint32_t nr = (uint32_t)(left < jb.rows_per_chunk ? left : jb.rows_per_chunk);
   const uint64_t B = jb.nbytes;
   const uint64_t soff = r0 * jb.src_pitch, doff = r0 * jb.dst_pitch;
+  if ((jb.src_pitch | jb.dst_pitch) & 15u) {
+    reduce_rows_elems<E, K, NTS>(jb, ptr, soff, doff, nr, avg, nf);
+    return;
+  }
   uint64_t head = (16u - (uint32_t)((ptr[jb.dst0] + doff) & 15u)) & 15u;
   if (head > B) head = B;
   const uint32_t vpr = (uint32_t)((B - head) >> 4);

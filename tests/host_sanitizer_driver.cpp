@@ -320,6 +320,10 @@ int main(int argc, char** argv) {
       {{{4097, 8}, {1009, 8}, {5, 64}, {3}}, {}},
       {{{6, 8}, {4, 16, 3}, {5, 3, 8}, {7, 3}, {16}, {64, 1024}, {3, 4, 8}}, {1, 1, 2, 0, 0, 1, 2}},
       {{{96, 64}, {7, 40}, {3}, {33, 128}, {5, 24, 2}, {2, 2048}, {9, 8}}, {1, 1, 0, 1, 1, 1, 1}},
+      // row pitches that are not multiples of 16 bytes (unit-wise blocks)
+      {{{64, 6}, {33, 12, 3}, {9, 20}, {1000, 6}, {3, 2050, 1}, {5, 8, 3}, {2, 1030, 4}, {7, 4, 5}},
+       {1, 1, 1, 1, 1, 1, 1, 1}},
+      {{{33, 4, 3}, {9, 12}, {7, 4, 5}, {100, 12}, {5}}, {1, 1, 1, 1, 0}},
       {{}, {}},
   };
   for (size_t ci = 0; ci < cases.size(); ++ci) {

@@ -567,6 +567,20 @@ def test_strided_blocks_all_steps(S, R, dtype):
     run_nonzero_dims(shapes, dims, S, R, dtype, aligned=True)
 
 
+@pytest.mark.parametrize("S,R,dtype,aligned", [(2, 4, torch.float32, False), (2, 4, torch.bfloat16, True),
+                                               (4, 8, torch.bfloat16, False), (4, 8, torch.float16, True),
+                                               (2, 6, torch.float16, False), (4, 4, torch.float32, True)])
+def test_odd_pitch_blocks_all_steps(S, R, dtype, aligned):
+    """Parameters sharded on dim 1 whose chunk rows have pitches that are
+    not multiples of 16 bytes: short rows and rows of 8-byte units move as
+    unit-wise blocks, long rows of 2-byte units one item per row; every
+    step against the oracle."""
+    shapes = [(64, 6), (33, 12, 3), (9, 20), (1000, 6), (3, 2050, 1), (5, 8, 3), (2, 1030, 4), (7, 4, 5),
+              (33, 4, 3), (9, 12), (100, 12), (5,)]
+    dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in shapes]
+    run_nonzero_dims(shapes, dims, S, R, dtype, aligned)
+
+
 def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):
     note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype} aligned={aligned}")
     # element offsets of the buffers: any, or multiples of 16 bytes
@@ -596,8 +610,9 @@ def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):
     assert ag.guards_intact() and first_mismatch(bits(ag.t), np_bits(ag_o)) == ""
     for i in range(P):
         assert full[i].guards_intact() and np.array_equal(bits(full[i].t), np_bits(xs[i]))
-    gnp = [[to_oracle(g) for g in grads[r]] for r in range(R)]
-    rs_o = [O.rs_copy_in(gnp[g], lay, np_dt) for g in range(R)]
+    # reduction operands in the oracle's value forms (fp16 as numpy float16)
+    gnp = [[to_oracle_values(g) for g in grads[r]] for r in range(R)]
+    rs_o = [O.rs_copy_in(gnp[g], lay, NP16.get(dtype, np.float32)) for g in range(R)]
     dgrads = [grads[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
     rs_in = [Guarded(S * I, dtype, v * (g % 3)) for g in range(R)]
     hp.fsdp_rs_copy_in(shapes, R, S, dgrads, [b.t for b in rs_in], shard_dims=dims)

@@ -86,11 +86,24 @@ def emulate_copy(segs, es, shift):
         k = c - begin[j]
         if rows > 1:
             # the block contract the planner guarantees
-            assert copy == total and sp % 16 == 0 and dp % 16 == 0
+            assert copy == total
             r0 = k * per
             nr = min(per, rows - r0)
             assert nr >= 1 and nr * copy <= CH
             d0, s0 = dst + r0 * dp, src + r0 * sp
+            if (sp | dp) % 16:  # rows_units: W-byte units, one flat range
+                m = s0 | d0 | sp | dp | copy
+                W = 8 if m % 8 == 0 else 4 if m % 4 == 0 else es
+                upr = copy // W
+                # 32-bit offsets from the chunk's first row on both sides
+                assert (nr - 1) * max(sp, dp) + copy < 1 << 32
+                for q in range(nr * upr):
+                    row, col = r0 + q // upr, (q % upr) * W
+                    a, sa = dst + row * dp + col, src + row * sp + col
+                    assert a % W == 0 and sa % W == 0
+                    writes.append((a, a + W, "data", sa, j, row))
+                    reads.append((sa, sa + W, j, row))
+                continue
             head = min((16 - (d0 & 15)) & 15, copy)
             vpr = (copy - head) >> 4
             tail = head + 16 * vpr
@@ -213,12 +226,23 @@ def emulate_reduce(jobs, ptr, shift, es=4):
         nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, per = jobs[j]
         k = c - begin[j]
         if rows > 1:
-            assert data == nbytes and sp % 16 == 0 and dp % 16 == 0
+            assert data == nbytes
             assert len({ptr[dst0 + m] & 15 for m in range(ndst)}) == 1
             r0 = k * per
             nr = min(per, rows - r0)
             assert nr >= 1 and nr * nbytes <= CH
             soff, doff = r0 * sp, r0 * dp
+            if (sp | dp) % 16:  # reduce_rows_elems: element by element
+                epr = nbytes // es
+                for q in range(nr * epr):
+                    row, col = r0 + q // epr, (q % epr) * es
+                    for t in range(nsrc):
+                        sa = ptr[src0 + t] + row * sp + col
+                        reads.append((sa, sa + es, j, t, row))
+                    for m in range(ndst):
+                        a = ptr[dst0 + m] + row * dp + col
+                        writes.append((a, a + es, "data", j, m, row))
+                continue
             head = min((16 - ((ptr[dst0] + doff) & 15)) & 15, nbytes)
             vpr = (nbytes - head) >> 4
             tail = head + 16 * vpr
@@ -343,15 +367,31 @@ def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
     return segs
 
 
-def block_ok(sp, dp, row_bytes, rows, shift):
-    """When the planner emits one strided block instead of one item per row."""
-    return rows >= 2 and 0 < row_bytes <= (1 << shift) and sp % 16 == 0 and dp % 16 == 0
+SHORT_ROW = 1024
+
+
+def copy_block_ok(src, dst, sp, dp, row_bytes, rows, shift):
+    """When the planner emits one strided copy block instead of one item
+    per row: the rows fit a chunk, and either both pitches are multiples of
+    16 (vector rows) or the rows are short or move in 8-byte units."""
+    if not (rows >= 2 and 0 < row_bytes <= (1 << shift)):
+        return False
+    if sp % 16 == 0 and dp % 16 == 0:
+        return True
+    if ((1 << shift) // row_bytes) * max(sp, dp) >= 1 << 32:  # the kernel's 32-bit offsets
+        return False
+    return row_bytes <= SHORT_ROW or (src | dst | sp | dp | row_bytes) % 8 == 0
+
+
+def reduce_block_ok(sp, dp, row_bytes, rows, shift):
+    """The same for a reduction block (other pitches go element by element)."""
+    return rows >= 2 and 0 < row_bytes <= (1 << shift) and ((sp % 16 == 0 and dp % 16 == 0) or row_bytes <= SHORT_ROW)
 
 
 def push_rows(segs, src, dst, row_bytes, rows, sp, dp, shift):
     if row_bytes == 0 or rows == 0:
         return
-    if block_ok(sp, dp, row_bytes, rows, shift):
+    if copy_block_ok(src, dst, sp, dp, row_bytes, rows, shift):
         segs.append((src, dst, row_bytes, row_bytes, rows, sp, dp, (1 << shift) // row_bytes))
     else:
         segs.extend((src + r * sp, dst + r * dp, row_bytes, row_bytes) for r in range(rows))
@@ -483,7 +523,8 @@ def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None, shift=
             out0 = out_addr(g) + L["in_off"][i] * es
             pitch = L["dk"][i] * L["inner"][i] * es
             srcs = [grad_addr(d * S + t, i) for t in range(S)]
-            if L["padded"][i] == L["outer"][i] * run and block_ok(pitch, run * es, run * es, L["outer"][i], shift):
+            if L["padded"][i] == L["outer"][i] * run and reduce_block_ok(pitch, run * es, run * es, L["outer"][i],
+                                                                          shift):
                 src0 = len(ptr)
                 ptr += [a + src_off for a in srcs]
                 dst0 = len(ptr)
@@ -745,3 +786,60 @@ def test_misaligned_strided_reduce_jobs_cover_exactly(S, es, shift):
         jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims, shift)
         assert any(len(jb) == 10 for jb in jobs)
         check_reduce(jobs, ptr, shift, es)
+
+
+# parameters whose dim-k chunks have row pitches that are not multiples of
+# 16 bytes: short rows (element-unit blocks), rows long enough for 8-byte
+# units, and long rows of narrow units (one item per row)
+ODD_PITCH_SHAPES = [(64, 6), (33, 12, 3), (9, 20), (1000, 6), (3, 2050, 1), (5, 8, 3), (2, 1030, 4), (7, 4, 5)]
+
+
+@pytest.mark.parametrize("S", [2, 4])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shift", (9, 14))
+def test_odd_pitch_blocks_cover_exactly(S, es, shift):
+    """Copy blocks and RS copy-reduce blocks of rows whose pitches are not
+    multiples of 16 bytes: the rows move in 8-, 4- or element-sized units
+    (every unit aligned to its width), every row byte written once, reads
+    inside the rows; buffers at element offsets."""
+    shapes = ODD_PITCH_SHAPES
+    dims = [1 if sh[1] % S == 0 else 0 for sh in shapes]
+    rng = np.random.default_rng(S * 17 + es + shift)
+    base = 1 << 32
+    ag = base + es * int(rng.integers(0, 9))
+    full = {i: base + (1 << 30) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = ag_copy_out_segs(shapes, S, es, ag, lambda i: full[i], dims, shift)
+    odd = [sg for sg in segs if len(sg) == 8 and (sg[5] | sg[6]) % 16]
+    assert odd, "no odd-pitch block planned"
+    check_copy(segs, es, shift)
+    grads = {i: (1 << 40) + i * (1 << 24) + es * int(rng.integers(0, 9)) for i in range(len(shapes))}
+    segs = rs_copy_in_segs(shapes, S, es, lambda i: grads[i], (1 << 44) + es * 3, dims, shift)
+    assert any(len(sg) == 8 and (sg[5] | sg[6]) % 16 for sg in segs)
+    check_copy(segs, es, shift)
+    R = 2 * S
+    gr = {(g, i): (1 << 40) + (g * 64 + i) * (1 << 24) + es * int(rng.integers(0, 8))
+          for g in range(R) for i in range(len(shapes))}
+    outs = {g: (1 << 46) + g * (1 << 26) + es * int(rng.integers(0, 8)) for g in range(R)}
+    jobs, ptr = rs_copy_reduce_jobs(shapes, R, S, es, lambda g, i: gr[(g, i)], lambda g: outs[g], dims, shift)
+    assert any(len(jb) == 10 and (jb[7] | jb[8]) % 16 for jb in jobs)
+    check_reduce(jobs, ptr, shift, es)
+
+
+def test_odd_pitch_unit_widths():
+    """The unit width the kernel picks for a chunk of odd-pitch rows: the
+    widest of 8, 4 and the element size that divides both first-row
+    addresses, both pitches and the row length."""
+    def unit(es, s0, d0, sp, dp, row):
+        m = s0 | d0 | sp | dp | row
+        return 8 if m % 8 == 0 else 4 if m % 4 == 0 else es
+    assert unit(4, 1 << 20, 8, 24, 40, 8) == 8
+    assert unit(4, 1 << 20, 4, 24, 40, 8) == 4
+    assert unit(2, 2, 0, 24, 40, 8) == 2
+    assert unit(2, 0, 0, 36, 18, 18) == 2
+    # the planner keeps long rows of narrow units one item per row
+    assert not copy_block_ok(0, 2, 4100, 2050, 2050, 3, 14)
+    assert copy_block_ok(0, 8, 8200, 4104, 4104, 3, 14)
+    assert copy_block_ok(2, 0, 36, 18, 18, 100, 14)
+    # a chunk's rows must lie within 4 GiB of its first row (32-bit offsets)
+    assert not copy_block_ok(0, 0, 1 << 20 | 4, 4, 4, 100, 14) and copy_block_ok(0, 0, (1 << 18) | 4, 4, 4, 100, 14)
+    assert not reduce_block_ok(8200, 4104, 4104, 3, 14) and reduce_block_ok(36, 18, 18, 100, 14)
