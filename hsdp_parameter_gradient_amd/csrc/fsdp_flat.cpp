@@ -464,6 +464,29 @@ void push_rows(std::vector<fsdp::CopySeg>& segs, uint64_t src, uint64_t dst, uin
     segs.push_back({src + r * src_pitch, dst + r * dst_pitch, row_bytes, row_bytes});
 }
 
+// Short rows of dim-k chunks: every cache line of the full tensor holds
+// pieces of several shard ranks' rows.  The S ranks' items for the same rows
+// are emitted next to each other, one item per chunk of rows, so that the
+// XCD-aware chunk order runs them back to back on one XCD, whose L2 then
+// merges the partial-line reads and writes.
+constexpr uint64_t kInterleaveRow = 256;
+
+bool interleave_rows(uint64_t row_bytes, uint64_t rows) {
+  return row_bytes > 0 && row_bytes < kInterleaveRow && rows >= 2;
+}
+
+// The S ranks' rows of one parameter: base[s] = (first source row, first
+// destination row) of rank s; the same row length, row count and pitches.
+void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<std::pair<uint64_t, uint64_t>>& base,
+                           uint64_t row_bytes, uint64_t rows, uint64_t src_pitch, uint64_t dst_pitch) {
+  const uint64_t per = (uint64_t(1) << fsdp::tuning().copy_shift) / row_bytes;
+  for (uint64_t r0 = 0; r0 < rows; r0 += per) {
+    const uint64_t nr = std::min(per, rows - r0);
+    for (const auto& b : base)
+      push_rows(segs, b.first + r0 * src_pitch, b.second + r0 * dst_pitch, row_bytes, nr, src_pitch, dst_pitch);
+  }
+}
+
 // Plan the segmented copy over `segs`.
 int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
   // the kernel's chunk search needs every item non-empty
@@ -670,13 +693,24 @@ int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     const int64_t nb = L.numel[i] * es;
     if ((rc = check_ptr(full[i], nb, es, "full", i))) return rc;
     outs.push_back({(uint64_t)full[i], (uint64_t)full[i] + (uint64_t)nb, i});
+    // rank s's chunk: outer runs of row_len*inner elements, dense in the
+    // slice, at stride dk*inner in the full parameter
+    auto src_of = [&](int32_t s) { return (uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es); };
+    auto dst_of = [&](int32_t s) {
+      return (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
+    };
+    const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
+    if (L.outer[i] > 1 && interleave_rows((uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es), (uint64_t)L.outer[i])) {
+      // a dim-k chunk (every rank the same run) of short rows
+      const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      std::vector<std::pair<uint64_t, uint64_t>> base;
+      for (int32_t s = 0; s < S; ++s) base.push_back({src_of(s), dst_of(s)});
+      push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], row, pitch);
+      continue;
+    }
     for (int32_t s = 0; s < S; ++s) {
-      // rank s's chunk: outer runs of row_len*inner elements, dense in the
-      // slice, at stride dk*inner in the full parameter
       const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
-      push_rows(segs, (uint64_t)ag + (uint64_t)((s * L.I + L.in_off[i]) * es),
-                (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es), (uint64_t)(run * es),
-                (uint64_t)L.outer[i], (uint64_t)(run * es), (uint64_t)(L.dk[i] * L.inner[i] * es));
+      push_rows(segs, src_of(s), dst_of(s), (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(run * es), pitch);
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
@@ -732,11 +766,25 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
           segs.push_back({run ? src : 0, d0, (uint64_t)(run * es), (uint64_t)(L.padded[i] * es)});
           continue;
         }
+        if (interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i])) continue;  // below
         push_rows(segs, src, d0, (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es),
                   (uint64_t)(run * es));
         if (L.padded[i] > data)
           segs.push_back({0, d0 + (uint64_t)(data * es), 0, (uint64_t)((L.padded[i] - data) * es)});
       }
+    }
+  }
+  // dim-k chunks of short rows (every rank the same run, no padding): the S
+  // ranks' pieces of the same rows next to each other
+  for (int32_t g = 0; g < R; ++g) {
+    for (int32_t i = 0; i < P; ++i) {
+      const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      if (L.padded[i] == 0 || L.outer[i] == 1 || !interleave_rows(row, (uint64_t)L.outer[i])) continue;
+      std::vector<std::pair<uint64_t, uint64_t>> base;
+      for (int32_t s = 0; s < S; ++s)
+        base.push_back({(uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es),
+                        (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es)});
+      push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es), row);
     }
   }
   if ((rc = check_overlap(outs, ins))) return rc;
@@ -831,6 +879,31 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
   // sum over its shard group of chunk s of gradient i, then zeros
   std::vector<fsdp::RedJob> jobs;
   std::vector<uint64_t> ptrs;
+  const uint64_t CH = uint64_t(1) << fsdp::tuning().reduce_shift;
+  // rows [r0, r0 + nr) of rank g's chunk of parameter i (runs of `run`
+  // elements, no tail) as one strided job, or one plain job for one row
+  auto push_block = [&](int32_t g, int32_t i, uint64_t r0, uint64_t nr) {
+    const int32_t d = g / S, s = g % S;
+    const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+    const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
+    const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es) + r0 * pitch;
+    fsdp::RedJob jb;
+    jb.nbytes = jb.data_bytes = (uint64_t)(run * es);
+    jb.src0 = (uint32_t)ptrs.size();
+    jb.nsrc = (uint32_t)S;
+    for (int32_t t = 0; t < S; ++t) ptrs.push_back((uint64_t)grads[(size_t)(d * S + t) * P + i] + src_off);
+    jb.dst0 = (uint32_t)ptrs.size();
+    jb.ndst = 1;
+    ptrs.push_back((uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es) + r0 * jb.nbytes);
+    if (nr > 1) {
+      jb.rows = nr;
+      jb.src_pitch = pitch;
+      jb.dst_pitch = jb.nbytes;
+      jb.rows_per_chunk = CH / jb.nbytes;
+    }
+    jobs.push_back(jb);
+  };
+  std::vector<uint8_t> interleaved((size_t)P, 0);
   for (int32_t g = 0; g < R; ++g) {
     const int32_t d = g / S, s = g % S;
     for (int32_t i = 0; i < P; ++i) {
@@ -847,20 +920,12 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
       const bool block = L.padded[i] == L.outer[i] * run &&
                          reduce_block_ok(pitch, (uint64_t)(run * es), (uint64_t)(run * es), (uint64_t)L.outer[i],
                                          fsdp::tuning().reduce_shift);
+      if (block && interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i])) {
+        interleaved[(size_t)i] = 1;  // below, with the other ranks of the group
+        continue;
+      }
       if (block) {
-        fsdp::RedJob jb;
-        jb.nbytes = jb.data_bytes = (uint64_t)(run * es);
-        jb.src0 = (uint32_t)ptrs.size();
-        jb.nsrc = (uint32_t)S;
-        for (int32_t t = 0; t < S; ++t) ptrs.push_back((uint64_t)grads[(size_t)(d * S + t) * P + i] + src_off);
-        jb.dst0 = (uint32_t)ptrs.size();
-        jb.ndst = 1;
-        ptrs.push_back(out0);
-        jb.rows = (uint64_t)L.outer[i];
-        jb.src_pitch = pitch;
-        jb.dst_pitch = (uint64_t)(run * es);
-        jb.rows_per_chunk = (uint64_t(1) << fsdp::tuning().reduce_shift) / jb.nbytes;
-        jobs.push_back(jb);
+        push_block(g, i, 0, (uint64_t)L.outer[i]);
         continue;
       }
       for (int64_t o = 0; o < L.outer[i]; ++o) {
@@ -878,6 +943,18 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
         ptrs.push_back(out0 + (uint64_t)(o * run * es));
         if (jb.nbytes) jobs.push_back(jb);
       }
+    }
+  }
+  // short rows (every rank of a dim-k chunk the same run): the S ranks of a
+  // shard group read pieces of the same gradient lines, so their jobs for
+  // the same rows go next to each other, one job per chunk of rows
+  for (int32_t d = 0; d < R / S; ++d) {
+    for (int32_t i = 0; i < P; ++i) {
+      if (!interleaved[(size_t)i]) continue;
+      const uint64_t rows = (uint64_t)L.outer[i];
+      const uint64_t per = CH / (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      for (uint64_t r0 = 0; r0 < rows; r0 += per)
+        for (int32_t s = 0; s < S; ++s) push_block(d * S + s, i, r0, std::min(per, rows - r0));
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");

@@ -397,14 +397,37 @@ def push_rows(segs, src, dst, row_bytes, rows, sp, dp, shift):
         segs.extend((src + r * sp, dst + r * dp, row_bytes, row_bytes) for r in range(rows))
 
 
+INTERLEAVE_ROW = 256
+
+
+def interleave_rows(row_bytes, rows):
+    """Short rows of a dim-k chunk: the S ranks' items of the same rows
+    are emitted next to each other, one item per chunk of rows."""
+    return 0 < row_bytes < INTERLEAVE_ROW and rows >= 2
+
+
+def push_rows_interleaved(segs, base, row_bytes, rows, sp, dp, shift):
+    per = (1 << shift) // row_bytes
+    for r0 in range(0, rows, per):
+        nr = min(per, rows - r0)
+        for src, dst in base:
+            push_rows(segs, src + r0 * sp, dst + r0 * dp, row_bytes, nr, sp, dp, shift)
+
+
 def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None, shift=14):
     L = layout(shapes, S, dims)
     segs = []
     for i in range(len(shapes)):
+        src = [ag + (s * L["I"] + L["in_off"][i]) * es for s in range(S)]
+        dst = [full_addr(i) + L["ro"][i][s] * L["inner"][i] * es for s in range(S)]
+        pitch = L["dk"][i] * L["inner"][i] * es
+        row = L["rl"][i][0] * L["inner"][i] * es
+        if L["outer"][i] > 1 and interleave_rows(row, L["outer"][i]):
+            push_rows_interleaved(segs, list(zip(src, dst)), row, L["outer"][i], row, pitch, shift)
+            continue
         for s in range(S):
             run = L["rl"][i][s] * L["inner"][i]
-            push_rows(segs, ag + (s * L["I"] + L["in_off"][i]) * es, full_addr(i) + L["ro"][i][s] * L["inner"][i] * es,
-                      run * es, L["outer"][i], run * es, L["dk"][i] * L["inner"][i] * es, shift)
+            push_rows(segs, src[s], dst[s], run * es, L["outer"][i], run * es, pitch, shift)
     return segs
 
 
@@ -422,10 +445,19 @@ def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None, shift=14):
             if L["outer"][i] == 1:
                 segs.append((src if run else 0, d0, run * es, L["padded"][i] * es))
                 continue
+            if interleave_rows(run * es, L["outer"][i]):
+                continue  # below
             push_rows(segs, src, d0, run * es, L["outer"][i], L["dk"][i] * L["inner"][i] * es, run * es, shift)
             data = L["outer"][i] * run
             if L["padded"][i] > data:
                 segs.append((0, d0 + data * es, 0, (L["padded"][i] - data) * es))
+    for i in range(len(shapes)):
+        row = L["rl"][i][0] * L["inner"][i] * es
+        if L["padded"][i] == 0 or L["outer"][i] == 1 or not interleave_rows(row, L["outer"][i]):
+            continue
+        base = [(grad_addr(i) + L["ro"][i][s] * L["inner"][i] * es, rs_in_addr + (s * L["I"] + L["in_off"][i]) * es)
+                for s in range(S)]
+        push_rows_interleaved(segs, base, row, L["outer"][i], L["dk"][i] * L["inner"][i] * es, row, shift)
     return segs
 
 
@@ -513,24 +545,35 @@ def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None, shift=
     per (rank, parameter, run of the chunk)."""
     L = layout(shapes, S, dims)
     jobs, ptr = [], []
+
+    def push_block(g, i, r0, nr):
+        d, s = divmod(g, S)
+        run = L["rl"][i][s] * L["inner"][i]
+        pitch = L["dk"][i] * L["inner"][i] * es
+        src_off = L["ro"][i][s] * L["inner"][i] * es + r0 * pitch
+        src0 = len(ptr)
+        ptr.extend(grad_addr(d * S + t, i) + src_off for t in range(S))
+        dst0 = len(ptr)
+        ptr.append(out_addr(g) + L["in_off"][i] * es + r0 * run * es)
+        if nr > 1:
+            jobs.append((run * es, run * es, src0, S, dst0, 1, nr, pitch, run * es, (1 << shift) // (run * es)))
+        else:
+            jobs.append((run * es, run * es, src0, S, dst0, 1))
+
+    interleaved = set()
     for g in range(R):
         d, s = divmod(g, S)
         for i, sh in enumerate(shapes):
             if L["padded"][i] == 0:
                 continue
             run = L["rl"][i][s] * L["inner"][i]
-            src_off = L["ro"][i][s] * L["inner"][i] * es
-            out0 = out_addr(g) + L["in_off"][i] * es
             pitch = L["dk"][i] * L["inner"][i] * es
-            srcs = [grad_addr(d * S + t, i) for t in range(S)]
             if L["padded"][i] == L["outer"][i] * run and reduce_block_ok(pitch, run * es, run * es, L["outer"][i],
                                                                           shift):
-                src0 = len(ptr)
-                ptr += [a + src_off for a in srcs]
-                dst0 = len(ptr)
-                ptr.append(out0)
-                jobs.append((run * es, run * es, src0, S, dst0, 1, L["outer"][i], pitch, run * es,
-                             (1 << shift) // (run * es)))
+                if interleave_rows(run * es, L["outer"][i]):
+                    interleaved.add(i)
+                else:
+                    push_block(g, i, 0, L["outer"][i])
                 continue
             for o in range(L["outer"][i]):
                 last = o + 1 == L["outer"][i]
@@ -542,6 +585,12 @@ def rs_copy_reduce_jobs(shapes, R, S, es, grad_addr, out_addr, dims=None, shift=
                 nbytes = ((L["padded"][i] - o * run) if last else run) * es
                 if nbytes:
                     jobs.append((nbytes, run * es, src0, S, dst0, 1))
+    for d in range(R // S):
+        for i in sorted(interleaved):
+            per = (1 << shift) // (L["rl"][i][0] * L["inner"][i] * es)
+            for r0 in range(0, L["outer"][i], per):
+                for s in range(S):
+                    push_block(d * S + s, i, r0, min(per, L["outer"][i] - r0))
     return jobs, ptr
 
 
