@@ -112,6 +112,8 @@ class _BucketArg:
         self._ndim = (c_int32 * max(P, 1))(*[len(s) for s in self.shapes])
         self._shape = (c_int64 * max(len(flat), 1))(*flat)
         self.dims = [int(shard_dim)] * P if shard_dims is None else [int(k) for k in shard_dims]
+        if len(self.dims) != P:
+            raise ValueError(f"shard_dims: {len(self.dims)} entries for {P} parameters")
         self._dims = (c_int32 * max(P, 1))(*self.dims) if shard_dims is not None else None
         self.struct = _Bucket(P, self._ndim, self._shape, int(shard_dim), self._dims)
         self.ref = ctypes.byref(self.struct)

@@ -207,6 +207,15 @@ def test_binding_checks_buffer_sizes():
         hp.fsdp_ag_copy_in([(4,)], 1, [x], x)
 
 
+def test_binding_checks_shard_dims_length():
+    """One shard dim per parameter: a shorter or longer list is refused
+    (the C side reads exactly n_params entries)."""
+    for dims in ([1], [0, 1, 0]):
+        with pytest.raises(ValueError, match="shard_dims"):
+            hp.fsdp_bucket_layout([(4, 8), (6, 8)], 2, shard_dims=dims)
+    assert hp.fsdp_bucket_layout([(4, 8), (6, 8)], 2, shard_dims=[1, 0]).I == 4 * 4 + 3 * 8
+
+
 def test_plain_c_consumer_of_the_header(tmp_path):
     """A C program that includes only include/fsdp_flat.h, links the library
     and calls the host-only entry points (and two argument errors) gets the
