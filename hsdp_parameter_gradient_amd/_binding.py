@@ -193,6 +193,12 @@ def _ptr_array(ptrs: Sequence[int]):
     return (c_void_p * max(len(ptrs), 1))(*[p or None for p in ptrs])
 
 
+def _op_code(op: str) -> int:
+    if op not in _OPS:
+        raise ValueError(f"reduce op {op!r}: expected {SUM!r} or {AVG!r}")
+    return _op_code(op)
+
+
 def _dtype_code(dtype: torch.dtype) -> int:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
@@ -311,6 +317,7 @@ def _reduce_dtype(tensors, what) -> torch.dtype:
 
 
 def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out, shard_dims=None):
+    opc = _op_code(op)
     b = _BucketArg(shapes, 0, shard_dims)
     lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     R, S = int(rank_size), int(shard_size)
@@ -319,11 +326,12 @@ def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out, s
     dt = _reduce_dtype(rs_in, "rs_in")
     iarr = _ptr_array([_dev(rs_in[g], f"rs_in[{g}]", S * lay.I, dt) for g in range(R)])
     oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, dt) for g in range(R)])
-    return _Call("fsdp_rs_reduce", (b.ref, R, S, int(dp_size), _OPS[op], _dtype_code(dt), iarr, oarr),
+    return _Call("fsdp_rs_reduce", (b.ref, R, S, int(dp_size), opc, _dtype_code(dt), iarr, oarr),
                  (b, iarr, oarr, tuple(rs_in), tuple(rs_out)))
 
 
 def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims=None):
+    opc = _op_code(op)
     b = _BucketArg(shapes, 0, shard_dims)
     lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
     R, S, P = int(rank_size), int(shard_size), len(b.shapes)
@@ -333,11 +341,12 @@ def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_o
     garr = _ptr_array([_dev(grads[g * P + i], f"grads[{g * P + i}]", _numel(b.shapes[i]), dt)
                        for g in range(R) for i in range(P)])
     oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, dt) for g in range(R)])
-    return _Call("fsdp_rs_copy_reduce", (b.ref, R, S, int(dp_size), _OPS[op], _dtype_code(dt), garr, oarr),
+    return _Call("fsdp_rs_copy_reduce", (b.ref, R, S, int(dp_size), opc, _dtype_code(dt), garr, oarr),
                  (b, garr, oarr, tuple(grads), tuple(rs_out)))
 
 
 def _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused):
+    opc = _op_code(op)
     n = len(seg_numel)
     sizes = (c_int64 * max(n, 1))(*[int(v) for v in seg_numel])
     R = int(rank_size)
@@ -346,7 +355,7 @@ def _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused):
     dt = _reduce_dtype(fused, "fused")
     _, F = fsdp_fused_layout(seg_numel, dt.itemsize)
     arr = _ptr_array([_dev(fused[g], f"fused[{g}]", F, dt) for g in range(R)])
-    return _Call("fsdp_fused_ar", (n, sizes, R, int(shard_size), int(dp_size), _OPS[op], _dtype_code(dt), arr),
+    return _Call("fsdp_fused_ar", (n, sizes, R, int(shard_size), int(dp_size), opc, _dtype_code(dt), arr),
                  (sizes, arr, tuple(fused)))
 
 

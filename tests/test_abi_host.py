@@ -207,6 +207,13 @@ def test_binding_checks_buffer_sizes():
         hp.fsdp_ag_copy_in([(4,)], 1, [x], x)
 
 
+def test_binding_refuses_unknown_ops():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4)
+    with pytest.raises(ValueError, match="reduce op"):
+        hp.fsdp_fused_ar([4], 2, 1, 2, "max", [x, x])
+
+
 def test_binding_checks_shard_dims_length():
     """One shard dim per parameter: a shorter or longer list is refused
     (the C side reads exactly n_params entries)."""
