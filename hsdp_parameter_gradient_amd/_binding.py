@@ -196,7 +196,7 @@ def _ptr_array(ptrs: Sequence[int]):
 def _op_code(op: str) -> int:
     if op not in _OPS:
         raise ValueError(f"reduce op {op!r}: expected {SUM!r} or {AVG!r}")
-    return _op_code(op)
+    return _OPS[op]
 
 
 def _dtype_code(dtype: torch.dtype) -> int:

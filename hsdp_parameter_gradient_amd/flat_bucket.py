@@ -130,12 +130,17 @@ class FlatBucket:
             st.append("fused_ar")
         return st
 
+    def _call(self, step: str):
+        if self._calls is None:
+            raise RuntimeError("FlatBucket: call bind(shards, grads) before running its steps")
+        return self._calls[step]
+
     def run(self, step: str, stream=None) -> None:
-        self._calls[step](stream)
+        self._call(step)(stream)
 
     def step(self, stream=None, fused_rs: bool = False) -> None:
         for name in self.steps(fused_rs):
-            self._calls[name](stream)
+            self._call(name)(stream)
 
 
 class FusedGroup:
@@ -147,14 +152,20 @@ class FusedGroup:
 
     def __init__(self, buckets: Sequence[Sequence[Sequence[int]]], rank_size: int, shard_size: int,
                  param_dtype: torch.dtype = torch.bfloat16, op: str = B.AVG, device: str = "cuda",
-                 grad_dtype: torch.dtype = torch.float32):
+                 grad_dtype: torch.dtype = torch.float32,
+                 shard_dims: Optional[Sequence[Optional[Sequence[int]]]] = None):
+        """buckets: the parameter shapes of each bucket; shard_dims: per
+        bucket, one shard dim per parameter (or None for dim 0)."""
         self.R, self.S = int(rank_size), int(shard_size)
-        seg = [B.fsdp_bucket_layout(b, self.S).I for b in buckets]
+        dims = list(shard_dims) if shard_dims is not None else [None] * len(buckets)
+        if len(dims) != len(buckets):
+            raise ValueError(f"shard_dims: {len(dims)} entries for {len(buckets)} buckets")
+        seg = [B.fsdp_bucket_layout(b, self.S, shard_dims=d).I for b, d in zip(buckets, dims)]
         _, F = B.fsdp_fused_layout(seg, grad_dtype.itemsize)
         self.seg_numel = seg
         self.fused = [torch.zeros(F, dtype=grad_dtype, device=torch.device(device)) for _ in range(self.R)]
         self.buckets = [FlatBucket(b, rank_size, shard_size, param_dtype, op, device, seg, k, grad_dtype,
-                                   fused=self.fused) for k, b in enumerate(buckets)]
+                                   shard_dims=dims[k], fused=self.fused) for k, b in enumerate(buckets)]
         self.op = op
         self.D = self.R // self.S
         self.do_ar = self.buckets[0].do_ar if self.buckets else False
@@ -162,6 +173,9 @@ class FusedGroup:
 
     def bind(self, shards: Sequence[Sequence[torch.Tensor]], grads: Sequence[Sequence[torch.Tensor]]) -> "FusedGroup":
         """shards[k] and grads[k]: bucket k's inputs, as FlatBucket.bind."""
+        if len(shards) != len(self.buckets) or len(grads) != len(self.buckets):
+            raise ValueError(f"bind: {len(shards)} shard lists and {len(grads)} gradient lists "
+                             f"for {len(self.buckets)} buckets")
         for fb, sh, gr in zip(self.buckets, shards, grads):
             fb.bind(sh, gr)
         self._ar = B.prepare("fsdp_fused_ar", self.seg_numel, self.R, self.S, self.D, self.op, self.fused)
@@ -169,6 +183,8 @@ class FusedGroup:
 
     def step(self, stream=None, fused_rs: bool = False) -> None:
         """Every bucket's AG and RS, then the one fused AR."""
+        if self._ar is None:
+            raise RuntimeError("FusedGroup: call bind(shards, grads) before step()")
         for fb in self.buckets:
             for name in fb.steps(fused_rs):
                 if name != "fused_ar":

@@ -212,6 +212,12 @@ def test_binding_refuses_unknown_ops():
     x = torch.zeros(4)
     with pytest.raises(ValueError, match="reduce op"):
         hp.fsdp_fused_ar([4], 2, 1, 2, "max", [x, x])
+    # the valid ops get past the op check to the buffer checks
+    from hsdp_parameter_gradient_amd import _binding as B
+    assert (B._op_code("sum"), B._op_code("avg")) == (0, 1)
+    for op in ("sum", "avg"):
+        with pytest.raises(ValueError, match="device tensor"):
+            hp.fsdp_fused_ar([4], 2, 1, 2, op, [x, x])
 
 
 def test_binding_checks_shard_dims_length():
@@ -242,3 +248,19 @@ def test_plain_c_consumer_of_the_header(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_flat_bucket_and_group_need_bind():
+    """Steps before bind() and mismatched bind() lists are refused with a
+    clear error (the checks run on the host, before any device call)."""
+    torch = pytest.importorskip("torch")
+    fb = hp.FlatBucket.__new__(hp.FlatBucket)
+    fb._calls = None
+    with pytest.raises(RuntimeError, match="bind"):
+        fb.run("ag_copy_in")
+    grp = hp.FusedGroup.__new__(hp.FusedGroup)
+    grp.buckets, grp._ar = [object(), object()], None
+    with pytest.raises(ValueError, match="bind"):
+        grp.bind([[]], [[], []])
+    with pytest.raises(RuntimeError, match="bind"):
+        grp.step()

@@ -849,3 +849,51 @@ def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
             assert m == "", f"rep {rep} fused rank {g}: {m}"
         for k, fb in enumerate(grp.buckets):
             assert np.array_equal(bits(fb.full[0]), bits(params[k].reshape(-1)))
+
+
+def test_fused_group_with_shard_dims():
+    """A FusedGroup whose buckets shard some parameters on dim 1: every
+    bucket's RS output lands in its segment of the shared fused buffers and
+    one AR covers them; the buffers against the oracle's RS copy-in, RS,
+    fused layout and fused AR composed per bucket."""
+    R, S = 8, 4
+    buckets = [[(64, 48), (7,)], [(33, 16, 3)], [(100,)]]
+    dims = [[1, 0], [1], None]
+    note("[parity] FusedGroup with shard dims")
+    grp = hp.FusedGroup(buckets, R, S, torch.bfloat16, op=O.AVG, shard_dims=dims)
+    flat = [sh for b in buckets for sh in b]
+    w = W.Workload("fused_group_dims", 31, R, S, tuple(flat), torch.bfloat16, ("normal", 0.02), ("normal", 1.0),
+                   ("avg",), W.ALL_STEPS)
+    params, g_cpu = W.params(w), W.grads(w)
+    j, shards, grads, segs_o = 0, [], [], [[] for _ in range(R)]
+    for k, (b, d) in enumerate(zip(buckets, dims)):
+        P = len(b)
+        shards.append(grp.buckets[k].shard_views([p.cuda() for p in params[j:j + P]]))
+        grads.append([g_cpu[g][j + i].cuda().reshape(-1) for g in range(R) for i in range(P)])
+        lay = O.bucket_layout(b, S, shard_dims=d)
+        rs_in = [O.rs_copy_in([g_cpu[g][j + i].numpy() for i in range(P)], lay) for g in range(R)]
+        for g, out in enumerate(O.rs_reduce(rs_in, lay.I, R, S, O.AVG)):
+            segs_o[g].append(out)
+        j += P
+    grp.bind(shards, grads)
+    offs, F = O.fused_layout(grp.seg_numel)
+    fused_o = []
+    for g in range(R):
+        buf = np.zeros(F, np.float32)
+        for o, seg in zip(offs, segs_o[g]):
+            buf[o:o + seg.size] = seg
+        fused_o.append(buf)
+    want = O.fused_ar(fused_o, R, S, O.AVG)
+    for fused_rs in (False, True):
+        for f in grp.fused:
+            f.zero_()
+        grp.step(fused_rs=fused_rs)
+        torch.cuda.synchronize()
+        for g in range(R):
+            m = first_mismatch(bits(grp.fused[g]), np_bits(want[g]))
+            assert m == "", f"fused_rs={fused_rs} rank {g}: {m}"
+        j = 0
+        for k, b in enumerate(buckets):
+            for i in range(len(b)):
+                assert np.array_equal(bits(grp.buckets[k].full[i]), bits(params[j + i].reshape(-1)))
+            j += len(b)
