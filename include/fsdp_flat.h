@@ -55,6 +55,12 @@
  *     plan without validating or planning again (its result cannot differ).
  *     At most 256 plans and 256 MiB of tables; evicting waits for every
  *     device that holds a cached table.  fsdp_release_cache() frees them all.
+ *   - A call whose plan is cached only enqueues one kernel launch, so it can
+ *     be captured into a HIP graph and replayed (the graph reads the
+ *     buffers' contents at replay time).  The first call of a signature
+ *     allocates and uploads its table and evicting synchronizes devices:
+ *     neither may happen under capture, so issue each call once before
+ *     capturing it.
  *   - Thread safe; calls that overlap in time on different streams must not
  *     share output buffers.
  */

@@ -897,3 +897,40 @@ def test_fused_group_with_shard_dims():
             for i in range(len(b)):
                 assert np.array_equal(bits(grp.buckets[k].full[i]), bits(params[j + i].reshape(-1)))
             j += len(b)
+
+
+@pytest.mark.parametrize("fused_rs", [False, True])
+def test_hip_graph_capture_of_cached_plans(fused_rs):
+    """Once a call signature's plan is cached, issuing it only launches a
+    kernel, so a whole pass can be captured in a HIP graph
+    (torch.cuda.graph) and replayed: every replay, with new gradient values
+    written eagerly between replays, matches the oracle."""
+    import dataclasses
+    w = W.scaled(W.HSDP_BLOCK, [(97, 64), (32, 64), (130, 32), (33, 128), (64,), (3,)])
+    R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+    note(f"[parity] HIP graph capture fused_rs={fused_rs}")
+    params, g_cpu = W.params(w), W.grads(w)
+    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG)
+    grads_dev = [g_cpu[g][i].cuda().reshape(-1) for g in range(R) for i in range(P)]
+    fb.bind(fb.shard_views([p.cuda() for p in params]), grads_dev)
+    fb.step(fused_rs=fused_rs)  # plans cached (tables uploaded) before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fb.step(fused_rs=fused_rs)
+    for rep in range(3):
+        new = W.grads(dataclasses.replace(w, number=w.number + 100 + rep))
+        for t, v in zip(grads_dev, [new[g][i].reshape(-1) for g in range(R) for i in range(P)]):
+            t.copy_(v)
+        for f in fb.full:
+            f.view(torch.int16).fill_(0x7FA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        gnp = [[t.numpy() for t in new[g]] for g in range(R)]
+        _, fused_o, _, _ = O.reduce_grads_fused(gnp, [list(w.param_shapes)], R, S, O.AVG)
+        for g in range(R):
+            m = first_mismatch(bits(fb.fused[g]), np_bits(fused_o[g]))
+            assert m == "", f"replay {rep} fused rank {g}: {m}"
+        for i in range(P):
+            assert np.array_equal(bits(fb.full[i]), bits(params[i].reshape(-1))), f"replay {rep} param {i}"
