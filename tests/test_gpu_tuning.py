@@ -1,7 +1,7 @@
 """GPU parity under other launch tunings, one child process each.
 
 The default launch (one workgroup per chunk, 16 KiB copy and 8 KiB reduce
-chunks) never makes a workgroup take a second chunk below 2^20 chunks.
+chunks) never makes a workgroup take a second chunk below 2^22 chunks.
 These runs cap the grid (so every workgroup walks the grid-stride loop, on
 a grid that is or is not a multiple of the 8 XCDs) and move both chunk
 sizes to the extremes the tuning accepts, and check the same parity cases
