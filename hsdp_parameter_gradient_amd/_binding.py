@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.fsdp_last_error.restype = c_char_p
         L.fsdp_release_cache.argtypes = []
         L.fsdp_release_cache.restype = None
+        L.fsdp_time_next_launch.argtypes = [c_void_p, c_void_p]
+        L.fsdp_time_next_launch.restype = c_int32
         _LIB = L
     return _LIB
 
@@ -94,6 +96,26 @@ def fsdp_last_error() -> str:
 
 def fsdp_release_cache() -> None:
     lib().fsdp_release_cache()
+
+
+def _event_handle(ev) -> Optional[int]:
+    if ev is None:
+        return None
+    if isinstance(ev, torch.cuda.Event):
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("the event has no HIP event yet: record it once before passing it")
+        return h
+    return int(ev) or None
+
+
+def fsdp_time_next_launch(start_event, stop_event) -> None:
+    """The calling thread's next kernel launch through this library records
+    start_event when it starts executing and stop_event when it ends
+    (torch.cuda.Event(enable_timing=True) objects recorded once before, or
+    raw hipEvent_t handles); None, None cancels."""
+    _check("fsdp_time_next_launch",
+           lib().fsdp_time_next_launch(c_void_p(_event_handle(start_event)), c_void_p(_event_handle(stop_event))))
 
 
 def _check(fn: str, rc: int) -> None:

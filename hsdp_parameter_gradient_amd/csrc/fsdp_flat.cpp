@@ -303,12 +303,21 @@ void drop_entry(std::list<Entry>::iterator it) {
   g_lru.erase(it);
 }
 
+// Events the calling thread's next kernel launch records at its start and
+// end (fsdp_time_next_launch); taken by that launch.
+thread_local void* g_time_start = nullptr;
+thread_local void* g_time_stop = nullptr;
+
 int enqueue(const Plan& p, hipStream_t stream) {
   if (!p.launch) return ok();
   const uint32_t max_grid = fsdp::tuning().max_grid;
+  void* t0 = g_time_start;
+  void* t1 = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
   int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
-                                         p.nts, stream)
-                    : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream);
+                                         p.nts, stream, t0, t1)
+                    : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream,
+                                           t0, t1);
   if (he != hipSuccess)
     return fail(FSDP_EHIP, "%s launch: %s", p.reduce ? "reduce" : "seg_copy", hipGetErrorString((hipError_t)he));
   return ok();
@@ -1037,6 +1046,14 @@ int guarded(F&& f) noexcept {
 extern "C" {
 
 const char* fsdp_last_error(void) { return g_err.c_str(); }
+
+int fsdp_time_next_launch(void* start_event, void* stop_event) {
+  if (!start_event != !stop_event)
+    return fail(FSDP_EINVAL, "fsdp_time_next_launch: give both events or neither");
+  g_time_start = start_event;
+  g_time_stop = stop_event;
+  return ok();
+}
 
 void fsdp_release_cache(void) {
   std::lock_guard<std::mutex> lock(g_mu);

@@ -42,6 +42,7 @@
 // multiply by its reciprocal); bf16 and fp16 results are rounded once, at
 // the store.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -995,63 +996,81 @@ inline uint32_t grid_for(uint64_t n_chunks, uint32_t max_grid) {
 
 }  // namespace
 
+namespace {
+// One launch: grid, block, stream and, when the caller times the kernel,
+// the events its dispatch records at the kernel's start and end.
+struct Launch {
+  dim3 grid, block;
+  hipStream_t stream;
+  hipEvent_t start, stop;
+  template <typename... KArgs, typename... Args>
+  void operator()(void (*kernel)(KArgs...), Args... args) const {
+    if (start || stop)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  }
+};
+}  // namespace
+
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, uint64_t n_chunks,
-                         uint32_t chunk_shift, uint32_t max_grid, int stream_stores, void* stream) {
+                         uint32_t chunk_shift, uint32_t max_grid, int stream_stores, void* stream,
+                         void* start_event, void* stop_event) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::CopySeg* segs = reinterpret_cast<const fsdp::CopySeg*>(begin + n_seg);
-  const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
+                  static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   if (elem_bytes == 4) {
     if (stream_stores)
-      hipLaunchKernelGGL((seg_copy_kernel<uint32_t, true>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint32_t, true>, begin, segs, n_seg, n_chunks, chunk_shift);
     else
-      hipLaunchKernelGGL((seg_copy_kernel<uint32_t, false>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint32_t, false>, begin, segs, n_seg, n_chunks, chunk_shift);
   } else {
     if (stream_stores)
-      hipLaunchKernelGGL((seg_copy_kernel<uint16_t, true>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint16_t, true>, begin, segs, n_seg, n_chunks, chunk_shift);
     else
-      hipLaunchKernelGGL((seg_copy_kernel<uint16_t, false>), grid, block, 0, st, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint16_t, false>, begin, segs, n_seg, n_chunks, chunk_shift);
   }
   return (int)hipGetLastError();
 }
 
 namespace {
 template <int E, bool NTS>
-void launch_reduce_k(uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
-                     const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
-                     uint32_t chunk_shift, int avg) {
+void launch_reduce_k(const Launch& go, uint32_t n_src, const uint64_t* begin, const fsdp::RedJob* jobs,
+                     const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks, uint32_t chunk_shift, int avg) {
   switch (n_src) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<E, 1, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<E, 2, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<E, 4, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<E, 8, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    default: hipLaunchKernelGGL((reduce_kernel<E, 0, NTS>), grid, block, 0, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 1: go(reduce_kernel<E, 1, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 2: go(reduce_kernel<E, 2, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 4: go(reduce_kernel<E, 4, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 8: go(reduce_kernel<E, 8, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    default: go(reduce_kernel<E, 0, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
   }
 }
 
 template <int E>
-void launch_reduce_e(int stream_stores, uint32_t n_src, dim3 grid, dim3 block, hipStream_t st, const uint64_t* begin,
+void launch_reduce_e(const Launch& go, int stream_stores, uint32_t n_src, const uint64_t* begin,
                      const fsdp::RedJob* jobs, const uint64_t* ptr, uint32_t n_job, uint64_t n_chunks,
                      uint32_t chunk_shift, int avg) {
   if (stream_stores)
-    launch_reduce_k<E, true>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+    launch_reduce_k<E, true>(go, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
   else
-    launch_reduce_k<E, false>(n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
+    launch_reduce_k<E, false>(go, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg);
 }
 }  // namespace
 
 int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
-                       uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream) {
+                       uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores, void* stream,
+                       void* start_event, void* stop_event) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::RedJob* jobs = reinterpret_cast<const fsdp::RedJob*>(begin + n_job);
   // the pointer array follows the jobs (64-byte records, so it is 8-byte aligned)
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(jobs + n_job);
-  const dim3 grid(grid_for(n_chunks, max_grid)), block(kBlock);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
+                  static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   switch (elt) {
-    case kF32: launch_reduce_e<kF32>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case kBF16: launch_reduce_e<kBF16>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
-    case kF16: launch_reduce_e<kF16>(stream_stores, n_src, grid, block, st, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case kF32: launch_reduce_e<kF32>(go, stream_stores, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case kBF16: launch_reduce_e<kBF16>(go, stream_stores, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case kF16: launch_reduce_e<kF16>(go, stream_stores, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

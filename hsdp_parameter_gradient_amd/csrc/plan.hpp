@@ -82,15 +82,17 @@ inline uint64_t item_chunks(uint64_t dst, uint64_t row_bytes, uint64_t rows, uin
 }  // namespace fsdp
 
 // Launchers (defined in kernels.hip).  Return hipSuccess or the launch error.
+// start_event / stop_event: hipEvent_t handles the kernel's dispatch records
+// at its start and end (for callers that time the kernel), or NULL.
 extern "C++" {
 // stream_stores: nontemporal stores for the outputs (see the store policy in
 // fsdp_flat.cpp).
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
                          uint64_t n_chunks, uint32_t chunk_shift, uint32_t max_grid,
-                         int stream_stores, void* stream);
+                         int stream_stores, void* stream, void* start_event, void* stop_event);
 // Every job of one launch has the same operand count n_src; elt is the
 // element kind, an FSDP dtype code: FSDP_F32, FSDP_BF16 or FSDP_F16.
 int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores,
-                       void* stream);
+                       void* stream, void* start_event, void* stop_event);
 }

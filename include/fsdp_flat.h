@@ -251,6 +251,19 @@ const char* fsdp_last_error(void);
  * holds one). */
 void fsdp_release_cache(void);
 
+/*
+ * For callers that time one kernel: the next kernel that the calling thread
+ * enqueues through any entry point above records start_event when it starts
+ * executing and stop_event when it ends (both in its own dispatch, so the
+ * interval excludes the launch and queue overheads that events recorded
+ * around a call include).  start_event and stop_event are hipEvent_t handles
+ * the caller created with timing enabled and on the launch's device; both
+ * NULL cancels a pending request.  A call that launches nothing (an empty
+ * bucket, an AR over one rank) leaves the request pending.
+ * Errors: FSDP_EINVAL (exactly one of the two is NULL).
+ */
+int fsdp_time_next_launch(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

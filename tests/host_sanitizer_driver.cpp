@@ -23,11 +23,12 @@
 
 #include "fsdp_flat.h"
 
-int fsdp_launch_seg_copy(int, const void*, uint32_t, uint64_t, uint32_t, uint32_t, int, void*) {
+int fsdp_launch_seg_copy(int, const void*, uint32_t, uint64_t, uint32_t, uint32_t, int, void*, void*, void*) {
   std::fprintf(stderr, "seg_copy launcher reached without a device\n");
   std::abort();
 }
-int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, uint32_t, int, int, void*) {
+int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, uint32_t, int, int, void*, void*,
+                       void*) {
   std::fprintf(stderr, "reduce launcher reached without a device\n");
   std::abort();
 }

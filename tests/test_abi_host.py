@@ -39,7 +39,7 @@ def test_header_declares_the_five_ops_and_queries():
     names = declared_functions()
     for n in ("fsdp_ag_copy_in", "fsdp_ag_copy_out", "fsdp_rs_copy_in", "fsdp_rs_reduce",
               "fsdp_rs_copy_reduce", "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
-              "fsdp_last_error", "fsdp_release_cache"):
+              "fsdp_last_error", "fsdp_release_cache", "fsdp_time_next_launch"):
         assert n in names
 
 
@@ -264,3 +264,12 @@ def test_flat_bucket_and_group_need_bind():
         grp.bind([[]], [[], []])
     with pytest.raises(RuntimeError, match="bind"):
         grp.step()
+
+
+def test_time_next_launch_arguments(L):
+    """Both events or neither: one NULL handle is FSDP_EINVAL (no HIP call)."""
+    assert L.fsdp_time_next_launch(None, None) == 0
+    assert L.fsdp_time_next_launch(ctypes.c_void_p(0x1000), None) == 1
+    assert L.fsdp_time_next_launch(None, ctypes.c_void_p(0x1000)) == 1
+    assert "both events" in hp.fsdp_last_error()
+    assert L.fsdp_time_next_launch(None, None) == 0

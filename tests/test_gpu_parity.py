@@ -934,3 +934,36 @@ def test_hip_graph_capture_of_cached_plans(fused_rs):
             assert m == "", f"replay {rep} fused rank {g}: {m}"
         for i in range(P):
             assert np.array_equal(bits(fb.full[i]), bits(params[i].reshape(-1))), f"replay {rep} param {i}"
+
+
+def test_time_next_launch_records_the_kernel():
+    """fsdp_time_next_launch: the next kernel's dispatch records the event
+    pair (a duration no shorter than its bytes at 8 TB/s); later launches
+    leave the events alone; a call that launches nothing (an AR over one
+    replica) leaves the request pending for the next launch."""
+    note("[parity] fsdp_time_next_launch")
+    n = 1 << 26  # 256 MiB of fp32 per side
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    hp.fsdp_time_next_launch(a, b)
+    hp.fsdp_ag_copy_in([(n,)], 1, [src], dst)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3
+    assert torch.equal(dst, src)
+    assert 2 * n * 4 / (8000e9) * 1e6 <= us < 100000, us
+    hp.fsdp_ag_copy_in([(n,)], 1, [dst], src)  # not timed
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) * 1e3 == us
+    # pending across a call with nothing to launch (D = 1: the AR is the identity)
+    f = torch.zeros(128, device="cuda")
+    hp.fsdp_time_next_launch(a, b)
+    hp.fsdp_fused_ar([128], 1, 1, 1, "avg", [f])
+    hp.fsdp_ag_copy_in([(n // 4,)], 1, [src[:n // 4]], dst[:n // 4])
+    torch.cuda.synchronize()
+    us2 = a.elapsed_time(b) * 1e3
+    assert us2 != us and 0 < us2 < us, (us2, us)
+    hp.fsdp_time_next_launch(None, None)
