@@ -150,18 +150,30 @@ class PureTPRunner:
         self.call(stream)
 
 
-def per_step_us(runner, steps, n):
-    """Average duration (us) of every step over n passes, from HIP events
-    recorded on the launch stream around each launch."""
+def timing_events(n):
+    """n pairs of timing events, created (recorded once) so that a kernel's
+    dispatch can record them (fsdp_time_next_launch)."""
     import torch
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
-          for _ in range(n)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    return ev
+
+
+def per_step_us(runner, steps, n):
+    """Average duration (us) of every step's kernel over n passes, from the
+    HIP events each kernel's own dispatch records at its start and end."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    flat = timing_events(n * len(steps))
+    ev = [flat[k * len(steps):(k + 1) * len(steps)] for k in range(n)]
     torch.cuda.synchronize()
     for k in range(n):
         for j, name in enumerate(steps):
-            ev[k][j][0].record()
+            hp.fsdp_time_next_launch(*ev[k][j])
             runner.run(name)
-            ev[k][j][1].record()
     torch.cuda.synchronize()
     return {name: sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(n)) / n * 1e3
             for j, name in enumerate(steps)}
@@ -176,7 +188,10 @@ def op_medians(runner, steps, reps: int, flush):
     import statistics
 
     import torch
+
+    import hsdp_parameter_gradient_amd as hp
     out = {}
+    a, b = timing_events(1)[0]
     for name in steps:
         res = {}
         for mode in ("cold", "warm"):
@@ -186,11 +201,9 @@ def op_medians(runner, steps, reps: int, flush):
                     flush.sum()
                 else:
                     runner.run(name)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
+                hp.fsdp_time_next_launch(a, b)
                 runner.run(name)
-                b.record()
-                b.synchronize()
+                torch.cuda.synchronize()
                 t.append(a.elapsed_time(b) * 1e3)
             res[mode] = statistics.median(t)
         out[name] = res
@@ -540,10 +553,7 @@ def main():
     dom = max(steps, key=probe.get)
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for a, b in ev:  # creates the HIP events; the dominant kernel's dispatch re-records them
-        a.record()
-        b.record()
+    ev = timing_events(K)  # the dominant kernel's dispatch records these
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
