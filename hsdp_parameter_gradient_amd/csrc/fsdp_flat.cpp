@@ -277,7 +277,19 @@ struct Plan {
   uint32_t nsrc = 0;
   int avg = 0;
   int nts = 0;
-  int device = 0;  // the device whose memory holds `dev`
+  // a second launch for the call's fold items (fold_copy_kernel), if any
+  void* fold_dev = nullptr;
+  size_t fold_bytes = 0;
+  uint32_t fold_items = 0;
+  uint64_t fold_chunks = 0;
+  int fold_nts = 0;
+  int device = 0;  // the device whose memory holds the tables
+
+  size_t table_bytes() const { return bytes + fold_bytes; }
+  void free_tables() const {
+    if (dev) (void)hipFree(dev);
+    if (fold_dev) (void)hipFree(fold_dev);
+  }
 };
 
 struct Entry {
@@ -298,8 +310,8 @@ void drop_entry(std::list<Entry>::iterator it) {
   auto& v = g_index[it->hash];
   v.erase(std::remove(v.begin(), v.end(), it), v.end());
   if (v.empty()) g_index.erase(it->hash);
-  if (it->plan.dev) (void)hipFree(it->plan.dev);
-  g_table_bytes -= it->plan.bytes;
+  it->plan.free_tables();
+  g_table_bytes -= it->plan.table_bytes();
   g_lru.erase(it);
 }
 
@@ -309,17 +321,25 @@ thread_local void* g_time_start = nullptr;
 thread_local void* g_time_stop = nullptr;
 
 int enqueue(const Plan& p, hipStream_t stream) {
-  if (!p.launch) return ok();
+  if (!p.launch && !p.fold_dev) return ok();
   const uint32_t max_grid = fsdp::tuning().max_grid;
+  // the first kernel of the call takes a pending timing request
   void* t0 = g_time_start;
   void* t1 = g_time_stop;
   g_time_start = g_time_stop = nullptr;
-  int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
-                                         p.nts, stream, t0, t1)
-                    : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream,
-                                           t0, t1);
-  if (he != hipSuccess)
-    return fail(FSDP_EHIP, "%s launch: %s", p.reduce ? "reduce" : "seg_copy", hipGetErrorString((hipError_t)he));
+  if (p.launch) {
+    int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
+                                           p.nts, stream, t0, t1)
+                      : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream,
+                                             t0, t1);
+    if (he != hipSuccess)
+      return fail(FSDP_EHIP, "%s launch: %s", p.reduce ? "reduce" : "seg_copy", hipGetErrorString((hipError_t)he));
+    t0 = t1 = nullptr;
+  }
+  if (p.fold_dev) {
+    int he = fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_nts, stream, t0, t1);
+    if (he != hipSuccess) return fail(FSDP_EHIP, "fold_copy launch: %s", hipGetErrorString((hipError_t)he));
+  }
   return ok();
 }
 
@@ -348,7 +368,7 @@ hipError_t sync_cached_devices() {
   if (e != hipSuccess) return e;
   std::vector<int> devs;
   for (const Entry& en : g_lru)
-    if (en.plan.dev && std::find(devs.begin(), devs.end(), en.plan.device) == devs.end())
+    if ((en.plan.dev || en.plan.fold_dev) && std::find(devs.begin(), devs.end(), en.plan.device) == devs.end())
       devs.push_back(en.plan.device);
   if (std::find(devs.begin(), devs.end(), cur) == devs.end()) devs.push_back(cur);
   for (int d : devs) {
@@ -362,33 +382,34 @@ hipError_t sync_cached_devices() {
 // Keep `plan` under `key` (evicting old plans first if needed) and launch it.
 int store_and_launch(Key&& key, Plan&& plan, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_lru.size() >= kMaxEntries || g_table_bytes + plan.bytes > kMaxTableBytes) {
+  const size_t nb = plan.table_bytes();
+  if (g_lru.size() >= kMaxEntries || g_table_bytes + nb > kMaxTableBytes) {
     // tables still in use by queued kernels must outlive them: wait for
     // every device that owns a cached table, not only the current one
     hipError_t e = sync_cached_devices();
     if (e != hipSuccess) {
-      if (plan.dev) (void)hipFree(plan.dev);
+      plan.free_tables();
       return fail(FSDP_EHIP, "device synchronize before evicting plans: %s", hipGetErrorString(e));
     }
-    while (!g_lru.empty() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + plan.bytes > kMaxTableBytes / 2))
+    while (!g_lru.empty() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + nb > kMaxTableBytes / 2))
       drop_entry(std::prev(g_lru.end()));
   }
   const uint64_t h = key.hash();
-  // the table must not leak if the host bookkeeping cannot grow
+  // the tables must not leak if the host bookkeeping cannot grow
   try {
     g_lru.push_front(Entry{std::move(key), h, plan});
   } catch (...) {
-    if (plan.dev) (void)hipFree(plan.dev);
+    plan.free_tables();
     throw;
   }
   try {
     g_index[h].push_back(g_lru.begin());
   } catch (...) {
     g_lru.pop_front();
-    if (plan.dev) (void)hipFree(plan.dev);
+    plan.free_tables();
     throw;
   }
-  g_table_bytes += plan.bytes;
+  g_table_bytes += nb;
   return enqueue(g_lru.front().plan, stream);
 }
 
@@ -411,19 +432,24 @@ bool stream_stores(Reuse reuse, uint64_t out_bytes) {
 
 // Upload a table (blocking copy into fresh device memory, so it is complete
 // before anything is enqueued on any stream).
-int upload(const std::vector<uint8_t>& table, Plan* p) {
-  hipError_t e = hipGetDevice(&p->device);
+int upload_table(const std::vector<uint8_t>& table, void** dev, size_t* bytes, int* device) {
+  hipError_t e = hipGetDevice(device);
   if (e != hipSuccess) return fail(FSDP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-  e = hipMalloc(&p->dev, table.size());
-  if (e != hipSuccess) return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", table.size(), hipGetErrorString(e));
-  if ((e = hipMemcpy(p->dev, table.data(), table.size(), hipMemcpyHostToDevice)) != hipSuccess) {
-    (void)hipFree(p->dev);
-    p->dev = nullptr;
+  e = hipMalloc(dev, table.size());
+  if (e != hipSuccess) {
+    *dev = nullptr;
+    return fail(FSDP_EHIP, "hipMalloc(%zu) for a descriptor table: %s", table.size(), hipGetErrorString(e));
+  }
+  if ((e = hipMemcpy(*dev, table.data(), table.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(*dev);
+    *dev = nullptr;
     return fail(FSDP_EHIP, "upload of a descriptor table: %s", hipGetErrorString(e));
   }
-  p->bytes = table.size();
+  *bytes = table.size();
   return FSDP_OK;
 }
+
+int upload(const std::vector<uint8_t>& table, Plan* p) { return upload_table(table, &p->dev, &p->bytes, &p->device); }
 
 // Strided blocks: `rows` runs of row_bytes, row r from src + r*src_pitch to
 // dst + r*dst_pitch.  The kernels move whole rows per chunk.  Pitches that
@@ -496,8 +522,48 @@ void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<s
   }
 }
 
-// Plan the segmented copy over `segs`.
-int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
+// A fold item for one parameter over all S ranks (rank s's first row at
+// rank0 + s*rank_pitch), when its dim-k chunk rows are short and the S
+// pieces of a full-tensor row fit a chunk; false otherwise.  The access
+// width is the widest of 16, 8, 4 and 2 bytes that divides the row length,
+// both bases and the rank pitch.  Measured on MI355X against the ranks'
+// interleaved blocks: gathering (AG copy-out) is faster at every width
+// (up to 2.9x); scattering (RS copy-in) is faster with 8- and 16-byte
+// units (up to 1.5x) and 5-13 % slower with 2- and 4-byte ones, so those
+// stay interleaved blocks.
+bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0, uint64_t rank_pitch, int32_t S,
+               uint64_t row_bytes, uint64_t rows, int es, bool gather) {
+  const uint64_t CH = uint64_t(1) << fsdp::tuning().copy_shift;
+  if (S < 2 || !interleave_rows(row_bytes, rows) || (uint64_t)S * row_bytes > CH) return false;
+  const uint64_t m = full | row_bytes | rank0 | rank_pitch;
+  const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
+  if (unit < (uint32_t)es || (!gather && unit < 8)) return false;
+  fsdp::FoldSeg f{};
+  f.full = full;
+  f.run_bytes = row_bytes;
+  f.rows = rows;
+  f.rows_per_chunk = CH / ((uint64_t)S * row_bytes);
+  f.rank0 = rank0;
+  f.rank_pitch = rank_pitch;
+  f.nrank = (uint32_t)S;
+  f.unit = unit;
+  f.gather = gather ? 1u : 0u;
+  folds.push_back(f);
+  return true;
+}
+
+// Output bytes of a call's fold items.
+uint64_t fold_out_bytes(const std::vector<fsdp::FoldSeg>& folds) {
+  uint64_t n = 0;
+  for (const auto& f : folds) n += f.rows * f.nrank * f.run_bytes;
+  return n;
+}
+
+// Plan the segmented copy over `segs` into *table (uploaded by the caller;
+// other_out: the output bytes of the call's other launch, for the store
+// policy).
+int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, uint64_t other_out, Plan* p,
+              std::vector<uint8_t>* table) {
   // the kernel's chunk search needs every item non-empty
   segs.erase(std::remove_if(segs.begin(), segs.end(), [](const fsdp::CopySeg& sg) { return sg.total_bytes == 0; }),
              segs.end());
@@ -511,22 +577,41 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, Plan* p) {
     n += fsdp::item_chunks(segs[k].dst, segs[k].total_bytes, segs[k].rows, segs[k].rows_per_chunk, tu.copy_shift);
     out_bytes += segs[k].total_bytes * segs[k].rows;
   }
-  std::vector<uint8_t> table;
-  table.reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
-  append(table, begin.data(), begin.size());
-  append(table, segs.data(), segs.size());
+  table->reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
+  append(*table, begin.data(), begin.size());
+  append(*table, segs.data(), segs.size());
 #ifdef FSDP_TABLE_HOOK
-  fsdp_table_hook(0, es, (uint32_t)segs.size(), n, tu.copy_shift, table);
+  fsdp_table_hook(0, es, (uint32_t)segs.size(), n, tu.copy_shift, *table);
 #endif
-  int rc = upload(table, p);
-  if (rc) return rc;
   p->launch = true;
   p->reduce = false;
   p->n_items = (uint32_t)segs.size();
   p->n_chunks = n;
   p->shift = tu.copy_shift;
   p->es = es;
-  p->nts = stream_stores(reuse, out_bytes);
+  p->nts = stream_stores(reuse, out_bytes + other_out);
+  return FSDP_OK;
+}
+
+// Plan the fold items of a copy (a launch of its own) into *table.
+int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint64_t other_out, Plan* p,
+              std::vector<uint8_t>* table) {
+  if (folds.empty()) return FSDP_OK;
+  if (folds.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many fold items");
+  std::vector<uint64_t> begin(folds.size());
+  uint64_t n = 0;
+  for (size_t k = 0; k < folds.size(); ++k) {
+    begin[k] = n;
+    n += (folds[k].rows + folds[k].rows_per_chunk - 1) / folds[k].rows_per_chunk;
+  }
+  append(*table, begin.data(), begin.size());
+  append(*table, folds.data(), folds.size());
+#ifdef FSDP_TABLE_HOOK
+  fsdp_table_hook(3, es, (uint32_t)folds.size(), n, fsdp::tuning().copy_shift, *table);
+#endif
+  p->fold_items = (uint32_t)folds.size();
+  p->fold_chunks = n;
+  p->fold_nts = stream_stores(reuse, fold_out_bytes(folds) + other_out);
   return FSDP_OK;
 }
 
@@ -568,10 +653,21 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
 }
 
 // Finish a validated call: plan it, cache the plan and launch it.
-int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream) {
+int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream,
+             const std::vector<fsdp::FoldSeg>& folds = {}) {
+  uint64_t seg_out = 0;
+  for (const auto& sg : segs) seg_out += sg.total_bytes * sg.rows;
   Plan p;
-  int rc = plan_copy(segs, es, reuse, &p);
-  if (rc) return rc;
+  std::vector<uint8_t> seg_table, fold_table;
+  int rc = plan_copy(segs, es, reuse, fold_out_bytes(folds), &p, &seg_table);
+  if (!rc) rc = plan_fold(folds, es, reuse, seg_out, &p, &fold_table);
+  // both tables are built before either is uploaded
+  if (!rc && !seg_table.empty()) rc = upload(seg_table, &p);
+  if (!rc && !fold_table.empty()) rc = upload_table(fold_table, &p.fold_dev, &p.fold_bytes, &p.device);
+  if (rc) {
+    p.free_tables();
+    return rc;
+  }
   return store_and_launch(std::move(key), std::move(p), stream);
 }
 
@@ -698,6 +794,7 @@ int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
   if (P > 0 && !full) return fail(FSDP_EINVAL, "full array is NULL");
   std::vector<Span> outs;
   std::vector<fsdp::CopySeg> segs;
+  std::vector<fsdp::FoldSeg> folds;
   for (int32_t i = 0; i < P; ++i) {
     const int64_t nb = L.numel[i] * es;
     if ((rc = check_ptr(full[i], nb, es, "full", i))) return rc;
@@ -710,8 +807,12 @@ int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     };
     const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
     if (L.outer[i] > 1 && interleave_rows((uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es), (uint64_t)L.outer[i])) {
-      // a dim-k chunk (every rank the same run) of short rows
+      // a dim-k chunk (every rank the same run) of short rows: all ranks'
+      // pieces of a full row in one fold item, else the ranks' blocks
+      // interleaved per chunk of rows
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      if (push_fold(folds, (uint64_t)full[i], src_of(0), (uint64_t)(L.I * es), S, row, (uint64_t)L.outer[i], es, true))
+        continue;
       std::vector<std::pair<uint64_t, uint64_t>> base;
       for (int32_t s = 0; s < S; ++s) base.push_back({src_of(s), dst_of(s)});
       push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], row, pitch);
@@ -723,7 +824,7 @@ int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
     }
   }
   if ((rc = check_overlap(outs, {{(uint64_t)ag, (uint64_t)ag + (uint64_t)ag_bytes, -1}}))) return rc;
-  return run_copy(std::move(key), segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream));
+  return run_copy(std::move(key), segs, es, Reuse::kFinal, static_cast<hipStream_t>(stream), folds);
 }
 
 int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dtype,
@@ -783,21 +884,27 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
       }
     }
   }
-  // dim-k chunks of short rows (every rank the same run, no padding): the S
-  // ranks' pieces of the same rows next to each other
+  // dim-k chunks of short rows (every rank the same run, no padding): all
+  // ranks' pieces of a full gradient row in one fold item, else the S
+  // ranks' blocks of the same rows next to each other
+  std::vector<fsdp::FoldSeg> folds;
   for (int32_t g = 0; g < R; ++g) {
     for (int32_t i = 0; i < P; ++i) {
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
       if (L.padded[i] == 0 || L.outer[i] == 1 || !interleave_rows(row, (uint64_t)L.outer[i])) continue;
+      auto rank_of = [&](int32_t s) { return (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es); };
+      if (push_fold(folds, (uint64_t)grads[(size_t)g * P + i], rank_of(0), (uint64_t)(L.I * es), S, row,
+                    (uint64_t)L.outer[i], es, false))
+        continue;
       std::vector<std::pair<uint64_t, uint64_t>> base;
       for (int32_t s = 0; s < S; ++s)
         base.push_back({(uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es),
-                        (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es)});
+                        rank_of(s)});
       push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es), row);
     }
   }
   if ((rc = check_overlap(outs, ins))) return rc;
-  return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream));
+  return run_copy(std::move(key), segs, es, Reuse::kReadNext, static_cast<hipStream_t>(stream), folds);
 }
 
 int rs_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,

@@ -1,10 +1,14 @@
 // gfx950 kernels of the FSDP/HSDP flat-buffer hot path.
 //
-// Two kernels serve the six device entry points:
+// Three kernels serve the six device entry points:
 //   seg_copy  — segmented copy with zero fill: AG copy-in (pack shards into
 //               padded rank slices), AG copy-out (unpack into the full
 //               parameters) and RS copy-in (chunk gradients into the padded
 //               rank-major RS input).  Bits are moved, never converted.
+//   fold_copy — AG copy-out and RS copy-in of parameters sharded on a
+//               non-zero dim whose chunk rows are short: all shard ranks'
+//               pieces of whole full-tensor rows per workgroup, so both
+//               sides move whole cache lines.
 //   reduce    — fixed-order reduction, in fp32, of K operands into M
 //               destinations, with a zero-filled tail per job: the RS of a
 //               shard group (K = S, M = 1), the RS read straight from the
@@ -987,6 +991,85 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// fold_copy
+// ---------------------------------------------------------------------------
+
+// Rows [r0, r0 + nr) of a fold item in W-sized units: unit q of the chunk is
+// full-tensor row q / upf of the chunk, rank s = (q % upf) / upr and unit
+// col = q % upr of that rank's piece.  Its full-side offset is q units from
+// the chunk's first full row (the full side is contiguous), its rank-side
+// address rank0 + s * rank_pitch + (r0 + row) * run_bytes + col units.
+// Consecutive lanes take consecutive full-side units, so both sides are
+// read and written in whole lines.  U units per lane per iteration, all
+// loads before the first store.
+template <typename W, bool NTS>
+__device__ __forceinline__ void fold_units(const fsdp::FoldSeg& f, uint64_t r0, uint32_t nr) {
+  constexpr int U = sizeof(W) >= 16 ? 4 : 8;
+  const uint32_t upr = (uint32_t)(f.run_bytes / sizeof(W));
+  const uint32_t upf = f.nrank * upr;
+  const uint32_t n = nr * upf;
+  const uint32_t run = (uint32_t)f.run_bytes;
+  const uint64_t full0 = f.full + r0 * f.nrank * f.run_bytes;
+  const uint64_t rank0 = f.rank0 + r0 * f.run_bytes;
+  auto rank_addr = [&](uint32_t q) -> uint64_t {
+    const uint32_t row = q / upf;
+    const uint32_t rem = q - row * upf;
+    const uint32_t s = rem / upr;
+    const uint32_t col = rem - s * upr;
+    return rank0 + s * f.rank_pitch + (row * run + col * (uint32_t)sizeof(W));
+  };
+  auto ld = [](uint64_t a) { return __builtin_nontemporal_load(gptr<W>(a)); };
+  auto st = [](uint64_t a, W v) {
+    if (NTS)
+      __builtin_nontemporal_store(v, gptr<W>(a));
+    else
+      *gptr<W>(a) = v;
+  };
+  uint32_t base = 0;
+  for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
+    W v[U];
+    if (f.gather) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld(rank_addr(base + threadIdx.x + u * kBlock));
+#pragma unroll
+      for (int u = 0; u < U; ++u) st(full0 + (uint64_t)(base + threadIdx.x + u * kBlock) * sizeof(W), v[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld(full0 + (uint64_t)(base + threadIdx.x + u * kBlock) * sizeof(W));
+#pragma unroll
+      for (int u = 0; u < U; ++u) st(rank_addr(base + threadIdx.x + u * kBlock), v[u]);
+    }
+  }
+  for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
+    const uint64_t fa = full0 + (uint64_t)q * sizeof(W);
+    if (f.gather)
+      st(fa, ld(rank_addr(q)));
+    else
+      st(rank_addr(q), ld(fa));
+  }
+}
+
+template <bool NTS>
+__global__ __launch_bounds__(kBlock) void fold_copy_kernel(const uint64_t* __restrict__ begin,
+                                                           const fsdp::FoldSeg* __restrict__ folds, uint32_t n_fold,
+                                                           uint64_t n_chunks) {
+  for (uint64_t slot = blockIdx.x; slot < n_chunks; slot += gridDim.x) {
+    const uint64_t c = xcd_chunk(slot, n_chunks);
+    const uint32_t j = find_item(begin, n_fold, c);
+    const fsdp::FoldSeg f = folds[j];
+    const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
+    const uint64_t left = f.rows - r0;
+    const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);
+    switch (f.unit) {
+      case 16: fold_units<u32x4, NTS>(f, r0, nr); break;
+      case 8: fold_units<uint64_t, NTS>(f, r0, nr); break;
+      case 4: fold_units<uint32_t, NTS>(f, r0, nr); break;
+      default: fold_units<uint16_t, NTS>(f, r0, nr); break;
+    }
+  }
+}
+
 // One workgroup per chunk up to max_grid; a capped grid is a multiple of 8
 // so that every grid-stride step keeps each workgroup on its XCD.
 inline uint32_t grid_for(uint64_t n_chunks, uint32_t max_grid) {
@@ -1073,5 +1156,18 @@ int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t 
     case kF16: launch_reduce_e<kF16>(go, stream_stores, n_src, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     default: return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, uint32_t max_grid,
+                     int stream_stores, void* stream, void* start_event, void* stop_event) {
+  const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
+  const fsdp::FoldSeg* folds = reinterpret_cast<const fsdp::FoldSeg*>(begin + n_fold);
+  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
+                  static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  if (stream_stores)
+    go(fold_copy_kernel<true>, begin, folds, n_fold, n_chunks);
+  else
+    go(fold_copy_kernel<false>, begin, folds, n_fold, n_chunks);
   return (int)hipGetLastError();
 }

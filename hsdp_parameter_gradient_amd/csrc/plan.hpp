@@ -5,6 +5,7 @@
 //
 //   copy table    uint64 chunk_begin[n]  |  CopySeg seg[n]
 //   reduce table  uint64 chunk_begin[n]  |  RedJob job[n]  |  uint64 ptr[m]
+//   fold table    uint64 chunk_begin[n]  |  FoldSeg fold[n]
 //
 // Work is cut into chunks of (1 << chunk_shift) destination bytes.  Chunk k
 // of a one-row item covers the window [base + k*CH, base + (k+1)*CH)
@@ -26,9 +27,10 @@ namespace fsdp {
 //
 // rows > 1 makes it a strided block of `rows` such rows, row r copied from
 // src + r*src_pitch to dst + r*dst_pitch.  Such a block has no zero fill
-// (copy_bytes == total_bytes), both pitches are multiples of 16 (every row
-// has the alignment of the first), and rows_per_chunk * copy_bytes is at
-// most the chunk size.
+// (copy_bytes == total_bytes) and rows_per_chunk * copy_bytes is at most the
+// chunk size.  When both pitches are multiples of 16 every row has the
+// alignment of the first; otherwise the rows of a chunk lie within 4 GiB of
+// its first row on both sides.
 struct CopySeg {
   uint64_t src;
   uint64_t dst;
@@ -49,8 +51,7 @@ struct CopySeg {
 // rows > 1 makes it a strided block of `rows` rows of nbytes: row r of
 // operand t at ptr[src0 + t] + r*src_pitch, of destination m at
 // ptr[dst0 + m] + r*dst_pitch.  Such a job has no zero fill (data_bytes ==
-// nbytes), both pitches are multiples of 16 (every row has the alignment of
-// the first), and rows_per_chunk * nbytes is at most the chunk size.
+// nbytes) and rows_per_chunk * nbytes is at most the chunk size.
 struct RedJob {
   uint64_t nbytes;
   uint64_t data_bytes;
@@ -64,8 +65,32 @@ struct RedJob {
   uint64_t rows_per_chunk = 1;
 };
 
+// A parameter sharded on a non-zero dim, all nrank shard ranks at once:
+// the full tensor is `rows` rows of nrank pieces of run_bytes (piece s of
+// row r is row r of rank s's chunk), contiguous from `full`; rank s's rows
+// are dense from rank0 + s*rank_pitch (row r at + r*run_bytes).
+// gather != 0: ranks to full (AG copy-out); else full to ranks (RS copy-in).
+// Used for short rows, where the ranks' pieces share every cache line of the
+// full tensor: a chunk is rows_per_chunk whole full-tensor rows (at most the
+// chunk size), so one workgroup reads and writes whole lines on both sides.
+// unit (16, 8, 4 or 2) is the access width; it divides run_bytes, full,
+// rank0 and rank_pitch.
+struct FoldSeg {
+  uint64_t full;
+  uint64_t run_bytes;
+  uint64_t rows;
+  uint64_t rows_per_chunk;
+  uint64_t rank0;
+  uint64_t rank_pitch;
+  uint32_t nrank;
+  uint32_t unit;
+  uint32_t gather;
+  uint32_t reserved;
+};
+
 static_assert(sizeof(CopySeg) == 64, "CopySeg layout");
 static_assert(sizeof(RedJob) == 64, "RedJob layout");
+static_assert(sizeof(FoldSeg) == 64, "FoldSeg layout");
 
 // Number of chunks of a one-row item [dst, dst + nbytes), nbytes > 0.
 inline uint64_t chunk_count(uint64_t dst, uint64_t nbytes, uint32_t shift) {
@@ -95,4 +120,7 @@ int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg,
 int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t n_src, uint64_t n_chunks,
                        uint32_t chunk_shift, uint32_t max_grid, int avg, int stream_stores,
                        void* stream, void* start_event, void* stop_event);
+// One chunk of a fold item is rows_per_chunk full-tensor rows.
+int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, uint32_t max_grid,
+                     int stream_stores, void* stream, void* start_event, void* stop_event);
 }

@@ -113,8 +113,9 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
     dump = str(tmp_path / "tables.bin")
     _run(driver, {"FSDP_DUMP_TABLES": dump, **TUNINGS[tuning]})
     counts = _check_tables(dump)
-    # the driver's buckets produce copy and reduce tables, strided blocks included
+    # the driver's buckets produce copy, reduce and fold tables, strided blocks included
     assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
+    assert counts[3] > (10 if tuning != "chunks_512B" else 0), counts
 
 
 def test_random_bucket_tables_pass_the_kernel_emulation(driver, tmp_path):
@@ -135,13 +136,26 @@ BC_SEED, BC_COUNT = 20261202, 40  # the cases of test_gpu_random.py (its SEED, C
 
 
 def _check_tables(dump):
-    counts = {0: 0, 1: 0, "blocks": 0}
-    outs = ins = None
+    """Run every dumped table through the emulated kernels; per call (the
+    tables between two span records), the writes of all its tables together
+    cover exactly the call's outputs, each byte once, and every read lies in
+    the aligned envelope of the call's inputs."""
+    counts = {0: 0, 1: 0, 3: 0, "blocks": 0}
+    state = {"outs": None, "ins": None, "w": [], "tables": 0}
+
+    def finish():
+        if state["tables"]:
+            w = state["w"]
+            assert _merge(w) == state["outs"], "the call's writes do not cover exactly its outputs"
+            assert sum(b - a for a, b in w) == sum(b - a for a, b in state["outs"]), "a byte written twice"
+        state["w"], state["tables"] = [], 0
+
     for kind, elt, a, b, n_chunks, blob in _records(dump):
         words = np.frombuffer(blob, dtype=np.uint64)
         if kind == 2:  # the next call's output and input spans
+            finish()
             sp = [(int(words[2 * k]), int(words[2 * k]) + int(words[2 * k + 1])) for k in range(a + b)]
-            outs, ins = _merge(sp[:a]), _merge(sp[a:])
+            state["outs"], state["ins"] = _merge(sp[:a]), _merge(sp[a:])
             continue
         n, shift = a, b
         begin = [int(v) for v in words[:n]]
@@ -158,6 +172,16 @@ def _check_tables(dump):
             w_iv = [(w[0], w[1]) for w in writes]
             r_iv = [(r[0], r[1]) for r in reads]
             counts["blocks"] += sum(sg[4] > 1 for sg in segs)
+        elif kind == 3:
+            raw = blob[8 * n:8 * n + 64 * n]
+            assert len(blob) == 8 * n + 64 * n
+            folds = [struct.unpack_from(KI.FOLD_FMT, raw, 64 * k) for k in range(n)]
+            fbegin, c, writes, reads = KI.emulate_fold(folds, 1 << shift)
+            assert begin == fbegin and c == n_chunks
+            w_iv = [(w[0], w[1]) for w in writes]
+            r_iv = [(r[0], r[1]) for r in reads]
+            # within a table every byte is written once
+            assert sum(y - x for x, y in w_iv) == sum(y - x for x, y in _merge(w_iv))
         else:
             raw = blob[8 * n:8 * n + 64 * n]
             jobs = [struct.unpack_from("<2Q4I4Q", raw, 64 * k) for k in range(n)]
@@ -172,10 +196,11 @@ def _check_tables(dump):
             w_iv = [(w[0], w[1]) for w in writes]
             r_iv = [(r[0], r[1]) for r in reads]
             counts["blocks"] += sum(jb[6] > 1 for jb in jobs)
-        # exactly the call's outputs are written (each byte once: checked above)
-        assert _merge(w_iv) == outs, f"table {counts[0] + counts[1]}: writes do not cover exactly the outputs"
-        env = _merge([(x & ~15, (y + 15) & ~15) for x, y in ins])
+        state["w"].extend(_merge(w_iv))
+        state["tables"] += 1
+        env = _merge([(x & ~15, (y + 15) & ~15) for x, y in state["ins"]])
         bad = _inside(r_iv, env)
         assert bad is None, f"read {bad} outside the inputs' aligned envelopes"
         counts[kind] += 1
+    finish()
     return counts

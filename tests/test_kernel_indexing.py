@@ -415,6 +415,9 @@ def push_rows_interleaved(segs, base, row_bytes, rows, sp, dp, shift):
 
 
 def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None, shift=14):
+    """AG copy-out segments as fsdp_ag_copy_out builds them when short dim-k
+    rows do not form fold items (its fallback; fold items are emulated by
+    emulate_fold and checked on the planner's own tables)."""
     L = layout(shapes, S, dims)
     segs = []
     for i in range(len(shapes)):
@@ -432,7 +435,8 @@ def ag_copy_out_segs(shapes, S, es, ag, full_addr, dims=None, shift=14):
 
 
 def rs_copy_in_segs(shapes, S, es, grad_addr, rs_in_addr, dims=None, shift=14):
-    """One rank's RS copy-in segments, as fsdp_rs_copy_in builds them."""
+    """One rank's RS copy-in segments, as fsdp_rs_copy_in builds them when
+    short dim-k rows do not form fold items (see ag_copy_out_segs)."""
     L = layout(shapes, S, dims)
     segs = []
     for s in range(S):
@@ -892,3 +896,94 @@ def test_odd_pitch_unit_widths():
     # a chunk's rows must lie within 4 GiB of its first row (32-bit offsets)
     assert not copy_block_ok(0, 0, 1 << 20 | 4, 4, 4, 100, 14) and copy_block_ok(0, 0, (1 << 18) | 4, 4, 4, 100, 14)
     assert not reduce_block_ok(8200, 4104, 4104, 3, 14) and reduce_block_ok(36, 18, 18, 100, 14)
+
+
+# ---------------------------------------------------------------------------
+# fold_copy_kernel: a dim-k parameter's short rows, all shard ranks at once
+# ---------------------------------------------------------------------------
+
+FOLD_FMT = "<6Q4I"  # full, run_bytes, rows, rows_per_chunk, rank0, rank_pitch, nrank, unit, gather, reserved
+
+
+def _merge(iv):
+    out = []
+    for a, b in sorted(x for x in iv if x[0] < x[1]):
+        if out and a <= out[-1][1]:
+            out[-1] = (out[-1][0], max(out[-1][1], b))
+        else:
+            out.append((a, b))
+    return out
+
+
+def emulate_fold(folds, CH):
+    """Writes as (lo, hi, item) and reads as (lo, hi, item), following
+    fold_copy_kernel: chunk k of item j is full-tensor rows [k*per, ...);
+    unit q of a chunk is row q // upf, rank (q % upf) // upr, column
+    q % upr; the full side is contiguous, rank s's rows dense from
+    rank0 + s*rank_pitch."""
+    begin, n = [], 0
+    for f in folds:
+        begin.append(n)
+        n += -(-f[2] // f[3])
+    writes, reads = [], []
+    for c in range(n):
+        j = find_item(begin, len(folds), c)
+        full, run, rows, per, rank0, pitch, S, W, gather = folds[j][:9]
+        assert W in (2, 4, 8, 16) and (full | run | rank0 | pitch) % W == 0
+        assert per * S * run <= CH and per >= 1
+        r0 = (c - begin[j]) * per
+        nr = min(per, rows - r0)
+        assert nr * run < 1 << 32  # the kernel's 32-bit rank-side offsets
+        upr = run // W
+        upf = S * upr
+        full0 = full + r0 * S * run
+        for q in range(nr * upf):
+            row, rem = divmod(q, upf)
+            s, col = divmod(rem, upr)
+            fa = full0 + q * W
+            ra = rank0 + s * pitch + (r0 + row) * run + col * W
+            (src, dst) = (ra, fa) if gather else (fa, ra)
+            reads.append((src, src + W, j))
+            writes.append((dst, dst + W, j))
+    return begin, n, writes, reads
+
+
+def fold_item(full, rank0, pitch, S, run, rows, es, gather, shift=14):
+    """A fold item as the planner builds it (push_fold)."""
+    CH = 1 << shift
+    m = full | run | rank0 | pitch
+    W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
+    assert W >= es
+    return (full, run, rows, CH // (S * run), rank0, pitch, S, W, int(gather), 0)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+@pytest.mark.parametrize("run", [2, 6, 12, 16, 24, 48, 200])
+@pytest.mark.parametrize("gather", [True, False])
+def test_fold_items_cover_exactly(S, run, gather):
+    """Every byte of the full tensor and of every rank's rows is moved
+    exactly once, from the right place, with aligned units of every width."""
+    es = 2 if run % 4 else 4
+    rows = 1000 + S
+    rng = np.random.default_rng(S * 100 + run)
+    full = (1 << 40) + es * int(rng.integers(0, 8)) * (1 if run % 16 else 8)
+    pitch = rows * run + es * int(rng.integers(0, 64))
+    rank0 = (1 << 44) + es * int(rng.integers(0, 8))
+    ranks = [rank0 + s * pitch for s in range(S)]
+    f = fold_item(full, rank0, pitch, S, run, rows, es, gather)
+    _, _, writes, reads = emulate_fold([f], 1 << 14)
+    for a, b, _ in writes:
+        assert b - a == f[7]
+    pairs = sorted(zip(writes, reads))
+    full_iv = [(full, full + rows * S * run)]
+    rank_iv = _merge([(b, b + rows * run) for b in ranks])
+    w_iv = [(a, b) for (a, b, _), _ in pairs]
+    r_iv = [(a, b) for _, (a, b, _) in pairs]
+    assert _merge(w_iv) == (full_iv if gather else rank_iv)
+    assert _merge(r_iv) == (rank_iv if gather else full_iv)
+    assert sum(b - a for a, b in w_iv) == rows * S * run  # each byte once
+    for (wa, wb, _), (ra, rb, _) in pairs:
+        fa, raddr = (wa, ra) if gather else (ra, wa)
+        r, rem = divmod(fa - full, S * run)
+        s, x = divmod(rem, run)
+        assert raddr == ranks[s] + r * run + x
