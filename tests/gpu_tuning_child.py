@@ -31,6 +31,8 @@ CASES = [
     ("strided blocks fp32", T.test_strided_blocks_all_steps, (4, 8, torch.float32)),
     ("strided blocks bf16", T.test_strided_blocks_all_steps, (8, 8, torch.bfloat16)),
     ("non-zero dims misaligned", T.test_nonzero_shard_dims_all_steps, (4, 8, torch.float32)),
+    ("short odd-pitch rows (fold items)", T.test_odd_pitch_blocks_all_steps, (4, 8, torch.bfloat16, False)),
+    ("short odd-pitch rows, aligned", T.test_odd_pitch_blocks_all_steps, (2, 4, torch.bfloat16, True)),
     ("rs copy-reduce ragged", T.test_rs_copy_reduce_ragged_heavy_scaled, ()),
     ("hsdp end to end 16 = 2 x 8", T.test_hsdp_end_to_end_multi_bucket, (16, 8, O.AVG)),
     ("16-bit rs copy-in and reduce", T.test_16bit_rs_copy_in_and_reduce, (8, 4, torch.float16)),
