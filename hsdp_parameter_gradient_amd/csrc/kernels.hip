@@ -657,7 +657,7 @@ template <int E, int K, bool NTS>
 __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                                uint64_t va, uint64_t nv, int avg, float nf) {
   if constexpr (K > 0) {
-    constexpr int U = (K >= 4 || E != kF32) ? 2 : 4;
+    constexpr int U = (K >= 3 || E != kF32) ? 2 : 4;
     // Shifted operands also hold a closing block each; with 8 of them one
     // vector per lane keeps the kernel at 4 waves per SIMD (measured on
     // MI355X: the RS of 8 misaligned slices 1320 -> 1206 us).
@@ -733,7 +733,7 @@ __device__ __forceinline__ void reduce_rows_run(const fsdp::RedJob& jb, const ui
                                                 const uint64_t (&sb)[K], uint64_t doff, uint32_t nr, uint32_t vpr,
                                                 uint32_t b, int avg, float nf) {
   // a shifted operand vector takes two loads: half as many per lane
-  constexpr int U0 = (K >= 4 || E != kF32) ? 2 : 4;
+  constexpr int U0 = (K >= 3 || E != kF32) ? 2 : 4;
   constexpr int U = MODE == 0 ? U0 : (U0 > 1 ? U0 / 2 : 1);
   const uint32_t nv = nr * vpr;
   auto store = [&](uint64_t dof, u32x4 o) {
@@ -1124,7 +1124,9 @@ void launch_reduce_k(const Launch& go, uint32_t n_src, const uint64_t* begin, co
   switch (n_src) {
     case 1: go(reduce_kernel<E, 1, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     case 2: go(reduce_kernel<E, 2, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 3: go(reduce_kernel<E, 3, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     case 4: go(reduce_kernel<E, 4, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
+    case 6: go(reduce_kernel<E, 6, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     case 8: go(reduce_kernel<E, 8, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
     default: go(reduce_kernel<E, 0, NTS>, begin, jobs, ptr, n_job, n_chunks, chunk_shift, avg); break;
   }

@@ -307,7 +307,7 @@ def run_hsdp_end_to_end(name, buckets, R, S, op, dtype=torch.float32, seed=7):
         j0 += len(b)
 
 
-@pytest.mark.parametrize("R,S", [(8, 4), (8, 2), (6, 2), (16, 8)])
+@pytest.mark.parametrize("R,S", [(8, 4), (8, 2), (6, 2), (16, 8), (12, 6), (18, 3)])
 @pytest.mark.parametrize("op", [O.AVG, O.SUM])
 def test_hsdp_end_to_end_multi_bucket(R, S, op):
     shapes = [(7, 8), (5, 3), (16,), (3,), (1000, 3), (129,), (4097, 2)]
@@ -433,7 +433,7 @@ NP16 = {torch.bfloat16: np.uint16, torch.float16: np.float16}
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("R,S", [(8, 4), (16, 8), (6, 3), (4, 1)])
+@pytest.mark.parametrize("R,S", [(8, 4), (16, 8), (6, 3), (4, 1), (12, 6)])
 def test_16bit_rs_copy_in_and_reduce(R, S, dtype):
     """bf16 / fp16 gradients: RS copy-in (a bit copy), RS (fp32 sum, one
     rounding) and the fused form agree with the oracle bit for bit."""
@@ -690,7 +690,7 @@ def _same_up_to_nan_payload(got_t, want_np):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("R,S", [(8, 4), (6, 3), (8, 8), (6, 2)])
+@pytest.mark.parametrize("R,S", [(8, 4), (6, 3), (8, 8), (6, 2), (6, 1), (12, 6)])
 def test_special_values_rs_and_fused_ar(dtype, R, S):
     """Signed zeros, infinities, NaN, denormals and values that overflow when
     added, through the RS (from the RS input and straight from the
