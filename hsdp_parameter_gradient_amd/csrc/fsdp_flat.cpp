@@ -596,6 +596,7 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, uint64_t ot
 // Plan the fold items of a copy (a launch of its own) into *table.
 int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint64_t other_out, Plan* p,
               std::vector<uint8_t>* table) {
+  (void)es;  // element bytes: only the test builds' table hook reports them
   if (folds.empty()) return FSDP_OK;
   if (folds.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many fold items");
   std::vector<uint64_t> begin(folds.size());
