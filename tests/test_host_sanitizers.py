@@ -98,7 +98,7 @@ def _inside(iv, allowed):
 
 TUNINGS = {
     "default": {},
-    # the smallest and a large chunk size the tuning accepts (for both kernels)
+    # the smallest and a large chunk size the tuning accepts (copy and reduce chunks)
     "chunks_512B": {"FSDP_COPY_CHUNK_SHIFT": "9", "FSDP_REDUCE_CHUNK_SHIFT": "9"},
     "chunks_1MiB": {"FSDP_COPY_CHUNK_SHIFT": "20", "FSDP_REDUCE_CHUNK_SHIFT": "20"},
 }

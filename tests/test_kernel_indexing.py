@@ -1,10 +1,11 @@
 """CPU emulation of the kernels' work decomposition (no GPU).
 
-Mirrors, line for line in Python, the address arithmetic of seg_copy_kernel
-and reduce_kernel (hsdp_parameter_gradient_amd/csrc/kernels.hip): the
-64-ary chunk search, the chunk windows, the whole-vector ranges, the
-zero-fill range and the element-wise edge vectors.  For many segment
-tables it checks that
+Mirrors, line for line in Python, the address arithmetic of seg_copy_kernel,
+reduce_kernel and fold_copy_kernel (hsdp_parameter_gradient_amd/csrc/
+kernels.hip): the 64-ary chunk search, the chunk windows, the whole-vector
+ranges, the strided and unit-wise row blocks, the fold items' unit
+decomposition, the zero-fill range and the element-wise edge vectors.  For
+many segment tables it checks that
 
   * every destination byte is written exactly once, with data from the
     right source offset before the data/padding edge and zero after it;
