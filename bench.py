@@ -426,7 +426,9 @@ def calibration_copy(mib: int, reps: int) -> None:
 
 
 def cpu_baseline(w, seconds: float, op: str):
-    """The oracle, as it stands, timed on whole steps of the workload."""
+    """The oracle, as it stands, timed on whole steps of the workload (and
+    on each of the step's operations, with perf_counter around each oracle
+    call).  Returns (steps run, seconds, F, seconds per operation)."""
     import numpy as np
     import torch
 
@@ -457,23 +459,32 @@ def cpu_baseline(w, seconds: float, op: str):
                 buf[o:o + t.size] = t.reshape(-1)
             fused0.append(buf)
 
+    per = {}
+
+    def timed(name, fn, *a):
+        t = time.perf_counter()
+        r = fn(*a)
+        per[name] = per.get(name, 0.0) + time.perf_counter() - t
+        return r
+
+    if S == 1:
         def one_step():
-            O.fused_ar(fused0, R, S, op)
+            timed("fused_ar", O.fused_ar, fused0, R, S, op)
     else:
         one_step = None
 
     def hsdp_step():
-        ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt)
-        O.ag_copy_out(O.all_gather(ag), lay)
-        rs_in = [O.rs_copy_in(gnp[g], lay) for g in range(R)]
-        out = O.rs_reduce(rs_in, lay.I, R, S, op)
+        ag = timed("ag_copy_in", lambda: O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt))
+        timed("ag_copy_out", lambda: O.ag_copy_out(O.all_gather(ag), lay))
+        rs_in = timed("rs_copy_in", lambda: [O.rs_copy_in(gnp[g], lay) for g in range(R)])
+        out = timed("rs_reduce", O.rs_reduce, rs_in, lay.I, R, S, op)
         fused = []
         for g in range(R):
             buf = np.zeros(F, np.float32)
             buf[offs[0]:offs[0] + lay.I] = out[g]
             fused.append(buf)
         if do_ar:
-            O.fused_ar(fused, R, S, op)
+            timed("fused_ar", O.fused_ar, fused, R, S, op)
 
     one_step = one_step or hsdp_step
     n, t0 = 0, time.perf_counter()
@@ -483,7 +494,7 @@ def cpu_baseline(w, seconds: float, op: str):
         el = time.perf_counter() - t0
         if el >= seconds or n >= 200:
             break
-    return n, el, F
+    return n, el, F, {k: v / n for k, v in per.items()}
 
 
 def main():
@@ -640,11 +651,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n, el, _ = cpu_baseline(w, args.cpu_seconds, op)
+        n, el, _, cpu_per = cpu_baseline(w, args.cpu_seconds, op)
         cpu = {"value": round(bytes_per_step * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{n} whole steps of {w.name} (all {len(steps)} steps, full size) in {el:.1f} s; "
-                         f"NumPy, single-threaded: 1 core of {os.cpu_count()} ({cpu_model()})"}
+                         f"NumPy, single-threaded: 1 core of {os.cpu_count()} ({cpu_model()})",
+               "ops": {k: {"ms": round(v * 1e3, 3), "GB/s": round(nbytes[k] / v / 1e9, 3)}
+                       for k, v in cpu_per.items() if k in nbytes}}
         log(f"  cpu oracle: {cpu['value']} GB/s over {n} steps ({el:.1f} s)")
 
     out = {
