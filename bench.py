@@ -406,6 +406,32 @@ def pipeline_variant(w, op, layers: int, reps: int):
     return out
 
 
+def graph_variant(runner, reps: int, warmup: int):
+    """The contract's pass captured once in a HIP graph (torch.cuda.graph)
+    and replayed: the same kernels with the same arguments, launched by the
+    graph instead of one host call each.  Plans are cached by the eager
+    passes before, so the capture records kernel launches only."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    runner.step()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        runner.step()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del graph
+    log(f"  HIP graph variant: step {ms * 1e3:.1f} us")
+    return {"ms_per_step": round(ms, 4), "note": "one graph replay per pass, same kernels and arguments"}
+
+
 def calibration_copy(mib: int, reps: int) -> None:
     """A plain copy of known size for calibrating the HBM byte counters: the
     copy kernel on one aligned fp32 segment (AG copy-out with one shard), so
@@ -638,6 +664,7 @@ def main():
             "note": "RS input never written; results identical to rs_copy_in + rs_reduce"}
         log(f"  fused RS variant: step {f_ms * 1e3:.1f} us (vs {ms_per_step * 1e3:.1f}); rs_copy_reduce "
             f"{f_us:.1f} us, {b / (f_us * 1e-6) / 1e9:.1f} GB/s")
+        variants["hip_graph"] = graph_variant(runner, K, args.warmup)
         if args.pipeline_layers > 1 and runner.do_ar:
             variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
         if not args.no_variants:

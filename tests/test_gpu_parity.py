@@ -205,6 +205,62 @@ def test_padding_rewritten_on_reuse_and_side_stream():
         assert np.array_equal(bits(ag), np_bits(want))
 
 
+_POISON = {torch.float32: -1, torch.bfloat16: -1, torch.float16: -1}  # all-ones bits: a NaN
+
+
+@pytest.mark.parametrize("case", [
+    # ragged dim-0 shards, zero-length ranks, a zero-size parameter
+    ("ragged_dim0", [(7, 8), (5, 3), (0, 4), (1,), (3,), (1000, 33), (4099,)], None, 8, torch.float32),
+    ("ragged_dim0_bf16", [(7, 8), (5, 3), (0, 4), (1,), (3,), (1000, 33), (4099,)], None, 6, torch.bfloat16),
+    # dim-1 shards (which have no padding: the dim divides S) between padded
+    # dim-0 ones: short rows (one workgroup per whole full row), long rows,
+    # pitches that are not multiples of 16 bytes
+    ("dim1_fp32", [(64, 8), (33, 12, 3), (5,), (9, 20), (1000, 6), (3, 2048, 1), (300, 1024)],
+     [1, 1, 0, 1, 1, 1, 1], 2,
+     torch.float32),
+    ("dim1_fp16", [(64, 8), (33, 12, 3), (9, 20), (5,), (1000, 12), (3, 2048, 1), (5, 8, 3)],
+     [1, 1, 1, 0, 1, 1, 1], 4,
+     torch.float16),
+])
+def test_ag_copy_out_never_reads_padding(case):
+    """AG copy-out reads only the actual rows of every rank slice: with all
+    padding of the gathered buffer overwritten by a NaN pattern, the full
+    parameters still come out bit for bit (padding never enters the module,
+    the ragged-sharding paper's section on padded shards)."""
+    name, shapes, dims, S, dtype = case
+    note(f"[parity] padding poison {name}: S={S} dtype={dtype}")
+    dims = dims if dims is not None else [0] * len(shapes)
+    lay = O.bucket_layout(shapes, S, shard_dims=dims)
+    P, I = len(shapes), lay.I
+    gen = torch.Generator().manual_seed(321)
+    xs = [torch.randn(sh, generator=gen).to(dtype) for sh in shapes]
+    np_dt = np.float32 if dtype == torch.float32 else np.uint16
+    # where the data lands: AG copy-in of all-ones shards is nonzero exactly there
+    ones = [np.ones(sh, np_dt) for sh in shapes]
+    data_mask = O.ag_copy_in(O.shard_params(ones, lay), lay, np_dt) != 0
+    n_pad = int((~data_mask).sum())
+    assert n_pad > 0
+    dparams = [x.cuda() for x in xs]
+    shards = [dparams[i].narrow(dims[i], lay.row_off[i][s], lay.row_len[i][s]).contiguous().reshape(-1)
+              for s in range(S) for i in range(P)]
+    ag = Guarded(S * I, dtype, 3)
+    hp.fsdp_ag_copy_in(shapes, S, shards, ag.t, shard_dims=dims)
+    it = _INT_VIEW[dtype]
+    pad_idx = torch.from_numpy(np.flatnonzero(~data_mask)).cuda()
+    ag.t.view(it).index_fill_(0, pad_idx, _POISON[dtype])
+    full = [Guarded(_numel(sh), dtype, 1) for sh in shapes]
+    hp.fsdp_ag_copy_out(shapes, S, ag.t, [f.t for f in full], shard_dims=dims)
+    torch.cuda.synchronize()
+    assert int((bits(ag.t)[~data_mask.reshape(-1)] == -1).sum()) == n_pad
+    for i in range(P):
+        assert full[i].guards_intact(), f"ag_copy_out wrote outside full[{i}]"
+        m = first_mismatch(bits(full[i].t), np_bits(to_oracle(xs[i]).reshape(-1)))
+        assert m == "", f"{name} param {i} {shapes[i]}: {m}"
+
+
+_INT_VIEW = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.float16: torch.int16}
+
+
 def test_empty_buckets():
     note("[parity] empty buckets")
     S, R = 4, 8
