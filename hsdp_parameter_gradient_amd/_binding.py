@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.fsdp_release_cache.restype = None
         L.fsdp_time_next_launch.argtypes = [c_void_p, c_void_p]
         L.fsdp_time_next_launch.restype = c_int32
+        L.fsdp_cache_info.argtypes = [POINTER(c_int64)] * 3
+        L.fsdp_cache_info.restype = c_int32
         _LIB = L
     return _LIB
 
@@ -96,6 +98,14 @@ def fsdp_last_error() -> str:
 
 def fsdp_release_cache() -> None:
     lib().fsdp_release_cache()
+
+
+def fsdp_cache_info() -> dict:
+    """The plan cache: cached plans, plans pinned by a graph capture, and
+    the device bytes of their tables."""
+    n, pinned, nbytes = c_int64(), c_int64(), c_int64()
+    _check("fsdp_cache_info", lib().fsdp_cache_info(ctypes.byref(n), ctypes.byref(pinned), ctypes.byref(nbytes)))
+    return {"plans": n.value, "pinned": pinned.value, "table_bytes": nbytes.value}
 
 
 def _event_handle(ev) -> Optional[int]:

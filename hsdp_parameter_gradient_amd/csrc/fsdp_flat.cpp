@@ -296,6 +296,9 @@ struct Entry {
   Key key;
   uint64_t hash;
   Plan plan;
+  // launched into a stream capture: a HIP graph holds the table's address,
+  // so the plan is never evicted (only fsdp_release_cache frees it)
+  bool pinned = false;
 };
 
 constexpr size_t kMaxEntries = 256;
@@ -343,6 +346,12 @@ int enqueue(const Plan& p, hipStream_t stream) {
   return ok();
 }
 
+// Is `stream` being captured into a HIP graph?
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 // Launch the cached plan of `key`, if there is one.
 bool launch_cached(const Key& key, hipStream_t stream, int* rc) {
   if (!key.valid()) return false;
@@ -353,6 +362,7 @@ bool launch_cached(const Key& key, hipStream_t stream, int* rc) {
   for (auto it : found->second) {
     if (it->key == key) {
       g_lru.splice(g_lru.begin(), g_lru, it);
+      if (!it->pinned && capturing(stream)) it->pinned = true;
       *rc = enqueue(it->plan, stream);
       return true;
     }
@@ -391,8 +401,15 @@ int store_and_launch(Key&& key, Plan&& plan, hipStream_t stream) {
       plan.free_tables();
       return fail(FSDP_EHIP, "device synchronize before evicting plans: %s", hipGetErrorString(e));
     }
-    while (!g_lru.empty() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + nb > kMaxTableBytes / 2))
-      drop_entry(std::prev(g_lru.end()));
+    // least recent first; plans held by captured graphs stay
+    for (auto it = g_lru.end();
+         it != g_lru.begin() && (g_lru.size() >= kMaxEntries / 2 || g_table_bytes + nb > kMaxTableBytes / 2);) {
+      auto victim = std::prev(it);
+      if (victim->pinned)
+        it = victim;
+      else
+        drop_entry(victim);
+    }
   }
   const uint64_t h = key.hash();
   // the tables must not leak if the host bookkeeping cannot grow
@@ -653,9 +670,20 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
   return FSDP_OK;
 }
 
+// A call without a cached plan allocates and uploads its tables (and may
+// evict, which synchronizes devices): refused while its stream is being
+// captured, before anything could invalidate the capture.
+int check_not_capturing(hipStream_t stream) {
+  if (capturing(stream))
+    return fail(FSDP_EINVAL, "the first call of a signature cannot be captured into a graph: "
+                "issue it once outside the capture");
+  return FSDP_OK;
+}
+
 // Finish a validated call: plan it, cache the plan and launch it.
 int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, hipStream_t stream,
              const std::vector<fsdp::FoldSeg>& folds = {}) {
+  if (int rc = check_not_capturing(stream)) return rc;
   uint64_t seg_out = 0;
   for (const auto& sg : segs) seg_out += sg.total_bytes * sg.rows;
   Plan p;
@@ -674,6 +702,7 @@ int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, h
 
 int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int dtype, int avg,
                Reuse reuse, hipStream_t stream) {
+  if (int rc = check_not_capturing(stream)) return rc;
   Plan p;
   int rc = plan_reduce(jobs, ptrs, dtype, avg, reuse, &p);
   if (rc) return rc;
@@ -1176,6 +1205,16 @@ void fsdp_release_cache(void) {
     }
   }
   while (!g_lru.empty()) drop_entry(g_lru.begin());
+}
+
+int fsdp_cache_info(int64_t* n_plans, int64_t* n_pinned, int64_t* table_bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int64_t pinned = 0;
+  for (const Entry& en : g_lru) pinned += en.pinned ? 1 : 0;
+  if (n_plans) *n_plans = (int64_t)g_lru.size();
+  if (n_pinned) *n_pinned = pinned;
+  if (table_bytes) *table_bytes = (int64_t)g_table_bytes;
+  return ok();
 }
 
 int fsdp_bucket_layout(const fsdp_bucket_t* bucket, int32_t shard_size, int64_t* slice_numel,

@@ -55,12 +55,16 @@
  *     plan without validating or planning again (its result cannot differ).
  *     At most 256 plans and 256 MiB of tables; evicting waits for every
  *     device that holds a cached table.  fsdp_release_cache() frees them all.
- *   - A call whose plan is cached only enqueues one kernel launch, so it can
- *     be captured into a HIP graph and replayed (the graph reads the
- *     buffers' contents at replay time).  The first call of a signature
- *     allocates and uploads its table and evicting synchronizes devices:
- *     neither may happen under capture, so issue each call once before
- *     capturing it.
+ *   - A call whose plan is cached only enqueues its kernel launches (one,
+ *     or two when some parameters take the fold kernel), so it can be
+ *     captured into a HIP graph and replayed (the graph reads the buffers'
+ *     contents at replay time).  A plan launched into a capture is pinned:
+ *     eviction never frees it, since the graph holds its table's address.
+ *     The first call of a signature allocates and uploads its tables and
+ *     may evict (synchronizing devices), so it is refused with FSDP_EINVAL
+ *     while its stream is being captured, before anything is enqueued:
+ *     issue each call once before capturing it.  No graph that captured a
+ *     call may be replayed after fsdp_release_cache().
  *   - Thread safe; calls that overlap in time on different streams must not
  *     share output buffers.
  */
@@ -247,9 +251,14 @@ int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size,
 /* Message for the calling thread's last error ("" after success). */
 const char* fsdp_last_error(void);
 
-/* Free the cached descriptor tables (waits first for every device that
- * holds one). */
+/* Free the cached descriptor tables, pinned ones included (waits first for
+ * every device that holds one).  Not while a stream is being captured. */
 void fsdp_release_cache(void);
+
+/* State of the plan cache: the number of cached plans, how many of them
+ * are pinned by a graph capture, and the device bytes their tables hold.
+ * Any pointer may be NULL.  Always FSDP_OK. */
+int fsdp_cache_info(int64_t* n_plans, int64_t* n_pinned, int64_t* table_bytes);
 
 /*
  * For callers that time one kernel: the next kernel that the calling thread

@@ -39,7 +39,7 @@ def test_header_declares_the_five_ops_and_queries():
     names = declared_functions()
     for n in ("fsdp_ag_copy_in", "fsdp_ag_copy_out", "fsdp_rs_copy_in", "fsdp_rs_reduce",
               "fsdp_rs_copy_reduce", "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
-              "fsdp_last_error", "fsdp_release_cache", "fsdp_time_next_launch"):
+              "fsdp_last_error", "fsdp_release_cache", "fsdp_time_next_launch", "fsdp_cache_info"):
         assert n in names
 
 
@@ -273,3 +273,10 @@ def test_time_next_launch_arguments(L):
     assert L.fsdp_time_next_launch(None, ctypes.c_void_p(0x1000)) == 1
     assert "both events" in hp.fsdp_last_error()
     assert L.fsdp_time_next_launch(None, None) == 0
+
+
+def test_cache_info_without_a_gpu(L):
+    """Nothing is cached without a GPU; NULL outputs are allowed."""
+    hp.fsdp_release_cache()
+    assert hp.fsdp_cache_info() == {"plans": 0, "pinned": 0, "table_bytes": 0}
+    assert L.fsdp_cache_info(None, None, None) == 0

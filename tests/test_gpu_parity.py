@@ -992,6 +992,82 @@ def test_hip_graph_capture_of_cached_plans(fused_rs):
             assert np.array_equal(bits(fb.full[i]), bits(params[i].reshape(-1))), f"replay {rep} param {i}"
 
 
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
+def test_captured_plans_are_pinned_through_eviction():
+    """A plan launched into a graph capture is pinned: after more new call
+    signatures than the cache holds, it is still cached and the graph still
+    replays correctly.  The first call of a signature under capture is
+    refused before anything is enqueued, and works once issued eagerly."""
+    note("[parity] captured plans pinned through eviction")
+    hp.fsdp_release_cache()
+    shapes, S = [(97, 64), (3,), (130, 32), (5,)], 4
+    lay = O.bucket_layout(shapes, S)
+    gen = torch.Generator().manual_seed(99)
+    xs = [torch.randn(sh, generator=gen) for sh in shapes]
+    dparams = [x.cuda() for x in xs]
+    shards, _ = make_shards(dparams, lay, torch.float32)
+    ag = torch.empty(S * lay.I, device="cuda")
+    full = [torch.empty(_numel(sh), device="cuda") for sh in shapes]
+    hp.fsdp_ag_copy_in(shapes, S, shards, ag)
+    hp.fsdp_ag_copy_out(shapes, S, ag, full)
+    torch.cuda.synchronize()
+    assert hp.fsdp_cache_info()["pinned"] == 0
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hp.fsdp_ag_copy_in(shapes, S, shards, ag)
+        hp.fsdp_ag_copy_out(shapes, S, ag, full)
+    assert hp.fsdp_cache_info()["pinned"] == 2
+
+    # 300 new signatures (one destination offset each): more than the cache
+    # holds, so every plan that is not pinned is evicted at least once
+    src = torch.randn(16, device="cuda")
+    dst = torch.empty(16 + 300, device="cuda")
+    for k in range(300):
+        hp.fsdp_ag_copy_in([(16,)], 1, [src], dst[k:k + 16])
+    torch.cuda.synchronize()
+    info = hp.fsdp_cache_info()
+    assert info["plans"] < 300 and info["pinned"] == 2, info
+    assert torch.equal(dst[299:315], src)
+
+    for rep in range(2):
+        ys = [torch.randn(sh, generator=gen) for sh in shapes]
+        for d, y in zip(dparams, ys):
+            d.copy_(y)
+        ag.view(torch.int32).fill_(0x7FA5A5A5)
+        for f in full:
+            f.view(torch.int32).fill_(0x7FA5A5A5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = O.ag_copy_in(O.shard_params([y.numpy() for y in ys], lay), lay, np.float32)
+        assert first_mismatch(bits(ag), np_bits(want)) == "", f"replay {rep}"
+        for i in range(len(shapes)):
+            assert np.array_equal(bits(full[i]), np_bits(ys[i].numpy().reshape(-1))), f"replay {rep} param {i}"
+
+    # an uncached signature under capture: refused, nothing enqueued
+    new_shapes = [(9, 5), (2,)]
+    lay2 = O.bucket_layout(new_shapes, 2)
+    zs = [torch.randn(sh, generator=gen) for sh in new_shapes]
+    shards2, _ = make_shards([z.cuda() for z in zs], lay2, torch.float32)
+    ag2 = torch.full((2 * lay2.I,), float("nan"), device="cuda")
+    before = hp.fsdp_cache_info()
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(hp.FSDPError, match="captured"):
+        with torch.cuda.graph(g2):
+            hp.fsdp_ag_copy_in(new_shapes, 2, shards2, ag2)
+    del g2
+    assert hp.fsdp_cache_info() == before
+    torch.cuda.synchronize()
+    assert torch.isnan(ag2).all()
+    hp.fsdp_ag_copy_in(new_shapes, 2, shards2, ag2)
+    torch.cuda.synchronize()
+    want2 = O.ag_copy_in(O.shard_params([z.numpy() for z in zs], lay2), lay2, np.float32)
+    assert first_mismatch(bits(ag2), np_bits(want2)) == ""
+    del graph
+    hp.fsdp_release_cache()
+    assert hp.fsdp_cache_info() == {"plans": 0, "pinned": 0, "table_bytes": 0}
+
+
 def test_time_next_launch_records_the_kernel():
     """fsdp_time_next_launch: the next kernel's dispatch records the event
     pair (a duration no shorter than its bytes at 8 TB/s); later launches
