@@ -18,7 +18,7 @@
 //               (16-bit elements widened exactly, summed in fp32, rounded
 //               once to nearest even).
 //
-// Both are HBM-bound streaming kernels (no data reuse, no dense
+// All three are HBM-bound streaming kernels (no data reuse, no dense
 // contraction): one workgroup of 256 lanes handles one chunk of destination
 // bytes at a time, with 128-bit loads and stores on 16-byte-aligned
 // destination addresses.  A source whose address differs from the
