@@ -38,10 +38,10 @@
 
 #ifdef FSDP_TABLE_HOOK
 // Test builds only (the host sanitizer driver): every planned table is
-// handed to this function before its upload (reduce: 0 copy / 1 reduce;
-// elt: element bytes of a copy, dtype code of a reduction), so the tables
-// the planner really builds can be checked against an emulation of the
-// kernels.
+// handed to this function before its upload (reduce: 0 copy, 1 reduce,
+// 3 fold copy, 4 fold reduce; elt: element bytes of a copy, dtype code of a
+// reduction), so the tables the planner really builds can be checked
+// against an emulation of the kernels.
 void fsdp_table_hook(int reduce, int elt, uint32_t n_items, uint64_t n_chunks, uint32_t shift,
                      const std::vector<uint8_t>& table);
 #endif
@@ -277,12 +277,17 @@ struct Plan {
   uint32_t nsrc = 0;
   int avg = 0;
   int nts = 0;
-  // a second launch for the call's fold items (fold_copy_kernel), if any
+  // a second launch for the call's fold items (fold_copy_kernel, or
+  // fold_reduce_kernel with the dtype code, operand count and op), if any
   void* fold_dev = nullptr;
   size_t fold_bytes = 0;
   uint32_t fold_items = 0;
   uint64_t fold_chunks = 0;
   int fold_nts = 0;
+  bool fold_reduce = false;
+  int fold_elt = 0;
+  uint32_t fold_nsrc = 0;
+  int fold_avg = 0;
   int device = 0;  // the device whose memory holds the tables
 
   size_t table_bytes() const { return bytes + fold_bytes; }
@@ -340,8 +345,14 @@ int enqueue(const Plan& p, hipStream_t stream) {
     t0 = t1 = nullptr;
   }
   if (p.fold_dev) {
-    int he = fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_nts, stream, t0, t1);
-    if (he != hipSuccess) return fail(FSDP_EHIP, "fold_copy launch: %s", hipGetErrorString((hipError_t)he));
+    int he = p.fold_reduce ? fsdp_launch_fold_reduce(p.fold_elt, p.fold_dev, p.fold_items, p.fold_nsrc,
+                                                     p.fold_chunks, max_grid, p.fold_avg, p.fold_nts, stream, t0,
+                                                     t1)
+                           : fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_nts,
+                                              stream, t0, t1);
+    if (he != hipSuccess)
+      return fail(FSDP_EHIP, "%s launch: %s", p.fold_reduce ? "fold_reduce" : "fold_copy",
+                  hipGetErrorString((hipError_t)he));
   }
   return ok();
 }
@@ -569,6 +580,35 @@ bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0,
   return true;
 }
 
+// A fold-reduce item for one parameter over one shard group (operand t's
+// full gradient at src[t], rank s's rows at dst[s]), when its dim-k chunk
+// rows are short and the S pieces of a full-tensor row fit a reduce chunk;
+// false otherwise.  The access width is the widest of 16, 8, 4 and 2 bytes
+// that divides the row length and every pointer, and at least the element.
+bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& ptrs, const std::vector<uint64_t>& src,
+                      const std::vector<uint64_t>& dst, uint64_t row_bytes, uint64_t rows, int es) {
+  const uint64_t CH = uint64_t(1) << fsdp::tuning().reduce_shift;
+  const uint64_t S = src.size();
+  if (S < 2 || dst.size() != S || !interleave_rows(row_bytes, rows) || S * row_bytes > CH) return false;
+  uint64_t m = row_bytes;
+  for (uint64_t a : src) m |= a;
+  for (uint64_t a : dst) m |= a;
+  const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
+  if (unit < (uint32_t)es) return false;
+  fsdp::FoldRed f{};
+  f.run_bytes = row_bytes;
+  f.rows = rows;
+  f.rows_per_chunk = CH / (S * row_bytes);
+  f.src0 = (uint32_t)ptrs.size();
+  ptrs.insert(ptrs.end(), src.begin(), src.end());
+  f.dst0 = (uint32_t)ptrs.size();
+  ptrs.insert(ptrs.end(), dst.begin(), dst.end());
+  f.nrank = (uint32_t)S;
+  f.unit = unit;
+  items.push_back(f);
+  return true;
+}
+
 // Output bytes of a call's fold items.
 uint64_t fold_out_bytes(const std::vector<fsdp::FoldSeg>& folds) {
   uint64_t n = 0;
@@ -633,9 +673,11 @@ int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint
   return FSDP_OK;
 }
 
-// Plan the reduction over `jobs` (every job with the same operand count).
+// Plan the reduction over `jobs` (every job with the same operand count)
+// into *table (uploaded by the caller; other_out: the output bytes of the
+// call's other launch, for the store policy).
 int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int dtype, int avg, Reuse reuse,
-                Plan* p) {
+                uint64_t other_out, Plan* p, std::vector<uint8_t>* table) {
   jobs.erase(std::remove_if(jobs.begin(), jobs.end(), [](const fsdp::RedJob& jb) { return jb.nbytes == 0; }),
              jobs.end());
   if (jobs.empty()) return FSDP_OK;
@@ -649,15 +691,12 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
                            tu.reduce_shift);
     out_bytes += jobs[k].nbytes * jobs[k].ndst * jobs[k].rows;
   }
-  std::vector<uint8_t> table;
-  append(table, begin.data(), begin.size());
-  append(table, jobs.data(), jobs.size());
-  append(table, ptrs.data(), ptrs.size());
+  append(*table, begin.data(), begin.size());
+  append(*table, jobs.data(), jobs.size());
+  append(*table, ptrs.data(), ptrs.size());
 #ifdef FSDP_TABLE_HOOK
-  fsdp_table_hook(1, dtype, (uint32_t)jobs.size(), n, tu.reduce_shift, table);
+  fsdp_table_hook(1, dtype, (uint32_t)jobs.size(), n, tu.reduce_shift, *table);
 #endif
-  int rc = upload(table, p);
-  if (rc) return rc;
   p->launch = true;
   p->reduce = true;
   p->n_items = (uint32_t)jobs.size();
@@ -666,7 +705,42 @@ int plan_reduce(std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, in
   p->es = dtype;
   p->nsrc = jobs[0].nsrc;
   p->avg = avg;
-  p->nts = stream_stores(reuse, out_bytes);
+  p->nts = stream_stores(reuse, out_bytes + other_out);
+  return FSDP_OK;
+}
+
+// Output bytes of a call's fold-reduce items.
+uint64_t fold_reduce_out_bytes(const std::vector<fsdp::FoldRed>& items) {
+  uint64_t n = 0;
+  for (const auto& f : items) n += f.rows * f.nrank * f.run_bytes;
+  return n;
+}
+
+// Plan the fold-reduce items of a reduction (a launch of its own; every
+// item with the same operand count) into *table.
+int plan_fold_reduce(const std::vector<fsdp::FoldRed>& items, const std::vector<uint64_t>& ptrs, int dtype, int avg,
+                     Reuse reuse, uint64_t other_out, Plan* p, std::vector<uint8_t>* table) {
+  if (items.empty()) return FSDP_OK;
+  if (items.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many fold items");
+  std::vector<uint64_t> begin(items.size());
+  uint64_t n = 0;
+  for (size_t k = 0; k < items.size(); ++k) {
+    begin[k] = n;
+    n += (items[k].rows + items[k].rows_per_chunk - 1) / items[k].rows_per_chunk;
+  }
+  append(*table, begin.data(), begin.size());
+  append(*table, items.data(), items.size());
+  append(*table, ptrs.data(), ptrs.size());
+#ifdef FSDP_TABLE_HOOK
+  fsdp_table_hook(4, dtype, (uint32_t)items.size(), n, fsdp::tuning().reduce_shift, *table);
+#endif
+  p->fold_items = (uint32_t)items.size();
+  p->fold_chunks = n;
+  p->fold_nts = stream_stores(reuse, fold_reduce_out_bytes(items) + other_out);
+  p->fold_reduce = true;
+  p->fold_elt = dtype;
+  p->fold_nsrc = items[0].nrank;
+  p->fold_avg = avg;
   return FSDP_OK;
 }
 
@@ -701,11 +775,22 @@ int run_copy(Key&& key, std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, h
 }
 
 int run_reduce(Key&& key, std::vector<fsdp::RedJob>& jobs, std::vector<uint64_t>& ptrs, int dtype, int avg,
-               Reuse reuse, hipStream_t stream) {
+               Reuse reuse, hipStream_t stream, const std::vector<fsdp::FoldRed>& folds = {},
+               const std::vector<uint64_t>& fold_ptrs = {}) {
   if (int rc = check_not_capturing(stream)) return rc;
+  uint64_t job_out = 0;
+  for (const auto& jb : jobs) job_out += jb.nbytes * jb.ndst * jb.rows;
   Plan p;
-  int rc = plan_reduce(jobs, ptrs, dtype, avg, reuse, &p);
-  if (rc) return rc;
+  std::vector<uint8_t> job_table, fold_table;
+  int rc = plan_reduce(jobs, ptrs, dtype, avg, reuse, fold_reduce_out_bytes(folds), &p, &job_table);
+  if (!rc) rc = plan_fold_reduce(folds, fold_ptrs, dtype, avg, reuse, job_out, &p, &fold_table);
+  // both tables are built before either is uploaded
+  if (!rc && !job_table.empty()) rc = upload(job_table, &p);
+  if (!rc && !fold_table.empty()) rc = upload_table(fold_table, &p.fold_dev, &p.fold_bytes, &p.device);
+  if (rc) {
+    p.free_tables();
+    return rc;
+  }
   return store_and_launch(std::move(key), std::move(p), stream);
 }
 
@@ -1092,20 +1177,31 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     }
   }
   // short rows (every rank of a dim-k chunk the same run): the S ranks of a
-  // shard group read pieces of the same gradient lines, so their jobs for
-  // the same rows go next to each other, one job per chunk of rows
+  // shard group read pieces of the same gradient lines.  One fold-reduce
+  // item per group sums whole gradient rows and hands each rank its piece;
+  // where the widths do not allow it, the ranks' jobs for the same rows go
+  // next to each other, one job per chunk of rows
+  std::vector<fsdp::FoldRed> folds;
+  std::vector<uint64_t> fold_ptrs;
   for (int32_t d = 0; d < R / S; ++d) {
     for (int32_t i = 0; i < P; ++i) {
       if (!interleaved[(size_t)i]) continue;
       const uint64_t rows = (uint64_t)L.outer[i];
-      const uint64_t per = CH / (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+      std::vector<uint64_t> src, dst;
+      for (int32_t t = 0; t < S; ++t) {
+        src.push_back((uint64_t)grads[(size_t)(d * S + t) * P + i]);
+        dst.push_back((uint64_t)rs_out[d * S + t] + (uint64_t)(L.in_off[i] * es));
+      }
+      if (push_fold_reduce(folds, fold_ptrs, src, dst, row, rows, es)) continue;
+      const uint64_t per = CH / row;
       for (uint64_t r0 = 0; r0 < rows; r0 += per)
         for (int32_t s = 0; s < S; ++s) push_block(d * S + s, i, r0, std::min(per, rows - r0));
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
   return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext,
-                    static_cast<hipStream_t>(stream));
+                    static_cast<hipStream_t>(stream), folds, fold_ptrs);
 }
 
 int fused_ar_impl(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,

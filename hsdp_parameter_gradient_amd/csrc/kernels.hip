@@ -1070,6 +1070,188 @@ __global__ __launch_bounds__(kBlock) void fold_copy_kernel(const uint64_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// fold_reduce
+// ---------------------------------------------------------------------------
+
+// A unit of W bytes as 32-bit words (a 2-byte unit in the low half of one).
+template <typename W>
+struct UnitWords {
+  static constexpr int N = sizeof(W) >= 4 ? (int)(sizeof(W) / 4) : 1;
+  uint32_t w[N];
+};
+template <typename W>
+__device__ __forceinline__ UnitWords<W> to_words(W v) {
+  UnitWords<W> u;
+  if constexpr (sizeof(W) == 16) {
+    u.w[0] = v.x, u.w[1] = v.y, u.w[2] = v.z, u.w[3] = v.w;
+  } else if constexpr (sizeof(W) == 8) {
+    u.w[0] = (uint32_t)v, u.w[1] = (uint32_t)(v >> 32);
+  } else {
+    u.w[0] = (uint32_t)v;
+  }
+  return u;
+}
+template <typename W>
+__device__ __forceinline__ W from_words(const UnitWords<W>& u) {
+  if constexpr (sizeof(W) == 16) return W{u.w[0], u.w[1], u.w[2], u.w[3]};
+  else if constexpr (sizeof(W) == 8) return (W)u.w[0] | ((W)u.w[1] << 32);
+  else return (W)u.w[0];
+}
+
+// Element e of kind E of a unit, in float32 (exactly).
+template <int E, typename W>
+__device__ __forceinline__ float unit_elt(const UnitWords<W>& u, int e) {
+  if constexpr (E == kF32) return __builtin_bit_cast(float, u.w[e]);
+  else return elt_to_f32<E>((u.w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+}
+
+// The reduction of K operand units of kind E: summed in ascending operand
+// order from the first operand, in float32; AVG divides by nf; rounded once.
+template <int E, typename W, int K>
+__device__ __forceinline__ W reduce_unit(const W (&v)[K], int avg, float nf) {
+  constexpr int NE = (int)sizeof(W) / (E == kF32 ? 4 : 2);
+  UnitWords<W> in[K];
+#pragma unroll
+  for (int t = 0; t < K; ++t) in[t] = to_words<W>(v[t]);
+  UnitWords<W> out;
+#pragma unroll
+  for (int i = 0; i < UnitWords<W>::N; ++i) out.w[i] = 0;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    float acc = unit_elt<E, W>(in[0], e);
+#pragma unroll
+    for (int t = 1; t < K; ++t) acc = acc + unit_elt<E, W>(in[t], e);
+    if (avg) acc = acc / nf;
+    if constexpr (E == kF32) out.w[e] = __builtin_bit_cast(uint32_t, acc);
+    else out.w[e >> 1] |= f32_to_elt<E>(acc) << ((e & 1) * 16);
+  }
+  return from_words<W>(out);
+}
+
+// Rows [r0, r0 + nr) of a fold-reduce item in W-sized units: unit q of the
+// chunk is full-tensor row q / upf of the chunk, rank s = (q % upf) / upr
+// and unit col = q % upr of that rank's piece.  Every operand is read at q
+// units from its chunk start (whole lines, consecutive lanes on consecutive
+// units); the result goes to rank s's rows.  Compile-time K: the operand
+// and destination bases are wave-uniform registers, the destination of a
+// unit a select among the K bases, and U units per lane per iteration keep
+// all K*U loads in flight.  K = 0: any operand count, loads one at a time.
+template <int E, int K, typename W, bool NTS>
+__device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
+                                                  uint64_t r0, uint32_t nr, int avg) {
+  const uint32_t S = f.nrank;
+  const uint32_t upr = (uint32_t)(f.run_bytes / sizeof(W));
+  const uint32_t upf = S * upr;
+  const uint32_t n = nr * upf;
+  const uint32_t run = (uint32_t)f.run_bytes;
+  const uint64_t src_off = r0 * S * f.run_bytes;
+  const uint64_t dst_off = r0 * f.run_bytes;
+  const float nf = (float)S;
+  auto split = [&](uint32_t q, uint32_t* s, uint32_t* dof) {
+    const uint32_t row = q / upf;
+    const uint32_t rem = q - row * upf;
+    *s = rem / upr;
+    *dof = row * run + (rem - *s * upr) * (uint32_t)sizeof(W);
+  };
+  auto st = [](uint64_t a, W v) {
+    if (NTS)
+      __builtin_nontemporal_store(v, gptr<W>(a));
+    else
+      *gptr<W>(a) = v;
+  };
+  uint32_t base = 0;
+  if constexpr (K > 0) {
+    constexpr int U0 = sizeof(W) >= 16 ? 8 : 16;
+    constexpr int U = U0 / K > 1 ? U0 / K : 1;
+    uint64_t sb[K], db[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+      sb[t] = ptr[f.src0 + t] + src_off;
+      db[t] = ptr[f.dst0 + t] + dst_off;
+    }
+    auto dst_base = [&](uint32_t s) {
+      uint64_t d = db[0];
+#pragma unroll
+      for (int t = 1; t < K; ++t) d = s == (uint32_t)t ? db[t] : d;
+      return d;
+    };
+    for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
+      W v[U][K];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < K; ++t)
+          v[u][t] = __builtin_nontemporal_load(gptr<W>(sb[t] + (uint64_t)(base + threadIdx.x + u * kBlock) * sizeof(W)));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t s, dof;
+        split(base + threadIdx.x + u * kBlock, &s, &dof);
+        st(dst_base(s) + dof, reduce_unit<E, W, K>(v[u], avg, nf));
+      }
+    }
+    for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
+      W v[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) v[t] = __builtin_nontemporal_load(gptr<W>(sb[t] + (uint64_t)q * sizeof(W)));
+      uint32_t s, dof;
+      split(q, &s, &dof);
+      st(dst_base(s) + dof, reduce_unit<E, W, K>(v, avg, nf));
+    }
+  } else {
+    constexpr int NE = (int)sizeof(W) / (E == kF32 ? 4 : 2);
+    for (uint32_t q = threadIdx.x; q < n; q += kBlock) {
+      const uint64_t so = src_off + (uint64_t)q * sizeof(W);
+      float acc[NE];
+      {
+        const UnitWords<W> u = to_words<W>(__builtin_nontemporal_load(gptr<W>(ptr[f.src0] + so)));
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = unit_elt<E, W>(u, e);
+      }
+      for (uint32_t t = 1; t < S; ++t) {
+        const UnitWords<W> u = to_words<W>(__builtin_nontemporal_load(gptr<W>(ptr[f.src0 + t] + so)));
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = acc[e] + unit_elt<E, W>(u, e);
+      }
+      UnitWords<W> out;
+#pragma unroll
+      for (int i = 0; i < UnitWords<W>::N; ++i) out.w[i] = 0;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float a = avg ? acc[e] / nf : acc[e];
+        if constexpr (E == kF32) out.w[e] = __builtin_bit_cast(uint32_t, a);
+        else out.w[e >> 1] |= f32_to_elt<E>(a) << ((e & 1) * 16);
+      }
+      uint32_t s, dof;
+      split(q, &s, &dof);
+      st(ptr[f.dst0 + s] + dst_off + dof, from_words<W>(out));
+    }
+  }
+}
+
+template <int E, int K, bool NTS>
+__global__ __launch_bounds__(kBlock) void fold_reduce_kernel(const uint64_t* __restrict__ begin,
+                                                             const fsdp::FoldRed* __restrict__ items,
+                                                             const uint64_t* __restrict__ ptr, uint32_t n_item,
+                                                             uint64_t n_chunks, int avg) {
+  for (uint64_t slot = blockIdx.x; slot < n_chunks; slot += gridDim.x) {
+    const uint64_t c = xcd_chunk(slot, n_chunks);
+    const uint32_t j = find_item(begin, n_item, c);
+    const fsdp::FoldRed f = items[j];
+    const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
+    const uint64_t left = f.rows - r0;
+    const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);
+    switch (f.unit) {
+      case 16: fold_reduce_units<E, K, u32x4, NTS>(f, ptr, r0, nr, avg); break;
+      case 8: fold_reduce_units<E, K, uint64_t, NTS>(f, ptr, r0, nr, avg); break;
+      case 4: fold_reduce_units<E, K, uint32_t, NTS>(f, ptr, r0, nr, avg); break;
+      default:
+        if constexpr (E != kF32) fold_reduce_units<E, K, uint16_t, NTS>(f, ptr, r0, nr, avg);
+        break;
+    }
+  }
+}
+
 // One workgroup per chunk up to max_grid; a capped grid is a multiple of 8
 // so that every grid-stride step keeps each workgroup on its XCD.
 inline uint32_t grid_for(uint64_t n_chunks, uint32_t max_grid) {
@@ -1171,5 +1353,45 @@ int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, 
     go(fold_copy_kernel<true>, begin, folds, n_fold, n_chunks);
   else
     go(fold_copy_kernel<false>, begin, folds, n_fold, n_chunks);
+  return (int)hipGetLastError();
+}
+
+namespace {
+template <int E, bool NTS>
+void launch_fold_reduce_k(const Launch& go, uint32_t n_src, const uint64_t* begin, const fsdp::FoldRed* items,
+                          const uint64_t* ptr, uint32_t n_item, uint64_t n_chunks, int avg) {
+  switch (n_src) {
+    case 2: go(fold_reduce_kernel<E, 2, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
+    case 4: go(fold_reduce_kernel<E, 4, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
+    case 8: go(fold_reduce_kernel<E, 8, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
+    default: go(fold_reduce_kernel<E, 0, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
+  }
+}
+
+template <int E>
+void launch_fold_reduce_e(const Launch& go, int stream_stores, uint32_t n_src, const uint64_t* begin,
+                          const fsdp::FoldRed* items, const uint64_t* ptr, uint32_t n_item, uint64_t n_chunks,
+                          int avg) {
+  if (stream_stores)
+    launch_fold_reduce_k<E, true>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+  else
+    launch_fold_reduce_k<E, false>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+}
+}  // namespace
+
+int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uint32_t n_src, uint64_t n_chunks,
+                            uint32_t max_grid, int avg, int stream_stores, void* stream, void* start_event,
+                            void* stop_event) {
+  const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
+  const fsdp::FoldRed* items = reinterpret_cast<const fsdp::FoldRed*>(begin + n_item);
+  const uint64_t* ptr = reinterpret_cast<const uint64_t*>(items + n_item);
+  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
+                  static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  switch (elt) {
+    case kF32: launch_fold_reduce_e<kF32>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    case kBF16: launch_fold_reduce_e<kBF16>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    case kF16: launch_fold_reduce_e<kF16>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }

@@ -6,6 +6,7 @@
 //   copy table    uint64 chunk_begin[n]  |  CopySeg seg[n]
 //   reduce table  uint64 chunk_begin[n]  |  RedJob job[n]  |  uint64 ptr[m]
 //   fold table    uint64 chunk_begin[n]  |  FoldSeg fold[n]
+//   fold-reduce   uint64 chunk_begin[n]  |  FoldRed item[n]  |  uint64 ptr[m]
 //
 // Work is cut into chunks of (1 << chunk_shift) destination bytes.  Chunk k
 // of a one-row item covers the window [base + k*CH, base + (k+1)*CH)
@@ -88,9 +89,30 @@ struct FoldSeg {
   uint32_t reserved;
 };
 
+// The fused RS of a parameter sharded on a non-zero dim with short chunk
+// rows, one shard group at a time: the group's nrank gradients are `rows`
+// full-tensor rows of nrank pieces of run_bytes each (piece s of row r is
+// row r of rank s's chunk), gradient t contiguous from ptr[src0 + t].  The
+// rows are summed over t in ascending order (whole rows, whole lines) and
+// piece s of the result goes to rank s's output, whose rows are dense from
+// ptr[dst0 + s].  A chunk is rows_per_chunk whole full-tensor rows (at most
+// the chunk size of destination bytes).  unit (16, 8, 4 or 2, at least the
+// element size) is the access width; it divides run_bytes and every pointer.
+struct FoldRed {
+  uint64_t run_bytes;
+  uint64_t rows;
+  uint64_t rows_per_chunk;
+  uint32_t src0;
+  uint32_t dst0;
+  uint32_t nrank;
+  uint32_t unit;
+  uint64_t reserved[3];
+};
+
 static_assert(sizeof(CopySeg) == 64, "CopySeg layout");
 static_assert(sizeof(RedJob) == 64, "RedJob layout");
 static_assert(sizeof(FoldSeg) == 64, "FoldSeg layout");
+static_assert(sizeof(FoldRed) == 64, "FoldRed layout");
 
 // Number of chunks of a one-row item [dst, dst + nbytes), nbytes > 0.
 inline uint64_t chunk_count(uint64_t dst, uint64_t nbytes, uint32_t shift) {
@@ -123,4 +145,9 @@ int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t 
 // One chunk of a fold item is rows_per_chunk full-tensor rows.
 int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, uint32_t max_grid,
                      int stream_stores, void* stream, void* start_event, void* stop_event);
+// Every item of one launch has n_src = nrank operands; elt as for the
+// reduce launch; one chunk of an item is rows_per_chunk full-tensor rows.
+int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uint32_t n_src, uint64_t n_chunks,
+                            uint32_t max_grid, int avg, int stream_stores, void* stream, void* start_event,
+                            void* stop_event);
 }

@@ -36,6 +36,10 @@ int fsdp_launch_fold(const void*, uint32_t, uint64_t, uint32_t, int, void*, void
   std::fprintf(stderr, "fold launcher reached without a device\n");
   std::abort();
 }
+int fsdp_launch_fold_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, int, int, void*, void*, void*) {
+  std::fprintf(stderr, "fold-reduce launcher reached without a device\n");
+  std::abort();
+}
 
 // Set by the "throw" mode: the hook then throws the given exception kind
 // (1 bad_alloc, 2 length_error, 3 runtime_error), as an allocation inside
@@ -44,7 +48,8 @@ int g_hook_throw = 0;
 
 // With FSDP_TABLE_HOOK, every planned table is appended to the file named
 // by FSDP_DUMP_TABLES (if set): a 32-byte header (kind: 0 copy, 1 reduce,
-// 3 fold; elt, n_items, shift, n_chunks, table bytes) and the table itself.
+// 3 fold copy, 4 fold reduce; elt, n_items, shift, n_chunks, table bytes)
+// and the table itself.
 void fsdp_table_hook(int reduce, int elt, uint32_t n_items, uint64_t n_chunks, uint32_t shift,
                      const std::vector<uint8_t>& table) {
   if (g_hook_throw == 1) throw std::bad_alloc();

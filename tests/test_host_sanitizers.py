@@ -113,9 +113,11 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
     dump = str(tmp_path / "tables.bin")
     _run(driver, {"FSDP_DUMP_TABLES": dump, **TUNINGS[tuning]})
     counts = _check_tables(dump)
-    # the driver's buckets produce copy, reduce and fold tables, strided blocks included
+    # the driver's buckets produce copy, reduce, fold and fold-reduce tables,
+    # strided blocks included
     assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
     assert counts[3] > (10 if tuning != "chunks_512B" else 0), counts
+    assert counts[4] > (10 if tuning != "chunks_512B" else 0), counts
 
 
 def test_random_bucket_tables_pass_the_kernel_emulation(driver, tmp_path):
@@ -140,7 +142,7 @@ def _check_tables(dump):
     tables between two span records), the writes of all its tables together
     cover exactly the call's outputs, each byte once, and every read lies in
     the aligned envelope of the call's inputs."""
-    counts = {0: 0, 1: 0, 3: 0, "blocks": 0}
+    counts = {0: 0, 1: 0, 3: 0, 4: 0, "blocks": 0}
     state = {"outs": None, "ins": None, "w": [], "tables": 0}
 
     def finish():
@@ -181,6 +183,15 @@ def _check_tables(dump):
             w_iv = [(w[0], w[1]) for w in writes]
             r_iv = [(r[0], r[1]) for r in reads]
             # within a table every byte is written once
+            assert sum(y - x for x, y in w_iv) == sum(y - x for x, y in _merge(w_iv))
+        elif kind == 4:
+            raw = blob[8 * n:8 * n + 64 * n]
+            items = [struct.unpack_from(KI.FOLD_RED_FMT, raw, 64 * k) for k in range(n)]
+            ptr = [int(v) for v in np.frombuffer(blob[8 * n + 64 * n:], dtype=np.uint64)]
+            fbegin, c, writes, reads = KI.emulate_fold_reduce(items, ptr, 1 << shift)
+            assert begin == fbegin and c == n_chunks
+            w_iv = [(w[0], w[1]) for w in writes]
+            r_iv = [(r[0], r[1]) for r in reads]
             assert sum(y - x for x, y in w_iv) == sum(y - x for x, y in _merge(w_iv))
         else:
             raw = blob[8 * n:8 * n + 64 * n]

@@ -988,3 +988,106 @@ def test_fold_items_cover_exactly(S, run, gather):
         r, rem = divmod(fa - full, S * run)
         s, x = divmod(rem, run)
         assert raddr == ranks[s] + r * run + x
+
+
+# ---------------------------------------------------------------------------
+# fold_reduce_kernel: the fused RS of short dim-k rows, one shard group per item
+# ---------------------------------------------------------------------------
+
+FOLD_RED_FMT = "<3Q4I3Q"  # run_bytes, rows, rows_per_chunk, src0, dst0, nrank, unit, reserved[3]
+
+
+def fold_reduce_item(src, dst, run, rows, es, shift=13):
+    """A fold-reduce item and its pointers as the planner builds them
+    (push_fold_reduce); None where the planner keeps interleaved jobs."""
+    CH = 1 << shift
+    S = len(src)
+    if S < 2 or not interleave_rows(run, rows) or S * run > CH:
+        return None
+    m = run
+    for a in list(src) + list(dst):
+        m |= a
+    W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
+    if W < es:
+        return None
+    return (run, rows, CH // (S * run), 0, S, S, W, 0, 0, 0), list(src) + list(dst)
+
+
+def emulate_fold_reduce(items, ptr, CH):
+    """Writes as (lo, hi, item, operand offset) and reads as (lo, hi, item),
+    following fold_reduce_kernel: chunk k of item j is full-tensor rows
+    [k*per, ...); unit q of a chunk is row q // upf, rank (q % upf) // upr,
+    column q % upr; every operand is read at the chunk's offset + q units,
+    the result written to rank s's dense rows."""
+    begin, n = [], 0
+    for f in items:
+        begin.append(n)
+        n += -(-f[1] // f[2])
+    writes, reads = [], []
+    for c in range(n):
+        j = find_item(begin, len(items), c)
+        run, rows, per, src0, dst0, S, W = items[j][:7]
+        assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= CH
+        assert all(ptr[k] % W == 0 for k in range(src0, src0 + S)) and all(ptr[k] % W == 0 for k in range(dst0, dst0 + S))
+        r0 = (c - begin[j]) * per
+        nr = min(per, rows - r0)
+        assert nr * S * run < 1 << 32  # the kernel's 32-bit unit indices and offsets
+        upr = run // W
+        upf = S * upr
+        for q in range(nr * upf):
+            row, rem = divmod(q, upf)
+            s, col = divmod(rem, upr)
+            so = r0 * S * run + q * W
+            for t in range(S):
+                reads.append((ptr[src0 + t] + so, ptr[src0 + t] + so + W, j))
+            d = ptr[dst0 + s] + (r0 + row) * run + col * W
+            writes.append((d, d + W, j, so))
+    return begin, n, writes, reads
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+@pytest.mark.parametrize("run", [2, 4, 6, 12, 16, 24, 48, 200])
+@pytest.mark.parametrize("es", [2, 4])
+def test_fold_reduce_items_cover_exactly(S, run, es):
+    """Every byte of every rank's rows is written exactly once, with the
+    reduction of the operands' bytes at that rank's piece of the same full
+    row and column, and every operand is read whole, once per unit."""
+    if run % es:
+        return
+    rows = 700 + 3 * S
+    rng = np.random.default_rng(S * 1000 + run * 10 + es)
+    src = [(1 << 40) + t * (1 << 32) + es * int(rng.integers(0, 8)) for t in range(S)]
+    dst = [(1 << 44) + s * (1 << 32) + es * int(rng.integers(0, 8)) for s in range(S)]
+    made = fold_reduce_item(src, dst, run, rows, es)
+    if made is None:
+        assert S * run > 1 << 13 or not interleave_rows(run, rows)
+        return
+    item, ptr = made
+    W = item[6]
+    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 13)
+    assert all(b - a == W for a, b, _, _ in writes)
+    w_iv = [(a, b) for a, b, _, _ in writes]
+    assert _merge(w_iv) == _merge([(d, d + rows * run) for d in dst])
+    assert sum(b - a for a, b in w_iv) == S * rows * run  # each byte once
+    for a, _, _, so in writes:
+        r, rem = divmod(so, S * run)
+        s, x = divmod(rem, run)
+        assert a == dst[s] + r * run + x
+    for t in range(S):
+        r_t = [(a, b) for a, b, _ in reads if src[t] <= a < src[t] + rows * S * run]
+        assert _merge(r_t) == [(src[t], src[t] + rows * S * run)]
+        assert sum(b - a for a, b in r_t) == rows * S * run
+
+
+def test_fold_reduce_unit_is_the_widest_common_alignment():
+    """The unit divides the row and every pointer and is at least the
+    element; a 2-byte alignment with 4-byte elements keeps interleaved jobs."""
+    src = [1 << 40, (1 << 40) + 4096]
+    dst = [1 << 44, (1 << 44) + 4096]
+    assert fold_reduce_item(src, dst, 32, 100, 4)[0][6] == 16
+    assert fold_reduce_item(src, [dst[0] + 8, dst[1]], 32, 100, 4)[0][6] == 8
+    assert fold_reduce_item(src, dst, 12, 100, 4)[0][6] == 4
+    assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 2)[0][6] == 2
+    assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 4) is None
+    assert fold_reduce_item(src[:1], dst[:1], 32, 100, 4) is None  # one rank: no fold
+    assert fold_reduce_item(src, dst, 256, 100, 4) is None  # long rows stay interleaved-free jobs
