@@ -285,6 +285,7 @@ struct Plan {
   uint64_t fold_chunks = 0;
   int fold_nts = 0;
   bool fold_reduce = false;
+  bool fold_narrow = false;  // fold copy: every item's unit is 2 or 4 bytes
   int fold_elt = 0;
   uint32_t fold_nsrc = 0;
   int fold_avg = 0;
@@ -348,8 +349,8 @@ int enqueue(const Plan& p, hipStream_t stream) {
     int he = p.fold_reduce ? fsdp_launch_fold_reduce(p.fold_elt, p.fold_dev, p.fold_items, p.fold_nsrc,
                                                      p.fold_chunks, max_grid, p.fold_avg, p.fold_nts, stream, t0,
                                                      t1)
-                           : fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_nts,
-                                              stream, t0, t1);
+                           : fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_narrow,
+                                              p.fold_nts, stream, t0, t1);
     if (he != hipSuccess)
       return fail(FSDP_EHIP, "%s launch: %s", p.fold_reduce ? "fold_reduce" : "fold_copy",
                   hipGetErrorString((hipError_t)he));
@@ -557,15 +558,15 @@ void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<s
 // both bases and the rank pitch.  Measured on MI355X against the ranks'
 // interleaved blocks: gathering (AG copy-out) is faster at every width
 // (up to 2.9x); scattering (RS copy-in) is faster with 8- and 16-byte
-// units (up to 1.5x) and 5-13 % slower with 2- and 4-byte ones, so those
-// stay interleaved blocks.
+// units (up to 1.5x) and, staged through LDS, with 2- and 4-byte ones (up
+// to 2.4x).
 bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0, uint64_t rank_pitch, int32_t S,
                uint64_t row_bytes, uint64_t rows, int es, bool gather) {
   const uint64_t CH = uint64_t(1) << fsdp::tuning().copy_shift;
   if (S < 2 || !interleave_rows(row_bytes, rows) || (uint64_t)S * row_bytes > CH) return false;
   const uint64_t m = full | row_bytes | rank0 | rank_pitch;
   const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
-  if (unit < (uint32_t)es || (!gather && unit < 8)) return false;
+  if (unit < (uint32_t)es) return false;
   fsdp::FoldSeg f{};
   f.full = full;
   f.run_bytes = row_bytes;
@@ -670,6 +671,7 @@ int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint
   p->fold_items = (uint32_t)folds.size();
   p->fold_chunks = n;
   p->fold_nts = stream_stores(reuse, fold_out_bytes(folds) + other_out);
+  p->fold_narrow = std::all_of(folds.begin(), folds.end(), [](const fsdp::FoldSeg& f) { return f.unit <= 4; });
   return FSDP_OK;
 }
 

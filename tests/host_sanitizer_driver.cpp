@@ -32,7 +32,7 @@ int fsdp_launch_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t,
   std::fprintf(stderr, "reduce launcher reached without a device\n");
   std::abort();
 }
-int fsdp_launch_fold(const void*, uint32_t, uint64_t, uint32_t, int, void*, void*, void*) {
+int fsdp_launch_fold(const void*, uint32_t, uint64_t, uint32_t, int, int, void*, void*, void*) {
   std::fprintf(stderr, "fold launcher reached without a device\n");
   std::abort();
 }

@@ -916,37 +916,140 @@ def _merge(iv):
     return out
 
 
-def emulate_fold(folds, CH):
-    """Writes as (lo, hi, item) and reads as (lo, hi, item), following
-    fold_copy_kernel: chunk k of item j is full-tensor rows [k*per, ...);
-    unit q of a chunk is row q // upf, rank (q % upf) // upr, column
-    q % upr; the full side is contiguous, rank s's rows dense from
-    rank0 + s*rank_pitch."""
+FOLD_LDS = 18 * 1024  # kFoldLds
+FOLD_LDS_MAX_UNIT = 4  # FSDP_FOLD_LDS_MAX_UNIT
+
+
+def fold_lds_bytes(f, r0, nr):
+    """LDS bytes a fold chunk needs, 0 if it does not fit (fold_lds_bytes)."""
+    full, run, S, gather = f[0], f[1], f[6], f[8]
+    L = nr * run
+    if gather:
+        need = S * ((L + 15) // 16 + 1) * 16
+    else:
+        F0 = full + r0 * S * run
+        need = ((F0 + L * S + 15) & ~15) - (F0 & ~15)
+    return need if need <= FOLD_LDS else 0
+
+
+class Recorder:
+    """Memory for the emulated kernels: records every access as (lo, hi,
+    item); with `mem` (a numpy uint8 array indexed by address) it also
+    moves the bytes."""
+
+    def __init__(self, mem=None):
+        self.mem, self.reads, self.writes, self.item = mem, [], [], 0
+
+    def load(self, a, n):
+        self.reads.append((a, a + n, self.item))
+        return bytes(self.mem[a:a + n]) if self.mem is not None else bytes(n)
+
+    def store(self, a, data):
+        self.writes.append((a, a + len(data), self.item))
+        if self.mem is not None:
+            self.mem[a:a + len(data)] = np.frombuffer(data, dtype=np.uint8)
+
+
+def _ends(lo, hi):
+    """The element runs of [lo, hi) outside its whole aligned vectors."""
+    va, vb = (lo + 15) & ~15, hi & ~15
+    return [(lo, va), (vb, hi)] if va < vb else [(lo, hi)]
+
+
+def fold_lds_chunk(f, r0, nr, io):
+    """One chunk of fold_copy_kernel's LDS path (fold_lds)."""
+    full, run, S, W, gather, pitch, rank0 = f[0], f[1], f[6], f[7], f[8], f[5], f[4]
+    g = 4 if W >= 4 else 2
+    FR, L = S * run, nr * run
+    F0, R0 = full + r0 * FR, rank0 + r0 * run
+    lds = bytearray(FOLD_LDS)
+    if gather:
+        nb = (L + 15) // 16 + 1
+        for i in range(S * nb):  # the kernel's flat block loop
+            s, k = divmod(i, nb)
+            a = R0 + s * pitch
+            blk = (a & ~15) + 16 * k
+            if blk < ((a + L + 15) & ~15):
+                assert 16 * i + 16 <= FOLD_LDS
+                lds[16 * i:16 * i + 16] = io.load(blk, 16)
+
+        def src(x):  # full-side chunk byte x
+            row, rem = divmod(x, FR)
+            s, col = divmod(rem, run)
+            o = s * nb * 16 + ((R0 + s * pitch) & 15) + row * run + col
+            assert o + g <= (s + 1) * nb * 16 <= FOLD_LDS  # inside window s
+            return bytes(lds[o:o + g])
+
+        va, vb = (F0 + 15) & ~15, (F0 + nr * FR) & ~15
+        for v in range(va, vb, 16):
+            io.store(v, b"".join(src(v - F0 + k) for k in range(0, 16, g)))
+        for lo, hi in _ends(F0, F0 + nr * FR):
+            for x in range(lo, hi, g):
+                io.store(x, src(x - F0))
+    else:
+        fa = F0 & ~15
+        delta = F0 - fa
+        for i in range((((F0 + nr * FR + 15) & ~15) - fa) // 16):
+            assert 16 * i + 16 <= FOLD_LDS
+            lds[16 * i:16 * i + 16] = io.load(fa + 16 * i, 16)
+        for s in range(S):
+            d = R0 + s * pitch
+
+            def src(y):  # rank s's chunk byte y
+                row, col = divmod(y, run)
+                o = delta + row * FR + s * run + col
+                assert o + g <= delta + nr * FR <= FOLD_LDS
+                return bytes(lds[o:o + g])
+
+            for v in range((d + 15) & ~15, (d + L) & ~15, 16):
+                io.store(v, b"".join(src(v - d + k) for k in range(0, 16, g)))
+            for lo, hi in _ends(d, d + L):
+                for y in range(lo, hi, g):
+                    io.store(y, src(y - d))
+
+
+def fold_units_chunk(f, r0, nr, io):
+    """One chunk of fold_copy_kernel's unit path (fold_units): unit q of a
+    chunk is row q // upf, rank (q % upf) // upr, column q % upr; the full
+    side is contiguous, rank s's rows dense from rank0 + s*rank_pitch."""
+    full, run, S, W, gather, pitch, rank0 = f[0], f[1], f[6], f[7], f[8], f[5], f[4]
+    assert nr * run < 1 << 32  # the kernel's 32-bit rank-side offsets
+    upr = run // W
+    upf = S * upr
+    full0 = full + r0 * S * run
+    for q in range(nr * upf):
+        row, rem = divmod(q, upf)
+        s, col = divmod(rem, upr)
+        fa = full0 + q * W
+        ra = rank0 + s * pitch + (r0 + row) * run + col * W
+        src, dst = (ra, fa) if gather else (fa, ra)
+        io.store(dst, io.load(src, W))
+
+
+def emulate_fold(folds, CH, io=None, lds=True):
+    """fold_copy_kernel over a fold table: returns the chunk prefix, the
+    chunk count and the reads and writes as (lo, hi, item).  Chunk k of item
+    j is full-tensor rows [k*per, ...); a chunk takes the LDS path when its
+    unit and its windows allow it (lds=False: the unit path always)."""
+    io = io if io is not None else Recorder()
     begin, n = [], 0
     for f in folds:
         begin.append(n)
         n += -(-f[2] // f[3])
-    writes, reads = [], []
     for c in range(n):
         j = find_item(begin, len(folds), c)
-        full, run, rows, per, rank0, pitch, S, W, gather = folds[j][:9]
+        f = folds[j]
+        full, run, rows, per, rank0, pitch, S, W = f[:8]
         assert W in (2, 4, 8, 16) and (full | run | rank0 | pitch) % W == 0
         assert per * S * run <= CH and per >= 1
         r0 = (c - begin[j]) * per
         nr = min(per, rows - r0)
-        assert nr * run < 1 << 32  # the kernel's 32-bit rank-side offsets
-        upr = run // W
-        upf = S * upr
-        full0 = full + r0 * S * run
-        for q in range(nr * upf):
-            row, rem = divmod(q, upf)
-            s, col = divmod(rem, upr)
-            fa = full0 + q * W
-            ra = rank0 + s * pitch + (r0 + row) * run + col * W
-            (src, dst) = (ra, fa) if gather else (fa, ra)
-            reads.append((src, src + W, j))
-            writes.append((dst, dst + W, j))
-    return begin, n, writes, reads
+        io.item = j
+        if lds and W <= FOLD_LDS_MAX_UNIT and fold_lds_bytes(f, r0, nr):
+            fold_lds_chunk(f, r0, nr, io)
+        else:
+            fold_units_chunk(f, r0, nr, io)
+    return begin, n, io.writes, io.reads
 
 
 def fold_item(full, rank0, pitch, S, run, rows, es, gather, shift=14):
@@ -972,7 +1075,7 @@ def test_fold_items_cover_exactly(S, run, gather):
     rank0 = (1 << 44) + es * int(rng.integers(0, 8))
     ranks = [rank0 + s * pitch for s in range(S)]
     f = fold_item(full, rank0, pitch, S, run, rows, es, gather)
-    _, _, writes, reads = emulate_fold([f], 1 << 14)
+    _, _, writes, reads = emulate_fold([f], 1 << 14, lds=False)
     for a, b, _ in writes:
         assert b - a == f[7]
     pairs = sorted(zip(writes, reads))
@@ -1091,3 +1194,46 @@ def test_fold_reduce_unit_is_the_widest_common_alignment():
     assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 4) is None
     assert fold_reduce_item(src[:1], dst[:1], 32, 100, 4) is None  # one rank: no fold
     assert fold_reduce_item(src, dst, 256, 100, 4) is None  # long rows stay interleaved-free jobs
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+@pytest.mark.parametrize("run", [2, 4, 6, 8, 12, 16, 24, 40, 200])
+@pytest.mark.parametrize("gather", [True, False])
+@pytest.mark.parametrize("shift", [9, 14, 16])
+def test_fold_moves_every_byte_to_its_place(S, run, gather, shift):
+    """The byte-level emulation of fold_copy_kernel (both its LDS and its
+    unit path, every chunk shape, bases at every unit alignment) turns the
+    source image into exactly the expected one: full row r is the S ranks'
+    rows r side by side, and no other byte of memory changes."""
+    es = 2 if run % 4 else 4
+    rows = 37 + 5 * S
+    rng = np.random.default_rng(S * 7919 + run * 31 + gather * 3 + shift)
+    size = 1 << 20
+    mem = rng.integers(0, 256, size, dtype=np.uint8)
+    full = 4096 + es * int(rng.integers(0, 16))
+    rank0 = (1 << 18) + es * int(rng.integers(0, 16))
+    pitch = rows * run + es * int(rng.integers(0, 40))
+    f = fold_item(full, rank0, pitch, S, run, rows, es, gather, shift=shift)
+    if f[3] < 1:
+        return  # S*run above the chunk: the planner makes no fold item
+    before = mem.copy()
+    io = Recorder(mem)
+    emulate_fold([f], 1 << shift, io)
+    want = before.copy()
+    for r in range(rows):
+        for s_ in range(S):
+            fa = full + (r * S + s_) * run
+            ra = rank0 + s_ * pitch + r * run
+            if gather:
+                want[fa:fa + run] = before[ra:ra + run]
+            else:
+                want[ra:ra + run] = before[fa:fa + run]
+    assert np.array_equal(mem, want)
+    # every byte written once, reads inside the sources' aligned blocks
+    w_iv = [(a, b) for a, b, _ in io.writes]
+    assert sum(b - a for a, b in w_iv) == sum(b - a for a, b in _merge(w_iv))
+    src = [(full, full + rows * S * run)] if not gather else [(rank0 + s_ * pitch, rank0 + s_ * pitch + rows * run)
+                                                             for s_ in range(S)]
+    env = _merge([(a & ~15, (b + 15) & ~15) for a, b in src])
+    for a, b, _ in io.reads:
+        assert any(x <= a and b <= y for x, y in env), (a, b)
