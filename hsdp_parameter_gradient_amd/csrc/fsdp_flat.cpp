@@ -285,7 +285,7 @@ struct Plan {
   uint64_t fold_chunks = 0;
   int fold_nts = 0;
   bool fold_reduce = false;
-  bool fold_narrow = false;  // fold copy: every item's unit is 2 or 4 bytes
+  bool fold_narrow = false;  // every fold item's unit is 2 or 4 bytes
   int fold_elt = 0;
   uint32_t fold_nsrc = 0;
   int fold_avg = 0;
@@ -347,8 +347,8 @@ int enqueue(const Plan& p, hipStream_t stream) {
   }
   if (p.fold_dev) {
     int he = p.fold_reduce ? fsdp_launch_fold_reduce(p.fold_elt, p.fold_dev, p.fold_items, p.fold_nsrc,
-                                                     p.fold_chunks, max_grid, p.fold_avg, p.fold_nts, stream, t0,
-                                                     t1)
+                                                     p.fold_chunks, max_grid, p.fold_narrow, p.fold_avg,
+                                                     p.fold_nts, stream, t0, t1)
                            : fsdp_launch_fold(p.fold_dev, p.fold_items, p.fold_chunks, max_grid, p.fold_narrow,
                                               p.fold_nts, stream, t0, t1);
     if (he != hipSuccess)
@@ -740,6 +740,7 @@ int plan_fold_reduce(const std::vector<fsdp::FoldRed>& items, const std::vector<
   p->fold_chunks = n;
   p->fold_nts = stream_stores(reuse, fold_reduce_out_bytes(items) + other_out);
   p->fold_reduce = true;
+  p->fold_narrow = std::all_of(items.begin(), items.end(), [](const fsdp::FoldRed& f) { return f.unit <= 4; });
   p->fold_elt = dtype;
   p->fold_nsrc = items[0].nrank;
   p->fold_avg = avg;

@@ -1400,11 +1400,98 @@ __device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const 
   }
 }
 
-template <int E, int K, bool NTS>
+// LDS staging of a fold-reduce chunk with 2- or 4-byte units, when every
+// operand has the same address modulo 16: the operands' aligned 16-byte
+// blocks over the chunk's full rows are reduced block by block (the reduce
+// kernel's arithmetic and operand order; the bytes of the edge blocks
+// outside the chunk are reduced too but never read back) into LDS, then
+// every rank's rows are written as in the scatter of fold_lds.
+__device__ __forceinline__ bool fold_reduce_lds_ok(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
+                                                   uint64_t r0, uint32_t nr) {
+  if (f.unit > FSDP_FOLD_LDS_MAX_UNIT) return false;
+  const uint64_t a = ptr[f.src0];
+  for (uint32_t t = 1; t < f.nrank; ++t)
+    if ((ptr[f.src0 + t] ^ a) & 15u) return false;
+  const uint64_t F0 = a + r0 * f.nrank * f.run_bytes;
+  return align_up16(F0 + (uint64_t)nr * f.nrank * f.run_bytes) - align_down16(F0) <= kFoldLds;
+}
+
+template <int E, int K, typename G, bool NTS>
+__device__ __forceinline__ void fold_reduce_lds(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
+                                                uint64_t r0, uint32_t nr, int avg, uint8_t* lds) {
+  constexpr uint32_t gb = sizeof(G);
+  constexpr uint32_t NE = 16 / gb;
+  const uint32_t S = f.nrank, run = (uint32_t)f.run_bytes;
+  const uint32_t FR = S * run, L = nr * run;
+  const uint64_t off = r0 * FR;  // the chunk's first byte in every operand
+  const uint64_t F0 = ptr[f.src0] + off;
+  const uint64_t fa = align_down16(F0);
+  const uint32_t delta = (uint32_t)(F0 - fa);
+  const uint32_t nblk = (uint32_t)((align_up16(F0 + (uint64_t)nr * FR) - fa) >> 4);
+  const float nf = (float)S;
+  if constexpr (K > 0) {
+    uint64_t sb[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) sb[t] = align_down16(ptr[f.src0 + t] + off);
+    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
+      u32x4 v[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t] + (uint64_t)i * 16));
+      Acc<E> acc = widen<E>(v[0]);
+#pragma unroll
+      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
+      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
+      Acc<E> acc = widen<E>(ldv(gptr<u32x4>(align_down16(ptr[f.src0] + off) + (uint64_t)i * 16)));
+      for (uint32_t t = 1; t < S; ++t)
+        accumulate<E>(acc, ldv(gptr<u32x4>(align_down16(ptr[f.src0 + t] + off) + (uint64_t)i * 16)));
+      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
+    }
+  }
+  __syncthreads();
+  auto rd = [&](uint32_t o) { return *reinterpret_cast<const G*>(lds + o); };
+  auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
+  const uint32_t vmax = L / 16;
+  for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
+    const uint32_t s = i / vmax, j = i - s * vmax;
+    const uint64_t d = ptr[f.dst0 + s] + r0 * run;
+    const uint64_t va = align_up16(d), vb = align_down16(d + L);
+    if (va + (uint64_t)j * 16 >= vb) continue;
+    const uint32_t y = (uint32_t)(va - d) + j * 16;
+    uint32_t row = y / run, col = y - row * run;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (uint32_t k = 0; k < NE; ++k) {
+      w[k * gb / 4] |= (uint32_t)rd(at(row, s, col)) << ((k * gb) % 4 * 8);
+      col += gb;
+      if (col == run) col = 0, ++row;
+    }
+    stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), u32x4{w[0], w[1], w[2], w[3]});
+  }
+  for (uint32_t t = threadIdx.x; t < 2 * S; t += kBlock) {
+    const uint32_t s = t >> 1;
+    const uint64_t d = ptr[f.dst0 + s] + r0 * run;
+    fold_ends<G, NTS>(d, d + L, t & 1u, [&](uint64_t ya) {
+      const uint32_t y = (uint32_t)(ya - d);
+      const uint32_t row = y / run;
+      return rd(at(row, s, y - row * run));
+    });
+  }
+  __syncthreads();  // the next chunk reuses the LDS
+}
+
+// NARROW: every item has a unit of at most FSDP_FOLD_LDS_MAX_UNIT bytes; a
+// chunk that cannot be staged (operands at different offsets modulo 16, or
+// too large for the LDS) takes the runtime-count unit loop, which keeps
+// this variant's registers those of the LDS path.
+template <int E, int K, bool NTS, bool NARROW>
 __global__ __launch_bounds__(kBlock) void fold_reduce_kernel(const uint64_t* __restrict__ begin,
                                                              const fsdp::FoldRed* __restrict__ items,
                                                              const uint64_t* __restrict__ ptr, uint32_t n_item,
                                                              uint64_t n_chunks, int avg) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFoldLds];
   for (uint64_t slot = blockIdx.x; slot < n_chunks; slot += gridDim.x) {
     const uint64_t c = xcd_chunk(slot, n_chunks);
     const uint32_t j = find_item(begin, n_item, c);
@@ -1412,6 +1499,20 @@ __global__ __launch_bounds__(kBlock) void fold_reduce_kernel(const uint64_t* __r
     const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
     const uint64_t left = f.rows - r0;
     const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);
+    if (fold_reduce_lds_ok(f, ptr, r0, nr)) {
+      if (f.unit == 4)
+        fold_reduce_lds<E, K, uint32_t, NTS>(f, ptr, r0, nr, avg, lds);
+      else if constexpr (E != kF32)
+        fold_reduce_lds<E, K, uint16_t, NTS>(f, ptr, r0, nr, avg, lds);
+      continue;
+    }
+    if constexpr (NARROW) {
+      if (f.unit == 4)
+        fold_reduce_units<E, 0, uint32_t, NTS>(f, ptr, r0, nr, avg);
+      else if constexpr (E != kF32)
+        fold_reduce_units<E, 0, uint16_t, NTS>(f, ptr, r0, nr, avg);
+      continue;
+    }
     switch (f.unit) {
       case 16: fold_reduce_units<E, K, u32x4, NTS>(f, ptr, r0, nr, avg); break;
       case 8: fold_reduce_units<E, K, uint64_t, NTS>(f, ptr, r0, nr, avg); break;
@@ -1535,40 +1636,47 @@ int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, 
 }
 
 namespace {
-template <int E, bool NTS>
+template <int E, bool NTS, bool NARROW>
 void launch_fold_reduce_k(const Launch& go, uint32_t n_src, const uint64_t* begin, const fsdp::FoldRed* items,
                           const uint64_t* ptr, uint32_t n_item, uint64_t n_chunks, int avg) {
   switch (n_src) {
-    case 2: go(fold_reduce_kernel<E, 2, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
-    case 4: go(fold_reduce_kernel<E, 4, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
-    case 8: go(fold_reduce_kernel<E, 8, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
-    default: go(fold_reduce_kernel<E, 0, NTS>, begin, items, ptr, n_item, n_chunks, avg); break;
+    case 2: go(fold_reduce_kernel<E, 2, NTS, NARROW>, begin, items, ptr, n_item, n_chunks, avg); break;
+    case 4: go(fold_reduce_kernel<E, 4, NTS, NARROW>, begin, items, ptr, n_item, n_chunks, avg); break;
+    case 8: go(fold_reduce_kernel<E, 8, NTS, NARROW>, begin, items, ptr, n_item, n_chunks, avg); break;
+    default: go(fold_reduce_kernel<E, 0, NTS, NARROW>, begin, items, ptr, n_item, n_chunks, avg); break;
   }
 }
 
 template <int E>
-void launch_fold_reduce_e(const Launch& go, int stream_stores, uint32_t n_src, const uint64_t* begin,
+void launch_fold_reduce_e(const Launch& go, int narrow, int stream_stores, uint32_t n_src, const uint64_t* begin,
                           const fsdp::FoldRed* items, const uint64_t* ptr, uint32_t n_item, uint64_t n_chunks,
                           int avg) {
-  if (stream_stores)
-    launch_fold_reduce_k<E, true>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
-  else
-    launch_fold_reduce_k<E, false>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+  if (narrow) {
+    if (stream_stores)
+      launch_fold_reduce_k<E, true, true>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+    else
+      launch_fold_reduce_k<E, false, true>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+  } else {
+    if (stream_stores)
+      launch_fold_reduce_k<E, true, false>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+    else
+      launch_fold_reduce_k<E, false, false>(go, n_src, begin, items, ptr, n_item, n_chunks, avg);
+  }
 }
 }  // namespace
 
 int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uint32_t n_src, uint64_t n_chunks,
-                            uint32_t max_grid, int avg, int stream_stores, void* stream, void* start_event,
-                            void* stop_event) {
+                            uint32_t max_grid, int narrow, int avg, int stream_stores, void* stream,
+                            void* start_event, void* stop_event) {
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::FoldRed* items = reinterpret_cast<const fsdp::FoldRed*>(begin + n_item);
   const uint64_t* ptr = reinterpret_cast<const uint64_t*>(items + n_item);
   const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
                   static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   switch (elt) {
-    case kF32: launch_fold_reduce_e<kF32>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
-    case kBF16: launch_fold_reduce_e<kBF16>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
-    case kF16: launch_fold_reduce_e<kF16>(go, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    case kF32: launch_fold_reduce_e<kF32>(go, narrow, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    case kBF16: launch_fold_reduce_e<kBF16>(go, narrow, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
+    case kF16: launch_fold_reduce_e<kF16>(go, narrow, stream_stores, n_src, begin, items, ptr, n_item, n_chunks, avg); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

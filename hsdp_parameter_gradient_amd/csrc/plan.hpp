@@ -147,8 +147,9 @@ int fsdp_launch_reduce(int elt, const void* dev_table, uint32_t n_job, uint32_t 
 int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, uint32_t max_grid, int narrow,
                      int stream_stores, void* stream, void* start_event, void* stop_event);
 // Every item of one launch has n_src = nrank operands; elt as for the
-// reduce launch; one chunk of an item is rows_per_chunk full-tensor rows.
+// reduce launch; one chunk of an item is rows_per_chunk full-tensor rows;
+// narrow: every item's unit is 2 or 4 bytes (the LDS-staged path).
 int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uint32_t n_src, uint64_t n_chunks,
-                            uint32_t max_grid, int avg, int stream_stores, void* stream, void* start_event,
-                            void* stop_event);
+                            uint32_t max_grid, int narrow, int avg, int stream_stores, void* stream,
+                            void* start_event, void* stop_event);
 }

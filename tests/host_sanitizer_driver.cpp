@@ -36,7 +36,8 @@ int fsdp_launch_fold(const void*, uint32_t, uint64_t, uint32_t, int, int, void*,
   std::fprintf(stderr, "fold launcher reached without a device\n");
   std::abort();
 }
-int fsdp_launch_fold_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, int, int, void*, void*, void*) {
+int fsdp_launch_fold_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint32_t, int, int, int, void*, void*,
+                            void*) {
   std::fprintf(stderr, "fold-reduce launcher reached without a device\n");
   std::abort();
 }

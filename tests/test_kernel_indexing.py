@@ -1116,36 +1116,97 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13):
     return (run, rows, CH // (S * run), 0, S, S, W, 0, 0, 0), list(src) + list(dst)
 
 
-def emulate_fold_reduce(items, ptr, CH):
-    """Writes as (lo, hi, item, operand offset) and reads as (lo, hi, item),
-    following fold_reduce_kernel: chunk k of item j is full-tensor rows
-    [k*per, ...); unit q of a chunk is row q // upf, rank (q % upf) // upr,
-    column q % upr; every operand is read at the chunk's offset + q units,
-    the result written to rank s's dense rows."""
+def fold_reduce_lds_ok(f, ptr, r0, nr):
+    """Does a fold-reduce chunk take the LDS path (fold_reduce_lds_ok)?"""
+    run, rows, per, src0, dst0, S, W = f[:7]
+    if W > FOLD_LDS_MAX_UNIT:
+        return False
+    a = ptr[src0]
+    if any((ptr[src0 + t] ^ a) & 15 for t in range(1, S)):
+        return False
+    F0 = a + r0 * S * run
+    return ((F0 + nr * S * run + 15) & ~15) - (F0 & ~15) <= FOLD_LDS
+
+
+def _sum_bytes(blocks, dtype):
+    """The elementwise reduction of equal-length byte strings holding
+    `dtype` values: summed in float32 in operand order from the first,
+    rounded once to dtype (the kernels' arithmetic, SUM)."""
+    vals = [np.frombuffer(b, dtype=dtype).astype(np.float32) for b in blocks]
+    acc = vals[0].copy()
+    with np.errstate(invalid="ignore", over="ignore"):  # edge-block bytes outside the rows may be any bits
+        for v in vals[1:]:
+            acc = acc + v
+        return acc.astype(dtype).tobytes()
+
+
+def emulate_fold_reduce(items, ptr, CH, io=None, lds=True, dtype=np.float32):
+    """fold_reduce_kernel over a fold-reduce table: the chunk prefix, the
+    chunk count, the writes as (lo, hi, item, operand offset or None) and
+    the reads as (lo, hi, item).  Chunk k of item j is full-tensor rows
+    [k*per, ...).  Unit path: unit q of a chunk is row q // upf, rank
+    (q % upf) // upr, column q % upr; every operand is read at the chunk's
+    offset + q units, the result written to rank s's dense rows.  LDS path
+    (lds=True, 2- and 4-byte units, operands at one offset modulo 16): the
+    operands' aligned blocks over the chunk are reduced into LDS, then every
+    rank's rows are written in aligned vectors and element-wise ends."""
+    io = io if io is not None else Recorder()
     begin, n = [], 0
     for f in items:
         begin.append(n)
         n += -(-f[1] // f[2])
-    writes, reads = [], []
+    writes = []
     for c in range(n):
         j = find_item(begin, len(items), c)
-        run, rows, per, src0, dst0, S, W = items[j][:7]
+        f = items[j]
+        run, rows, per, src0, dst0, S, W = f[:7]
         assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= CH
         assert all(ptr[k] % W == 0 for k in range(src0, src0 + S)) and all(ptr[k] % W == 0 for k in range(dst0, dst0 + S))
         r0 = (c - begin[j]) * per
         nr = min(per, rows - r0)
         assert nr * S * run < 1 << 32  # the kernel's 32-bit unit indices and offsets
+        io.item = j
+        FR, off = S * run, r0 * S * run
+        if lds and fold_reduce_lds_ok(f, ptr, r0, nr):
+            g = 4 if W >= 4 else 2
+            F0 = ptr[src0] + off
+            fa = F0 & ~15
+            delta = F0 - fa
+            nblk = (((F0 + nr * FR + 15) & ~15) - fa) // 16
+            assert nblk * 16 <= FOLD_LDS
+            lds_mem = bytearray(FOLD_LDS)
+            for i in range(nblk):
+                blocks = [io.load(((ptr[src0 + t] + off) & ~15) + 16 * i, 16) for t in range(S)]
+                lds_mem[16 * i:16 * i + 16] = _sum_bytes(blocks, dtype) if io.mem is not None else bytes(16)
+            for s_ in range(S):
+                d = ptr[dst0 + s_] + r0 * run
+
+                def src(y):
+                    row, col = divmod(y, run)
+                    o = delta + row * FR + s_ * run + col
+                    assert o + g <= nblk * 16
+                    return bytes(lds_mem[o:o + g])
+
+                L = nr * run
+                for v in range((d + 15) & ~15, (d + L) & ~15, 16):
+                    io.store(v, b"".join(src(v - d + k) for k in range(0, 16, g)))
+                    writes.append((v, v + 16, j, None))
+                for lo, hi in _ends(d, d + L):
+                    for y in range(lo, hi, g):
+                        io.store(y, src(y - d))
+                        writes.append((y, y + g, j, None))
+            continue
         upr = run // W
         upf = S * upr
         for q in range(nr * upf):
             row, rem = divmod(q, upf)
-            s, col = divmod(rem, upr)
-            so = r0 * S * run + q * W
-            for t in range(S):
-                reads.append((ptr[src0 + t] + so, ptr[src0 + t] + so + W, j))
-            d = ptr[dst0 + s] + (r0 + row) * run + col * W
+            s_, col = divmod(rem, upr)
+            so = off + q * W
+            blocks = [io.load(ptr[src0 + t] + so, W) for t in range(S)]
+            d = ptr[dst0 + s_] + (r0 + row) * run + col * W
+            io.store(d, _sum_bytes(blocks, dtype) if io.mem is not None else bytes(W))
             writes.append((d, d + W, j, so))
-    return begin, n, writes, reads
+    return begin, n, writes, io.reads
 
 
 @pytest.mark.parametrize("S", [2, 3, 4, 8])
@@ -1167,7 +1228,7 @@ def test_fold_reduce_items_cover_exactly(S, run, es):
         return
     item, ptr = made
     W = item[6]
-    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 13)
+    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 13, lds=False)
     assert all(b - a == W for a, b, _, _ in writes)
     w_iv = [(a, b) for a, b, _, _ in writes]
     assert _merge(w_iv) == _merge([(d, d + rows * run) for d in dst])
@@ -1235,5 +1296,48 @@ def test_fold_moves_every_byte_to_its_place(S, run, gather, shift):
     src = [(full, full + rows * S * run)] if not gather else [(rank0 + s_ * pitch, rank0 + s_ * pitch + rows * run)
                                                              for s_ in range(S)]
     env = _merge([(a & ~15, (b + 15) & ~15) for a, b in src])
+    for a, b, _ in io.reads:
+        assert any(x <= a and b <= y for x, y in env), (a, b)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+@pytest.mark.parametrize("run", [2, 4, 6, 8, 12, 16, 40])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("same_offset", [True, False])
+def test_fold_reduce_moves_sums_to_their_place(S, run, dtype, same_offset):
+    """The byte-level emulation of fold_reduce_kernel (LDS path when the
+    operands share their offset modulo 16, else the unit path) writes, for
+    every rank s and row r, the sum over the group of the gradients' piece
+    s of full row r, and changes no other byte."""
+    es = np.dtype(dtype).itemsize
+    if run % es:
+        return
+    rows = 29 + 7 * S
+    rng = np.random.default_rng(S * 131 + run * 7 + es + same_offset)
+    mem = rng.integers(0, 256, 1 << 20, dtype=np.uint8)
+    n_el = rows * S * run // es
+    src, dst = [], []
+    for t in range(S):
+        a = 4096 + t * 40000 + (0 if same_offset else es * t) + 16 * int(rng.integers(0, 4))
+        mem[a:a + n_el * es] = np.frombuffer(rng.integers(-50, 50, n_el).astype(dtype).tobytes(), np.uint8)
+        src.append(a)
+    for s_ in range(S):
+        dst.append((1 << 19) + s_ * 20000 + es * int(rng.integers(0, 16)))
+    made = fold_reduce_item(src, dst, run, rows, es)
+    if made is None:
+        return
+    item, ptr = made
+    before = mem.copy()
+    io = Recorder(mem)
+    emulate_fold_reduce([item], ptr, 1 << 13, io, dtype=dtype)
+    want = before.copy()
+    for r in range(rows):
+        for s_ in range(S):
+            o = (r * S + s_) * run
+            blocks = [bytes(before[a + o:a + o + run]) for a in src]
+            d = dst[s_] + r * run
+            want[d:d + run] = np.frombuffer(_sum_bytes(blocks, dtype), np.uint8)
+    assert np.array_equal(mem, want)
+    env = _merge([(a & ~15, (a + n_el * es + 15) & ~15) for a in src])
     for a, b, _ in io.reads:
         assert any(x <= a and b <= y for x, y in env), (a, b)
