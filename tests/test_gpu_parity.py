@@ -637,6 +637,21 @@ def test_odd_pitch_blocks_all_steps(S, R, dtype, aligned):
     run_nonzero_dims(shapes, dims, S, R, dtype, aligned)
 
 
+@pytest.mark.parametrize("S,R,dtype,aligned", [(2, 4, torch.float32, True), (3, 6, torch.bfloat16, True),
+                                               (4, 8, torch.float16, True), (8, 8, torch.float32, True),
+                                               (16, 16, torch.bfloat16, True), (4, 8, torch.float32, False),
+                                               (8, 16, torch.bfloat16, False), (3, 3, torch.float16, False)])
+def test_narrow_fold_paths_all_steps(S, R, dtype, aligned):
+    """Dim-1 chunks whose rank pieces are 2-12 bytes (2- and 4-byte units):
+    AG copy-out, RS copy-in and the RS copy-reduce stage their chunks through
+    LDS; with buffers at other offsets modulo 16 (aligned=False) the fold
+    reduce takes its unit fallback.  Group sizes cover the compiled operand
+    counts and the runtime-count path; every step against the oracle."""
+    shapes = [(5000, S), (1700, 3 * S), (900, 2 * S, 1), (333, S, 3), (7,), (40, 5 * S)]
+    dims = [1, 1, 1, 1, 0, 1]
+    run_nonzero_dims(shapes, dims, S, R, dtype, aligned)
+
+
 def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):
     note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype} aligned={aligned}")
     # element offsets of the buffers: any, or multiples of 16 bytes
