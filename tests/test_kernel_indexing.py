@@ -1119,7 +1119,7 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13):
 def fold_reduce_lds_ok(f, ptr, r0, nr):
     """Does a fold-reduce chunk take the LDS path (fold_reduce_lds_ok)?"""
     run, rows, per, src0, dst0, S, W = f[:7]
-    if W > FOLD_LDS_MAX_UNIT:
+    if W > FOLD_LDS_MAX_UNIT and S < 4:
         return False
     a = ptr[src0]
     if any((ptr[src0 + t] ^ a) & 15 for t in range(1, S)):
@@ -1147,7 +1147,8 @@ def emulate_fold_reduce(items, ptr, CH, io=None, lds=True, dtype=np.float32):
     [k*per, ...).  Unit path: unit q of a chunk is row q // upf, rank
     (q % upf) // upr, column q % upr; every operand is read at the chunk's
     offset + q units, the result written to rank s's dense rows.  LDS path
-    (lds=True, 2- and 4-byte units, operands at one offset modulo 16): the
+    (lds=True: 2- and 4-byte units, or wider in groups of 4 ranks or more;
+    operands at one offset modulo 16): the
     operands' aligned blocks over the chunk are reduced into LDS, then every
     rank's rows are written in aligned vectors and element-wise ends."""
     io = io if io is not None else Recorder()
