@@ -1,6 +1,6 @@
 // gfx950 kernels of the FSDP/HSDP flat-buffer hot path.
 //
-// Three kernels serve the six device entry points:
+// Four kernels serve the six device entry points:
 //   seg_copy  — segmented copy with zero fill: AG copy-in (pack shards into
 //               padded rank slices), AG copy-out (unpack into the full
 //               parameters) and RS copy-in (chunk gradients into the padded
@@ -8,7 +8,8 @@
 //   fold_copy — AG copy-out and RS copy-in of parameters sharded on a
 //               non-zero dim whose chunk rows are short: all shard ranks'
 //               pieces of whole full-tensor rows per workgroup, so both
-//               sides move whole cache lines.
+//               sides move whole cache lines (2- and 4-byte pieces staged
+//               through LDS).
 //   reduce    — fixed-order reduction, in fp32, of K operands into M
 //               destinations, with a zero-filled tail per job: the RS of a
 //               shard group (K = S, M = 1), the RS read straight from the
@@ -17,8 +18,12 @@
 //               replicate group (K = M = D).  fp32, bf16 or fp16 elements
 //               (16-bit elements widened exactly, summed in fp32, rounded
 //               once to nearest even).
+//   fold_reduce — the RS read straight from the full gradients for the
+//               short-row parameters of fold_copy: one shard group's
+//               gradients summed over whole full-tensor rows (the reduce
+//               arithmetic), each rank's piece written to its output.
 //
-// All three are HBM-bound streaming kernels (no data reuse, no dense
+// All four are HBM-bound streaming kernels (no data reuse, no dense
 // contraction): one workgroup of 256 lanes handles one chunk of destination
 // bytes at a time, with 128-bit loads and stores on 16-byte-aligned
 // destination addresses.  A source whose address differs from the
