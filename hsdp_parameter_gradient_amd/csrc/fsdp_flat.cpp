@@ -324,6 +324,12 @@ void drop_entry(std::list<Entry>::iterator it) {
   g_lru.erase(it);
 }
 
+// Is `stream` being captured into a HIP graph?
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 // Events the calling thread's next kernel launch records at its start and
 // end (fsdp_time_next_launch); taken by that launch.
 thread_local void* g_time_start = nullptr;
@@ -332,10 +338,16 @@ thread_local void* g_time_stop = nullptr;
 int enqueue(const Plan& p, hipStream_t stream) {
   if (!p.launch && !p.fold_dev) return ok();
   const uint32_t max_grid = fsdp::tuning().max_grid;
-  // the first kernel of the call takes a pending timing request
-  void* t0 = g_time_start;
-  void* t1 = g_time_stop;
-  g_time_start = g_time_stop = nullptr;
+  // the first kernel of the call takes a pending timing request (not one
+  // launched into a graph capture: the request then waits for the next
+  // launch outside a capture)
+  void* t0 = nullptr;
+  void* t1 = nullptr;
+  if (g_time_start && !capturing(stream)) {
+    t0 = g_time_start;
+    t1 = g_time_stop;
+    g_time_start = g_time_stop = nullptr;
+  }
   if (p.launch) {
     int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
                                            p.nts, stream, t0, t1)
@@ -356,12 +368,6 @@ int enqueue(const Plan& p, hipStream_t stream) {
                   hipGetErrorString((hipError_t)he));
   }
   return ok();
-}
-
-// Is `stream` being captured into a HIP graph?
-bool capturing(hipStream_t stream) {
-  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  return hipStreamIsCapturing(stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
 }
 
 // Launch the cached plan of `key`, if there is one.

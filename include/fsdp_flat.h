@@ -268,7 +268,8 @@ int fsdp_cache_info(int64_t* n_plans, int64_t* n_pinned, int64_t* table_bytes);
  * around a call include).  start_event and stop_event are hipEvent_t handles
  * the caller created with timing enabled and on the launch's device; both
  * NULL cancels a pending request.  A call that launches nothing (an empty
- * bucket, an AR over one rank) leaves the request pending.
+ * bucket, an AR over one rank), or launches into a stream that is being
+ * captured into a graph, leaves the request pending.
  * Errors: FSDP_EINVAL (exactly one of the two is NULL).
  */
 int fsdp_time_next_launch(void* start_event, void* stop_event);

@@ -1113,4 +1113,24 @@ def test_time_next_launch_records_the_kernel():
     torch.cuda.synchronize()
     us2 = a.elapsed_time(b) * 1e3
     assert us2 != us and 0 < us2 < us, (us2, us)
+    # pending across a launch into a graph capture (the graph records no
+    # events), taken by the next launch outside it
+    m = n // 16
+    hp.fsdp_ag_copy_in([(m,)], 1, [src[:m]], dst[:m])  # cached before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    hp.fsdp_time_next_launch(a, b)
+    with torch.cuda.graph(graph):
+        hp.fsdp_ag_copy_in([(m,)], 1, [src[:m]], dst[:m])
+    torch.cuda.synchronize()
+    dst[:m].zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:m], src[:m])
+    assert a.elapsed_time(b) * 1e3 == us2  # the capture and the replay left the events alone
+    hp.fsdp_ag_copy_in([(n // 2,)], 1, [src[:n // 2]], dst[:n // 2])
+    torch.cuda.synchronize()
+    us3 = a.elapsed_time(b) * 1e3
+    assert us3 != us2 and 0 < us3 < us, (us3, us2, us)
+    del graph
     hp.fsdp_time_next_launch(None, None)
