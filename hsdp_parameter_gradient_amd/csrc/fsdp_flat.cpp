@@ -545,6 +545,19 @@ bool interleave_rows(uint64_t row_bytes, uint64_t rows) {
   return row_bytes > 0 && row_bytes < kInterleaveRow && rows >= 2;
 }
 
+// Dim-k chunk rows that the fold kernels take, over S ranks: short rows,
+// or longer ones that are not a multiple of 8 bytes (each rank's rows then
+// sit at their own alignment, which the fold's LDS staging absorbs), when
+// the S pieces of a full-tensor row fit a chunk of CH bytes.  Measured on
+// MI355X for the long ones against one item (or job) per row or unit-wise
+// blocks: (30000, 2050, 1) bf16 over 2 ranks AG copy-out / RS copy-in / RS
+// copy-reduce 156 / 324 / 276 -> 54 / 97 / 85 us; (20000, 1540) bf16 over 4
+// ranks 42 / 109 / 111 -> 30 / 94 / 59 us.
+bool fold_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH) {
+  if (S < 2 || rows < 2 || row_bytes == 0 || S * row_bytes > CH) return false;
+  return row_bytes < kInterleaveRow || row_bytes % 8 != 0;
+}
+
 // The S ranks' rows of one parameter: base[s] = (first source row, first
 // destination row) of rank s; the same row length, row count and pitches.
 void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<std::pair<uint64_t, uint64_t>>& base,
@@ -569,7 +582,7 @@ void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<s
 bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0, uint64_t rank_pitch, int32_t S,
                uint64_t row_bytes, uint64_t rows, int es, bool gather) {
   const uint64_t CH = uint64_t(1) << fsdp::tuning().copy_shift;
-  if (S < 2 || !interleave_rows(row_bytes, rows) || (uint64_t)S * row_bytes > CH) return false;
+  if (!fold_rows(row_bytes, rows, (uint64_t)S, CH)) return false;
   const uint64_t m = full | row_bytes | rank0 | rank_pitch;
   const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
   if (unit < (uint32_t)es) return false;
@@ -596,7 +609,7 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
                       const std::vector<uint64_t>& dst, uint64_t row_bytes, uint64_t rows, int es) {
   const uint64_t CH = uint64_t(1) << fsdp::tuning().reduce_shift;
   const uint64_t S = src.size();
-  if (S < 2 || dst.size() != S || !interleave_rows(row_bytes, rows) || S * row_bytes > CH) return false;
+  if (dst.size() != S || !fold_rows(row_bytes, rows, S, CH)) return false;
   uint64_t m = row_bytes;
   for (uint64_t a : src) m |= a;
   for (uint64_t a : dst) m |= a;
@@ -930,13 +943,14 @@ int ag_copy_out_impl(const fsdp_bucket_t* bucket, int32_t shard_size, int32_t dt
       return (uint64_t)full[i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
     };
     const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
-    if (L.outer[i] > 1 && interleave_rows((uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es), (uint64_t)L.outer[i])) {
-      // a dim-k chunk (every rank the same run) of short rows: all ranks'
-      // pieces of a full row in one fold item, else the ranks' blocks
-      // interleaved per chunk of rows
-      const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
-      if (push_fold(folds, (uint64_t)full[i], src_of(0), (uint64_t)(L.I * es), S, row, (uint64_t)L.outer[i], es, true))
-        continue;
+    // a dim-k chunk (every rank the same run): all ranks' pieces of whole
+    // full rows in one fold item where its rows allow it, else short rows
+    // as the ranks' blocks interleaved per chunk of rows
+    const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
+    if (L.outer[i] > 1 &&
+        push_fold(folds, (uint64_t)full[i], src_of(0), (uint64_t)(L.I * es), S, row, (uint64_t)L.outer[i], es, true))
+      continue;
+    if (L.outer[i] > 1 && interleave_rows(row, (uint64_t)L.outer[i])) {
       std::vector<std::pair<uint64_t, uint64_t>> base;
       for (int32_t s = 0; s < S; ++s) base.push_back({src_of(s), dst_of(s)});
       push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], row, pitch);
@@ -1000,7 +1014,9 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
           segs.push_back({run ? src : 0, d0, (uint64_t)(run * es), (uint64_t)(L.padded[i] * es)});
           continue;
         }
-        if (interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i])) continue;  // below
+        if (interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i]) ||
+            fold_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift))
+          continue;  // below
         push_rows(segs, src, d0, (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es),
                   (uint64_t)(run * es));
         if (L.padded[i] > data)
@@ -1008,23 +1024,33 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
       }
     }
   }
-  // dim-k chunks of short rows (every rank the same run, no padding): all
-  // ranks' pieces of a full gradient row in one fold item, else the S
-  // ranks' blocks of the same rows next to each other
+  // dim-k chunks (every rank the same run, no padding) whose rows the fold
+  // takes, or short ones: all ranks' pieces of whole full gradient rows in
+  // one fold item, else short rows as the S ranks' blocks of the same rows
+  // next to each other, longer ones as each rank's block
   std::vector<fsdp::FoldSeg> folds;
+  const uint64_t CHC = uint64_t(1) << fsdp::tuning().copy_shift;
   for (int32_t g = 0; g < R; ++g) {
     for (int32_t i = 0; i < P; ++i) {
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
-      if (L.padded[i] == 0 || L.outer[i] == 1 || !interleave_rows(row, (uint64_t)L.outer[i])) continue;
-      auto rank_of = [&](int32_t s) { return (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es); };
-      if (push_fold(folds, (uint64_t)grads[(size_t)g * P + i], rank_of(0), (uint64_t)(L.I * es), S, row,
-                    (uint64_t)L.outer[i], es, false))
+      const uint64_t rows = (uint64_t)L.outer[i];
+      if (L.padded[i] == 0 || L.outer[i] == 1 || !(interleave_rows(row, rows) || fold_rows(row, rows, S, CHC)))
         continue;
-      std::vector<std::pair<uint64_t, uint64_t>> base;
-      for (int32_t s = 0; s < S; ++s)
-        base.push_back({(uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es),
-                        rank_of(s)});
-      push_rows_interleaved(segs, base, row, (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es), row);
+      auto rank_of = [&](int32_t s) { return (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es); };
+      auto grad_of = [&](int32_t s) {
+        return (uint64_t)grads[(size_t)g * P + i] + (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
+      };
+      const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
+      if (push_fold(folds, (uint64_t)grads[(size_t)g * P + i], rank_of(0), (uint64_t)(L.I * es), S, row, rows, es,
+                    false))
+        continue;
+      if (interleave_rows(row, rows)) {
+        std::vector<std::pair<uint64_t, uint64_t>> base;
+        for (int32_t s = 0; s < S; ++s) base.push_back({grad_of(s), rank_of(s)});
+        push_rows_interleaved(segs, base, row, rows, pitch, row);
+        continue;
+      }
+      for (int32_t s = 0; s < S; ++s) push_rows(segs, grad_of(s), rank_of(s), row, rows, pitch, row);
     }
   }
   if ((rc = check_overlap(outs, ins))) return rc;
@@ -1143,58 +1169,66 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     }
     jobs.push_back(jb);
   };
-  std::vector<uint8_t> interleaved((size_t)P, 0);
-  for (int32_t g = 0; g < R; ++g) {
+  // Rank s's chunk of parameter i, for rank g = d*S + s: outer runs of
+  // row_len*inner elements (stride dk*inner in the gradients, dense in the
+  // output), then the zero tail.  block: one strided job fits (the rows fit
+  // a chunk, both pitches keep the rows' alignment or the rows are short,
+  // and there is no tail); else one job per run, the last one with the tail.
+  auto block_ok = [&](int32_t i, int32_t s) {
+    const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+    return L.padded[i] == L.outer[i] * run &&
+           reduce_block_ok((uint64_t)(L.dk[i] * L.inner[i] * es), (uint64_t)(run * es), (uint64_t)(run * es),
+                           (uint64_t)L.outer[i], fsdp::tuning().reduce_shift);
+  };
+  auto emit_rank = [&](int32_t g, int32_t i) {
     const int32_t d = g / S, s = g % S;
-    for (int32_t i = 0; i < P; ++i) {
-      if (L.padded[i] == 0) continue;
-      // rank s's chunk: outer runs of row_len*inner elements (stride
-      // dk*inner in the gradients, dense in the output), then the zero
-      // tail; one strided job when the rows fit a chunk and either both
-      // pitches keep the rows' alignment or the rows are short (and there
-      // is no tail), else one job per run, the last one with the tail
-      const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
-      const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
-      const uint64_t out0 = (uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es);
-      const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
-      const bool block = L.padded[i] == L.outer[i] * run &&
-                         reduce_block_ok(pitch, (uint64_t)(run * es), (uint64_t)(run * es), (uint64_t)L.outer[i],
-                                         fsdp::tuning().reduce_shift);
-      if (block && interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i])) {
-        interleaved[(size_t)i] = 1;  // below, with the other ranks of the group
-        continue;
-      }
-      if (block) {
-        push_block(g, i, 0, (uint64_t)L.outer[i]);
-        continue;
-      }
-      for (int64_t o = 0; o < L.outer[i]; ++o) {
-        const bool last = o + 1 == L.outer[i];
-        const uint64_t row_src = src_off + (uint64_t)o * pitch;
-        fsdp::RedJob jb;
-        jb.nbytes = (uint64_t)((last ? L.padded[i] - o * run : run) * es);
-        jb.data_bytes = (uint64_t)(run * es);
-        jb.src0 = (uint32_t)ptrs.size();
-        jb.nsrc = (uint32_t)S;
-        for (int32_t t = 0; t < S; ++t)
-          ptrs.push_back(run ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + row_src : 0);
-        jb.dst0 = (uint32_t)ptrs.size();
-        jb.ndst = 1;
-        ptrs.push_back(out0 + (uint64_t)(o * run * es));
-        if (jb.nbytes) jobs.push_back(jb);
-      }
+    const int64_t run = L.row_len[(size_t)i * S + s] * L.inner[i];
+    const uint64_t src_off = (uint64_t)(L.row_off[(size_t)i * S + s] * L.inner[i] * es);
+    const uint64_t out0 = (uint64_t)rs_out[g] + (uint64_t)(L.in_off[i] * es);
+    const uint64_t pitch = (uint64_t)(L.dk[i] * L.inner[i] * es);
+    if (block_ok(i, s)) {
+      push_block(g, i, 0, (uint64_t)L.outer[i]);
+      return;
     }
+    for (int64_t o = 0; o < L.outer[i]; ++o) {
+      const bool last = o + 1 == L.outer[i];
+      const uint64_t row_src = src_off + (uint64_t)o * pitch;
+      fsdp::RedJob jb;
+      jb.nbytes = (uint64_t)((last ? L.padded[i] - o * run : run) * es);
+      jb.data_bytes = (uint64_t)(run * es);
+      jb.src0 = (uint32_t)ptrs.size();
+      jb.nsrc = (uint32_t)S;
+      for (int32_t t = 0; t < S; ++t)
+        ptrs.push_back(run ? (uint64_t)grads[(size_t)(d * S + t) * P + i] + row_src : 0);
+      jb.dst0 = (uint32_t)ptrs.size();
+      jb.ndst = 1;
+      ptrs.push_back(out0 + (uint64_t)(o * run * es));
+      if (jb.nbytes) jobs.push_back(jb);
+    }
+  };
+  // Dim-k chunks (every rank the same run, no tail) whose rows the fold
+  // takes, and short rows that fit one block: the S ranks of a shard group
+  // read pieces of the same gradient rows, so they are planned per group
+  // below; everything else per rank here.
+  std::vector<uint8_t> per_group((size_t)P, 0);
+  for (int32_t i = 0; i < P; ++i) {
+    const int64_t run = L.row_len[(size_t)i * S] * L.inner[i];
+    const uint64_t row = (uint64_t)(run * es), rows = (uint64_t)L.outer[i];
+    per_group[(size_t)i] = L.padded[i] > 0 && L.outer[i] > 1 && L.padded[i] == L.outer[i] * run &&
+                           (fold_rows(row, rows, (uint64_t)S, CH) || (block_ok(i, 0) && interleave_rows(row, rows)));
   }
-  // short rows (every rank of a dim-k chunk the same run): the S ranks of a
-  // shard group read pieces of the same gradient lines.  One fold-reduce
-  // item per group sums whole gradient rows and hands each rank its piece;
-  // where the widths do not allow it, the ranks' jobs for the same rows go
-  // next to each other, one job per chunk of rows
+  for (int32_t g = 0; g < R; ++g)
+    for (int32_t i = 0; i < P; ++i)
+      if (L.padded[i] > 0 && !per_group[(size_t)i]) emit_rank(g, i);
+  // One fold-reduce item per group sums whole gradient rows and hands each
+  // rank its piece; where the widths do not allow it, short rows go as the
+  // ranks' jobs for the same rows next to each other, one job per chunk of
+  // rows, and longer ones rank by rank
   std::vector<fsdp::FoldRed> folds;
   std::vector<uint64_t> fold_ptrs;
   for (int32_t d = 0; d < R / S; ++d) {
     for (int32_t i = 0; i < P; ++i) {
-      if (!interleaved[(size_t)i]) continue;
+      if (!per_group[(size_t)i]) continue;
       const uint64_t rows = (uint64_t)L.outer[i];
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
       std::vector<uint64_t> src, dst;
@@ -1203,9 +1237,13 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
         dst.push_back((uint64_t)rs_out[d * S + t] + (uint64_t)(L.in_off[i] * es));
       }
       if (push_fold_reduce(folds, fold_ptrs, src, dst, row, rows, es)) continue;
-      const uint64_t per = CH / row;
-      for (uint64_t r0 = 0; r0 < rows; r0 += per)
-        for (int32_t s = 0; s < S; ++s) push_block(d * S + s, i, r0, std::min(per, rows - r0));
+      if (block_ok(i, 0) && interleave_rows(row, rows)) {
+        const uint64_t per = CH / row;
+        for (uint64_t r0 = 0; r0 < rows; r0 += per)
+          for (int32_t s = 0; s < S; ++s) push_block(d * S + s, i, r0, std::min(per, rows - r0));
+        continue;
+      }
+      for (int32_t s = 0; s < S; ++s) emit_rank(d * S + s, i);
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");

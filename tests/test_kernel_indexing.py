@@ -407,6 +407,15 @@ def interleave_rows(row_bytes, rows):
     return 0 < row_bytes < INTERLEAVE_ROW and rows >= 2
 
 
+def fold_rows(row_bytes, rows, S, CH):
+    """Dim-k chunk rows the fold kernels take (fold_rows): short rows, or
+    longer ones that are not a multiple of 8 bytes, when the S pieces of a
+    full row fit a chunk."""
+    if S < 2 or rows < 2 or row_bytes == 0 or S * row_bytes > CH:
+        return False
+    return row_bytes < INTERLEAVE_ROW or row_bytes % 8 != 0
+
+
 def push_rows_interleaved(segs, base, row_bytes, rows, sp, dp, shift):
     per = (1 << shift) // row_bytes
     for r0 in range(0, rows, per):
@@ -1105,7 +1114,7 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13):
     (push_fold_reduce); None where the planner keeps interleaved jobs."""
     CH = 1 << shift
     S = len(src)
-    if S < 2 or not interleave_rows(run, rows) or S * run > CH:
+    if not fold_rows(run, rows, S, CH):
         return None
     m = run
     for a in list(src) + list(dst):
@@ -1225,7 +1234,7 @@ def test_fold_reduce_items_cover_exactly(S, run, es):
     dst = [(1 << 44) + s * (1 << 32) + es * int(rng.integers(0, 8)) for s in range(S)]
     made = fold_reduce_item(src, dst, run, rows, es)
     if made is None:
-        assert S * run > 1 << 13 or not interleave_rows(run, rows)
+        assert not fold_rows(run, rows, S, 1 << 13)
         return
     item, ptr = made
     W = item[6]
