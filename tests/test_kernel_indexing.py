@@ -1109,12 +1109,14 @@ def test_fold_items_cover_exactly(S, run, gather):
 FOLD_RED_FMT = "<3Q4I3Q"  # run_bytes, rows, rows_per_chunk, src0, dst0, nrank, unit, reserved[3]
 
 
-def fold_reduce_item(src, dst, run, rows, es, shift=13):
+def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     """A fold-reduce item and its pointers as the planner builds them
-    (push_fold_reduce); None where the planner keeps interleaved jobs."""
-    CH = 1 << shift
+    (push_fold_reduce: reduce-sized chunks, or copy-sized ones where a
+    reduce chunk would hold one full row); None where the planner keeps
+    other jobs."""
+    CH, CHX = 1 << shift, 1 << max(shift, copy_shift)
     S = len(src)
-    if not fold_rows(run, rows, S, CH):
+    if not fold_rows(run, rows, S, CHX):
         return None
     m = run
     for a in list(src) + list(dst):
@@ -1122,7 +1124,8 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13):
     W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
     if W < es:
         return None
-    return (run, rows, CH // (S * run), 0, S, S, W, 0, 0, 0), list(src) + list(dst)
+    per = CH // (S * run) if 2 * S * run <= CH else CHX // (S * run)
+    return (run, rows, per, 0, S, S, W, 0, 0, 0), list(src) + list(dst)
 
 
 def fold_reduce_lds_ok(f, ptr, r0, nr):
@@ -1234,11 +1237,11 @@ def test_fold_reduce_items_cover_exactly(S, run, es):
     dst = [(1 << 44) + s * (1 << 32) + es * int(rng.integers(0, 8)) for s in range(S)]
     made = fold_reduce_item(src, dst, run, rows, es)
     if made is None:
-        assert not fold_rows(run, rows, S, 1 << 13)
+        assert not fold_rows(run, rows, S, 1 << 14)
         return
     item, ptr = made
     W = item[6]
-    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 13, lds=False)
+    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 14, lds=False)
     assert all(b - a == W for a, b, _, _ in writes)
     w_iv = [(a, b) for a, b, _, _ in writes]
     assert _merge(w_iv) == _merge([(d, d + rows * run) for d in dst])
@@ -1264,7 +1267,9 @@ def test_fold_reduce_unit_is_the_widest_common_alignment():
     assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 2)[0][6] == 2
     assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 4) is None
     assert fold_reduce_item(src[:1], dst[:1], 32, 100, 4) is None  # one rank: no fold
-    assert fold_reduce_item(src, dst, 256, 100, 4) is None  # long rows stay interleaved-free jobs
+    assert fold_reduce_item(src, dst, 256, 100, 4) is None  # 256-byte rows at a multiple of 8: per-rank jobs
+    assert fold_reduce_item(src, dst, 770, 100, 2)[0][2] == (1 << 13) // (2 * 770)  # 8 KiB chunks
+    assert fold_reduce_item(src, dst, 2052, 100, 2)[0][2] == (1 << 14) // (2 * 2052)  # one row per 8 KiB: 16 KiB
 
 
 @pytest.mark.parametrize("S", [2, 3, 4, 8])
@@ -1311,7 +1316,7 @@ def test_fold_moves_every_byte_to_its_place(S, run, gather, shift):
 
 
 @pytest.mark.parametrize("S", [2, 3, 4, 8])
-@pytest.mark.parametrize("run", [2, 4, 6, 8, 12, 16, 40])
+@pytest.mark.parametrize("run", [2, 4, 6, 8, 12, 16, 40, 770, 2052])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 @pytest.mark.parametrize("same_offset", [True, False])
 def test_fold_reduce_moves_sums_to_their_place(S, run, dtype, same_offset):
@@ -1322,24 +1327,25 @@ def test_fold_reduce_moves_sums_to_their_place(S, run, dtype, same_offset):
     es = np.dtype(dtype).itemsize
     if run % es:
         return
-    rows = 29 + 7 * S
+    rows = 29 + 7 * S if run < 256 else 9
     rng = np.random.default_rng(S * 131 + run * 7 + es + same_offset)
-    mem = rng.integers(0, 256, 1 << 20, dtype=np.uint8)
     n_el = rows * S * run // es
+    span = (n_el * es + 64 + 4095) & ~4095  # per operand, and per destination region
+    mem = rng.integers(0, 256, 4096 + 2 * S * span, dtype=np.uint8)
     src, dst = [], []
     for t in range(S):
-        a = 4096 + t * 40000 + (0 if same_offset else es * t) + 16 * int(rng.integers(0, 4))
+        a = 4096 + t * span + (0 if same_offset else es * t) + 16 * int(rng.integers(0, 4))
         mem[a:a + n_el * es] = np.frombuffer(rng.integers(-50, 50, n_el).astype(dtype).tobytes(), np.uint8)
         src.append(a)
     for s_ in range(S):
-        dst.append((1 << 19) + s_ * 20000 + es * int(rng.integers(0, 16)))
+        dst.append(4096 + (S + s_) * span + es * int(rng.integers(0, 16)))
     made = fold_reduce_item(src, dst, run, rows, es)
     if made is None:
         return
     item, ptr = made
     before = mem.copy()
     io = Recorder(mem)
-    emulate_fold_reduce([item], ptr, 1 << 13, io, dtype=dtype)
+    emulate_fold_reduce([item], ptr, 1 << 14, io, dtype=dtype)
     want = before.copy()
     for r in range(rows):
         for s_ in range(S):
