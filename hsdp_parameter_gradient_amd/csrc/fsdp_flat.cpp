@@ -546,16 +546,19 @@ bool interleave_rows(uint64_t row_bytes, uint64_t rows) {
 }
 
 // Dim-k chunk rows that the fold kernels take, over S ranks: short rows,
-// or longer ones that are not a multiple of 8 bytes (each rank's rows then
-// sit at their own alignment, which the fold's LDS staging absorbs), when
-// the S pieces of a full-tensor row fit a chunk of CH bytes.  Measured on
+// or longer ones that are not a multiple of m bytes (each rank's rows then
+// sit at their own alignment, which the fold absorbs), when the S pieces of
+// a full-tensor row fit a chunk of CH bytes.  Copies use m = 8 (unit-wise
+// blocks of 8-byte units are as fast), the RS copy-reduce m = 16 (its rows
+// at other pitches go element by element or one job per row).  Measured on
 // MI355X for the long ones against one item (or job) per row or unit-wise
 // blocks: (30000, 2050, 1) bf16 over 2 ranks AG copy-out / RS copy-in / RS
 // copy-reduce 156 / 324 / 276 -> 54 / 97 / 85 us; (20000, 1540) bf16 over 4
-// ranks 42 / 109 / 111 -> 30 / 94 / 59 us.
-bool fold_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH) {
+// ranks 42 / 109 / 111 -> 30 / 94 / 59 us; (20000, 1030, 4) fp16 over 2
+// ranks (8-byte units) RS copy-reduce 205 -> 109 us.
+bool fold_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH, uint64_t m) {
   if (S < 2 || rows < 2 || row_bytes == 0 || S * row_bytes > CH) return false;
-  return row_bytes < kInterleaveRow || row_bytes % 8 != 0;
+  return row_bytes < kInterleaveRow || row_bytes % m != 0;
 }
 
 // The S ranks' rows of one parameter: base[s] = (first source row, first
@@ -582,7 +585,7 @@ void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<s
 bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0, uint64_t rank_pitch, int32_t S,
                uint64_t row_bytes, uint64_t rows, int es, bool gather) {
   const uint64_t CH = uint64_t(1) << fsdp::tuning().copy_shift;
-  if (!fold_rows(row_bytes, rows, (uint64_t)S, CH)) return false;
+  if (!fold_rows(row_bytes, rows, (uint64_t)S, CH, 8)) return false;
   const uint64_t m = full | row_bytes | rank0 | rank_pitch;
   const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
   if (unit < (uint32_t)es) return false;
@@ -617,7 +620,7 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
   const uint64_t CH = uint64_t(1) << fsdp::tuning().reduce_shift;
   const uint64_t CHX = fold_reduce_max_chunk();
   const uint64_t S = src.size();
-  if (dst.size() != S || !fold_rows(row_bytes, rows, S, CHX)) return false;
+  if (dst.size() != S || !fold_rows(row_bytes, rows, S, CHX, 16)) return false;
   uint64_t m = row_bytes;
   for (uint64_t a : src) m |= a;
   for (uint64_t a : dst) m |= a;
@@ -1028,7 +1031,7 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
           continue;
         }
         if (interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i]) ||
-            fold_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift))
+            fold_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift, 8))
           continue;  // below
         push_rows(segs, src, d0, (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es),
                   (uint64_t)(run * es));
@@ -1047,7 +1050,7 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
     for (int32_t i = 0; i < P; ++i) {
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
       const uint64_t rows = (uint64_t)L.outer[i];
-      if (L.padded[i] == 0 || L.outer[i] == 1 || !(interleave_rows(row, rows) || fold_rows(row, rows, S, CHC)))
+      if (L.padded[i] == 0 || L.outer[i] == 1 || !(interleave_rows(row, rows) || fold_rows(row, rows, S, CHC, 8)))
         continue;
       auto rank_of = [&](int32_t s) { return (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es); };
       auto grad_of = [&](int32_t s) {
@@ -1228,7 +1231,7 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     const int64_t run = L.row_len[(size_t)i * S] * L.inner[i];
     const uint64_t row = (uint64_t)(run * es), rows = (uint64_t)L.outer[i];
     per_group[(size_t)i] = L.padded[i] > 0 && L.outer[i] > 1 && L.padded[i] == L.outer[i] * run &&
-                           (fold_rows(row, rows, (uint64_t)S, fold_reduce_max_chunk()) ||
+                           (fold_rows(row, rows, (uint64_t)S, fold_reduce_max_chunk(), 16) ||
                             (block_ok(i, 0) && interleave_rows(row, rows)));
   }
   for (int32_t g = 0; g < R; ++g)

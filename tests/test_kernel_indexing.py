@@ -407,13 +407,13 @@ def interleave_rows(row_bytes, rows):
     return 0 < row_bytes < INTERLEAVE_ROW and rows >= 2
 
 
-def fold_rows(row_bytes, rows, S, CH):
+def fold_rows(row_bytes, rows, S, CH, m=8):
     """Dim-k chunk rows the fold kernels take (fold_rows): short rows, or
-    longer ones that are not a multiple of 8 bytes, when the S pieces of a
-    full row fit a chunk."""
+    longer ones that are not a multiple of m bytes (8 for copies, 16 for the
+    RS copy-reduce), when the S pieces of a full row fit a chunk."""
     if S < 2 or rows < 2 or row_bytes == 0 or S * row_bytes > CH:
         return False
-    return row_bytes < INTERLEAVE_ROW or row_bytes % 8 != 0
+    return row_bytes < INTERLEAVE_ROW or row_bytes % m != 0
 
 
 def push_rows_interleaved(segs, base, row_bytes, rows, sp, dp, shift):
@@ -1116,7 +1116,7 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     other jobs."""
     CH, CHX = 1 << shift, 1 << max(shift, copy_shift)
     S = len(src)
-    if not fold_rows(run, rows, S, CHX):
+    if not fold_rows(run, rows, S, CHX, 16):
         return None
     m = run
     for a in list(src) + list(dst):
@@ -1237,7 +1237,7 @@ def test_fold_reduce_items_cover_exactly(S, run, es):
     dst = [(1 << 44) + s * (1 << 32) + es * int(rng.integers(0, 8)) for s in range(S)]
     made = fold_reduce_item(src, dst, run, rows, es)
     if made is None:
-        assert not fold_rows(run, rows, S, 1 << 14)
+        assert not fold_rows(run, rows, S, 1 << 14, 16)
         return
     item, ptr = made
     W = item[6]
@@ -1267,7 +1267,8 @@ def test_fold_reduce_unit_is_the_widest_common_alignment():
     assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 2)[0][6] == 2
     assert fold_reduce_item([src[0] + 2, src[1]], dst, 12, 100, 4) is None
     assert fold_reduce_item(src[:1], dst[:1], 32, 100, 4) is None  # one rank: no fold
-    assert fold_reduce_item(src, dst, 256, 100, 4) is None  # 256-byte rows at a multiple of 8: per-rank jobs
+    assert fold_reduce_item(src, dst, 256, 100, 4) is None  # 256-byte rows at a multiple of 16: per-rank blocks
+    assert fold_reduce_item(src, dst, 264, 100, 4)[0][6] == 8  # a multiple of 8 only: folded
     assert fold_reduce_item(src, dst, 770, 100, 2)[0][2] == (1 << 13) // (2 * 770)  # 8 KiB chunks
     assert fold_reduce_item(src, dst, 2052, 100, 2)[0][2] == (1 << 14) // (2 * 2052)  # one row per 8 KiB: 16 KiB
 
