@@ -652,6 +652,17 @@ def test_narrow_fold_paths_all_steps(S, R, dtype, aligned):
     run_nonzero_dims(shapes, dims, S, R, dtype, aligned)
 
 
+@pytest.mark.parametrize("shapes,S,R,dtype", [
+    ([(2000000, 6)], 2, 4, torch.float32),  # 4-byte pieces: LDS-staged folds, ~1500 copy chunks
+    ([(20000, 2050, 1)], 2, 2, torch.bfloat16),  # 2050-byte rows at every alignment: folded long rows
+    ([(300000, 12), (5000, 1028, 4)], 4, 8, torch.float16),  # 6-byte pieces; 2056-byte rows (8 mod 16)
+])
+def test_fold_paths_at_scale(shapes, S, R, dtype):
+    """The fold kernels over thousands of chunks (tens of MB per rank), every
+    step against the oracle bit for bit."""
+    run_nonzero_dims(shapes, [1] * len(shapes), S, R, dtype, True)
+
+
 def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):
     note(f"[parity] non-zero shard dims S={S} R={R} dtype={dtype} aligned={aligned}")
     # element offsets of the buffers: any, or multiples of 16 bytes
