@@ -451,6 +451,65 @@ def calibration_copy(mib: int, reps: int) -> None:
                                            "launches": reps, "grid": -(-4 * n // (1 << 14))}}), flush=True)
 
 
+# Parameters sharded on dim 1 whose chunk rows are short or sit at per-row
+# alignments (the fold kernels' cases), with a control of 16-byte-aligned
+# rows: (shapes, S, R, dtype name).
+FOLD_SHAPES = [
+    ([(8000000, 6)], 2, 2, "float32"),
+    ([(4000000, 12, 3)], 4, 4, "bfloat16"),
+    ([(1000000, 32)], 4, 4, "float32"),
+    ([(500000, 48)], 8, 16, "float16"),
+    ([(30000, 2050, 1)], 2, 2, "bfloat16"),
+    ([(20000, 1540)], 4, 4, "bfloat16"),
+    ([(20000, 1030, 4)], 2, 2, "float16"),
+    ([(20000, 1024)], 4, 4, "bfloat16"),
+]
+
+
+def fold_shapes(reps: int) -> None:
+    """AG copy-out, RS copy-in and RS copy-reduce of every FOLD_SHAPES case
+    (one parameter sharded on dim 1, SUM): prepared calls issued back to
+    back, events around `reps` calls of each step, one JSON line."""
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    out = []
+    for shapes, S, R, dt_name in FOLD_SHAPES:
+        dt = getattr(torch, dt_name)
+        n = _numel(shapes[0])
+        dims = [1]
+        I = hp.fsdp_bucket_layout(shapes, S, shard_dims=dims).I
+        e = torch.empty(0, dtype=dt).element_size()
+        ag = torch.randn(S * I, device="cuda").to(dt)
+        full = [torch.empty(n, dtype=dt, device="cuda")]
+        g = [torch.randn(n, device="cuda").to(dt) for _ in range(R)]
+        rs_in = [torch.empty(S * I, dtype=dt, device="cuda") for _ in range(R)]
+        rs_out = [torch.empty(I, dtype=dt, device="cuda") for _ in range(R)]
+        calls = {"ag_copy_out": (hp.prepare("fsdp_ag_copy_out", shapes, S, ag, full, dims), 2 * n * e),
+                 "rs_copy_in": (hp.prepare("fsdp_rs_copy_in", shapes, R, S, g, rs_in, dims), R * (n + S * I) * e),
+                 "rs_copy_reduce": (hp.prepare("fsdp_rs_copy_reduce", shapes, R, S, R // S, "sum", g, rs_out, dims),
+                                    R * (n + I) * e)}
+        res = {}
+        for step, (call, nbytes) in calls.items():
+            for _ in range(3):
+                call()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            b.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            res[step] = {"us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log(f"  {shapes[0]} {dt_name} S={S} R={R}: " +
+            ", ".join(f"{k} {v['us']:.1f} us ({v['GB/s']:.0f} GB/s)" for k, v in res.items()))
+        out.append({"shape": list(shapes[0]), "shard_dim": 1, "S": S, "R": R, "dtype": dt_name, "ops": res})
+        del ag, full, g, rs_in, rs_out, calls
+    hp.fsdp_release_cache()
+    print(json.dumps({"fold_shapes": out, "timing": f"events around {reps} back-to-back prepared calls"}), flush=True)
+
+
 def cpu_baseline(w, seconds: float, op: str):
     """The oracle, as it stands, timed on whole steps of the workload (and
     on each of the step's operations, with perf_counter around each oracle
@@ -541,6 +600,8 @@ def main():
                     help="size of the plain device-to-device copy ceiling (0 = skip)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--fold-shapes", action="store_true",
+                    help="only time the dim-1 short-row and odd-pitch cases (fold kernels) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -558,6 +619,9 @@ def main():
         sys.exit(1)
     if args.calibration_copy:
         calibration_copy(args.calibration_copy, max(1, args.steps))
+        return
+    if args.fold_shapes:
+        fold_shapes(max(1, args.steps))
         return
     w = W.WORKLOADS[args.workload]
     R, S, D = w.rank_size, w.shard_size, w.dp_size
