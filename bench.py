@@ -372,7 +372,8 @@ def dataclasses_replace(obj, **kw):
 def pipeline_variant(w, op, layers: int, reps: int):
     """The backward of `layers` buckets of this workload (RS copy-reduce of
     each layer, fused AR of the previous layer): serial on one stream vs the
-    4-step overlap on two streams (BackwardPipeline)."""
+    4-step overlap on two streams (BackwardPipeline), issued eagerly and
+    replayed from a captured HIP graph."""
     import dataclasses
 
     import torch
@@ -390,7 +391,9 @@ def pipeline_variant(w, op, layers: int, reps: int):
         buckets.append(fb)
     pipe = hp.BackwardPipeline(buckets, fused_rs=True)
     out = {"layers": layers}
-    for name, fn in (("serial_ms", pipe.run_serial), ("pipelined_ms", pipe.run_pipelined)):
+    g_serial, g_pipe = pipe.graph(pipelined=False), pipe.graph(pipelined=True)
+    for name, fn in (("serial_ms", pipe.run_serial), ("pipelined_ms", pipe.run_pipelined),
+                     ("graph_serial_ms", g_serial.replay), ("graph_pipelined_ms", g_pipe.replay)):
         for _ in range(3):
             fn()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -401,8 +404,10 @@ def pipeline_variant(w, op, layers: int, reps: int):
         e.record()
         torch.cuda.synchronize()
         out[name] = round(s.elapsed_time(e) / reps, 4)
+    del g_serial, g_pipe
     log(f"  backward pipeline, {layers} layers: serial {out['serial_ms']:.3f} ms, "
-        f"two streams {out['pipelined_ms']:.3f} ms")
+        f"two streams {out['pipelined_ms']:.3f} ms; replayed from a HIP graph: serial "
+        f"{out['graph_serial_ms']:.3f} ms, two streams {out['graph_pipelined_ms']:.3f} ms")
     return out
 
 

@@ -14,7 +14,8 @@ RS copy-reduce) on the RS stream, and the fused AR of layer l-1 on the AR
 stream after an event recorded behind that layer's RS.  run_serial() issues
 the same kernels in the same order on one stream, for comparison; both give
 identical results (every kernel reads and writes the same buffers, only the
-overlap differs).  All streams keep the default priority.
+overlap differs).  graph() captures either order once into a HIP graph.
+All streams keep the default priority.
 """
 
 from __future__ import annotations
@@ -63,6 +64,21 @@ class BackwardPipeline:
         if b.do_ar:
             self.ar_stream.wait_event(self._rs_done[l])
             b.run("fused_ar", self.ar_stream)
+
+    def graph(self, pipelined: bool = True) -> torch.cuda.CUDAGraph:
+        """The backward captured once into a HIP graph (replay() re-runs it):
+        the two-stream order, or the serial one.  Every call is issued once
+        eagerly first, so that the capture records kernel launches only.  A
+        replay runs without the per-layer host work of the eager issue (the
+        event records and cross-stream waits), which on one GPU is what lets
+        the overlap pay."""
+        run = self.run_pipelined if pipelined else self.run_serial
+        run()
+        torch.cuda.current_stream().synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        return g
 
     def run_serial(self) -> None:
         """The same kernels in the same order on the current stream."""

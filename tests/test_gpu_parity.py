@@ -567,7 +567,8 @@ def test_zero_copy_ag_views_one_parameter_buckets():
 @pytest.mark.parametrize("fused_rs", [True, False])
 def test_backward_pipeline_two_streams_matches_serial_and_oracle(fused_rs):
     """The 4-step RS/AR overlap over 5 layers on two streams gives the same
-    fused buffers as the serial order, and both match the oracle."""
+    fused buffers as the serial order, eagerly and replayed from captured HIP
+    graphs, and all match the oracle."""
     R, S = 8, 4
     layer_shapes = [[(7, 8), (5, 3), (16,)], [(1000, 3), (129,)], [(4097, 2)], [(3,), (33, 7)],
                     [(2048, 64), (64,)]]
@@ -585,19 +586,29 @@ def test_backward_pipeline_two_streams_matches_serial_and_oracle(fused_rs):
                                                 O.AVG)
         want.append(fused_o)
     pipe = hp.BackwardPipeline(layers, fused_rs=fused_rs)
-    for rep in range(3):
+    graphs = {}
+    for rep in range(7):
         for fb in layers:  # the RS must rewrite its views; the gaps stay zero
             for v in fb.rs_out:
                 v.fill_(float("nan"))
-        if rep % 2 == 0:
-            pipe.run_pipelined()
-        else:
-            pipe.run_serial()
+        torch.cuda.synchronize()
+        if rep < 3:
+            (pipe.run_pipelined if rep % 2 == 0 else pipe.run_serial)()
+        else:  # replays of the captured backward, eager work between them
+            pipelined = rep % 2 == 1
+            if pipelined not in graphs:
+                graphs[pipelined] = pipe.graph(pipelined=pipelined)
+                for fb in layers:
+                    for v in fb.rs_out:
+                        v.fill_(float("nan"))
+                torch.cuda.synchronize()
+            graphs[pipelined].replay()
         torch.cuda.synchronize()
         for l, fb in enumerate(layers):
             for g in range(R):
                 m = first_mismatch(bits(fb.fused[g]), np_bits(want[l][g]))
                 assert m == "", f"rep {rep} layer {l} rank {g}: {m}"
+    graphs.clear()
 
 
 @pytest.mark.parametrize("S,R,dtype", [(4, 8, torch.float32), (2, 4, torch.bfloat16), (1, 2, torch.float32),
