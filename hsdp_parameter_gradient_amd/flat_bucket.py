@@ -191,3 +191,39 @@ class FusedGroup:
                     fb.run(name, stream)
         if self.do_ar:
             self._ar(stream)
+
+    def graph(self, n_streams: int = 3, fused_rs: bool = False) -> torch.cuda.CUDAGraph:
+        """The step captured once into a HIP graph (replay() re-runs it), with
+        the buckets' AG and RS spread round-robin over n_streams streams (the
+        buckets are independent: their own buffers, disjoint fused segments)
+        and the fused AR after all of them.  Each call is issued once eagerly
+        first, so that the capture records kernel launches only.  Replayed,
+        the short kernels of different buckets run side by side (measured on
+        MI355X, 6 one-parameter buckets of the HSDP block: 298 us eager, 266 us
+        replayed over 3 streams)."""
+        if self._ar is None:
+            raise RuntimeError("FusedGroup: call bind(shards, grads) before graph()")
+        if n_streams < 1:
+            raise ValueError(f"n_streams {n_streams} < 1")
+        streams = [torch.cuda.Stream(device=self.fused[0].device) for _ in range(n_streams)] if self.fused else []
+
+        def run():
+            cur = torch.cuda.current_stream()
+            for st in streams:
+                st.wait_stream(cur)
+            for k, fb in enumerate(self.buckets):
+                for name in fb.steps(fused_rs):
+                    if name != "fused_ar":
+                        fb.run(name, streams[k % n_streams])
+            for st in streams:
+                cur.wait_stream(st)
+            if self.do_ar:
+                self._ar(None)
+
+        run()
+        torch.cuda.current_stream().synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        g.streams = streams  # the capture's side streams live as long as the graph
+        return g

@@ -917,7 +917,8 @@ def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
     """The HSDP block with one bucket per parameter: six RS outputs as
     512-byte-aligned segments of one fused buffer per rank, one fused AR;
     the fused buffers (gaps included) and the gathered parameters against
-    the oracle's fused path."""
+    the oracle's fused path, issued eagerly and replayed from the step
+    captured over three streams."""
     w = W.scaled(W.HSDP_BLOCK, [(97, 64), (32, 64), (130, 32), (33, 128), (64,), (3,)])
     R, S = w.rank_size, w.shard_size
     buckets = [[sh] for sh in w.param_shapes]
@@ -928,11 +929,19 @@ def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
     shards = [fb.shard_views([dparams[k]]) for k, fb in enumerate(grp.buckets)]
     grads = [[g_cpu[g][k].cuda().reshape(-1) for g in range(R)] for k in range(len(buckets))]
     grp.bind(shards, grads)
-    for rep in range(2):
+    graph = None
+    for rep in range(5):
+        if rep == 2:  # then replays of the step captured over three streams
+            graph = grp.graph(n_streams=3, fused_rs=fused_rs)
         for fb in grp.buckets:
             for v in fb.rs_out:
                 v.fill_(float("nan"))
-        grp.step(fused_rs=fused_rs)
+            fb.full[0].view(torch.int16).fill_(0x7FA5)
+        torch.cuda.synchronize()
+        if graph is None:
+            grp.step(fused_rs=fused_rs)
+        else:
+            graph.replay()
         torch.cuda.synchronize()
         gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
         _, fused_o, offs_o, _ = O.reduce_grads_fused(gnp, buckets, R, S, O.AVG)
@@ -941,7 +950,8 @@ def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
             m = first_mismatch(bits(grp.fused[g]), np_bits(fused_o[g]))
             assert m == "", f"rep {rep} fused rank {g}: {m}"
         for k, fb in enumerate(grp.buckets):
-            assert np.array_equal(bits(fb.full[0]), bits(params[k].reshape(-1)))
+            assert np.array_equal(bits(fb.full[0]), bits(params[k].reshape(-1))), f"rep {rep} param {k}"
+    del graph
 
 
 def test_fused_group_with_shard_dims():
