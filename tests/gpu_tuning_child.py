@@ -33,6 +33,9 @@ CASES = [
     ("non-zero dims misaligned", T.test_nonzero_shard_dims_all_steps, (4, 8, torch.float32)),
     ("short odd-pitch rows (fold items)", T.test_odd_pitch_blocks_all_steps, (4, 8, torch.bfloat16, False)),
     ("short odd-pitch rows, aligned", T.test_odd_pitch_blocks_all_steps, (2, 4, torch.bfloat16, True)),
+    ("narrow fold pieces, 4-byte units", T.test_narrow_fold_paths_all_steps, (4, 8, torch.float32, True)),
+    ("narrow fold pieces, runtime group size", T.test_narrow_fold_paths_all_steps, (3, 6, torch.bfloat16, True)),
+    ("narrow fold pieces, operands at other offsets", T.test_narrow_fold_paths_all_steps, (8, 16, torch.bfloat16, False)),
     ("rs copy-reduce ragged", T.test_rs_copy_reduce_ragged_heavy_scaled, ()),
     ("hsdp end to end 16 = 2 x 8", T.test_hsdp_end_to_end_multi_bucket, (16, 8, O.AVG)),
     ("16-bit rs copy-in and reduce", T.test_16bit_rs_copy_in_and_reduce, (8, 4, torch.float16)),
