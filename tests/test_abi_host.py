@@ -264,6 +264,11 @@ def test_flat_bucket_and_group_need_bind():
         grp.bind([[]], [[], []])
     with pytest.raises(RuntimeError, match="bind"):
         grp.step()
+    with pytest.raises(RuntimeError, match="bind"):
+        grp.graph()
+    grp._ar = object()
+    with pytest.raises(ValueError, match="n_streams"):
+        grp.graph(n_streams=0)
 
 
 def test_time_next_launch_arguments(L):
