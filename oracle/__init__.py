@@ -31,4 +31,3 @@ from .fsdp_oracle import (  # noqa: F401
     shard_params,
     sharded_grad,
 )
-from . import pointwise  # noqa: F401

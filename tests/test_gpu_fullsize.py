@@ -1,11 +1,20 @@
-"""Full-size parity on the two big workloads, in the launch configuration the
-benchmark times (FlatBucket, inputs resident in HBM).
+"""Full-size parity on the two largest workloads, every element, in the
+launch configuration the benchmark times (FlatBucket with prepared calls,
+inputs resident in HBM).
 
-The oracle cannot materialise these buffers quickly, so it is evaluated
-element by element (oracle/pointwise.py) at a few hundred thousand random
-positions plus every position next to a region, padding or slice edge, and
-compared bit for bit.  Properties that hold at any size are checked on the
-whole buffers: all_gather(shard(x)) == x and every padding element is 0.
+The oracle runs at full size on the host, streamed rank by rank: the AG
+buffer and the full parameters from the host copy of the parameters, each
+rank's RS input from that rank's gradients (copied back from the device,
+where the workload draws them), the RS outputs from the oracle's own RS
+inputs.  Every element of ag, full[i], rs_in[g], rs_out[g] (AVG and SUM)
+and of the fused RS copy-reduce output (AVG and SUM) is compared bit for
+bit.  Every output buffer is filled with a NaN pattern before the kernels
+run, so an element (padding included) that a kernel skipped cannot match.
+
+Host memory: the 4-layer Llama-7B-shaped bucket keeps its eight oracle RS
+inputs (8 x 3.24 GB) while its RS is checked; everything else is per rank.
+Properties that hold at any size (the 16-bit and dim-1 variants) and items
+beyond 4 GiB are checked at the end.
 """
 
 import numpy as np
@@ -14,120 +23,145 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import bits, note, require_gpu
-from oracle import pointwise as PW
+from gpu_util import bits, first_mismatch, note, np_bits, require_gpu, to_oracle
 
 hp = pytest.importorskip("hsdp_parameter_gradient_amd")
 
 pytestmark = pytest.mark.gpu
 
-N_RANDOM = 300_000
+BIG = ["llama7b_4layer_r8_s8", "ragged_heavy_r8_s8"]
+NAN_PATTERN = {torch.float32: (torch.int32, 0x7FA5A5A5), torch.bfloat16: (torch.int16, 0x7FA5),
+               torch.float16: (torch.int16, 0x7FA5)}
 
 
-@pytest.fixture(scope="module", autouse=True)
-def _gpu():
+def _poison(t: torch.Tensor) -> None:
+    it, pat = NAN_PATTERN[t.dtype]
+    t.view(it).fill_(pat)
+
+
+def _same(t: torch.Tensor, want: np.ndarray, what: str) -> None:
+    got = bits(t)
+    exp = np_bits(want)
+    assert got.shape == exp.shape and np.array_equal(got, exp), f"{what}: {first_mismatch(got, exp)}"
+
+
+class FullSize:
+    """One workload at full size on the GPU, its steps run once in the
+    benchmark's configuration, and the host side of the oracle, computed on
+    demand and kept for the checks that need it."""
+
+    def __init__(self, wname: str):
+        w = W.WORKLOADS[wname]
+        self.w = w
+        self.R, self.S, self.D = w.rank_size, w.shard_size, w.dp_size
+        self.P = len(w.param_shapes)
+        self.lay = O.bucket_layout(w.param_shapes, self.S)
+        self.I = self.lay.I
+        note(f"[fullsize] {w.name}: P={self.P} I={self.I} R={self.R} S={self.S}: drawing inputs, running the steps")
+        self.params = W.params(w, device="cuda")
+        self.grads = W.grads(w, device="cuda")
+        self.flat_grads = [self.grads[g][i].reshape(-1) for g in range(self.R) for i in range(self.P)]
+        fb = hp.FlatBucket(w.param_shapes, self.R, self.S, w.param_dtype, op=O.AVG)
+        for t in [fb.ag, *fb.full, *fb.rs_in, *fb.fused]:
+            _poison(t)
+        fb.bind(fb.shard_views(self.params), self.flat_grads)
+        for step in ("ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"):
+            fb.run(step)
+        torch.cuda.synchronize()
+        self.fb = fb
+        self.host_params = [to_oracle(p) for p in self.params]
+        self._ag = None
+        self._rs_in = {}
+        self._rs_out = {}
+
+    def oracle_ag(self) -> np.ndarray:
+        if self._ag is None:
+            dt = np.float32 if self.w.param_dtype == torch.float32 else np.uint16
+            self._ag = O.ag_copy_in(O.shard_params(self.host_params, self.lay), self.lay, dt)
+        return self._ag
+
+    def oracle_rs_in(self, g: int) -> np.ndarray:
+        if g not in self._rs_in:
+            host = [t.cpu().numpy() for t in self.grads[g]]
+            self._rs_in[g] = O.rs_copy_in(host, self.lay)
+        return self._rs_in[g]
+
+    def oracle_rs_out(self, op: str):
+        if op not in self._rs_out:
+            rs_in = [self.oracle_rs_in(g) for g in range(self.R)]
+            self._rs_out[op] = O.rs_reduce(rs_in, self.I, self.R, self.S, op)
+        return self._rs_out[op]
+
+    def release(self) -> None:
+        self.fb = self.params = self.grads = self.flat_grads = None
+        self._ag = None
+        self._rs_in.clear()
+        self._rs_out.clear()
+
+
+@pytest.fixture(scope="module", params=BIG)
+def big(request):
     require_gpu()
     hp.lib()
-    yield
+    st = FullSize(request.param)
+    yield st
+    st.release()
     hp.fsdp_release_cache()
     torch.cuda.empty_cache()
 
 
-def _np16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+def test_ag_copy_in_every_element(big):
+    note(f"[fullsize] {big.w.name}: ag_copy_in, {big.S * big.I} elements")
+    _same(big.fb.ag, big.oracle_ag(), "ag_copy_in")
 
 
-def _fetcher(tensors):
-    """fetch(i, flat) -> host values (float32 or uint16 bits) of tensors[i]."""
-    def fetch(i, flat):
-        idx = torch.from_numpy(np.asarray(flat, dtype=np.int64)).cuda()
-        v = tensors[i].reshape(-1)[idx]
-        return v.cpu().numpy() if v.dtype == torch.float32 else _np16(v)
-    return fetch
+def test_ag_copy_out_every_element(big):
+    note(f"[fullsize] {big.w.name}: ag_copy_out, {big.P} parameters")
+    want = O.ag_copy_out(O.all_gather(big.oracle_ag()), big.lay)
+    for i in range(big.P):
+        _same(big.fb.full[i], want[i], f"ag_copy_out param {i}")
+        # the round trip restores the parameter itself
+        _same(big.fb.full[i], big.host_params[i], f"ag_copy_out param {i} vs the parameter")
 
 
-def _gpu_vals(t, pos):
-    idx = torch.from_numpy(np.asarray(pos, dtype=np.int64)).cuda()
-    return bits(t.reshape(-1)[idx])
+@pytest.mark.parametrize("g", range(8))
+def test_rs_copy_in_every_element(big, g):
+    note(f"[fullsize] {big.w.name}: rs_copy_in rank {g}, {big.S * big.I} elements")
+    _same(big.fb.rs_in[g], big.oracle_rs_in(g), f"rs_copy_in rank {g}")
 
 
-@pytest.mark.parametrize("wname", ["llama7b_4layer_r8_s8", "ragged_heavy_r8_s8"])
-def test_full_size_sampled(wname):
-    w = W.WORKLOADS[wname]
-    R, S, D = w.rank_size, w.shard_size, w.dp_size
-    P = len(w.param_shapes)
-    lay = O.bucket_layout(w.param_shapes, S)
-    I = lay.I
-    rng = np.random.default_rng(w.number)
-    note(f"[fullsize] {w.name}: P={P} I={I} R={R} S={S}")
+def test_rs_reduce_avg_every_element(big):
+    note(f"[fullsize] {big.w.name}: rs_reduce AVG, {big.R} x {big.I} elements")
+    want = big.oracle_rs_out(O.AVG)
+    for g in range(big.R):
+        _same(big.fb.rs_out[g], want[g], f"rs_reduce AVG rank {g}")
 
-    params = W.params(w, device="cuda")
-    grads = W.grads(w, device="cuda")
-    fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=O.AVG)
-    fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
-    for step in ("ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"):
-        fb.run(step)
+
+def test_rs_reduce_sum_every_element(big):
+    note(f"[fullsize] {big.w.name}: rs_reduce SUM, {big.R} x {big.I} elements")
+    out = [torch.empty(big.I, dtype=torch.float32, device="cuda") for _ in range(big.R)]
+    for t in out:
+        _poison(t)
+    hp.fsdp_rs_reduce(big.w.param_shapes, big.R, big.S, big.D, O.SUM, big.fb.rs_in, out)
     torch.cuda.synchronize()
-    np_dtype = np.float32 if w.param_dtype == torch.float32 else np.uint16
-    to_bits = (lambda a: a.view(np.int32)) if np_dtype == np.float32 else (lambda a: a.view(np.int16))
+    want = big.oracle_rs_out(O.SUM)
+    for g in range(big.R):
+        _same(out[g], want[g], f"rs_reduce SUM rank {g}")
 
-    # --- AG copy-in: sampled values, and all padding is zero -------------
-    edges = PW.boundary_positions(lay)
-    pos = np.unique(np.concatenate([rng.integers(0, S * I, N_RANDOM),
-                                    (np.arange(S)[:, None] * I + edges[None, :]).reshape(-1)]))
-    want = PW.packed_values(lay, pos, _fetcher(params), np_dtype)
-    got = _gpu_vals(fb.ag, pos)
-    assert np.array_equal(got, to_bits(want)), "ag_copy_in sampled mismatch"
-    pad_nonzero = 0
-    for s in range(S):
-        for i in range(P):
-            a = s * I + lay.in_off[i] + lay.row_len[i][s] * lay.inner[i]
-            b = s * I + lay.in_off[i] + lay.padded[i]
-            if b > a:
-                pad_nonzero += int(torch.count_nonzero(fb.ag[a:b].view(torch.int16 if np_dtype == np.uint16 else torch.int32)))
-    assert pad_nonzero == 0
 
-    # --- AG copy-out: the round trip is exact on every element -----------
-    for i in range(P):
-        it = torch.int16 if np_dtype == np.uint16 else torch.int32
-        assert torch.equal(fb.full[i].reshape(-1).view(it), params[i].reshape(-1).view(it)), \
-            f"ag_copy_out param {i} differs from the parameter"
-        n = fb.full[i].numel()
-        if n:
-            flat = np.unique(np.concatenate([rng.integers(0, n, 2000), [0, n - 1]]))
-            src = PW.unpacked_sources(lay, i, flat)
-            assert np.array_equal(_gpu_vals(fb.full[i], flat), _gpu_vals(fb.ag, src))
-
-    # --- RS copy-in: sampled per rank -------------------------------------
-    for g in range(R):
-        pos = np.unique(np.concatenate([rng.integers(0, S * I, N_RANDOM // R),
-                                        (np.arange(S)[:, None] * I + edges[None, :]).reshape(-1)]))
-        want = PW.packed_values(lay, pos, _fetcher(grads[g]), np.float32)
-        assert np.array_equal(_gpu_vals(fb.rs_in[g], pos), want.view(np.int32)), f"rs_copy_in rank {g}"
-
-    # --- RS reduce (AVG, then SUM): sampled, from the gradients directly ---
-    fetch_rs_in = lambda m, p: PW.packed_values(lay, p, _fetcher(grads[m]), np.float32)  # noqa: E731
-    for op in (O.AVG, O.SUM):
-        if op == O.SUM:
-            hp.fsdp_rs_reduce(w.param_shapes, R, S, D, op, fb.rs_in, fb.rs_out)
-            torch.cuda.synchronize()
-        for g in range(R):
-            k = np.unique(np.concatenate([rng.integers(0, I, N_RANDOM // R), edges]))
-            want = PW.rs_reduce_values(I, R, S, op, g, k, fetch_rs_in)
-            assert np.array_equal(_gpu_vals(fb.rs_out[g], k), want.view(np.int32)), f"rs_reduce {op} rank {g}"
-    # --- RS copy-in fused into the RS: the whole result equals the two-step
-    # one (SUM, just computed) bit for bit, and samples match the oracle ---
-    fused_out = [torch.empty(I, dtype=torch.float32, device="cuda") for _ in range(R)]
-    hp.fsdp_rs_copy_reduce(w.param_shapes, R, S, D, O.SUM, [grads[g][i].reshape(-1) for g in range(R) for i in range(P)],
-                           fused_out)
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_rs_copy_reduce_every_element(big, op):
+    """RS copy-in fused into the RS: by the oracle's definition the RS of the
+    RS inputs, so every element equals the oracle's RS output."""
+    note(f"[fullsize] {big.w.name}: rs_copy_reduce {op}, {big.R} x {big.I} elements")
+    out = [torch.empty(big.I, dtype=torch.float32, device="cuda") for _ in range(big.R)]
+    for t in out:
+        _poison(t)
+    hp.fsdp_rs_copy_reduce(big.w.param_shapes, big.R, big.S, big.D, op, big.flat_grads, out)
     torch.cuda.synchronize()
-    for g in range(R):
-        assert torch.equal(fused_out[g].view(torch.int32), fb.rs_out[g].view(torch.int32)), f"rs_copy_reduce rank {g}"
-        k = np.unique(np.concatenate([rng.integers(0, I, N_RANDOM // R), edges]))
-        want = PW.rs_reduce_values(I, R, S, O.SUM, g, k, fetch_rs_in)
-        assert np.array_equal(_gpu_vals(fused_out[g], k), want.view(np.int32)), f"rs_copy_reduce sampled rank {g}"
-    del fb, params, grads, fused_out
-    torch.cuda.empty_cache()
+    want = big.oracle_rs_out(op)
+    for g in range(big.R):
+        _same(out[g], want[g], f"rs_copy_reduce {op} rank {g}")
 
 
 @pytest.mark.parametrize("wname,grad_dtype,on_dim_1", [
@@ -144,6 +178,8 @@ def test_full_size_properties(wname, grad_dtype, on_dim_1):
     quotient exact in the gradient dtype, whatever the order) the RS output
     is the chunk of the group's sum divided by S, and the fused AR output
     that divided by D."""
+    require_gpu()
+    hp.lib()
     w = W.WORKLOADS[wname]
     R, S, D = w.rank_size, w.shard_size, w.dp_size
     P = len(w.param_shapes)
@@ -200,6 +236,7 @@ def test_full_size_properties(wname, grad_dtype, on_dim_1):
     for g in range(R):
         assert torch.equal(fb.fused[g].view(gi), before[g].view(gi)), f"fused RS rank {g}"
     del fb, params, grads, before
+    hp.fsdp_release_cache()
     torch.cuda.empty_cache()
 
 
@@ -209,6 +246,8 @@ def test_items_beyond_4gib():
     elements with shard_size 1 (one 4 GiB + 2 KiB segment), and the fused
     AR of two replicas of 2^30 + 1000 fp32 elements (integer-valued, so the
     sum is exact)."""
+    require_gpu()
+    hp.lib()
     note("[fullsize] items beyond 4 GiB")
     n = (1 << 31) + 1001
     x = torch.empty(n, dtype=torch.int16, device="cuda").random_().view(torch.bfloat16)
@@ -230,4 +269,5 @@ def test_items_beyond_4gib():
     for f in fused:
         assert torch.equal(f, want)
     del fused, want
+    hp.fsdp_release_cache()
     torch.cuda.empty_cache()

@@ -17,7 +17,6 @@ import torch
 
 import oracle as O
 from oracle import fsdp_oracle as F
-from oracle import pointwise as PW
 
 RNG = np.random.default_rng(1234)
 
@@ -249,22 +248,6 @@ def test_single_parameter_gather_prefix_is_the_parameter():
                 ag = O.ag_copy_in(O.shard_params([x], lay), lay, np.float32)
                 assert np.array_equal(ag[:x.size], x.reshape(-1))
                 assert not np.any(ag[x.size:])  # the rest is padding
-
-
-def test_pointwise_forms_match_full_forms():
-    shapes = [(7, 8), (5, 3), (16,), (0, 3), (3,)]
-    for S in (1, 3, 4, 8):
-        xs = [(RNG.standard_normal(sh) + 5).astype(np.float32) for sh in shapes]
-        lay = O.bucket_layout(shapes, S)
-        ag = O.ag_copy_in(O.shard_params(xs, lay), lay, np.float32)
-        pos = np.arange(ag.size)
-        got = PW.packed_values(lay, pos, lambda i, f: xs[i].reshape(-1)[f], np.float32)
-        assert np.array_equal(got, ag)
-        outs = O.ag_copy_out(ag, lay)
-        for i, x in enumerate(xs):
-            src = PW.unpacked_sources(lay, i, np.arange(x.size))
-            assert np.array_equal(ag[src], outs[i].reshape(-1))
-        assert set(PW.boundary_positions(lay).tolist()) <= set(range(lay.I))
 
 
 @pytest.mark.parametrize("R,S", [(4, 4), (8, 4), (8, 8), (8, 2), (6, 3)])
@@ -632,6 +615,35 @@ def _rs_copy_in_pad_one(grads, lay, dtype=np.float32):
     return buf
 
 
+def _replicate_major_shard_groups(R, S):
+    # the shard group of replicate d read as ranks d, D + d, 2D + d, ...
+    _, D = F.group_sizes(R, S)
+    return [[s * D + d for s in range(S)] for d in range(D)]
+
+
+def _rs_avg_over_dp_size(rs_in, I, R, S, op):
+    outs = _ORIG_RS_REDUCE(rs_in, I, R, S, F.SUM)
+    return [o / np.float32(R // S) for o in outs] if op == F.AVG else outs
+
+
+def _rs_slice_at_replicate_index(rs_in, I, R, S, op):
+    # every rank of shard group d keeps slice d instead of its own slice s
+    out = [None] * R
+    for d, group in enumerate(F.shard_groups(R, S)):
+        for g in group:
+            operands = [rs_in[m][d * I:(d + 1) * I] for m in group]
+            out[g] = F._store(F._scale(F._ordered_sum(operands), op, S), rs_in[group[0]])
+    return out
+
+
+_ORIG_FUSED_AR = F.fused_ar
+
+
+def _ar_avg_over_shard_size(fused, R, S, op):
+    outs = _ORIG_FUSED_AR(fused, R, S, F.SUM)
+    return [o / np.float32(S) for o in outs] if op == F.AVG else outs
+
+
 MUTANTS = {
     "bf16_truncation": ("f32_to_bf16", _truncating_bf16),
     "floor_chunk": ("dim0_chunk", _floor_chunk),
@@ -648,6 +660,10 @@ MUTANTS = {
     "rs_padding_not_zero": ("rs_copy_in", _rs_copy_in_pad_one),
     "f16_round_each_add": ("_ordered_sum", _f16_round_each_add),
     "f16_truncating_store": ("_store", _f16_truncating_store),
+    "rs_groups_replicate_major": ("shard_groups", _replicate_major_shard_groups),
+    "rs_avg_over_dp_size": ("rs_reduce", _rs_avg_over_dp_size),
+    "rs_slice_at_replicate_index": ("rs_reduce", _rs_slice_at_replicate_index),
+    "ar_avg_over_shard_size": ("fused_ar", _ar_avg_over_shard_size),
 }
 
 
