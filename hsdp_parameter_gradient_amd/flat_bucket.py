@@ -10,7 +10,10 @@ of one bucket of parameters with all R simulated ranks resident in HBM:
   fused[g]  [F]     rank g's 512-byte-aligned fused AR buffer; the RS output
                     of rank g is the view fused[g][off : off + I]
                     (zero-copy, PR #758 write-up of the Hyper
-                    communication-overlap scheme, section 2.1)
+                    communication-overlap scheme, section 2.1); the
+                    bucket's own fused_ar step reduces that segment and
+                    its trailing gap (FusedGroup reduces the whole buffer
+                    once for all its buckets)
 
 and runs the hot path with one library call per step.  Which gradient
 collectives run follows the decision matrix of the FullyShard
@@ -73,6 +76,12 @@ class FlatBucket:
             if len(self.fused) != self.R or any(f.numel() != self.F or f.dtype != grad_dtype for f in self.fused):
                 raise ValueError(f"fused: expected {self.R} buffers of {self.F} {grad_dtype} elements")
         self.rs_out = [f[self.fused_off:self.fused_off + I] for f in self.fused]
+        # this bucket's own fused AR covers its segment and the zero gap up to
+        # the next 512-byte boundary only: with buffers shared by several
+        # buckets it never reduces another bucket's segment a second time, nor
+        # touches memory that another bucket's RS writes meanwhile
+        _, self.ar_numel = B.fsdp_fused_layout([I], grad_dtype.itemsize)
+        self.ar_buffers = [f[self.fused_off:self.fused_off + self.ar_numel] for f in self.fused]
         self._calls = None
 
     # -- the caller's inputs ------------------------------------------------
@@ -116,7 +125,7 @@ class FlatBucket:
                                    dims),
             "rs_copy_reduce": B.prepare("fsdp_rs_copy_reduce", self.shapes, R, S, self.D, self.op, list(grads),
                                         self.rs_out, dims),
-            "fused_ar": B.prepare("fsdp_fused_ar", self.seg_numel, R, S, self.D, self.op, self.fused),
+            "fused_ar": B.prepare("fsdp_fused_ar", [self.layout.I], R, S, self.D, self.op, self.ar_buffers),
         }
         return self
 

@@ -271,6 +271,33 @@ def test_flat_bucket_and_group_need_bind():
         grp.graph(n_streams=0)
 
 
+def test_shared_fused_buffers_each_bucket_ar_covers_its_own_segment():
+    """Buckets sharing a fused buffer (FusedGroup): each bucket's own fused_ar
+    step covers its segment and the zero gap after it, on a 512-byte
+    boundary, and nothing else; the segments' AR ranges are disjoint and
+    together cover the whole buffer (host tensors: no device call)."""
+    torch = pytest.importorskip("torch")
+    buckets = [[(7, 8), (5, 3)], [(16,)], [(1000, 3)], [(3,)]]
+    for R, S, dt in ((8, 4, torch.float32), (4, 2, torch.bfloat16)):
+        grp = hp.FusedGroup(buckets, R, S, torch.float32, grad_dtype=dt, device="cpu")
+        es = dt.itemsize
+        F = grp.fused[0].numel()
+        spans = []
+        for fb in grp.buckets:
+            I = fb.layout.I
+            for g in range(R):
+                v = fb.ar_buffers[g]
+                off = (v.data_ptr() - grp.fused[g].data_ptr()) // es
+                assert v.untyped_storage().data_ptr() == grp.fused[g].untyped_storage().data_ptr()
+                assert (off * es) % 512 == 0 and off == fb.fused_off
+                assert (v.numel() * es) % 512 == 0 and I <= v.numel() < I + 512 // es
+                assert fb.rs_out[g].data_ptr() == v.data_ptr() and fb.rs_out[g].numel() == I
+            spans.append((fb.fused_off, fb.fused_off + fb.ar_numel))
+        spans.sort()
+        assert spans[0][0] == 0 and spans[-1][1] == F
+        assert all(a[1] == b[0] for a, b in zip(spans, spans[1:])), spans
+
+
 def test_time_next_launch_arguments(L):
     """Both events or neither: one NULL handle is FSDP_EINVAL (no HIP call)."""
     assert L.fsdp_time_next_launch(None, None) == 0

@@ -954,6 +954,50 @@ def test_fused_group_one_ar_over_per_parameter_buckets(fused_rs):
     del graph
 
 
+def test_backward_pipeline_over_shared_fused_buffers():
+    """BackwardPipeline over the buckets of one FusedGroup (their RS outputs
+    are segments of shared fused buffers): each bucket's own fused AR covers
+    only its segment and gap, so the per-layer ARs never re-reduce another
+    bucket's segment (SUM would multiply it by D per extra AR) nor race with
+    the next bucket's RS into the same buffers.  Eager and replayed, both
+    orders, against the oracle's fused path over the same buckets."""
+    w = W.scaled(W.HSDP_BLOCK, [(97, 64), (32, 64), (130, 32), (33, 128), (64,), (3,)])
+    R, S = w.rank_size, w.shard_size
+    buckets = [[sh] for sh in w.param_shapes]
+    note(f"[parity] backward pipeline over a FusedGroup of {len(buckets)} buckets (SUM)")
+    g_cpu = W.grads(w)
+    grp = hp.FusedGroup(buckets, R, S, w.param_dtype, op=O.SUM)
+    zeros = [torch.zeros(sh, dtype=w.param_dtype, device="cuda") for sh in w.param_shapes]
+    grp.bind([fb.shard_views([zeros[k]]) for k, fb in enumerate(grp.buckets)],
+             [[g_cpu[g][k].cuda().reshape(-1) for g in range(R)] for k in range(len(buckets))])
+    gnp = [[t.numpy() for t in g_cpu[g]] for g in range(R)]
+    _, fused_o, offs_o, _ = O.reduce_grads_fused(gnp, buckets, R, S, O.SUM)
+    assert [fb.fused_off for fb in grp.buckets] == offs_o
+    pipe = hp.BackwardPipeline(grp.buckets, fused_rs=True)
+    graphs = {}
+    for rep in range(6):
+        for fb in grp.buckets:
+            for v in fb.rs_out:
+                v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        if rep < 2:
+            (pipe.run_pipelined if rep == 0 else pipe.run_serial)()
+        else:
+            pipelined = rep % 2 == 0
+            if pipelined not in graphs:
+                graphs[pipelined] = pipe.graph(pipelined=pipelined)
+                for fb in grp.buckets:
+                    for v in fb.rs_out:
+                        v.fill_(float("nan"))
+                torch.cuda.synchronize()
+            graphs[pipelined].replay()
+        torch.cuda.synchronize()
+        for g in range(R):
+            m = first_mismatch(bits(grp.fused[g]), np_bits(fused_o[g]))
+            assert m == "", f"rep {rep} fused rank {g}: {m}"
+    graphs.clear()
+
+
 def test_fused_group_with_shard_dims():
     """A FusedGroup whose buckets shard some parameters on dim 1: every
     bucket's RS output lands in its segment of the shared fused buffers and
