@@ -6,9 +6,10 @@ resident in HBM: AG copy-in (pack the shards of all S ranks into the padded
 AG buffer), AG copy-out (unpack into the full parameters), RS copy-in (chunk
 the R ranks' full gradients into their padded RS inputs), RS over every
 shard group into views of the 512-byte-aligned fused buffers, and the fused
-AR over every replicate group.  The default workload is the HSDP
-transformer block (hidden 1024; rank_size 8 = 2 replicas x 4 shards; bf16
-parameters, fp32 gradients, AVG).
+AR over every replicate group when dp_size > 1.  The headline workload is
+the 4-layer Llama-7B-shaped bucket (hidden 4096, ffn 11008; rank_size 8 =
+shard_size 8; bf16 parameters, fp32 gradients, AVG): 84 GB per step, far
+beyond the 256 MB Infinity Cache, so HBM sets the rate.
 
 value = algorithmic bytes of one step x steps / time (GB/s, whole job).
 Algorithmic bytes count every required read and write once (padding is
@@ -24,8 +25,11 @@ separate pass afterwards gives every step's time (the "ops" breakdown), and
 medians of single launches with the Infinity Cache flushed first (cold) or
 not (warm).  A 4 GiB device-to-device copy (hipMemcpyAsync, and the
 library's copy kernel) gives the plain-copy ceiling.
-The CPU oracle is timed on a bounded number of whole steps of the same
-workload (cpu_baseline).
+The CPU oracle is timed on whole steps of a bounded sample of the same
+workload (cpu_baseline: its first layer).  The other workloads (the HSDP
+block, which alone runs all five steps and carries the variants; the
+ragged-heavy set; the pure-TP AR; the tiny bucket) follow under
+"other_workloads", each with its own pass, dominant kernel and breakdown.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -49,10 +53,11 @@ KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kern
                   "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
                   "rs_copy_reduce": "reduce_kernel", "fused_ar": "reduce_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
-# what fixes the kernels' memory traffic: their code, the descriptor formats
-# and the launch tuning (chunk sizes, store policy)
+# what fixes the kernels' memory traffic: their code, the descriptor formats,
+# the launch tuning (chunk sizes, store policy) and the planner that builds
+# the tables
 KERNEL_SRC = [os.path.join(ROOT, "hsdp_parameter_gradient_amd", "csrc", f)
-              for f in ("kernels.hip", "plan.hpp", "tuning.hpp")]
+              for f in ("kernels.hip", "plan.hpp", "tuning.hpp", "fsdp_flat.cpp")]
 
 
 def log(msg: str) -> None:
@@ -530,32 +535,50 @@ def fold_shapes(reps: int) -> None:
     print(json.dumps({"fold_shapes": out, "timing": f"events around {reps} back-to-back prepared calls"}), flush=True)
 
 
-def cpu_baseline(w, seconds: float, op: str):
-    """The oracle, as it stands, timed on whole steps of the workload (and
-    on each of the step's operations, with perf_counter around each oracle
-    call).  Returns (steps run, seconds, F, seconds per operation)."""
+def sample_shapes(w):
+    """The CPU baseline's sample of a workload: the whole bucket when it has
+    at most 64 M elements, else its leading parameters up to a quarter of
+    its elements (for the 4-layer Llama-7B-shaped bucket: exactly its first
+    layer, 9 parameters)."""
+    n_all = sum(_numel(s) for s in w.param_shapes)
+    if n_all <= 64 << 20:
+        return len(w.param_shapes)
+    k, n = 0, 0
+    while k < len(w.param_shapes) and (k == 0 or n + _numel(w.param_shapes[k]) <= n_all // 4):
+        n += _numel(w.param_shapes[k])
+        k += 1
+    return k
+
+
+def cpu_baseline(w, seconds: float, op: str, params, grads):
+    """The oracle, as it stands, timed on whole steps of a bounded sample of
+    the workload (sample_shapes: its leading parameters, the same ranks, the
+    same values, copied from the device tensors the GPU pass used), and on
+    each of the step's operations (perf_counter around each oracle call).
+    Returns (parameters in the sample, steps run, seconds, bytes per sample
+    step, seconds per operation)."""
+    import dataclasses
+
     import numpy as np
     import torch
 
     import oracle as O
-    import workloads as W
 
     R, S = w.rank_size, w.shard_size
-    lay = O.bucket_layout(w.param_shapes, S)
-    params = W.params(w, "cpu")
-    grads = W.grads(w, "cpu")
+    k = sample_shapes(w)
+    ws = dataclasses.replace(w, param_shapes=tuple(w.param_shapes[:k]))
+    lay = O.bucket_layout(ws.param_shapes, S)
     if w.param_dtype == torch.float32:
-        xs = [p.numpy() for p in params]
+        xs = [p.cpu().numpy() for p in params[:k]]
         np_dt = np.float32
     else:
-        xs = [p.view(torch.int16).numpy().view(np.uint16) for p in params]
+        xs = [p.view(torch.int16).cpu().numpy().view(np.uint16) for p in params[:k]]
         np_dt = np.uint16
-    gnp = [[t.numpy() for t in grads[g]] for g in range(R)]
-    offs, F = O.fused_layout([lay.I])
+    gnp = [[t.cpu().numpy() for t in grads[g][:k]] for g in range(R)]
     do_ar = bool([c for c in O.grad_sync_plan(R, S) if c[0] == "AR"])
 
     if S == 1:  # pure-TP compatible path: the fused AR is the whole step
-        sizes = [_numel(s) for s in w.param_shapes]
+        sizes = [_numel(s) for s in ws.param_shapes]
         offs, F = O.fused_layout(sizes)
         fused0 = []
         for g in range(R):
@@ -563,7 +586,11 @@ def cpu_baseline(w, seconds: float, op: str):
             for o, t in zip(offs, gnp[g]):
                 buf[o:o + t.size] = t.reshape(-1)
             fused0.append(buf)
-
+    else:
+        offs, F = O.fused_layout([lay.I])
+    nb = step_bytes(ws, lay, F)
+    steps = ["fused_ar"] if S == 1 else (["ag_copy_in", "ag_copy_out", "rs_copy_in", "rs_reduce"] +
+                                        (["fused_ar"] if do_ar else []))
     per = {}
 
     def timed(name, fn, *a):
@@ -572,26 +599,24 @@ def cpu_baseline(w, seconds: float, op: str):
         per[name] = per.get(name, 0.0) + time.perf_counter() - t
         return r
 
-    if S == 1:
-        def one_step():
-            timed("fused_ar", O.fused_ar, fused0, R, S, op)
-    else:
-        one_step = None
+    def pure_tp_step():
+        timed("fused_ar", O.fused_ar, fused0, R, S, op)
 
     def hsdp_step():
         ag = timed("ag_copy_in", lambda: O.ag_copy_in(O.shard_params(xs, lay), lay, np_dt))
         timed("ag_copy_out", lambda: O.ag_copy_out(O.all_gather(ag), lay))
         rs_in = timed("rs_copy_in", lambda: [O.rs_copy_in(gnp[g], lay) for g in range(R)])
         out = timed("rs_reduce", O.rs_reduce, rs_in, lay.I, R, S, op)
-        fused = []
-        for g in range(R):
-            buf = np.zeros(F, np.float32)
-            buf[offs[0]:offs[0] + lay.I] = out[g]
-            fused.append(buf)
+        del rs_in
         if do_ar:
+            fused = []
+            for g in range(R):
+                buf = np.zeros(F, np.float32)
+                buf[offs[0]:offs[0] + lay.I] = out[g]
+                fused.append(buf)
             timed("fused_ar", O.fused_ar, fused, R, S, op)
 
-    one_step = one_step or hsdp_step
+    one_step = pure_tp_step if S == 1 else hsdp_step
     n, t0 = 0, time.perf_counter()
     while True:
         one_step()
@@ -599,7 +624,177 @@ def cpu_baseline(w, seconds: float, op: str):
         el = time.perf_counter() - t0
         if el >= seconds or n >= 200:
             break
-    return n, el, F, {k: v / n for k, v in per.items()}
+    return k, n, el, sum(nb[s] for s in steps), {s: (per[s] / n, nb[s]) for s in steps}
+
+
+def frac_vs(achieved: float, ceiling) -> dict:
+    """A rate against the published peak and, when measured, against the
+    same run's plain 4 GiB copy with the library's copy kernel."""
+    out = {"frac_of_peak": round(achieved / HBM_PEAK_GBS, 4)}
+    if ceiling:
+        c = ceiling["seg_copy_kernel"]["GB/s"]
+        out["frac_of_copy_ceiling"] = round(achieved / c, 4)
+    return out
+
+
+class Pass:
+    """One workload's whole pass on the GPU: the runner, its inputs (kept
+    for the CPU baseline's sample) and the byte model."""
+
+    def __init__(self, w, op):
+        import torch
+
+        import hsdp_parameter_gradient_amd as hp
+        import workloads as W
+        self.w, self.op = w, op
+        R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+        if S > 1:
+            fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
+            self.params = W.params(w, "cuda")
+            self.grads = W.grads(w, "cuda")
+            fb.bind(fb.shard_views(self.params), [self.grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+            self.runner = fb
+            self.lay, self.F = fb.layout, fb.F
+        else:
+            self.runner = PureTPRunner(w, op)
+            self.lay, self.F = self.runner.layout, self.runner.F
+            self.params = None
+            self.grads = None
+        self.steps = self.runner.steps()
+        self.nbytes = step_bytes(w, self.lay, self.F)
+        self.bytes_per_step = sum(self.nbytes[s] for s in self.steps)
+        torch.cuda.synchronize()
+
+    def measure(self, K: int, warmup: int, cold_warm_reps: int):
+        """W untimed steps, then K timed steps between synchronisations, the
+        dominant kernel's own dispatch recording its start and end in every
+        timed step; then the per-step breakdown and, if asked, the cold and
+        warm single-launch medians."""
+        import torch
+
+        import hsdp_parameter_gradient_amd as hp
+        runner, steps, nbytes = self.runner, self.steps, self.nbytes
+        for _ in range(warmup):
+            runner.step()
+        torch.cuda.synchronize()
+        # a few untimed steps with events around every step find the dominant
+        # kernel; the timed region then records events around that one only
+        probe = per_step_us(runner, steps, max(3, warmup))
+        dom = max(steps, key=probe.get)
+        ev = timing_events(K)  # the dominant kernel's dispatch records these
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for k in range(K):
+            for name in steps:
+                if name == dom:
+                    hp.fsdp_time_next_launch(ev[k][0], ev[k][1])
+                runner.run(name)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(end)
+        res = {"ms_per_step": total_ms / K, "wall_s": wall, "dominant": dom,
+               "value": self.bytes_per_step * K / (total_ms * 1e-3) / 1e9,
+               "dom_us": sum(a.elapsed_time(b) for a, b in ev) / K * 1e3}
+        # per-step breakdown, measured after the timed region (events around
+        # every step perturb the whole-step time, so they stay out of it)
+        after = per_step_us(runner, steps, K)
+        ops = {}
+        for name in steps:
+            us = after[name]
+            gbs = nbytes[name] / (us * 1e-6) / 1e9
+            ops[name] = {"kernel": KERNEL_OF_STEP[name], "bytes": nbytes[name], "us": round(us, 2),
+                         "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"  {name:12s} {nbytes[name] / 1e6:10.1f} MB  {us:9.1f} us  {gbs:8.1f} GB/s  "
+                f"{100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
+        res["ops"] = ops
+        cw = {}
+        if cold_warm_reps > 0:
+            flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+            med = op_medians(runner, steps, cold_warm_reps, flush)
+            del flush
+            for name in steps:
+                cw[name] = {m: {"us": round(med[name][m], 2),
+                                "GB/s": round(nbytes[name] / (med[name][m] * 1e-6) / 1e9, 1)}
+                            for m in ("cold", "warm")}
+                log(f"  {name:12s} median of {cold_warm_reps}: cold {med[name]['cold']:8.1f} us "
+                    f"({cw[name]['cold']['GB/s']:7.1f} GB/s), warm {med[name]['warm']:8.1f} us "
+                    f"({cw[name]['warm']['GB/s']:7.1f} GB/s)")
+        res["cold_warm"] = cw or None
+        log(f"  step: {res['ms_per_step'] * 1e3:.1f} us, {res['value']:.1f} GB/s; wall {wall:.3f} s for {K} steps")
+        return res
+
+    def roofline(self, res, ceiling):
+        dom = res["dominant"]
+        achieved = self.nbytes[dom] / (res["dom_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": KERNEL_OF_STEP[dom], "step": dom,
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(self.w.name, dom),
+                "algorithmic_bytes_per_launch": self.nbytes[dom], "avg_launch_us": round(res["dom_us"], 2),
+                "timing": "HIP events recorded by the call's own kernel dispatch at its start and end, "
+                          "every timed step"}
+        if ceiling:
+            roof["frac_of_copy_ceiling"] = round(achieved / ceiling["seg_copy_kernel"]["GB/s"], 4)
+        return roof
+
+    def fused_rs_variant(self, K: int, warmup: int):
+        """The same pass with RS copy-in fused into the RS (the RS input is
+        never materialised): reported beside the contract's step."""
+        import torch
+        runner = self.runner
+        fsteps = runner.steps(fused_rs=True)
+        for _ in range(warmup):
+            runner.step(fused_rs=True)
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        fs.record()
+        for _ in range(K):
+            runner.step(fused_rs=True)
+        fe.record()
+        torch.cuda.synchronize()
+        f_ms = fs.elapsed_time(fe) / K
+        f_us = per_step_us(runner, ["rs_copy_reduce"], K)["rs_copy_reduce"]
+        b = self.nbytes["rs_copy_reduce"]
+        pass_bytes = sum(self.nbytes[s] for s in fsteps)
+        log(f"  fused RS variant: step {f_ms * 1e3:.1f} us; rs_copy_reduce {f_us:.1f} us, "
+            f"{b / (f_us * 1e-6) / 1e9:.1f} GB/s")
+        return {"steps_per_pass": fsteps, "ms_per_step": round(f_ms, 4), "bytes_per_step": pass_bytes,
+                "GB/s": round(pass_bytes / (f_ms * 1e-3) / 1e9, 1),
+                "rs_copy_reduce": {"bytes": b, "us": round(f_us, 2), "GB/s": round(b / (f_us * 1e-6) / 1e9, 1)},
+                "note": "RS input never written; results identical to rs_copy_in + rs_reduce"}
+
+    def release(self):
+        import torch
+
+        import hsdp_parameter_gradient_amd as hp
+        self.runner = self.params = self.grads = None
+        hp.fsdp_release_cache()
+        torch.cuda.empty_cache()
+
+
+def config_of(p: Pass):
+    w = p.w
+    return {"workload": w.name, "rank_size": w.rank_size, "shard_size": w.shard_size, "dp_size": w.dp_size,
+            "param_dtype": str(w.param_dtype).replace("torch.", ""), "grad_dtype": "float32",
+            "reduce_op": p.op, "params": len(w.param_shapes), "elements": sum(_numel(s) for s in w.param_shapes),
+            "slice_numel": p.lay.I, "fused_numel": p.F, "bytes_per_step": p.bytes_per_step,
+            "steps_per_pass": p.steps}
+
+
+def bench_op(w) -> str:
+    """The reduce op a workload is timed with: AVG (the pages' default for
+    gradients not managed as DTensors) where the workload runs it."""
+    return "avg" if "avg" in w.reduce_ops else w.reduce_ops[0]
+
+
+HEADLINE = "llama7b_4layer_r8_s8"
+OTHERS = ("hsdp_block_h1024_r8_s4_d2", "ragged_heavy_r8_s8", "pure_tp_2000grads_r8_s1_d8", "tiny_fsdp_r4_s4")
+MALL_NOTE = ("working set ~1.3 GB per step against the 256 MB MALL: the RS input (403 MB) is written with "
+             "cacheable stores and partly re-read from the MALL by the RS, so its fractions can exceed the "
+             "HBM-only plain-copy ceiling (MALL-assisted)")
 
 
 def main():
@@ -607,11 +802,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="hsdp_block_h1024_r8_s4_d2")
+    ap.add_argument("--workload", default=HEADLINE, help="the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the 16-bit-gradient and shard-dim-1 variants")
+                    help="skip the HSDP block's variants (16-bit gradients, shard dim 1, zero-copy AG, "
+                         "per-parameter buckets, backward overlap) and the headline's HIP-graph pass")
     ap.add_argument("--pipeline-layers", type=int, default=8,
                     help="layers in the backward-overlap variant (0 = skip it)")
     ap.add_argument("--cold-warm-reps", type=int, default=20,
@@ -643,150 +841,84 @@ def main():
     if args.fold_shapes:
         fold_shapes(max(1, args.steps))
         return
-    w = W.WORKLOADS[args.workload]
-    R, S, D = w.rank_size, w.shard_size, w.dp_size
-    op = w.reduce_ops[0]
-    P = len(w.param_shapes)
     torch.cuda.set_device(0)
-    log(f"bench: workload {w.name} ({w.description}); R={R} S={S} D={D} op={op}")
-
-    if S > 1:
-        fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=op)
-        params = W.params(w, "cuda")
-        grads = W.grads(w, "cuda")
-        fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
-        runner = fb
-        lay, F = fb.layout, fb.F
-    else:
-        runner = PureTPRunner(w, op)
-        lay, F = runner.layout, runner.F
-    steps = runner.steps()
-    nbytes = step_bytes(w, lay, F)
-    bytes_per_step = sum(nbytes[s] for s in steps)
-
-    for _ in range(args.warmup):
-        runner.step()
-    torch.cuda.synchronize()
-
-    # a few untimed steps with events around every step find the dominant
-    # kernel; the timed region then records events around that one only
-    probe = per_step_us(runner, steps, max(3, args.warmup))
-    dom = max(steps, key=probe.get)
-
     K = args.steps
-    ev = timing_events(K)  # the dominant kernel's dispatch records these
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for k in range(K):
-        for name in steps:
-            if name == dom:
-                hp.fsdp_time_next_launch(ev[k][0], ev[k][1])
-            runner.run(name)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
-    value = bytes_per_step * K / (total_ms * 1e-3) / 1e9
-    dom_us = sum(a.elapsed_time(b) for a, b in ev) / K * 1e3
-
-    # per-step breakdown, measured after the timed region (events around
-    # every step perturb the whole-step time, so they stay out of it)
-    after = per_step_us(runner, steps, K)
-    ops = {}
-    for name in steps:
-        us = after[name]
-        gbs = nbytes[name] / (us * 1e-6) / 1e9
-        ops[name] = {"kernel": KERNEL_OF_STEP[name], "bytes": nbytes[name], "us": round(us, 2),
-                     "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"  {name:12s} {nbytes[name] / 1e6:10.1f} MB  {us:9.1f} us  {gbs:8.1f} GB/s  "
-            f"{100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
-    # cold / warm medians of single launches, and the plain-copy ceiling
-    cw = {}
-    if args.cold_warm_reps > 0:
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        med = op_medians(runner, steps, args.cold_warm_reps, flush)
-        del flush
-        for name in steps:
-            cw[name] = {m: {"us": round(med[name][m], 2),
-                            "GB/s": round(nbytes[name] / (med[name][m] * 1e-6) / 1e9, 1)} for m in ("cold", "warm")}
-            log(f"  {name:12s} median of {args.cold_warm_reps}: cold {med[name]['cold']:8.1f} us "
-                f"({cw[name]['cold']['GB/s']:7.1f} GB/s), warm {med[name]['warm']:8.1f} us "
-                f"({cw[name]['warm']['GB/s']:7.1f} GB/s)")
+    w = W.WORKLOADS[args.workload]
+    op = bench_op(w)
+    log(f"bench: workload {w.name} ({w.description}); R={w.rank_size} S={w.shard_size} D={w.dp_size} op={op}")
+    head = Pass(w, op)
+    res = head.measure(K, args.warmup, args.cold_warm_reps)
     ceiling = copy_ceiling(args.ceiling_mib, 10) if args.ceiling_mib > 0 else None
-    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
-    roof = {"bound": "hbm", "kernel": KERNEL_OF_STEP[dom], "step": dom,
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, dom),
-            "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": round(dom_us, 2),
-            "timing": "HIP events recorded by the kernel's own dispatch at its start and end, every timed step"}
-    log(f"  step: {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s; wall {wall:.3f} s for {K} steps")
-
-    # the same pass with RS copy-in fused into the RS (the RS input is never
-    # materialised): reported beside the contract's step, not instead of it
+    roof = head.roofline(res, ceiling)
     variants = {}
-    if isinstance(runner, hp.FlatBucket):
-        fsteps = runner.steps(fused_rs=True)
-        for _ in range(args.warmup):
-            runner.step(fused_rs=True)
-        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        fs.record()
-        for _ in range(K):
-            runner.step(fused_rs=True)
-        fe.record()
-        torch.cuda.synchronize()
-        f_ms = fs.elapsed_time(fe) / K
-        f_us = per_step_us(runner, ["rs_copy_reduce"], K)["rs_copy_reduce"]
-        b = nbytes["rs_copy_reduce"]
-        variants["fused_rs_copy_reduce"] = {
-            "steps_per_pass": fsteps, "ms_per_step": round(f_ms, 4),
-            "rs_copy_reduce": {"bytes": b, "us": round(f_us, 2), "GB/s": round(b / (f_us * 1e-6) / 1e9, 1)},
-            "note": "RS input never written; results identical to rs_copy_in + rs_reduce"}
-        log(f"  fused RS variant: step {f_ms * 1e3:.1f} us (vs {ms_per_step * 1e3:.1f}); rs_copy_reduce "
-            f"{f_us:.1f} us, {b / (f_us * 1e-6) / 1e9:.1f} GB/s")
-        variants["hip_graph"] = graph_variant(runner, K, args.warmup)
-        if args.pipeline_layers > 1 and runner.do_ar:
-            variants["backward_pipeline"] = pipeline_variant(w, op, args.pipeline_layers, K)
+    if isinstance(head.runner, hp.FlatBucket):
+        variants["fused_rs_copy_reduce"] = head.fused_rs_variant(K, args.warmup)
         if not args.no_variants:
-            variants["zero_copy_ag"] = zero_copy_ag_variant(w, op, K)
-            variants["per_parameter_buckets_one_ar"] = fused_group_variant(w, op, K, args.warmup)
-            variants["bf16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.bfloat16)
-            variants["fp16_grads"] = bucket_variant(w, op, K, args.warmup, grad_dtype=torch.float16)
-            dims = [1 if len(sh) > 1 and sh[1] % S == 0 else 0 for sh in w.param_shapes]
-            if any(dims):
-                variants["shard_dim_1"] = bucket_variant(w, op, K, args.warmup, shard_dims=dims)
-
+            variants["hip_graph"] = graph_variant(head.runner, K, args.warmup)
     cpu = None
     if not args.no_cpu_baseline:
-        n, el, _, cpu_per = cpu_baseline(w, args.cpu_seconds, op)
-        cpu = {"value": round(bytes_per_step * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{n} whole steps of {w.name} (all {len(steps)} steps, full size) in {el:.1f} s; "
-                         f"NumPy, single-threaded: 1 core of {os.cpu_count()} ({cpu_model()})",
-               "ops": {k: {"ms": round(v * 1e3, 3), "GB/s": round(nbytes[k] / v / 1e9, 3)}
-                       for k, v in cpu_per.items() if k in nbytes}}
-        log(f"  cpu oracle: {cpu['value']} GB/s over {n} steps ({el:.1f} s)")
-
+        k, n, el, sb, cpu_per = cpu_baseline(w, args.cpu_seconds, op, head.params or [], head.grads or [])
+        what = "the whole bucket" if k == len(w.param_shapes) else \
+            f"its first {k} of {len(w.param_shapes)} parameters ({sum(_numel(s) for s in w.param_shapes[:k])} " \
+            f"of {sum(_numel(s) for s in w.param_shapes)} elements)"
+        cpu = {"value": round(sb * n / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} whole steps of {w.name} restricted to {what}, same ranks and values, in "
+                         f"{el:.1f} s; NumPy, single-threaded: 1 core of {os.cpu_count()} ({cpu_model()})",
+               "ops": {s: {"ms": round(t * 1e3, 3), "GB/s": round(b / t / 1e9, 3)} for s, (t, b) in cpu_per.items()}}
+        log(f"  cpu oracle: {cpu['value']} GB/s over {n} sample steps ({el:.1f} s)")
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "rank_size": R, "shard_size": S, "dp_size": D,
-                   "param_dtype": str(w.param_dtype).replace("torch.", ""), "grad_dtype": "float32",
-                   "reduce_op": op, "params": P, "elements": sum(_numel(s) for s in w.param_shapes),
-                   "slice_numel": lay.I, "fused_numel": F, "bytes_per_step": bytes_per_step,
-                   "steps_per_pass": steps},
+        "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16/f32", "data": "synthetic",
+        "dtype_note": "copies move bf16 parameter bits and fp32 gradient bits; reductions compute in fp32",
+        "config": config_of(head),
         "roofline": roof,
         "cpu_baseline": cpu,
-        "ops": ops,
-        "ops_cold_warm": cw or None,
+        "ops": res["ops"],
+        "ops_cold_warm": res["cold_warm"],
         "copy_ceiling": ceiling,
         "variants": variants,
     }
+    head.release()
+    del head
+
+    # the other workloads: their own pass, dominant kernel and breakdown;
+    # the HSDP block (the only one running all five steps) carries the
+    # variants that need a replicate group
+    others = {}
+    if not args.no_other_workloads:
+        for name in OTHERS:
+            if name == w.name:
+                continue
+            wo = W.WORKLOADS[name]
+            log(f"bench: other workload {wo.name} ({wo.description})")
+            p = Pass(wo, bench_op(wo))
+            r = p.measure(K, args.warmup, 0)
+            ent = {"config": config_of(p), "value": round(r["value"], 1), "unit": "GB/s",
+                   "ms_per_step": round(r["ms_per_step"], 4), "roofline": p.roofline(r, ceiling),
+                   "ops": r["ops"]}
+            ent["value_vs"] = frac_vs(r["value"], ceiling)
+            if wo.name == "hsdp_block_h1024_r8_s4_d2":
+                ent["note"] = MALL_NOTE
+            if wo.name == "tiny_fsdp_r4_s4":
+                ent["note"] = "under 4 KB per step: launch latency only"
+            if isinstance(p.runner, hp.FlatBucket):
+                v = {"fused_rs_copy_reduce": p.fused_rs_variant(K, args.warmup)}
+                if not args.no_variants and wo.name == "hsdp_block_h1024_r8_s4_d2":
+                    v["hip_graph"] = graph_variant(p.runner, K, args.warmup)
+                    if args.pipeline_layers > 1 and p.runner.do_ar:
+                        v["backward_pipeline"] = pipeline_variant(wo, p.op, args.pipeline_layers, K)
+                    v["zero_copy_ag"] = zero_copy_ag_variant(wo, p.op, K)
+                    v["per_parameter_buckets_one_ar"] = fused_group_variant(wo, p.op, K, args.warmup)
+                    v["bf16_grads"] = bucket_variant(wo, p.op, K, args.warmup, grad_dtype=torch.bfloat16)
+                    v["fp16_grads"] = bucket_variant(wo, p.op, K, args.warmup, grad_dtype=torch.float16)
+                    dims = [1 if len(sh) > 1 and sh[1] % wo.shard_size == 0 else 0 for sh in wo.param_shapes]
+                    if any(dims):
+                        v["shard_dim_1"] = bucket_variant(wo, p.op, K, args.warmup, shard_dims=dims)
+                ent["variants"] = v
+            p.release()
+            others[wo.name] = ent
+    out["other_workloads"] = others or None
     print(json.dumps(out), flush=True)
 
 

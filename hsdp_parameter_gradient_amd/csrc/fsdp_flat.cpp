@@ -338,9 +338,9 @@ thread_local void* g_time_stop = nullptr;
 int enqueue(const Plan& p, hipStream_t stream) {
   if (!p.launch && !p.fold_dev) return ok();
   const uint32_t max_grid = fsdp::tuning().max_grid;
-  // the first kernel of the call takes a pending timing request (not one
-  // launched into a graph capture: the request then waits for the next
-  // launch outside a capture)
+  // a pending timing request spans the whole call: the first kernel records
+  // the start event, the last one the stop event (not in a launch into a
+  // graph capture: the request then waits for the next launch outside one)
   void* t0 = nullptr;
   void* t1 = nullptr;
   if (g_time_start && !capturing(stream)) {
@@ -349,13 +349,14 @@ int enqueue(const Plan& p, hipStream_t stream) {
     g_time_start = g_time_stop = nullptr;
   }
   if (p.launch) {
+    void* stop = p.fold_dev ? nullptr : t1;  // a fold launch follows: it records the stop
     int he = p.reduce ? fsdp_launch_reduce(p.es, p.dev, p.n_items, p.nsrc, p.n_chunks, p.shift, max_grid, p.avg,
-                                           p.nts, stream, t0, t1)
+                                           p.nts, stream, t0, stop)
                       : fsdp_launch_seg_copy(p.es, p.dev, p.n_items, p.n_chunks, p.shift, max_grid, p.nts, stream,
-                                             t0, t1);
+                                             t0, stop);
     if (he != hipSuccess)
       return fail(FSDP_EHIP, "%s launch: %s", p.reduce ? "reduce" : "seg_copy", hipGetErrorString((hipError_t)he));
-    t0 = t1 = nullptr;
+    t0 = nullptr;
   }
   if (p.fold_dev) {
     int he = p.fold_reduce ? fsdp_launch_fold_reduce(p.fold_elt, p.fold_dev, p.fold_items, p.fold_nsrc,

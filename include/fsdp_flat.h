@@ -261,11 +261,13 @@ void fsdp_release_cache(void);
 int fsdp_cache_info(int64_t* n_plans, int64_t* n_pinned, int64_t* table_bytes);
 
 /*
- * For callers that time one kernel: the next kernel that the calling thread
- * enqueues through any entry point above records start_event when it starts
- * executing and stop_event when it ends (both in its own dispatch, so the
- * interval excludes the launch and queue overheads that events recorded
- * around a call include).  start_event and stop_event are hipEvent_t handles
+ * For callers that time one call: the next call that the calling thread
+ * makes through any device entry point above records start_event when its
+ * first kernel starts executing and stop_event when its last kernel ends
+ * (in the kernels' own dispatches, so the interval excludes the launch and
+ * queue overheads that events recorded around a call include; a call that
+ * launches two kernels, when some parameters take the fold kernel, is
+ * timed from the start of the first to the end of the second).  start_event and stop_event are hipEvent_t handles
  * the caller created with timing enabled and on the launch's device; both
  * NULL cancels a pending request.  A call that launches nothing (an empty
  * bucket, an AR over one rank), or launches into a stream that is being
