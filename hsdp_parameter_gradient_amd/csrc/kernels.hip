@@ -575,12 +575,11 @@ __device__ __forceinline__ u32x4 narrow(Acc<E>& a, int avg, float nf) {
   }
 }
 
-// Operand vector q: MODE 0 aligned, MODE 1 shifted by r = 4*Q + b bytes
-// (compile-time dword shift), MODE 2 any shift r.
-template <int MODE, int Q>
-__device__ __forceinline__ u32x4 operand(const gvec* __restrict__ s, uint64_t q, uint32_t r, uint32_t b) {
+// Operand vector q: MODE 0 aligned, MODE 2 any shift r (two aligned
+// blocks, realigned).
+template <int MODE>
+__device__ __forceinline__ u32x4 operand(const gvec* __restrict__ s, uint64_t q, uint32_t r) {
   if (MODE == 0) return ldv(s + q);
-  if (MODE == 1) return funnel<Q>(ldv(s + q), ldv(s + q + 1), b);
   return load_shifted(s, q, r);
 }
 
@@ -595,62 +594,120 @@ __device__ __forceinline__ void store_vectors(const u32x4 (&o)[U], const fsdp::R
   }
 }
 
+// 16-byte blocks between the start of the 128-byte line holding address a
+// and a.  The loops below start their lane-linear index that many blocks
+// before the first vector, so that every wave's 64 consecutive blocks (1 KiB)
+// cover whole lines of the operands: a line cut by two waves' ranges is
+// requested by both, and under streaming loads the second request often
+// misses L2 (measured on MI355X: the RS of the ragged-heavy set, whose
+// slices sit at 4-byte offsets, fetched 3.5 % more than its operands hold
+// with unrotated runs).  The blocks before the first vector lie in the line
+// of the first one (never outside its page); they are read and discarded.
+__device__ __forceinline__ uint32_t line_phase(uint64_t a) { return (uint32_t)((a >> 4) & 7u); }
+
 // All data vectors [0, nv) of one job window for a compile-time operand
-// count K: whole iterations of U vectors per lane with the K*U operand loads
-// in flight together, then a tail of single vectors.
-template <int E, int K, int U, int MODE, int Q, bool NTS>
+// count K, every operand aligned (MODE 0) or at shifts of its own (MODE 2):
+// whole iterations of U vectors per lane with the K*U operand loads in
+// flight together, then a tail of single vectors, the lanes rotated by the
+// operands' common line phase e (line_phase; 0 when they differ).
+template <int E, int K, int U, int MODE, bool NTS>
 __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
                                            const uint64_t (&sb)[K], const uint32_t (&sr)[K], uint64_t va,
-                                           uint64_t nv, int avg, float nf) {
-  const uint32_t b = sr[0] & 3u;
-  const uint32_t lane = threadIdx.x & 63u;
+                                           uint64_t nv, int avg, float nf, uint32_t e) {
+  const uint64_t n = nv + e;  // lane-linear index j is vector j - e
   uint64_t base = 0;
-  for (; base + (uint64_t)kBlock * U <= nv; base += (uint64_t)kBlock * U) {
+  for (; base + (uint64_t)kBlock * U <= n; base += (uint64_t)kBlock * U) {
     u32x4 v[K][U];
-    uint64_t j;  // this lane's first vector; its U vectors are j + u * stride
-    uint64_t stride;
-    if (MODE == 1) {
-      // wave-contiguous groups, each source block loaded once (see copy_run)
-      const uint64_t wb = base + (uint64_t)(threadIdx.x >> 6) * 64u * U;
-      j = wb + lane;
-      stride = 64;
-      u32x4 tail[K];
+    const uint64_t j = base + threadIdx.x;  // this lane's U indices are j + u * kBlock
 #pragma unroll
-      for (int t = 0; t < K; ++t) {
-        const gvec* __restrict__ s = gptr<u32x4>(sb[t]);
+    for (int t = 0; t < K; ++t)
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[t][u] = ldv(s + j + u * 64);
-        tail[t] = s[wb + 64 * U];
-      }
-#pragma unroll
-      for (int t = 0; t < K; ++t) realign_groups<Q, U>(v[t], tail[t], lane, b);
-    } else {
-      j = base + threadIdx.x;
-      stride = kBlock;
-#pragma unroll
-      for (int t = 0; t < K; ++t)
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[t][u] = operand<MODE, Q>(gptr<u32x4>(sb[t]), j + u * kBlock, sr[t], b);
-    }
-    u32x4 o[U];
+      for (int u = 0; u < U; ++u) v[t][u] = operand<MODE>(gptr<u32x4>(sb[t]) - e, j + u * kBlock, sr[t]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Acc<E> acc = widen<E>(v[0][u]);
 #pragma unroll
       for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t][u]);
-      o[u] = narrow<E>(acc, avg, nf);
+      const u32x4 o[1] = {narrow<E>(acc, avg, nf)};
+      if (j + u * kBlock >= e) store_vectors<1, NTS>(o, jb, ptr, va, j + u * kBlock - e, kBlock);
     }
-    store_vectors<U, NTS>(o, jb, ptr, va, j, stride);
   }
-  for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
+  for (uint64_t j = base + threadIdx.x; j < n; j += kBlock) {
     u32x4 v[K];
 #pragma unroll
-    for (int t = 0; t < K; ++t) v[t] = operand<(MODE == 1 ? 2 : MODE), Q>(gptr<u32x4>(sb[t]), j, sr[t], b);
+    for (int t = 0; t < K; ++t) v[t] = operand<MODE>(gptr<u32x4>(sb[t]) - e, j, sr[t]);
     Acc<E> acc = widen<E>(v[0]);
 #pragma unroll
     for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
     const u32x4 o[1] = {narrow<E>(acc, avg, nf)};
-    store_vectors<1, NTS>(o, jb, ptr, va, j, kBlock);
+    if (j >= e) store_vectors<1, NTS>(o, jb, ptr, va, j - e, kBlock);
+  }
+}
+
+// Destination vectors per LDS piece of the shifted reduction (one 8 KiB
+// reduce chunk at the default chunk size); its LDS holds the piece's result
+// blocks and up to 7 blocks of line phase before them.
+constexpr uint32_t kRedPiece = 512;
+constexpr uint32_t kRedLds = kRedPiece + 8;
+
+// All data vectors [0, nv) of one job window whose K operands share one
+// shift r = 4*Q + b != 0 against the destination (compile-time K): the
+// operands are summed block by block in their own aligned frame (block j =
+// bytes [16 j, 16 j + 16) past sb[t]), each result block finished (AVG,
+// 16-bit rounding; both act per element, so they commute with the shift)
+// and written to LDS; destination vector q is then bytes [r, r + 16) of
+// result blocks q and q + 1.  A piece of P destination vectors reads P + 1
+// aligned blocks per operand (and the e blocks of their common line phase
+// before them, line_phase), each once, and realigns only the results, not
+// every operand.  Measured on MI355X on the RS of the ragged-heavy set (8
+// slices at 4-byte shifts): realigning each operand in registers
+// (neighbour lane's block through ds_bpermute, a closing block per operand
+// and wave, one vector per lane) 1227 us; this path 1190 us; with the lanes
+// rotated to the line phase 1166-1170 us, its fetched bytes 1.035 -> 1.011
+// times its operands' (the rest: the line at each window edge, read by both
+// windows; making those edge loads cacheable changes nothing, and moving
+// the window edges to the operands' line starts, which splits a destination
+// vector at every edge, fetched 1.028 times and took 1272 us).
+template <int E, int K, int U, int Q, bool NTS>
+__device__ __forceinline__ void reduce_run_lds(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
+                                               const uint64_t (&sb)[K], uint64_t va, uint64_t nv, uint32_t b,
+                                               int avg, float nf, u32x4* __restrict__ lds, uint32_t e) {
+  // LDS slot i holds result block i - e
+  for (uint64_t p0 = 0; p0 < nv; p0 += kRedPiece) {
+    const uint32_t np = (uint32_t)((nv - p0) < kRedPiece ? (nv - p0) : kRedPiece);
+    const uint32_t nb = np + 1 + e;  // result blocks p0 - e .. p0 + np
+    uint32_t j0 = 0;
+    for (; j0 + (uint32_t)kBlock * U <= nb; j0 += (uint32_t)kBlock * U) {
+      u32x4 v[K][U];
+#pragma unroll
+      for (int t = 0; t < K; ++t) {
+        const gvec* __restrict__ s = gptr<u32x4>(sb[t]) + p0 - e;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[t][u] = ldv(s + j0 + threadIdx.x + u * kBlock);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Acc<E> acc = widen<E>(v[0][u]);
+#pragma unroll
+        for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t][u]);
+        lds[j0 + threadIdx.x + u * kBlock] = narrow<E>(acc, avg, nf);
+      }
+    }
+    for (uint32_t j = j0 + threadIdx.x; j < nb; j += kBlock) {
+      u32x4 v[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t]) + p0 - e + j);
+      Acc<E> acc = widen<E>(v[0]);
+#pragma unroll
+      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
+      lds[j] = narrow<E>(acc, avg, nf);
+    }
+    __syncthreads();
+    for (uint32_t q = threadIdx.x; q < np; q += kBlock) {
+      const u32x4 o[1] = {funnel<Q>(lds[q + e], lds[q + e + 1], b)};
+      store_vectors<1, NTS>(o, jb, ptr, va, p0 + q, kBlock);
+    }
+    __syncthreads();  // the next piece reuses the LDS
   }
 }
 
@@ -660,34 +717,40 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
 // at a time.
 template <int E, int K, bool NTS>
 __device__ __forceinline__ void reduce_vectors(const fsdp::RedJob& jb, const uint64_t* __restrict__ ptr,
-                                               uint64_t va, uint64_t nv, int avg, float nf) {
+                                               uint64_t va, uint64_t nv, int avg, float nf,
+                                               u32x4* __restrict__ lds) {
   if constexpr (K > 0) {
     constexpr int U = (K >= 3 || E != kF32) ? 2 : 4;
-    // Shifted operands also hold a closing block each; with 8 of them one
-    // vector per lane keeps the kernel at 4 waves per SIMD (measured on
-    // MI355X: the RS of 8 misaligned slices 1320 -> 1206 us).
+    // Operands at different shifts realign each operand in registers; with
+    // 8 of them one vector per lane keeps the kernel at 4 waves per SIMD.
     constexpr int US = K >= 8 ? 1 : U;
     uint64_t sb[K];
     uint32_t sr[K];
-    bool same = true;
+    bool same = true, same_phase = true;
 #pragma unroll
     for (int t = 0; t < K; ++t) {
       const uint64_t sa = ptr[jb.src0 + t] + va;
       sr[t] = (uint32_t)(sa & 15u);
       sb[t] = sa - sr[t];
       same = same && sr[t] == sr[0];
+      same_phase = same_phase && line_phase(sb[t]) == line_phase(sb[0]);
     }
+    // the lanes are rotated to the operands' common line phase; operands at
+    // different phases are not rotated (a rotation by another operand's
+    // phase could reach into the line before an operand's first one)
+    const uint32_t e = same_phase ? line_phase(sb[0]) : 0u;
     if (same && sr[0] == 0) {
-      reduce_run<E, K, U, 0, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<E, K, U, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf, e);
     } else if (same) {
+      const uint32_t b = sr[0] & 3u;
       switch (sr[0] >> 2) {
-        case 0: reduce_run<E, K, US, 1, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 1: reduce_run<E, K, US, 1, 1, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        case 2: reduce_run<E, K, US, 1, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
-        default: reduce_run<E, K, US, 1, 3, NTS>(jb, ptr, sb, sr, va, nv, avg, nf); break;
+        case 0: reduce_run_lds<E, K, U, 0, NTS>(jb, ptr, sb, va, nv, b, avg, nf, lds, e); break;
+        case 1: reduce_run_lds<E, K, U, 1, NTS>(jb, ptr, sb, va, nv, b, avg, nf, lds, e); break;
+        case 2: reduce_run_lds<E, K, U, 2, NTS>(jb, ptr, sb, va, nv, b, avg, nf, lds, e); break;
+        default: reduce_run_lds<E, K, U, 3, NTS>(jb, ptr, sb, va, nv, b, avg, nf, lds, e); break;
       }
     } else {
-      reduce_run<E, K, US, 2, 0, NTS>(jb, ptr, sb, sr, va, nv, avg, nf);
+      reduce_run<E, K, US, 2, NTS>(jb, ptr, sb, sr, va, nv, avg, nf, 0u);
     }
   } else {
     for (uint64_t j = threadIdx.x; j < nv; j += kBlock) {
@@ -952,6 +1015,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
                                                         const uint64_t* __restrict__ ptr,
                                                         uint32_t n_job, uint64_t n_chunks,
                                                         uint32_t shift, int avg) {
+  // result blocks of the shifted path (reduce_run_lds)
+  __shared__ u32x4 lds[kRedLds];
   const uint64_t CH = uint64_t(1) << shift;
   for (uint64_t slot = blockIdx.x; slot < n_chunks; slot += gridDim.x) {
     const uint64_t c = xcd_chunk(slot, n_chunks);
@@ -974,7 +1039,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     // whole vectors of data: offsets [va, vb) relative to d0
     const uint64_t ca = align_up16(lo);
     const uint64_t cb = align_down16(hi < cend ? hi : cend);
-    if (ca < cb) reduce_vectors<E, K, NTS>(jb, ptr, ca - d0, (cb - ca) >> 4, avg, nf);
+    if (ca < cb) reduce_vectors<E, K, NTS>(jb, ptr, ca - d0, (cb - ca) >> 4, avg, nf, lds);
     // whole vectors of padding (zero) in every destination
     const uint64_t za = align_up16(lo > cend ? lo : cend);
     const uint64_t zb = align_down16(hi);

@@ -209,7 +209,10 @@ def _check_tables(dump):
             counts["blocks"] += sum(jb[6] > 1 for jb in jobs)
         state["w"].extend(_merge(w_iv))
         state["tables"] += 1
-        env = _merge([(x & ~15, (y + 15) & ~15) for x, y in state["ins"]])
+        # an input's envelope: from the 128-byte line of its first byte (the
+        # reduction's line-phase rotation reads there; a line never spans two
+        # pages) to the 16-byte block of its last byte
+        env = _merge([(x & ~127, (y + 15) & ~15) for x, y in state["ins"]])
         bad = _inside(r_iv, env)
         assert bad is None, f"read {bad} outside the inputs' aligned envelopes"
         counts[kind] += 1

@@ -60,6 +60,7 @@ def item_chunks(dst, row_bytes, rows, per, shift):
     return -(-rows // per) if rows > 1 else chunk_count(dst, row_bytes, shift)
 
 
+
 def row_vectors(k, rows, per, row_bytes, CH):
     """Chunk k of a strided block: (row, byte column) of every vector, in
     the kernel's flat order (row = q // vpr)."""
@@ -277,10 +278,15 @@ def emulate_reduce(jobs, ptr, shift, es=4):
         ca, cb = align_up16(lo), align_down16(min(hi, cend))
         if ca < cb:
             va, nv = ca - d0, (cb - ca) >> 4
+            sa = [ptr[src0 + t] + va for t in range(nsrc)]
+            rs = [a & 15 for a in sa]
+            sb = [a - r for a, r in zip(sa, rs)]
+            # compile-time operand counts rotate their lanes by the common
+            # line phase (blocks before the first one in its 128-byte line)
+            phase = {(a >> 4) & 7 for a in sb}
+            e = phase.pop() if nsrc in COMPILED_K and len(phase) == 1 and len(set(rs)) == 1 else 0
             for t in range(nsrc):
-                sa = ptr[src0 + t] + va
-                r = sa & 15
-                reads.append((sa - r, sa - r + 16 * nv + (16 if r else 0), j, t, 0))
+                reads.append((sb[t] - 16 * e, sb[t] + 16 * nv + (16 if rs[t] else 0), j, t, 0))
             for m in range(ndst):
                 writes.append((ptr[dst0 + m] + va, ptr[dst0 + m] + va + 16 * nv, "data", j, m, 0))
         za, zb = align_up16(max(lo, cend)), align_down16(hi)
@@ -305,6 +311,13 @@ def emulate_reduce(jobs, ptr, shift, es=4):
     return writes, reads
 
 
+COMPILED_K = (1, 2, 3, 4, 6, 8)  # the reduce kernel's compile-time operand counts
+
+
+def align_down128(a):
+    return a & ~127
+
+
 def check_reduce(jobs, ptr, shift, es=4):
     writes, reads = emulate_reduce(jobs, ptr, shift, es)
     per = {}
@@ -327,7 +340,9 @@ def check_reduce(jobs, ptr, shift, es=4):
     for (a, b, j, t, row) in reads:
         nbytes, data, src0, nsrc, dst0, ndst, rows, sp, dp, _ = job10(jobs[j])
         s = ptr[src0 + t] + row * sp
-        assert align_down16(s) <= a and b <= align_up16(s + data), "operand read outside its envelope"
+        # reads may start anywhere in the 128-byte line of the operand's
+        # first byte (never in another page) and end in its last 16-byte block
+        assert align_down128(s) <= a and b <= align_up16(s + data), "operand read outside its envelope"
     return writes, reads
 
 
@@ -634,7 +649,7 @@ def test_find_item_all_chunks():
 
 
 # ---------------------------------------------------------------------------
-# per-lane loops inside one window (copy_run / reduce_run)
+# per-lane loops inside one window (copy_run / reduce_run / reduce_run_lds)
 # ---------------------------------------------------------------------------
 
 def lane_loop(nv, U, shifted, block=256):
@@ -679,6 +694,107 @@ def test_lane_loops_cover_each_vector_once(U, shifted):
         assert idx == list(range(nv)), (nv, U, shifted)
         top = nv if shifted else nv - 1  # a shifted source may read block nv
         assert all(0 <= r <= top for _, r in reads), (nv, U, shifted)
+
+
+def lds_piece_loop(nv, U, e=0, block=256, piece=512):
+    """The shifted reduction's loops (reduce_run_lds): per piece of at most
+    `piece` destination vectors, whole iterations of block*U result blocks
+    then a block-strided tail load the piece's np + 1 aligned blocks of
+    every operand and the e blocks of line phase before them, writing result
+    block b to LDS slot b + e; after a barrier lane q writes destination
+    vector p0 + q from LDS slots q + e and q + e + 1.  Returns (writes,
+    reads, lds_writes, lds_reads, runs): global vector / block indices,
+    (piece, slot) pairs, and the first block of every wave's 64-lane run."""
+    writes, reads, lds_w, lds_r, runs = [], [], [], [], []
+    p0 = 0
+    while p0 < nv:
+        np_ = min(piece, nv - p0)
+        nb = np_ + 1 + e
+        j0 = 0
+        while j0 + block * U <= nb:
+            for tid in range(block):
+                for u in range(U):
+                    j = j0 + tid + u * block
+                    reads.append(p0 - e + j)
+                    lds_w.append((p0, j))
+                    if tid % 64 == 0:
+                        runs.append(p0 - e + j)
+            j0 += block * U
+        for tid in range(block):
+            j = j0 + tid
+            while j < nb:
+                reads.append(p0 - e + j)
+                lds_w.append((p0, j))
+                j += block
+        written = {slot for (pp, slot) in lds_w if pp == p0}
+        for tid in range(block):
+            q = tid
+            while q < np_:
+                assert q + e in written and q + e + 1 in written  # the barrier sits between the phases
+                lds_r.extend([(p0, q + e), (p0, q + e + 1)])
+                writes.append(p0 + q)
+                q += block
+        p0 += piece
+    return writes, reads, lds_w, lds_r, runs
+
+
+@pytest.mark.parametrize("U", [1, 2, 4])
+def test_shifted_reduce_lds_pieces(U):
+    """Each destination vector is written once; each operand block in
+    [-e, nv] (block nv holds the last vector's shifted bytes; the e blocks
+    before block 0 share its 128-byte line) is read, once per piece; only the
+    blocks around a piece edge are read twice; LDS slots stay below
+    piece + 8; every wave's run of 64 blocks starts on a line (block index
+    + e a multiple of 8, with the operand's block 0 at phase e)."""
+    for piece in (512, 64):
+        for e in (0, 1, 3, 7):
+            for nv in (1, 2, 63, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 3000):
+                writes, reads, lds_w, lds_r, runs = lds_piece_loop(nv, U, e, piece=piece)
+                assert sorted(writes) == list(range(nv)), (nv, U, piece, e)
+                assert min(reads) == -e and max(reads) == nv, (nv, U, piece, e)
+                dup = sorted(b for b in set(reads) if reads.count(b) > 1)
+                edges = sorted({b for p in range(piece, nv, piece) for b in range(p - e, p + 1)})
+                assert dup == edges, (nv, U, piece, e, dup)
+                assert len(lds_w) == len(set(lds_w)) and all(0 <= s < piece + 8 for _, s in lds_w + lds_r)
+                assert all((r + e) % 8 == 0 for r in runs), (nv, U, piece, e)
+
+
+def rotated_lane_loop(nv, U, e, block=256):
+    """reduce_run's loops (aligned operands, MODE 0) with the lanes rotated
+    by the line phase e: lane-linear index j reads vector j - e (blocks
+    before vector 0 share its line) and writes it when j >= e.  Returns
+    (writes, reads, runs)."""
+    writes, reads, runs = [], [], []
+    n = nv + e
+    base = 0
+    while base + block * U <= n:
+        for tid in range(block):
+            for u in range(U):
+                j = base + tid + u * block
+                reads.append(j - e)
+                if tid % 64 == 0:
+                    runs.append(j - e)
+                if j >= e:
+                    writes.append(j - e)
+        base += block * U
+    for tid in range(block):
+        j = base + tid
+        while j < n:
+            reads.append(j - e)
+            if j >= e:
+                writes.append(j - e)
+            j += block
+    return writes, reads, runs
+
+
+@pytest.mark.parametrize("U", [1, 2, 4])
+def test_rotated_reduce_lanes(U):
+    for e in range(8):
+        for nv in (0, 1, 7, 8, 63, 255, 256, 257, 511, 512, 1024, 1025, 3000):
+            writes, reads, runs = rotated_lane_loop(nv, U, e)
+            assert sorted(writes) == list(range(nv)), (nv, U, e)
+            assert len(reads) == len(set(reads)) and all(-e <= r < nv for r in reads), (nv, U, e)
+            assert all((r + e) % 8 == 0 for r in runs), (nv, U, e)
 
 
 def test_realign_neighbour_is_next_block():
