@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     fsdp_release_cache,
     fsdp_rs_copy_in,
     fsdp_rs_copy_reduce,
+    fsdp_rs_copy_reduce_noalloc,
     fsdp_rs_reduce,
     fsdp_time_next_launch,
     lib,
@@ -36,7 +37,8 @@ __all__ = [
     "FlatBucket", "FusedGroup", "BackwardPipeline",
     "AVG", "SUM", "FSDPError", "Layout", "fsdp_ag_copy_in", "fsdp_ag_copy_out",
     "fsdp_bucket_layout", "fsdp_cache_info", "fsdp_fused_ar", "fsdp_fused_layout", "fsdp_group_ranks",
-    "fsdp_last_error", "fsdp_release_cache", "fsdp_rs_copy_in", "fsdp_rs_copy_reduce", "fsdp_rs_reduce",
+    "fsdp_last_error", "fsdp_release_cache", "fsdp_rs_copy_in", "fsdp_rs_copy_reduce",
+    "fsdp_rs_copy_reduce_noalloc", "fsdp_rs_reduce",
     "fsdp_time_next_launch",
     "lib", "lib_path", "prepare",
 ]

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                POINTER(c_void_p), c_void_p],
             "fsdp_rs_copy_reduce": [B, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p),
                                     POINTER(c_void_p), c_void_p],
+            "fsdp_rs_copy_reduce_noalloc": [B, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p),
+                                            POINTER(c_void_p), c_void_p],
             "fsdp_fused_ar": [c_int32, P64, c_int32, c_int32, c_int32, c_int32, c_int32,
                               POINTER(c_void_p), c_void_p],
         }
@@ -362,7 +364,8 @@ def _prep_rs_reduce(shapes, rank_size, shard_size, dp_size, op, rs_in, rs_out, s
                  (b, iarr, oarr, tuple(rs_in), tuple(rs_out)))
 
 
-def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims=None):
+def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims=None,
+                         name="fsdp_rs_copy_reduce"):
     opc = _op_code(op)
     b = _BucketArg(shapes, 0, shard_dims)
     lay = fsdp_bucket_layout(b.shapes, shard_size, 0, shard_dims)
@@ -373,8 +376,13 @@ def _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_o
     garr = _ptr_array([_dev(grads[g * P + i], f"grads[{g * P + i}]", _numel(b.shapes[i]), dt)
                        for g in range(R) for i in range(P)])
     oarr = _ptr_array([_dev(rs_out[g], f"rs_out[{g}]", lay.I, dt) for g in range(R)])
-    return _Call("fsdp_rs_copy_reduce", (b.ref, R, S, int(dp_size), opc, _dtype_code(dt), garr, oarr),
+    return _Call(name, (b.ref, R, S, int(dp_size), opc, _dtype_code(dt), garr, oarr),
                  (b, garr, oarr, tuple(grads), tuple(rs_out)))
+
+
+def _prep_rs_copy_reduce_noalloc(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims=None):
+    return _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims,
+                                name="fsdp_rs_copy_reduce_noalloc")
 
 
 def _prep_fused_ar(seg_numel, rank_size, shard_size, dp_size, op, fused):
@@ -397,6 +405,7 @@ _PREP = {
     "fsdp_rs_copy_in": _prep_rs_copy_in,
     "fsdp_rs_reduce": _prep_rs_reduce,
     "fsdp_rs_copy_reduce": _prep_rs_copy_reduce,
+    "fsdp_rs_copy_reduce_noalloc": _prep_rs_copy_reduce_noalloc,
     "fsdp_fused_ar": _prep_fused_ar,
 }
 
@@ -439,6 +448,15 @@ def fsdp_rs_copy_reduce(shapes, rank_size: int, shard_size: int, dp_size: int, o
     """RS copy-in and RS in one pass: reduce chunk s of every gradient over
     each shard group straight into rs_out[g] (I elements, padding zero)."""
     _prep_rs_copy_reduce(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims)(stream)
+
+
+def fsdp_rs_copy_reduce_noalloc(shapes, rank_size: int, shard_size: int, dp_size: int, op: str,
+                                grads: Sequence[torch.Tensor], rs_out: Sequence[torch.Tensor], stream=None,
+                                shard_dims=None) -> None:
+    """fsdp_rs_copy_reduce without any device allocation (its tables go to
+    the GPU's scratch array): for graph capture and serving loops.  Calls
+    overlapping on one GPU race on that array."""
+    _prep_rs_copy_reduce_noalloc(shapes, rank_size, shard_size, dp_size, op, grads, rs_out, shard_dims)(stream)
 
 
 def fsdp_fused_ar(seg_numel, rank_size: int, shard_size: int, dp_size: int, op: str,

@@ -1123,18 +1123,19 @@ int rs_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard
                     static_cast<hipStream_t>(stream));
 }
 
-int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+// The jobs of an RS copy-reduce call (validated first), for the cached
+// entry point and the one that allocates nothing.
+struct CopyReducePlan {
+  std::vector<fsdp::RedJob> jobs;
+  std::vector<uint64_t> ptrs;
+  std::vector<fsdp::FoldRed> folds;
+  std::vector<uint64_t> fold_ptrs;
+};
+
+int plan_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
                         int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
-                        void* stream) {
-  Key key(kRsCopyReduce);
-  if (key.bucket(bucket)) {
-    for (int64_t v : {(int64_t)rank_size, (int64_t)shard_size, (int64_t)dp_size, (int64_t)op, (int64_t)dtype})
-      key.add(v);
-    key.ptrs(grads, (int64_t)rank_size * bucket->n_params);
-    key.ptrs(rs_out, rank_size);
-  }
+                        CopyReducePlan* out) {
   int rc = FSDP_OK;
-  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
   if ((rc = check_groups(rank_size, shard_size))) return rc;
   if (dp_size != rank_size / shard_size)
     return fail(FSDP_EINVAL, "dp_size %d != rank_size / shard_size = %d", dp_size, rank_size / shard_size);
@@ -1265,8 +1266,78 @@ int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     }
   }
   if (jobs.size() > 0xffffffffu || ptrs.size() > 0xffffffffu) return fail(FSDP_EINVAL, "too many jobs");
-  return run_reduce(std::move(key), jobs, ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext,
-                    static_cast<hipStream_t>(stream), folds, fold_ptrs);
+  out->jobs = std::move(jobs);
+  out->ptrs = std::move(ptrs);
+  out->folds = std::move(folds);
+  out->fold_ptrs = std::move(fold_ptrs);
+  return FSDP_OK;
+}
+
+int rs_copy_reduce_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size, int32_t dp_size,
+                        int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
+                        void* stream) {
+  Key key(kRsCopyReduce);
+  if (key.bucket(bucket)) {
+    for (int64_t v : {(int64_t)rank_size, (int64_t)shard_size, (int64_t)dp_size, (int64_t)op, (int64_t)dtype})
+      key.add(v);
+    key.ptrs(grads, (int64_t)rank_size * bucket->n_params);
+    key.ptrs(rs_out, rank_size);
+  }
+  int rc = FSDP_OK;
+  if (launch_cached(key, static_cast<hipStream_t>(stream), &rc)) return rc;
+  CopyReducePlan cp;
+  if ((rc = plan_rs_copy_reduce(bucket, rank_size, shard_size, dp_size, op, dtype, grads, rs_out, &cp))) return rc;
+  return run_reduce(std::move(key), cp.jobs, cp.ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext,
+                    static_cast<hipStream_t>(stream), cp.folds, cp.fold_ptrs);
+}
+
+// The same call with its descriptor tables written into the current GPU's
+// scratch array instead of cached device allocations: planned on every call
+// (nothing is cached), the tables carried to the GPU in the kernel
+// arguments of small writer launches on the call's stream, then the same
+// kernels launched on the same stream.  No device or pinned memory is
+// allocated, so the call can run under graph capture.
+int rs_copy_reduce_noalloc_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
+                                int32_t dp_size, int32_t op, int32_t dtype, const void* const* grads,
+                                void* const* rs_out, void* stream) {
+  CopyReducePlan cp;
+  int rc = plan_rs_copy_reduce(bucket, rank_size, shard_size, dp_size, op, dtype, grads, rs_out, &cp);
+  if (rc) return rc;
+  uint64_t job_out = 0;
+  for (const auto& jb : cp.jobs) job_out += jb.nbytes * jb.ndst * jb.rows;
+  Plan p;
+  std::vector<uint8_t> job_table, fold_table;
+  rc = plan_reduce(cp.jobs, cp.ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext, fold_reduce_out_bytes(cp.folds), &p,
+                   &job_table);
+  if (!rc) rc = plan_fold_reduce(cp.folds, cp.fold_ptrs, dtype, op == FSDP_AVG, Reuse::kReadNext, job_out, &p,
+                                 &fold_table);
+  if (rc) return rc;
+  if (job_table.empty() && fold_table.empty()) return ok();
+  const size_t fold_at = (job_table.size() + 255) / 256 * 256;
+  const size_t need = fold_at + fold_table.size();
+  if (need > fsdp::kScratchBytes)
+    return fail(FSDP_EINVAL, "fsdp_rs_copy_reduce_noalloc: the call's descriptor tables need %zu bytes, more than "
+                "the %zu-byte scratch array holds (use fsdp_rs_copy_reduce, or split the bucket)",
+                need, fsdp::kScratchBytes);
+  void* base = nullptr;
+  int he = fsdp_scratch_ptr(&base);
+  if (he != hipSuccess) return fail(FSDP_EHIP, "scratch array address: %s", hipGetErrorString((hipError_t)he));
+  if (!job_table.empty() &&
+      (he = fsdp_scratch_write(base, job_table.data(), job_table.size(), 0, stream)) != hipSuccess)
+    return fail(FSDP_EHIP, "descriptor table write: %s", hipGetErrorString((hipError_t)he));
+  if (!fold_table.empty() &&
+      (he = fsdp_scratch_write(base, fold_table.data(), fold_table.size(), fold_at, stream)) != hipSuccess)
+    return fail(FSDP_EHIP, "descriptor table write: %s", hipGetErrorString((hipError_t)he));
+  if (!job_table.empty()) {
+    p.dev = base;
+    p.bytes = job_table.size();
+  }
+  if (!fold_table.empty()) {
+    p.fold_dev = static_cast<uint8_t*>(base) + fold_at;
+    p.fold_bytes = fold_table.size();
+  }
+  // the plan's tables belong to the scratch array: never freed
+  return enqueue(p, static_cast<hipStream_t>(stream));
 }
 
 int fused_ar_impl(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,
@@ -1417,6 +1488,14 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
                         int32_t op, int32_t dtype, const void* const* grads, void* const* rs_out,
                         void* stream) {
   return guarded([&] { return rs_copy_reduce_impl(bucket, rank_size, shard_size, dp_size, op, dtype, grads, rs_out, stream); });
+}
+
+int fsdp_rs_copy_reduce_noalloc(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
+                                int32_t dp_size, int32_t op, int32_t dtype, const void* const* grads,
+                                void* const* rs_out, void* stream) {
+  return guarded([&] {
+    return rs_copy_reduce_noalloc_impl(bucket, rank_size, shard_size, dp_size, op, dtype, grads, rs_out, stream);
+  });
 }
 
 int fsdp_fused_ar(int32_t n_seg, const int64_t* seg_numel, int32_t rank_size, int32_t shard_size,

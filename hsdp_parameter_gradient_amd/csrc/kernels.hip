@@ -55,6 +55,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "plan.hpp"
@@ -1752,4 +1754,74 @@ int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uin
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scratch: the descriptor tables of the entry point that allocates nothing
+// (fsdp_rs_copy_reduce_noalloc).  One array per GPU, held until the process
+// ends; every such call on a GPU rewrites it, so calls that overlap in time
+// on one GPU (different streams) race on it.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[fsdp::kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Table bytes carried by one writer launch, in its kernel arguments (which
+// the launch copies, so the host buffer may go away when the call returns).
+constexpr uint32_t kTablePiece = 3072;
+
+struct TablePiece {
+  uint64_t offset;  // into the scratch array
+  uint32_t bytes;   // a multiple of 16, at most kTablePiece
+  uint32_t reserved;
+  u32x4 data[kTablePiece / 16];
+};
+
+// Writes one piece of a descriptor table into the scratch array: 16-byte
+// vector stores, one per lane.
+__global__ __launch_bounds__(kBlock) void table_write_kernel(uint8_t* __restrict__ dst, TablePiece piece) {
+  for (uint32_t i = threadIdx.x; i * 16u < piece.bytes; i += kBlock)
+    *reinterpret_cast<u32x4*>(dst + piece.offset + 16u * i) = piece.data[i];
+}
+
+}  // namespace
+
+int fsdp_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the host-side name of the array is not a device address: look up this
+    // device's copy once, with the device current, and use that address
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return (int)hipSuccess;
+}
+
+int fsdp_scratch_write(void* base, const void* host, size_t bytes, size_t offset, void* stream) {
+  const uint8_t* src = static_cast<const uint8_t*>(host);
+  for (size_t done = 0; done < bytes; done += kTablePiece) {
+    TablePiece piece;
+    const size_t n = bytes - done < kTablePiece ? bytes - done : kTablePiece;
+    std::memset(&piece, 0, sizeof piece);
+    std::memcpy(piece.data, src + done, n);
+    piece.offset = offset + done;
+    piece.bytes = (uint32_t)((n + 15) & ~size_t(15));
+    hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint8_t*>(base), piece);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return (int)hipSuccess;
 }

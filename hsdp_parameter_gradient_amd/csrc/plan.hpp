@@ -19,6 +19,7 @@
 // chunk; items are never empty.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fsdp {
@@ -109,6 +110,10 @@ struct FoldRed {
   uint64_t reserved[3];
 };
 
+// Bytes of the per-GPU scratch array that holds the descriptor tables of
+// the entry point that allocates nothing (fsdp_rs_copy_reduce_noalloc).
+constexpr size_t kScratchBytes = size_t(1) << 20;
+
 static_assert(sizeof(CopySeg) == 64, "CopySeg layout");
 static_assert(sizeof(RedJob) == 64, "RedJob layout");
 static_assert(sizeof(FoldSeg) == 64, "FoldSeg layout");
@@ -152,4 +157,11 @@ int fsdp_launch_fold(const void* dev_table, uint32_t n_fold, uint64_t n_chunks, 
 int fsdp_launch_fold_reduce(int elt, const void* dev_table, uint32_t n_item, uint32_t n_src, uint64_t n_chunks,
                             uint32_t max_grid, int narrow, int avg, int stream_stores, void* stream,
                             void* start_event, void* stop_event);
+// The current device's scratch array (fsdp::kScratchBytes, 256-byte
+// aligned; its address is looked up once per device).
+int fsdp_scratch_ptr(void** out);
+// Enqueue on `stream` the writes of `bytes` host bytes to base + offset
+// (base: fsdp_scratch_ptr's address), carried in kernel arguments: the host
+// buffer may be freed when this returns.  offset is a multiple of 16.
+int fsdp_scratch_write(void* base, const void* host, size_t bytes, size_t offset, void* stream);
 }

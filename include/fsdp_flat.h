@@ -235,6 +235,25 @@ int fsdp_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
                         const void* const* grads, void* const* rs_out, void* stream);
 
 /*
+ * fsdp_rs_copy_reduce for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result (bit for bit), validation and
+ * errors as fsdp_rs_copy_reduce; it allocates no device or pinned host
+ * memory.  Its descriptor tables live in a static per-GPU scratch array of
+ * 1 MiB (held until the process ends), written on every call by small
+ * kernel launches on `stream` that carry the table bytes in their kernel
+ * arguments, followed by the same kernels as fsdp_rs_copy_reduce.  Nothing
+ * is cached: every call plans again on the host (host heap memory only).
+ * Every call on a GPU rewrites that GPU's array, so calls that overlap in
+ * time on one GPU (on different streams) race; calls in one stream order
+ * are safe.  A call whose tables exceed the array (roughly 10,000 jobs) is
+ * refused with FSDP_EINVAL before anything is enqueued.
+ */
+int fsdp_rs_copy_reduce_noalloc(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shard_size,
+                                int32_t dp_size, int32_t op, int32_t dtype,
+                                const void* const* grads, void* const* rs_out, void* stream);
+
+/*
  * Fused AR over every replicate group, in place ([HYPER] 2.1, 2.3):
  *   acc = sum_{d=0..D-1} fused[d*S+s][k]  (ascending d, fp32),
  *   AVG: acc = acc / D;  fused[d*S+s][k] = acc for every d,

@@ -80,6 +80,7 @@ int main(void) {
   /* device entry points reject bad arguments before any HIP call */
   CHECK(fsdp_ag_copy_in(&b, 4, 7, NULL, NULL, NULL) == FSDP_ENOTIMPL);
   CHECK(fsdp_rs_reduce(&b, 8, 4, 3, FSDP_SUM, FSDP_F32, NULL, NULL, NULL) == FSDP_EINVAL);
+  CHECK(fsdp_rs_copy_reduce_noalloc(&b, 8, 4, 3, FSDP_SUM, FSDP_F32, NULL, NULL, NULL) == FSDP_EINVAL);
 
   if (failures) return 1;
   printf("ok\n");

@@ -42,6 +42,15 @@ int fsdp_launch_fold_reduce(int, const void*, uint32_t, uint32_t, uint64_t, uint
   std::abort();
 }
 
+int fsdp_scratch_ptr(void** out) {
+  *out = nullptr;
+  return (int)hipErrorNoDevice;  // no device here: the call stops after planning
+}
+int fsdp_scratch_write(void*, const void*, size_t, size_t, void*) {
+  std::fprintf(stderr, "scratch writer reached without a device\n");
+  std::abort();
+}
+
 // Set by the "throw" mode: the hook then throws the given exception kind
 // (1 bad_alloc, 2 length_error, 3 runtime_error), as an allocation inside
 // the planner would.
@@ -207,6 +216,15 @@ void run_case(const Case& c, int32_t S, int32_t R, int32_t es, bool misalign) {
   EXPECT(fsdp_rs_reduce(&b, R, S, D, FSDP_AVG, dtype, rs_in_c, rs_out.data(), nullptr), want);
   dump_io(out_sp, grad_sp);
   EXPECT(fsdp_rs_copy_reduce(&b, R, S, D, FSDP_SUM, dtype, grads.data(), rs_out.data(), nullptr), want);
+  // the variant that allocates nothing plans the same tables, then stops at
+  // the scratch array's address (no device), or refuses tables too large
+  // for the scratch array
+  dump_io(out_sp, grad_sp);
+  {
+    const int rc = fsdp_rs_copy_reduce_noalloc(&b, R, S, D, FSDP_SUM, dtype, grads.data(), rs_out.data(), nullptr);
+    const bool big = rc == FSDP_EINVAL && std::strstr(fsdp_last_error(), "scratch");
+    if (!(rc == want || (work && big))) expect(rc, want, "fsdp_rs_copy_reduce_noalloc", __LINE__);
+  }
 
   // fused buffers: this bucket's RS output plus two more segments
   const int64_t segs[3] = {I, 3, 1000};

@@ -39,7 +39,8 @@ def test_header_declares_the_five_ops_and_queries():
     names = declared_functions()
     for n in ("fsdp_ag_copy_in", "fsdp_ag_copy_out", "fsdp_rs_copy_in", "fsdp_rs_reduce",
               "fsdp_rs_copy_reduce", "fsdp_fused_ar", "fsdp_bucket_layout", "fsdp_fused_layout", "fsdp_group_ranks",
-              "fsdp_last_error", "fsdp_release_cache", "fsdp_time_next_launch", "fsdp_cache_info"):
+              "fsdp_last_error", "fsdp_release_cache", "fsdp_time_next_launch", "fsdp_cache_info",
+              "fsdp_rs_copy_reduce_noalloc"):
         assert n in names
 
 
@@ -190,6 +191,10 @@ def test_device_entry_points_reject_bad_arguments(L):
     inside = _ptrs([BASE + 0x100000 + 8] + [BASE + 0x10000000 * (g + 1) for g in range(1, 8)])
     assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 2, 0, 0, g8, inside, None) == 5
     assert L.fsdp_rs_copy_reduce(b.ref, 8, S, 3, 0, 0, g8, out8, None) == 1
+    # the variant that allocates nothing validates the same way
+    assert L.fsdp_rs_copy_reduce_noalloc(b.ref, 8, S, 2, 0, 5, g8, out8, None) == 2
+    assert L.fsdp_rs_copy_reduce_noalloc(b.ref, 8, S, 2, 0, 0, g8, inside, None) == 5
+    assert L.fsdp_rs_copy_reduce_noalloc(b.ref, 8, S, 3, 0, 0, g8, out8, None) == 1
     # fused_ar: base not 512-byte aligned, an unknown dtype
     segs = (ctypes.c_int64 * 2)(100, 3)
     f8 = _ptrs([BASE + 0x100000 * g + 256 for g in range(8)])
@@ -296,6 +301,20 @@ def test_shared_fused_buffers_each_bucket_ar_covers_its_own_segment():
         spans.sort()
         assert spans[0][0] == 0 and spans[-1][1] == F
         assert all(a[1] == b[0] for a, b in zip(spans, spans[1:])), spans
+
+
+def test_noalloc_refuses_tables_beyond_its_scratch(L):
+    """fsdp_rs_copy_reduce_noalloc plans on the host first: a call whose
+    descriptor tables exceed the 1 MiB scratch array is refused with
+    FSDP_EINVAL and a message naming the sizes, before any HIP call (so it
+    runs here, without a GPU, on fake addresses)."""
+    P, R, S = 2000, 8, 8
+    b = hp._binding._BucketArg([(8,)] * P)
+    g = _ptrs([BASE + 0x1000 * (k + 1) for k in range(R * P)])
+    out = _ptrs([BASE + 0x40000000 + 0x100000 * (k + 1) for k in range(R)])
+    assert L.fsdp_rs_copy_reduce_noalloc(b.ref, R, S, 1, 0, 0, g, out, None) == 1
+    msg = hp.fsdp_last_error()
+    assert "scratch" in msg and "1048576" in msg, msg
 
 
 def test_time_next_launch_arguments(L):
