@@ -535,6 +535,142 @@ def fold_shapes(reps: int) -> None:
     print(json.dumps({"fold_shapes": out, "timing": f"events around {reps} back-to-back prepared calls"}), flush=True)
 
 
+def pipeline_cases():
+    """The backward-overlap cases: 8 layers of the HSDP block, and 2 layers
+    shaped like one Llama-7B layer each (its q, k, v, o, gate, up, down and
+    two norms) in the same HSDP configuration (rank_size 8 = 2 x 4), since
+    the 4-layer bucket itself has no replicate group (dp_size 1)."""
+    import dataclasses
+
+    import workloads as W
+    blk = W.HSDP_BLOCK
+    llama_layer = dataclasses.replace(blk, name="llama7b_layer_r8_s4_d2", number=6,
+                                      param_shapes=W.LLAMA7B_4L.param_shapes[:9],
+                                      param_dtype=W.LLAMA7B_4L.param_dtype)
+    return [(blk, 8), (llama_layer, 2)]
+
+
+def pipeline_trace(reps: int) -> None:
+    """Replays of the captured backward (RS copy-reduce of each layer, fused
+    AR of the previous one; BackwardPipeline) for every pipeline case:
+    first the serial graph, then the two-stream graph, `reps` timed replays
+    each after 3 untimed ones, a synchronisation after every replay (so
+    that a kernel trace of this command shows the passes apart).  Prints
+    one JSON line with the median pass times."""
+    import statistics
+
+    import torch
+
+    import hsdp_parameter_gradient_amd as hp
+    import workloads as W
+    out = []
+    for w, layers in pipeline_cases():
+        R, S, P = w.rank_size, w.shard_size, len(w.param_shapes)
+        buckets = []
+        for l in range(layers):
+            wl = dataclasses_replace(w, number=w.number * 1000 + l)
+            fb = hp.FlatBucket(w.param_shapes, R, S, w.param_dtype, op=bench_op(w))
+            params = [torch.zeros(sh, dtype=w.param_dtype, device="cuda") for sh in w.param_shapes]
+            grads = W.grads(wl, "cuda")
+            fb.bind(fb.shard_views(params), [grads[g][i].reshape(-1) for g in range(R) for i in range(P)])
+            buckets.append(fb)
+        pipe = hp.BackwardPipeline(buckets, fused_rs=True)
+        res = {"case": w.name, "layers": layers, "rank_size": R, "shard_size": S, "dp_size": R // S}
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for name, pipelined in (("serial", False), ("pipelined", True)):
+            g = pipe.graph(pipelined=pipelined)
+            for _ in range(3):
+                g.replay()
+                torch.cuda.synchronize()
+            t = []
+            for _ in range(reps):
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                t.append(a.elapsed_time(b))
+            res[name + "_ms_median"] = round(statistics.median(t), 4)
+            del g
+        log(f"  {w.name} x {layers} layers: graph replay serial {res['serial_ms_median']:.3f} ms, "
+            f"two streams {res['pipelined_ms_median']:.3f} ms")
+        out.append(res)
+        del pipe, buckets
+        hp.fsdp_release_cache()
+        torch.cuda.empty_cache()
+    print(json.dumps({"pipeline_trace": out, "replays_per_order": reps}), flush=True)
+
+
+def overlap_summary(csv_path: str, reps: int, gap_us: float = 15.0) -> None:
+    """Reads a rocprofv3 kernel trace (trace_kernel_trace.csv) of
+    `bench.py --pipeline-trace --steps reps` and finds its passes (told apart
+    by idle gaps of more than gap_us); per pass, the pass time, the busy
+    time of the RS copy-reduce kernels (4 operands) and of the fused AR
+    kernels (2 operands), and the time both run at once.  Per case (the
+    passes with one kernel count), its last 2 (reps + 3) passes are the
+    replays, the serial graph's then the two-stream graph's; prints their
+    medians.  One JSON line."""
+    import statistics
+    import csv
+    ev = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            kind = "rs" if "reduce_kernel<0, 4" in name else "ar" if "reduce_kernel<0, 2" in name else None
+            if kind:
+                ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind))
+    ev.sort()
+    passes, cur, end = [], [], 0
+    for e in ev:
+        if cur and e[0] - end > gap_us * 1e3:
+            passes.append(cur)
+            cur = []
+        end = max(end, e[1]) if cur else e[1]
+        cur.append(e)
+    if cur:
+        passes.append(cur)
+
+    def union(iv):
+        iv = sorted(iv)
+        out = []
+        for a, b in iv:
+            if out and a <= out[-1][1]:
+                out[-1][1] = max(out[-1][1], b)
+            else:
+                out.append([a, b])
+        return out
+
+    def inter(x, y):
+        i = j = 0
+        tot = 0
+        while i < len(x) and j < len(y):
+            lo, hi = max(x[i][0], y[j][0]), min(x[i][1], y[j][1])
+            tot += max(0, hi - lo)
+            if x[i][1] < y[j][1]:
+                i += 1
+            else:
+                j += 1
+        return tot
+
+    rows = []
+    for p in passes:
+        rs = union([(a, b) for a, b, k in p if k == "rs"])
+        ar = union([(a, b) for a, b, k in p if k == "ar"])
+        rows.append({"kernels": len(p), "pass_us": (max(b for _, b, _ in p) - p[0][0]) / 1e3,
+                     "rs_busy_us": sum(b - a for a, b in rs) / 1e3, "ar_busy_us": sum(b - a for a, b in ar) / 1e3,
+                     "overlap_us": inter(rs, ar) / 1e3})
+    cases = []
+    for nk in dict.fromkeys(r["kernels"] for r in rows if r["kernels"] > 1):
+        sel = [r for r in rows if r["kernels"] == nk][-2 * (reps + 3):]
+        half = len(sel) // 2
+        case = {"kernels_per_pass": nk}
+        for order, part in (("serial", sel[:half]), ("pipelined", sel[half:])):
+            case[order] = {k: round(statistics.median(r[k] for r in part), 2)
+                           for k in ("pass_us", "rs_busy_us", "ar_busy_us", "overlap_us")}
+            case[order]["passes"] = len(part)
+        cases.append(case)
+    print(json.dumps({"trace": csv_path, "cases": cases}), flush=True)
+
+
 def sample_shapes(w):
     """The CPU baseline's sample of a workload: the whole bucket when it has
     at most 64 M elements, else its leading parameters up to a quarter of
@@ -820,7 +956,15 @@ def main():
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--fold-shapes", action="store_true",
                     help="only time the dim-1 short-row and odd-pitch cases (fold kernels) and exit")
+    ap.add_argument("--pipeline-trace", action="store_true",
+                    help="only replay the captured backward overlap (serial, then two streams) and exit")
+    ap.add_argument("--overlap-summary", metavar="CSV",
+                    help="only summarise a rocprofv3 kernel trace of --pipeline-trace and exit (no GPU)")
     args = ap.parse_args()
+
+    if args.overlap_summary:
+        overlap_summary(args.overlap_summary, max(1, args.steps))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: the benchmark runs on one GPU only (the R ranks are "
@@ -840,6 +984,9 @@ def main():
         return
     if args.fold_shapes:
         fold_shapes(max(1, args.steps))
+        return
+    if args.pipeline_trace:
+        pipeline_trace(max(1, args.steps))
         return
     torch.cuda.set_device(0)
     K = args.steps
