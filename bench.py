@@ -477,8 +477,9 @@ def calibration_copy(mib: int, reps: int) -> None:
 
 
 # Parameters sharded on dim 1 whose chunk rows are short or sit at per-row
-# alignments (the fold kernels' cases), with a control of 16-byte-aligned
-# rows: (shapes, S, R, dtype name).
+# alignments (the fold kernels' cases, the last two with rows too long for
+# one chunk: flat chunks), with a control of 16-byte-aligned rows:
+# (shapes, S, R, dtype name).
 FOLD_SHAPES = [
     ([(8000000, 6)], 2, 2, "float32"),
     ([(4000000, 12, 3)], 4, 4, "bfloat16"),
@@ -488,6 +489,8 @@ FOLD_SHAPES = [
     ([(20000, 1540)], 4, 4, "bfloat16"),
     ([(20000, 1030, 4)], 2, 2, "float16"),
     ([(20000, 1024)], 4, 4, "bfloat16"),
+    ([(10000, 4098)], 2, 2, "float32"),
+    ([(3000, 8248)], 8, 8, "bfloat16"),
 ]
 
 

@@ -562,6 +562,20 @@ bool fold_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH, uint6
   return row_bytes < kInterleaveRow || row_bytes % m != 0;
 }
 
+// Dim-k chunk rows too long for the S pieces of a full-tensor row to fit one
+// chunk, at per-row alignments (not a multiple of m bytes): the full tensor
+// is cut into flat chunks of kFlatChunk bytes whatever rows they cross
+// (rows_per_chunk 0 in the fold items), staged through LDS so that both
+// sides move aligned vectors.  Pieces of at least kFlatMinRun bytes keep the
+// pieces meeting one chunk few.
+constexpr uint64_t kFlatChunk = 12288;
+constexpr uint64_t kFlatMinRun = 1024;
+
+bool long_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH, uint64_t m) {
+  return S >= 2 && rows >= 2 && S * row_bytes > CH && row_bytes >= kFlatMinRun && row_bytes % m != 0 &&
+         S * row_bytes <= (uint64_t(1) << 31);
+}
+
 // The S ranks' rows of one parameter: base[s] = (first source row, first
 // destination row) of rank s; the same row length, row count and pitches.
 void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<std::pair<uint64_t, uint64_t>>& base,
@@ -586,7 +600,8 @@ void push_rows_interleaved(std::vector<fsdp::CopySeg>& segs, const std::vector<s
 bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0, uint64_t rank_pitch, int32_t S,
                uint64_t row_bytes, uint64_t rows, int es, bool gather) {
   const uint64_t CH = uint64_t(1) << fsdp::tuning().copy_shift;
-  if (!fold_rows(row_bytes, rows, (uint64_t)S, CH, 8)) return false;
+  const bool whole = fold_rows(row_bytes, rows, (uint64_t)S, CH, 8);
+  if (!whole && !long_rows(row_bytes, rows, (uint64_t)S, CH, 8)) return false;
   const uint64_t m = full | row_bytes | rank0 | rank_pitch;
   const uint32_t unit = (m & 15u) == 0 ? 16u : (m & 7u) == 0 ? 8u : (m & 3u) == 0 ? 4u : 2u;
   if (unit < (uint32_t)es) return false;
@@ -594,7 +609,8 @@ bool push_fold(std::vector<fsdp::FoldSeg>& folds, uint64_t full, uint64_t rank0,
   f.full = full;
   f.run_bytes = row_bytes;
   f.rows = rows;
-  f.rows_per_chunk = CH / ((uint64_t)S * row_bytes);
+  f.rows_per_chunk = whole ? CH / ((uint64_t)S * row_bytes) : 0;  // 0: flat chunks
+  f.reserved = whole ? 0u : (uint32_t)kFlatChunk;
   f.rank0 = rank0;
   f.rank_pitch = rank_pitch;
   f.nrank = (uint32_t)S;
@@ -621,7 +637,13 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
   const uint64_t CH = uint64_t(1) << fsdp::tuning().reduce_shift;
   const uint64_t CHX = fold_reduce_max_chunk();
   const uint64_t S = src.size();
-  if (dst.size() != S || !fold_rows(row_bytes, rows, S, CHX, 16)) return false;
+  if (dst.size() != S) return false;
+  const bool whole = fold_rows(row_bytes, rows, S, CHX, 16);
+  // flat chunks are staged through LDS block by block, which needs every
+  // operand at the same address modulo 16
+  bool same16 = true;
+  for (uint64_t a : src) same16 = same16 && ((a ^ src[0]) & 15u) == 0;
+  if (!whole && !(same16 && long_rows(row_bytes, rows, S, CHX, 16))) return false;
   uint64_t m = row_bytes;
   for (uint64_t a : src) m |= a;
   for (uint64_t a : dst) m |= a;
@@ -633,8 +655,9 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
   // reduce-sized chunks, or larger ones where a reduce chunk would hold
   // one full row and leave most of itself empty (measured on MI355X:
   // (30000, 2050, 1) bf16 over 2 ranks 85 -> 67 us; short rows lose 2-4 %
-  // with the larger chunks)
-  f.rows_per_chunk = 2 * S * row_bytes <= CH ? CH / (S * row_bytes) : CHX / (S * row_bytes);
+  // with the larger chunks); 0: flat chunks of kFlatChunk bytes
+  f.rows_per_chunk = !whole ? 0 : 2 * S * row_bytes <= CH ? CH / (S * row_bytes) : CHX / (S * row_bytes);
+  f.reserved[0] = whole ? 0 : kFlatChunk;
   f.src0 = (uint32_t)ptrs.size();
   ptrs.insert(ptrs.end(), src.begin(), src.end());
   f.dst0 = (uint32_t)ptrs.size();
@@ -686,6 +709,13 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, uint64_t ot
   return FSDP_OK;
 }
 
+// Chunks of a fold or fold-reduce item: whole full rows per chunk, or with
+// rows_per_chunk 0 flat chunks of sub bytes of the whole full tensor.
+uint64_t fold_item_chunks(uint64_t rows, uint64_t rows_per_chunk, uint64_t full_row, uint64_t sub) {
+  if (rows_per_chunk == 0) return (rows * full_row + sub - 1) / sub;
+  return (rows + rows_per_chunk - 1) / rows_per_chunk;
+}
+
 // Plan the fold items of a copy (a launch of its own) into *table.
 int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint64_t other_out, Plan* p,
               std::vector<uint8_t>* table) {
@@ -696,7 +726,8 @@ int plan_fold(const std::vector<fsdp::FoldSeg>& folds, int es, Reuse reuse, uint
   uint64_t n = 0;
   for (size_t k = 0; k < folds.size(); ++k) {
     begin[k] = n;
-    n += (folds[k].rows + folds[k].rows_per_chunk - 1) / folds[k].rows_per_chunk;
+    n += fold_item_chunks(folds[k].rows, folds[k].rows_per_chunk, folds[k].nrank * folds[k].run_bytes,
+                     folds[k].reserved);
   }
   append(*table, begin.data(), begin.size());
   append(*table, folds.data(), folds.size());
@@ -763,7 +794,8 @@ int plan_fold_reduce(const std::vector<fsdp::FoldRed>& items, const std::vector<
   uint64_t n = 0;
   for (size_t k = 0; k < items.size(); ++k) {
     begin[k] = n;
-    n += (items[k].rows + items[k].rows_per_chunk - 1) / items[k].rows_per_chunk;
+    n += fold_item_chunks(items[k].rows, items[k].rows_per_chunk, items[k].nrank * items[k].run_bytes,
+                     items[k].reserved[0]);
   }
   append(*table, begin.data(), begin.size());
   append(*table, items.data(), items.size());
@@ -1032,7 +1064,8 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
           continue;
         }
         if (interleave_rows((uint64_t)(run * es), (uint64_t)L.outer[i]) ||
-            fold_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift, 8))
+            fold_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift, 8) ||
+            long_rows((uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)S, uint64_t(1) << fsdp::tuning().copy_shift, 8))
           continue;  // below
         push_rows(segs, src, d0, (uint64_t)(run * es), (uint64_t)L.outer[i], (uint64_t)(L.dk[i] * L.inner[i] * es),
                   (uint64_t)(run * es));
@@ -1051,7 +1084,8 @@ int rs_copy_in_impl(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t shar
     for (int32_t i = 0; i < P; ++i) {
       const uint64_t row = (uint64_t)(L.row_len[(size_t)i * S] * L.inner[i] * es);
       const uint64_t rows = (uint64_t)L.outer[i];
-      if (L.padded[i] == 0 || L.outer[i] == 1 || !(interleave_rows(row, rows) || fold_rows(row, rows, S, CHC, 8)))
+      if (L.padded[i] == 0 || L.outer[i] == 1 ||
+          !(interleave_rows(row, rows) || fold_rows(row, rows, S, CHC, 8) || long_rows(row, rows, S, CHC, 8)))
         continue;
       auto rank_of = [&](int32_t s) { return (uint64_t)rs_in[g] + (uint64_t)((s * L.I + L.in_off[i]) * es); };
       auto grad_of = [&](int32_t s) {
@@ -1234,6 +1268,7 @@ int plan_rs_copy_reduce(const fsdp_bucket_t* bucket, int32_t rank_size, int32_t 
     const uint64_t row = (uint64_t)(run * es), rows = (uint64_t)L.outer[i];
     per_group[(size_t)i] = L.padded[i] > 0 && L.outer[i] > 1 && L.padded[i] == L.outer[i] * run &&
                            (fold_rows(row, rows, (uint64_t)S, fold_reduce_max_chunk(), 16) ||
+                            long_rows(row, rows, (uint64_t)S, fold_reduce_max_chunk(), 16) ||
                             (block_ok(i, 0) && interleave_rows(row, rows)));
   }
   for (int32_t g = 0; g < R; ++g)

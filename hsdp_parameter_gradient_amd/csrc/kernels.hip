@@ -1274,6 +1274,153 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
   __syncthreads();  // the next chunk reuses the LDS
 }
 
+// Flat chunks of a fold item whose full-tensor row does not fit one chunk
+// (rows_per_chunk == 0, fsdp::FoldSeg): the full tensor is contiguous, so
+// chunk k is its bytes [X0, X1) = [k sub, (k + 1) sub) (the last one
+// shorter), whatever rows they cross.  The full tensor is a sequence of
+// pieces of run bytes, piece p being row p / S of rank p % S; the chunk
+// meets pieces p_lo .. p_hi, piece p's part being its bytes [a, b)
+// (chunk-relative, a multiple of the unit apart).  Each part is contiguous
+// on both sides; the chunk is staged through LDS so that both sides move
+// aligned 16-byte vectors, the ends element by element (G-sized elements,
+// 2 or 4 bytes).
+struct FlatChunk {
+  uint64_t X0;      // first full-tensor byte
+  uint32_t n;       // bytes
+  uint64_t p_lo;    // first piece
+  uint32_t off0;    // X0 - p_lo * run (< run)
+  uint32_t pieces;  // p_hi - p_lo + 1
+};
+
+__device__ __forceinline__ FlatChunk flat_chunk(uint64_t k, uint64_t total, uint32_t sub, uint32_t run) {
+  FlatChunk c;
+  c.X0 = k * sub;
+  c.n = (uint32_t)(total - c.X0 < sub ? total - c.X0 : sub);
+  c.p_lo = c.X0 / run;
+  c.off0 = (uint32_t)(c.X0 - c.p_lo * run);
+  c.pieces = (c.off0 + c.n - 1) / run + 1;
+  return c;
+}
+
+// Piece q of a chunk (q < pieces): chunk-relative bytes [a, b).
+__device__ __forceinline__ void flat_part(const FlatChunk& c, uint32_t run, uint32_t q, uint32_t* a, uint32_t* b) {
+  const uint32_t lo = q * run, hi = lo + run;  // in off0-shifted coordinates
+  *a = (lo > c.off0 ? lo : c.off0) - c.off0;
+  *b = (hi < c.off0 + c.n ? hi : c.off0 + c.n) - c.off0;
+}
+
+// LDS bytes kept at the end of the fold LDS for the pieces' offsets.
+constexpr uint32_t kFlatAdj = 256;
+
+template <typename G>
+__device__ __forceinline__ u32x4 pack_elts(const G (&e)[16 / sizeof(G)]) {
+  constexpr uint32_t gb = sizeof(G);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (uint32_t k = 0; k < 16 / gb; ++k) w[k * gb / 4] |= (uint32_t)e[k] << ((k * gb) % 4 * 8);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// The 16 bytes at LDS byte offset o (a multiple of the element): four
+// dwords when o is 4-byte aligned, else five from the one holding o,
+// realigned (the fifth may lie past the bytes written, never past the LDS
+// array).
+__device__ __forceinline__ u32x4 lds_vec(const uint8_t* lds, uint32_t o) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + (o & ~3u));
+  const uint32_t b = o & 3u;
+  if (b == 0) return u32x4{w[0], w[1], w[2], w[3]};
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
+  return u32x4{__builtin_amdgcn_alignbyte(w1, w0, b), __builtin_amdgcn_alignbyte(w2, w1, b),
+               __builtin_amdgcn_alignbyte(w3, w2, b), __builtin_amdgcn_alignbyte(w4, w3, b)};
+}
+
+// Scatter of a flat chunk whose full-tensor bytes sit in LDS at offset
+// delta + (chunk-relative byte): every piece's part, piece p's at
+// dst(p, a) (its bytes from the part's start), written as aligned vectors
+// (16 consecutive LDS bytes each) and element-wise ends.
+template <typename G, bool NTS, typename Dst>
+__device__ __forceinline__ void flat_scatter(const FlatChunk& c, uint32_t run, uint32_t delta, const uint8_t* lds,
+                                             Dst dst) {
+  for (uint32_t q = 0; q < c.pieces; ++q) {
+    uint32_t a, b;
+    flat_part(c, run, q, &a, &b);
+    const uint64_t d = dst(c.p_lo + q, a);
+    const uint64_t va = align_up16(d), vb = align_down16(d + (b - a));
+    const uint32_t nv = va < vb ? (uint32_t)((vb - va) >> 4) : 0u;
+    const uint32_t o0 = delta + a + (uint32_t)(va - d);
+    for (uint32_t j = threadIdx.x; j < nv; j += kBlock)
+      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), lds_vec(lds, o0 + j * 16));
+    if (threadIdx.x < 2)
+      fold_ends<G, NTS>(d, d + (b - a), threadIdx.x, [&](uint64_t y) {
+        return *reinterpret_cast<const G*>(lds + delta + a + (uint32_t)(y - d));
+      });
+  }
+}
+
+template <typename G, bool NTS>
+__device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, uint8_t* lds) {
+  constexpr uint32_t gb = sizeof(G);
+  constexpr uint32_t NE = 16 / gb;
+  const uint32_t run = (uint32_t)f.run_bytes, S = f.nrank;
+  const FlatChunk c = flat_chunk(k, f.rows * S * run, f.reserved, run);
+  const uint64_t F = f.full + c.X0;  // the chunk's first full-tensor byte
+  // rank-side address of byte a (chunk-relative) of piece p
+  auto src = [&](uint64_t p, uint32_t a) {
+    const uint64_t r = p / S;
+    const uint32_t s = (uint32_t)(p - r * S);
+    return f.rank0 + s * f.rank_pitch + r * run + (c.X0 + a - p * run);
+  };
+  if (f.gather) {
+    // window of piece q: the aligned blocks of its part, the windows one
+    // after another; adj[q] = LDS offset of chunk byte 0 in piece q's frame
+    int32_t* adj = reinterpret_cast<int32_t*>(lds + kFoldLds - kFlatAdj);
+    uint32_t w = 0;
+    for (uint32_t q = 0; q < c.pieces; ++q) {
+      uint32_t a, b;
+      flat_part(c, run, q, &a, &b);
+      const uint64_t p = src(c.p_lo + q, a);
+      const uint64_t blk0 = align_down16(p);
+      const uint32_t nb = (uint32_t)((align_up16(p + (b - a)) - blk0) >> 4);
+      if (threadIdx.x == 0) adj[q] = (int32_t)(w + (uint32_t)(p & 15u)) - (int32_t)a;
+      for (uint32_t j = threadIdx.x; j < nb; j += kBlock)
+        *reinterpret_cast<u32x4*>(lds + w + j * 16) = ldv(gptr<u32x4>(blk0 + (uint64_t)j * 16));
+      w += nb * 16;
+    }
+    __syncthreads();
+    auto elt = [&](uint32_t x) {  // chunk-relative byte x
+      const uint32_t q = (x + c.off0) / run;
+      return *reinterpret_cast<const G*>(lds + (adj[q] + (int32_t)x));
+    };
+    const uint64_t va = align_up16(F), vb = align_down16(F + c.n);
+    const uint32_t nv = va < vb ? (uint32_t)((vb - va) >> 4) : 0u;
+    const uint32_t xa = (uint32_t)(va - F);
+    for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
+      const uint32_t x = xa + j * 16;
+      const uint32_t q = (x + c.off0) / run;
+      u32x4 v;
+      if (x + c.off0 + 16 <= (q + 1) * run) {  // inside one piece: 16 consecutive LDS bytes
+        v = lds_vec(lds, (uint32_t)(adj[q] + (int32_t)x));
+      } else {
+        G e[NE];
+#pragma unroll
+        for (uint32_t i = 0; i < NE; ++i) e[i] = elt(x + i * gb);
+        v = pack_elts<G>(e);
+      }
+      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), v);
+    }
+    if (threadIdx.x < 2)
+      fold_ends<G, NTS>(F, F + c.n, threadIdx.x, [&](uint64_t xb) { return elt((uint32_t)(xb - F)); });
+  } else {
+    const uint64_t fa = align_down16(F);
+    const uint32_t nblk = (uint32_t)((align_up16(F + c.n) - fa) >> 4);
+    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock)
+      *reinterpret_cast<u32x4*>(lds + i * 16) = ldv(gptr<u32x4>(fa + (uint64_t)i * 16));
+    __syncthreads();
+    flat_scatter<G, NTS>(c, run, (uint32_t)(F - fa), lds, src);
+  }
+  __syncthreads();  // the next chunk reuses the LDS
+}
+
 // NARROW: every item has a unit of at most FSDP_FOLD_LDS_MAX_UNIT bytes, so
 // the unit-wise path only serves chunks whose windows do not fit the LDS;
 // it then moves one unit per lane per iteration, which keeps this variant's
@@ -1287,6 +1434,13 @@ __global__ __launch_bounds__(kBlock) void fold_copy_kernel(const uint64_t* __res
     const uint64_t c = xcd_chunk(slot, n_chunks);
     const uint32_t j = find_item(begin, n_fold, c);
     const fsdp::FoldSeg f = folds[j];
+    if (f.rows_per_chunk == 0) {  // rows too long for one chunk: flat chunks
+      if (f.unit >= 4)
+        fold_flat<uint32_t, NTS>(f, c - begin[j], lds);
+      else
+        fold_flat<uint16_t, NTS>(f, c - begin[j], lds);
+      continue;
+    }
     const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
     const uint64_t left = f.rows - r0;
     const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);
@@ -1556,12 +1710,56 @@ __device__ __forceinline__ void fold_reduce_lds(const fsdp::FoldRed& f, const ui
   __syncthreads();  // the next chunk reuses the LDS
 }
 
+// Flat chunks of a fold-reduce item (rows_per_chunk == 0, as in fold_flat):
+// the operands' aligned blocks over full-tensor bytes [X0, X1) (every
+// operand at the same address modulo 16, which the planner checks) are
+// reduced block by block into LDS (the reduce kernel's arithmetic and
+// order), then every piece's part is written as in fold_flat's scatter.
+template <int E, int K, typename G, bool NTS>
+__device__ __forceinline__ void fold_reduce_flat(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
+                                                 uint64_t k, int avg, uint8_t* lds) {
+  const uint32_t S = f.nrank, run = (uint32_t)f.run_bytes;
+  const FlatChunk c = flat_chunk(k, f.rows * S * run, (uint32_t)f.reserved[0], run);
+  const uint64_t F0 = ptr[f.src0] + c.X0;
+  const uint64_t fa = align_down16(F0);
+  const uint32_t nblk = (uint32_t)((align_up16(F0 + c.n) - fa) >> 4);
+  const float nf = (float)S;
+  if constexpr (K > 0) {
+    uint64_t sb[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) sb[t] = align_down16(ptr[f.src0 + t] + c.X0);
+    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
+      u32x4 v[K];
+#pragma unroll
+      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t] + (uint64_t)i * 16));
+      Acc<E> acc = widen<E>(v[0]);
+#pragma unroll
+      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
+      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
+      Acc<E> acc = widen<E>(ldv(gptr<u32x4>(align_down16(ptr[f.src0] + c.X0) + (uint64_t)i * 16)));
+      for (uint32_t t = 1; t < S; ++t)
+        accumulate<E>(acc, ldv(gptr<u32x4>(align_down16(ptr[f.src0 + t] + c.X0) + (uint64_t)i * 16)));
+      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
+    }
+  }
+  __syncthreads();
+  flat_scatter<G, NTS>(c, run, (uint32_t)(F0 - fa), lds, [&](uint64_t p, uint32_t a) {
+    const uint64_t r = p / S;
+    const uint32_t s = (uint32_t)(p - r * S);
+    return ptr[f.dst0 + s] + r * run + (c.X0 + a - p * run);
+  });
+  __syncthreads();  // the next chunk reuses the LDS
+}
+
 // NARROW: every item has a unit of at most FSDP_FOLD_LDS_MAX_UNIT bytes; a
 // chunk that cannot be staged (operands at different offsets modulo 16, or
 // too large for the LDS) takes the runtime-count unit loop, which keeps
 // this variant's registers those of the LDS path.
 template <int E, int K, bool NTS, bool NARROW>
-__global__ __launch_bounds__(kBlock) void fold_reduce_kernel(const uint64_t* __restrict__ begin,
+__global__ __launch_bounds__(kBlock, 4) void fold_reduce_kernel(const uint64_t* __restrict__ begin,
                                                              const fsdp::FoldRed* __restrict__ items,
                                                              const uint64_t* __restrict__ ptr, uint32_t n_item,
                                                              uint64_t n_chunks, int avg) {
@@ -1570,6 +1768,13 @@ __global__ __launch_bounds__(kBlock) void fold_reduce_kernel(const uint64_t* __r
     const uint64_t c = xcd_chunk(slot, n_chunks);
     const uint32_t j = find_item(begin, n_item, c);
     const fsdp::FoldRed f = items[j];
+    if (f.rows_per_chunk == 0) {  // rows too long for one chunk: flat chunks
+      if (f.unit >= 4)
+        fold_reduce_flat<E, K, uint32_t, NTS>(f, ptr, c - begin[j], avg, lds);
+      else if constexpr (E != kF32)
+        fold_reduce_flat<E, K, uint16_t, NTS>(f, ptr, c - begin[j], avg, lds);
+      continue;
+    }
     const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
     const uint64_t left = f.rows - r0;
     const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);

@@ -77,6 +77,11 @@ struct RedJob {
 // chunk size), so one workgroup reads and writes whole lines on both sides.
 // unit (16, 8, 4 or 2) is the access width; it divides run_bytes, full,
 // rank0 and rank_pitch.
+//
+// rows_per_chunk == 0 marks rows too long for one chunk: the contiguous
+// full tensor is cut into flat chunks of `reserved` bytes (a multiple of
+// 16), chunk k being its bytes [k * reserved, (k + 1) * reserved), whatever
+// rows they cross; such chunks are staged through LDS.
 struct FoldSeg {
   uint64_t full;
   uint64_t run_bytes;
@@ -99,6 +104,9 @@ struct FoldSeg {
 // ptr[dst0 + s].  A chunk is rows_per_chunk whole full-tensor rows (at most
 // the chunk size of destination bytes).  unit (16, 8, 4 or 2, at least the
 // element size) is the access width; it divides run_bytes and every pointer.
+// rows_per_chunk == 0 marks flat chunks of reserved[0] bytes of the full
+// tensor, as for FoldSeg; every operand then sits at the same address
+// modulo 16.
 struct FoldRed {
   uint64_t run_bytes;
   uint64_t rows;

@@ -353,6 +353,9 @@ int main(int argc, char** argv) {
       {{{64, 6}, {33, 12, 3}, {9, 20}, {1000, 6}, {3, 2050, 1}, {5, 8, 3}, {2, 1030, 4}, {7, 4, 5}},
        {1, 1, 1, 1, 1, 1, 1, 1}},
       {{{33, 4, 3}, {9, 12}, {7, 4, 5}, {100, 12}, {5}}, {1, 1, 1, 1, 0}},
+      // rows too long for one chunk at per-row alignments (flat chunks)
+      {{{3, 4098}, {9, 8}}, {1, 0}},
+      {{{5, 8248}, {7, 16}}, {1, 1}},
       {{}, {}},
   };
   for (size_t ci = 0; ci < cases.size(); ++ci) {

@@ -667,11 +667,28 @@ def test_narrow_fold_paths_all_steps(S, R, dtype, aligned):
     ([(2000000, 6)], 2, 4, torch.float32),  # 4-byte pieces: LDS-staged folds, ~1500 copy chunks
     ([(20000, 2050, 1)], 2, 2, torch.bfloat16),  # 2050-byte rows at every alignment: folded long rows
     ([(300000, 12), (5000, 1028, 4)], 4, 8, torch.float16),  # 6-byte pieces; 2056-byte rows (8 mod 16)
+    ([(10000, 4098)], 2, 2, torch.float32),  # 8196-byte pieces: a full row spans two flat chunks
+    ([(3000, 8248)], 8, 8, torch.bfloat16),  # 2062-byte pieces over 8 ranks: flat chunks
 ])
 def test_fold_paths_at_scale(shapes, S, R, dtype):
     """The fold kernels over thousands of chunks (tens of MB per rank), every
     step against the oracle bit for bit."""
     run_nonzero_dims(shapes, [1] * len(shapes), S, R, dtype, True)
+
+
+@pytest.mark.parametrize("shapes,S,R,dtype", [
+    ([(7, 4098), (9, 8)], 2, 4, torch.float32),
+    ([(5, 8248), (3, 16390)], 2, 2, torch.float16),
+    ([(6, 8248)], 4, 8, torch.bfloat16),
+    ([(4, 8248), (5, 2056)], 8, 8, torch.float32),
+])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_long_rows_in_flat_chunks(shapes, S, R, dtype, aligned):
+    """Dim-1 chunk rows too long for the S pieces of a full row to fit one
+    chunk, at per-row alignments: the full tensor is cut into flat chunks
+    (fold and fold-reduce items staged through LDS); every step against the
+    oracle, buffers at every element offset or at multiples of 16 bytes."""
+    run_nonzero_dims(shapes, [1] * len(shapes), S, R, dtype, aligned)
 
 
 def run_nonzero_dims(shapes, dims, S, R, dtype, aligned):

@@ -118,6 +118,8 @@ def test_planner_tables_pass_the_kernel_emulation(driver, tmp_path, tuning):
     assert counts[0] > 100 and counts[1] > 100 and counts["blocks"] > (50 if tuning == "default" else 0), counts
     assert counts[3] > (10 if tuning != "chunks_512B" else 0), counts
     assert counts[4] > (10 if tuning != "chunks_512B" else 0), counts
+    # long rows at per-row alignments: fold and fold-reduce items of flat chunks
+    assert tuning != "default" or counts["flat_chunks"] > 10, counts
 
 
 def test_random_bucket_tables_pass_the_kernel_emulation(driver, tmp_path):
@@ -142,7 +144,7 @@ def _check_tables(dump):
     tables between two span records), the writes of all its tables together
     cover exactly the call's outputs, each byte once, and every read lies in
     the aligned envelope of the call's inputs."""
-    counts = {0: 0, 1: 0, 3: 0, 4: 0, "blocks": 0}
+    counts = {0: 0, 1: 0, 3: 0, 4: 0, "blocks": 0, "flat_chunks": 0}
     state = {"outs": None, "ins": None, "w": [], "tables": 0}
 
     def finish():
@@ -178,6 +180,7 @@ def _check_tables(dump):
             raw = blob[8 * n:8 * n + 64 * n]
             assert len(blob) == 8 * n + 64 * n
             folds = [struct.unpack_from(KI.FOLD_FMT, raw, 64 * k) for k in range(n)]
+            counts["flat_chunks"] += sum(f[3] == 0 for f in folds)
             fbegin, c, writes, reads = KI.emulate_fold(folds, 1 << shift)
             assert begin == fbegin and c == n_chunks
             w_iv = [(w[0], w[1]) for w in writes]
@@ -187,6 +190,7 @@ def _check_tables(dump):
         elif kind == 4:
             raw = blob[8 * n:8 * n + 64 * n]
             items = [struct.unpack_from(KI.FOLD_RED_FMT, raw, 64 * k) for k in range(n)]
+            counts["flat_chunks"] += sum(f[2] == 0 for f in items)
             ptr = [int(v) for v in np.frombuffer(blob[8 * n + 64 * n:], dtype=np.uint64)]
             fbegin, c, writes, reads = KI.emulate_fold_reduce(items, ptr, 1 << shift)
             assert begin == fbegin and c == n_chunks

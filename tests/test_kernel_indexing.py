@@ -1151,6 +1151,118 @@ def fold_units_chunk(f, r0, nr, io):
         io.store(dst, io.load(src, W))
 
 
+FLAT_CHUNK = 12288     # kFlatChunk: full-tensor bytes of a flat chunk
+FLAT_MIN_RUN = 1024     # kFlatMinRun
+FLAT_ADJ = 256          # kFlatAdj: LDS bytes kept for the pieces' offsets
+
+
+def fold_item_chunks(rows, per, full_row, sub):
+    """Chunks of a fold or fold-reduce item (fold_item_chunks)."""
+    return -(-(rows * full_row) // sub) if per == 0 else -(-rows // per)
+
+
+def flat_chunk(k, total, sub, run):
+    """A flat chunk (flat_chunk): first byte, length, first piece, and the
+    parts (piece, a, b) it meets, a and b chunk-relative."""
+    X0 = k * sub
+    n = min(total - X0, sub)
+    p_lo = X0 // run
+    off0 = X0 - p_lo * run
+    pieces = (off0 + n - 1) // run + 1
+    parts = []
+    for q in range(pieces):
+        lo, hi = q * run, (q + 1) * run
+        parts.append((p_lo + q, max(lo, off0) - off0, min(hi, off0 + n) - off0))
+    return X0, n, p_lo, off0, parts
+
+
+def _flat_scatter(parts, delta, lds, g, dst, io, writes=None, j=None):
+    """flat_scatter: every part written from LDS (chunk byte x at delta + x)."""
+    for p, a, b in parts:
+        d = dst(p, a)
+
+        def src(y, a=a, d=d):
+            o = delta + a + (y - d)
+            assert 0 <= o and o + g <= len(lds)
+            return bytes(lds[o:o + g])
+
+        for v in range((d + 15) & ~15, (d + b - a) & ~15, 16):
+            # the kernel reads the vector's 16 LDS bytes as four or five dwords
+            assert ((delta + a + (v - d)) & ~3) + 20 <= FOLD_LDS
+            io.store(v, b"".join(src(v + k) for k in range(0, 16, g)))
+            if writes is not None:
+                writes.append((v, v + 16, j, None))
+        for lo, hi in _ends(d, d + b - a):
+            for y in range(lo, hi, g):
+                io.store(y, src(y))
+                if writes is not None:
+                    writes.append((y, y + g, j, None))
+
+
+def fold_sub_chunk(f, k, io):
+    """One flat chunk of fold_copy_kernel (fold_flat)."""
+    full, run, rows, per, rank0, pitch, S, W, gather, sub = f
+    assert per == 0 and sub % 16 == 0 and sub % W == 0
+    g = 4 if W >= 4 else 2
+    X0, n, p_lo, off0, parts = flat_chunk(k, rows * S * run, sub, run)
+    assert n > 0 and 4 * len(parts) <= FLAT_ADJ
+    F = full + X0
+
+    def src_addr(p, a):
+        r, s_ = divmod(p, S)
+        return rank0 + s_ * pitch + r * run + (X0 + a - p * run)
+
+    if gather:
+        lds = bytearray(FOLD_LDS)
+        w, adj, win = 0, {}, {}
+        for q, (p, a, b) in enumerate(parts):
+            ad = src_addr(p, a)
+            lo, hi = ad & ~15, (ad + (b - a) + 15) & ~15
+            adj[q] = w + (ad & 15) - a
+            win[q] = (w, w + hi - lo)
+            for blk in range(lo, hi, 16):
+                assert w + 16 <= FOLD_LDS - FLAT_ADJ
+                lds[w:w + 16] = io.load(blk, 16)
+                w += 16
+
+        def rd(x):
+            q = (x + off0) // run
+            o = adj[q] + x
+            assert win[q][0] <= o and o + g <= win[q][1]  # inside piece q's window
+            return bytes(lds[o:o + g])
+
+        for v in range((F + 15) & ~15, (F + n) & ~15, 16):
+            x = v - F
+            q = (x + off0) // run
+            if x + off0 + 16 <= (q + 1) * run:  # one piece: four or five dwords from LDS
+                assert ((adj[q] + x) & ~3) + 20 <= FOLD_LDS - FLAT_ADJ + 4
+            io.store(v, b"".join(rd(x + i) for i in range(0, 16, g)))
+        for lo, hi in _ends(F, F + n):
+            for xa in range(lo, hi, g):
+                io.store(xa, rd(xa - F))
+    else:
+        fa = F & ~15
+        nblk = (((F + n + 15) & ~15) - fa) // 16
+        assert nblk * 16 <= FOLD_LDS
+        lds = bytearray(nblk * 16)
+        for i in range(nblk):
+            lds[16 * i:16 * i + 16] = io.load(fa + 16 * i, 16)
+        _flat_scatter(parts, F - fa, lds, g, src_addr, io)
+
+
+def flat_fold_item(full, rank0, pitch, S, run, rows, es, gather, shift=14):
+    """A flat-chunk fold item as the planner builds it (push_fold, rows too
+    long for one chunk); None where the planner makes none."""
+    CH = 1 << shift
+    if not (S >= 2 and rows >= 2 and S * run > CH and run >= FLAT_MIN_RUN and run % 8):
+        return None
+    m = full | run | rank0 | pitch
+    W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
+    if W < es:
+        return None
+    return (full, run, rows, 0, rank0, pitch, S, W, int(gather), FLAT_CHUNK)
+
+
 def emulate_fold(folds, CH, io=None, lds=True):
     """fold_copy_kernel over a fold table: returns the chunk prefix, the
     chunk count and the reads and writes as (lo, hi, item).  Chunk k of item
@@ -1160,12 +1272,16 @@ def emulate_fold(folds, CH, io=None, lds=True):
     begin, n = [], 0
     for f in folds:
         begin.append(n)
-        n += -(-f[2] // f[3])
+        n += fold_item_chunks(f[2], f[3], f[6] * f[1], f[9])
     for c in range(n):
         j = find_item(begin, len(folds), c)
         f = folds[j]
         full, run, rows, per, rank0, pitch, S, W = f[:8]
         assert W in (2, 4, 8, 16) and (full | run | rank0 | pitch) % W == 0
+        if per == 0:  # flat chunks
+            io.item = j
+            fold_sub_chunk(f, c - begin[j], io)
+            continue
         assert per * S * run <= CH and per >= 1
         r0 = (c - begin[j]) * per
         nr = min(per, rows - r0)
@@ -1283,12 +1399,34 @@ def emulate_fold_reduce(items, ptr, CH, io=None, lds=True, dtype=np.float32):
     begin, n = [], 0
     for f in items:
         begin.append(n)
-        n += -(-f[1] // f[2])
+        n += fold_item_chunks(f[1], f[2], f[5] * f[0], f[7])
     writes = []
     for c in range(n):
         j = find_item(begin, len(items), c)
         f = items[j]
         run, rows, per, src0, dst0, S, W = f[:7]
+        if per == 0:  # flat chunks (fold_reduce_flat)
+            io.item = j
+            sub = f[7]
+            assert W in (2, 4, 8, 16) and run % W == 0 and sub % 16 == 0
+            assert all(((ptr[src0 + t] ^ ptr[src0]) & 15) == 0 for t in range(S))
+            g = 4 if W >= 4 else 2
+            X0, nb_, p_lo, off0, parts = flat_chunk(c - begin[j], rows * S * run, sub, run)
+            F0 = ptr[src0] + X0
+            fa = F0 & ~15
+            nblk = (((F0 + nb_ + 15) & ~15) - fa) // 16
+            assert nblk * 16 <= FOLD_LDS
+            lds_mem = bytearray(nblk * 16)
+            for i in range(nblk):
+                blocks = [io.load(((ptr[src0 + t] + X0) & ~15) + 16 * i, 16) for t in range(S)]
+                lds_mem[16 * i:16 * i + 16] = _sum_bytes(blocks, dtype) if io.mem is not None else bytes(16)
+
+            def dst_addr(p, a, X0=X0):
+                r, s_ = divmod(p, S)
+                return ptr[dst0 + s_] + r * run + (X0 + a - p * run)
+
+            _flat_scatter(parts, F0 - fa, lds_mem, g, dst_addr, io, writes, j)
+            continue
         assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= CH
         assert all(ptr[k] % W == 0 for k in range(src0, src0 + S)) and all(ptr[k] % W == 0 for k in range(dst0, dst0 + S))
         r0 = (c - begin[j]) * per
@@ -1473,4 +1611,93 @@ def test_fold_reduce_moves_sums_to_their_place(S, run, dtype, same_offset):
     assert np.array_equal(mem, want)
     env = _merge([(a & ~15, (a + n_el * es + 15) & ~15) for a in src])
     for a, b, _ in io.reads:
+        assert any(x <= a and b <= y for x, y in env), (a, b)
+
+
+# ---------------------------------------------------------------------------
+# flat chunks: dim-k rows too long for one chunk
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("run", [1028, 2052, 4100, 8196, 6150])
+@pytest.mark.parametrize("gather", [True, False])
+def test_flat_chunk_fold_moves_every_byte_to_its_place(S, run, gather):
+    """Fold items of long rows (the S pieces of a full row exceed a chunk)
+    are cut into flat chunks of the full tensor; their byte-level emulation turns the
+    source image into exactly the expected one, writes every byte once and
+    reads only the aligned blocks of the sources."""
+    es = 2 if run % 4 else 4
+    rows = 5
+    rng = np.random.default_rng(S * 7 + run + gather)
+    size = 1 << 21
+    mem = rng.integers(0, 256, size, dtype=np.uint8)
+    full = 4096 + es * int(rng.integers(0, 16))
+    rank0 = (1 << 20) + es * int(rng.integers(0, 16))
+    pitch = rows * run + es * int(rng.integers(0, 40))
+    f = flat_fold_item(full, rank0, pitch, S, run, rows, es, gather)
+    if f is None:
+        assert S * run <= 1 << 14 or run % 8 == 0
+        return
+    before = mem.copy()
+    io = Recorder(mem)
+    emulate_fold([f], 1 << 14, io)
+    want = before.copy()
+    for r in range(rows):
+        for s_ in range(S):
+            fa = full + (r * S + s_) * run
+            ra = rank0 + s_ * pitch + r * run
+            if gather:
+                want[fa:fa + run] = before[ra:ra + run]
+            else:
+                want[ra:ra + run] = before[fa:fa + run]
+    assert np.array_equal(mem, want)
+    w_iv = [(a, b) for a, b, _ in io.writes]
+    assert sum(b - a for a, b in w_iv) == sum(b - a for a, b in _merge(w_iv)) == rows * S * run
+    src = [(full, full + rows * S * run)] if not gather else [(rank0 + s_ * pitch, rank0 + s_ * pitch + rows * run)
+                                                             for s_ in range(S)]
+    env = _merge([(a & ~15, (b + 15) & ~15) for a, b in src])
+    for a, b, _ in io.reads:
+        assert any(x <= a and b <= y for x, y in env), (a, b)
+
+
+@pytest.mark.parametrize("S", [2, 4])
+@pytest.mark.parametrize("run", [4100, 8196])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_flat_chunk_fold_reduce_moves_sums_to_their_place(S, run, dtype):
+    """Fold-reduce items of long rows (flat chunks): every rank's rows get
+    the group's sum of their pieces, every byte once; no other byte changes."""
+    es = np.dtype(dtype).itemsize
+    rows = 4
+    rng = np.random.default_rng(S * 13 + run + es)
+    n_el = rows * S * run // es
+    span = (n_el * es + 64 + 4095) & ~4095
+    mem = rng.integers(0, 256, 4096 + 2 * S * span, dtype=np.uint8)
+    src, dst = [], []
+    for t in range(S):
+        a = 4096 + t * span + 16 * int(rng.integers(0, 4))
+        mem[a:a + n_el * es] = np.frombuffer(rng.integers(-50, 50, n_el).astype(dtype).tobytes(), np.uint8)
+        src.append(a)
+    for s_ in range(S):
+        dst.append(4096 + (S + s_) * span + es * int(rng.integers(0, 16)))
+    m = run
+    for a in src + dst:
+        m |= a
+    W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
+    item = (run, rows, 0, 0, S, S, W, FLAT_CHUNK, 0, 0)
+    ptr = src + dst
+    before = mem.copy()
+    io = Recorder(mem)
+    _, _, writes, reads = emulate_fold_reduce([item], ptr, 1 << 14, io, dtype=dtype)
+    want = before.copy()
+    for r in range(rows):
+        for s_ in range(S):
+            o = (r * S + s_) * run
+            blocks = [bytes(before[a + o:a + o + run]) for a in src]
+            d = dst[s_] + r * run
+            want[d:d + run] = np.frombuffer(_sum_bytes(blocks, dtype), np.uint8)
+    assert np.array_equal(mem, want)
+    w_iv = [(a, b) for a, b, _, _ in writes]
+    assert sum(b - a for a, b in w_iv) == sum(b - a for a, b in _merge(w_iv)) == rows * S * run
+    env = _merge([(a & ~15, (a + n_el * es + 15) & ~15) for a in src])
+    for a, b, _ in reads:
         assert any(x <= a and b <= y for x, y in env), (a, b)
