@@ -625,13 +625,22 @@ __device__ __forceinline__ void reduce_run(const fsdp::RedJob& jb, const uint64_
     for (int t = 0; t < K; ++t)
 #pragma unroll
       for (int u = 0; u < U; ++u) v[t][u] = operand<MODE>(gptr<u32x4>(sb[t]) - e, j + u * kBlock, sr[t]);
+    u32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Acc<E> acc = widen<E>(v[0][u]);
 #pragma unroll
       for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t][u]);
-      const u32x4 o[1] = {narrow<E>(acc, avg, nf)};
-      if (j + u * kBlock >= e) store_vectors<1, NTS>(o, jb, ptr, va, j + u * kBlock - e, kBlock);
+      o[u] = narrow<E>(acc, avg, nf);
+    }
+    if (base >= e) {  // every index of the iteration is a vector: U stores per destination
+      store_vectors<U, NTS>(o, jb, ptr, va, j - e, kBlock);
+    } else {  // the first iteration of a rotated run: the indices before vector 0 are not stored
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u32x4 w[1] = {o[u]};
+        if (j + u * kBlock >= e) store_vectors<1, NTS>(w, jb, ptr, va, j + u * kBlock - e, kBlock);
+      }
     }
   }
   for (uint64_t j = base + threadIdx.x; j < n; j += kBlock) {
