@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_OF_STEP = {"ag_copy_in": "seg_copy_kernel", "ag_copy_out": "seg_copy_kernel",
                   "rs_copy_in": "seg_copy_kernel", "rs_reduce": "reduce_kernel",
                   "rs_copy_reduce": "reduce_kernel", "fused_ar": "reduce_kernel"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "l2_fabric_traffic_{workload}.json")
 # what fixes the kernels' memory traffic: their code, the descriptor formats,
 # the launch tuning (chunk sizes, store policy) and the planner that builds
 # the tables
@@ -105,9 +105,12 @@ def _numel(shape):
 
 
 def measured_traffic(workload: str, step: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 PMC summary, or None when absent or when the kernel source has
-    changed since the counters were taken."""
+    """Bytes per launch of the dominant kernel between L2 and the memory
+    fabric (rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what it reads
+    for a plain copy of known size) from the committed PMC summary, or None
+    when absent or when the kernel source has changed since the counters
+    were taken.  The counters see L2 misses, Infinity Cache hits included:
+    no per-kernel DRAM byte counter exists on this ROCm."""
     try:
         with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
@@ -872,6 +875,8 @@ class Pass:
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(self.w.name, dom),
+                "traffic_note": "L2-to-fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a plain "
+                                "copy); Infinity Cache hits are included, so not DRAM bytes",
                 "algorithmic_bytes_per_launch": self.nbytes[dom], "avg_launch_us": round(res["dom_us"], 2),
                 "timing": "HIP events recorded by the call's own kernel dispatch at its start and end, "
                           "every timed step"}
