@@ -1576,10 +1576,12 @@ __device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const 
       sb[t] = ptr[f.src0 + t] + src_off;
       db[t] = ptr[f.dst0 + t] + dst_off;
     }
+    // a mask, not a select: the compiler turns a chain of selects among the
+    // array's elements into one lane-indexed load, which puts db in scratch
     auto dst_base = [&](uint32_t s) {
       uint64_t d = db[0];
 #pragma unroll
-      for (int t = 1; t < K; ++t) d = s == (uint32_t)t ? db[t] : d;
+      for (int t = 1; t < K; ++t) d ^= (db[t] ^ d) & (0ull - (uint64_t)(s == (uint32_t)t));
       return d;
     };
     for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
