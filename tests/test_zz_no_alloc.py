@@ -78,3 +78,57 @@ def test_noalloc_refuses_oversized_tables_before_enqueueing():
     assert e.value.code == 1 and "scratch" in e.value.message
     torch.cuda.synchronize()
     assert all(bool((o == 7.0).all()) for o in out)
+
+
+def test_noalloc_replayed_from_a_captured_graph():
+    """The entry point inside a HIP graph capture: the captured table writes
+    and kernels are replayed three times, each after new gradients were
+    written and after an eager call of another shape rewrote the scratch
+    array, and every replay equals the cached-plan rs_copy_reduce of the
+    gradients it saw."""
+    require_gpu()
+    hp.lib()
+    name, shapes, dims, R, S = CASES[0]
+    other = CASES[2]
+    P = len(shapes)
+    note(f"[no-alloc] graph capture: {name} R={R} S={S}")
+    w = W.Workload("noalloc_graph", 950, R, S, tuple(shapes), torch.float32, ("uniform", 1.0), ("uniform", 1.0),
+                   ("sum", "avg"), W.ALL_STEPS)
+    grads = W.grads(w, device="cuda")
+    flat = [grads[g][i].reshape(-1) for g in range(R) for i in range(P)]
+    I = hp.fsdp_bucket_layout(shapes, S, shard_dims=dims).I
+    got = [torch.empty(I, device="cuda") for _ in range(R)]
+    want = [torch.empty(I, device="cuda") for _ in range(R)]
+    # eager first: the scratch array's address is looked up outside the capture
+    hp.fsdp_rs_copy_reduce_noalloc(shapes, R, S, R // S, "avg", flat, got, shard_dims=dims)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hp.fsdp_rs_copy_reduce_noalloc(shapes, R, S, R // S, "avg", flat, got, shard_dims=dims)
+    torch.cuda.synchronize()
+    o_name, o_shapes, o_dims, o_R, o_S = other
+    ow = W.Workload("noalloc_graph_other", 951, o_R, o_S, tuple(o_shapes), torch.float32, ("uniform", 1.0),
+                    ("uniform", 1.0), ("sum", "avg"), W.ALL_STEPS)
+    og = W.grads(ow, device="cuda")
+    oflat = [og[g][i].reshape(-1) for g in range(o_R) for i in range(len(o_shapes))]
+    oI = hp.fsdp_bucket_layout(o_shapes, o_S, shard_dims=o_dims).I
+    oout = [torch.empty(oI, device="cuda") for _ in range(o_R)]
+    gen = torch.Generator(device="cuda")
+    for rep in range(3):
+        note(f"[no-alloc] graph replay {rep}")
+        gen.manual_seed(960 + rep)
+        for t in flat:
+            t.copy_(2 * torch.rand(t.shape, device="cuda", generator=gen) - 1)
+        for t in got + want:
+            _poison(t)
+        # another shape's tables overwrite the scratch array before the replay
+        hp.fsdp_rs_copy_reduce_noalloc(o_shapes, o_R, o_S, o_R // o_S, "sum", oflat, oout, shard_dims=o_dims)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        hp.fsdp_rs_copy_reduce(shapes, R, S, R // S, "avg", flat, want, shard_dims=dims)
+        torch.cuda.synchronize()
+        for g in range(R):
+            m = first_mismatch(bits(got[g]), bits(want[g]))
+            assert m == "", f"replay {rep} rank {g}: {m}"
+    del graph
