@@ -567,9 +567,9 @@ bool fold_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH, uint6
 // is cut into flat chunks of kFlatChunk bytes whatever rows they cross
 // (rows_per_chunk 0 in the fold items), staged through LDS so that both
 // sides move aligned vectors.  Pieces of at least kFlatMinRun bytes keep the
-// pieces meeting one chunk few.
-constexpr uint64_t kFlatChunk = 12288;
-constexpr uint64_t kFlatMinRun = 1024;
+// pieces meeting one chunk few (plan.hpp).
+using fsdp::kFlatChunk;
+using fsdp::kFlatMinRun;
 
 bool long_rows(uint64_t row_bytes, uint64_t rows, uint64_t S, uint64_t CH, uint64_t m) {
   return S >= 2 && rows >= 2 && S * row_bytes > CH && row_bytes >= kFlatMinRun && row_bytes % m != 0 &&

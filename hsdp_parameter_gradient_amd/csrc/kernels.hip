@@ -1161,6 +1161,64 @@ __device__ __forceinline__ uint32_t fold_lds_bytes(const fsdp::FoldSeg& f, uint6
   return need <= kFoldLds ? (uint32_t)need : 0u;
 }
 
+// Loads in flight per lane while a chunk is staged through LDS: a loop of
+// one load and one LDS store per block waits a whole memory round trip per
+// block, which caps each workgroup's share of the bandwidth.
+constexpr int kStage = 4;
+
+// Stages blocks [0, n) of a chunk in LDS: block i (16 bytes at the aligned
+// global address src(i), or nothing when src(i) is 0) goes to LDS bytes
+// [16 i, 16 i + 16); each lane issues up to kStage loads before their LDS
+// stores.
+template <typename Src>
+__device__ __forceinline__ void stage_blocks(uint8_t* lds, uint32_t n, Src src) {
+  for (uint32_t i0 = threadIdx.x; i0 < n; i0 += (uint32_t)kStage * kBlock) {
+    u32x4 v[kStage];
+    uint64_t a[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const uint32_t i = i0 + u * kBlock;
+      a[u] = i < n ? src(i) : 0;
+      if (a[u]) v[u] = ldv(gptr<u32x4>(a[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u)
+      if (a[u]) *reinterpret_cast<u32x4*>(lds + 16u * (i0 + u * kBlock)) = v[u];
+  }
+}
+
+// Reduces blocks [0, n) of a chunk into LDS: block i of every operand t
+// (16 bytes at sb[t] + 16 i) summed in operand order, finished (AVG, 16-bit
+// rounding) and stored at LDS bytes [16 i, 16 i + 16); each lane issues the
+// K loads of two blocks (of one for K >= 4) before the first add, which
+// keeps the wide-unit fold reduce under its register cap.
+template <int E, int K>
+__device__ __forceinline__ void reduce_blocks(uint8_t* lds, uint32_t n, const uint64_t (&sb)[K], int avg,
+                                              float nf) {
+  constexpr int B = K >= 4 ? 1 : 2;
+  for (uint32_t i0 = threadIdx.x; i0 < n; i0 += (uint32_t)B * kBlock) {
+    u32x4 v[B][K];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t i = i0 + u * kBlock;
+      if (i < n) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) v[u][t] = ldv(gptr<u32x4>(sb[t] + (uint64_t)i * 16));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t i = i0 + u * kBlock;
+      if (i < n) {
+        Acc<E> acc = widen<E>(v[u][0]);
+#pragma unroll
+        for (int t = 1; t < K; ++t) accumulate<E>(acc, v[u][t]);
+        *reinterpret_cast<u32x4*>(lds + 16u * i) = narrow<E>(acc, avg, nf);
+      }
+    }
+  }
+}
+
 // The element runs [lo, hi) of a destination range not covered by its whole
 // aligned vectors: its head and tail, or all of it when it has no whole
 // vector.  Element x (absolute address) gets get(x).
@@ -1205,12 +1263,12 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     // window s: the aligned blocks of rank s's L bytes, rank byte y at
     // s * nb * 16 + (rank base & 15) + y
     const uint32_t nb = (L + 15) / 16 + 1;
-    for (uint32_t i = threadIdx.x; i < S * nb; i += kBlock) {
+    stage_blocks(lds, S * nb, [&](uint32_t i) -> uint64_t {
       const uint32_t s = i / nb, k = i - s * nb;
       const uint64_t a = R0 + s * f.rank_pitch;
       const uint64_t blk = align_down16(a) + (uint64_t)k * 16;
-      if (blk < align_up16(a + L)) *reinterpret_cast<u32x4*>(lds + i * 16) = ldv(gptr<u32x4>(blk));
-    }
+      return blk < align_up16(a + L) ? blk : 0;
+    });
     __syncthreads();
     // full-side byte x of the chunk: row x / FR, rank (x % FR) / run, column x % run
     auto at = [&](uint32_t row, uint32_t s, uint32_t col) {
@@ -1248,8 +1306,7 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     const uint64_t fa = align_down16(F0);
     const uint32_t delta = (uint32_t)(F0 - fa);
     const uint32_t nblk = (uint32_t)((align_up16(F0 + (uint64_t)nr * FR) - fa) >> 4);
-    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock)
-      *reinterpret_cast<u32x4*>(lds + i * 16) = ldv(gptr<u32x4>(fa + (uint64_t)i * 16));
+    stage_blocks(lds, nblk, [&](uint32_t i) -> uint64_t { return fa + (uint64_t)i * 16; });
     __syncthreads();
     // rank s's byte y of the chunk: row y / run, column y % run
     auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
@@ -1318,8 +1375,17 @@ __device__ __forceinline__ void flat_part(const FlatChunk& c, uint32_t run, uint
   *b = (hi < c.off0 + c.n ? hi : c.off0 + c.n) - c.off0;
 }
 
-// LDS bytes kept at the end of the fold LDS for the pieces' offsets.
+// LDS bytes kept at the end of the fold LDS for the gather's window table
+// (one FlatWin per piece, at most kFlatWinMax pieces, then one entry whose
+// start is the blocks of all windows).
 constexpr uint32_t kFlatAdj = 256;
+struct FlatWin {
+  uint64_t blk0;   // first aligned global block of the window
+  uint32_t start;  // first LDS block of the window
+  int32_t adj;     // LDS offset of chunk byte 0 in the piece's frame
+};
+constexpr uint32_t kFlatWinMax = kFlatAdj / sizeof(FlatWin) - 1;
+static_assert(fsdp::kFlatMaxPieces <= kFlatWinMax, "a flat chunk's windows must fit the LDS table");
 
 template <typename G>
 __device__ __forceinline__ u32x4 pack_elts(const G (&e)[16 / sizeof(G)]) {
@@ -1381,24 +1447,44 @@ __device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, ui
   };
   if (f.gather) {
     // window of piece q: the aligned blocks of its part, the windows one
-    // after another; adj[q] = LDS offset of chunk byte 0 in piece q's frame
-    int32_t* adj = reinterpret_cast<int32_t*>(lds + kFoldLds - kFlatAdj);
-    uint32_t w = 0;
-    for (uint32_t q = 0; q < c.pieces; ++q) {
+    // after another in LDS.  Lane q < pieces describes window q in the
+    // table at the end of the LDS: its first global block, its first LDS
+    // block, and adj = the LDS offset of chunk byte 0 in piece q's frame.
+    FlatWin* win = reinterpret_cast<FlatWin*>(lds + kFoldLds - kFlatAdj);
+    auto window = [&](uint32_t q, uint64_t* blk0, uint32_t* a) {
+      uint32_t b;
+      flat_part(c, run, q, a, &b);
+      const uint64_t p = src(c.p_lo + q, *a);
+      *blk0 = align_down16(p);
+      return p;
+    };
+    auto blocks = [&](uint32_t q) {
+      uint64_t blk0;
       uint32_t a, b;
+      const uint64_t p = window(q, &blk0, &a);
       flat_part(c, run, q, &a, &b);
-      const uint64_t p = src(c.p_lo + q, a);
-      const uint64_t blk0 = align_down16(p);
-      const uint32_t nb = (uint32_t)((align_up16(p + (b - a)) - blk0) >> 4);
-      if (threadIdx.x == 0) adj[q] = (int32_t)(w + (uint32_t)(p & 15u)) - (int32_t)a;
-      for (uint32_t j = threadIdx.x; j < nb; j += kBlock)
-        *reinterpret_cast<u32x4*>(lds + w + j * 16) = ldv(gptr<u32x4>(blk0 + (uint64_t)j * 16));
-      w += nb * 16;
+      return (uint32_t)((align_up16(p + (b - a)) - blk0) >> 4);
+    };
+    if (threadIdx.x < c.pieces) {
+      const uint32_t q = threadIdx.x;
+      uint32_t start = 0;
+      for (uint32_t k = 0; k < q; ++k) start += blocks(k);
+      uint64_t blk0;
+      uint32_t a;
+      const uint64_t p = window(q, &blk0, &a);
+      win[q] = FlatWin{blk0, start, (int32_t)(start * 16 + (uint32_t)(p & 15u)) - (int32_t)a};
+      if (q + 1 == c.pieces) win[kFlatWinMax].start = start + blocks(q);  // the blocks of all windows
     }
+    __syncthreads();
+    stage_blocks(lds, win[kFlatWinMax].start, [&](uint32_t i) -> uint64_t {
+      uint32_t q = 0;
+      while (q + 1 < c.pieces && win[q + 1].start <= i) ++q;
+      return win[q].blk0 + (uint64_t)(i - win[q].start) * 16;
+    });
     __syncthreads();
     auto elt = [&](uint32_t x) {  // chunk-relative byte x
       const uint32_t q = (x + c.off0) / run;
-      return *reinterpret_cast<const G*>(lds + (adj[q] + (int32_t)x));
+      return *reinterpret_cast<const G*>(lds + (win[q].adj + (int32_t)x));
     };
     const uint64_t va = align_up16(F), vb = align_down16(F + c.n);
     const uint32_t nv = va < vb ? (uint32_t)((vb - va) >> 4) : 0u;
@@ -1408,7 +1494,7 @@ __device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, ui
       const uint32_t q = (x + c.off0) / run;
       u32x4 v;
       if (x + c.off0 + 16 <= (q + 1) * run) {  // inside one piece: 16 consecutive LDS bytes
-        v = lds_vec(lds, (uint32_t)(adj[q] + (int32_t)x));
+        v = lds_vec(lds, (uint32_t)(win[q].adj + (int32_t)x));
       } else {
         G e[NE];
 #pragma unroll
@@ -1422,8 +1508,7 @@ __device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, ui
   } else {
     const uint64_t fa = align_down16(F);
     const uint32_t nblk = (uint32_t)((align_up16(F + c.n) - fa) >> 4);
-    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock)
-      *reinterpret_cast<u32x4*>(lds + i * 16) = ldv(gptr<u32x4>(fa + (uint64_t)i * 16));
+    stage_blocks(lds, nblk, [&](uint32_t i) -> uint64_t { return fa + (uint64_t)i * 16; });
     __syncthreads();
     flat_scatter<G, NTS>(c, run, (uint32_t)(F - fa), lds, src);
   }
@@ -1672,15 +1757,7 @@ __device__ __forceinline__ void fold_reduce_lds(const fsdp::FoldRed& f, const ui
     uint64_t sb[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) sb[t] = align_down16(ptr[f.src0 + t] + off);
-    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
-      u32x4 v[K];
-#pragma unroll
-      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t] + (uint64_t)i * 16));
-      Acc<E> acc = widen<E>(v[0]);
-#pragma unroll
-      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
-      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
-    }
+    reduce_blocks<E, K>(lds, nblk, sb, avg, nf);
   } else {
     for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
       Acc<E> acc = widen<E>(ldv(gptr<u32x4>(align_down16(ptr[f.src0] + off) + (uint64_t)i * 16)));
@@ -1739,15 +1816,7 @@ __device__ __forceinline__ void fold_reduce_flat(const fsdp::FoldRed& f, const u
     uint64_t sb[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) sb[t] = align_down16(ptr[f.src0 + t] + c.X0);
-    for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
-      u32x4 v[K];
-#pragma unroll
-      for (int t = 0; t < K; ++t) v[t] = ldv(gptr<u32x4>(sb[t] + (uint64_t)i * 16));
-      Acc<E> acc = widen<E>(v[0]);
-#pragma unroll
-      for (int t = 1; t < K; ++t) accumulate<E>(acc, v[t]);
-      *reinterpret_cast<u32x4*>(lds + i * 16) = narrow<E>(acc, avg, nf);
-    }
+    reduce_blocks<E, K>(lds, nblk, sb, avg, nf);
   } else {
     for (uint32_t i = threadIdx.x; i < nblk; i += kBlock) {
       Acc<E> acc = widen<E>(ldv(gptr<u32x4>(align_down16(ptr[f.src0] + c.X0) + (uint64_t)i * 16)));

@@ -79,9 +79,15 @@ struct RedJob {
 // rank0 and rank_pitch.
 //
 // rows_per_chunk == 0 marks rows too long for one chunk: the contiguous
-// full tensor is cut into flat chunks of `reserved` bytes (a multiple of
-// 16), chunk k being its bytes [k * reserved, (k + 1) * reserved), whatever
-// rows they cross; such chunks are staged through LDS.
+// full tensor is cut into flat chunks of `reserved` bytes (kFlatChunk),
+// chunk k being its bytes [k * reserved, (k + 1) * reserved), whatever
+// rows they cross; such chunks are staged through LDS.  The planner emits
+// them only for rank rows of at least kFlatMinRun bytes, so a flat chunk
+// meets at most kFlatMaxPieces rank rows.
+constexpr uint64_t kFlatChunk = 12288;
+constexpr uint64_t kFlatMinRun = 1024;
+constexpr uint32_t kFlatMaxPieces = (uint32_t)(kFlatChunk / kFlatMinRun + 2);
+
 struct FoldSeg {
   uint64_t full;
   uint64_t run_bytes;
