@@ -1242,6 +1242,19 @@ __device__ __forceinline__ void fold_ends(uint64_t lo, uint64_t hi, uint32_t lan
   }
 }
 
+__device__ __forceinline__ u32x4 lds_vec(const uint8_t* lds, uint32_t o);
+
+// Bytes [0, k) of a and [k, 16) of b (0 < k < 16): a destination vector
+// that spans the end of one run and the start of the next.
+__device__ __forceinline__ u32x4 merge_bytes(u32x4 a, u32x4 b, uint32_t k) {
+  auto m = [k](int d) {
+    const int r = (int)k - 4 * d;
+    return r <= 0 ? 0u : r >= 4 ? ~0u : (1u << (8 * r)) - 1u;
+  };
+  return u32x4{(a.x & m(0)) | (b.x & ~m(0)), (a.y & m(1)) | (b.y & ~m(1)), (a.z & m(2)) | (b.z & ~m(2)),
+               (a.w & m(3)) | (b.w & ~m(3))};
+}
+
 template <typename G, bool NTS>
 __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, uint32_t nr, uint8_t* lds) {
   constexpr uint32_t gb = sizeof(G);
@@ -1277,11 +1290,8 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     const uint64_t va = align_up16(F0), vb = align_down16(F0 + (uint64_t)nr * FR);
     const uint32_t nv = va < vb ? (uint32_t)((vb - va) >> 4) : 0u;
     const uint32_t x0 = (uint32_t)(va - F0);
-    for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
-      const uint32_t x = x0 + j * 16;
-      uint32_t row = x / FR;
-      const uint32_t rem = x - row * FR;
-      uint32_t s = rem / run, col = rem - s * run;
+    const uint32_t staged = S * nb * 16;
+    auto elements = [&](uint32_t row, uint32_t s, uint32_t col) {
       G e[NE];
 #pragma unroll
       for (uint32_t k = 0; k < NE; ++k) {
@@ -1292,7 +1302,36 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
           if (++s == S) s = 0, ++row;
         }
       }
-      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), pack(e));
+      return pack(e);
+    };
+    if (run >= 16) {
+      for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
+        const uint32_t x = x0 + j * 16;
+        const uint32_t row = x / FR;
+        const uint32_t rem = x - row * FR;
+        const uint32_t s = rem / run, col = rem - s * run;
+        // the vector's bytes in rank s's row from col on, then (k1 < 16)
+        // in the next piece of the full row (rank s + 1, or rank 0 of the
+        // next row): one or two unaligned LDS reads
+        const uint32_t k1 = run - col, o = at(row, s, col);
+        const uint32_t o2 = k1 < 16 ? (s + 1 == S ? at(row + 1, 0, 0) : at(row, s + 1, 0)) - k1 : 0u;
+        u32x4 v;
+        if (k1 >= 16 && o + 20 <= staged)
+          v = lds_vec(lds, o);
+        else if (o + 20 <= staged && o2 + 20 <= staged)
+          v = merge_bytes(lds_vec(lds, o), lds_vec(lds, o2), k1);
+        else
+          v = elements(row, s, col);
+        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), v);
+      }
+    } else {
+      for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
+        const uint32_t x = x0 + j * 16;
+        const uint32_t row = x / FR;
+        const uint32_t rem = x - row * FR;
+        const uint32_t s = rem / run;
+        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(row, s, rem - s * run));
+      }
     }
     if (threadIdx.x < 2) {
       fold_ends<G, NTS>(F0, F0 + (uint64_t)nr * FR, threadIdx.x, [&](uint64_t xa) {
@@ -1310,14 +1349,7 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     __syncthreads();
     // rank s's byte y of the chunk: row y / run, column y % run
     auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
-    const uint32_t vmax = L / 16;  // whole vectors of one rank's L bytes, at most
-    for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-      const uint32_t s = i / vmax, j = i - s * vmax;
-      const uint64_t d = R0 + s * f.rank_pitch;
-      const uint64_t va = align_up16(d), vb = align_down16(d + L);
-      if (va + (uint64_t)j * 16 >= vb) continue;
-      const uint32_t y = (uint32_t)(va - d) + j * 16;
-      uint32_t row = y / run, col = y - row * run;
+    auto elements = [&](uint32_t s, uint32_t row, uint32_t col) {
       G e[NE];
 #pragma unroll
       for (uint32_t k = 0; k < NE; ++k) {
@@ -1325,7 +1357,40 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
         col += gb;
         if (col == run) col = 0, ++row;
       }
-      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), pack(e));
+      return pack(e);
+    };
+    const uint32_t vmax = L / 16;  // whole vectors of one rank's L bytes, at most
+    if (run >= 16) {
+      for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
+        const uint32_t s = i / vmax, j = i - s * vmax;
+        const uint64_t d = R0 + s * f.rank_pitch;
+        const uint64_t va = align_up16(d), vb = align_down16(d + L);
+        if (va + (uint64_t)j * 16 >= vb) continue;
+        const uint32_t y = (uint32_t)(va - d) + j * 16;
+        const uint32_t row = y / run, col = y - row * run;
+        // rank s's bytes from col of row on, then (k1 < 16) from the start
+        // of its next row: one or two unaligned LDS reads
+        const uint32_t k1 = run - col, o = at(row, s, col);
+        const uint32_t o2 = k1 < 16 ? at(row + 1, s, 0) - k1 : 0u;
+        u32x4 v;
+        if (k1 >= 16 && o + 20 <= nblk * 16)
+          v = lds_vec(lds, o);
+        else if (o + 20 <= nblk * 16 && o2 + 20 <= nblk * 16)
+          v = merge_bytes(lds_vec(lds, o), lds_vec(lds, o2), k1);
+        else
+          v = elements(s, row, col);
+        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), v);
+      }
+    } else {
+      for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
+        const uint32_t s = i / vmax, j = i - s * vmax;
+        const uint64_t d = R0 + s * f.rank_pitch;
+        const uint64_t va = align_up16(d), vb = align_down16(d + L);
+        if (va + (uint64_t)j * 16 >= vb) continue;
+        const uint32_t y = (uint32_t)(va - d) + j * 16;
+        const uint32_t row = y / run;
+        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(s, row, y - row * run));
+      }
     }
     for (uint32_t t = threadIdx.x; t < 2 * S; t += kBlock) {
       const uint32_t s = t >> 1;
@@ -1520,7 +1585,7 @@ __device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, ui
 // it then moves one unit per lane per iteration, which keeps this variant's
 // registers (and so its occupancy) those of the LDS path.
 template <bool NTS, bool NARROW>
-__global__ __launch_bounds__(kBlock) void fold_copy_kernel(const uint64_t* __restrict__ begin,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NARROW ? 8 : 1))) void fold_copy_kernel(const uint64_t* __restrict__ begin,
                                                            const fsdp::FoldSeg* __restrict__ folds, uint32_t n_fold,
                                                            uint64_t n_chunks) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFoldLds];
