@@ -1243,6 +1243,8 @@ __device__ __forceinline__ void fold_ends(uint64_t lo, uint64_t hi, uint32_t lan
 }
 
 __device__ __forceinline__ u32x4 lds_vec(const uint8_t* lds, uint32_t o);
+template <typename G>
+__device__ __forceinline__ u32x4 pack_elts(const G (&e)[16 / sizeof(G)]);
 
 // Bytes [0, k) of a and [k, 16) of b (0 < k < 16): a destination vector
 // that spans the end of one run and the start of the next.
@@ -1253,6 +1255,77 @@ __device__ __forceinline__ u32x4 merge_bytes(u32x4 a, u32x4 b, uint32_t k) {
   };
   return u32x4{(a.x & m(0)) | (b.x & ~m(0)), (a.y & m(1)) | (b.y & ~m(1)), (a.z & m(2)) | (b.z & ~m(2)),
                (a.w & m(3)) | (b.w & ~m(3))};
+}
+
+// Scatter of an LDS-staged chunk of nr full rows (S runs of run bytes each,
+// full-side byte x at LDS byte delta + x, nblk blocks staged): rank s's L =
+// nr * run bytes go to dst(s) in aligned 16-byte vectors and element-wise
+// ends.  With 2-byte elements and runs of at least 16 bytes a vector is one
+// unaligned LDS read (inside a run) or two merged ones (across the end of a
+// row), else it is assembled element by element (4-byte elements take as
+// many LDS reads either way, and measured faster element by element); the
+// choice is per chunk, so each loop keeps its own schedule.
+template <typename G, bool NTS, typename Dst>
+__device__ __forceinline__ void scatter_rows(const uint8_t* lds, uint32_t delta, uint32_t nblk, uint32_t S,
+                                             uint32_t run, uint32_t nr, Dst dst) {
+  constexpr uint32_t gb = sizeof(G);
+  constexpr uint32_t NE = 16 / gb;
+  const uint32_t FR = S * run, L = nr * run;
+  auto rd = [&](uint32_t off) { return *reinterpret_cast<const G*>(lds + off); };
+  // rank s's byte y of the chunk: row y / run, column y % run
+  auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
+  auto elements = [&](uint32_t s, uint32_t row, uint32_t col) {
+    G e[NE];
+#pragma unroll
+    for (uint32_t k = 0; k < NE; ++k) {
+      e[k] = rd(at(row, s, col));
+      col += gb;
+      if (col == run) col = 0, ++row;
+    }
+    return pack_elts<G>(e);
+  };
+  const uint32_t vmax = L / 16;  // whole vectors of one rank's L bytes, at most
+  if (gb == 2 && run >= 16) {
+    for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
+      const uint32_t s = i / vmax, j = i - s * vmax;
+      const uint64_t d = dst(s);
+      const uint64_t va = align_up16(d), vb = align_down16(d + L);
+      if (va + (uint64_t)j * 16 >= vb) continue;
+      const uint32_t y = (uint32_t)(va - d) + j * 16;
+      const uint32_t row = y / run, col = y - row * run;
+      // rank s's bytes from col of row on, then (k1 < 16) from the start of
+      // its next row
+      const uint32_t k1 = run - col, o = at(row, s, col);
+      const uint32_t o2 = k1 < 16 ? at(row + 1, s, 0) - k1 : 0u;
+      u32x4 v;
+      if (k1 >= 16 && o + 20 <= nblk * 16)
+        v = lds_vec(lds, o);
+      else if (o + 20 <= nblk * 16 && o2 + 20 <= nblk * 16)
+        v = merge_bytes(lds_vec(lds, o), lds_vec(lds, o2), k1);
+      else
+        v = elements(s, row, col);
+      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), v);
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
+      const uint32_t s = i / vmax, j = i - s * vmax;
+      const uint64_t d = dst(s);
+      const uint64_t va = align_up16(d), vb = align_down16(d + L);
+      if (va + (uint64_t)j * 16 >= vb) continue;
+      const uint32_t y = (uint32_t)(va - d) + j * 16;
+      const uint32_t row = y / run;
+      stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(s, row, y - row * run));
+    }
+  }
+  for (uint32_t t = threadIdx.x; t < 2 * S; t += kBlock) {
+    const uint32_t s = t >> 1;
+    const uint64_t d = dst(s);
+    fold_ends<G, NTS>(d, d + L, t & 1u, [&](uint64_t ya) {
+      const uint32_t y = (uint32_t)(ya - d);
+      const uint32_t row = y / run;
+      return rd(at(row, s, y - row * run));
+    });
+  }
 }
 
 template <typename G, bool NTS>
@@ -1291,6 +1364,9 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     const uint32_t nv = va < vb ? (uint32_t)((vb - va) >> 4) : 0u;
     const uint32_t x0 = (uint32_t)(va - F0);
     const uint32_t staged = S * nb * 16;
+    // 2-byte elements and runs of at least 16 bytes: whole vectors from LDS
+    // (as in scatter_rows)
+    const bool vec = gb == 2 && run >= 16;
     auto elements = [&](uint32_t row, uint32_t s, uint32_t col) {
       G e[NE];
 #pragma unroll
@@ -1304,7 +1380,7 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
       }
       return pack(e);
     };
-    if (run >= 16) {
+    if (vec) {
       for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
         const uint32_t x = x0 + j * 16;
         const uint32_t row = x / FR;
@@ -1347,60 +1423,7 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     const uint32_t nblk = (uint32_t)((align_up16(F0 + (uint64_t)nr * FR) - fa) >> 4);
     stage_blocks(lds, nblk, [&](uint32_t i) -> uint64_t { return fa + (uint64_t)i * 16; });
     __syncthreads();
-    // rank s's byte y of the chunk: row y / run, column y % run
-    auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
-    auto elements = [&](uint32_t s, uint32_t row, uint32_t col) {
-      G e[NE];
-#pragma unroll
-      for (uint32_t k = 0; k < NE; ++k) {
-        e[k] = rd(at(row, s, col));
-        col += gb;
-        if (col == run) col = 0, ++row;
-      }
-      return pack(e);
-    };
-    const uint32_t vmax = L / 16;  // whole vectors of one rank's L bytes, at most
-    if (run >= 16) {
-      for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-        const uint32_t s = i / vmax, j = i - s * vmax;
-        const uint64_t d = R0 + s * f.rank_pitch;
-        const uint64_t va = align_up16(d), vb = align_down16(d + L);
-        if (va + (uint64_t)j * 16 >= vb) continue;
-        const uint32_t y = (uint32_t)(va - d) + j * 16;
-        const uint32_t row = y / run, col = y - row * run;
-        // rank s's bytes from col of row on, then (k1 < 16) from the start
-        // of its next row: one or two unaligned LDS reads
-        const uint32_t k1 = run - col, o = at(row, s, col);
-        const uint32_t o2 = k1 < 16 ? at(row + 1, s, 0) - k1 : 0u;
-        u32x4 v;
-        if (k1 >= 16 && o + 20 <= nblk * 16)
-          v = lds_vec(lds, o);
-        else if (o + 20 <= nblk * 16 && o2 + 20 <= nblk * 16)
-          v = merge_bytes(lds_vec(lds, o), lds_vec(lds, o2), k1);
-        else
-          v = elements(s, row, col);
-        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), v);
-      }
-    } else {
-      for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-        const uint32_t s = i / vmax, j = i - s * vmax;
-        const uint64_t d = R0 + s * f.rank_pitch;
-        const uint64_t va = align_up16(d), vb = align_down16(d + L);
-        if (va + (uint64_t)j * 16 >= vb) continue;
-        const uint32_t y = (uint32_t)(va - d) + j * 16;
-        const uint32_t row = y / run;
-        stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(s, row, y - row * run));
-      }
-    }
-    for (uint32_t t = threadIdx.x; t < 2 * S; t += kBlock) {
-      const uint32_t s = t >> 1;
-      const uint64_t d = R0 + s * f.rank_pitch;
-      fold_ends<G, NTS>(d, d + L, t & 1u, [&](uint64_t ya) {
-        const uint32_t y = (uint32_t)(ya - d);
-        const uint32_t row = y / run;
-        return rd(at(row, s, y - row * run));
-      });
-    }
+    scatter_rows<G, NTS>(lds, delta, nblk, S, run, nr, [&](uint32_t s) { return R0 + s * f.rank_pitch; });
   }
   __syncthreads();  // the next chunk reuses the LDS
 }
@@ -1808,10 +1831,8 @@ __device__ __forceinline__ bool fold_reduce_lds_ok(const fsdp::FoldRed& f, const
 template <int E, int K, typename G, bool NTS>
 __device__ __forceinline__ void fold_reduce_lds(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
                                                 uint64_t r0, uint32_t nr, int avg, uint8_t* lds) {
-  constexpr uint32_t gb = sizeof(G);
-  constexpr uint32_t NE = 16 / gb;
   const uint32_t S = f.nrank, run = (uint32_t)f.run_bytes;
-  const uint32_t FR = S * run, L = nr * run;
+  const uint32_t FR = S * run;
   const uint64_t off = r0 * FR;  // the chunk's first byte in every operand
   const uint64_t F0 = ptr[f.src0] + off;
   const uint64_t fa = align_down16(F0);
@@ -1832,34 +1853,7 @@ __device__ __forceinline__ void fold_reduce_lds(const fsdp::FoldRed& f, const ui
     }
   }
   __syncthreads();
-  auto rd = [&](uint32_t o) { return *reinterpret_cast<const G*>(lds + o); };
-  auto at = [&](uint32_t row, uint32_t s, uint32_t col) { return delta + row * FR + s * run + col; };
-  const uint32_t vmax = L / 16;
-  for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-    const uint32_t s = i / vmax, j = i - s * vmax;
-    const uint64_t d = ptr[f.dst0 + s] + r0 * run;
-    const uint64_t va = align_up16(d), vb = align_down16(d + L);
-    if (va + (uint64_t)j * 16 >= vb) continue;
-    const uint32_t y = (uint32_t)(va - d) + j * 16;
-    uint32_t row = y / run, col = y - row * run;
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (uint32_t k = 0; k < NE; ++k) {
-      w[k * gb / 4] |= (uint32_t)rd(at(row, s, col)) << ((k * gb) % 4 * 8);
-      col += gb;
-      if (col == run) col = 0, ++row;
-    }
-    stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), u32x4{w[0], w[1], w[2], w[3]});
-  }
-  for (uint32_t t = threadIdx.x; t < 2 * S; t += kBlock) {
-    const uint32_t s = t >> 1;
-    const uint64_t d = ptr[f.dst0 + s] + r0 * run;
-    fold_ends<G, NTS>(d, d + L, t & 1u, [&](uint64_t ya) {
-      const uint32_t y = (uint32_t)(ya - d);
-      const uint32_t row = y / run;
-      return rd(at(row, s, y - row * run));
-    });
-  }
+  scatter_rows<G, NTS>(lds, delta, nblk, S, run, nr, [&](uint32_t s) { return ptr[f.dst0 + s] + r0 * run; });
   __syncthreads();  // the next chunk reuses the LDS
 }
 
