@@ -669,6 +669,11 @@ def test_narrow_fold_paths_all_steps(S, R, dtype, aligned):
     ([(300000, 12), (5000, 1028, 4)], 4, 8, torch.float16),  # 6-byte pieces; 2056-byte rows (8 mod 16)
     ([(10000, 4098)], 2, 2, torch.float32),  # 8196-byte pieces: a full row spans two flat chunks
     ([(3000, 8248)], 8, 8, torch.bfloat16),  # 2062-byte pieces over 8 ranks: flat chunks
+    # 2-byte elements in runs of 16 bytes or more: destination vectors read
+    # from LDS whole (inside a run) or merged from two reads (across a run end)
+    ([(400000, 12, 3)], 4, 4, torch.bfloat16),  # 18-byte pieces
+    ([(200000, 40), (30000, 16, 2)], 4, 8, torch.float16),  # 20- and 16-byte pieces
+    ([(60000, 22, 3)], 2, 2, torch.bfloat16),  # 66-byte pieces
 ])
 def test_fold_paths_at_scale(shapes, S, R, dtype):
     """The fold kernels over thousands of chunks (tens of MB per rank), every
