@@ -693,9 +693,18 @@ int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, uint64_t ot
     n += fsdp::item_chunks(segs[k].dst, segs[k].total_bytes, segs[k].rows, segs[k].rows_per_chunk, tu.copy_shift);
     out_bytes += segs[k].total_bytes * segs[k].rows;
   }
-  table->reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg));
+  // the kernel indexes chunks and its grid with 32-bit integers
+  if (n >= (uint64_t(1) << 31)) return fail(FSDP_EINVAL, "too many copy chunks (%llu)", (unsigned long long)n);
+  // item_of[c]: the item of chunk c (the kernel's one-load item lookup)
+  std::vector<uint32_t> item_of(n);
+  for (size_t k = 0; k < segs.size(); ++k) {
+    const uint64_t e = k + 1 < segs.size() ? begin[k + 1] : n;
+    std::fill(item_of.begin() + begin[k], item_of.begin() + e, (uint32_t)k);
+  }
+  table->reserve(begin.size() * 8 + segs.size() * sizeof(fsdp::CopySeg) + item_of.size() * 4);
   append(*table, begin.data(), begin.size());
   append(*table, segs.data(), segs.size());
+  append(*table, item_of.data(), item_of.size());
 #ifdef FSDP_TABLE_HOOK
   fsdp_table_hook(0, es, (uint32_t)segs.size(), n, tu.copy_shift, *table);
 #endif

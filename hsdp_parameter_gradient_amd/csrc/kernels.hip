@@ -24,8 +24,9 @@
 //               arithmetic), each rank's piece written to its output.
 //
 // All four are HBM-bound streaming kernels (no data reuse, no dense
-// contraction): one workgroup of 256 lanes handles one chunk of destination
-// bytes at a time, with 128-bit loads and stores on 16-byte-aligned
+// contraction): one workgroup (512 lanes for the copy, two 16-byte vectors
+// each per 16 KiB chunk; 256 lanes for the others) handles one chunk of
+// destination bytes at a time, with 128-bit loads and stores on 16-byte-aligned
 // destination addresses.  A source whose address differs from the
 // destination's modulo 16 is read as the two aligned 16-byte blocks around
 // each destination vector and realigned in registers with v_alignbyte
@@ -69,8 +70,19 @@
 #ifndef FSDP_NT_LOADS
 #define FSDP_NT_LOADS 1
 #endif
+// The copy kernel's workgroup shape: FSDP_COPY_BLOCK lanes, each with
+// FSDP_COPY_UNROLL 16-byte vectors in flight per iteration, so a 16 KiB chunk
+// is one iteration.  Fewer bytes in flight per wave keep the HBM better fed:
+// measured on MI355X, 512 lanes x 2 vectors move the 51.8 GB RS copy-in of
+// four Llama-7B-shaped layers at 6.4 TB/s and a plain 4 GiB copy at 6.5 TB/s,
+// against 6.0-6.1 TB/s for both with 256 lanes x 4 vectors; 1024 lanes x 1
+// vector is no faster on the large copies and slower on buckets of a few
+// thousand chunks (fewer, larger workgroups fill the chip unevenly).
 #ifndef FSDP_COPY_UNROLL
-#define FSDP_COPY_UNROLL 4
+#define FSDP_COPY_UNROLL 2
+#endif
+#ifndef FSDP_COPY_BLOCK
+#define FSDP_COPY_BLOCK 512
 #endif
 
 namespace {
@@ -88,8 +100,10 @@ __device__ __forceinline__ GMEM T* gptr(uint64_t a) {
   return reinterpret_cast<GMEM T*>(a);
 }
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 256;  // every kernel but the copy
+constexpr int kCopyBlock = FSDP_COPY_BLOCK;
 constexpr int kCopyUnroll = FSDP_COPY_UNROLL;
+static_assert(kCopyBlock % 64 == 0 && kCopyBlock <= 1024, "the copy block is whole waves");
 
 // XCD-aware chunk order.  Workgroups are dispatched to the 8 XCDs
 // round-robin in blockIdx order (and every grid-stride step is a multiple
@@ -226,14 +240,14 @@ __device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __res
   constexpr int QQ = Q >= 0 ? Q : 0;
   const uint32_t lane = threadIdx.x & 63u;
   uint64_t base = 0;
-  for (; base + (uint64_t)kBlock * U <= nv; base += (uint64_t)kBlock * U) {
+  for (; base + (uint64_t)kCopyBlock * U <= nv; base += (uint64_t)kCopyBlock * U) {
     u32x4 a[U];
     if (Q < 0) {
       const uint64_t j = base + threadIdx.x;
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = ldv(s + j + u * kBlock);
+      for (int u = 0; u < U; ++u) a[u] = ldv(s + j + u * kCopyBlock);
 #pragma unroll
-      for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * kBlock, a[u]);
+      for (int u = 0; u < U; ++u) stv<NTS>(d + j + u * kCopyBlock, a[u]);
     } else {
       // each wave owns 64*U consecutive vectors; one extra uniform block
       // (the first of the next wave's range, at most block nv) closes it
@@ -246,7 +260,7 @@ __device__ __forceinline__ void copy_run(gvec* __restrict__ d, const gvec* __res
       for (int u = 0; u < U; ++u) stv<NTS>(d + wb + u * 64 + lane, a[u]);
     }
   }
-  for (uint64_t j = base + threadIdx.x; j < nv; j += kBlock) {
+  for (uint64_t j = base + threadIdx.x; j < nv; j += kCopyBlock) {
     const u32x4 a = ldv(s + j);
     if (Q >= 0) {
       const u32x4 c = ldv(s + j + 1);
@@ -276,11 +290,12 @@ __device__ __forceinline__ void copy_vectors(uint64_t dst, uint64_t src, uint64_
   }
 }
 
-template <bool NTS>
+// nv zero vectors from dst, by a workgroup of BLK lanes.
+template <int BLK, bool NTS>
 __device__ __forceinline__ void zero_vectors(uint64_t dst, uint64_t nv) {
   gvec* __restrict__ d = gptr<u32x4>(dst);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (uint64_t j = threadIdx.x; j < nv; j += kBlock) stv<NTS>(d + j, z);
+  for (uint64_t j = threadIdx.x; j < nv; j += BLK) stv<NTS>(d + j, z);
 }
 
 template <typename T>
@@ -321,12 +336,12 @@ __device__ __forceinline__ void rows_run(uint64_t s0, uint64_t d0, uint32_t nr, 
   constexpr int QQ = Q >= 0 ? Q : 0;
   const uint32_t nv = nr * vpr;
   uint32_t base = 0;
-  for (; base + (uint32_t)kBlock * U <= nv; base += (uint32_t)kBlock * U) {
+  for (; base + (uint32_t)kCopyBlock * U <= nv; base += (uint32_t)kCopyBlock * U) {
     u32x4 a[U];
     uint64_t dof[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const RowVec x = row_vec(base + threadIdx.x + u * kBlock, vpr, src_pitch, dst_pitch);
+      const RowVec x = row_vec(base + threadIdx.x + u * kCopyBlock, vpr, src_pitch, dst_pitch);
       const gvec* sp = gptr<u32x4>(s0 + x.src);
       a[u] = Q < 0 ? ldv(sp) : funnel<QQ>(sp[0], sp[1], b);
       dof[u] = x.dst;
@@ -334,7 +349,7 @@ __device__ __forceinline__ void rows_run(uint64_t s0, uint64_t d0, uint32_t nr, 
 #pragma unroll
     for (int u = 0; u < U; ++u) stv<NTS>(gptr<u32x4>(d0 + dof[u]), a[u]);
   }
-  for (uint32_t q = base + threadIdx.x; q < nv; q += kBlock) {
+  for (uint32_t q = base + threadIdx.x; q < nv; q += kCopyBlock) {
     const RowVec x = row_vec(q, vpr, src_pitch, dst_pitch);
     const gvec* sp = gptr<u32x4>(s0 + x.src);
     stv<NTS>(gptr<u32x4>(d0 + x.dst), Q < 0 ? ldv(sp) : funnel<QQ>(sp[0], sp[1], b));
@@ -356,11 +371,13 @@ __device__ __forceinline__ uint32_t unit_bytes(uint64_t s0, uint64_t d0, uint64_
 // keeps a chunk's rows within 4 GiB of its first row on both sides, so
 // offsets are 32-bit (the workgroup-uniform base plus a 32-bit offset per
 // lane keeps the register count of the whole kernel down).  U units per
-// lane per iteration, all loads before the first store.
+// lane per iteration (as many as a 16 KiB chunk needs, at most 4), all loads
+// before the first store; the remainder is one predicated iteration.
 template <typename W, bool NTS>
 __device__ __forceinline__ void rows_units(uint64_t s0, uint64_t d0, uint32_t nr, uint32_t upr, uint32_t sp,
                                            uint32_t dp) {
-  constexpr int U = sizeof(W) >= 8 ? 4 : 6;
+  constexpr int UC = 16384 / (kCopyBlock * (int)sizeof(W));
+  constexpr int U = UC < 1 ? 1 : UC > 4 ? 4 : UC;
   const uint32_t n = nr * upr;
   const GMEM uint8_t* __restrict__ sb = gptr<uint8_t>(s0);
   GMEM uint8_t* __restrict__ db = gptr<uint8_t>(d0);
@@ -377,14 +394,26 @@ __device__ __forceinline__ void rows_units(uint64_t s0, uint64_t d0, uint32_t nr
       *a = v;
   };
   uint32_t base = 0;
-  for (; base + (uint32_t)kBlock * U <= n; base += (uint32_t)kBlock * U) {
+  for (; base + (uint32_t)kCopyBlock * U <= n; base += (uint32_t)kCopyBlock * U) {
     W v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld(off(base + threadIdx.x + u * kBlock, sp));
+    for (int u = 0; u < U; ++u) v[u] = ld(off(base + threadIdx.x + u * kCopyBlock, sp));
 #pragma unroll
-    for (int u = 0; u < U; ++u) st(off(base + threadIdx.x + u * kBlock, dp), v[u]);
+    for (int u = 0; u < U; ++u) st(off(base + threadIdx.x + u * kCopyBlock, dp), v[u]);
   }
-  for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) st(off(q, dp), ld(off(q, sp)));
+  if (base < n) {
+    W v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t q = base + threadIdx.x + u * kCopyBlock;
+      if (q < n) v[u] = ld(off(q, sp));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t q = base + threadIdx.x + u * kCopyBlock;
+      if (q < n) st(off(q, dp), v[u]);
+    }
+  }
 }
 
 // Chunk k of a strided block (CopySeg with rows > 1): rows
@@ -434,7 +463,7 @@ __device__ __forceinline__ void copy_rows(const fsdp::CopySeg& sg, uint64_t k) {
     }
   }
   if (head || tail < B) {
-    for (uint32_t t = threadIdx.x; t < 2 * nr; t += kBlock) {
+    for (uint32_t t = threadIdx.x; t < 2 * nr; t += kCopyBlock) {
       const uint32_t row = t >> 1;
       const uint64_t lo = (t & 1) ? tail : 0, hi = (t & 1) ? B : head;
       const uint64_t sr = s0 + row * sg.src_pitch, dr = d0 + row * sg.dst_pitch;
@@ -443,48 +472,60 @@ __device__ __forceinline__ void copy_rows(const fsdp::CopySeg& sg, uint64_t k) {
   }
 }
 
+// Chunk k of item sg.
 template <typename T, bool NTS>
-__global__ __launch_bounds__(kBlock) void seg_copy_kernel(const uint64_t* __restrict__ begin,
-                                                          const fsdp::CopySeg* __restrict__ segs,
-                                                          uint32_t n_seg, uint64_t n_chunks,
-                                                          uint32_t shift) {
+__device__ __forceinline__ void copy_chunk(const fsdp::CopySeg& sg, uint64_t k, uint32_t shift) {
+  if (sg.rows > 1) {
+    copy_rows<T, NTS>(sg, k);
+    return;
+  }
   const uint64_t CH = uint64_t(1) << shift;
-  for (uint64_t slot = blockIdx.x; slot < n_chunks; slot += gridDim.x) {
-    const uint64_t c = xcd_chunk(slot, n_chunks);
-    const uint32_t j = find_item(begin, n_seg, c);
-    const fsdp::CopySeg sg = segs[j];
-    const uint64_t k = c - begin[j];
-    if (sg.rows > 1) {
-      copy_rows<T, NTS>(sg, k);
-      continue;
-    }
-    const uint64_t base = (sg.dst >> shift) << shift;
-    const uint64_t seg_end = sg.dst + sg.total_bytes;
-    const uint64_t cend = sg.dst + sg.copy_bytes;
-    const uint64_t w0 = base + k * CH;
-    const uint64_t lo = w0 > sg.dst ? w0 : sg.dst;
-    const uint64_t hi = (w0 + CH) < seg_end ? (w0 + CH) : seg_end;
+  const uint64_t base = (sg.dst >> shift) << shift;
+  const uint64_t seg_end = sg.dst + sg.total_bytes;
+  const uint64_t cend = sg.dst + sg.copy_bytes;
+  const uint64_t w0 = base + k * CH;
+  const uint64_t lo = w0 > sg.dst ? w0 : sg.dst;
+  const uint64_t hi = (w0 + CH) < seg_end ? (w0 + CH) : seg_end;
 
-    // whole vectors of data
-    const uint64_t ca = align_up16(lo);
-    const uint64_t cb = align_down16(hi < cend ? hi : cend);
-    if (ca < cb) copy_vectors<NTS>(ca, sg.src + (ca - sg.dst), (cb - ca) >> 4);
-    // whole vectors of padding
-    const uint64_t za = align_up16(lo > cend ? lo : cend);
-    const uint64_t zb = align_down16(hi);
-    if (za < zb) zero_vectors<NTS>(za, (zb - za) >> 4);
-    // vectors cut by the window start, the data/padding edge, the segment end
-    if (threadIdx.x < 3) {
-      const uint64_t a_lo = align_down16(lo);
-      const uint64_t a_c = align_down16(cend);
-      const uint64_t a_hi = align_down16(hi);
-      const bool p_lo = (lo & 15) != 0;
-      const bool p_c = (cend & 15) != 0 && lo < cend && cend < hi && !(p_lo && a_c == a_lo);
-      const bool p_hi = (hi & 15) != 0 && !(p_lo && a_hi == a_lo) && !(p_c && a_hi == a_c);
-      if (threadIdx.x == 0 && p_lo) copy_partial<T>(a_lo, lo, hi, sg);
-      if (threadIdx.x == 1 && p_c) copy_partial<T>(a_c, lo, hi, sg);
-      if (threadIdx.x == 2 && p_hi) copy_partial<T>(a_hi, lo, hi, sg);
-    }
+  // whole vectors of data
+  const uint64_t ca = align_up16(lo);
+  const uint64_t cb = align_down16(hi < cend ? hi : cend);
+  if (ca < cb) copy_vectors<NTS>(ca, sg.src + (ca - sg.dst), (cb - ca) >> 4);
+  // whole vectors of padding
+  const uint64_t za = align_up16(lo > cend ? lo : cend);
+  const uint64_t zb = align_down16(hi);
+  if (za < zb) zero_vectors<kCopyBlock, NTS>(za, (zb - za) >> 4);
+  // vectors cut by the window start, the data/padding edge, the segment end
+  if (threadIdx.x < 3) {
+    const uint64_t a_lo = align_down16(lo);
+    const uint64_t a_c = align_down16(cend);
+    const uint64_t a_hi = align_down16(hi);
+    const bool p_lo = (lo & 15) != 0;
+    const bool p_c = (cend & 15) != 0 && lo < cend && cend < hi && !(p_lo && a_c == a_lo);
+    const bool p_hi = (hi & 15) != 0 && !(p_lo && a_hi == a_lo) && !(p_c && a_hi == a_c);
+    if (threadIdx.x == 0 && p_lo) copy_partial<T>(a_lo, lo, hi, sg);
+    if (threadIdx.x == 1 && p_c) copy_partial<T>(a_c, lo, hi, sg);
+    if (threadIdx.x == 2 && p_hi) copy_partial<T>(a_hi, lo, hi, sg);
+  }
+}
+
+// item_of[c] is the item that chunk c belongs to (the planner's table), so
+// a workgroup finds its item with one scalar load; a search of the chunk
+// prefix (64 lanes probing 64 cache lines) cost the one-vector-per-lane
+// copy a fifth of its rate.  The grid is the chunk count, or a multiple of 8
+// below it (n_chunks < 2^31); the loop tests for the exit right after the
+// stores, so no wave waits for its stores to land before it ends.
+template <typename T, bool NTS>
+__global__ __launch_bounds__(kCopyBlock) void seg_copy_kernel(const uint64_t* __restrict__ begin,
+                                                              const fsdp::CopySeg* __restrict__ segs,
+                                                              const uint32_t* __restrict__ item_of,
+                                                              uint32_t n_chunks, uint32_t shift) {
+  for (uint32_t slot = blockIdx.x;;) {
+    const uint32_t c = (uint32_t)xcd_chunk(slot, n_chunks);
+    const uint32_t j = item_of[c];
+    copy_chunk<T, NTS>(segs[j], c - begin[j], shift);
+    slot += gridDim.x;
+    if (slot >= n_chunks) return;
   }
 }
 
@@ -1055,7 +1096,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
     const uint64_t za = align_up16(lo > cend ? lo : cend);
     const uint64_t zb = align_down16(hi);
     if (za < zb) {
-      for (uint32_t m = 0; m < jb.ndst; ++m) zero_vectors<NTS>(ptr[jb.dst0 + m] + (za - d0), (zb - za) >> 4);
+      for (uint32_t m = 0; m < jb.ndst; ++m) zero_vectors<kBlock, NTS>(ptr[jb.dst0 + m] + (za - d0), (zb - za) >> 4);
     }
     // vectors cut by the window start, the data/padding edge, the job end
     if (threadIdx.x < 3) {
@@ -1971,20 +2012,23 @@ struct Launch {
 int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, uint64_t n_chunks,
                          uint32_t chunk_shift, uint32_t max_grid, int stream_stores, void* stream,
                          void* start_event, void* stop_event) {
+  if (n_chunks == 0 || n_chunks >= (uint64_t(1) << 31)) return (int)hipErrorInvalidValue;
   const uint64_t* begin = static_cast<const uint64_t*>(dev_table);
   const fsdp::CopySeg* segs = reinterpret_cast<const fsdp::CopySeg*>(begin + n_seg);
-  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kBlock), static_cast<hipStream_t>(stream),
+  const uint32_t* item_of = reinterpret_cast<const uint32_t*>(segs + n_seg);
+  const uint32_t nc = (uint32_t)n_chunks;
+  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kCopyBlock), static_cast<hipStream_t>(stream),
                   static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   if (elem_bytes == 4) {
     if (stream_stores)
-      go(seg_copy_kernel<uint32_t, true>, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint32_t, true>, begin, segs, item_of, nc, chunk_shift);
     else
-      go(seg_copy_kernel<uint32_t, false>, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint32_t, false>, begin, segs, item_of, nc, chunk_shift);
   } else {
     if (stream_stores)
-      go(seg_copy_kernel<uint16_t, true>, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint16_t, true>, begin, segs, item_of, nc, chunk_shift);
     else
-      go(seg_copy_kernel<uint16_t, false>, begin, segs, n_seg, n_chunks, chunk_shift);
+      go(seg_copy_kernel<uint16_t, false>, begin, segs, item_of, nc, chunk_shift);
   }
   return (int)hipGetLastError();
 }

@@ -3,7 +3,7 @@
 // A table is one contiguous blob in device memory, uploaded once per
 // distinct content and cached by the planner:
 //
-//   copy table    uint64 chunk_begin[n]  |  CopySeg seg[n]
+//   copy table    uint64 chunk_begin[n]  |  CopySeg seg[n]  |  uint32 item_of[chunks]
 //   reduce table  uint64 chunk_begin[n]  |  RedJob job[n]  |  uint64 ptr[m]
 //   fold table    uint64 chunk_begin[n]  |  FoldSeg fold[n]
 //   fold-reduce   uint64 chunk_begin[n]  |  FoldRed item[n]  |  uint64 ptr[m]
@@ -16,7 +16,8 @@
 // of several rows (a strided block: the chunk of a parameter sharded on a
 // non-zero dim) is cut into whole rows instead, rows_per_chunk rows (at most
 // CH bytes) per chunk.  chunk_begin[j] is the global index of item j's first
-// chunk; items are never empty.
+// chunk; items are never empty.  The copy table also maps every chunk to
+// its item (item_of[c] = j with chunk_begin[j] <= c < chunk_begin[j+1]).
 #pragma once
 
 #include <stddef.h>

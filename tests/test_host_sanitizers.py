@@ -155,7 +155,7 @@ def _check_tables(dump):
         state["w"], state["tables"] = [], 0
 
     for kind, elt, a, b, n_chunks, blob in _records(dump):
-        words = np.frombuffer(blob, dtype=np.uint64)
+        words = np.frombuffer(blob[:len(blob) // 8 * 8], dtype=np.uint64)  # a copy table ends in 32-bit words
         if kind == 2:  # the next call's output and input spans
             finish()
             sp = [(int(words[2 * k]), int(words[2 * k]) + int(words[2 * k + 1])) for k in range(a + b)]
@@ -166,12 +166,16 @@ def _check_tables(dump):
         if kind == 0:
             recs = words[n:n + 8 * n].reshape(n, 8)
             segs = [tuple(int(v) for v in r) for r in recs]
-            # the planner's chunk prefix is the one the kernel searches
+            # the planner's chunk prefix is the one the kernel indexes
             want, c = [], 0
             for sg in segs:
                 want.append(c)
                 c += KI.item_chunks(sg[1], sg[3], sg[4], sg[7], shift)
             assert begin == want and c == n_chunks
+            # item_of maps every chunk to its item, as the prefix does
+            assert len(blob) == 72 * n + 4 * n_chunks
+            item_of = np.frombuffer(blob[72 * n:], dtype=np.uint32)
+            assert np.array_equal(item_of, np.repeat(np.arange(n, dtype=np.uint32), np.diff(want + [c])))
             writes, reads = KI.check_copy(segs, elt, shift)
             w_iv = [(w[0], w[1]) for w in writes]
             r_iv = [(r[0], r[1]) for r in reads]

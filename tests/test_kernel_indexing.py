@@ -696,6 +696,46 @@ def test_lane_loops_cover_each_vector_once(U, shifted):
         assert all(0 <= r <= top for _, r in reads), (nv, U, shifted)
 
 
+@pytest.mark.parametrize("block,U", [(1024, 1), (512, 2), (256, 4), (256, 1)])
+@pytest.mark.parametrize("shifted", [False, True])
+def test_copy_lane_loops_cover_each_vector_once(block, U, shifted):
+    """copy_run at the copy kernel's workgroup shape (512 lanes, two vectors
+    per lane per iteration) and the other shapes it can be built with."""
+    for nv in (0, 1, 63, 64, 65, 1023, 1024, 1025, 2047, 2048, 3000, 4096, 16384 + 7):
+        writes, reads = lane_loop(nv, U, shifted, block)
+        assert sorted(v for _, v in writes) == list(range(nv)), (nv, block, U, shifted)
+        top = nv if shifted else nv - 1
+        assert all(0 <= r <= top for _, r in reads), (nv, block, U, shifted)
+
+
+def units_loop(n, U, block):
+    """rows_units: whole iterations of block*U units (all loads before the
+    stores), then the remainder as one predicated iteration.  Returns the
+    units each lane moves, as (thread, unit)."""
+    done, base = [], 0
+    while base + block * U <= n:
+        done += [(tid, base + tid + u * block) for tid in range(block) for u in range(U)]
+        base += block * U
+    if base < n:
+        done += [(tid, q) for tid in range(block) for u in range(U)
+                 for q in [base + tid + u * block] if q < n]
+    return done
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+@pytest.mark.parametrize("block", [1024, 512, 256])
+def test_units_loop_moves_each_unit_once(W, block):
+    U = max(1, min(4, 16384 // (block * W)))  # the kernel's units per lane
+    for n in (0, 1, 63, 1023, 1024, 1025, 4095, 4096, 4097, 8192, 8193, 3 * block * U + 5):
+        done = units_loop(n, U, block)
+        assert sorted(q for _, q in done) == list(range(n)), (W, block, n)
+        per_lane = {}
+        for tid, _ in done:
+            per_lane[tid] = per_lane.get(tid, 0) + 1
+        # the units are spread evenly: no lane moves more than its share rounded up
+        assert max(per_lane.values(), default=0) <= -(-n // block)
+
+
 def lds_piece_loop(nv, U, e=0, block=256, piece=512):
     """The shifted reduction's loops (reduce_run_lds): per piece of at most
     `piece` destination vectors, whole iterations of block*U result blocks
