@@ -118,12 +118,17 @@ static_assert(kCopyBlock % 64 == 0 && kCopyBlock <= 1024, "the copy block is who
 // to 128 chunks are all better than the plain order; runs of 256 and one
 // contiguous eighth per XCD are worse on the small bucket).
 constexpr uint64_t kXcdRun = 64;
+#ifndef FSDP_COPY_XCD_RUN
+#define FSDP_COPY_XCD_RUN 64
+#endif
+constexpr uint64_t kCopyXcdRun = FSDP_COPY_XCD_RUN;
 
+template <uint64_t RUN = kXcdRun>
 __device__ __forceinline__ uint64_t xcd_chunk(uint64_t c, uint64_t n) {
-  constexpr uint64_t G = 8 * kXcdRun;
+  constexpr uint64_t G = 8 * RUN;
   if (c >= n / G * G) return c;
   const uint64_t rem = c % G;
-  return c - rem + (rem & 7) * kXcdRun + (rem >> 3);
+  return c - rem + (rem & 7) * RUN + (rem >> 3);
 }
 
 __device__ __forceinline__ uint64_t align_down16(uint64_t a) { return a & ~uint64_t(15); }
@@ -521,7 +526,7 @@ __global__ __launch_bounds__(kCopyBlock) void seg_copy_kernel(const uint64_t* __
                                                               const uint32_t* __restrict__ item_of,
                                                               uint32_t n_chunks, uint32_t shift) {
   for (uint32_t slot = blockIdx.x;;) {
-    const uint32_t c = (uint32_t)xcd_chunk(slot, n_chunks);
+    const uint32_t c = (uint32_t)xcd_chunk<kCopyXcdRun>(slot, n_chunks);
     const uint32_t j = item_of[c];
     copy_chunk<T, NTS>(segs[j], c - begin[j], shift);
     slot += gridDim.x;
