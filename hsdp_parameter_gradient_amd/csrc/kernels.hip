@@ -524,12 +524,14 @@ template <typename T, bool NTS>
 __global__ __launch_bounds__(kCopyBlock) void seg_copy_kernel(const uint64_t* __restrict__ begin,
                                                               const fsdp::CopySeg* __restrict__ segs,
                                                               const uint32_t* __restrict__ item_of,
-                                                              uint32_t n_chunks, uint32_t shift) {
+                                                              uint32_t n_chunks, uint32_t shift, uint32_t grid) {
+  // grid (the launch's workgroup count) comes in with the other kernel
+  // arguments, so the exit test needs no load after the stores
   for (uint32_t slot = blockIdx.x;;) {
     const uint32_t c = (uint32_t)xcd_chunk<kCopyXcdRun>(slot, n_chunks);
     const uint32_t j = item_of[c];
     copy_chunk<T, NTS>(segs[j], c - begin[j], shift);
-    slot += gridDim.x;
+    slot += grid;
     if (slot >= n_chunks) return;
   }
 }
@@ -2022,18 +2024,19 @@ int fsdp_launch_seg_copy(int elem_bytes, const void* dev_table, uint32_t n_seg, 
   const fsdp::CopySeg* segs = reinterpret_cast<const fsdp::CopySeg*>(begin + n_seg);
   const uint32_t* item_of = reinterpret_cast<const uint32_t*>(segs + n_seg);
   const uint32_t nc = (uint32_t)n_chunks;
-  const Launch go{dim3(grid_for(n_chunks, max_grid)), dim3(kCopyBlock), static_cast<hipStream_t>(stream),
+  const uint32_t grid = grid_for(n_chunks, max_grid);
+  const Launch go{dim3(grid), dim3(kCopyBlock), static_cast<hipStream_t>(stream),
                   static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   if (elem_bytes == 4) {
     if (stream_stores)
-      go(seg_copy_kernel<uint32_t, true>, begin, segs, item_of, nc, chunk_shift);
+      go(seg_copy_kernel<uint32_t, true>, begin, segs, item_of, nc, chunk_shift, grid);
     else
-      go(seg_copy_kernel<uint32_t, false>, begin, segs, item_of, nc, chunk_shift);
+      go(seg_copy_kernel<uint32_t, false>, begin, segs, item_of, nc, chunk_shift, grid);
   } else {
     if (stream_stores)
-      go(seg_copy_kernel<uint16_t, true>, begin, segs, item_of, nc, chunk_shift);
+      go(seg_copy_kernel<uint16_t, true>, begin, segs, item_of, nc, chunk_shift, grid);
     else
-      go(seg_copy_kernel<uint16_t, false>, begin, segs, item_of, nc, chunk_shift);
+      go(seg_copy_kernel<uint16_t, false>, begin, segs, item_of, nc, chunk_shift, grid);
   }
   return (int)hipGetLastError();
 }
