@@ -137,6 +137,54 @@ def textbook_rs(grads_int, shapes, members, s, S):
     return out
 
 
+def _fold_operands(n_ops, n, seed):
+    """n_ops float32 arrays of n values over twelve decades (sums of them are
+    not exact, so their bits depend on the order of the additions), with
+    every operand -0.0 at the first four positions (only a fold that starts
+    from the first operand keeps -0.0 there)."""
+    rng = np.random.default_rng(seed)
+    ops = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6, n)).astype(np.float32) for _ in range(n_ops)]
+    for x in ops:
+        x[:4] = np.float32(-0.0)
+    return ops
+
+
+def _left_fold(ops):
+    """NumPy's float32 add.accumulate over the operands in the listed order:
+    out[k] = out[k-1] + ops[k], the sequential fold by the ufunc's definition."""
+    return np.add.accumulate(np.stack(ops), axis=0, dtype=np.float32)[-1]
+
+
+def pin_fold_order(R, S, op, n=2048, seed=7):
+    """The fixed rank order: every RS and fused-AR output is, bit for bit,
+    the ascending-rank left fold of its group's operands in float32 (a
+    different routine from the oracle's loop), then for AVG one float32
+    division by the group size.  Catches a reversed or tree-shaped order and
+    a fold started from +0.0."""
+    bad = []
+    D = R // S
+    I = n
+    rs_in = _fold_operands(R, S * I, seed)
+    outs = O.rs_reduce(rs_in, I, R, S, op)
+    for g in range(R):
+        d, s = divmod(g, S)
+        want = _left_fold([rs_in[d * S + t][s * I:(s + 1) * I] for t in range(S)])
+        if op == O.AVG:
+            want = np.divide(want, np.float32(S), dtype=np.float32)
+        if not np.array_equal(outs[g].view(np.int32), want.view(np.int32)):
+            bad.append(f"RS fold order R={R} S={S} {op} g={g}")
+    fused = _fold_operands(R, I, seed + 1)
+    outs = O.fused_ar(fused, R, S, op)
+    for g in range(R):
+        s = g % S
+        want = _left_fold([fused[d * S + s] for d in range(D)])
+        if op == O.AVG:
+            want = np.divide(want, np.float32(D), dtype=np.float32)
+        if not np.array_equal(outs[g].view(np.int32), want.view(np.int32)):
+            bad.append(f"AR fold order R={R} S={S} {op} g={g}")
+    return bad
+
+
 def pin_rs_exact(R, S, op, shapes, bf16=False):
     """Integer-valued gradients in [-8, 8]: every partial sum is exact in
     float32 and in bfloat16 (|sum| <= 64 < 2**8), whatever the order."""
@@ -405,6 +453,23 @@ def test_end_to_end_exact_integer_sums(R, S, op):
     assert pin_end_to_end_exact(R, S, op, shapes, buckets=[[s] for s in shapes]) == []
 
 
+@pytest.mark.parametrize("R,S", [(8, 8), (8, 4), (8, 2), (6, 3), (8, 1)])
+@pytest.mark.parametrize("op", [O.SUM, O.AVG])
+def test_reductions_are_the_ascending_rank_fold(R, S, op):
+    assert pin_fold_order(R, S, op) == []
+
+
+def test_fold_order_inputs_tell_orders_apart():
+    """The pin's inputs are sensitive: the reversed fold and a pairwise tree
+    give other bits at many positions, and a fold from +0.0 loses -0.0."""
+    ops = _fold_operands(8, 2048, 7)
+    fwd = _left_fold(ops)
+    assert np.count_nonzero(fwd.view(np.int32) != _left_fold(ops[::-1]).view(np.int32)) > 100
+    tree = ((ops[0] + ops[1]) + (ops[2] + ops[3])) + ((ops[4] + ops[5]) + (ops[6] + ops[7]))
+    assert np.count_nonzero(fwd.view(np.int32) != tree.view(np.int32)) > 100
+    assert np.all(np.signbit(fwd[:4])) and not np.any(np.signbit(np.float32(0.0) + fwd[:4]))
+
+
 def test_float64_error_bound():
     """Non-integer float32 sums: within the float32 rounding bound of the
     exact (float64) result, whatever the summation order."""
@@ -639,6 +704,27 @@ def _rs_slice_at_replicate_index(rs_in, I, R, S, op):
 _ORIG_FUSED_AR = F.fused_ar
 
 
+def _descending_sum(operands):
+    return _ORIG_ORDERED_SUM(list(operands)[::-1])
+
+
+def _pairwise_sum(operands):
+    ops = [F._as_f32(x).astype(np.float32) for x in operands]
+    while len(ops) > 1:
+        ops = [ops[k] + ops[k + 1] if k + 1 < len(ops) else ops[k] for k in range(0, len(ops), 2)]
+    return ops[0]
+
+
+def _zero_start_sum(operands):
+    acc = np.zeros_like(F._as_f32(operands[0]), dtype=np.float32)
+    for x in operands:
+        acc = acc + F._as_f32(x)
+    return acc
+
+
+_ORIG_ORDERED_SUM = F._ordered_sum
+
+
 def _ar_avg_over_shard_size(fused, R, S, op):
     outs = _ORIG_FUSED_AR(fused, R, S, F.SUM)
     return [o / np.float32(S) for o in outs] if op == F.AVG else outs
@@ -664,6 +750,9 @@ MUTANTS = {
     "rs_avg_over_dp_size": ("rs_reduce", _rs_avg_over_dp_size),
     "rs_slice_at_replicate_index": ("rs_reduce", _rs_slice_at_replicate_index),
     "ar_avg_over_shard_size": ("fused_ar", _ar_avg_over_shard_size),
+    "descending_rank_order": ("_ordered_sum", _descending_sum),
+    "pairwise_tree_sum": ("_ordered_sum", _pairwise_sum),
+    "fold_from_zero": ("_ordered_sum", _zero_start_sum),
 }
 
 
@@ -697,6 +786,8 @@ def _all_pins(golden):
         pin_avg_correctly_rounded,
         pin_nonzero_dims,
         lambda: pin_fused_layout(golden),
+        lambda: pin_fold_order(8, 4, O.SUM, n=256),
+        lambda: pin_fold_order(8, 2, O.AVG, n=256),
     ]
     bad = []
     for k, pin in enumerate(pins):
