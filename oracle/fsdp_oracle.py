@@ -48,9 +48,9 @@ formula (worked examples, torch.chunk, brute-force inverse maps, exact
 integer sums, float64 bounds, group lists).  The bit pattern of a non-exact
 float32 sum depends on the summation order: the reductions use the fixed
 rank order, ascending within each group and starting from the first operand
-(the pages leave the order open; the ascending fold is this build's reading
-of a fixed rank order), and a test pins every output bit of them to NumPy's
-float32 add.accumulate over the group's operands in that order.
+(the pages leave the order open; the ascending fold is the reading taken
+here), and a test pins every output bit of them to NumPy's float32
+add.accumulate over the group's operands in that order.
 """
 
 from __future__ import annotations
