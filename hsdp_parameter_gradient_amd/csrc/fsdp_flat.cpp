@@ -680,7 +680,7 @@ uint64_t fold_out_bytes(const std::vector<fsdp::FoldSeg>& folds) {
 // policy).
 int plan_copy(std::vector<fsdp::CopySeg>& segs, int es, Reuse reuse, uint64_t other_out, Plan* p,
               std::vector<uint8_t>* table) {
-  // the kernel's chunk search needs every item non-empty
+  // the chunk prefix and the per-chunk item map need every item non-empty
   segs.erase(std::remove_if(segs.begin(), segs.end(), [](const fsdp::CopySeg& sg) { return sg.total_bytes == 0; }),
              segs.end());
   if (segs.empty()) return FSDP_OK;

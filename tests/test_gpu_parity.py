@@ -151,13 +151,18 @@ def test_fp32_nonpow2_shard_group():
 
 def test_many_parameters_deep_chunk_search():
     """700 small ragged parameters over 8 ranks: 5600 AG segments and 44800
-    RS copy-in segments, so the 64-ary chunk search takes three levels."""
+    RS copy-in segments, most of them a part of one chunk, so the copy
+    kernel's per-chunk item map holds thousands of items; the fused RS
+    copy-reduce's 5600 jobs take the reduce kernel's 64-ary chunk search
+    three levels deep."""
     rng = np.random.default_rng(77)
     shapes = [tuple([int(rng.integers(0, 40))] + ([int(rng.choice([1, 3, 8]))] if rng.random() < 0.5 else []))
               for _ in range(700)]
     w = W.Workload("many_params", 21, 8, 8, tuple(shapes), torch.float32, ("uniform", 1.0), ("normal", 1.0),
                    ("sum", "avg"), W.ALL_STEPS)
-    run_copy_and_rs(w.name, shapes, 8, 8, W.params(w), W.grads(w), shard_offsets=[0, 1, 2, 3], out_offset=1)
+    grads = W.grads(w)
+    run_copy_and_rs(w.name, shapes, 8, 8, W.params(w), grads, shard_offsets=[0, 1, 2, 3], out_offset=1)
+    run_rs_copy_reduce(w.name, shapes, 8, 8, grads, out_offset=1)
 
 
 def test_random_buckets():

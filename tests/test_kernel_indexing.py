@@ -2,7 +2,9 @@
 
 Mirrors, line for line in Python, the address arithmetic of seg_copy_kernel,
 reduce_kernel and fold_copy_kernel (hsdp_parameter_gradient_amd/csrc/
-kernels.hip): the 64-ary chunk search, the chunk windows, the whole-vector
+kernels.hip): the 64-ary chunk search of the reductions and fold kernels
+(the copy kernel reads a per-chunk item map; the host checker compares that
+map with the chunk prefix), the chunk windows, the whole-vector
 ranges, the strided and unit-wise row blocks, the fold items' unit
 decomposition, the zero-fill range and the element-wise edge vectors.  For
 many segment tables it checks that
@@ -12,7 +14,8 @@ many segment tables it checks that
   * no byte outside the destination segments is written;
   * every 16-byte source block read lies inside the aligned envelope of its
     source range (so no read leaves the source's pages);
-  * the chunk search finds the right item for every chunk.
+  * the chunk search finds the right item for every chunk (reductions and
+    fold kernels; the copy's per-chunk map is built from the same prefix).
 
 This is the host-side bounds check of the kernels' indexing; it runs before
 any GPU does.
