@@ -1211,8 +1211,19 @@ __device__ __forceinline__ uint32_t fold_lds_bytes(const fsdp::FoldSeg& f, uint6
 
 // Loads in flight per lane while a chunk is staged through LDS: a loop of
 // one load and one LDS store per block waits a whole memory round trip per
-// block, which caps each workgroup's share of the bandwidth.
-constexpr int kStage = 4;
+// block, which caps each workgroup's share of the bandwidth.  Five blocks per
+// lane cover the whole 18 KiB staging buffer (1152 blocks) in one pass; with
+// four, the few blocks past 1024 (each rank window's edge block of a gather,
+// a scatter's row-edge blocks) cost every chunk a second round trip.
+// Measured on MI355X: RS copy-in of (30000, 2050, 1) and (20000, 1540) bf16
+// on dim 1 3-4 % faster, AG copy-outs of short-row gathers 1-2 % faster,
+// six blocks per lane no better.
+#ifndef FSDP_FOLD_STAGE
+#define FSDP_FOLD_STAGE 5
+#endif
+constexpr int kStage = FSDP_FOLD_STAGE;
+static_assert(FSDP_FOLD_STAGE < 5 || (uint32_t)kStage * kBlock * 16u >= kFoldLds,
+              "one staging pass covers the LDS buffer");
 
 // Stages blocks [0, n) of a chunk in LDS: block i (16 bytes at the aligned
 // global address src(i), or nothing when src(i) is 0) goes to LDS bytes

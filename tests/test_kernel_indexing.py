@@ -711,6 +711,29 @@ def test_copy_lane_loops_cover_each_vector_once(block, U, shifted):
         assert all(0 <= r <= top for _, r in reads), (nv, block, U, shifted)
 
 
+def stage_loop(n, stage, block=256):
+    """stage_blocks: lane t takes blocks i0 + u*block (u < stage) per pass,
+    i0 = t, t + stage*block, ...; returns (passes, [(thread, block)])."""
+    done, passes = [], 0
+    i0 = 0
+    while i0 < n:
+        passes += 1
+        done += [(t, i0 + t + u * block) for t in range(block) for u in range(stage) if i0 + t + u * block < n]
+        i0 += stage * block
+    return passes, done
+
+
+@pytest.mark.parametrize("stage", [4, 5, 6])
+def test_fold_staging_covers_each_block_once(stage):
+    lds_blocks = 18 * 1024 // 16  # the fold kernels' LDS staging buffer
+    for n in (0, 1, 255, 256, 1023, 1024, 1025, 1027, 1100, lds_blocks):
+        passes, done = stage_loop(n, stage)
+        assert sorted(b for _, b in done) == list(range(n)), (stage, n)
+        assert all(16 * b + 16 <= 18 * 1024 for _, b in done)
+        if stage >= 5:  # the kernel's depth: one pass for any window that fits the buffer
+            assert passes <= 1, (stage, n, passes)
+
+
 def units_loop(n, U, block):
     """rows_units: whole iterations of block*U units (all loads before the
     stores), then the remainder as one predicated iteration.  Returns the
