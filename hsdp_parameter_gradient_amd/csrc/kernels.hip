@@ -1249,12 +1249,13 @@ __device__ __forceinline__ void stage_blocks(uint8_t* lds, uint32_t n, Src src) 
 // Reduces blocks [0, n) of a chunk into LDS: block i of every operand t
 // (16 bytes at sb[t] + 16 i) summed in operand order, finished (AVG, 16-bit
 // rounding) and stored at LDS bytes [16 i, 16 i + 16); each lane issues the
-// K loads of two blocks (of one for K >= 4) before the first add, which
-// keeps the wide-unit fold reduce under its register cap.
+// K loads of two blocks (of one for K = 8) before the first add.  Measured on
+// MI355X: two blocks make the 4-rank fold reductions 2-3.5 % faster than
+// one; over 8 ranks they cost occupancy and run 2 % slower.
 template <int E, int K>
 __device__ __forceinline__ void reduce_blocks(uint8_t* lds, uint32_t n, const uint64_t (&sb)[K], int avg,
                                               float nf) {
-  constexpr int B = K >= 4 ? 1 : 2;
+  constexpr int B = K >= 8 ? 1 : 2;
   for (uint32_t i0 = threadIdx.x; i0 < n; i0 += (uint32_t)B * kBlock) {
     u32x4 v[B][K];
 #pragma unroll
