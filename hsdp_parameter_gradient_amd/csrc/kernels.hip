@@ -1225,6 +1225,18 @@ constexpr int kStage = FSDP_FOLD_STAGE;
 static_assert(FSDP_FOLD_STAGE < 5 || (uint32_t)kStage * kBlock * 16u >= kFoldLds,
               "one staging pass covers the LDS buffer");
 
+// x / d in one high multiply, exact whenever x * d < 2^32: with
+// m = ceil(2^32 / d), x * m / 2^32 exceeds x / d by less than x / 2^32, which
+// is below 1 / d, so the floor never reaches the next integer.  The LDS paths
+// of the fold kernels divide offsets inside one chunk's staging window by
+// sizes inside it (both below 2^15), once per vector; the generic 32-bit
+// division takes a reciprocal and two correction steps each time.
+struct FastDiv {
+  uint32_t m;  // 0 stands for d = 1
+  __device__ __forceinline__ explicit FastDiv(uint32_t d) : m(d > 1u ? 0xFFFFFFFFu / d + 1u : 0u) {}
+  __device__ __forceinline__ uint32_t operator()(uint32_t x) const { return m ? __umulhi(x, m) : x; }
+};
+
 // Stages blocks [0, n) of a chunk in LDS: block i (16 bytes at the aligned
 // global address src(i), or nothing when src(i) is 0) goes to LDS bytes
 // [16 i, 16 i + 16); each lane issues up to kStage loads before their LDS
@@ -1345,14 +1357,16 @@ __device__ __forceinline__ void scatter_rows(const uint8_t* lds, uint32_t delta,
     return pack_elts<G>(e);
   };
   const uint32_t vmax = L / 16;  // whole vectors of one rank's L bytes, at most
+  // i < S * vmax and y < L, both within the staged window (below 2^15)
+  const FastDiv by_vmax(vmax), by_run(run);
   if (gb == 2 && run >= 16) {
     for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-      const uint32_t s = i / vmax, j = i - s * vmax;
+      const uint32_t s = by_vmax(i), j = i - s * vmax;
       const uint64_t d = dst(s);
       const uint64_t va = align_up16(d), vb = align_down16(d + L);
       if (va + (uint64_t)j * 16 >= vb) continue;
       const uint32_t y = (uint32_t)(va - d) + j * 16;
-      const uint32_t row = y / run, col = y - row * run;
+      const uint32_t row = by_run(y), col = y - row * run;
       // rank s's bytes from col of row on, then (k1 < 16) from the start of
       // its next row
       const uint32_t k1 = run - col, o = at(row, s, col);
@@ -1368,12 +1382,12 @@ __device__ __forceinline__ void scatter_rows(const uint8_t* lds, uint32_t delta,
     }
   } else {
     for (uint32_t i = threadIdx.x; i < S * vmax; i += kBlock) {
-      const uint32_t s = i / vmax, j = i - s * vmax;
+      const uint32_t s = by_vmax(i), j = i - s * vmax;
       const uint64_t d = dst(s);
       const uint64_t va = align_up16(d), vb = align_down16(d + L);
       if (va + (uint64_t)j * 16 >= vb) continue;
       const uint32_t y = (uint32_t)(va - d) + j * 16;
-      const uint32_t row = y / run;
+      const uint32_t row = by_run(y);
       stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(s, row, y - row * run));
     }
   }
@@ -1409,8 +1423,11 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     // window s: the aligned blocks of rank s's L bytes, rank byte y at
     // s * nb * 16 + (rank base & 15) + y
     const uint32_t nb = (L + 15) / 16 + 1;
+    // block indices, chunk offsets and sizes all lie within the staged
+    // window (below 2^15)
+    const FastDiv by_nb(nb), by_fr(FR), by_run(run);
     stage_blocks(lds, S * nb, [&](uint32_t i) -> uint64_t {
-      const uint32_t s = i / nb, k = i - s * nb;
+      const uint32_t s = by_nb(i), k = i - s * nb;
       const uint64_t a = R0 + s * f.rank_pitch;
       const uint64_t blk = align_down16(a) + (uint64_t)k * 16;
       return blk < align_up16(a + L) ? blk : 0;
@@ -1443,9 +1460,9 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     if (vec) {
       for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
         const uint32_t x = x0 + j * 16;
-        const uint32_t row = x / FR;
+        const uint32_t row = by_fr(x);
         const uint32_t rem = x - row * FR;
-        const uint32_t s = rem / run, col = rem - s * run;
+        const uint32_t s = by_run(rem), col = rem - s * run;
         // the vector's bytes in rank s's row from col on, then (k1 < 16)
         // in the next piece of the full row (rank s + 1, or rank 0 of the
         // next row): one or two unaligned LDS reads
@@ -1463,9 +1480,9 @@ __device__ __forceinline__ void fold_lds(const fsdp::FoldSeg& f, uint64_t r0, ui
     } else {
       for (uint32_t j = threadIdx.x; j < nv; j += kBlock) {
         const uint32_t x = x0 + j * 16;
-        const uint32_t row = x / FR;
+        const uint32_t row = by_fr(x);
         const uint32_t rem = x - row * FR;
-        const uint32_t s = rem / run;
+        const uint32_t s = by_run(rem);
         stv<NTS>(gptr<u32x4>(va + (uint64_t)j * 16), elements(row, s, rem - s * run));
       }
     }

@@ -711,6 +711,32 @@ def test_copy_lane_loops_cover_each_vector_once(block, U, shifted):
         assert all(0 <= r <= top for _, r in reads), (nv, block, U, shifted)
 
 
+def fast_div(x, d):
+    """FastDiv (kernels.hip): x / d as the high 32 bits of x * m, with
+    m = 0xFFFFFFFF // d + 1 (= ceil(2**32 / d)) and d = 1 passed through."""
+    x = np.asarray(x, dtype=np.uint64)
+    if d == 1:
+        return x
+    m = np.uint64(0xFFFFFFFF // d + 1)
+    return (x * m) >> np.uint64(32)
+
+
+def test_fast_div_is_exact_inside_a_staging_window():
+    """Every divisor and numerator below 2**15 (the fold kernels' LDS windows
+    hold 18 KiB): exact at every multiple of d and one below it, and on a
+    dense sample."""
+    lim = 1 << 15
+    for d in range(1, lim):
+        k = np.arange(0, lim // d + 1, dtype=np.uint64) * np.uint64(d)
+        x = np.concatenate([k, k[1:] - np.uint64(1)])
+        x = x[x < lim]
+        assert np.array_equal(fast_div(x, d), x // np.uint64(d)), d
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, lim, 1 << 20).astype(np.uint64)
+    for d in rng.integers(1, lim, 64):
+        assert np.array_equal(fast_div(x, int(d)), x // np.uint64(d)), d
+
+
 def stage_loop(n, stage, block=256):
     """stage_blocks: lane t takes blocks i0 + u*block (u < stage) per pass,
     i0 = t, t + stage*block, ...; returns (passes, [(thread, block)])."""
