@@ -655,8 +655,13 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
   // reduce-sized chunks, or larger ones where a reduce chunk would hold
   // one full row and leave most of itself empty (measured on MI355X:
   // (30000, 2050, 1) bf16 over 2 ranks 85 -> 67 us; short rows lose 2-4 %
-  // with the larger chunks); 0: flat chunks of kFlatChunk bytes
-  f.rows_per_chunk = !whole ? 0 : 2 * S * row_bytes <= CH ? CH / (S * row_bytes) : CHX / (S * row_bytes);
+  // with the larger chunks); chunks of kFoldUnitChunk bytes where the
+  // kernel never stages them through LDS; 0: flat chunks of kFlatChunk bytes
+  const bool units_only = unit > fsdp::kFoldLdsMaxUnit && S < 4;
+  f.rows_per_chunk = !whole        ? 0
+                     : units_only ? std::max<uint64_t>(1, fsdp::kFoldUnitChunk / (S * row_bytes))
+                     : 2 * S * row_bytes <= CH ? CH / (S * row_bytes)
+                                               : CHX / (S * row_bytes);
   f.reserved[0] = whole ? 0 : kFlatChunk;
   f.src0 = (uint32_t)ptrs.size();
   ptrs.insert(ptrs.end(), src.begin(), src.end());

@@ -1131,7 +1131,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
 // address rank0 + s * rank_pitch + (r0 + row) * run_bytes + col units.
 // Consecutive lanes take consecutive full-side units, so both sides are
 // read and written in whole lines.  U units per lane per iteration, all
-// loads before the first store.
+// loads before the first store; the units left after the whole iterations
+// take one predicated iteration (a chunk of one 8 KiB full row of 8-byte
+// units is only that, where a loop of one unit at a time cost a memory
+// round trip per unit).
 template <typename W, bool NTS, int UL = 0>
 __device__ __forceinline__ void fold_units(const fsdp::FoldSeg& f, uint64_t r0, uint32_t nr) {
   constexpr int U = UL > 0 ? UL : sizeof(W) >= 16 ? 4 : 8;
@@ -1170,12 +1173,34 @@ __device__ __forceinline__ void fold_units(const fsdp::FoldSeg& f, uint64_t r0, 
       for (int u = 0; u < U; ++u) st(rank_addr(base + threadIdx.x + u * kBlock), v[u]);
     }
   }
-  for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
-    const uint64_t fa = full0 + (uint64_t)q * sizeof(W);
-    if (f.gather)
-      st(fa, ld(rank_addr(q)));
-    else
-      st(rank_addr(q), ld(fa));
+  if (base < n) {  // the rest: one iteration, all loads first
+    // lanes past the end load the last unit again (no branch around the
+    // loads, which made the compiler wait for each load before the next)
+    // and store nothing
+    W v[U];
+    if (f.gather) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = base + threadIdx.x + u * kBlock;
+        v[u] = ld(rank_addr(q < n ? q : n - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = base + threadIdx.x + u * kBlock;
+        if (q < n) st(full0 + (uint64_t)q * sizeof(W), v[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = base + threadIdx.x + u * kBlock;
+        v[u] = ld(full0 + (uint64_t)(q < n ? q : n - 1) * sizeof(W));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = base + threadIdx.x + u * kBlock;
+        if (q < n) st(rank_addr(q), v[u]);
+      }
+    }
   }
 }
 
@@ -1191,9 +1216,6 @@ __device__ __forceinline__ void fold_units(const fsdp::FoldSeg& f, uint64_t r0, 
 // unit-wise path: AG copy-out 18-27 % faster, RS copy-in up to 2.4x; with 8-
 // and 16-byte units it is 5-25 % slower).  A chunk whose windows do not fit
 // kFoldLds keeps the unit-wise path.
-#ifndef FSDP_FOLD_LDS_MAX_UNIT
-#define FSDP_FOLD_LDS_MAX_UNIT 4
-#endif
 constexpr uint32_t kFoldLds = 18u * 1024u;
 
 // LDS bytes a fold chunk of nr rows needs (0: it does not fit).
@@ -1680,7 +1702,7 @@ __device__ __forceinline__ void fold_flat(const fsdp::FoldSeg& f, uint64_t k, ui
   __syncthreads();  // the next chunk reuses the LDS
 }
 
-// NARROW: every item has a unit of at most FSDP_FOLD_LDS_MAX_UNIT bytes, so
+// NARROW: every item has a unit of at most fsdp::kFoldLdsMaxUnit bytes, so
 // the unit-wise path only serves chunks whose windows do not fit the LDS;
 // it then moves one unit per lane per iteration, which keeps this variant's
 // registers (and so its occupancy) those of the LDS path.
@@ -1703,7 +1725,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NARROW ?
     const uint64_t r0 = (c - begin[j]) * f.rows_per_chunk;
     const uint64_t left = f.rows - r0;
     const uint32_t nr = (uint32_t)(left < f.rows_per_chunk ? left : f.rows_per_chunk);
-    if (f.unit <= FSDP_FOLD_LDS_MAX_UNIT && fold_lds_bytes(f, r0, nr)) {
+    if (f.unit <= fsdp::kFoldLdsMaxUnit && fold_lds_bytes(f, r0, nr)) {
       if (f.unit >= 4)
         fold_lds<uint32_t, NTS>(f, r0, nr, lds);
       else
@@ -1792,7 +1814,9 @@ __device__ __forceinline__ W reduce_unit(const W (&v)[K], int avg, float nf) {
 // units); the result goes to rank s's rows.  Compile-time K: the operand
 // and destination bases are wave-uniform registers, the destination of a
 // unit a select among the K bases, and U units per lane per iteration keep
-// all K*U loads in flight.  K = 0: any operand count, loads one at a time.
+// all K*U loads in flight; over 2 ranks with units under 16 bytes the rest
+// takes one or two more such iterations (a chunk of one 8 KiB row of 8-byte
+// units is only that).  K = 0: any operand count, loads one at a time.
 template <int E, int K, typename W, bool NTS>
 __device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
                                                   uint64_t r0, uint32_t nr, int avg) {
@@ -1848,13 +1872,43 @@ __device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const 
         st(dst_base(s) + dof, reduce_unit<E, W, K>(v[u], avg, nf));
       }
     }
-    for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
-      W v[K];
+    if constexpr (K == 2 && sizeof(W) < 16) {
+      // the rest of a 2-rank group's chunk (never staged through LDS with
+      // such units, so this path carries every chunk): iterations of UT
+      // units per lane, all loads of each first; lanes past the end load
+      // the last unit again (no branch around the loads, which made the
+      // compiler wait for each load before the next) and store nothing.
+      // One iteration for fp32, two for 16-bit elements (which keeps them
+      // out of scratch).
+      constexpr int UT = E != kF32 ? U / 2 : U;
+      for (; base < n; base += (uint32_t)kBlock * UT) {
+        W v[UT][K];
 #pragma unroll
-      for (int t = 0; t < K; ++t) v[t] = __builtin_nontemporal_load(gptr<W>(sb[t] + (uint64_t)q * sizeof(W)));
-      uint32_t s, dof;
-      split(q, &s, &dof);
-      st(dst_base(s) + dof, reduce_unit<E, W, K>(v, avg, nf));
+        for (int u = 0; u < UT; ++u) {
+          const uint32_t q = base + threadIdx.x + u * kBlock;
+          const uint64_t o = (uint64_t)(q < n ? q : n - 1) * sizeof(W);
+#pragma unroll
+          for (int t = 0; t < K; ++t) v[u][t] = __builtin_nontemporal_load(gptr<W>(sb[t] + o));
+        }
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+          const uint32_t q = base + threadIdx.x + u * kBlock;
+          if (q < n) {
+            uint32_t s, dof;
+            split(q, &s, &dof);
+            st(dst_base(s) + dof, reduce_unit<E, W, K>(v[u], avg, nf));
+          }
+        }
+      }
+    } else {  // groups of 4 and 8 ranks stage their chunks through LDS where they can
+      for (uint32_t q = base + threadIdx.x; q < n; q += kBlock) {
+        W v[K];
+#pragma unroll
+        for (int t = 0; t < K; ++t) v[t] = __builtin_nontemporal_load(gptr<W>(sb[t] + (uint64_t)q * sizeof(W)));
+        uint32_t s, dof;
+        split(q, &s, &dof);
+        st(dst_base(s) + dof, reduce_unit<E, W, K>(v, avg, nf));
+      }
     }
   } else {
     constexpr int NE = (int)sizeof(W) / (E == kF32 ? 4 : 2);
@@ -1897,7 +1951,7 @@ __device__ __forceinline__ void fold_reduce_units(const fsdp::FoldRed& f, const 
 // every rank's rows are written as in the scatter of fold_lds.
 __device__ __forceinline__ bool fold_reduce_lds_ok(const fsdp::FoldRed& f, const uint64_t* __restrict__ ptr,
                                                    uint64_t r0, uint32_t nr) {
-  if (f.unit > FSDP_FOLD_LDS_MAX_UNIT && f.nrank < 4) return false;
+  if (f.unit > fsdp::kFoldLdsMaxUnit && f.nrank < 4) return false;
   const uint64_t a = ptr[f.src0];
   for (uint32_t t = 1; t < f.nrank; ++t)
     if ((ptr[f.src0 + t] ^ a) & 15u) return false;
@@ -1970,7 +2024,7 @@ __device__ __forceinline__ void fold_reduce_flat(const fsdp::FoldRed& f, const u
   __syncthreads();  // the next chunk reuses the LDS
 }
 
-// NARROW: every item has a unit of at most FSDP_FOLD_LDS_MAX_UNIT bytes; a
+// NARROW: every item has a unit of at most fsdp::kFoldLdsMaxUnit bytes; a
 // chunk that cannot be staged (operands at different offsets modulo 16, or
 // too large for the LDS) takes the runtime-count unit loop, which keeps
 // this variant's registers those of the LDS path.

@@ -89,6 +89,21 @@ constexpr uint64_t kFlatChunk = 12288;
 constexpr uint64_t kFlatMinRun = 1024;
 constexpr uint32_t kFlatMaxPieces = (uint32_t)(kFlatChunk / kFlatMinRun + 2);
 
+// Fold chunks with units of at most kFoldLdsMaxUnit bytes (and fold-reduce
+// chunks over at least 4 ranks) are staged through LDS where they fit.  A
+// fold-reduce item with wider units over fewer ranks never is: its chunks
+// hold up to kFoldUnitChunk bytes of full-tensor rows, more than the LDS
+// would, so that the fixed cost of a chunk (its item, its bases) is spread
+// over more rows.
+#ifndef FSDP_FOLD_LDS_MAX_UNIT
+#define FSDP_FOLD_LDS_MAX_UNIT 4
+#endif
+#ifndef FSDP_FOLD_UNIT_CHUNK
+#define FSDP_FOLD_UNIT_CHUNK 32768
+#endif
+constexpr uint32_t kFoldLdsMaxUnit = FSDP_FOLD_LDS_MAX_UNIT;
+constexpr uint64_t kFoldUnitChunk = FSDP_FOLD_UNIT_CHUNK;
+
 struct FoldSeg {
   uint64_t full;
   uint64_t run_bytes;
@@ -109,7 +124,8 @@ struct FoldSeg {
 // rows are summed over t in ascending order (whole rows, whole lines) and
 // piece s of the result goes to rank s's output, whose rows are dense from
 // ptr[dst0 + s].  A chunk is rows_per_chunk whole full-tensor rows (at most
-// the chunk size of destination bytes).  unit (16, 8, 4 or 2, at least the
+// the larger of the copy and reduce chunk sizes, or kFoldUnitChunk bytes
+// where the kernel never stages the item through LDS).  unit (16, 8, 4 or 2, at least the
 // element size) is the access width; it divides run_bytes and every pointer.
 // rows_per_chunk == 0 marks flat chunks of reserved[0] bytes of the full
 // tensor, as for FoldSeg; every operand then sits at the same address

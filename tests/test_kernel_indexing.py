@@ -788,6 +788,53 @@ def test_units_loop_moves_each_unit_once(W, block):
         assert max(per_lane.values(), default=0) <= -(-n // block)
 
 
+def tail_units_loop(n, U, UT, block=256):
+    """fold_units / fold_reduce_units: whole iterations of block*U units
+    (all loads before the stores), then the rest in predicated iterations
+    of block*UT units (UT = 1: the loop of one unit per lane at a time).
+    Returns (thread, unit) pairs and the iteration count."""
+    done, base, iters = [], 0, 0
+    while base + block * U <= n:
+        done += [(tid, base + tid + u * block) for tid in range(block) for u in range(U)]
+        base += block * U
+        iters += 1
+    while base < n:
+        done += [(tid, q) for tid in range(block) for u in range(UT)
+                 for q in [base + tid + u * block] if q < n]
+        base += block * UT
+        iters += 1
+    return done, iters
+
+
+@pytest.mark.parametrize("W", [2, 4, 8, 16])
+@pytest.mark.parametrize("K", [None, 2, 3, 4, 6, 8])
+def test_fold_unit_loops_move_each_unit_once(W, K):
+    """K None: the fold copy (U = 4 for 16-byte units, else 8, one
+    predicated iteration for the rest); K: the fold reduce over K operands
+    (U = max(1, U0 // K), U0 = 8 for 16-byte units, else 16; over 2 ranks
+    units under 16 bytes finish in one predicated iteration of U, or two of
+    U // 2 for 16-bit elements, the rest one unit per lane at a time)."""
+    if K is None:
+        U = 4 if W >= 16 else 8
+        UT = U
+    else:
+        U0 = 8 if W >= 16 else 16
+        U = max(1, U0 // K)
+        UT = U if K == 2 and W < 16 else 1  # fp32; 16-bit elements: U // 2 (below)
+    uts = {UT, U // 2} if K == 2 and W < 16 else {UT}
+    for ut in sorted(uts):
+        for rows, run in ((1, 4120), (3, 4120), (1, 8240), (128, 32), (7, 24), (2, 2048)):
+            n = rows * 2 * (run // W) if run % W == 0 else 0
+            done, iters = tail_units_loop(n, U, ut)
+            assert sorted(q for _, q in done) == list(range(n)), (W, K, ut, rows, run)
+            # the whole iterations, then at most ceil(U / ut) predicated ones
+            assert iters <= n // (256 * U) + -(-U // ut)
+            per_lane = {}
+            for tid, _ in done:
+                per_lane[tid] = per_lane.get(tid, 0) + 1
+            assert max(per_lane.values(), default=0) <= -(-n // 256)
+
+
 def lds_piece_loop(nv, U, e=0, block=256, piece=512):
     """The shifted reduction's loops (reduce_run_lds): per piece of at most
     `piece` destination vectors, whole iterations of block*U result blocks
@@ -1134,7 +1181,8 @@ def _merge(iv):
 
 
 FOLD_LDS = 18 * 1024  # kFoldLds
-FOLD_LDS_MAX_UNIT = 4  # FSDP_FOLD_LDS_MAX_UNIT
+FOLD_LDS_MAX_UNIT = 4  # kFoldLdsMaxUnit
+FOLD_UNIT_CHUNK = 32768  # kFoldUnitChunk
 
 
 def fold_lds_bytes(f, r0, nr):
@@ -1436,8 +1484,8 @@ FOLD_RED_FMT = "<3Q4I3Q"  # run_bytes, rows, rows_per_chunk, src0, dst0, nrank, 
 def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     """A fold-reduce item and its pointers as the planner builds them
     (push_fold_reduce: reduce-sized chunks, or copy-sized ones where a
-    reduce chunk would hold one full row); None where the planner keeps
-    other jobs."""
+    reduce chunk would hold one full row, or kFoldUnitChunk-sized ones where
+    the kernel never stages them); None where the planner keeps other jobs."""
     CH, CHX = 1 << shift, 1 << max(shift, copy_shift)
     S = len(src)
     if not fold_rows(run, rows, S, CHX, 16):
@@ -1448,7 +1496,10 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
     if W < es:
         return None
-    per = CH // (S * run) if 2 * S * run <= CH else CHX // (S * run)
+    if W > FOLD_LDS_MAX_UNIT and S < 4:  # never staged: kFoldUnitChunk-byte chunks
+        per = max(1, FOLD_UNIT_CHUNK // (S * run))
+    else:
+        per = CH // (S * run) if 2 * S * run <= CH else CHX // (S * run)
     return (run, rows, per, 0, S, S, W, 0, 0, 0), list(src) + list(dst)
 
 
@@ -1519,7 +1570,8 @@ def emulate_fold_reduce(items, ptr, CH, io=None, lds=True, dtype=np.float32):
 
             _flat_scatter(parts, F0 - fa, lds_mem, g, dst_addr, io, writes, j)
             continue
-        assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= CH
+        cap = FOLD_UNIT_CHUNK if W > FOLD_LDS_MAX_UNIT and S < 4 else CH  # never staged: kFoldUnitChunk
+        assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= cap
         assert all(ptr[k] % W == 0 for k in range(src0, src0 + S)) and all(ptr[k] % W == 0 for k in range(dst0, dst0 + S))
         r0 = (c - begin[j]) * per
         nr = min(per, rows - r0)
