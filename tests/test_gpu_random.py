@@ -9,7 +9,14 @@ element offset.  Per bucket: AG copy-in and copy-out, RS copy-in, the RS
 into a view of a 512-byte-aligned fused buffer that also holds other
 segments, the fused AR over it, and the fused RS copy-reduce, each against
 the oracle on guard-banded NaN-filled buffers.
+
+FSDP_RANDOM_CASES=SEED:COUNT runs COUNT other buckets drawn with SEED
+instead (a longer sweep; their tables are not the ones the CPU emulation
+checks unless tests/bucket_cases.py's generator is run there with the same
+seed).
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -25,6 +32,8 @@ hp = pytest.importorskip("hsdp_parameter_gradient_amd")
 pytestmark = pytest.mark.gpu
 
 SEED, COUNT = 20261202, 40  # the cases test_host_sanitizers.py emulates
+if os.environ.get("FSDP_RANDOM_CASES"):
+    SEED, COUNT = (int(x) for x in os.environ["FSDP_RANDOM_CASES"].split(":"))
 CASES = BC.random_cases(SEED, COUNT)
 
 TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}

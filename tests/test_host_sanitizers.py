@@ -137,6 +137,8 @@ def test_random_bucket_tables_pass_the_kernel_emulation(driver, tmp_path):
 
 
 BC_SEED, BC_COUNT = 20261202, 40  # the cases of test_gpu_random.py (its SEED, COUNT)
+if os.environ.get("FSDP_RANDOM_CASES"):  # a longer sweep, as in test_gpu_random.py
+    BC_SEED, BC_COUNT = (int(x) for x in os.environ["FSDP_RANDOM_CASES"].split(":"))
 
 
 def _check_tables(dump):
