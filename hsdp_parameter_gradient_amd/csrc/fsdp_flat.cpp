@@ -655,11 +655,15 @@ bool push_fold_reduce(std::vector<fsdp::FoldRed>& items, std::vector<uint64_t>& 
   // reduce-sized chunks, or larger ones where a reduce chunk would hold
   // one full row and leave most of itself empty (measured on MI355X:
   // (30000, 2050, 1) bf16 over 2 ranks 85 -> 67 us; short rows lose 2-4 %
-  // with the larger chunks); chunks of kFoldUnitChunk bytes where the
-  // kernel never stages them through LDS; 0: flat chunks of kFlatChunk bytes
+  // with the larger chunks); where the kernel never stages the chunks
+  // through LDS, kFoldUnitChunk bytes and at least two rows (measured on
+  // MI355X, RS copy-reduce over 2 ranks against reduce-sized chunks:
+  // (20000, 1030, 4) fp16 110 -> 84 us, short rows of 8 to 128 bytes 6-15 %
+  // faster; 32 KiB chunks were 3-10 % slower than 16 KiB on short rows);
+  // 0: flat chunks of kFlatChunk bytes
   const bool units_only = unit > fsdp::kFoldLdsMaxUnit && S < 4;
   f.rows_per_chunk = !whole        ? 0
-                     : units_only ? std::max<uint64_t>(1, fsdp::kFoldUnitChunk / (S * row_bytes))
+                     : units_only ? std::max<uint64_t>(2, fsdp::kFoldUnitChunk / (S * row_bytes))
                      : 2 * S * row_bytes <= CH ? CH / (S * row_bytes)
                                                : CHX / (S * row_bytes);
   f.reserved[0] = whole ? 0 : kFlatChunk;

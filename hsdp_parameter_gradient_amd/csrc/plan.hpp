@@ -92,14 +92,16 @@ constexpr uint32_t kFlatMaxPieces = (uint32_t)(kFlatChunk / kFlatMinRun + 2);
 // Fold chunks with units of at most kFoldLdsMaxUnit bytes (and fold-reduce
 // chunks over at least 4 ranks) are staged through LDS where they fit.  A
 // fold-reduce item with wider units over fewer ranks never is: its chunks
-// hold up to kFoldUnitChunk bytes of full-tensor rows, more than the LDS
-// would, so that the fixed cost of a chunk (its item, its bases) is spread
-// over more rows.
+// hold kFoldUnitChunk bytes of full-tensor rows per operand, and at least
+// two rows.  Over 2 ranks that is one whole iteration of the kernel's unit
+// loop for 8- and 16-byte units (every load of the chunk in flight at
+// once); a row longer than half of it would leave half an iteration idle,
+// so such rows go two to a chunk.
 #ifndef FSDP_FOLD_LDS_MAX_UNIT
 #define FSDP_FOLD_LDS_MAX_UNIT 4
 #endif
 #ifndef FSDP_FOLD_UNIT_CHUNK
-#define FSDP_FOLD_UNIT_CHUNK 32768
+#define FSDP_FOLD_UNIT_CHUNK 16384
 #endif
 constexpr uint32_t kFoldLdsMaxUnit = FSDP_FOLD_LDS_MAX_UNIT;
 constexpr uint64_t kFoldUnitChunk = FSDP_FOLD_UNIT_CHUNK;
@@ -124,8 +126,8 @@ struct FoldSeg {
 // rows are summed over t in ascending order (whole rows, whole lines) and
 // piece s of the result goes to rank s's output, whose rows are dense from
 // ptr[dst0 + s].  A chunk is rows_per_chunk whole full-tensor rows (at most
-// the larger of the copy and reduce chunk sizes, or kFoldUnitChunk bytes
-// where the kernel never stages the item through LDS).  unit (16, 8, 4 or 2, at least the
+// the larger of the copy and reduce chunk sizes; where the kernel never
+// stages the item through LDS, kFoldUnitChunk bytes or two rows).  unit (16, 8, 4 or 2, at least the
 // element size) is the access width; it divides run_bytes and every pointer.
 // rows_per_chunk == 0 marks flat chunks of reserved[0] bytes of the full
 // tensor, as for FoldSeg; every operand then sits at the same address

@@ -1182,7 +1182,7 @@ def _merge(iv):
 
 FOLD_LDS = 18 * 1024  # kFoldLds
 FOLD_LDS_MAX_UNIT = 4  # kFoldLdsMaxUnit
-FOLD_UNIT_CHUNK = 32768  # kFoldUnitChunk
+FOLD_UNIT_CHUNK = 16384  # kFoldUnitChunk
 
 
 def fold_lds_bytes(f, r0, nr):
@@ -1484,8 +1484,9 @@ FOLD_RED_FMT = "<3Q4I3Q"  # run_bytes, rows, rows_per_chunk, src0, dst0, nrank, 
 def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     """A fold-reduce item and its pointers as the planner builds them
     (push_fold_reduce: reduce-sized chunks, or copy-sized ones where a
-    reduce chunk would hold one full row, or kFoldUnitChunk-sized ones where
-    the kernel never stages them); None where the planner keeps other jobs."""
+    reduce chunk would hold one full row, or kFoldUnitChunk-sized ones of at
+    least two rows where the kernel never stages them); None where the
+    planner keeps other jobs."""
     CH, CHX = 1 << shift, 1 << max(shift, copy_shift)
     S = len(src)
     if not fold_rows(run, rows, S, CHX, 16):
@@ -1496,8 +1497,8 @@ def fold_reduce_item(src, dst, run, rows, es, shift=13, copy_shift=14):
     W = 16 if m % 16 == 0 else 8 if m % 8 == 0 else 4 if m % 4 == 0 else 2
     if W < es:
         return None
-    if W > FOLD_LDS_MAX_UNIT and S < 4:  # never staged: kFoldUnitChunk-byte chunks
-        per = max(1, FOLD_UNIT_CHUNK // (S * run))
+    if W > FOLD_LDS_MAX_UNIT and S < 4:  # never staged: kFoldUnitChunk bytes, at least two rows
+        per = max(2, FOLD_UNIT_CHUNK // (S * run))
     else:
         per = CH // (S * run) if 2 * S * run <= CH else CHX // (S * run)
     return (run, rows, per, 0, S, S, W, 0, 0, 0), list(src) + list(dst)
@@ -1570,7 +1571,8 @@ def emulate_fold_reduce(items, ptr, CH, io=None, lds=True, dtype=np.float32):
 
             _flat_scatter(parts, F0 - fa, lds_mem, g, dst_addr, io, writes, j)
             continue
-        cap = FOLD_UNIT_CHUNK if W > FOLD_LDS_MAX_UNIT and S < 4 else CH  # never staged: kFoldUnitChunk
+        # never staged: kFoldUnitChunk bytes or two rows
+        cap = max(FOLD_UNIT_CHUNK, 2 * S * run) if W > FOLD_LDS_MAX_UNIT and S < 4 else CH
         assert W in (2, 4, 8, 16) and run % W == 0 and per >= 1 and per * S * run <= cap
         assert all(ptr[k] % W == 0 for k in range(src0, src0 + S)) and all(ptr[k] % W == 0 for k in range(dst0, dst0 + S))
         r0 = (c - begin[j]) * per
