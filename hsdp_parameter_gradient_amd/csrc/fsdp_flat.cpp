@@ -502,13 +502,24 @@ bool rows_fit(uint64_t row_bytes, uint64_t rows, uint32_t shift) {
   return rows >= 2 && row_bytes > 0 && row_bytes <= (uint64_t(1) << shift);
 }
 
+// Rows per chunk of a strided copy block: as many whole rows as a chunk
+// holds, or, for unit-wise rows, the fewest that fill it (one row may cross
+// the chunk size).  Measured on MI355X, 4,120-byte rows of 8-byte units over
+// 2 ranks ((20000, 1030, 4) fp16 sharded on dim 1): four rows per 16 KiB
+// chunk instead of three, RS copy-in 135 -> 117 us, AG copy-out 63 -> 60 us;
+// twice the chunk size was slower than both.
+uint64_t block_rows_per_chunk(uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes, uint32_t shift) {
+  const uint64_t CH = uint64_t(1) << shift;
+  return vector_rows(src_pitch, dst_pitch) ? CH / row_bytes : (CH + row_bytes - 1) / row_bytes;
+}
+
 bool copy_block_ok(uint64_t src, uint64_t dst, uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes,
                    uint64_t rows, uint32_t shift) {
   if (!rows_fit(row_bytes, rows, shift)) return false;
   if (vector_rows(src_pitch, dst_pitch)) return true;
   // unit-wise rows: a chunk's rows lie within 4 GiB of its first row (the
   // kernel's offsets are 32-bit)
-  const uint64_t per = (uint64_t(1) << shift) / row_bytes;
+  const uint64_t per = block_rows_per_chunk(src_pitch, dst_pitch, row_bytes, shift);
   if (per * std::max(src_pitch, dst_pitch) >= (uint64_t(1) << 32)) return false;
   return row_bytes <= kShortRow || ((src | dst | src_pitch | dst_pitch | row_bytes) & 7u) == 0;
 }
@@ -527,7 +538,7 @@ void push_rows(std::vector<fsdp::CopySeg>& segs, uint64_t src, uint64_t dst, uin
     sg.rows = rows;
     sg.src_pitch = src_pitch;
     sg.dst_pitch = dst_pitch;
-    sg.rows_per_chunk = (uint64_t(1) << shift) / row_bytes;
+    sg.rows_per_chunk = block_rows_per_chunk(src_pitch, dst_pitch, row_bytes, shift);
     segs.push_back(sg);
     return;
   }

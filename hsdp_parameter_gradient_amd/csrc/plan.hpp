@@ -30,10 +30,11 @@ namespace fsdp {
 //
 // rows > 1 makes it a strided block of `rows` such rows, row r copied from
 // src + r*src_pitch to dst + r*dst_pitch.  Such a block has no zero fill
-// (copy_bytes == total_bytes) and rows_per_chunk * copy_bytes is at most the
-// chunk size.  When both pitches are multiples of 16 every row has the
-// alignment of the first; otherwise the rows of a chunk lie within 4 GiB of
-// its first row on both sides.
+// (copy_bytes == total_bytes).  When both pitches are multiples of 16 every
+// row has the alignment of the first and rows_per_chunk * copy_bytes is at
+// most the chunk size; otherwise the rows of a chunk lie within 4 GiB of
+// its first row on both sides and rows_per_chunk * copy_bytes is less than
+// the chunk size plus one row.
 struct CopySeg {
   uint64_t src;
   uint64_t dst;

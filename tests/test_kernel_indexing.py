@@ -94,7 +94,8 @@ def emulate_copy(segs, es, shift):
             assert copy == total
             r0 = k * per
             nr = min(per, rows - r0)
-            assert nr >= 1 and nr * copy <= CH
+            # at most a chunk of vector rows; unit-wise rows may cross it by one row
+            assert nr >= 1 and (nr * copy <= CH if (sp | dp) % 16 == 0 else nr * copy < CH + copy)
             d0, s0 = dst + r0 * dp, src + r0 * sp
             if (sp | dp) % 16:  # rows_units: W-byte units, one flat range
                 m = s0 | d0 | sp | dp | copy
@@ -389,6 +390,13 @@ def ag_copy_in_segs(shapes, S, es, ag, shard_addr):
 SHORT_ROW = 1024
 
 
+def block_rows(sp, dp, row_bytes, shift):
+    """Rows per chunk of a strided copy block (block_rows_per_chunk): as many
+    as a chunk holds, or for unit-wise rows the fewest that fill it."""
+    CH = 1 << shift
+    return CH // row_bytes if sp % 16 == 0 and dp % 16 == 0 else -(-CH // row_bytes)
+
+
 def copy_block_ok(src, dst, sp, dp, row_bytes, rows, shift):
     """When the planner emits one strided copy block instead of one item
     per row: the rows fit a chunk, and either both pitches are multiples of
@@ -397,7 +405,7 @@ def copy_block_ok(src, dst, sp, dp, row_bytes, rows, shift):
         return False
     if sp % 16 == 0 and dp % 16 == 0:
         return True
-    if ((1 << shift) // row_bytes) * max(sp, dp) >= 1 << 32:  # the kernel's 32-bit offsets
+    if block_rows(sp, dp, row_bytes, shift) * max(sp, dp) >= 1 << 32:  # the kernel's 32-bit offsets
         return False
     return row_bytes <= SHORT_ROW or (src | dst | sp | dp | row_bytes) % 8 == 0
 
@@ -411,7 +419,7 @@ def push_rows(segs, src, dst, row_bytes, rows, sp, dp, shift):
     if row_bytes == 0 or rows == 0:
         return
     if copy_block_ok(src, dst, sp, dp, row_bytes, rows, shift):
-        segs.append((src, dst, row_bytes, row_bytes, rows, sp, dp, (1 << shift) // row_bytes))
+        segs.append((src, dst, row_bytes, row_bytes, rows, sp, dp, block_rows(sp, dp, row_bytes, shift)))
     else:
         segs.extend((src + r * sp, dst + r * dp, row_bytes, row_bytes) for r in range(rows))
 
