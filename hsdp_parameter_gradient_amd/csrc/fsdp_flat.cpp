@@ -506,7 +506,7 @@ bool rows_fit(uint64_t row_bytes, uint64_t rows, uint32_t shift) {
 // holds, or, for unit-wise rows, the fewest that fill it (one row may cross
 // the chunk size).  Measured on MI355X, 4,120-byte rows of 8-byte units over
 // 2 ranks ((20000, 1030, 4) fp16 sharded on dim 1): four rows per 16 KiB
-// chunk instead of three, RS copy-in 135 -> 117 us, AG copy-out 63 -> 60 us;
+// chunk instead of three, RS copy-in 132 -> 115 us, AG copy-out 63 -> 60 us;
 // twice the chunk size was slower than both.
 uint64_t block_rows_per_chunk(uint64_t src_pitch, uint64_t dst_pitch, uint64_t row_bytes, uint32_t shift) {
   const uint64_t CH = uint64_t(1) << shift;
