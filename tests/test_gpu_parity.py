@@ -639,6 +639,20 @@ def test_strided_blocks_all_steps(S, R, dtype):
     run_nonzero_dims(shapes, dims, S, R, dtype, aligned=True)
 
 
+@pytest.mark.parametrize("S,R,dtype,aligned", [(2, 4, torch.float16, True), (2, 4, torch.float32, True),
+                                               (2, 2, torch.bfloat16, False), (2, 6, torch.float16, False)])
+def test_chunk_filling_rows_all_steps(S, R, dtype, aligned):
+    """Dim-1 parameters over 2 ranks with many rows per item: 4,120-byte
+    rank rows of 8-byte units (strided copy blocks whose chunks take the
+    fewest rows that fill them, one row crossing the chunk size; fold
+    reductions of 8-byte units, two rows per chunk) and rows of 8 to 128
+    bytes whose fold reductions take 16 KiB chunks of the unit loop, several
+    chunks each and a short last one; every step against the oracle."""
+    shapes = [(50, 1030, 4), (3001, 4), (3000, 8), (1000, 64), (77, 1030, 2), (5,)]
+    dims = [1, 1, 1, 1, 1, 0]
+    run_nonzero_dims(shapes, dims, S, R, dtype, aligned)
+
+
 @pytest.mark.parametrize("S,R,dtype,aligned", [(2, 4, torch.float32, False), (2, 4, torch.bfloat16, True),
                                                (4, 8, torch.bfloat16, False), (4, 8, torch.float16, True),
                                                (2, 6, torch.float16, False), (4, 4, torch.float32, True)])
