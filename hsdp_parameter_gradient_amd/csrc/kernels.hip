@@ -1132,9 +1132,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const uint64_t* __restri
 // Consecutive lanes take consecutive full-side units, so both sides are
 // read and written in whole lines.  U units per lane per iteration, all
 // loads before the first store; the units left after the whole iterations
-// take one predicated iteration (a chunk of one 8 KiB full row of 8-byte
-// units is only that, where a loop of one unit at a time cost a memory
-// round trip per unit).
+// take one more such iteration with predicated stores (a loop of one unit
+// at a time would cost a memory round trip per unit).
 template <typename W, bool NTS, int UL = 0>
 __device__ __forceinline__ void fold_units(const fsdp::FoldSeg& f, uint64_t r0, uint32_t nr) {
   constexpr int U = UL > 0 ? UL : sizeof(W) >= 16 ? 4 : 8;
